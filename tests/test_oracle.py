@@ -1,0 +1,374 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each test ties the oracle to something other than itself: a closed form, a
+different but mathematically equal formula, an invariant the pages imply, a
+brute-force O(N^2) form, finite differences, or published known-answer data.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import synth
+from oracle import dense, stream
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand_case(seed, N, d, P, L, scale_w=1.0):
+    rng = np.random.default_rng(seed)
+    Q = rng.standard_normal((N, d))
+    K = rng.standard_normal((N, d))
+    V = rng.standard_normal((N, d))
+    dO = rng.standard_normal((N, d))
+    W = scale_w * rng.standard_normal((L, P, d))
+    return Q, K, V, dO, W
+
+
+def sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def assignments_by_product(X, W, beta):
+    """Independent closed form of the corner softmax: because the corner
+    logit is a sum of per-plane terms, softmax over the 2^P corners equals the
+    product over planes of sigmoid(2*beta*sign*tanh(h))."""
+    L, P, d = W.shape
+    Xh = X / np.linalg.norm(X, axis=1, keepdims=True)
+    u = np.tanh(np.einsum("nd,lpd->nlp", Xh, W))
+    a = np.ones((X.shape[0], L, 1 << P))
+    for r in range(1 << P):
+        for p in range(P):
+            sgn = 1.0 if (r >> p) & 1 else -1.0
+            a[:, :, r] *= sigmoid(2.0 * beta * sgn * u[:, :, p])
+    return a
+
+
+# --------------------------------------------------------------------------
+# soft bucketing
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("P", [1, 2, 3, 4, 6])
+@pytest.mark.parametrize("beta", [0.3, 1.0, 4.0])
+def test_corner_softmax_equals_product_of_sigmoids(P, beta):
+    Q, _, _, _, W = rand_case(P * 7 + int(beta * 10), 20, 8, P, 3)
+    a, _ = dense.soft_buckets(Q, W, beta)
+    np.testing.assert_allclose(a, assignments_by_product(Q, W, beta), rtol=0, atol=1e-14)
+
+
+def test_assignments_sum_to_one():
+    Q, _, _, _, W = rand_case(3, 50, 16, 4, 5)
+    a, _ = dense.soft_buckets(Q, W, 1.0)
+    assert np.max(np.abs(a.sum(-1) - 1.0)) < 1e-12
+    assert np.all(a > 0)
+
+
+def test_hard_id_bit_order():
+    # Planes e0, e1, e2 and x = (1, -1, 1, 0): signs (+, -, +) -> bits 0 and 2 -> id 5.
+    W = np.zeros((1, 3, 4))
+    W[0, 0, 0] = W[0, 1, 1] = W[0, 2, 2] = 1.0
+    X = np.array([[1.0, -1.0, 1.0, 0.0], [-1.0, 1.0, 0.5, 0.0], [-1.0, -1.0, -1.0, 2.0]])
+    ids, nz = dense.hard_hash(X, W)
+    assert ids[:, 0].tolist() == [5, 6, 0]
+    assert nz == 0
+    ids2, nz2 = stream.hard_hash(X, W)
+    assert ids2.tolist() == ids.tolist() and nz2 == 0
+
+
+def test_large_beta_reaches_hard_assignment():
+    """As beta grows the soft assignment becomes the one-hot of the hard id:
+    ties the soft corner convention to the hard-hash bit order."""
+    Q, _, _, _, W = rand_case(11, 60, 16, 3, 4)
+    ids, _ = dense.hard_hash(Q, W)
+    Xh = Q / np.linalg.norm(Q, axis=1, keepdims=True)
+    h = np.einsum("nd,lpd->nlp", Xh, W)
+    a, _ = dense.soft_buckets(Q, W, 1e4)
+    ok = np.min(np.abs(h), axis=-1) > 1e-2
+    onehot = np.eye(8)[ids]
+    assert np.max(np.abs(a - onehot)[ok]) < 1e-6
+    assert ok.mean() > 0.5
+
+
+# --------------------------------------------------------------------------
+# closed forms: collision probability and the expected soft kernel
+# --------------------------------------------------------------------------
+
+def pair_at_angle(theta, d, rng):
+    x = rng.standard_normal(d)
+    x /= np.linalg.norm(x)
+    y = rng.standard_normal(d)
+    y -= x * (x @ y)
+    y /= np.linalg.norm(y)
+    return x, math.cos(theta) * x + math.sin(theta) * y
+
+
+@pytest.mark.parametrize("theta", [0.3, 1.0, 2.0])
+@pytest.mark.parametrize("P", [1, 4])
+def test_hard_collision_probability(theta, P):
+    """Sign random projections collide with probability 1 - theta/pi per plane
+    (Goemans-Williamson / Charikar), so P independent planes give
+    (1 - theta/pi)^P: the angular kernel power the pages call gamma = P."""
+    rng = np.random.default_rng(int(theta * 100) + P)
+    d, L = 8, 200_000
+    q, k = pair_at_angle(theta, d, rng)
+    W = rng.standard_normal((L, P, d))
+    iq, _ = stream.hard_hash(q[None], W)
+    ik, _ = stream.hard_hash(k[None], W)
+    rate = np.mean(iq[0] == ik[0])
+    p = (1.0 - theta / math.pi) ** P
+    sigma = math.sqrt(p * (1 - p) / L)
+    assert abs(rate - p) < 4.5 * sigma, (rate, p, sigma)
+
+
+def kappa(theta, beta, n=2401, span=8.0):
+    """E over one Gaussian plane of the per-plane soft overlap, by a tensor
+    trapezoid rule over (s, t) standard normal with correlation cos(theta)."""
+    x = np.linspace(-span, span, n)
+    w = np.full(n, x[1] - x[0])
+    w[0] = w[-1] = 0.5 * (x[1] - x[0])
+    w = w * np.exp(-0.5 * x * x) / math.sqrt(2 * math.pi)
+    rho = math.cos(theta)
+    s = x[:, None]
+    t = rho * x[:, None] + math.sqrt(max(0.0, 1 - rho * rho)) * x[None, :]
+    ps = sigmoid(2 * beta * np.tanh(s))
+    pt = sigmoid(2 * beta * np.tanh(t))
+    f = ps * pt + (1 - ps) * (1 - pt)
+    return float(np.sum(w[:, None] * w[None, :] * f))
+
+
+@pytest.mark.parametrize("theta,beta,P", [(0.3, 1.0, 4), (1.0, 1.0, 2), (1.5, 3.0, 3)])
+def test_expected_soft_kernel(theta, beta, P):
+    rng = np.random.default_rng(5)
+    d, L = 8, 40_000
+    q, k = pair_at_angle(theta, d, rng)
+    W = rng.standard_normal((L, P, d))
+    aq, _ = dense.soft_buckets(q[None], W, beta)
+    ak, _ = dense.soft_buckets(k[None], W, beta)
+    per_table = np.sum(aq[0] * ak[0], axis=-1)
+    est, se = per_table.mean(), per_table.std() / math.sqrt(L)
+    assert abs(est - kappa(theta, beta) ** P) < 4.5 * se
+
+
+def test_kappa_limits():
+    # beta -> infinity: the soft overlap tends to the hard collision probability.
+    assert abs(kappa(0.3, 200.0) - (1 - 0.3 / math.pi)) < 3e-3
+    # beta -> 0: uniform assignment, overlap 1/2 per plane.
+    assert abs(kappa(1.0, 1e-6) - 0.5) < 1e-6
+
+
+# --------------------------------------------------------------------------
+# aggregation + readout == brute-force kernel attention
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("P,L", [(1, 1), (2, 3), (4, 5)])
+def test_sketch_equals_bruteforce_kernel_attention(causal, P, L):
+    """O_i = sum_j Khat_ij v_j / sum_j Khat_ij with Khat_ij = sum_l <a_Q[i,l], a_K[j,l]>
+    (masked to j <= i when causal): the sketch reaches this exactly by
+    associativity."""
+    Q, K, V, _, W = rand_case(P * 10 + L, 33, 12, P, L)
+    beta = 0.7
+    aq = assignments_by_product(Q, W, beta)
+    ak = assignments_by_product(K, W, beta)
+    Kh = np.einsum("ilr,jlr->ij", aq, ak)
+    if causal:
+        Kh = np.tril(Kh)
+    ref = (Kh @ V) / Kh.sum(1, keepdims=True)
+    np.testing.assert_allclose(dense.forward(Q, K, V, W, beta, causal), ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(stream.forward(Q, K, V, W, beta, causal), ref, rtol=1e-12, atol=1e-13)
+
+
+def test_large_beta_many_tables_approaches_angular_attention():
+    """In the hard limit with many tables RACE estimates attention with the
+    angular kernel (1 - theta/pi)^P; the error shrinks with L (the variance
+    term of the pages' error bound)."""
+    rng = np.random.default_rng(9)
+    N, d, P = 24, 8, 2
+    Q = rng.standard_normal((N, d))
+    K = rng.standard_normal((N, d))
+    V = rng.standard_normal((N, d))
+    qh = Q / np.linalg.norm(Q, axis=1, keepdims=True)
+    kh = K / np.linalg.norm(K, axis=1, keepdims=True)
+    Kang = (1 - np.arccos(np.clip(qh @ kh.T, -1, 1)) / math.pi) ** P
+    ref = (Kang @ V) / Kang.sum(1, keepdims=True)
+    errs = []
+    for L in (64, 4096):
+        W = rng.standard_normal((L, P, d))
+        O = stream.forward(Q, K, V, W, 1e4, False)
+        errs.append(np.linalg.norm(O - ref) / np.linalg.norm(ref))
+    assert errs[1] < errs[0] and errs[1] < 0.05, errs
+
+
+# --------------------------------------------------------------------------
+# invariants
+# --------------------------------------------------------------------------
+
+def test_causal_future_perturbation_bit_identical():
+    Q, K, V, dO, W = rand_case(21, 40, 8, 3, 2)
+    t = 17
+    O = stream.forward(Q, K, V, W, 1.0, True)
+    Q2, K2, V2 = Q.copy(), K.copy(), V.copy()
+    Q2[t + 1:] += 3.0
+    K2[t + 1:] *= -2.0
+    V2[t + 1:] += 1.0
+    O2 = stream.forward(Q2, K2, V2, W, 1.0, True)
+    assert np.array_equal(O[: t + 1], O2[: t + 1])
+    assert not np.allclose(O[t + 1:], O2[t + 1:])
+    # mirror for the backward: earlier queries and dO do not reach later dK/dV
+    g = stream.backward(Q, K, V, W, dO, 1.0, True)
+    Q3, dO3 = Q.copy(), dO.copy()
+    Q3[:t] += 1.5
+    dO3[:t] *= -3.0
+    g3 = stream.backward(Q3, K, V, W, dO3, 1.0, True)
+    for a, b in zip(g[1:], g3[1:]):
+        np.testing.assert_allclose(a[t:], b[t:], rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_scale_invariance_of_queries_and_keys(causal):
+    Q, K, V, _, W = rand_case(4, 30, 8, 2, 3)
+    O = stream.forward(Q, K, V, W, 1.0, causal)
+    O2 = stream.forward(3.7 * Q, 0.05 * K, V, W, 1.0, causal)
+    np.testing.assert_allclose(O, O2, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_values_linear_and_affine(causal):
+    Q, K, V, _, W = rand_case(6, 30, 8, 2, 3)
+    rng = np.random.default_rng(1)
+    V2 = rng.standard_normal(V.shape)
+    b = rng.standard_normal(V.shape[1])
+    f = lambda VV: stream.forward(Q, K, VV, W, 1.0, causal)
+    np.testing.assert_allclose(f(2 * V - 3 * V2), 2 * f(V) - 3 * f(V2), atol=1e-12)
+    np.testing.assert_allclose(f(V + b), f(V) + b, atol=1e-12)
+    np.testing.assert_allclose(f(np.ones_like(V)), 1.0, atol=1e-13)
+
+
+def test_identical_keys_give_mean_and_running_mean():
+    Q, K, V, _, W = rand_case(8, 25, 8, 3, 2)
+    K[:] = K[0]
+    np.testing.assert_allclose(stream.forward(Q, K, V, W, 1.0, False),
+                               np.broadcast_to(V.mean(0), V.shape), atol=1e-12)
+    run = np.cumsum(V, 0) / np.arange(1, len(V) + 1)[:, None]
+    np.testing.assert_allclose(stream.forward(Q, K, V, W, 1.0, True), run, atol=1e-12)
+
+
+def test_noncausal_permutation_equivariance():
+    Q, K, V, _, W = rand_case(12, 30, 8, 2, 3)
+    rng = np.random.default_rng(2)
+    pk = rng.permutation(30)
+    pq = rng.permutation(30)
+    O = stream.forward(Q, K, V, W, 1.0, False)
+    np.testing.assert_allclose(stream.forward(Q, K[pk], V[pk], W, 1.0, False), O, atol=1e-13)
+    np.testing.assert_allclose(stream.forward(Q[pq], K, V, W, 1.0, False), O[pq], atol=1e-13)
+
+
+@settings(max_examples=25, deadline=None)
+@given(seed=st.integers(0, 10**6), N=st.integers(1, 20), P=st.integers(1, 4),
+       L=st.integers(1, 4), causal=st.booleans(), beta=st.floats(0.1, 5.0))
+def test_property_rows_are_convex_combinations(seed, N, P, L, causal, beta):
+    """Each output row is a convex combination of (visible) value rows, so it
+    lies inside their coordinate-wise bounds."""
+    Q, K, V, _, W = rand_case(seed, N, 6, P, L)
+    O = stream.forward(Q, K, V, W, beta, causal)
+    for i in range(N):
+        vis = V[: i + 1] if causal else V
+        assert np.all(O[i] <= vis.max(0) + 1e-12) and np.all(O[i] >= vis.min(0) - 1e-12)
+
+
+# --------------------------------------------------------------------------
+# backward: finite differences
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("P,L,beta", [(1, 1, 1.0), (2, 3, 0.6), (3, 2, 2.5)])
+def test_gradients_match_central_differences(causal, P, L, beta):
+    N, d = 9, 5
+    Q, K, V, dO, W = rand_case(100 + P * 3 + L, N, d, P, L)
+    dQ, dK, dV = stream.backward(Q, K, V, W, dO, beta, causal)
+    dQd, dKd, dVd = dense.backward(Q, K, V, W, dO, beta, causal)
+    for a, b in ((dQ, dQd), (dK, dKd), (dV, dVd)):
+        np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-13)
+
+    def loss(Qx, Kx, Vx):
+        return float(np.sum(stream.forward(Qx, Kx, Vx, W, beta, causal) * dO))
+
+    h = 1e-6
+    for which, grad in ((0, dQ), (1, dK), (2, dV)):
+        fd = np.zeros_like(grad)
+        for i in range(N):
+            for k in range(d):
+                args_p = [Q.copy(), K.copy(), V.copy()]
+                args_m = [Q.copy(), K.copy(), V.copy()]
+                args_p[which][i, k] += h
+                args_m[which][i, k] -= h
+                fd[i, k] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        rel = np.max(np.abs(fd - grad)) / np.max(np.abs(grad))
+        assert rel < 1e-6, (which, rel)
+
+
+def test_zero_upstream_gradient_gives_zero():
+    Q, K, V, dO, W = rand_case(5, 12, 6, 2, 2)
+    for g in stream.backward(Q, K, V, W, np.zeros_like(dO), 1.0, True):
+        assert np.all(g == 0)
+
+
+# --------------------------------------------------------------------------
+# streaming oracle: dtypes and sampling
+# --------------------------------------------------------------------------
+
+def test_stream_dtypes_and_sampling():
+    rng = np.random.default_rng(0)
+    N, d, P, L = 64, 16, 2, 3
+    Qb = synth.normal(1, 1, (2, N, d), "bf16")
+    Kb = synth.normal(1, 2, (2, N, d), "bf16")
+    Vb = synth.normal(1, 3, (2, N, d), "bf16")
+    W = rng.standard_normal((L, P, d))
+    up = synth.bf16_bits_to_f64
+    for causal in (False, True):
+        O = stream.forward(Qb, Kb, Vb, W, 1.0, causal)
+        O64 = stream.forward(up(Qb), up(Kb), up(Vb), W, 1.0, causal)
+        assert np.array_equal(O, O64)
+        smp = np.array([0, 3, 63])
+        np.testing.assert_array_equal(stream.forward(Qb, Kb, Vb, W, 1.0, causal, sample=smp),
+                                      O[:, smp])
+        ref0 = dense.forward(up(Qb[1]), up(Kb[1]), up(Vb[1]), W, 1.0, causal)
+        np.testing.assert_allclose(O[1], ref0, rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# input generator
+# --------------------------------------------------------------------------
+
+def test_philox_known_answers():
+    with open(os.path.join(GOLDEN, "philox_kat.json")) as f:
+        kat = json.load(f)
+    for v in kat["vectors"]:
+        ctr = [int(x, 16) for x in v["ctr"]]
+        key = [int(x, 16) for x in v["key"]]
+        assert synth.philox(ctr, key) == [int(x, 16) for x in v["out"]]
+
+
+def test_generator_moments_and_rounding():
+    x = synth.normal(7, 3, (400_000,), "f64")
+    assert abs(x.mean()) < 0.01 and abs(x.std() - 1) < 0.01
+    xf = synth.normal(7, 3, (1000,), "f32")
+    xb = synth.normal(7, 3, (1000,), "bf16")
+    np.testing.assert_array_equal(xf, x[:1000].astype(np.float32))
+    # bf16 = round-to-nearest-even of the float32 value
+    f32 = xf.view(np.uint32).astype(np.uint64)
+    rne = ((f32 + 0x7FFF + ((f32 >> 16) & 1)) >> 16).astype(np.uint16)
+    np.testing.assert_array_equal(xb, rne)
+    # chunked generation is position-exact
+    np.testing.assert_array_equal(synth.normal(7, 3, (10,), "f64", start=995), x[995:1005])
+
+
+def test_mixture_rows_are_unit_and_clustered():
+    X = synth.mixture(3, 1, 6, 2000, 64, "f64")
+    np.testing.assert_allclose(np.linalg.norm(X, axis=1), 1.0, atol=1e-12)
+    G = X @ X.T
+    hi = np.sort(G, axis=1)[:, -2]     # best match other than itself
+    assert np.median(hi) > 0.85
