@@ -1,0 +1,131 @@
+/*
+ * libraceattn — RACE Attention (soft-LSH sketch attention) on AMD MI355X (gfx950).
+ *
+ * The operation (arXiv 2510.04008, "RACE Attention: A Strictly Linear-Time
+ * Attention for Long-Sequence Training", as summarised on gist.science and
+ * fugumt.com):
+ *   - the similarity of a query and a key is a sharpened angular kernel of
+ *     their normalised dot product (Japanese gist.science page, section 2.1;
+ *     Italian page, Sommario tecnico section 2, Concetti Chiave 1);
+ *   - queries and keys are unit-normalised and projected on L tables of P
+ *     random hyperplanes, softened with tanh and assigned to the R = 2^P
+ *     hypercube corners by a softmax with temperature beta (Italian page,
+ *     section 2, Concetti Chiave 2; Korean page, 기술 요약 section 2;
+ *     Japanese page, section 2.2);
+ *   - keys accumulate per-bucket mass and value sums; each query reads its
+ *     own soft buckets and the output is the normalised weighted average over
+ *     the tables (Italian page, section 2, Algoritmo; Japanese page,
+ *     section 2.1);
+ *   - the causal variant restricts the sums to keys at or before the query
+ *     through prefix sums (Japanese page, section 2.2);
+ *   - the layer is trained end to end, so the library also returns the
+ *     gradients with respect to Q, K and V (Japanese page, section 2.2;
+ *     fugumt.com abstract: forward-backward pass).
+ *
+ * Per query i and table l (a = soft assignment, c_r = corner signs):
+ *   a_l(x) = softmax_r( beta * <c_r, tanh(W_l x / |x|)> )
+ *   O_i    = sum_l sum_r a_l(q_i)[r] S_l[r]  /  sum_l sum_r a_l(q_i)[r] z_l[r]
+ *   S_l[r] = sum_{j in scope(i)} a_l(k_j)[r] v_j,   z_l[r] = sum_{j in scope(i)} a_l(k_j)[r]
+ * scope(i) = all keys (non-causal) or keys j <= i (causal).
+ * Corner r has sign +1 on plane p when bit p of r is set. Hard-hash id of a
+ * table = sum_p [h_p > 0] 2^p.
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers unless stated otherwise; the caller
+ *     owns all memory; the library allocates nothing and keeps no mutable
+ *     global state (thread-safe; concurrent calls on different streams with
+ *     different buffers are independent).
+ *   - Q, K, V, O, dO, dQ, dK, dV: [B, H, N, d] contiguous row-major, element
+ *     type `dtype`. W: [L, P, d] contiguous, element type `dtype`, shared by
+ *     queries, keys, batches and heads; it is a fixed random projection and
+ *     receives no gradient.
+ *   - Every tensor pointer (and ws, saved) must be 16-byte aligned, else
+ *     RACE_ERR_INVALID_ARG.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *     default stream). Argument errors are reported synchronously, before any
+ *     device work is enqueued. Device faults surface at the caller's next
+ *     synchronisation.
+ *   - Supported: d = 64; 1 <= P <= 4; L >= 1 with L * P' <= 128 where P' is P
+ *     rounded up to a power of two; N >= 1; B, H >= 1; chunk >= 1; dtype
+ *     RACE_F32 or RACE_BF16. Other shapes return RACE_ERR_UNSUPPORTED.
+ *   - Numerics: bf16 inputs are multiplied on bf16 matrix cores with float32
+ *     accumulation; float32 inputs use float32 matrix cores throughout.
+ *     Sketch states and all reductions are float32. No atomics are used on
+ *     the attention path, so results are bitwise reproducible run to run.
+ *   - `chunk` is the number of tokens a workgroup owns; per-chunk sketch
+ *     states are published and prefix-scanned at that granularity. Results do
+ *     not depend on it beyond float32 rounding.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef RACE_ATTN_H
+#define RACE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RACE_OK = 0,
+    RACE_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, bad dtype, overflow */
+    RACE_ERR_UNSUPPORTED = 2,   /* valid but outside the supported shape set */
+    RACE_ERR_WORKSPACE = 3,     /* ws_bytes smaller than required */
+    RACE_ERR_HIP = 4            /* a HIP launch or query failed */
+} race_status_t;
+
+typedef enum { RACE_F32 = 0, RACE_BF16 = 1 } race_dtype_t;
+
+/* Bytes of device workspace `ws` needed by race_attn_fwd (for_backward = 0)
+ * or race_attn_bwd (for_backward = 1) for this shape. Writes *bytes.
+ * Depends on dtype only through the element size of a small projection
+ * table, so the value for RACE_F32 is an upper bound for both. */
+race_status_t race_attn_workspace_bytes(int64_t B, int64_t H, int64_t N, int d, int P, int L,
+                                        int causal, int chunk, int for_backward, size_t *bytes);
+
+/* Bytes of the optional `saved` buffer: the float32 sketch state at the start
+ * of every chunk (causal) or the whole-sequence sketch (non-causal), per
+ * (batch, head). Layout is private to the library; pass the same buffer and
+ * the same shape arguments to race_attn_bwd to skip recomputing it. */
+race_status_t race_attn_saved_bytes(int64_t B, int64_t H, int64_t N, int d, int P, int L,
+                                    int causal, int chunk, size_t *bytes);
+
+/* Forward: O = RACE-Attention(Q, K, V; W, P, L, temperature, causal).
+ * `temperature` is the pages' beta: it multiplies the corner logits, so a
+ * larger value gives harder bucket assignments. `saved` may be NULL; if not
+ * NULL it receives the per-chunk sketch states (race_attn_saved_bytes).
+ * `ws` must hold race_attn_workspace_bytes(..., for_backward = 0). */
+race_status_t race_attn_fwd(const void *Q, const void *K, const void *V, const void *W,
+                            int64_t B, int64_t H, int64_t N, int d, int P, int L,
+                            float temperature, int causal, int chunk, race_dtype_t dtype,
+                            void *O, void *saved, void *ws, size_t ws_bytes, void *stream);
+
+/* Backward: given dO = dLoss/dO, writes dQ, dK, dV (the exact gradients of
+ * the forward above). `saved` may be NULL (states are recomputed) or the
+ * buffer a forward call with identical arguments filled. The forward output
+ * O is not needed: it is recomputed from the sketch states.
+ * `ws` must hold race_attn_workspace_bytes(..., for_backward = 1). */
+race_status_t race_attn_bwd(const void *Q, const void *K, const void *V, const void *W,
+                            const void *dO, const void *saved, int64_t B, int64_t H,
+                            int64_t N, int d, int P, int L, float temperature, int causal,
+                            int chunk, race_dtype_t dtype, void *dQ, void *dK, void *dV,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/* Hard-hash diagnostic (the beta -> infinity limit of the soft assignment):
+ * bucket_ids[row, l] = sum_p [<W_lp, x_row / |x_row|> > 0] 2^p for the
+ * rows of X ([B, H, N, d], dtype), written as int32 [B, H, N, L].
+ * *near_zero (a device counter, added to, not reset) receives the number of
+ * projections with |<W_lp, x/|x|>| < 1e-5, whose sign is not reliable. */
+race_status_t race_attn_hash(const void *X, const void *W, int64_t B, int64_t H, int64_t N,
+                             int d, int P, int L, race_dtype_t dtype, int32_t *bucket_ids,
+                             unsigned long long *near_zero, void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *race_attn_status_string(race_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RACE_ATTN_H */

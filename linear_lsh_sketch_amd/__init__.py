@@ -1,0 +1,180 @@
+"""Python binding of libraceattn (RACE Attention on MI355X).
+
+Argument marshalling only: every step of the attention path runs in the HIP
+kernels of ``libraceattn.so``; PyTorch provides device memory and the stream.
+The names mirror the C ABI in ``include/race_attn.h``.  There is no CPU
+fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libraceattn.so")
+
+RACE_OK, RACE_ERR_INVALID_ARG, RACE_ERR_UNSUPPORTED, RACE_ERR_WORKSPACE, RACE_ERR_HIP = range(5)
+RACE_F32, RACE_BF16 = 0, 1
+
+SYMBOLS = ("race_attn_workspace_bytes", "race_attn_saved_bytes", "race_attn_fwd",
+           "race_attn_bwd", "race_attn_hash", "race_attn_status_string")
+
+
+class RaceError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {status_string(code)} ({code})")
+
+
+_lib = None
+
+
+def lib():
+    """Load libraceattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libraceattn.so not built at {LIB_PATH}; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+        fl = ctypes.c_float
+        L.race_attn_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, i32,
+                                                ctypes.POINTER(sz)]
+        L.race_attn_saved_bytes.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+        L.race_attn_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, fl, i32, i32, i32,
+                                    vp, vp, vp, sz, vp]
+        L.race_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, fl, i32, i32,
+                                    i32, vp, vp, vp, vp, sz, vp]
+        L.race_attn_hash.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, i32, vp, vp, vp]
+        L.race_attn_status_string.argtypes = [i32]
+        L.race_attn_status_string.restype = ctypes.c_char_p
+        for name in SYMBOLS[:-1]:
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().race_attn_status_string(int(code)).decode()
+
+
+def _check(code: int, where: str):
+    if code != RACE_OK:
+        raise RaceError(code, where)
+
+
+def workspace_bytes(B, H, N, d, P, L, causal, chunk, for_backward) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().race_attn_workspace_bytes(B, H, N, d, P, L, int(bool(causal)), chunk,
+                                           int(bool(for_backward)), ctypes.byref(out)),
+           "race_attn_workspace_bytes")
+    return out.value
+
+
+def saved_bytes(B, H, N, d, P, L, causal, chunk) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().race_attn_saved_bytes(B, H, N, d, P, L, int(bool(causal)), chunk, ctypes.byref(out)),
+           "race_attn_saved_bytes")
+    return out.value
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return RACE_F32
+    if t.dtype == torch.bfloat16:
+        return RACE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check_inputs(*ts):
+    dt = ts[0].dtype
+    dev = ts[0].device
+    for t in ts:
+        if not t.is_cuda or t.device != dev:
+            raise ValueError("all tensors must be on the same GPU")
+        if t.dtype != dt:
+            raise ValueError("all tensors must share one dtype")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def alloc_workspace(B, H, N, P, L, causal, chunk, for_backward, device):
+    import torch
+    n = workspace_bytes(B, H, N, 64, P, L, causal, chunk, for_backward)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def alloc_saved(B, H, N, P, L, causal, chunk, device):
+    import torch
+    n = saved_bytes(B, H, N, 64, P, L, causal, chunk)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def race_attn_fwd(Q, K, V, W, P, L, temperature=1.0, causal=False, chunk=1024, out=None,
+                  saved=None, ws=None, stream=None):
+    """O = RACE attention of Q, K, V ([B, H, N, d]) with hyperplanes W ([L, P, d])."""
+    import torch
+    _check_inputs(Q, K, V, W)
+    B, H, N, d = Q.shape
+    if tuple(W.shape) != (L, P, d):
+        raise ValueError(f"W must be [L, P, d] = {(L, P, d)}, got {tuple(W.shape)}")
+    if K.shape != Q.shape or V.shape != Q.shape:
+        raise ValueError("Q, K, V must share one shape")
+    O = out if out is not None else torch.empty_like(Q)
+    if ws is None:
+        ws = alloc_workspace(B, H, N, P, L, causal, chunk, False, Q.device)
+    code = lib().race_attn_fwd(_p(Q), _p(K), _p(V), _p(W), B, H, N, d, P, L, float(temperature),
+                               int(bool(causal)), chunk, _dtype_code(Q), _p(O), _p(saved), _p(ws),
+                               ws.numel(), _stream(stream))
+    _check(code, "race_attn_fwd")
+    return O
+
+
+def race_attn_bwd(Q, K, V, W, dO, P, L, temperature=1.0, causal=False, chunk=1024, saved=None,
+                  ws=None, grads=None, stream=None):
+    """(dQ, dK, dV) of <dO, RACE-attention(Q, K, V)>."""
+    import torch
+    _check_inputs(Q, K, V, W, dO)
+    B, H, N, d = Q.shape
+    if tuple(W.shape) != (L, P, d):
+        raise ValueError(f"W must be [L, P, d] = {(L, P, d)}, got {tuple(W.shape)}")
+    if grads is None:
+        grads = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V))
+    dQ, dK, dV = grads
+    if ws is None:
+        ws = alloc_workspace(B, H, N, P, L, causal, chunk, True, Q.device)
+    code = lib().race_attn_bwd(_p(Q), _p(K), _p(V), _p(W), _p(dO), _p(saved), B, H, N, d, P, L,
+                               float(temperature), int(bool(causal)), chunk, _dtype_code(Q), _p(dQ),
+                               _p(dK), _p(dV), _p(ws), ws.numel(), _stream(stream))
+    _check(code, "race_attn_bwd")
+    return dQ, dK, dV
+
+
+def race_attn_hash(X, W, P, L, stream=None):
+    """Hard bucket ids [B, H, N, L] (int32) and the near-zero projection count."""
+    import torch
+    _check_inputs(X, W)
+    B, H, N, d = X.shape
+    ids = torch.empty((B, H, N, L), dtype=torch.int32, device=X.device)
+    nz = torch.zeros(1, dtype=torch.int64, device=X.device)
+    code = lib().race_attn_hash(_p(X), _p(W), B, H, N, d, P, L, _dtype_code(X), _p(ids), _p(nz),
+                                _stream(stream))
+    _check(code, "race_attn_hash")
+    return ids, nz
+
+
+# short aliases
+forward = race_attn_fwd
+backward = race_attn_bwd
+hard_hash = race_attn_hash

@@ -1,0 +1,133 @@
+// C-ABI entry points of libraceattn: argument validation, workspace sizing and
+// dispatch to the bf16 / float32 launch sequences. No C++ exception escapes.
+#include <cmath>
+#include <cstdint>
+#include <initializer_list>
+
+#include "race_attn.h"
+#include "race_dispatch.hpp"
+
+using namespace race;
+
+namespace {
+
+race_status_t prepare(int64_t B, int64_t H, int64_t N, int d, int P, int L, int causal, int chunk,
+                      Shape& s, Derived& dv) {
+    s.B = B; s.H = H; s.N = N; s.d = d; s.P = P; s.L = L; s.causal = causal ? 1 : 0; s.chunk = chunk;
+    return derive(s, dv);
+}
+
+bool dtype_ok(race_dtype_t t) { return t == RACE_F32 || t == RACE_BF16; }
+
+// Vector loads and stores of 16 bytes need 16-byte aligned tensors.
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool all_aligned(std::initializer_list<const void*> ps) {
+    for (const void* p : ps)
+        if (!aligned(p)) return false;
+    return true;
+}
+
+race_status_t guarded(race_status_t (*fn)(const Shape&, const Derived&, const WsLayout&, const Call&),
+                      const Shape& s, const Derived& dv, const WsLayout& wl, const Call& c) {
+    try {
+        return fn(s, dv, wl, c);
+    } catch (...) {
+        return RACE_ERR_HIP;
+    }
+}
+
+race_status_t go(race_dtype_t dtype, const Shape& s, const Derived& dv, const WsLayout& wl, const Call& c) {
+    (void)hipGetLastError();  // clear a stale error so it is not reported as ours
+    return dtype == RACE_F32 ? guarded(dispatch<true>, s, dv, wl, c) : guarded(dispatch<false>, s, dv, wl, c);
+}
+
+}  // namespace
+
+extern "C" {
+
+race_status_t race_attn_workspace_bytes(int64_t B, int64_t H, int64_t N, int d, int P, int L, int causal,
+                                        int chunk, int for_backward, size_t* bytes) {
+    if (!bytes) return RACE_ERR_INVALID_ARG;
+    Shape s;
+    Derived dv;
+    race_status_t rc = prepare(B, H, N, d, P, L, causal, chunk, s, dv);
+    if (rc != RACE_OK) return rc;
+    *bytes = ws_layout(s, dv, for_backward ? 1 : 0).total;
+    return RACE_OK;
+}
+
+race_status_t race_attn_saved_bytes(int64_t B, int64_t H, int64_t N, int d, int P, int L, int causal,
+                                    int chunk, size_t* bytes) {
+    if (!bytes) return RACE_ERR_INVALID_ARG;
+    Shape s;
+    Derived dv;
+    race_status_t rc = prepare(B, H, N, d, P, L, causal, chunk, s, dv);
+    if (rc != RACE_OK) return rc;
+    *bytes = saved_bytes(s, dv);
+    return RACE_OK;
+}
+
+race_status_t race_attn_fwd(const void* Q, const void* K, const void* V, const void* W, int64_t B, int64_t H,
+                            int64_t N, int d, int P, int L, float temperature, int causal, int chunk,
+                            race_dtype_t dtype, void* O, void* saved, void* ws, size_t ws_bytes, void* stream) {
+    if (!Q || !K || !V || !W || !O || !ws || !dtype_ok(dtype) || !std::isfinite(temperature) ||
+        !all_aligned({Q, K, V, W, O, ws, saved}))
+        return RACE_ERR_INVALID_ARG;
+    Shape s;
+    Derived dv;
+    race_status_t rc = prepare(B, H, N, d, P, L, causal, chunk, s, dv);
+    if (rc != RACE_OK) return rc;
+    const WsLayout wl = ws_layout(s, dv, 0);
+    if (ws_bytes < wl.total) return RACE_ERR_WORKSPACE;
+    Call c{};
+    c.op = OP_FWD; c.Q = Q; c.K = K; c.V = V; c.W = W; c.saved_out = saved; c.beta = temperature; c.O = O;
+    c.ws = ws; c.stream = reinterpret_cast<hipStream_t>(stream);
+    return go(dtype, s, dv, wl, c);
+}
+
+race_status_t race_attn_bwd(const void* Q, const void* K, const void* V, const void* W, const void* dO,
+                            const void* saved, int64_t B, int64_t H, int64_t N, int d, int P, int L,
+                            float temperature, int causal, int chunk, race_dtype_t dtype, void* dQ, void* dK,
+                            void* dV, void* ws, size_t ws_bytes, void* stream) {
+    if (!Q || !K || !V || !W || !dO || !dQ || !dK || !dV || !ws || !dtype_ok(dtype) ||
+        !std::isfinite(temperature) || !all_aligned({Q, K, V, W, dO, saved, dQ, dK, dV, ws}))
+        return RACE_ERR_INVALID_ARG;
+    Shape s;
+    Derived dv;
+    race_status_t rc = prepare(B, H, N, d, P, L, causal, chunk, s, dv);
+    if (rc != RACE_OK) return rc;
+    const WsLayout wl = ws_layout(s, dv, 1);
+    if (ws_bytes < wl.total) return RACE_ERR_WORKSPACE;
+    Call c{};
+    c.op = OP_BWD; c.Q = Q; c.K = K; c.V = V; c.W = W; c.dO = dO; c.saved_in = saved; c.beta = temperature;
+    c.dQ = dQ; c.dK = dK; c.dV = dV; c.ws = ws; c.stream = reinterpret_cast<hipStream_t>(stream);
+    return go(dtype, s, dv, wl, c);
+}
+
+race_status_t race_attn_hash(const void* X, const void* W, int64_t B, int64_t H, int64_t N, int d, int P, int L,
+                             race_dtype_t dtype, int32_t* bucket_ids, unsigned long long* near_zero,
+                             void* stream) {
+    if (!X || !W || !bucket_ids || !near_zero || !dtype_ok(dtype) || !all_aligned({X, W}))
+        return RACE_ERR_INVALID_ARG;
+    Shape s;
+    Derived dv;
+    race_status_t rc = prepare(B, H, N, d, P, L, 0, 1, s, dv);
+    if (rc != RACE_OK) return rc;
+    Call c{};
+    c.op = OP_HASH; c.X = X; c.W = W; c.ids = bucket_ids; c.near_zero = near_zero;
+    c.stream = reinterpret_cast<hipStream_t>(stream);
+    return go(dtype, s, dv, WsLayout{}, c);
+}
+
+const char* race_attn_status_string(race_status_t status) {
+    switch (status) {
+        case RACE_OK: return "RACE_OK";
+        case RACE_ERR_INVALID_ARG: return "RACE_ERR_INVALID_ARG";
+        case RACE_ERR_UNSUPPORTED: return "RACE_ERR_UNSUPPORTED";
+        case RACE_ERR_WORKSPACE: return "RACE_ERR_WORKSPACE";
+        case RACE_ERR_HIP: return "RACE_ERR_HIP";
+    }
+    return "RACE_ERR_UNKNOWN";
+}
+
+}  // extern "C"

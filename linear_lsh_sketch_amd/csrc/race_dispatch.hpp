@@ -1,0 +1,155 @@
+// Launch sequences for the forward, backward and hash entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "race_host.hpp"
+#include "race_kernels.hpp"
+
+namespace race {
+
+enum { OP_FWD = 0, OP_BWD = 1, OP_HASH = 2 };
+
+struct Call {
+    int op;
+    const void *Q, *K, *V, *W, *dO;
+    const void* saved_in;   // backward: states from a forward call (may be null)
+    void* saved_out;        // forward: where to keep the states (may be null)
+    float beta;
+    void *O, *dQ, *dK, *dV;
+    void* ws;
+    hipStream_t stream;
+    const void* X;                 // hash
+    int32_t* ids;                  // hash
+    unsigned long long* near_zero; // hash
+};
+
+template <bool F32>
+race_status_t dispatch(const Shape& s, const Derived& d, const WsLayout& wl, const Call& c);
+
+inline race_status_t launch_ok() {
+    return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
+}
+
+#define RACE_TRY(x)                          \
+    do {                                     \
+        race_status_t rc_ = (x);             \
+        if (rc_ != RACE_OK) return rc_;      \
+    } while (0)
+
+template <class C>
+race_status_t run_totals(const Shape& s, const Derived& d, const void* Xb, const void* Z, const float* Dv,
+                         const float* Ev, int kind, const void* W, float beta, float* out, hipStream_t st) {
+    TotArgs a;
+    a.Xb = Xb; a.Z = Z; a.Dv = Dv; a.Ev = Ev; a.W = W; a.out = out;
+    a.N = s.N; a.chunk = s.chunk; a.nchunks = (int)d.NC; a.L = s.L; a.beta = beta; a.kind = kind;
+    hipLaunchKernelGGL(k_totals<C>, dim3((unsigned)d.NC, (unsigned)d.BH), dim3(NT), 0, st, a);
+    return launch_ok();
+}
+
+template <int KIND>
+race_status_t run_scan(const Derived& d, float* states, float* total, hipStream_t st) {
+    const int elems = (int)d.F65;
+    hipLaunchKernelGGL(k_scan<KIND>, dim3((unsigned)((elems + 255) / 256), (unsigned)d.BH), dim3(256), 0, st,
+                       states, total, (int)d.NC, elems);
+    return launch_ok();
+}
+
+template <class C, int MODE>
+race_status_t run_pass(const Shape& s, const Derived& d, PassArgs a, hipStream_t st) {
+    a.N = s.N; a.chunk = s.chunk; a.L = s.L; a.causal = s.causal;
+    hipLaunchKernelGGL((k_pass<C, MODE>), dim3((unsigned)d.NC, (unsigned)d.BH), dim3(NT), 0, st, a);
+    return launch_ok();
+}
+
+template <class C>
+race_status_t run(const Shape& s, const Derived& d, const WsLayout& wl, const Call& c) {
+    char* ws = reinterpret_cast<char*>(c.ws);
+    hipStream_t st = c.stream;
+    if (c.op == OP_HASH) {
+        const int64_t rows = d.BH * s.N;
+        const int64_t blocks = (rows + 63) / 64;
+        if (blocks > 0x7fffffff) return RACE_ERR_UNSUPPORTED;
+        hipLaunchKernelGGL(k_hash<C>, dim3((unsigned)blocks), dim3(NT), 0, st, c.X, c.W, rows, s.L, c.ids,
+                           c.near_zero);
+        return launch_ok();
+    }
+    const int64_t chunk_stride = d.F65;
+    const int64_t bh_stride = d.NC * d.F65;
+    if (c.op == OP_FWD) {
+        float* Sb = (s.causal && c.saved_out) ? reinterpret_cast<float*>(c.saved_out)
+                                              : reinterpret_cast<float*>(ws + wl.S);
+        RACE_TRY(run_totals<C>(s, d, c.K, c.V, nullptr, nullptr, 0, c.W, c.beta, Sb, st));
+        PassArgs a{};
+        a.Xa = c.Q; a.Xb = c.K; a.Zsrc = c.V; a.Ysrc = nullptr; a.W = c.W; a.WTp = nullptr;
+        a.beta = c.beta; a.Dv = nullptr; a.Ev = nullptr; a.out0 = c.O; a.out1 = nullptr;
+        if (s.causal) {
+            RACE_TRY(run_scan<SCAN_EXCL>(d, Sb, nullptr, st));
+            a.state = Sb; a.state_bh_stride = bh_stride; a.state_chunk_stride = chunk_stride;
+        } else {
+            float* St = c.saved_out ? reinterpret_cast<float*>(c.saved_out) : reinterpret_cast<float*>(ws + wl.St);
+            RACE_TRY(run_scan<SCAN_TOTAL>(d, Sb, St, st));
+            a.state = St; a.state_bh_stride = d.F65; a.state_chunk_stride = 0;
+        }
+        return run_pass<C, MODE_FWD>(s, d, a, st);
+    }
+    // backward
+    using elem = typename Prec<C::F32>::elem;
+    elem* WTp = reinterpret_cast<elem*>(ws + wl.wt);
+    hipLaunchKernelGGL(k_prep<C>, dim3(8), dim3(256), 0, st, reinterpret_cast<const elem*>(c.W), s.L, WTp);
+    RACE_TRY(launch_ok());
+    float* Dv = reinterpret_cast<float*>(ws + wl.D);
+    float* Ev = reinterpret_cast<float*>(ws + wl.E);
+    PassArgs q{};
+    q.Xa = c.Q; q.Xb = c.K; q.Zsrc = c.V; q.Ysrc = c.dO; q.W = c.W; q.WTp = WTp; q.beta = c.beta;
+    q.Dv = Dv; q.Ev = Ev; q.out0 = c.dQ; q.out1 = nullptr;
+    if (s.causal) {
+        const float* Sb = reinterpret_cast<const float*>(c.saved_in);
+        if (!Sb) {
+            float* Sw = reinterpret_cast<float*>(ws + wl.S);
+            RACE_TRY(run_totals<C>(s, d, c.K, c.V, nullptr, nullptr, 0, c.W, c.beta, Sw, st));
+            RACE_TRY(run_scan<SCAN_EXCL>(d, Sw, nullptr, st));
+            Sb = Sw;
+        }
+        q.state = Sb; q.state_bh_stride = bh_stride; q.state_chunk_stride = chunk_stride;
+    } else {
+        const float* St = reinterpret_cast<const float*>(c.saved_in);
+        if (!St) {
+            float* Sw = reinterpret_cast<float*>(ws + wl.S);
+            float* Stw = reinterpret_cast<float*>(ws + wl.St);
+            RACE_TRY(run_totals<C>(s, d, c.K, c.V, nullptr, nullptr, 0, c.W, c.beta, Sw, st));
+            RACE_TRY(run_scan<SCAN_TOTAL>(d, Sw, Stw, st));
+            St = Stw;
+        }
+        q.state = St; q.state_bh_stride = d.F65; q.state_chunk_stride = 0;
+    }
+    RACE_TRY((run_pass<C, MODE_BWD_Q>(s, d, q, st)));
+    float* Tw = reinterpret_cast<float*>(ws + wl.T);
+    RACE_TRY(run_totals<C>(s, d, c.Q, c.dO, Dv, Ev, 1, c.W, c.beta, Tw, st));
+    PassArgs k{};
+    k.Xa = c.K; k.Xb = c.Q; k.Zsrc = c.dO; k.Ysrc = c.V; k.W = c.W; k.WTp = WTp; k.beta = c.beta;
+    k.Dv = Dv; k.Ev = Ev; k.out0 = c.dK; k.out1 = c.dV;
+    if (s.causal) {
+        RACE_TRY(run_scan<SCAN_REV_EXCL>(d, Tw, nullptr, st));
+        k.state = Tw; k.state_bh_stride = bh_stride; k.state_chunk_stride = chunk_stride;
+    } else {
+        float* Ttw = reinterpret_cast<float*>(ws + wl.Tt);
+        RACE_TRY(run_scan<SCAN_TOTAL>(d, Tw, Ttw, st));
+        k.state = Ttw; k.state_bh_stride = d.F65; k.state_chunk_stride = 0;
+    }
+    return run_pass<C, MODE_BWD_K>(s, d, k, st);
+}
+
+#define RACE_CASE(P_, MT_)                                                   \
+    if (s.P == P_ && d.MT == MT_) return run<Cfg<P_, MT_, F32>>(s, d, wl, c);
+
+template <bool F32>
+race_status_t dispatch(const Shape& s, const Derived& d, const WsLayout& wl, const Call& c) {
+    RACE_CASE(1, 1) RACE_CASE(1, 2) RACE_CASE(1, 4) RACE_CASE(1, 8)
+    RACE_CASE(2, 1) RACE_CASE(2, 2) RACE_CASE(2, 4) RACE_CASE(2, 8)
+    RACE_CASE(3, 1) RACE_CASE(3, 2) RACE_CASE(3, 4) RACE_CASE(3, 8)
+    RACE_CASE(4, 1) RACE_CASE(4, 2) RACE_CASE(4, 4) RACE_CASE(4, 8)
+    return RACE_ERR_UNSUPPORTED;
+}
+
+}  // namespace race

@@ -1,0 +1,95 @@
+// Host-side shape validation and workspace layout (no device code).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <cmath>
+
+#include "race_attn.h"
+
+namespace race {
+
+struct Shape {
+    int64_t B, H, N;
+    int d, P, L;
+    int causal, chunk;
+};
+
+struct Derived {
+    int Pp, MT, KB, F, NPAIR;
+    int64_t BH, NC;
+    int64_t F65;   // floats per sketch state: F * 64 value sums + F masses
+};
+
+struct WsLayout {
+    size_t wt;     // back-projection operand table
+    size_t S;      // per-chunk sketch states (or chunk totals, non-causal)
+    size_t St;     // non-causal: whole-sequence sketch
+    size_t T;      // backward: per-chunk gradient sketch states
+    size_t Tt;     // backward non-causal: whole-sequence gradient sketch
+    size_t D;      // backward: per-token denominators
+    size_t E;      // backward: per-token e = -<dO, O>/D
+    size_t total;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+inline bool mul_ok(int64_t a, int64_t b, int64_t& out) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > INT64_MAX / a) return false;
+    out = a * b;
+    return true;
+}
+
+inline race_status_t derive(const Shape& s, Derived& d) {
+    if (s.B < 1 || s.H < 1 || s.N < 1 || s.d < 1 || s.P < 1 || s.L < 1 || s.chunk < 1)
+        return RACE_ERR_INVALID_ARG;
+    if (s.d != 64 || s.P > 4) return RACE_ERR_UNSUPPORTED;
+    d.Pp = (s.P == 3) ? 4 : s.P;
+    const int64_t rows = (int64_t)s.L * d.Pp;
+    if (rows > 128) return RACE_ERR_UNSUPPORTED;
+    int mt = (int)((rows + 15) / 16);
+    int p2 = 1;
+    while (p2 < mt) p2 <<= 1;
+    d.MT = p2;
+    d.KB = (s.P == 4) ? 2 : 1;
+    d.F = 32 * d.MT * d.KB;
+    d.NPAIR = (d.MT + 1) / 2;
+    int64_t bh, elems;
+    if (!mul_ok(s.B, s.H, bh) || !mul_ok(bh, s.N, elems) || !mul_ok(elems, s.d, elems))
+        return RACE_ERR_INVALID_ARG;
+    if (elems > INT64_MAX / 8) return RACE_ERR_INVALID_ARG;
+    d.BH = bh;
+    d.NC = (s.N + s.chunk - 1) / s.chunk;
+    d.F65 = (int64_t)d.F * 65;
+    if (d.BH > 65535 || d.NC > 0x7fffffff) return RACE_ERR_UNSUPPORTED;
+    return RACE_OK;
+}
+
+// Sizes of the optional saved buffer: per-chunk states (causal) or the total.
+inline size_t saved_bytes(const Shape& s, const Derived& d) {
+    const size_t per = (size_t)d.F65 * sizeof(float);
+    return s.causal ? (size_t)d.BH * (size_t)d.NC * per : (size_t)d.BH * per;
+}
+
+inline WsLayout ws_layout(const Shape& s, const Derived& d, int for_backward) {
+    WsLayout w{};
+    const size_t per = (size_t)d.F65 * sizeof(float);
+    const size_t chunks = (size_t)d.BH * (size_t)d.NC * per;
+    const size_t totals = (size_t)d.BH * per;
+    size_t off = 0;
+    w.wt = off;  off = align256(off + (size_t)d.NPAIR * 4 * 64 * 8 * sizeof(float));
+    w.S = off;   off = align256(off + chunks);
+    w.St = off;  off = align256(off + (s.causal ? 0 : totals));
+    if (for_backward) {
+        w.T = off;   off = align256(off + chunks);
+        w.Tt = off;  off = align256(off + (s.causal ? 0 : totals));
+        w.D = off;   off = align256(off + (size_t)d.BH * (size_t)s.N * sizeof(float));
+        w.E = off;   off = align256(off + (size_t)d.BH * (size_t)s.N * sizeof(float));
+    }
+    w.total = off;
+    return w;
+}
+
+}  // namespace race

@@ -1,0 +1,939 @@
+// RACE Attention kernels for gfx950.
+//
+// Method (arXiv 2510.04008 summaries): unit-normalise q and k, project on L
+// tables of P Gaussian hyperplanes, soften with tanh, softmax over the 2^P
+// hypercube corners (Italian gist.science page, Sommario tecnico section 2;
+// Korean page, 기술 요약 section 2); keys add mass and value sums per bucket;
+// queries read their own buckets; causal mode uses prefix sums (Japanese
+// page, sections 2.1 and 2.2). The corner softmax is evaluated as the product
+// of per-plane sigmoids sigmoid(2 beta c_p tanh h_p), which equals it exactly
+// because the corner logit is a sum of per-plane terms.
+//
+// Decomposition (per (batch, head), the sequence cut into chunks of `chunk`
+// tokens, one workgroup per chunk, sub-blocks of 64 tokens inside a chunk):
+//   k_totals  : per-chunk sketch  M_c = sum_{b in c} phi(x_b)^T [z_b | m_b]
+//   k_scan    : exclusive prefix (causal), reverse exclusive prefix (backward
+//               key side) or total (non-causal) over chunks
+//   k_pass    : per sub-block readout against the running sketch plus the
+//               intra-sub-block causal term, then the sketch update; in the
+//               backward modes also the gradient wrt the readout-side features,
+//               the corner-softmax chain rule and the back-projection.
+// Roles in k_pass:
+//   FWD   : a = queries, b = keys,    z_b = [v | 1]          -> O
+//   BWD_Q : a = queries, b = keys,    z_b = [v | 1], y_a = [dO/D | e] -> dQ, D, e
+//   BWD_K : a = keys,    b = queries, z_b = [dO/D | e], y_a = [v | 1] -> dK, dV
+// with e = -<dO, O>/D. The sketch M = sum_b phi_b^T z_b is held in float32
+// accumulators, split by value columns over the four waves (wave w owns
+// columns 16w..16w+15; the mass column is split by feature chunk).
+#pragma once
+
+#include <type_traits>
+
+#include "race_device.hpp"
+
+namespace race {
+
+enum { MODE_FWD = 0, MODE_BWD_Q = 1, MODE_BWD_K = 2 };
+enum { SCAN_EXCL = 0, SCAN_REV_EXCL = 1, SCAN_TOTAL = 2 };
+
+// ---------------------------------------------------------------------------
+// Back-projection operand table: W'^T in the paired-tile K order (row 4g+j
+// of tile 2m for j < 4, row 4g+j-4 of tile 2m+1 otherwise).
+// ---------------------------------------------------------------------------
+template <class C>
+__global__ void k_prep(const typename Prec<C::F32>::elem* __restrict__ W, int L,
+                       typename Prec<C::F32>::elem* __restrict__ WTp) {
+    using elem = typename Prec<C::F32>::elem;
+    const int n2 = C::NPAIR * 4 * 64 * 8;
+    for (int k = blockIdx.x * blockDim.x + threadIdx.x; k < n2; k += gridDim.x * blockDim.x) {
+        elem v = to_elem<C::F32>(0.f);
+        const int m = k / 2048, dt = (k / 512) & 3, l = (k / 8) & 63, j = k & 7;
+        const int d = 16 * dt + (l & 15);
+        const int tile = 2 * m + (j >> 2);
+        const int ri = 4 * (l >> 4) + (j & 3);
+        if (tile < C::MT) {
+            int table, plane;
+            row_table<C>(tile, ri, table, plane);
+            if (table < L && plane < C::P) v = W[((size_t)table * C::P + plane) * DH + d];
+        }
+        WTp[k] = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// shared pieces
+// ---------------------------------------------------------------------------
+template <bool F32>
+struct In {
+    using T = typename std::conditional<F32, float, __bf16>::type;
+};
+
+// Load 16 consecutive input values (cols c0..c0+15 of a [*, 64] row) as float.
+template <bool F32>
+__device__ inline void load16(const void* base, size_t off, float v[16]) {
+    if constexpr (F32) {
+        const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float4 x = p[q];
+            v[4 * q] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
+        }
+    } else {
+        const bf16x8* p = reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(base) + off);
+        bf16x8 a = p[0], b = p[1];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { v[j] = (float)a[j]; v[8 + j] = (float)b[j]; }
+    }
+}
+
+// Projection operand of one token row: K positions 32 s + 8 g .. +7 for s = 0, 1;
+// also returns 1 / max(|x|, eps) (identical in the four lane groups).
+template <bool F32>
+__device__ inline void load_x(const void* X, size_t row, bool valid, int g,
+                              typename Prec<F32>::frag xf[2], float& inv, float& nrm) {
+    float ss = 0.f;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        if constexpr (F32) {
+            f32x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (valid) v = *reinterpret_cast<const f32x8*>(reinterpret_cast<const float*>(X) + row * DH + 32 * s + 8 * g);
+            xf[s] = v;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ss += v[j] * v[j];
+        } else {
+            bf16x8 v = zero_frag<false>();
+            if (valid) v = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(X) + row * DH + 32 * s + 8 * g);
+            xf[s] = v;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) { const float f = (float)v[j]; ss += f * f; }
+        }
+    }
+    ss = sum_groups(ss);
+    nrm = sqrtf(ss);
+    inv = 1.f / fmaxf(nrm, NORM_EPS);
+}
+
+template <class C>
+__device__ inline f32x4 project(const typename Prec<C::F32>::elem* __restrict__ W, int L, int t, int ln,
+                                int g, const typename Prec<C::F32>::frag xf[2]) {
+    int table, plane;
+    row_table<C>(t, ln, table, plane);
+    const bool ok = table < L && plane < C::P;
+    const typename Prec<C::F32>::elem* wr = W + ((size_t)(ok ? table * C::P + plane : 0)) * DH + 8 * g;
+    typename Prec<C::F32>::frag wf[2] = {zero_frag<C::F32>(), zero_frag<C::F32>()};
+    if (ok) {
+        wf[0] = ld_frag<C::F32>(wr);
+        wf[1] = ld_frag<C::F32>(wr + 32);
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = mma(wf[0], xf[0], acc);
+    acc = mma(wf[1], xf[1], acc);
+    return acc;
+}
+
+// Fill the transposed value tile ZT [80][ROWT] (and optionally the row tile
+// Zrow [64][ROWE]) for tokens row0 .. row0+63 (nv valid):
+//   kind 0: z = [x | 1]; kind 1: z = [x / D | e] with D, e per token.
+template <class C>
+__device__ inline void load_aug(const void* X, const float* __restrict__ Dv, const float* __restrict__ Ev,
+                                int kind, size_t row0, int nv, typename Prec<C::F32>::elem* ZT,
+                                typename Prec<C::F32>::elem* Zrow) {
+    using elem = typename Prec<C::F32>::elem;
+    const int th = threadIdx.x, r = th >> 2, q = th & 3;
+    const bool ok = r < nv;
+    float v[16];
+    float mass = 0.f;
+    if (ok) {
+        load16<C::F32>(X, (row0 + r) * DH + 16 * q, v);
+        if (kind == 0) {
+            mass = 1.f;
+        } else {
+            const float invD = 1.f / Dv[row0 + r];
+#pragma unroll
+            for (int c = 0; c < 16; ++c) v[c] *= invD;
+            mass = Ev[row0 + r];
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) v[c] = 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < 16; ++c) ZT[(16 * q + c) * C::ROWT + r] = to_elem<C::F32>(v[c]);
+    if (q == 0) {
+        ZT[64 * C::ROWT + r] = to_elem<C::F32>(mass);
+#pragma unroll
+        for (int c = 65; c < ZR; ++c) ZT[c * C::ROWT + r] = to_elem<C::F32>(0.f);
+    }
+    if (Zrow) {
+        st_frag<C::F32>(Zrow + r * C::ROWE + 16 * q, pack8<C::F32>(v));
+        st_frag<C::F32>(Zrow + r * C::ROWE + 16 * q + 8, pack8<C::F32>(v + 8));
+        if (q == 0) {
+            float m[8] = {mass, 0, 0, 0, 0, 0, 0, 0};
+            float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            st_frag<C::F32>(Zrow + r * C::ROWE + 64, pack8<C::F32>(m));
+            st_frag<C::F32>(Zrow + r * C::ROWE + 72, pack8<C::F32>(z));
+            st_frag<C::F32>(Zrow + r * C::ROWE + 80, pack8<C::F32>(z));
+            st_frag<C::F32>(Zrow + r * C::ROWE + 88, pack8<C::F32>(z));
+        }
+    }
+    (void)sizeof(elem);
+}
+
+// State block of one (bh, chunk): value sums [F][64] then masses [F], float32.
+template <class C>
+__device__ inline void load_state(const float* __restrict__ st, int w, int ln, int g,
+                                  f32x4 Macc[C::NKC * 2], f32x4 Zacc[C::NOWN * 2]) {
+#pragma unroll
+    for (int kc = 0; kc < C::NKC; ++kc)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int f = 32 * kc + 8 * g + 4 * h + i;
+                Macc[2 * kc + h][i] = st[(size_t)f * DH + 16 * w + ln];
+            }
+#pragma unroll
+    for (int o = 0; o < C::NOWN; ++o) {
+        const int kc = w + 4 * o;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int f = 32 * kc + 8 * g + 4 * h + i;
+                Zacc[2 * o + h][i] = (kc < C::NKC && ln == 0) ? st[(size_t)C::F * DH + f] : 0.f;
+            }
+    }
+}
+
+template <class C>
+__device__ inline void store_state(float* __restrict__ st, int w, int ln, int g,
+                                   const f32x4 Macc[C::NKC * 2], const f32x4 Zacc[C::NOWN * 2]) {
+#pragma unroll
+    for (int kc = 0; kc < C::NKC; ++kc)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int f = 32 * kc + 8 * g + 4 * h + i;
+                st[(size_t)f * DH + 16 * w + ln] = Macc[2 * kc + h][i];
+            }
+#pragma unroll
+    for (int o = 0; o < C::NOWN; ++o) {
+        const int kc = w + 4 * o;
+        if (kc < C::NKC && ln == 0) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int f = 32 * kc + 8 * g + 4 * h + i;
+                    st[(size_t)C::F * DH + f] = Zacc[2 * o + h][i];
+                }
+        }
+    }
+}
+
+// Project the own 16-token tile for the tiles of feature block fb and write
+// the features to LDS. Returns the features of the lane in `phi_frag` (one
+// operand per chunk of the block) when `keep` is set.
+template <class C>
+__device__ inline void block_features(const typename Prec<C::F32>::elem* __restrict__ W, int fb, int lane,
+                                      int w, int ln, int g, const typename Prec<C::F32>::frag xf[2],
+                                      float inv, bool valid, float beta, int L,
+                                      typename Prec<C::F32>::elem* rows /* [64][ROWF] or null */,
+                                      typename Prec<C::F32>::elem* cols /* [FBK*32][ROWT] or null */,
+                                      typename Prec<C::F32>::frag phi_frag[C::FBK]) {
+#pragma unroll
+    for (int tb = 0; tb < C::TPB; ++tb) {
+        const int t = fb * C::TPB + tb;
+        const f32x4 acc = project<C>(W, L, t, ln, g, xf);
+        float hs[4], phi[C::KB * 8], u[4], s[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hs[i] = acc[i] * inv;
+        soft_features<C>(t, g, hs, beta, L, phi, u, s);
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) {
+            const int kcl = tb * C::KB + kb;
+            float p8[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) p8[j] = valid ? phi[kb * 8 + j] : 0.f;
+            const typename Prec<C::F32>::frag fr = pack8<C::F32>(p8);
+            phi_frag[kcl] = fr;
+            if (rows) st_frag<C::F32>(rows + (16 * w + ln) * C::ROWF + 32 * kcl + 8 * g, fr);
+            if (cols) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) cols[(32 * kcl + 8 * g + j) * C::ROWT + 16 * w + ln] = fr[j];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// per-chunk sketch totals
+// ---------------------------------------------------------------------------
+struct TotArgs {
+    const void* Xb;      // rows that write the sketch (K, or Q for the gradient sketch)
+    const void* Z;       // V (kind 0) or dO (kind 1)
+    const float* Dv;     // kind 1: per-token D
+    const float* Ev;     // kind 1: per-token e
+    const void* W;       // [L, P, 64]
+    float* out;          // [BH][NC][F*65]
+    int64_t N;
+    int chunk;
+    int nchunks;
+    int L;
+    float beta;
+    int kind;
+};
+
+template <class C>
+__global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
+    using elem = typename Prec<C::F32>::elem;
+    using frag = typename Prec<C::F32>::frag;
+    __shared__ __attribute__((aligned(32))) elem s_cols[C::FBK * 32 * C::ROWT];
+    __shared__ __attribute__((aligned(32))) elem s_ZT[ZR * C::ROWT];
+
+    const int lane = threadIdx.x & 63, ln = lane & 15, g = lane >> 4;
+    // wave index as a scalar: every branch on it is wave-uniform, so no MFMA is
+    // ever issued under a partial or empty EXEC mask
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int bh = blockIdx.y, c = blockIdx.x;
+    const int64_t seg0 = (int64_t)c * a.chunk;
+    const int64_t seg1 = seg0 + a.chunk < a.N ? seg0 + a.chunk : a.N;
+    const size_t base = (size_t)bh * a.N;
+    const elem* W = reinterpret_cast<const elem*>(a.W);
+
+    f32x4 Macc[C::NKC * 2], Zacc[C::NOWN * 2];
+#pragma unroll
+    for (int i = 0; i < C::NKC * 2; ++i) Macc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < C::NOWN * 2; ++i) Zacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int64_t t0 = seg0; t0 < seg1; t0 += TB) {
+        const int nv = (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
+        const bool valid = 16 * w + ln < nv;
+        frag xf[2];
+        float inv, nrm;
+        load_x<C::F32>(a.Xb, base + t0 + 16 * w + ln, valid, g, xf, inv, nrm);
+        load_aug<C>(a.Z, a.Dv, a.Ev, a.kind, base + t0, nv, s_ZT, nullptr);
+#pragma unroll
+        for (int fb = 0; fb < C::NBLK; ++fb) {
+            frag phi[C::FBK];
+            block_features<C>(W, fb, lane, w, ln, g, xf, inv, valid, a.beta, a.L, nullptr, s_cols, phi);
+            __syncthreads();
+            frag zt[2], zm[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                zt[s] = ld_frag<C::F32>(s_ZT + (16 * w + ln) * C::ROWT + 32 * s + 8 * g);
+                zm[s] = ld_frag<C::F32>(s_ZT + (64 + ln) * C::ROWT + 32 * s + 8 * g);
+            }
+#pragma unroll
+            for (int kcl = 0; kcl < C::FBK; ++kcl) {
+                const int kc = fb * C::FBK + kcl;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const elem* arow = s_cols + (32 * kcl + canon_of_row(h, ln)) * C::ROWT + 8 * g;
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        const frag af = ld_frag<C::F32>(arow + 32 * s);
+                        Macc[2 * kc + h] = mma(af, zt[s], Macc[2 * kc + h]);
+                        if ((kc & 3) == w) Zacc[2 * (kc >> 2) + h] = mma(af, zm[s], Zacc[2 * (kc >> 2) + h]);
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    store_state<C>(a.out + ((size_t)bh * a.nchunks + c) * (size_t)(C::F * 65), w, ln, g, Macc, Zacc);
+}
+
+// ---------------------------------------------------------------------------
+// scans over chunks (one thread per state element, fixed order: deterministic)
+// ---------------------------------------------------------------------------
+template <int KIND>
+__global__ __launch_bounds__(256) void k_scan(float* __restrict__ st, float* __restrict__ total,
+                                              int nchunks, int elems) {
+    const int e = blockIdx.x * blockDim.x + threadIdx.x;
+    const int bh = blockIdx.y;
+    if (e >= elems) return;
+    float* p = st + (size_t)bh * nchunks * elems + e;
+    float run = 0.f;
+    if constexpr (KIND == SCAN_EXCL) {
+        for (int c = 0; c < nchunks; ++c) {
+            const float v = p[(size_t)c * elems];
+            p[(size_t)c * elems] = run;
+            run += v;
+        }
+    } else if constexpr (KIND == SCAN_REV_EXCL) {
+        for (int c = nchunks - 1; c >= 0; --c) {
+            const float v = p[(size_t)c * elems];
+            p[(size_t)c * elems] = run;
+            run += v;
+        }
+    } else {
+        for (int c = 0; c < nchunks; ++c) run += p[(size_t)c * elems];
+        total[(size_t)bh * elems + e] = run;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// the sub-block pass
+// ---------------------------------------------------------------------------
+struct PassArgs {
+    const void* Xa;        // readout-side rows
+    const void* Xb;        // sketch-side rows
+    const void* Zsrc;      // FWD/BWD_Q: V; BWD_K: dO
+    const void* Ysrc;      // BWD_Q: dO; BWD_K: V
+    const void* W;         // [L, P, 64]
+    const void* WTp;       // back-projection operands (k_prep)
+    const float* state;    // sketch before the chunk (causal) or the total
+    int64_t state_bh_stride;
+    int64_t state_chunk_stride;
+    float* Dv;             // per-token D  (BWD_Q writes, BWD_K reads)
+    float* Ev;             // per-token e
+    void* out0;            // FWD: O; BWD_Q: dQ; BWD_K: dK
+    void* out1;            // BWD_K: dV
+    int64_t N;
+    int chunk;
+    int L;
+    float beta;
+    int causal;
+};
+
+template <class C, int MODE>
+struct PassLds {
+    using elem = typename Prec<C::F32>::elem;
+    static constexpr bool BWD = MODE != MODE_FWD;
+    static constexpr int n_rows = TB * C::ROWF;                 // a-side features [64][ROWF]
+    static constexpr int n_brow = TB * C::ROWF;                 // b-side features [64][ROWF]
+    static constexpr int n_cols = C::FBK * 32 * C::ROWT;        // b-side features transposed
+    static constexpr int n_zt = ZR * C::ROWT;                   // z_b transposed
+    static constexpr int n_sc = TB * C::ROWT;                   // intra scores [a][b]
+    static constexpr int n_zr = BWD ? TB * C::ROWE : 0;         // z_b rows
+    static constexpr int n_yr = BWD ? TB * C::ROWE : 0;         // y_a rows
+    // aliases of [rows | brow] after the feature-block loop of phase 1
+    static constexpr int n_ms = C::FBK * 32 * C::ROWE;          // sketch rows (phase 2)
+    static constexpr int n_stage = TB * C::ROWD;                // O / dV / dO staging
+    static_assert(n_ms <= n_rows + n_brow, "sketch rows must fit the feature tiles");
+    static_assert(n_stage <= n_rows + n_brow, "staging must fit the feature tiles");
+    static constexpr int o_rows = 0;
+    static constexpr int o_brow = o_rows + n_rows;
+    static constexpr int o_cols = o_brow + n_brow;
+    static constexpr int o_zt = o_cols + n_cols;
+    static constexpr int o_sc = o_zt + n_zt;
+    static constexpr int o_zr = o_sc + n_sc;
+    static constexpr int o_yr = o_zr + n_zr;
+    static constexpr int n_elem = o_yr + n_yr;
+    static constexpr int n_float = 4 * TB + 4 * TB + 3 * TB;  // Dpart, dpart, Dint, Dfull, Efull
+    static constexpr int bytes = n_elem * (int)sizeof(elem) + n_float * 4;
+    static_assert(bytes <= 160 * 1024, "LDS budget");
+};
+
+template <class C, int MODE>
+__global__ __launch_bounds__(NT) void k_pass(PassArgs a) {
+    using elem = typename Prec<C::F32>::elem;
+    using frag = typename Prec<C::F32>::frag;
+    using LD = PassLds<C, MODE>;
+    constexpr bool BWD = MODE != MODE_FWD;
+    constexpr bool REV = MODE == MODE_BWD_K;   // b visible when b >= a, sub-blocks in reverse
+    __shared__ __attribute__((aligned(32))) elem lds[LD::n_elem];
+    __shared__ float ldf[LD::n_float];
+    elem* s_rows = lds + LD::o_rows;
+    elem* s_brow = lds + LD::o_brow;
+    elem* s_cols = lds + LD::o_cols;
+    elem* s_ZT = lds + LD::o_zt;
+    elem* s_sc = lds + LD::o_sc;
+    elem* s_zr = lds + LD::o_zr;
+    elem* s_yr = lds + LD::o_yr;
+    elem* s_ms = lds + LD::o_rows;      // phase-2 alias
+    elem* s_stage = lds + LD::o_rows;   // staging alias
+    float* f_Dpart = ldf;               // [4][64]
+    float* f_dpart = ldf + 4 * TB;      // [4][64]
+    float* f_Dint = ldf + 8 * TB;       // [64]
+    float* f_D = ldf + 9 * TB;          // [64]
+    float* f_E = ldf + 10 * TB;         // [64]
+
+    const int lane = threadIdx.x & 63, ln = lane & 15, g = lane >> 4;
+    // wave index as a scalar: every branch on it is wave-uniform, so no MFMA is
+    // ever issued under a partial or empty EXEC mask
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int bh = blockIdx.y, c = blockIdx.x;
+    const int64_t seg0 = (int64_t)c * a.chunk;
+    const int64_t seg1 = seg0 + a.chunk < a.N ? seg0 + a.chunk : a.N;
+    const size_t base = (size_t)bh * a.N;
+    const elem* W = reinterpret_cast<const elem*>(a.W);
+    const elem* WTp = reinterpret_cast<const elem*>(a.WTp);
+    const bool causal = a.causal != 0;
+
+    f32x4 Macc[C::NKC * 2], Zacc[C::NOWN * 2];
+    load_state<C>(a.state + bh * a.state_bh_stride + c * a.state_chunk_stride, w, ln, g, Macc, Zacc);
+
+    const int nsub = (int)((seg1 - seg0 + TB - 1) / TB);
+    for (int it = 0; it < nsub; ++it) {
+        const int sb = REV ? nsub - 1 - it : it;
+        const int64_t t0 = seg0 + (int64_t)sb * TB;
+        const int nv = (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
+        const int my = 16 * w + ln;              // own token within the sub-block
+        const bool valid = my < nv;
+        const size_t row = base + t0 + my;
+
+        frag xa[2], xb[2];
+        float inv_a, nrm_a, inv_b, nrm_b;
+        load_x<C::F32>(a.Xa, row, valid, g, xa, inv_a, nrm_a);
+        load_x<C::F32>(a.Xb, row, valid, g, xb, inv_b, nrm_b);
+        load_aug<C>(a.Zsrc, a.Dv, a.Ev, REV ? 1 : 0, base + t0, nv, s_ZT, BWD ? s_zr : nullptr);
+
+        f32x4 Y[4], Dacc[4], Sc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            Y[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            Dacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            Sc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        // ----------------------------- phase 1 -------------------------------
+#pragma unroll
+        for (int fb = 0; fb < C::NBLK; ++fb) {
+            frag phiA[C::FBK], phiB[C::FBK];
+            block_features<C>(W, fb, lane, w, ln, g, xa, inv_a, true, a.beta, a.L, s_rows, nullptr, phiA);
+            block_features<C>(W, fb, lane, w, ln, g, xb, inv_b, valid, a.beta, a.L, s_brow,
+                              (!BWD && causal) ? s_cols : nullptr, phiB);
+            __syncthreads();
+            frag zt[2], zm[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                zt[s] = ld_frag<C::F32>(s_ZT + (16 * w + ln) * C::ROWT + 32 * s + 8 * g);
+                zm[s] = ld_frag<C::F32>(s_ZT + (64 + ln) * C::ROWT + 32 * s + 8 * g);
+            }
+            if (causal) {
+#pragma unroll
+                for (int bt = 0; bt < 4; ++bt) {
+                    const bool vis = REV ? (bt >= w) : (bt <= w);
+                    if (vis) {
+#pragma unroll
+                        for (int kcl = 0; kcl < C::FBK; ++kcl)
+                            Sc[bt] = mma(ld_frag<C::F32>(s_brow + (16 * bt + ln) * C::ROWF + 32 * kcl + 8 * g),
+                                         phiA[kcl], Sc[bt]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int kcl = 0; kcl < C::FBK; ++kcl) {
+                const int kc = fb * C::FBK + kcl;
+                const frag mf = pack<C::F32>(Macc[2 * kc], Macc[2 * kc + 1]);
+                const bool own = (kc & 3) == w;
+                frag zf;
+                if constexpr (MODE != MODE_BWD_K) zf = pack<C::F32>(Zacc[2 * (kc >> 2)], Zacc[2 * (kc >> 2) + 1]);
+#pragma unroll
+                for (int at = 0; at < 4; ++at) {
+                    const frag af = ld_frag<C::F32>(s_rows + (16 * at + ln) * C::ROWF + 32 * kcl + 8 * g);
+                    Y[at] = mma(af, mf, Y[at]);
+                    if constexpr (MODE != MODE_BWD_K)
+                        if (own) Dacc[at] = mma(af, zf, Dacc[at]);
+                }
+            }
+            if constexpr (MODE == MODE_FWD) {
+                if (causal) {
+#pragma unroll
+                    for (int kcl = 0; kcl < C::FBK; ++kcl) {
+                        const int kc = fb * C::FBK + kcl;
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const elem* arow = s_cols + (32 * kcl + canon_of_row(h, ln)) * C::ROWT + 8 * g;
+#pragma unroll
+                            for (int s = 0; s < 2; ++s) {
+                                const frag af = ld_frag<C::F32>(arow + 32 * s);
+                                Macc[2 * kc + h] = mma(af, zt[s], Macc[2 * kc + h]);
+                                if ((kc & 3) == w) Zacc[2 * (kc >> 2) + h] = mma(af, zm[s], Zacc[2 * (kc >> 2) + h]);
+                            }
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+        }
+        // intra-sub-block term
+        if (causal) {
+            float dint = 0.f;
+#pragma unroll
+            for (int bt = 0; bt < 4; ++bt) {
+                f32x4 v;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int b = 16 * bt + 4 * g + i;
+                    const bool vis = (REV ? (b >= my) : (b <= my)) && b < nv;
+                    v[i] = vis ? Sc[bt][i] : 0.f;
+                    dint += v[i];
+                }
+                st_half<C::F32>(s_sc + my * C::ROWT + 16 * bt + 4 * g, v);
+            }
+            if constexpr (MODE != MODE_BWD_K) {
+                dint = sum_groups(dint);
+                if (g == 0) f_Dint[my] = dint;
+            }
+        }
+        if constexpr (MODE != MODE_BWD_K) {
+            if (ln == 0) {
+#pragma unroll
+                for (int at = 0; at < 4; ++at)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) f_Dpart[w * TB + 16 * at + 4 * g + i] = Dacc[at][i];
+            }
+        }
+        __syncthreads();
+        if (causal) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const frag zt = ld_frag<C::F32>(s_ZT + (16 * w + ln) * C::ROWT + 32 * s + 8 * g);
+#pragma unroll
+                for (int at = 0; at < 4; ++at)
+                    Y[at] = mma(ld_frag<C::F32>(s_sc + (16 * at + ln) * C::ROWT + 32 * s + 8 * g), zt, Y[at]);
+            }
+        }
+        // ----------------------- readout epilogues ----------------------------
+        if constexpr (MODE == MODE_FWD || MODE == MODE_BWD_Q) {
+            float Dr[4][4];
+#pragma unroll
+            for (int at = 0; at < 4; ++at)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * at + 4 * g + i;
+                    float d = f_Dpart[r] + f_Dpart[TB + r] + f_Dpart[2 * TB + r] + f_Dpart[3 * TB + r];
+                    if (causal) d += f_Dint[r];
+                    Dr[at][i] = d;
+                }
+            if constexpr (MODE == MODE_FWD) {
+#pragma unroll
+                for (int at = 0; at < 4; ++at)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        s_stage[(16 * at + 4 * g + i) * C::ROWD + 16 * w + ln] = to_elem<C::F32>(Y[at][i] / Dr[at][i]);
+                __syncthreads();
+                {
+                    const int th = threadIdx.x, r = th >> 2, q = th & 3;
+                    if (r < nv) {
+                        using T = typename In<C::F32>::T;
+                        T* o = reinterpret_cast<T*>(a.out0) + (base + t0 + r) * DH + 16 * q;
+                        const elem* src = s_stage + r * C::ROWD + 16 * q;
+                        *reinterpret_cast<frag*>(o) = ld_frag<C::F32>(src);
+                        *reinterpret_cast<frag*>(o + 8) = ld_frag<C::F32>(src + 8);
+                    }
+                }
+                __syncthreads();
+                continue;
+            } else {
+                // BWD_Q: O, delta = <dO, O>, e = -delta / D, y = [dO / D | e]
+                {
+                    const int th = threadIdx.x, r = th >> 2, q = th & 3;
+                    float v[16];
+                    if (r < nv) load16<C::F32>(a.Ysrc, (base + t0 + r) * DH + 16 * q, v);
+                    else
+#pragma unroll
+                        for (int cc = 0; cc < 16; ++cc) v[cc] = 0.f;
+                    st_frag<C::F32>(s_stage + r * C::ROWD + 16 * q, pack8<C::F32>(v));
+                    st_frag<C::F32>(s_stage + r * C::ROWD + 16 * q + 8, pack8<C::F32>(v + 8));
+                }
+                __syncthreads();
+#pragma unroll
+                for (int at = 0; at < 4; ++at)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = 16 * at + 4 * g + i;
+                        const float o = Y[at][i] / Dr[at][i];
+                        float p = o * elem_f<C::F32>(s_stage[r * C::ROWD + 16 * w + ln]);
+                        p = sum_row16(p);
+                        if (ln == 0) f_dpart[w * TB + r] = p;
+                    }
+                __syncthreads();
+                {
+                    const int th = threadIdx.x, r = th >> 2, q = th & 3;
+                    const bool ok = r < nv;
+                    float D = 1.f, e = 0.f;
+                    if (ok) {
+                        D = f_Dpart[r] + f_Dpart[TB + r] + f_Dpart[2 * TB + r] + f_Dpart[3 * TB + r] +
+                            (causal ? f_Dint[r] : 0.f);
+                        const float delta = f_dpart[r] + f_dpart[TB + r] + f_dpart[2 * TB + r] + f_dpart[3 * TB + r];
+                        e = -delta / D;
+                    }
+                    const float invD = ok ? 1.f / D : 0.f;
+                    float v[16];
+#pragma unroll
+                    for (int cc = 0; cc < 16; ++cc) v[cc] = elem_f<C::F32>(s_stage[r * C::ROWD + 16 * q + cc]) * invD;
+                    st_frag<C::F32>(s_yr + r * C::ROWE + 16 * q, pack8<C::F32>(v));
+                    st_frag<C::F32>(s_yr + r * C::ROWE + 16 * q + 8, pack8<C::F32>(v + 8));
+                    if (q == 0) {
+                        float m[8] = {e, 0, 0, 0, 0, 0, 0, 0};
+                        float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                        st_frag<C::F32>(s_yr + r * C::ROWE + 64, pack8<C::F32>(m));
+                        st_frag<C::F32>(s_yr + r * C::ROWE + 72, pack8<C::F32>(z));
+                        st_frag<C::F32>(s_yr + r * C::ROWE + 80, pack8<C::F32>(z));
+                        st_frag<C::F32>(s_yr + r * C::ROWE + 88, pack8<C::F32>(z));
+                        if (ok) {
+                            a.Dv[base + t0 + r] = D;
+                            a.Ev[base + t0 + r] = e;
+                        }
+                    }
+                }
+                __syncthreads();
+            }
+        } else {
+            // BWD_K: dV = Y (value columns); y rows = [v | 1]
+#pragma unroll
+            for (int at = 0; at < 4; ++at)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    s_stage[(16 * at + 4 * g + i) * C::ROWD + 16 * w + ln] = to_elem<C::F32>(Y[at][i]);
+            {
+                // y rows = [v | 1 | 0]
+                const int th = threadIdx.x, r = th >> 2, q = th & 3;
+                float v[16];
+                const bool ok = r < nv;
+                if (ok) load16<C::F32>(a.Ysrc, (base + t0 + r) * DH + 16 * q, v);
+                else
+#pragma unroll
+                    for (int cc = 0; cc < 16; ++cc) v[cc] = 0.f;
+                st_frag<C::F32>(s_yr + r * C::ROWE + 16 * q, pack8<C::F32>(v));
+                st_frag<C::F32>(s_yr + r * C::ROWE + 16 * q + 8, pack8<C::F32>(v + 8));
+                if (q == 0) {
+                    float m[8] = {ok ? 1.f : 0.f, 0, 0, 0, 0, 0, 0, 0};
+                    float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                    st_frag<C::F32>(s_yr + r * C::ROWE + 64, pack8<C::F32>(m));
+                    st_frag<C::F32>(s_yr + r * C::ROWE + 72, pack8<C::F32>(z));
+                    st_frag<C::F32>(s_yr + r * C::ROWE + 80, pack8<C::F32>(z));
+                    st_frag<C::F32>(s_yr + r * C::ROWE + 88, pack8<C::F32>(z));
+                }
+            }
+            __syncthreads();
+            {
+                const int th = threadIdx.x, r = th >> 2, q = th & 3;
+                if (r < nv) {
+                    using T = typename In<C::F32>::T;
+                    T* o = reinterpret_cast<T*>(a.out1) + (base + t0 + r) * DH + 16 * q;
+                    const elem* src = s_stage + r * C::ROWD + 16 * q;
+                    *reinterpret_cast<frag*>(o) = ld_frag<C::F32>(src);
+                    *reinterpret_cast<frag*>(o + 8) = ld_frag<C::F32>(src + 8);
+                }
+            }
+            __syncthreads();
+        }
+        if constexpr (BWD) {
+            // ----------------------------- phase 2 ---------------------------
+            frag Cf[2];
+            if (causal) {
+                f32x4 Cc[4];
+                frag yf[3];
+#pragma unroll
+                for (int s = 0; s < 3; ++s) yf[s] = ld_frag<C::F32>(s_yr + my * C::ROWE + 32 * s + 8 * g);
+#pragma unroll
+                for (int bt = 0; bt < 4; ++bt) {
+                    Cc[bt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    const bool vis = REV ? (bt >= w) : (bt <= w);
+                    if (vis) {
+#pragma unroll
+                        for (int s = 0; s < 3; ++s)
+                            Cc[bt] = mma(ld_frag<C::F32>(s_zr + (16 * bt + ln) * C::ROWE + 32 * s + 8 * g), yf[s], Cc[bt]);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int b = 16 * bt + 4 * g + i;
+                        const bool v2 = (REV ? (b >= my) : (b <= my)) && b < nv;
+                        if (!v2) Cc[bt][i] = 0.f;
+                    }
+                }
+                Cf[0] = pack<C::F32>(Cc[0], Cc[1]);
+                Cf[1] = pack<C::F32>(Cc[2], Cc[3]);
+            }
+            frag yf[3];
+#pragma unroll
+            for (int s = 0; s < 3; ++s) yf[s] = ld_frag<C::F32>(s_yr + my * C::ROWE + 32 * s + 8 * g);
+            // zero the padding columns 65..95 of the sketch rows once
+            for (int idx = threadIdx.x; idx < C::FBK * 32 * 31; idx += NT) {
+                const int r = idx / 31, cc = 65 + idx % 31;
+                s_ms[r * C::ROWE + cc] = to_elem<C::F32>(0.f);
+            }
+            f32x4 dX[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dX[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            f32x4 dhp[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int fb = 0; fb < C::NBLK; ++fb) {
+                // sketch rows of this block (before this sub-block's update)
+#pragma unroll
+                for (int kcl = 0; kcl < C::FBK; ++kcl) {
+                    const int kc = fb * C::FBK + kcl;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int fl = 32 * kcl + 8 * g + 4 * h + i;
+                            s_ms[fl * C::ROWE + 16 * w + ln] = to_elem<C::F32>(Macc[2 * kc + h][i]);
+                            if ((kc & 3) == w && ln == 0)
+                                s_ms[fl * C::ROWE + 64] = to_elem<C::F32>(Zacc[2 * (kc >> 2) + h][i]);
+                        }
+                }
+                // b-side features (own tile) -> transposed tile
+                frag phiB[C::FBK];
+                block_features<C>(W, fb, lane, w, ln, g, xb, inv_b, valid, a.beta, a.L, nullptr, s_cols, phiB);
+                __syncthreads();
+                f32x4 G[C::FBK * 2];
+#pragma unroll
+                for (int m = 0; m < C::FBK * 2; ++m) {
+                    const int kcl = m >> 1, h = m & 1;
+                    const int fl = 32 * kcl + canon_of_row(h, ln);
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < 3; ++s)
+                        acc = mma(ld_frag<C::F32>(s_ms + fl * C::ROWE + 32 * s + 8 * g), yf[s], acc);
+                    if (causal) {
+#pragma unroll
+                        for (int s2 = 0; s2 < 2; ++s2) {
+                            const elem* p = s_cols + fl * C::ROWT + 32 * s2 + 4 * g;
+                            acc = mma(ld_frag2<C::F32>(p, p + 16), Cf[s2], acc);
+                        }
+                    }
+                    G[m] = acc;
+                }
+                // chain rule and back-projection, tile by tile
+#pragma unroll
+                for (int tb = 0; tb < C::TPB; ++tb) {
+                    const int t = fb * C::TPB + tb;
+                    const f32x4 acc = project<C>(W, a.L, t, ln, g, xa);
+                    float hs[4], phi[C::KB * 8], u[4], s[4], dA[C::KB * 8], dh[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) hs[i] = acc[i] * inv_a;
+                    soft_features<C>(t, g, hs, a.beta, a.L, phi, u, s);
+#pragma unroll
+                    for (int kb = 0; kb < C::KB; ++kb) {
+                        const int kcl = tb * C::KB + kb;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            dA[kb * 8 + i] = G[2 * kcl][i];
+                            dA[kb * 8 + 4 + i] = G[2 * kcl + 1][i];
+                        }
+                    }
+                    soft_features_backward<C>(phi, dA, u, a.beta, dh);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) dhp[t & 1][i] = dh[i];
+                    if ((t & 1) == 1 || t == C::MT - 1) {
+                        const frag df = pack<C::F32>(dhp[0], (t & 1) ? dhp[1] : f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                        for (int dt = 0; dt < 4; ++dt)
+                            dX[dt] = mma(ld_frag<C::F32>(WTp + ((size_t)((t >> 1) * 4 + dt) * 64 + lane) * 8), df, dX[dt]);
+                        dhp[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        dhp[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    }
+                }
+                // sketch update for this block
+                if (causal) {
+                    frag zt[2], zm[2];
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        zt[s] = ld_frag<C::F32>(s_ZT + (16 * w + ln) * C::ROWT + 32 * s + 8 * g);
+                        zm[s] = ld_frag<C::F32>(s_ZT + (64 + ln) * C::ROWT + 32 * s + 8 * g);
+                    }
+#pragma unroll
+                    for (int kcl = 0; kcl < C::FBK; ++kcl) {
+                        const int kc = fb * C::FBK + kcl;
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const elem* arow = s_cols + (32 * kcl + canon_of_row(h, ln)) * C::ROWT + 8 * g;
+#pragma unroll
+                            for (int s = 0; s < 2; ++s) {
+                                const frag af = ld_frag<C::F32>(arow + 32 * s);
+                                Macc[2 * kc + h] = mma(af, zt[s], Macc[2 * kc + h]);
+                                if ((kc & 3) == w) Zacc[2 * (kc >> 2) + h] = mma(af, zm[s], Zacc[2 * (kc >> 2) + h]);
+                            }
+                        }
+                    }
+                }
+                __syncthreads();
+            }
+            // dx = (dx_hat - x_hat <x_hat, dx_hat>) / |x|
+            {
+                float xv[4][4];
+                float radial = 0.f;
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) {
+                    const size_t off = row * DH + 16 * dt + 4 * g;
+                    if constexpr (C::F32) {
+                        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+                        if (valid) v = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(a.Xa) + off);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) xv[dt][i] = v[i];
+                    } else {
+                        bf16x4 v = {};
+                        if (valid) v = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(a.Xa) + off);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) xv[dt][i] = valid ? (float)v[i] : 0.f;
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) radial += xv[dt][i] * inv_a * dX[dt][i];
+                }
+                radial = sum_groups(radial);
+                const bool tangent = nrm_a > NORM_EPS;
+                if (valid) {
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt) {
+                        f32x4 o;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            o[i] = (tangent ? dX[dt][i] - xv[dt][i] * inv_a * radial : dX[dt][i]) * inv_a;
+                        using T = typename In<C::F32>::T;
+                        T* dst = reinterpret_cast<T*>(a.out0) + row * DH + 16 * dt + 4 * g;
+                        if constexpr (C::F32) {
+                            *reinterpret_cast<f32x4*>(dst) = o;
+                        } else {
+                            bf16x4 ob;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) ob[i] = (__bf16)o[i];
+                            *reinterpret_cast<bf16x4*>(dst) = ob;
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// hard-hash diagnostic
+// ---------------------------------------------------------------------------
+template <class C>
+__global__ __launch_bounds__(NT) void k_hash(const void* X, const void* Wv, int64_t rows, int L,
+                                             int32_t* __restrict__ ids, unsigned long long* near_zero) {
+    using elem = typename Prec<C::F32>::elem;
+    using frag = typename Prec<C::F32>::frag;
+    const int lane = threadIdx.x & 63, ln = lane & 15, g = lane >> 4;
+    // wave index as a scalar: every branch on it is wave-uniform, so no MFMA is
+    // ever issued under a partial or empty EXEC mask
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t r = ((int64_t)blockIdx.x * NW + w) * 16 + ln;
+    const bool valid = r < rows;
+    const elem* W = reinterpret_cast<const elem*>(Wv);
+    frag xf[2];
+    float inv, nrm;
+    load_x<C::F32>(X, valid ? (size_t)r : 0, valid, g, xf, inv, nrm);
+    unsigned int nz = 0;
+#pragma unroll
+    for (int t = 0; t < C::MT; ++t) {
+        const f32x4 acc = project<C>(W, L, t, ln, g, xf);
+#pragma unroll
+        for (int tl = 0; tl < C::TPL; ++tl) {
+            const int table = t * C::TPT + g * C::TPL + tl;
+            int id = 0;
+#pragma unroll
+            for (int p = 0; p < C::P; ++p) {
+                const float h = acc[tl * C::Pp + p];
+                if (h > 0.f) id |= 1 << p;
+                if (valid && table < L && fabsf(h * inv) < NEAR_ZERO) ++nz;
+            }
+            if (valid && table < L) ids[(size_t)r * L + table] = id;
+        }
+    }
+    // wave-level sum of the near-zero count, one atomic per wave
+    unsigned int tot = nz;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
+    if (lane == 0 && tot) atomicAdd(near_zero, (unsigned long long)tot);
+}
+
+}  // namespace race

@@ -1,0 +1,93 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, sizes workspaces, and rejects bad arguments before any
+device work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_lsh_sketch_amd as race
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "race_attn.h")
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails validation first
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(race_attn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = race.lib()
+    names = declared_symbols()
+    assert set(names) == set(race.SYMBOLS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    assert race.status_string(0) == "RACE_OK"
+    assert race.status_string(3) == "RACE_ERR_WORKSPACE"
+    assert race.status_string(99) == "RACE_ERR_UNKNOWN"
+
+
+def test_workspace_and_saved_sizes():
+    # causal: per-chunk states of F * 65 floats; F = 32 * MT * KB
+    fwd = race.workspace_bytes(1, 4, 12_000_000, 64, 4, 16, True, 1024, False)
+    bwd = race.workspace_bytes(1, 4, 12_000_000, 64, 4, 16, True, 1024, True)
+    saved = race.saved_bytes(1, 4, 12_000_000, 64, 4, 16, True, 1024)
+    nchunks = -(-12_000_000 // 1024)
+    assert saved == 4 * nchunks * 256 * 65 * 4
+    assert fwd >= saved and bwd >= 2 * saved + 2 * 4 * 12_000_000 * 4
+    assert race.saved_bytes(2, 3, 100, 64, 2, 8, False, 64) == 6 * 32 * 65 * 4
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, 1, 10, 64, 4, 8, 1, 16, 0), race.RACE_ERR_INVALID_ARG),        # B = 0
+    ((1, 1, 0, 64, 4, 8, 1, 16, 0), race.RACE_ERR_INVALID_ARG),         # N = 0
+    ((1, 1, 10, 32, 4, 8, 1, 16, 0), race.RACE_ERR_UNSUPPORTED),        # d != 64
+    ((1, 1, 10, 64, 5, 8, 1, 16, 0), race.RACE_ERR_UNSUPPORTED),        # P > 4
+    ((1, 1, 10, 64, 0, 8, 1, 16, 0), race.RACE_ERR_INVALID_ARG),        # P = 0
+    ((1, 1, 10, 64, 4, 33, 1, 16, 0), race.RACE_ERR_UNSUPPORTED),       # L * P' > 128
+    ((1, 1, 10, 64, 4, 8, 1, 0, 0), race.RACE_ERR_INVALID_ARG),         # chunk = 0
+    ((1, 70000, 10, 64, 4, 8, 1, 16, 0), race.RACE_ERR_UNSUPPORTED),    # B*H > 65535
+    ((1 << 40, 1 << 20, 1 << 20, 64, 4, 8, 1, 16, 0), race.RACE_ERR_INVALID_ARG),  # overflow
+])
+def test_workspace_bytes_rejects(args, code):
+    out = ctypes.c_size_t(0)
+    assert race.lib().race_attn_workspace_bytes(*args, ctypes.byref(out)) == code
+
+
+def test_forward_argument_errors_before_device_work():
+    L = race.lib()
+    ok = (FAKE, FAKE, FAKE, FAKE, 1, 1, 100, 64, 4, 8, 1.0, 1, 64, race.RACE_BF16, FAKE, None, FAKE)
+    need = race.workspace_bytes(1, 1, 100, 64, 4, 8, True, 64, False)
+    # null query
+    assert L.race_attn_fwd(None, *ok[1:], need, None) == race.RACE_ERR_INVALID_ARG
+    # bad dtype
+    bad = list(ok); bad[13] = 7
+    assert L.race_attn_fwd(*bad, need, None) == race.RACE_ERR_INVALID_ARG
+    # non-finite temperature
+    bad = list(ok); bad[10] = float("nan")
+    assert L.race_attn_fwd(*bad, need, None) == race.RACE_ERR_INVALID_ARG
+    # workspace too small
+    assert L.race_attn_fwd(*ok, need - 1, None) == race.RACE_ERR_WORKSPACE
+    # unsupported head dim
+    bad = list(ok); bad[7] = 128
+    assert L.race_attn_fwd(*bad, need, None) == race.RACE_ERR_UNSUPPORTED
+
+
+def test_backward_and_hash_argument_errors():
+    L = race.lib()
+    need = race.workspace_bytes(1, 1, 100, 64, 4, 8, False, 64, True)
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 100, 64, 4, 8, 1.0, 0, 64, race.RACE_F32,
+            FAKE, FAKE, FAKE, FAKE]
+    assert L.race_attn_bwd(*args, need - 1, None) == race.RACE_ERR_WORKSPACE
+    a2 = list(args); a2[16] = None   # dQ
+    assert L.race_attn_bwd(*a2, need, None) == race.RACE_ERR_INVALID_ARG
+    assert L.race_attn_hash(FAKE, FAKE, 1, 1, 10, 64, 4, 8, race.RACE_F32, None, FAKE, None) == \
+        race.RACE_ERR_INVALID_ARG
+    assert L.race_attn_hash(FAKE, FAKE, 1, 1, 10, 64, 6, 8, race.RACE_F32, FAKE, FAKE, None) == \
+        race.RACE_ERR_UNSUPPORTED
