@@ -1,0 +1,214 @@
+"""RACE Attention layer benchmark on one MI355X.
+
+One step = forward + backward of the whole RACE MHA layer core (all heads)
+over one batch of synthetic input already resident in HBM: race_attn_fwd
+(keeping the per-chunk sketch states) then race_attn_bwd (reusing them).
+
+Default workload: causal, B=1, H=4, N=12,000,000, d=64, P=4, L=16,
+chunk=1024, bf16 inputs with float32 sketches; Q, K, V, dO iid N(0,1) from
+the seeded Philox stream. Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12           # bytes/s, MI355X HBM3E
+MFMA_PEAK = {"bf16": 2.5e15, "f32": 157.3e12}   # dense matrix FLOP/s
+
+METRIC = "RACE MHA layer fwd+bwd tokens/s (causal, N=12M) + % of HBM/MFMA roofline"
+
+
+def per_token_head_counts(w):
+    """Algorithmic bytes and FLOPs per (batch, head, token), d = 64.
+
+    Layer: forward reads Q, K, V and writes O; backward reads Q, K, V, dO and
+    writes dQ, dK, dV. FLOPs: forward 4 d L P (two projections) + 2 U (one
+    sketch-sized contraction to read out, one to write), backward 8 d L P + 4 U,
+    with U = 2 L R (d + 1).
+    Per kernel (its own inputs and outputs, each touched once):
+      pass_fwd   : Q, K, V in, O out;            4dLP + 2U
+      pass_bwd_q : Q, K, V, dO in, dQ out;       6dLP + U   (projections, dA_Q, back-projection)
+      pass_bwd_k : Q, K, V, dO in, dK, dV out;   6dLP + 3U  (projections, T, dV, dA_K, back-projection)
+      totals_kv  : K, V in;                      2dLP + U
+      totals_qg  : Q, dO in;                     2dLP + U
+    """
+    es = 2 if w.dtype == "bf16" else 4
+    row = w.d * es
+    R = 1 << w.P
+    U = 2 * w.L * R * (w.d + 1)
+    dLP = w.d * w.L * w.P
+    layer = {"bytes": 4 * row + 7 * row, "flops": (4 * dLP + 2 * U) + (8 * dLP + 4 * U)}
+    kernels = {
+        "pass_fwd": (4 * row, 4 * dLP + 2 * U),
+        "pass_bwd_q": (5 * row, 6 * dLP + U),
+        "pass_bwd_k": (6 * row, 6 * dLP + 3 * U),
+        "totals_kv": (2 * row, 2 * dLP + U),
+        "totals_qg": (2 * row, 2 * dLP + U),
+    }
+    return layer, kernels
+
+
+def cpu_baseline(w, n_sample: int):
+    """The float64 oracle on the first n_sample tokens of every head of the
+    same workload (same seeded inputs), causal forward + backward."""
+    import numpy as np
+    import synth
+    from oracle import stream as oracle
+
+    shape = (w.B, w.H, n_sample, w.d)
+    host = {}
+    for name, tid in (("Q", synth.TID_Q), ("K", synth.TID_K), ("V", synth.TID_V), ("dO", synth.TID_DO)):
+        arr = np.empty(shape, np.uint16 if w.dtype == "bf16" else np.float32)
+        for b in range(w.B):
+            for h in range(w.H):
+                start = ((b * w.H + h) * w.N) * w.d
+                arr[b, h] = synth.normal(w.seed, tid, (n_sample, w.d), w.dtype, start=start)
+        host[name] = arr
+    W = synth.normal(w.seed, synth.TID_W, (w.L, w.P, w.d), w.dtype)
+    W64 = synth.bf16_bits_to_f64(W) if w.dtype == "bf16" else W.astype(np.float64)
+    threads = min(w.B * w.H, len(os.sched_getaffinity(0)))
+    os.environ.setdefault("OMP_NUM_THREADS", str(threads))
+    t0 = time.perf_counter()
+    oracle.forward(host["Q"], host["K"], host["V"], W64, w.beta, w.causal)
+    oracle.backward(host["Q"], host["K"], host["V"], W64, host["dO"], w.beta, w.causal)
+    dt = time.perf_counter() - t0
+    return {"value": w.B * n_sample / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n_sample} tokens of each of the {w.B * w.H} (batch, head) sequences, "
+                      f"causal fwd+bwd in float64, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="causal_long_n12M")
+    ap.add_argument("--cpu-sample", type=int, default=131072)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the sequence-sharded "
+              "multi-GPU path is a design, not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import linear_lsh_sketch_amd as race
+    import synth
+    from synth.workloads import BY_NAME
+
+    w = BY_NAME[args.workload]
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    shape = (w.B, w.H, w.N, w.d)
+    t = {}
+    for name, tid in (("Q", synth.TID_Q), ("K", synth.TID_K), ("V", synth.TID_V), ("dO", synth.TID_DO)):
+        t[name] = torch.empty(shape, dtype=tdt, device=dev)
+        if w.qk_dist == "mixture" and name in ("Q", "K"):
+            synth.mixture_device(w.seed, tid, synth.TID_QIDS if name == "Q" else synth.TID_KIDS, t[name])
+        else:
+            synth.normal_device(w.seed, tid, t[name])
+    t["W"] = synth.normal_device(w.seed, synth.TID_W, torch.empty((w.L, w.P, w.d), dtype=tdt, device=dev))
+    O = torch.empty(shape, dtype=tdt, device=dev)
+    grads = tuple(torch.empty(shape, dtype=tdt, device=dev) for _ in range(3))
+    ws_f = race.alloc_workspace(w.B, w.H, w.N, w.P, w.L, w.causal, w.chunk, False, dev)
+    ws_b = race.alloc_workspace(w.B, w.H, w.N, w.P, w.L, w.causal, w.chunk, True, dev)
+    saved = race.alloc_saved(w.B, w.H, w.N, w.P, w.L, w.causal, w.chunk, dev)
+    torch.cuda.synchronize()
+
+    def step():
+        race.forward(t["Q"], t["K"], t["V"], t["W"], w.P, w.L, w.beta, w.causal, w.chunk, out=O,
+                     saved=saved, ws=ws_f)
+        race.backward(t["Q"], t["K"], t["V"], t["W"], t["dO"], w.P, w.L, w.beta, w.causal, w.chunk,
+                      saved=saved, ws=ws_b, grads=grads)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps; per-kernel HIP events on the library's stream
+    timer = race.StageTimer()
+    stage_ms = {}
+    stage_n = {}
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    with timer:
+        for _ in range(args.steps):
+            for call in ("fwd", "bwd"):
+                if call == "fwd":
+                    race.forward(t["Q"], t["K"], t["V"], t["W"], w.P, w.L, w.beta, w.causal, w.chunk,
+                                 out=O, saved=saved, ws=ws_f)
+                else:
+                    race.backward(t["Q"], t["K"], t["V"], t["W"], t["dO"], w.P, w.L, w.beta, w.causal,
+                                  w.chunk, saved=saved, ws=ws_b, grads=grads)
+                for name, ms in timer.stages():
+                    stage_ms[name] = stage_ms.get(name, 0.0) + ms
+                    stage_n[name] = stage_n.get(name, 0) + 1
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    timer.close()
+    ms_step = start.elapsed_time(end) / args.steps
+    tokens = w.B * w.N
+    value = tokens / (ms_step / 1e3)
+
+    layer, kernels = per_token_head_counts(w)
+    units = w.token_heads
+    # dominant kernel: largest total time in the timed region
+    dom = max(stage_ms, key=lambda k: stage_ms[k])
+    avg_ms = stage_ms[dom] / stage_n[dom]
+    kb, kf = kernels.get(dom, (0, 0))
+    peak_f = MFMA_PEAK[w.dtype]
+    t_hbm, t_mma = kb * units / HBM_PEAK, kf * units / peak_f
+    if t_hbm >= t_mma:
+        roof = {"bound": "hbm", "achieved": kb * units / (avg_ms / 1e3) / 1e9, "peak": HBM_PEAK / 1e9,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": kf * units / (avg_ms / 1e3) / 1e12, "peak": peak_f / 1e12,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["kernel_avg_ms"] = avg_ms
+    layer_t = max(layer["bytes"] * units / HBM_PEAK, layer["flops"] * units / peak_f)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "P": w.P, "L": w.L,
+                   "chunk": w.chunk, "causal": w.causal, "temperature": w.beta, "seed": w.seed,
+                   "qk_dist": w.qk_dist},
+        "roofline": roof,
+        "layer_roofline": {"bound": "hbm" if layer["bytes"] * units / HBM_PEAK >= layer["flops"] * units / peak_f
+                           else "mfma", "frac": layer_t / (ms_step / 1e3),
+                           "alg_bytes_per_token_head": layer["bytes"], "alg_flops_per_token_head": layer["flops"]},
+        "stages_ms_per_step": {k: v / args.steps for k, v in sorted(stage_ms.items(), key=lambda kv: -kv[1])},
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_sample, w.N))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

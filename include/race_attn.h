@@ -121,6 +121,19 @@ race_status_t race_attn_hash(const void *X, const void *W, int64_t B, int64_t H,
                              int d, int P, int L, race_dtype_t dtype, int32_t *bucket_ids,
                              unsigned long long *near_zero, void *stream);
 
+/* Profiling aid (not needed for computation). For the CALLING THREAD only:
+ * `events` is an array of `capacity` (>= 2) caller-created hipEvent_t handles.
+ * Each subsequent race_attn_fwd / _bwd / _hash call on this thread records
+ * events[i] on its stream just before its i-th kernel launch and one more
+ * event after the last launch, so stage i took elapsed(events[i], events[i+1]).
+ * Pass events = NULL to stop. race_attn_profile_count() gives the number of
+ * events the last call recorded; race_attn_profile_stage(i) the name of the
+ * kernel launched after event i ("end" for the last). Calls on other threads
+ * are unaffected. */
+race_status_t race_attn_profile_events(void **events, int capacity);
+int race_attn_profile_count(void);
+const char *race_attn_profile_stage(int i);
+
 /* Static, human-readable name of a status code. */
 const char *race_attn_status_string(race_status_t status);
 

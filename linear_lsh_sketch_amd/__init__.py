@@ -17,7 +17,8 @@ RACE_OK, RACE_ERR_INVALID_ARG, RACE_ERR_UNSUPPORTED, RACE_ERR_WORKSPACE, RACE_ER
 RACE_F32, RACE_BF16 = 0, 1
 
 SYMBOLS = ("race_attn_workspace_bytes", "race_attn_saved_bytes", "race_attn_fwd",
-           "race_attn_bwd", "race_attn_hash", "race_attn_status_string")
+           "race_attn_bwd", "race_attn_hash", "race_attn_profile_events", "race_attn_profile_count",
+           "race_attn_profile_stage", "race_attn_status_string")
 
 
 class RaceError(RuntimeError):
@@ -46,9 +47,15 @@ def lib():
         L.race_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, fl, i32, i32,
                                     i32, vp, vp, vp, vp, sz, vp]
         L.race_attn_hash.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, i32, vp, vp, vp]
+        L.race_attn_profile_events.argtypes = [vp, i32]
+        L.race_attn_profile_count.argtypes = []
+        L.race_attn_profile_stage.argtypes = [i32]
+        L.race_attn_profile_stage.restype = ctypes.c_char_p
         L.race_attn_status_string.argtypes = [i32]
         L.race_attn_status_string.restype = ctypes.c_char_p
-        for name in SYMBOLS[:-1]:
+        for name in ("race_attn_workspace_bytes", "race_attn_saved_bytes", "race_attn_fwd",
+                     "race_attn_bwd", "race_attn_hash", "race_attn_profile_events",
+                     "race_attn_profile_count"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -172,6 +179,50 @@ def race_attn_hash(X, W, P, L, stream=None):
                                 _stream(stream))
     _check(code, "race_attn_hash")
     return ids, nz
+
+
+class StageTimer:
+    """Per-kernel timing of library calls with HIP events (the library records
+    them on its own stream between its launches; see race_attn_profile_events)."""
+
+    def __init__(self, capacity: int = 17):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.n = capacity
+        self.events = (ctypes.c_void_p * capacity)()
+        for i in range(capacity):
+            ev = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.events[i] = ev
+
+    def __enter__(self):
+        _check(lib().race_attn_profile_events(self.events, self.n), "race_attn_profile_events")
+        return self
+
+    def __exit__(self, *exc):
+        lib().race_attn_profile_events(None, 0)
+
+    def stages(self):
+        """[(kernel name, milliseconds)] of the last call on this thread (synchronises)."""
+        n = lib().race_attn_profile_count()
+        if n < 2:
+            return []
+        self.hip.hipEventSynchronize(self.events[n - 1])
+        out = []
+        for i in range(n - 1):
+            ms = ctypes.c_float(0)
+            self.hip.hipEventElapsedTime(ctypes.byref(ms), self.events[i], self.events[i + 1])
+            out.append((lib().race_attn_profile_stage(i).decode(), float(ms.value)))
+        return out
+
+    def close(self):
+        for i in range(self.n):
+            self.hip.hipEventDestroy(self.events[i])
 
 
 # short aliases

@@ -11,6 +11,15 @@ using namespace race;
 
 namespace {
 
+// Per-thread profiling state (race_attn_profile_events). Only the calling
+// thread's own calls read or write it, so concurrent callers do not interact.
+constexpr int kMaxStages = 16;
+thread_local hipEvent_t* t_events = nullptr;
+thread_local int t_capacity = 0;
+thread_local int t_count = 0;
+thread_local const char* t_names[kMaxStages + 1];
+thread_local hipStream_t t_stream = nullptr;
+
 race_status_t prepare(int64_t B, int64_t H, int64_t N, int d, int P, int L, int causal, int chunk,
                       Shape& s, Derived& dv) {
     s.B = B; s.H = H; s.N = N; s.d = d; s.P = P; s.L = L; s.causal = causal ? 1 : 0; s.chunk = chunk;
@@ -38,12 +47,37 @@ race_status_t guarded(race_status_t (*fn)(const Shape&, const Derived&, const Ws
 
 race_status_t go(race_dtype_t dtype, const Shape& s, const Derived& dv, const WsLayout& wl, const Call& c) {
     (void)hipGetLastError();  // clear a stale error so it is not reported as ours
-    return dtype == RACE_F32 ? guarded(dispatch<true>, s, dv, wl, c) : guarded(dispatch<false>, s, dv, wl, c);
+    t_count = 0;
+    t_stream = c.stream;
+    race_status_t rc =
+        dtype == RACE_F32 ? guarded(dispatch<true>, s, dv, wl, c) : guarded(dispatch<false>, s, dv, wl, c);
+    profile_mark("end", c.stream);
+    return rc;
 }
 
 }  // namespace
 
+namespace race {
+void profile_mark(const char* stage, hipStream_t stream) {
+    if (!t_events || t_count >= t_capacity || t_count > kMaxStages) return;
+    if (hipEventRecord(t_events[t_count], stream) == hipSuccess) t_names[t_count++] = stage;
+}
+}  // namespace race
+
 extern "C" {
+
+race_status_t race_attn_profile_events(void** events, int capacity) {
+    if (events && capacity < 2) return RACE_ERR_INVALID_ARG;
+    t_events = reinterpret_cast<hipEvent_t*>(events);
+    t_capacity = events ? (capacity < kMaxStages + 1 ? capacity : kMaxStages + 1) : 0;
+    t_count = 0;
+    return RACE_OK;
+}
+
+int race_attn_profile_count(void) { return t_count; }
+
+const char* race_attn_profile_stage(int i) { return (i >= 0 && i < t_count) ? t_names[i] : nullptr; }
+
 
 race_status_t race_attn_workspace_bytes(int64_t B, int64_t H, int64_t N, int d, int P, int L, int causal,
                                         int chunk, int for_backward, size_t* bytes) {

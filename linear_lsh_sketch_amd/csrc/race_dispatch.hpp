@@ -27,6 +27,10 @@ struct Call {
 template <bool F32>
 race_status_t dispatch(const Shape& s, const Derived& d, const WsLayout& wl, const Call& c);
 
+// Profiling aid (race_attn_profile_events): records a caller-owned event on the
+// stream before each launch of the current call, when enabled on this thread.
+void profile_mark(const char* stage, hipStream_t stream);
+
 inline race_status_t launch_ok() {
     return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
 }
@@ -43,6 +47,7 @@ race_status_t run_totals(const Shape& s, const Derived& d, const void* Xb, const
     TotArgs a;
     a.Xb = Xb; a.Z = Z; a.Dv = Dv; a.Ev = Ev; a.W = W; a.out = out;
     a.N = s.N; a.chunk = s.chunk; a.nchunks = (int)d.NC; a.L = s.L; a.beta = beta; a.kind = kind;
+    profile_mark(kind == 0 ? "totals_kv" : "totals_qg", st);
     hipLaunchKernelGGL(k_totals<C>, dim3((unsigned)d.NC, (unsigned)d.BH), dim3(NT), 0, st, a);
     return launch_ok();
 }
@@ -50,6 +55,7 @@ race_status_t run_totals(const Shape& s, const Derived& d, const void* Xb, const
 template <int KIND>
 race_status_t run_scan(const Derived& d, float* states, float* total, hipStream_t st) {
     const int elems = (int)d.F65;
+    profile_mark(KIND == SCAN_EXCL ? "scan_excl" : KIND == SCAN_REV_EXCL ? "scan_rev_excl" : "scan_total", st);
     hipLaunchKernelGGL(k_scan<KIND>, dim3((unsigned)((elems + 255) / 256), (unsigned)d.BH), dim3(256), 0, st,
                        states, total, (int)d.NC, elems);
     return launch_ok();
@@ -58,6 +64,7 @@ race_status_t run_scan(const Derived& d, float* states, float* total, hipStream_
 template <class C, int MODE>
 race_status_t run_pass(const Shape& s, const Derived& d, PassArgs a, hipStream_t st) {
     a.N = s.N; a.chunk = s.chunk; a.L = s.L; a.causal = s.causal;
+    profile_mark(MODE == MODE_FWD ? "pass_fwd" : MODE == MODE_BWD_Q ? "pass_bwd_q" : "pass_bwd_k", st);
     hipLaunchKernelGGL((k_pass<C, MODE>), dim3((unsigned)d.NC, (unsigned)d.BH), dim3(NT), 0, st, a);
     return launch_ok();
 }
@@ -70,6 +77,7 @@ race_status_t run(const Shape& s, const Derived& d, const WsLayout& wl, const Ca
         const int64_t rows = d.BH * s.N;
         const int64_t blocks = (rows + 63) / 64;
         if (blocks > 0x7fffffff) return RACE_ERR_UNSUPPORTED;
+        profile_mark("hash", st);
         hipLaunchKernelGGL(k_hash<C>, dim3((unsigned)blocks), dim3(NT), 0, st, c.X, c.W, rows, s.L, c.ids,
                            c.near_zero);
         return launch_ok();
@@ -96,6 +104,7 @@ race_status_t run(const Shape& s, const Derived& d, const WsLayout& wl, const Ca
     // backward
     using elem = typename Prec<C::F32>::elem;
     elem* WTp = reinterpret_cast<elem*>(ws + wl.wt);
+    profile_mark("prep", st);
     hipLaunchKernelGGL(k_prep<C>, dim3(8), dim3(256), 0, st, reinterpret_cast<const elem*>(c.W), s.L, WTp);
     RACE_TRY(launch_ok());
     float* Dv = reinterpret_cast<float*>(ws + wl.D);

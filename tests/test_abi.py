@@ -27,6 +27,15 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, n), n
 
 
+def test_profile_hook_without_gpu():
+    L = race.lib()
+    assert L.race_attn_profile_events(None, 0) == race.RACE_OK
+    assert L.race_attn_profile_count() == 0
+    assert L.race_attn_profile_stage(0) is None
+    arr = (ctypes.c_void_p * 1)()
+    assert L.race_attn_profile_events(arr, 1) == race.RACE_ERR_INVALID_ARG
+
+
 def test_status_strings():
     assert race.status_string(0) == "RACE_OK"
     assert race.status_string(3) == "RACE_ERR_WORKSPACE"
