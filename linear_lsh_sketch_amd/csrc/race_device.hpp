@@ -151,13 +151,20 @@ __device__ inline float elem_f(typename Prec<F32>::elem x) {
 // a pair of 16-row tiles: rho = 16 h + 4 g + i  ->  8 g + 4 h + i
 __device__ inline int canon_of_row(int h, int m) { return 8 * (m >> 2) + 4 * h + (m & 3); }
 
+// Transcendentals on the hardware units: v_exp_f32 (2^x) and v_rcp_f32, each
+// about 1 ulp; no IEEE division sequences on the hot path.
+__device__ inline float rcp_(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ inline float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
+constexpr float LOG2E = 1.4426950408889634f;
+
+// tanh(x) = sign(x) (1 - e^{-2|x|}) / (1 + e^{-2|x|})
 __device__ inline float fast_tanh(float x) {
-    float t = __expf(-2.f * fabsf(x));
-    float r = (1.f - t) / (1.f + t);
-    return copysignf(r, x);
+    const float t = exp2_(-2.f * LOG2E * fabsf(x));
+    return copysignf((1.f - t) * rcp_(1.f + t), x);
 }
 
-__device__ inline float sigmoidf_(float x) { return 1.f / (1.f + __expf(-x)); }
+// sigmoid(x) = 1 / (1 + e^{-x})
+__device__ inline float sigmoidf_(float x) { return rcp_(1.f + exp2_(-LOG2E * x)); }
 
 // Sum over the four lane groups holding the same column (lanes ln, ln+16, ...).
 __device__ inline float sum_groups(float v) {
@@ -194,7 +201,9 @@ struct Cfg {
     static constexpr int FBK = FBK0 < NKC ? FBK0 : NKC;
     static constexpr int TPB = FBK / KB;          // tiles per block
     static constexpr int NBLK = NKC / FBK;
-    static constexpr int NOWN = (NKC + 3) / 4;    // mass chunks owned per wave (max)
+    // Mass column: in feature block fb, wave w < FBK owns chunk w of the block
+    // (global chunk fb * FBK + w); its accumulators are Zacc[2 fb + h].
+    static constexpr int NOWN = NBLK;
     static constexpr int NPAIR = (MT + 1) / 2;    // 32-row pairs of projection tiles
     static constexpr int PAD = Prec<F32>::PAD;
     static constexpr int ROWF = FBK * 32 + PAD;   // row stride of token x feature tiles

@@ -68,54 +68,79 @@ struct In {
     using T = typename std::conditional<F32, float, __bf16>::type;
 };
 
-// Load 16 consecutive input values (cols c0..c0+15 of a [*, 64] row) as float.
+// Global loads are issued one sub-block ahead ("raw" registers) and consumed
+// by the next iteration, so their latency overlaps the current sub-block.
+
+// This lane's projection operand of one token row: K positions 32 s + 8 g .. +7.
 template <bool F32>
-__device__ inline void load16(const void* base, size_t off, float v[16]) {
-    if constexpr (F32) {
-        const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
+__device__ inline void load_row_raw(const void* X, size_t row, bool valid, int g,
+                                    typename Prec<F32>::frag x[2]) {
+    using T = typename In<F32>::T;
+    const T* p = reinterpret_cast<const T*>(X) + row * DH + 8 * g;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            float4 x = p[q];
-            v[4 * q] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
-        }
-    } else {
-        const bf16x8* p = reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(base) + off);
-        bf16x8 a = p[0], b = p[1];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) { v[j] = (float)a[j]; v[8 + j] = (float)b[j]; }
-    }
+    for (int s = 0; s < 2; ++s)
+        x[s] = valid ? *reinterpret_cast<const typename Prec<F32>::frag*>(p + 32 * s) : zero_frag<F32>();
 }
 
-// Projection operand of one token row: K positions 32 s + 8 g .. +7 for s = 0, 1;
-// also returns 1 / max(|x|, eps) (identical in the four lane groups).
+// 1 / max(|x|, eps) of the row held by load_row_raw (same in all four lane groups).
 template <bool F32>
-__device__ inline void load_x(const void* X, size_t row, bool valid, int g,
-                              typename Prec<F32>::frag xf[2], float& inv, float& nrm) {
+__device__ inline void row_norm(const typename Prec<F32>::frag x[2], float& inv, float& nrm) {
     float ss = 0.f;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        if constexpr (F32) {
-            f32x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (valid) v = *reinterpret_cast<const f32x8*>(reinterpret_cast<const float*>(X) + row * DH + 32 * s + 8 * g);
-            xf[s] = v;
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) ss += v[j] * v[j];
-        } else {
-            bf16x8 v = zero_frag<false>();
-            if (valid) v = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(X) + row * DH + 32 * s + 8 * g);
-            xf[s] = v;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) { const float f = (float)v[j]; ss += f * f; }
+        for (int j = 0; j < 8; ++j) {
+            const float f = (float)x[s][j];
+            ss += f * f;
         }
-    }
     ss = sum_groups(ss);
     nrm = sqrtf(ss);
-    inv = 1.f / fmaxf(nrm, NORM_EPS);
+    inv = rcp_(fmaxf(nrm, NORM_EPS));
 }
 
+// 16 consecutive values (columns 16 q .. 16 q + 15 of a [*, 64] row).
+template <bool F32>
+__device__ inline void load_q16_raw(const void* X, size_t off, bool ok, typename Prec<F32>::frag v[2]) {
+    using T = typename In<F32>::T;
+    const T* p = reinterpret_cast<const T*>(X) + off;
+    v[0] = ok ? *reinterpret_cast<const typename Prec<F32>::frag*>(p) : zero_frag<F32>();
+    v[1] = ok ? *reinterpret_cast<const typename Prec<F32>::frag*>(p + 8) : zero_frag<F32>();
+}
+
+template <bool F32>
+__device__ inline float q16_at(const typename Prec<F32>::frag v[2], int c) {
+    return (float)v[c >> 3][c & 7];
+}
+
+// Projection operands W' (rows in tile order) in LDS, laid out per lane:
+// [tile][K half s][lane][8], filled once per workgroup.
 template <class C>
-__device__ inline f32x4 project(const typename Prec<C::F32>::elem* __restrict__ W, int L, int t, int ln,
-                                int g, const typename Prec<C::F32>::frag xf[2]) {
+__device__ inline void stage_w(const typename Prec<C::F32>::elem* __restrict__ W, int L,
+                               typename Prec<C::F32>::elem* s_w) {
+    for (int idx = threadIdx.x; idx < C::MT * 1024; idx += NT) {
+        const int t = idx / 1024, s = (idx / 512) & 1, l = (idx / 8) & 63, j = idx & 7;
+        int table, plane;
+        row_table<C>(t, l & 15, table, plane);
+        typename Prec<C::F32>::elem v = to_elem<C::F32>(0.f);
+        if (table < L && plane < C::P) v = W[((size_t)table * C::P + plane) * DH + 32 * s + 8 * (l >> 4) + j];
+        s_w[idx] = v;
+    }
+}
+
+// H^T tile t (rows 4g..4g+3 of column = this lane's token) from LDS-staged W'.
+template <class C>
+__device__ inline f32x4 project_lds(const typename Prec<C::F32>::elem* s_w, int t, int lane,
+                                    const typename Prec<C::F32>::frag xf[2]) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) acc = mma(ld_frag<C::F32>(s_w + ((t * 2 + s) * 64 + lane) * 8), xf[s], acc);
+    return acc;
+}
+
+// Same from W in global memory (used where LDS is full, and by the hash kernel).
+template <class C>
+__device__ inline f32x4 project_global(const typename Prec<C::F32>::elem* __restrict__ W, int L, int t, int ln,
+                                       int g, const typename Prec<C::F32>::frag xf[2]) {
     int table, plane;
     row_table<C>(t, ln, table, plane);
     const bool ok = table < L && plane < C::P;
@@ -131,52 +156,46 @@ __device__ inline f32x4 project(const typename Prec<C::F32>::elem* __restrict__ 
     return acc;
 }
 
-// Fill the transposed value tile ZT [80][ROWT] (and optionally the row tile
-// Zrow [64][ROWE]) for tokens row0 .. row0+63 (nv valid):
-//   kind 0: z = [x | 1]; kind 1: z = [x / D | e] with D, e per token.
+// Source of the projection operands: LDS-staged when `s_w` is set.
 template <class C>
-__device__ inline void load_aug(const void* X, const float* __restrict__ Dv, const float* __restrict__ Ev,
-                                int kind, size_t row0, int nv, typename Prec<C::F32>::elem* ZT,
-                                typename Prec<C::F32>::elem* Zrow) {
-    using elem = typename Prec<C::F32>::elem;
-    const int th = threadIdx.x, r = th >> 2, q = th & 3;
-    const bool ok = r < nv;
-    float v[16];
-    float mass = 0.f;
-    if (ok) {
-        load16<C::F32>(X, (row0 + r) * DH + 16 * q, v);
-        if (kind == 0) {
-            mass = 1.f;
-        } else {
-            const float invD = 1.f / Dv[row0 + r];
-#pragma unroll
-            for (int c = 0; c < 16; ++c) v[c] *= invD;
-            mass = Ev[row0 + r];
-        }
-    } else {
-#pragma unroll
-        for (int c = 0; c < 16; ++c) v[c] = 0.f;
+struct WSrc {
+    const typename Prec<C::F32>::elem* s_w;
+    const typename Prec<C::F32>::elem* W;
+    int L;
+    __device__ inline f32x4 project(int t, int lane, int ln, int g, const typename Prec<C::F32>::frag xf[2]) const {
+        return s_w ? project_lds<C>(s_w, t, lane, xf) : project_global<C>(W, L, t, ln, g, xf);
     }
+};
+
+// Write the value tile of the 64 tokens (this thread: row th/4, quarter th%4)
+// into ZT [80][ROWT] (transposed) and optionally Zrow [64][ROWE] (rows):
+// z = [x * scale | mass]. Rows/columns 65.. stay zero from stage_constants.
+template <class C>
+__device__ inline void write_aug(const typename Prec<C::F32>::frag zr[2], float scale, float mass,
+                                 typename Prec<C::F32>::elem* ZT, typename Prec<C::F32>::elem* Zrow) {
+    const int th = threadIdx.x, r = th >> 2, q = th & 3;
+    float v[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) v[c] = q16_at<C::F32>(zr, c) * scale;
 #pragma unroll
     for (int c = 0; c < 16; ++c) ZT[(16 * q + c) * C::ROWT + r] = to_elem<C::F32>(v[c]);
-    if (q == 0) {
-        ZT[64 * C::ROWT + r] = to_elem<C::F32>(mass);
-#pragma unroll
-        for (int c = 65; c < ZR; ++c) ZT[c * C::ROWT + r] = to_elem<C::F32>(0.f);
-    }
+    if (q == 0) ZT[64 * C::ROWT + r] = to_elem<C::F32>(mass);
     if (Zrow) {
         st_frag<C::F32>(Zrow + r * C::ROWE + 16 * q, pack8<C::F32>(v));
         st_frag<C::F32>(Zrow + r * C::ROWE + 16 * q + 8, pack8<C::F32>(v + 8));
-        if (q == 0) {
-            float m[8] = {mass, 0, 0, 0, 0, 0, 0, 0};
-            float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-            st_frag<C::F32>(Zrow + r * C::ROWE + 64, pack8<C::F32>(m));
-            st_frag<C::F32>(Zrow + r * C::ROWE + 72, pack8<C::F32>(z));
-            st_frag<C::F32>(Zrow + r * C::ROWE + 80, pack8<C::F32>(z));
-            st_frag<C::F32>(Zrow + r * C::ROWE + 88, pack8<C::F32>(z));
-        }
+        if (q == 0) Zrow[r * C::ROWE + 64] = to_elem<C::F32>(mass);
     }
-    (void)sizeof(elem);
+}
+
+// Zero the constant padding of ZT (rows 65..79) and of row tiles (cols 65..95).
+template <class C>
+__device__ inline void zero_pads(typename Prec<C::F32>::elem* ZT, typename Prec<C::F32>::elem* rows_a,
+                                 typename Prec<C::F32>::elem* rows_b) {
+    for (int idx = threadIdx.x; idx < 15 * TB; idx += NT) ZT[(65 + idx / TB) * C::ROWT + idx % TB] = to_elem<C::F32>(0.f);
+    if (rows_a)
+        for (int idx = threadIdx.x; idx < 31 * TB; idx += NT) rows_a[(idx / 31) * C::ROWE + 65 + idx % 31] = to_elem<C::F32>(0.f);
+    if (rows_b)
+        for (int idx = threadIdx.x; idx < 31 * TB; idx += NT) rows_b[(idx / 31) * C::ROWE + 65 + idx % 31] = to_elem<C::F32>(0.f);
 }
 
 // State block of one (bh, chunk): value sums [F][64] then masses [F], float32.
@@ -193,14 +212,14 @@ __device__ inline void load_state(const float* __restrict__ st, int w, int ln, i
                 Macc[2 * kc + h][i] = st[(size_t)f * DH + 16 * w + ln];
             }
 #pragma unroll
-    for (int o = 0; o < C::NOWN; ++o) {
-        const int kc = w + 4 * o;
+    for (int fb = 0; fb < C::NBLK; ++fb) {
+        const int kc = fb * C::FBK + w;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int f = 32 * kc + 8 * g + 4 * h + i;
-                Zacc[2 * o + h][i] = (kc < C::NKC && ln == 0) ? st[(size_t)C::F * DH + f] : 0.f;
+                Zacc[2 * fb + h][i] = (w < C::FBK && ln == 0) ? st[(size_t)C::F * DH + f] : 0.f;
             }
     }
 }
@@ -217,35 +236,68 @@ __device__ inline void store_state(float* __restrict__ st, int w, int ln, int g,
                 const int f = 32 * kc + 8 * g + 4 * h + i;
                 st[(size_t)f * DH + 16 * w + ln] = Macc[2 * kc + h][i];
             }
+    if (w < C::FBK && ln == 0) {
 #pragma unroll
-    for (int o = 0; o < C::NOWN; ++o) {
-        const int kc = w + 4 * o;
-        if (kc < C::NKC && ln == 0) {
+        for (int fb = 0; fb < C::NBLK; ++fb) {
+            const int kc = fb * C::FBK + w;
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int f = 32 * kc + 8 * g + 4 * h + i;
-                    st[(size_t)C::F * DH + f] = Zacc[2 * o + h][i];
+                    st[(size_t)C::F * DH + f] = Zacc[2 * fb + h][i];
                 }
         }
     }
 }
 
-// Project the own 16-token tile for the tiles of feature block fb and write
-// the features to LDS. Returns the features of the lane in `phi_frag` (one
-// operand per chunk of the block) when `keep` is set.
+// Sketch update for feature block fb from the transposed b-side features
+// (cols) and the transposed value tile: value columns of wave w, then the
+// mass accumulators of the chunk wave w owns in this block.
 template <class C>
-__device__ inline void block_features(const typename Prec<C::F32>::elem* __restrict__ W, int fb, int lane,
-                                      int w, int ln, int g, const typename Prec<C::F32>::frag xf[2],
-                                      float inv, bool valid, float beta, int L,
-                                      typename Prec<C::F32>::elem* rows /* [64][ROWF] or null */,
+__device__ inline void sketch_update(int fb, int w, int ln, int g, const typename Prec<C::F32>::elem* cols,
+                                     const typename Prec<C::F32>::elem* ZT, f32x4 Macc[C::NKC * 2],
+                                     f32x4 Zacc[C::NOWN * 2]) {
+    using frag = typename Prec<C::F32>::frag;
+    frag zt[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) zt[s] = ld_frag<C::F32>(ZT + (16 * w + ln) * C::ROWT + 32 * s + 8 * g);
+#pragma unroll
+    for (int kcl = 0; kcl < C::FBK; ++kcl) {
+        const int kc = fb * C::FBK + kcl;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const typename Prec<C::F32>::elem* arow = cols + (32 * kcl + canon_of_row(h, ln)) * C::ROWT + 8 * g;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) Macc[2 * kc + h] = mma(ld_frag<C::F32>(arow + 32 * s), zt[s], Macc[2 * kc + h]);
+        }
+    }
+    if (w < C::FBK) {
+        frag zm[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) zm[s] = ld_frag<C::F32>(ZT + (64 + ln) * C::ROWT + 32 * s + 8 * g);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const typename Prec<C::F32>::elem* arow = cols + (32 * w + canon_of_row(h, ln)) * C::ROWT + 8 * g;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) Zacc[2 * fb + h] = mma(ld_frag<C::F32>(arow + 32 * s), zm[s], Zacc[2 * fb + h]);
+        }
+    }
+}
+
+// Project the own 16-token tile for the tiles of feature block fb and write
+// the features to LDS (row layout `rows` and/or transposed `cols`); when KEEP,
+// also return the lane's operands (one per chunk of the block) in phi_frag.
+template <class C, bool KEEP>
+__device__ inline void block_features(const WSrc<C>& wsrc, int fb, int lane, int w, int ln, int g,
+                                      const typename Prec<C::F32>::frag xf[2], float inv, bool valid, float beta,
+                                      int L, typename Prec<C::F32>::elem* rows /* [64][ROWF] or null */,
                                       typename Prec<C::F32>::elem* cols /* [FBK*32][ROWT] or null */,
-                                      typename Prec<C::F32>::frag phi_frag[C::FBK]) {
+                                      typename Prec<C::F32>::frag (&phi_frag)[C::FBK]) {
 #pragma unroll
     for (int tb = 0; tb < C::TPB; ++tb) {
         const int t = fb * C::TPB + tb;
-        const f32x4 acc = project<C>(W, L, t, ln, g, xf);
+        const f32x4 acc = wsrc.project(t, lane, ln, g, xf);
         float hs[4], phi[C::KB * 8], u[4], s[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) hs[i] = acc[i] * inv;
@@ -257,7 +309,7 @@ __device__ inline void block_features(const typename Prec<C::F32>::elem* __restr
 #pragma unroll
             for (int j = 0; j < 8; ++j) p8[j] = valid ? phi[kb * 8 + j] : 0.f;
             const typename Prec<C::F32>::frag fr = pack8<C::F32>(p8);
-            phi_frag[kcl] = fr;
+            if constexpr (KEEP) phi_frag[kcl] = fr;
             if (rows) st_frag<C::F32>(rows + (16 * w + ln) * C::ROWF + 32 * kcl + 8 * g, fr);
             if (cols) {
 #pragma unroll
@@ -286,21 +338,37 @@ struct TotArgs {
 };
 
 template <class C>
+struct TotLds {
+    using elem = typename Prec<C::F32>::elem;
+    static constexpr int n_cols = C::FBK * 32 * C::ROWT;
+    static constexpr int n_zt = ZR * C::ROWT;
+    static constexpr int n_w = C::MT * 1024;
+    static constexpr int n_elem = n_cols + n_zt + n_w;
+    static_assert(n_elem * (int)sizeof(elem) <= 160 * 1024, "LDS budget");
+};
+
+template <class C>
 __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
     using elem = typename Prec<C::F32>::elem;
     using frag = typename Prec<C::F32>::frag;
-    __shared__ __attribute__((aligned(32))) elem s_cols[C::FBK * 32 * C::ROWT];
-    __shared__ __attribute__((aligned(32))) elem s_ZT[ZR * C::ROWT];
+    using LD = TotLds<C>;
+    __shared__ __attribute__((aligned(32))) elem lds[LD::n_elem];
+    elem* s_cols = lds;
+    elem* s_ZT = lds + LD::n_cols;
+    elem* s_w = s_ZT + LD::n_zt;
 
     const int lane = threadIdx.x & 63, ln = lane & 15, g = lane >> 4;
     // wave index as a scalar: every branch on it is wave-uniform, so no MFMA is
     // ever issued under a partial or empty EXEC mask
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int th = threadIdx.x, tr = th >> 2, tq = th & 3;
     const int bh = blockIdx.y, c = blockIdx.x;
     const int64_t seg0 = (int64_t)c * a.chunk;
     const int64_t seg1 = seg0 + a.chunk < a.N ? seg0 + a.chunk : a.N;
     const size_t base = (size_t)bh * a.N;
-    const elem* W = reinterpret_cast<const elem*>(a.W);
+    stage_w<C>(reinterpret_cast<const elem*>(a.W), a.L, s_w);
+    zero_pads<C>(s_ZT, nullptr, nullptr);
+    const WSrc<C> wsrc{s_w, reinterpret_cast<const elem*>(a.W), a.L};
 
     f32x4 Macc[C::NKC * 2], Zacc[C::NOWN * 2];
 #pragma unroll
@@ -308,38 +376,37 @@ __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
 #pragma unroll
     for (int i = 0; i < C::NOWN * 2; ++i) Zacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // prefetch registers for the next sub-block
+    frag nx[2], nz[2];
+    float nd = 1.f, ne = 0.f;
+    auto issue = [&](int64_t t0) {
+        const int nv = (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
+        load_row_raw<C::F32>(a.Xb, base + t0 + 16 * w + ln, 16 * w + ln < nv, g, nx);
+        const bool ok = tr < nv;
+        load_q16_raw<C::F32>(a.Z, (base + t0 + tr) * DH + 16 * tq, ok, nz);
+        if (a.kind == 1 && ok) {
+            nd = a.Dv[base + t0 + tr];
+            ne = a.Ev[base + t0 + tr];
+        }
+    };
+    issue(seg0);
     for (int64_t t0 = seg0; t0 < seg1; t0 += TB) {
         const int nv = (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
         const bool valid = 16 * w + ln < nv;
-        frag xf[2];
+        frag xf[2] = {nx[0], nx[1]}, zr[2] = {nz[0], nz[1]};
+        const float dz = nd, ez = ne;
+        if (t0 + TB < seg1) issue(t0 + TB);
         float inv, nrm;
-        load_x<C::F32>(a.Xb, base + t0 + 16 * w + ln, valid, g, xf, inv, nrm);
-        load_aug<C>(a.Z, a.Dv, a.Ev, a.kind, base + t0, nv, s_ZT, nullptr);
+        row_norm<C::F32>(xf, inv, nrm);
+        const bool ok = tr < nv;
+        if (a.kind == 0) write_aug<C>(zr, 1.f, ok ? 1.f : 0.f, s_ZT, nullptr);
+        else write_aug<C>(zr, ok ? rcp_(dz) : 0.f, ok ? ez : 0.f, s_ZT, nullptr);
 #pragma unroll
         for (int fb = 0; fb < C::NBLK; ++fb) {
-            frag phi[C::FBK];
-            block_features<C>(W, fb, lane, w, ln, g, xf, inv, valid, a.beta, a.L, nullptr, s_cols, phi);
+            frag unused[C::FBK];
+            block_features<C, false>(wsrc, fb, lane, w, ln, g, xf, inv, valid, a.beta, a.L, nullptr, s_cols, unused);
             __syncthreads();
-            frag zt[2], zm[2];
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                zt[s] = ld_frag<C::F32>(s_ZT + (16 * w + ln) * C::ROWT + 32 * s + 8 * g);
-                zm[s] = ld_frag<C::F32>(s_ZT + (64 + ln) * C::ROWT + 32 * s + 8 * g);
-            }
-#pragma unroll
-            for (int kcl = 0; kcl < C::FBK; ++kcl) {
-                const int kc = fb * C::FBK + kcl;
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const elem* arow = s_cols + (32 * kcl + canon_of_row(h, ln)) * C::ROWT + 8 * g;
-#pragma unroll
-                    for (int s = 0; s < 2; ++s) {
-                        const frag af = ld_frag<C::F32>(arow + 32 * s);
-                        Macc[2 * kc + h] = mma(af, zt[s], Macc[2 * kc + h]);
-                        if ((kc & 3) == w) Zacc[2 * (kc >> 2) + h] = mma(af, zm[s], Zacc[2 * (kc >> 2) + h]);
-                    }
-                }
-            }
+            sketch_update<C>(fb, w, ln, g, s_cols, s_ZT, Macc, Zacc);
             __syncthreads();
         }
     }
@@ -422,8 +489,14 @@ struct PassLds {
     static constexpr int o_sc = o_zt + n_zt;
     static constexpr int o_zr = o_sc + n_sc;
     static constexpr int o_yr = o_zr + n_zr;
-    static constexpr int n_elem = o_yr + n_yr;
-    static constexpr int n_float = 4 * TB + 4 * TB + 3 * TB;  // Dpart, dpart, Dint, Dfull, Efull
+    static constexpr int n_float = 4 * TB + 4 * TB + TB;      // Dpart, dpart, Dint
+    static constexpr int base_elem = o_yr + n_yr;
+    // W' staged in LDS when it fits (else projections read it from global memory)
+    static constexpr int n_w0 = C::MT * 1024;
+    static constexpr bool W_LDS = (base_elem + n_w0) * (int)sizeof(elem) + n_float * 4 <= 160 * 1024;
+    static constexpr int n_w = W_LDS ? n_w0 : 0;
+    static constexpr int o_w = base_elem;
+    static constexpr int n_elem = base_elem + n_w;
     static constexpr int bytes = n_elem * (int)sizeof(elem) + n_float * 4;
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
@@ -433,6 +506,7 @@ __global__ __launch_bounds__(NT) void k_pass(PassArgs a) {
     using elem = typename Prec<C::F32>::elem;
     using frag = typename Prec<C::F32>::frag;
     using LD = PassLds<C, MODE>;
+    using T = typename In<C::F32>::T;
     constexpr bool BWD = MODE != MODE_FWD;
     constexpr bool REV = MODE == MODE_BWD_K;   // b visible when b >= a, sub-blocks in reverse
     __shared__ __attribute__((aligned(32))) elem lds[LD::n_elem];
@@ -449,13 +523,12 @@ __global__ __launch_bounds__(NT) void k_pass(PassArgs a) {
     float* f_Dpart = ldf;               // [4][64]
     float* f_dpart = ldf + 4 * TB;      // [4][64]
     float* f_Dint = ldf + 8 * TB;       // [64]
-    float* f_D = ldf + 9 * TB;          // [64]
-    float* f_E = ldf + 10 * TB;         // [64]
 
     const int lane = threadIdx.x & 63, ln = lane & 15, g = lane >> 4;
     // wave index as a scalar: every branch on it is wave-uniform, so no MFMA is
     // ever issued under a partial or empty EXEC mask
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int th = threadIdx.x, tr = th >> 2, tq = th & 3;   // tile-row role of this thread
     const int bh = blockIdx.y, c = blockIdx.x;
     const int64_t seg0 = (int64_t)c * a.chunk;
     const int64_t seg1 = seg0 + a.chunk < a.N ? seg0 + a.chunk : a.N;
@@ -463,24 +536,58 @@ __global__ __launch_bounds__(NT) void k_pass(PassArgs a) {
     const elem* W = reinterpret_cast<const elem*>(a.W);
     const elem* WTp = reinterpret_cast<const elem*>(a.WTp);
     const bool causal = a.causal != 0;
+    elem* s_w = LD::W_LDS ? lds + LD::o_w : nullptr;
+    if (LD::W_LDS) stage_w<C>(W, a.L, s_w);
+    zero_pads<C>(s_ZT, BWD ? s_zr : nullptr, BWD ? s_yr : nullptr);
+    const WSrc<C> wsrc{s_w, W, a.L};
 
     f32x4 Macc[C::NKC * 2], Zacc[C::NOWN * 2];
     load_state<C>(a.state + bh * a.state_bh_stride + c * a.state_chunk_stride, w, ln, g, Macc, Zacc);
 
     const int nsub = (int)((seg1 - seg0 + TB - 1) / TB);
+    const int my = 16 * w + ln;              // own token within the sub-block
+
+    // prefetch registers (one sub-block ahead)
+    frag n_xa[2], n_xb[2], n_z[2], n_y[2];
+    float n_d = 1.f, n_e = 0.f;
+    auto issue = [&](int it2) {
+        const int sb2 = REV ? nsub - 1 - it2 : it2;
+        const int64_t t0 = seg0 + (int64_t)sb2 * TB;
+        const int nv = (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
+        load_row_raw<C::F32>(a.Xa, base + t0 + my, my < nv, g, n_xa);
+        load_row_raw<C::F32>(a.Xb, base + t0 + my, my < nv, g, n_xb);
+        const bool ok = tr < nv;
+        load_q16_raw<C::F32>(a.Zsrc, (base + t0 + tr) * DH + 16 * tq, ok, n_z);
+        if constexpr (BWD) load_q16_raw<C::F32>(a.Ysrc, (base + t0 + tr) * DH + 16 * tq, ok, n_y);
+        if (REV && ok) {
+            n_d = a.Dv[base + t0 + tr];
+            n_e = a.Ev[base + t0 + tr];
+        }
+    };
+    issue(0);
+
     for (int it = 0; it < nsub; ++it) {
         const int sb = REV ? nsub - 1 - it : it;
         const int64_t t0 = seg0 + (int64_t)sb * TB;
         const int nv = (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
-        const int my = 16 * w + ln;              // own token within the sub-block
         const bool valid = my < nv;
         const size_t row = base + t0 + my;
+        const bool tok = tr < nv;
 
-        frag xa[2], xb[2];
+        frag xa[2] = {n_xa[0], n_xa[1]}, xb[2] = {n_xb[0], n_xb[1]};
+        frag zr[2] = {n_z[0], n_z[1]}, yr[2];
+        if constexpr (BWD) {
+            yr[0] = n_y[0];
+            yr[1] = n_y[1];
+        }
+        const float zd = n_d, ze = n_e;
+        if (it + 1 < nsub) issue(it + 1);
+
         float inv_a, nrm_a, inv_b, nrm_b;
-        load_x<C::F32>(a.Xa, row, valid, g, xa, inv_a, nrm_a);
-        load_x<C::F32>(a.Xb, row, valid, g, xb, inv_b, nrm_b);
-        load_aug<C>(a.Zsrc, a.Dv, a.Ev, REV ? 1 : 0, base + t0, nv, s_ZT, BWD ? s_zr : nullptr);
+        row_norm<C::F32>(xa, inv_a, nrm_a);
+        row_norm<C::F32>(xb, inv_b, nrm_b);
+        if (REV) write_aug<C>(zr, tok ? rcp_(zd) : 0.f, tok ? ze : 0.f, s_ZT, s_zr);
+        else write_aug<C>(zr, 1.f, tok ? 1.f : 0.f, s_ZT, BWD ? s_zr : nullptr);
 
         f32x4 Y[4], Dacc[4], Sc[4];
 #pragma unroll
@@ -492,17 +599,11 @@ __global__ __launch_bounds__(NT) void k_pass(PassArgs a) {
         // ----------------------------- phase 1 -------------------------------
 #pragma unroll
         for (int fb = 0; fb < C::NBLK; ++fb) {
-            frag phiA[C::FBK], phiB[C::FBK];
-            block_features<C>(W, fb, lane, w, ln, g, xa, inv_a, true, a.beta, a.L, s_rows, nullptr, phiA);
-            block_features<C>(W, fb, lane, w, ln, g, xb, inv_b, valid, a.beta, a.L, s_brow,
-                              (!BWD && causal) ? s_cols : nullptr, phiB);
+            frag phiA[C::FBK], unused[C::FBK];
+            block_features<C, true>(wsrc, fb, lane, w, ln, g, xa, inv_a, true, a.beta, a.L, s_rows, nullptr, phiA);
+            block_features<C, false>(wsrc, fb, lane, w, ln, g, xb, inv_b, valid, a.beta, a.L, s_brow,
+                                     (!BWD && causal) ? s_cols : nullptr, unused);
             __syncthreads();
-            frag zt[2], zm[2];
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                zt[s] = ld_frag<C::F32>(s_ZT + (16 * w + ln) * C::ROWT + 32 * s + 8 * g);
-                zm[s] = ld_frag<C::F32>(s_ZT + (64 + ln) * C::ROWT + 32 * s + 8 * g);
-            }
             if (causal) {
 #pragma unroll
                 for (int bt = 0; bt < 4; ++bt) {
@@ -519,34 +620,18 @@ __global__ __launch_bounds__(NT) void k_pass(PassArgs a) {
             for (int kcl = 0; kcl < C::FBK; ++kcl) {
                 const int kc = fb * C::FBK + kcl;
                 const frag mf = pack<C::F32>(Macc[2 * kc], Macc[2 * kc + 1]);
-                const bool own = (kc & 3) == w;
-                frag zf;
-                if constexpr (MODE != MODE_BWD_K) zf = pack<C::F32>(Zacc[2 * (kc >> 2)], Zacc[2 * (kc >> 2) + 1]);
 #pragma unroll
-                for (int at = 0; at < 4; ++at) {
-                    const frag af = ld_frag<C::F32>(s_rows + (16 * at + ln) * C::ROWF + 32 * kcl + 8 * g);
-                    Y[at] = mma(af, mf, Y[at]);
-                    if constexpr (MODE != MODE_BWD_K)
-                        if (own) Dacc[at] = mma(af, zf, Dacc[at]);
-                }
+                for (int at = 0; at < 4; ++at)
+                    Y[at] = mma(ld_frag<C::F32>(s_rows + (16 * at + ln) * C::ROWF + 32 * kcl + 8 * g), mf, Y[at]);
+            }
+            if (MODE != MODE_BWD_K && w < C::FBK) {
+                const frag zf = pack<C::F32>(Zacc[2 * fb], Zacc[2 * fb + 1]);
+#pragma unroll
+                for (int at = 0; at < 4; ++at)
+                    Dacc[at] = mma(ld_frag<C::F32>(s_rows + (16 * at + ln) * C::ROWF + 32 * w + 8 * g), zf, Dacc[at]);
             }
             if constexpr (MODE == MODE_FWD) {
-                if (causal) {
-#pragma unroll
-                    for (int kcl = 0; kcl < C::FBK; ++kcl) {
-                        const int kc = fb * C::FBK + kcl;
-#pragma unroll
-                        for (int h = 0; h < 2; ++h) {
-                            const elem* arow = s_cols + (32 * kcl + canon_of_row(h, ln)) * C::ROWT + 8 * g;
-#pragma unroll
-                            for (int s = 0; s < 2; ++s) {
-                                const frag af = ld_frag<C::F32>(arow + 32 * s);
-                                Macc[2 * kc + h] = mma(af, zt[s], Macc[2 * kc + h]);
-                                if ((kc & 3) == w) Zacc[2 * (kc >> 2) + h] = mma(af, zm[s], Zacc[2 * (kc >> 2) + h]);
-                            }
-                        }
-                    }
-                }
+                if (causal) sketch_update<C>(fb, w, ln, g, s_cols, s_ZT, Macc, Zacc);
             }
             __syncthreads();
         }
@@ -590,7 +675,7 @@ __global__ __launch_bounds__(NT) void k_pass(PassArgs a) {
         }
         // ----------------------- readout epilogues ----------------------------
         if constexpr (MODE == MODE_FWD || MODE == MODE_BWD_Q) {
-            float Dr[4][4];
+            float rD[4][4];
 #pragma unroll
             for (int at = 0; at < 4; ++at)
 #pragma unroll
@@ -598,77 +683,58 @@ __global__ __launch_bounds__(NT) void k_pass(PassArgs a) {
                     const int r = 16 * at + 4 * g + i;
                     float d = f_Dpart[r] + f_Dpart[TB + r] + f_Dpart[2 * TB + r] + f_Dpart[3 * TB + r];
                     if (causal) d += f_Dint[r];
-                    Dr[at][i] = d;
+                    rD[at][i] = rcp_(d);
                 }
             if constexpr (MODE == MODE_FWD) {
 #pragma unroll
                 for (int at = 0; at < 4; ++at)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        s_stage[(16 * at + 4 * g + i) * C::ROWD + 16 * w + ln] = to_elem<C::F32>(Y[at][i] / Dr[at][i]);
+                        s_stage[(16 * at + 4 * g + i) * C::ROWD + 16 * w + ln] = to_elem<C::F32>(Y[at][i] * rD[at][i]);
                 __syncthreads();
-                {
-                    const int th = threadIdx.x, r = th >> 2, q = th & 3;
-                    if (r < nv) {
-                        using T = typename In<C::F32>::T;
-                        T* o = reinterpret_cast<T*>(a.out0) + (base + t0 + r) * DH + 16 * q;
-                        const elem* src = s_stage + r * C::ROWD + 16 * q;
-                        *reinterpret_cast<frag*>(o) = ld_frag<C::F32>(src);
-                        *reinterpret_cast<frag*>(o + 8) = ld_frag<C::F32>(src + 8);
-                    }
+                if (tok) {
+                    T* o = reinterpret_cast<T*>(a.out0) + (base + t0 + tr) * DH + 16 * tq;
+                    const elem* src = s_stage + tr * C::ROWD + 16 * tq;
+                    *reinterpret_cast<frag*>(o) = ld_frag<C::F32>(src);
+                    *reinterpret_cast<frag*>(o + 8) = ld_frag<C::F32>(src + 8);
                 }
                 __syncthreads();
                 continue;
             } else {
                 // BWD_Q: O, delta = <dO, O>, e = -delta / D, y = [dO / D | e]
-                {
-                    const int th = threadIdx.x, r = th >> 2, q = th & 3;
-                    float v[16];
-                    if (r < nv) load16<C::F32>(a.Ysrc, (base + t0 + r) * DH + 16 * q, v);
-                    else
-#pragma unroll
-                        for (int cc = 0; cc < 16; ++cc) v[cc] = 0.f;
-                    st_frag<C::F32>(s_stage + r * C::ROWD + 16 * q, pack8<C::F32>(v));
-                    st_frag<C::F32>(s_stage + r * C::ROWD + 16 * q + 8, pack8<C::F32>(v + 8));
-                }
+                st_frag<C::F32>(s_stage + tr * C::ROWD + 16 * tq, yr[0]);
+                st_frag<C::F32>(s_stage + tr * C::ROWD + 16 * tq + 8, yr[1]);
                 __syncthreads();
 #pragma unroll
                 for (int at = 0; at < 4; ++at)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int r = 16 * at + 4 * g + i;
-                        const float o = Y[at][i] / Dr[at][i];
+                        const float o = Y[at][i] * rD[at][i];
                         float p = o * elem_f<C::F32>(s_stage[r * C::ROWD + 16 * w + ln]);
                         p = sum_row16(p);
                         if (ln == 0) f_dpart[w * TB + r] = p;
                     }
                 __syncthreads();
                 {
-                    const int th = threadIdx.x, r = th >> 2, q = th & 3;
-                    const bool ok = r < nv;
                     float D = 1.f, e = 0.f;
-                    if (ok) {
-                        D = f_Dpart[r] + f_Dpart[TB + r] + f_Dpart[2 * TB + r] + f_Dpart[3 * TB + r] +
-                            (causal ? f_Dint[r] : 0.f);
-                        const float delta = f_dpart[r] + f_dpart[TB + r] + f_dpart[2 * TB + r] + f_dpart[3 * TB + r];
-                        e = -delta / D;
+                    if (tok) {
+                        D = f_Dpart[tr] + f_Dpart[TB + tr] + f_Dpart[2 * TB + tr] + f_Dpart[3 * TB + tr] +
+                            (causal ? f_Dint[tr] : 0.f);
+                        const float delta = f_dpart[tr] + f_dpart[TB + tr] + f_dpart[2 * TB + tr] + f_dpart[3 * TB + tr];
+                        e = -delta * rcp_(D);
                     }
-                    const float invD = ok ? 1.f / D : 0.f;
+                    const float sc = tok ? rcp_(D) : 0.f;
                     float v[16];
 #pragma unroll
-                    for (int cc = 0; cc < 16; ++cc) v[cc] = elem_f<C::F32>(s_stage[r * C::ROWD + 16 * q + cc]) * invD;
-                    st_frag<C::F32>(s_yr + r * C::ROWE + 16 * q, pack8<C::F32>(v));
-                    st_frag<C::F32>(s_yr + r * C::ROWE + 16 * q + 8, pack8<C::F32>(v + 8));
-                    if (q == 0) {
-                        float m[8] = {e, 0, 0, 0, 0, 0, 0, 0};
-                        float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-                        st_frag<C::F32>(s_yr + r * C::ROWE + 64, pack8<C::F32>(m));
-                        st_frag<C::F32>(s_yr + r * C::ROWE + 72, pack8<C::F32>(z));
-                        st_frag<C::F32>(s_yr + r * C::ROWE + 80, pack8<C::F32>(z));
-                        st_frag<C::F32>(s_yr + r * C::ROWE + 88, pack8<C::F32>(z));
-                        if (ok) {
-                            a.Dv[base + t0 + r] = D;
-                            a.Ev[base + t0 + r] = e;
+                    for (int cc = 0; cc < 16; ++cc) v[cc] = q16_at<C::F32>(yr, cc) * sc;
+                    st_frag<C::F32>(s_yr + tr * C::ROWE + 16 * tq, pack8<C::F32>(v));
+                    st_frag<C::F32>(s_yr + tr * C::ROWE + 16 * tq + 8, pack8<C::F32>(v + 8));
+                    if (tq == 0) {
+                        s_yr[tr * C::ROWE + 64] = to_elem<C::F32>(e);
+                        if (tok) {
+                            a.Dv[base + t0 + tr] = D;
+                            a.Ev[base + t0 + tr] = e;
                         }
                     }
                 }
@@ -682,35 +748,19 @@ __global__ __launch_bounds__(NT) void k_pass(PassArgs a) {
                 for (int i = 0; i < 4; ++i)
                     s_stage[(16 * at + 4 * g + i) * C::ROWD + 16 * w + ln] = to_elem<C::F32>(Y[at][i]);
             {
-                // y rows = [v | 1 | 0]
-                const int th = threadIdx.x, r = th >> 2, q = th & 3;
                 float v[16];
-                const bool ok = r < nv;
-                if (ok) load16<C::F32>(a.Ysrc, (base + t0 + r) * DH + 16 * q, v);
-                else
 #pragma unroll
-                    for (int cc = 0; cc < 16; ++cc) v[cc] = 0.f;
-                st_frag<C::F32>(s_yr + r * C::ROWE + 16 * q, pack8<C::F32>(v));
-                st_frag<C::F32>(s_yr + r * C::ROWE + 16 * q + 8, pack8<C::F32>(v + 8));
-                if (q == 0) {
-                    float m[8] = {ok ? 1.f : 0.f, 0, 0, 0, 0, 0, 0, 0};
-                    float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-                    st_frag<C::F32>(s_yr + r * C::ROWE + 64, pack8<C::F32>(m));
-                    st_frag<C::F32>(s_yr + r * C::ROWE + 72, pack8<C::F32>(z));
-                    st_frag<C::F32>(s_yr + r * C::ROWE + 80, pack8<C::F32>(z));
-                    st_frag<C::F32>(s_yr + r * C::ROWE + 88, pack8<C::F32>(z));
-                }
+                for (int cc = 0; cc < 16; ++cc) v[cc] = q16_at<C::F32>(yr, cc);
+                st_frag<C::F32>(s_yr + tr * C::ROWE + 16 * tq, pack8<C::F32>(v));
+                st_frag<C::F32>(s_yr + tr * C::ROWE + 16 * tq + 8, pack8<C::F32>(v + 8));
+                if (tq == 0) s_yr[tr * C::ROWE + 64] = to_elem<C::F32>(tok ? 1.f : 0.f);
             }
             __syncthreads();
-            {
-                const int th = threadIdx.x, r = th >> 2, q = th & 3;
-                if (r < nv) {
-                    using T = typename In<C::F32>::T;
-                    T* o = reinterpret_cast<T*>(a.out1) + (base + t0 + r) * DH + 16 * q;
-                    const elem* src = s_stage + r * C::ROWD + 16 * q;
-                    *reinterpret_cast<frag*>(o) = ld_frag<C::F32>(src);
-                    *reinterpret_cast<frag*>(o + 8) = ld_frag<C::F32>(src + 8);
-                }
+            if (tok) {
+                T* o = reinterpret_cast<T*>(a.out1) + (base + t0 + tr) * DH + 16 * tq;
+                const elem* src = s_stage + tr * C::ROWD + 16 * tq;
+                *reinterpret_cast<frag*>(o) = ld_frag<C::F32>(src);
+                *reinterpret_cast<frag*>(o + 8) = ld_frag<C::F32>(src + 8);
             }
             __syncthreads();
         }
@@ -765,13 +815,21 @@ __global__ __launch_bounds__(NT) void k_pass(PassArgs a) {
                         for (int i = 0; i < 4; ++i) {
                             const int fl = 32 * kcl + 8 * g + 4 * h + i;
                             s_ms[fl * C::ROWE + 16 * w + ln] = to_elem<C::F32>(Macc[2 * kc + h][i]);
-                            if ((kc & 3) == w && ln == 0)
-                                s_ms[fl * C::ROWE + 64] = to_elem<C::F32>(Zacc[2 * (kc >> 2) + h][i]);
                         }
                 }
+                if (w < C::FBK && ln == 0) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            s_ms[(32 * w + 8 * g + 4 * h + i) * C::ROWE + 64] = to_elem<C::F32>(Zacc[2 * fb + h][i]);
+                }
                 // b-side features (own tile) -> transposed tile
-                frag phiB[C::FBK];
-                block_features<C>(W, fb, lane, w, ln, g, xb, inv_b, valid, a.beta, a.L, nullptr, s_cols, phiB);
+                {
+                    frag unused[C::FBK];
+                    block_features<C, false>(wsrc, fb, lane, w, ln, g, xb, inv_b, valid, a.beta, a.L, nullptr, s_cols,
+                                             unused);
+                }
                 __syncthreads();
                 f32x4 G[C::FBK * 2];
 #pragma unroll
@@ -795,7 +853,7 @@ __global__ __launch_bounds__(NT) void k_pass(PassArgs a) {
 #pragma unroll
                 for (int tb = 0; tb < C::TPB; ++tb) {
                     const int t = fb * C::TPB + tb;
-                    const f32x4 acc = project<C>(W, a.L, t, ln, g, xa);
+                    const f32x4 acc = wsrc.project(t, lane, ln, g, xa);
                     float hs[4], phi[C::KB * 8], u[4], s[4], dA[C::KB * 8], dh[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) hs[i] = acc[i] * inv_a;
@@ -822,28 +880,7 @@ __global__ __launch_bounds__(NT) void k_pass(PassArgs a) {
                     }
                 }
                 // sketch update for this block
-                if (causal) {
-                    frag zt[2], zm[2];
-#pragma unroll
-                    for (int s = 0; s < 2; ++s) {
-                        zt[s] = ld_frag<C::F32>(s_ZT + (16 * w + ln) * C::ROWT + 32 * s + 8 * g);
-                        zm[s] = ld_frag<C::F32>(s_ZT + (64 + ln) * C::ROWT + 32 * s + 8 * g);
-                    }
-#pragma unroll
-                    for (int kcl = 0; kcl < C::FBK; ++kcl) {
-                        const int kc = fb * C::FBK + kcl;
-#pragma unroll
-                        for (int h = 0; h < 2; ++h) {
-                            const elem* arow = s_cols + (32 * kcl + canon_of_row(h, ln)) * C::ROWT + 8 * g;
-#pragma unroll
-                            for (int s = 0; s < 2; ++s) {
-                                const frag af = ld_frag<C::F32>(arow + 32 * s);
-                                Macc[2 * kc + h] = mma(af, zt[s], Macc[2 * kc + h]);
-                                if ((kc & 3) == w) Zacc[2 * (kc >> 2) + h] = mma(af, zm[s], Zacc[2 * (kc >> 2) + h]);
-                            }
-                        }
-                    }
-                }
+                if (causal) sketch_update<C>(fb, w, ln, g, s_cols, s_ZT, Macc, Zacc);
                 __syncthreads();
             }
             // dx = (dx_hat - x_hat <x_hat, dx_hat>) / |x|
@@ -911,11 +948,12 @@ __global__ __launch_bounds__(NT) void k_hash(const void* X, const void* Wv, int6
     const elem* W = reinterpret_cast<const elem*>(Wv);
     frag xf[2];
     float inv, nrm;
-    load_x<C::F32>(X, valid ? (size_t)r : 0, valid, g, xf, inv, nrm);
+    load_row_raw<C::F32>(X, valid ? (size_t)r : 0, valid, g, xf);
+    row_norm<C::F32>(xf, inv, nrm);
     unsigned int nz = 0;
 #pragma unroll
     for (int t = 0; t < C::MT; ++t) {
-        const f32x4 acc = project<C>(W, L, t, ln, g, xf);
+        const f32x4 acc = project_global<C>(W, L, t, ln, g, xf);
 #pragma unroll
         for (int tl = 0; tl < C::TPL; ++tl) {
             const int table = t * C::TPT + g * C::TPL + tl;
