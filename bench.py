@@ -202,6 +202,8 @@ def main():
         "layer_roofline": {"bound": "hbm" if layer["bytes"] * units / HBM_PEAK >= layer["flops"] * units / peak_f
                            else "mfma", "frac": layer_t / (ms_step / 1e3),
                            "alg_bytes_per_token_head": layer["bytes"], "alg_flops_per_token_head": layer["flops"]},
+        "hbm_peak_GiB": torch.cuda.max_memory_allocated() / 2**30,
+        "hbm_capacity_GiB": torch.cuda.get_device_properties(0).total_memory / 2**30,
         "stages_ms_per_step": {k: v / args.steps for k, v in sorted(stage_ms.items(), key=lambda kv: -kv[1])},
         "wall_s_timed": wall,
     }

@@ -211,15 +211,18 @@ __device__ inline void load_state(const float* __restrict__ st, int w, int ln, i
                 const int f = 32 * kc + 8 * g + 4 * h + i;
                 Macc[2 * kc + h][i] = st[(size_t)f * DH + 16 * w + ln];
             }
+    const bool owner = w < C::FBK && ln == 0;   // waves w >= FBK own no mass chunk
 #pragma unroll
     for (int fb = 0; fb < C::NBLK; ++fb) {
-        const int kc = fb * C::FBK + w;
+        const int kc = fb * C::FBK + (owner ? w : 0);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int f = 32 * kc + 8 * g + 4 * h + i;
-                Zacc[2 * fb + h][i] = (w < C::FBK && ln == 0) ? st[(size_t)C::F * DH + f] : 0.f;
+                float v = 0.f;
+                if (owner) v = st[(size_t)C::F * DH + f];
+                Zacc[2 * fb + h][i] = v;
             }
     }
 }
@@ -368,6 +371,7 @@ __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
     const size_t base = (size_t)bh * a.N;
     stage_w<C>(reinterpret_cast<const elem*>(a.W), a.L, s_w);
     zero_pads<C>(s_ZT, nullptr, nullptr);
+    __syncthreads();   // W' and the padding are written by all waves, read by each
     const WSrc<C> wsrc{s_w, reinterpret_cast<const elem*>(a.W), a.L};
 
     f32x4 Macc[C::NKC * 2], Zacc[C::NOWN * 2];
@@ -477,6 +481,11 @@ struct PassLds {
     static constexpr int n_sc = TB * C::ROWT;                   // intra scores [a][b]
     static constexpr int n_zr = BWD ? TB * C::ROWE : 0;         // z_b rows
     static constexpr int n_yr = BWD ? TB * C::ROWE : 0;         // y_a rows
+    // bf16 residual of the query-side y rows ([g | e]): the intra-sub-block
+    // product g.v + e cancels for the first keys of a sequence, so it is
+    // formed from y = hi + lo in fp32 accumulation
+    static constexpr bool YLO = MODE == MODE_BWD_Q && !C::F32;
+    static constexpr int n_ylo = YLO ? TB * C::ROWE : 0;
     // aliases of [rows | brow] after the feature-block loop of phase 1
     static constexpr int n_ms = C::FBK * 32 * C::ROWE;          // sketch rows (phase 2)
     static constexpr int n_stage = TB * C::ROWD;                // O / dV / dO staging
@@ -489,8 +498,9 @@ struct PassLds {
     static constexpr int o_sc = o_zt + n_zt;
     static constexpr int o_zr = o_sc + n_sc;
     static constexpr int o_yr = o_zr + n_zr;
+    static constexpr int o_ylo = o_yr + n_yr;
     static constexpr int n_float = 4 * TB + 4 * TB + TB;      // Dpart, dpart, Dint
-    static constexpr int base_elem = o_yr + n_yr;
+    static constexpr int base_elem = o_ylo + n_ylo;
     // W' staged in LDS when it fits (else projections read it from global memory)
     static constexpr int n_w0 = C::MT * 1024;
     static constexpr bool W_LDS = (base_elem + n_w0) * (int)sizeof(elem) + n_float * 4 <= 160 * 1024;
@@ -518,6 +528,7 @@ __global__ __launch_bounds__(NT) void k_pass(PassArgs a) {
     elem* s_sc = lds + LD::o_sc;
     elem* s_zr = lds + LD::o_zr;
     elem* s_yr = lds + LD::o_yr;
+    elem* s_ylo = lds + LD::o_ylo;
     elem* s_ms = lds + LD::o_rows;      // phase-2 alias
     elem* s_stage = lds + LD::o_rows;   // staging alias
     float* f_Dpart = ldf;               // [4][64]
@@ -539,6 +550,8 @@ __global__ __launch_bounds__(NT) void k_pass(PassArgs a) {
     elem* s_w = LD::W_LDS ? lds + LD::o_w : nullptr;
     if (LD::W_LDS) stage_w<C>(W, a.L, s_w);
     zero_pads<C>(s_ZT, BWD ? s_zr : nullptr, BWD ? s_yr : nullptr);
+    if (LD::YLO) zero_pads<C>(s_ZT, s_ylo, nullptr);
+    __syncthreads();   // W' and the padding are written by all waves, read by each
     const WSrc<C> wsrc{s_w, W, a.L};
 
     f32x4 Macc[C::NKC * 2], Zacc[C::NOWN * 2];
@@ -728,10 +741,23 @@ __global__ __launch_bounds__(NT) void k_pass(PassArgs a) {
                     float v[16];
 #pragma unroll
                     for (int cc = 0; cc < 16; ++cc) v[cc] = q16_at<C::F32>(yr, cc) * sc;
-                    st_frag<C::F32>(s_yr + tr * C::ROWE + 16 * tq, pack8<C::F32>(v));
-                    st_frag<C::F32>(s_yr + tr * C::ROWE + 16 * tq + 8, pack8<C::F32>(v + 8));
+                    const frag h0 = pack8<C::F32>(v), h1 = pack8<C::F32>(v + 8);
+                    st_frag<C::F32>(s_yr + tr * C::ROWE + 16 * tq, h0);
+                    st_frag<C::F32>(s_yr + tr * C::ROWE + 16 * tq + 8, h1);
+                    if constexpr (LD::YLO) {
+                        float lo[16];
+#pragma unroll
+                        for (int cc = 0; cc < 8; ++cc) {
+                            lo[cc] = v[cc] - elem_f<C::F32>(h0[cc]);
+                            lo[8 + cc] = v[8 + cc] - elem_f<C::F32>(h1[cc]);
+                        }
+                        st_frag<C::F32>(s_ylo + tr * C::ROWE + 16 * tq, pack8<C::F32>(lo));
+                        st_frag<C::F32>(s_ylo + tr * C::ROWE + 16 * tq + 8, pack8<C::F32>(lo + 8));
+                    }
                     if (tq == 0) {
-                        s_yr[tr * C::ROWE + 64] = to_elem<C::F32>(e);
+                        const elem eh = to_elem<C::F32>(e);
+                        s_yr[tr * C::ROWE + 64] = eh;
+                        if constexpr (LD::YLO) s_ylo[tr * C::ROWE + 64] = to_elem<C::F32>(e - elem_f<C::F32>(eh));
                         if (tok) {
                             a.Dv[base + t0 + tr] = D;
                             a.Ev[base + t0 + tr] = e;
@@ -778,8 +804,12 @@ __global__ __launch_bounds__(NT) void k_pass(PassArgs a) {
                     const bool vis = REV ? (bt >= w) : (bt <= w);
                     if (vis) {
 #pragma unroll
-                        for (int s = 0; s < 3; ++s)
-                            Cc[bt] = mma(ld_frag<C::F32>(s_zr + (16 * bt + ln) * C::ROWE + 32 * s + 8 * g), yf[s], Cc[bt]);
+                        for (int s = 0; s < 3; ++s) {
+                            const frag zf = ld_frag<C::F32>(s_zr + (16 * bt + ln) * C::ROWE + 32 * s + 8 * g);
+                            Cc[bt] = mma(zf, yf[s], Cc[bt]);
+                            if constexpr (LD::YLO)
+                                Cc[bt] = mma(zf, ld_frag<C::F32>(s_ylo + my * C::ROWE + 32 * s + 8 * g), Cc[bt]);
+                        }
                     }
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -805,24 +835,53 @@ __global__ __launch_bounds__(NT) void k_pass(PassArgs a) {
             f32x4 dhp[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
             for (int fb = 0; fb < C::NBLK; ++fb) {
-                // sketch rows of this block (before this sub-block's update)
+                // sketch rows of this block (before this sub-block's update). Only
+                // dA - <a, dA> per table is used below, so each table's corner mean is
+                // subtracted in fp32 first: the bf16 operand then carries the part that
+                // survives instead of a large common offset. A lane holds every corner
+                // of its tables for its value column.
 #pragma unroll
-                for (int kcl = 0; kcl < C::FBK; ++kcl) {
-                    const int kc = fb * C::FBK + kcl;
+                for (int tb = 0; tb < C::TPB; ++tb) {
+                    float v[C::KB * 8];
 #pragma unroll
-                    for (int h = 0; h < 2; ++h)
+                    for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int fl = 32 * kcl + 8 * g + 4 * h + i;
-                            s_ms[fl * C::ROWE + 16 * w + ln] = to_elem<C::F32>(Macc[2 * kc + h][i]);
-                        }
+                        for (int h = 0; h < 2; ++h)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                v[kb * 8 + 4 * h + i] = Macc[2 * (fb * C::FBK + tb * C::KB + kb) + h][i];
+                    constexpr int RR = (C::P == 4) ? 16 : C::R;
+#pragma unroll
+                    for (int t0c = 0; t0c < C::KB * 8; t0c += RR) {
+                        float m = 0.f;
+#pragma unroll
+                        for (int r = 0; r < RR; ++r) m += v[t0c + r];
+                        m *= 1.f / (float)RR;
+#pragma unroll
+                        for (int r = 0; r < RR; ++r) v[t0c + r] -= m;
+                    }
+#pragma unroll
+                    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const int fl = 32 * (tb * C::KB + kb) + 8 * g + 4 * h + i;
+                                s_ms[fl * C::ROWE + 16 * w + ln] = to_elem<C::F32>(v[kb * 8 + 4 * h + i]);
+                            }
                 }
                 if (w < C::FBK && ln == 0) {
+                    // Query side: every table's masses sum to the number n of keys in the
+                    // state, so z_r = n/R + (small fluctuation). A per-table constant in dA
+                    // cancels in a * (dA - <a, dA>), so store z_r - n/R: the bf16 operand
+                    // then keeps the fluctuation instead of rounding it away at large n.
+                    const float zshift = (MODE == MODE_BWD_Q) ? (causal ? (float)t0 : (float)a.N) / (float)C::R : 0.f;
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
-                            s_ms[(32 * w + 8 * g + 4 * h + i) * C::ROWE + 64] = to_elem<C::F32>(Zacc[2 * fb + h][i]);
+                            s_ms[(32 * w + 8 * g + 4 * h + i) * C::ROWE + 64] =
+                                to_elem<C::F32>(Zacc[2 * fb + h][i] - zshift);
                 }
                 // b-side features (own tile) -> transposed tile
                 {
