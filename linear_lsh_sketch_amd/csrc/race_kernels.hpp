@@ -423,27 +423,35 @@ __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
 template <int KIND>
 __global__ __launch_bounds__(256) void k_scan(float* __restrict__ st, float* __restrict__ total,
                                               int nchunks, int elems) {
+    // Loads of a batch of chunks are issued together so the memory round trip
+    // is paid once per batch, not once per chunk; the running sum keeps the
+    // fixed chunk order (deterministic).
+    constexpr int BATCH = 16;
     const int e = blockIdx.x * blockDim.x + threadIdx.x;
     const int bh = blockIdx.y;
     if (e >= elems) return;
     float* p = st + (size_t)bh * nchunks * elems + e;
     float run = 0.f;
-    if constexpr (KIND == SCAN_EXCL) {
-        for (int c = 0; c < nchunks; ++c) {
-            const float v = p[(size_t)c * elems];
-            p[(size_t)c * elems] = run;
-            run += v;
+    const int nfull = nchunks / BATCH * BATCH;
+    for (int c0 = 0; c0 < nchunks; c0 += BATCH) {
+        float v[BATCH];
+        const int n = c0 < nfull ? BATCH : nchunks - c0;
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) {
+            const int kk = k < n ? k : 0;
+            const int c = (KIND == SCAN_REV_EXCL) ? nchunks - 1 - (c0 + kk) : c0 + kk;
+            v[k] = p[(size_t)c * elems];
         }
-    } else if constexpr (KIND == SCAN_REV_EXCL) {
-        for (int c = nchunks - 1; c >= 0; --c) {
-            const float v = p[(size_t)c * elems];
-            p[(size_t)c * elems] = run;
-            run += v;
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) {
+            if (k < n) {
+                const int c = (KIND == SCAN_REV_EXCL) ? nchunks - 1 - (c0 + k) : c0 + k;
+                if constexpr (KIND != SCAN_TOTAL) p[(size_t)c * elems] = run;
+                run += v[k];
+            }
         }
-    } else {
-        for (int c = 0; c < nchunks; ++c) run += p[(size_t)c * elems];
-        total[(size_t)bh * elems + e] = run;
     }
+    if constexpr (KIND == SCAN_TOTAL) total[(size_t)bh * elems + e] = run;
 }
 
 // ---------------------------------------------------------------------------
@@ -501,9 +509,12 @@ struct PassLds {
     static constexpr int o_ylo = o_yr + n_yr;
     static constexpr int n_float = 4 * TB + 4 * TB + TB;      // Dpart, dpart, Dint
     static constexpr int base_elem = o_ylo + n_ylo;
+    // Target workgroups per CU: the forward pass runs two (its VGPR budget is
+    // capped at 256 so two waves share each SIMD and hide each other's latency).
+    static constexpr int OCC = (MODE == MODE_FWD && !C::F32 && C::NKC <= 8) ? 2 : 1;
     // W' staged in LDS when it fits (else projections read it from global memory)
     static constexpr int n_w0 = C::MT * 1024;
-    static constexpr bool W_LDS = (base_elem + n_w0) * (int)sizeof(elem) + n_float * 4 <= 160 * 1024;
+    static constexpr bool W_LDS = ((base_elem + n_w0) * (int)sizeof(elem) + n_float * 4) * OCC <= 160 * 1024;
     static constexpr int n_w = W_LDS ? n_w0 : 0;
     static constexpr int o_w = base_elem;
     static constexpr int n_elem = base_elem + n_w;
@@ -512,7 +523,7 @@ struct PassLds {
 };
 
 template <class C, int MODE>
-__global__ __launch_bounds__(NT) void k_pass(PassArgs a) {
+__global__ __launch_bounds__(NT, (PassLds<C, MODE>::OCC)) void k_pass(PassArgs a) {
     using elem = typename Prec<C::F32>::elem;
     using frag = typename Prec<C::F32>::frag;
     using LD = PassLds<C, MODE>;
