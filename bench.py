@@ -2,7 +2,8 @@
 
 One step = forward + backward of the whole RACE MHA layer core (all heads)
 over one batch of synthetic input already resident in HBM: race_attn_fwd
-(keeping the per-chunk sketch states) then race_attn_bwd (reusing them).
+(keeping the per-chunk sketch states and per-token denominators) then
+race_attn_bwd (reusing them with O).
 
 Default workload: causal, B=1, H=4, N=12,000,000, d=64, P=4, L=16,
 chunk=1024, bf16 inputs with float32 sketches; Q, K, V, dO iid N(0,1) from
@@ -119,8 +120,8 @@ def main():
     t["W"] = synth.normal_device(w.seed, synth.TID_W, torch.empty((w.L, w.P, w.d), dtype=tdt, device=dev))
     O = torch.empty(shape, dtype=tdt, device=dev)
     grads = tuple(torch.empty(shape, dtype=tdt, device=dev) for _ in range(3))
-    ws_f = race.alloc_workspace(w.B, w.H, w.N, w.P, w.L, w.causal, w.chunk, False, dev)
-    ws_b = race.alloc_workspace(w.B, w.H, w.N, w.P, w.L, w.causal, w.chunk, True, dev)
+    ws_f = race.alloc_workspace(w.B, w.H, w.N, w.P, w.L, w.causal, w.chunk, race.WS_FWD, dev)
+    ws_b = race.alloc_workspace(w.B, w.H, w.N, w.P, w.L, w.causal, w.chunk, race.WS_BWD, dev)
     saved = race.alloc_saved(w.B, w.H, w.N, w.P, w.L, w.causal, w.chunk, dev)
     torch.cuda.synchronize()
 
@@ -128,7 +129,7 @@ def main():
         race.forward(t["Q"], t["K"], t["V"], t["W"], w.P, w.L, w.beta, w.causal, w.chunk, out=O,
                      saved=saved, ws=ws_f)
         race.backward(t["Q"], t["K"], t["V"], t["W"], t["dO"], w.P, w.L, w.beta, w.causal, w.chunk,
-                      saved=saved, ws=ws_b, grads=grads)
+                      O=O, saved=saved, ws=ws_b, grads=grads)
 
     for _ in range(args.warmup):
         step()
@@ -150,7 +151,7 @@ def main():
                                  out=O, saved=saved, ws=ws_f)
                 else:
                     race.backward(t["Q"], t["K"], t["V"], t["W"], t["dO"], w.P, w.L, w.beta, w.causal,
-                                  w.chunk, saved=saved, ws=ws_b, grads=grads)
+                                  w.chunk, O=O, saved=saved, ws=ws_b, grads=grads)
                 for name, ms in timer.stages():
                     stage_ms[name] = stage_ms.get(name, 0.0) + ms
                     stage_n[name] = stage_n.get(name, 0) + 1

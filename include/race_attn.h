@@ -77,24 +77,29 @@ typedef enum {
 
 typedef enum { RACE_F32 = 0, RACE_BF16 = 1 } race_dtype_t;
 
-/* Bytes of device workspace `ws` needed by race_attn_fwd (for_backward = 0)
- * or race_attn_bwd (for_backward = 1) for this shape. Writes *bytes.
- * Depends on dtype only through the element size of a small projection
- * table, so the value for RACE_F32 is an upper bound for both. */
+/* Bytes of device workspace `ws` for this shape. Writes *bytes.
+ *   for_backward = 0: race_attn_fwd;
+ *   for_backward = 1: race_attn_bwd given O and `saved` from the forward;
+ *   for_backward = 2: race_attn_bwd with O = saved = NULL (it then recomputes
+ *                     the forward into this workspace);
+ * any other value gives RACE_ERR_INVALID_ARG. The size depends on dtype only
+ * through element sizes, so it is computed for RACE_F32, an upper bound for
+ * both dtypes. */
 race_status_t race_attn_workspace_bytes(int64_t B, int64_t H, int64_t N, int d, int P, int L,
                                         int causal, int chunk, int for_backward, size_t *bytes);
 
-/* Bytes of the optional `saved` buffer: the float32 sketch state at the start
- * of every chunk (causal) or the whole-sequence sketch (non-causal), per
- * (batch, head). Layout is private to the library; pass the same buffer and
- * the same shape arguments to race_attn_bwd to skip recomputing it. */
+/* Bytes of the optional `saved` buffer a forward call fills for the backward:
+ * the float32 sketch state at the start of every chunk (causal) or the
+ * whole-sequence sketch (non-causal), then the float32 per-token softmax
+ * denominators D_i = sum_l sum_r a_l(q_i)[r] z_l[r] (the same quantity the
+ * output divides by), per (batch, head). Layout is private to the library. */
 race_status_t race_attn_saved_bytes(int64_t B, int64_t H, int64_t N, int d, int P, int L,
                                     int causal, int chunk, size_t *bytes);
 
 /* Forward: O = RACE-Attention(Q, K, V; W, P, L, temperature, causal).
  * `temperature` is the pages' beta: it multiplies the corner logits, so a
  * larger value gives harder bucket assignments. `saved` may be NULL; if not
- * NULL it receives the per-chunk sketch states (race_attn_saved_bytes).
+ * NULL it receives the sketch states and denominators (race_attn_saved_bytes).
  * `ws` must hold race_attn_workspace_bytes(..., for_backward = 0). */
 race_status_t race_attn_fwd(const void *Q, const void *K, const void *V, const void *W,
                             int64_t B, int64_t H, int64_t N, int d, int P, int L,
@@ -102,15 +107,20 @@ race_status_t race_attn_fwd(const void *Q, const void *K, const void *V, const v
                             void *O, void *saved, void *ws, size_t ws_bytes, void *stream);
 
 /* Backward: given dO = dLoss/dO, writes dQ, dK, dV (the exact gradients of
- * the forward above). `saved` may be NULL (states are recomputed) or the
- * buffer a forward call with identical arguments filled. The forward output
- * O is not needed: it is recomputed from the sketch states.
- * `ws` must hold race_attn_workspace_bytes(..., for_backward = 1). */
+ * the forward above; the pages train the layer end to end, Japanese
+ * gist.science page, section 2.2). With g_i = dO_i / D_i and
+ * e_i = -<dO_i, O_i> / D_i, the query side reads the key sketch with [g | e]
+ * and the key side reads the reverse sketch sum_i a(q_i)^T [g_i | e_i].
+ * O (the forward's output) and `saved` (the buffer that forward call filled,
+ * with identical arguments) are given together, or both NULL: then the
+ * forward is recomputed inside the call. Exactly one of them NULL gives
+ * RACE_ERR_INVALID_ARG. `ws` must hold race_attn_workspace_bytes(...,
+ * for_backward = 1) when they are given, (..., for_backward = 2) when not. */
 race_status_t race_attn_bwd(const void *Q, const void *K, const void *V, const void *W,
-                            const void *dO, const void *saved, int64_t B, int64_t H,
-                            int64_t N, int d, int P, int L, float temperature, int causal,
-                            int chunk, race_dtype_t dtype, void *dQ, void *dK, void *dV,
-                            void *ws, size_t ws_bytes, void *stream);
+                            const void *O, const void *dO, const void *saved, int64_t B,
+                            int64_t H, int64_t N, int d, int P, int L, float temperature,
+                            int causal, int chunk, race_dtype_t dtype, void *dQ, void *dK,
+                            void *dV, void *ws, size_t ws_bytes, void *stream);
 
 /* Hard-hash diagnostic (the beta -> infinity limit of the soft assignment):
  * bucket_ids[row, l] = sum_p [<W_lp, x_row / |x_row|> > 0] 2^p for the

@@ -44,7 +44,7 @@ def lib():
         L.race_attn_saved_bytes.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
         L.race_attn_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, fl, i32, i32, i32,
                                     vp, vp, vp, sz, vp]
-        L.race_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, fl, i32, i32,
+        L.race_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, fl, i32, i32,
                                     i32, vp, vp, vp, vp, sz, vp]
         L.race_attn_hash.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, i32, vp, vp, vp]
         L.race_attn_profile_events.argtypes = [vp, i32]
@@ -70,10 +70,15 @@ def _check(code: int, where: str):
         raise RaceError(code, where)
 
 
-def workspace_bytes(B, H, N, d, P, L, causal, chunk, for_backward) -> int:
+WS_FWD, WS_BWD, WS_BWD_RECOMPUTE = 0, 1, 2
+
+
+def workspace_bytes(B, H, N, d, P, L, causal, chunk, kind) -> int:
+    """Workspace bytes: kind 0 forward, 1 backward given O and saved, 2 backward
+    recomputing the forward (race_attn_workspace_bytes' for_backward)."""
     out = ctypes.c_size_t(0)
-    _check(lib().race_attn_workspace_bytes(B, H, N, d, P, L, int(bool(causal)), chunk,
-                                           int(bool(for_backward)), ctypes.byref(out)),
+    _check(lib().race_attn_workspace_bytes(B, H, N, d, P, L, int(bool(causal)), chunk, int(kind),
+                                           ctypes.byref(out)),
            "race_attn_workspace_bytes")
     return out.value
 
@@ -116,9 +121,9 @@ def _check_inputs(*ts):
             raise ValueError("tensors must be contiguous")
 
 
-def alloc_workspace(B, H, N, P, L, causal, chunk, for_backward, device):
+def alloc_workspace(B, H, N, P, L, causal, chunk, kind, device):
     import torch
-    n = workspace_bytes(B, H, N, 64, P, L, causal, chunk, for_backward)
+    n = workspace_bytes(B, H, N, 64, P, L, causal, chunk, kind)
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
 
@@ -140,7 +145,7 @@ def race_attn_fwd(Q, K, V, W, P, L, temperature=1.0, causal=False, chunk=1024, o
         raise ValueError("Q, K, V must share one shape")
     O = out if out is not None else torch.empty_like(Q)
     if ws is None:
-        ws = alloc_workspace(B, H, N, P, L, causal, chunk, False, Q.device)
+        ws = alloc_workspace(B, H, N, P, L, causal, chunk, WS_FWD, Q.device)
     code = lib().race_attn_fwd(_p(Q), _p(K), _p(V), _p(W), B, H, N, d, P, L, float(temperature),
                                int(bool(causal)), chunk, _dtype_code(Q), _p(O), _p(saved), _p(ws),
                                ws.numel(), _stream(stream))
@@ -148,20 +153,29 @@ def race_attn_fwd(Q, K, V, W, P, L, temperature=1.0, causal=False, chunk=1024, o
     return O
 
 
-def race_attn_bwd(Q, K, V, W, dO, P, L, temperature=1.0, causal=False, chunk=1024, saved=None,
+def race_attn_bwd(Q, K, V, W, dO, P, L, temperature=1.0, causal=False, chunk=1024, O=None, saved=None,
                   ws=None, grads=None, stream=None):
-    """(dQ, dK, dV) of <dO, RACE-attention(Q, K, V)>."""
+    """(dQ, dK, dV) of <dO, RACE-attention(Q, K, V)>. O and saved (from the
+    forward call) are given together, or both omitted (the forward is then
+    recomputed inside the call)."""
     import torch
     _check_inputs(Q, K, V, W, dO)
+    if (O is None) != (saved is None):
+        raise ValueError("O and saved are given together or not at all")
     B, H, N, d = Q.shape
     if tuple(W.shape) != (L, P, d):
         raise ValueError(f"W must be [L, P, d] = {(L, P, d)}, got {tuple(W.shape)}")
+    if O is not None:
+        _check_inputs(Q, O)
+        if O.shape != Q.shape:
+            raise ValueError("O must have the shape of Q")
     if grads is None:
         grads = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V))
     dQ, dK, dV = grads
     if ws is None:
-        ws = alloc_workspace(B, H, N, P, L, causal, chunk, True, Q.device)
-    code = lib().race_attn_bwd(_p(Q), _p(K), _p(V), _p(W), _p(dO), _p(saved), B, H, N, d, P, L,
+        ws = alloc_workspace(B, H, N, P, L, causal, chunk, WS_BWD if saved is not None else WS_BWD_RECOMPUTE,
+                             Q.device)
+    code = lib().race_attn_bwd(_p(Q), _p(K), _p(V), _p(W), _p(O), _p(dO), _p(saved), B, H, N, d, P, L,
                                float(temperature), int(bool(causal)), chunk, _dtype_code(Q), _p(dQ),
                                _p(dK), _p(dV), _p(ws), ws.numel(), _stream(stream))
     _check(code, "race_attn_bwd")

@@ -81,12 +81,12 @@ const char* race_attn_profile_stage(int i) { return (i >= 0 && i < t_count) ? t_
 
 race_status_t race_attn_workspace_bytes(int64_t B, int64_t H, int64_t N, int d, int P, int L, int causal,
                                         int chunk, int for_backward, size_t* bytes) {
-    if (!bytes) return RACE_ERR_INVALID_ARG;
+    if (!bytes || for_backward < WS_FWD || for_backward > WS_BWD_RECOMPUTE) return RACE_ERR_INVALID_ARG;
     Shape s;
     Derived dv;
     race_status_t rc = prepare(B, H, N, d, P, L, causal, chunk, s, dv);
     if (rc != RACE_OK) return rc;
-    *bytes = ws_layout(s, dv, for_backward ? 1 : 0).total;
+    *bytes = ws_layout(s, dv, for_backward).total;
     return RACE_OK;
 }
 
@@ -111,7 +111,7 @@ race_status_t race_attn_fwd(const void* Q, const void* K, const void* V, const v
     Derived dv;
     race_status_t rc = prepare(B, H, N, d, P, L, causal, chunk, s, dv);
     if (rc != RACE_OK) return rc;
-    const WsLayout wl = ws_layout(s, dv, 0);
+    const WsLayout wl = ws_layout(s, dv, WS_FWD);
     if (ws_bytes < wl.total) return RACE_ERR_WORKSPACE;
     Call c{};
     c.op = OP_FWD; c.Q = Q; c.K = K; c.V = V; c.W = W; c.saved_out = saved; c.beta = temperature; c.O = O;
@@ -119,22 +119,24 @@ race_status_t race_attn_fwd(const void* Q, const void* K, const void* V, const v
     return go(dtype, s, dv, wl, c);
 }
 
-race_status_t race_attn_bwd(const void* Q, const void* K, const void* V, const void* W, const void* dO,
-                            const void* saved, int64_t B, int64_t H, int64_t N, int d, int P, int L,
-                            float temperature, int causal, int chunk, race_dtype_t dtype, void* dQ, void* dK,
+race_status_t race_attn_bwd(const void* Q, const void* K, const void* V, const void* W, const void* O,
+                            const void* dO, const void* saved, int64_t B, int64_t H, int64_t N, int d, int P,
+                            int L, float temperature, int causal, int chunk, race_dtype_t dtype, void* dQ, void* dK,
                             void* dV, void* ws, size_t ws_bytes, void* stream) {
     if (!Q || !K || !V || !W || !dO || !dQ || !dK || !dV || !ws || !dtype_ok(dtype) ||
-        !std::isfinite(temperature) || !all_aligned({Q, K, V, W, dO, saved, dQ, dK, dV, ws}))
+        !std::isfinite(temperature) || (O == nullptr) != (saved == nullptr) ||
+        !all_aligned({Q, K, V, W, O, dO, saved, dQ, dK, dV, ws}))
         return RACE_ERR_INVALID_ARG;
     Shape s;
     Derived dv;
     race_status_t rc = prepare(B, H, N, d, P, L, causal, chunk, s, dv);
     if (rc != RACE_OK) return rc;
-    const WsLayout wl = ws_layout(s, dv, 1);
+    const WsLayout wl = ws_layout(s, dv, saved ? WS_BWD : WS_BWD_RECOMPUTE);
     if (ws_bytes < wl.total) return RACE_ERR_WORKSPACE;
     Call c{};
-    c.op = OP_BWD; c.Q = Q; c.K = K; c.V = V; c.W = W; c.dO = dO; c.saved_in = saved; c.beta = temperature;
-    c.dQ = dQ; c.dK = dK; c.dV = dV; c.ws = ws; c.stream = reinterpret_cast<hipStream_t>(stream);
+    c.op = OP_BWD; c.Q = Q; c.K = K; c.V = V; c.W = W; c.dO = dO; c.O_in = O; c.saved_in = saved;
+    c.beta = temperature; c.dQ = dQ; c.dK = dK; c.dV = dV; c.ws = ws;
+    c.stream = reinterpret_cast<hipStream_t>(stream);
     return go(dtype, s, dv, wl, c);
 }
 

@@ -13,8 +13,9 @@ enum { OP_FWD = 0, OP_BWD = 1, OP_HASH = 2 };
 struct Call {
     int op;
     const void *Q, *K, *V, *W, *dO;
-    const void* saved_in;   // backward: states from a forward call (may be null)
-    void* saved_out;        // forward: where to keep the states (may be null)
+    const void* O_in;       // backward: the forward output (null: recompute the forward)
+    const void* saved_in;   // backward: what the forward kept (null: recompute the forward)
+    void* saved_out;        // forward: where to keep the states and D (may be null)
     float beta;
     void *O, *dQ, *dK, *dV;
     void* ws;
@@ -61,12 +62,45 @@ race_status_t run_scan(const Derived& d, float* states, float* total, hipStream_
     return launch_ok();
 }
 
-template <class C, int MODE>
+enum { PASS_FWD = 0, PASS_BWD_Q = 1, PASS_BWD_K = 2 };
+
+template <class C, int KIND>
 race_status_t run_pass(const Shape& s, const Derived& d, PassArgs a, hipStream_t st) {
     a.N = s.N; a.chunk = s.chunk; a.L = s.L; a.causal = s.causal;
-    profile_mark(MODE == MODE_FWD ? "pass_fwd" : MODE == MODE_BWD_Q ? "pass_bwd_q" : "pass_bwd_k", st);
-    hipLaunchKernelGGL((k_pass<C, MODE>), dim3((unsigned)d.NC, (unsigned)d.BH), dim3(NT), 0, st, a);
+    const dim3 grid((unsigned)d.NC, (unsigned)d.BH), block(NT);
+    if constexpr (KIND == PASS_FWD) {
+        profile_mark("pass_fwd", st);
+        hipLaunchKernelGGL(k_fwd<C>, grid, block, 0, st, a);
+    } else if constexpr (KIND == PASS_BWD_Q) {
+        profile_mark("pass_bwd_q", st);
+        hipLaunchKernelGGL(k_bwd_q<C>, grid, block, 0, st, a);
+    } else {
+        profile_mark("pass_bwd_k", st);
+        hipLaunchKernelGGL(k_bwd_k<C>, grid, block, 0, st, a);
+    }
     return launch_ok();
+}
+
+// Forward into O; when `saved` is set it receives the sketch states and D.
+template <class C>
+race_status_t run_forward(const Shape& s, const Derived& d, const WsLayout& wl, const Call& c, void* O, void* saved) {
+    char* ws = reinterpret_cast<char*>(c.ws);
+    hipStream_t st = c.stream;
+    const SavedLayout sl = saved_layout(s, d);
+    float* Sb = (s.causal && saved) ? reinterpret_cast<float*>(saved) : reinterpret_cast<float*>(ws + wl.S);
+    RACE_TRY(run_totals<C>(s, d, c.K, c.V, nullptr, nullptr, 0, c.W, c.beta, Sb, st));
+    PassArgs a{};
+    a.Xa = c.Q; a.Xb = c.K; a.Zsrc = c.V; a.W = c.W; a.beta = c.beta; a.out0 = O;
+    a.Dv = saved ? reinterpret_cast<float*>(reinterpret_cast<char*>(saved) + sl.D) : nullptr;
+    if (s.causal) {
+        RACE_TRY(run_scan<SCAN_EXCL>(d, Sb, nullptr, st));
+        a.state = Sb; a.state_bh_stride = d.NC * d.F65; a.state_chunk_stride = d.F65;
+    } else {
+        float* St = saved ? reinterpret_cast<float*>(saved) : reinterpret_cast<float*>(ws + wl.St);
+        RACE_TRY(run_scan<SCAN_TOTAL>(d, Sb, St, st));
+        a.state = St; a.state_bh_stride = d.F65; a.state_chunk_stride = 0;
+    }
+    return run_pass<C, PASS_FWD>(s, d, a, st);
 }
 
 template <class C>
@@ -82,57 +116,34 @@ race_status_t run(const Shape& s, const Derived& d, const WsLayout& wl, const Ca
                            c.near_zero);
         return launch_ok();
     }
-    const int64_t chunk_stride = d.F65;
-    const int64_t bh_stride = d.NC * d.F65;
-    if (c.op == OP_FWD) {
-        float* Sb = (s.causal && c.saved_out) ? reinterpret_cast<float*>(c.saved_out)
-                                              : reinterpret_cast<float*>(ws + wl.S);
-        RACE_TRY(run_totals<C>(s, d, c.K, c.V, nullptr, nullptr, 0, c.W, c.beta, Sb, st));
-        PassArgs a{};
-        a.Xa = c.Q; a.Xb = c.K; a.Zsrc = c.V; a.Ysrc = nullptr; a.W = c.W; a.WTp = nullptr;
-        a.beta = c.beta; a.Dv = nullptr; a.Ev = nullptr; a.out0 = c.O; a.out1 = nullptr;
-        if (s.causal) {
-            RACE_TRY(run_scan<SCAN_EXCL>(d, Sb, nullptr, st));
-            a.state = Sb; a.state_bh_stride = bh_stride; a.state_chunk_stride = chunk_stride;
-        } else {
-            float* St = c.saved_out ? reinterpret_cast<float*>(c.saved_out) : reinterpret_cast<float*>(ws + wl.St);
-            RACE_TRY(run_scan<SCAN_TOTAL>(d, Sb, St, st));
-            a.state = St; a.state_bh_stride = d.F65; a.state_chunk_stride = 0;
-        }
-        return run_pass<C, MODE_FWD>(s, d, a, st);
+    if (c.op == OP_FWD) return run_forward<C>(s, d, wl, c, c.O, c.saved_out);
+
+    // backward: O and what the forward kept, recomputed when not given
+    const void* O = c.O_in;
+    const void* saved = c.saved_in;
+    if (!saved) {
+        RACE_TRY(run_forward<C>(s, d, wl, c, ws + wl.Ov, ws + wl.Sv));
+        O = ws + wl.Ov;
+        saved = ws + wl.Sv;
     }
-    // backward
+    const SavedLayout sl = saved_layout(s, d);
+    const float* S = reinterpret_cast<const float*>(saved);
+    float* Dv = reinterpret_cast<float*>(const_cast<char*>(reinterpret_cast<const char*>(saved)) + sl.D);
+    float* Ev = reinterpret_cast<float*>(ws + wl.E);
     using elem = typename Prec<C::F32>::elem;
     elem* WTp = reinterpret_cast<elem*>(ws + wl.wt);
     profile_mark("prep", st);
     hipLaunchKernelGGL(k_prep<C>, dim3(8), dim3(256), 0, st, reinterpret_cast<const elem*>(c.W), s.L, WTp);
     RACE_TRY(launch_ok());
-    float* Dv = reinterpret_cast<float*>(ws + wl.D);
-    float* Ev = reinterpret_cast<float*>(ws + wl.E);
+
     PassArgs q{};
-    q.Xa = c.Q; q.Xb = c.K; q.Zsrc = c.V; q.Ysrc = c.dO; q.W = c.W; q.WTp = WTp; q.beta = c.beta;
-    q.Dv = Dv; q.Ev = Ev; q.out0 = c.dQ; q.out1 = nullptr;
-    if (s.causal) {
-        const float* Sb = reinterpret_cast<const float*>(c.saved_in);
-        if (!Sb) {
-            float* Sw = reinterpret_cast<float*>(ws + wl.S);
-            RACE_TRY(run_totals<C>(s, d, c.K, c.V, nullptr, nullptr, 0, c.W, c.beta, Sw, st));
-            RACE_TRY(run_scan<SCAN_EXCL>(d, Sw, nullptr, st));
-            Sb = Sw;
-        }
-        q.state = Sb; q.state_bh_stride = bh_stride; q.state_chunk_stride = chunk_stride;
-    } else {
-        const float* St = reinterpret_cast<const float*>(c.saved_in);
-        if (!St) {
-            float* Sw = reinterpret_cast<float*>(ws + wl.S);
-            float* Stw = reinterpret_cast<float*>(ws + wl.St);
-            RACE_TRY(run_totals<C>(s, d, c.K, c.V, nullptr, nullptr, 0, c.W, c.beta, Sw, st));
-            RACE_TRY(run_scan<SCAN_TOTAL>(d, Sw, Stw, st));
-            St = Stw;
-        }
-        q.state = St; q.state_bh_stride = d.F65; q.state_chunk_stride = 0;
-    }
-    RACE_TRY((run_pass<C, MODE_BWD_Q>(s, d, q, st)));
+    q.Xa = c.Q; q.Xb = c.K; q.Zsrc = c.V; q.Ysrc = c.dO; q.Osrc = O; q.W = c.W; q.WTp = WTp; q.beta = c.beta;
+    q.Dv = Dv; q.Ev = Ev; q.out0 = c.dQ;
+    q.state = S;
+    q.state_bh_stride = s.causal ? d.NC * d.F65 : d.F65;
+    q.state_chunk_stride = s.causal ? d.F65 : 0;
+    RACE_TRY((run_pass<C, PASS_BWD_Q>(s, d, q, st)));
+
     float* Tw = reinterpret_cast<float*>(ws + wl.T);
     RACE_TRY(run_totals<C>(s, d, c.Q, c.dO, Dv, Ev, 1, c.W, c.beta, Tw, st));
     PassArgs k{};
@@ -140,13 +151,13 @@ race_status_t run(const Shape& s, const Derived& d, const WsLayout& wl, const Ca
     k.Dv = Dv; k.Ev = Ev; k.out0 = c.dK; k.out1 = c.dV;
     if (s.causal) {
         RACE_TRY(run_scan<SCAN_REV_EXCL>(d, Tw, nullptr, st));
-        k.state = Tw; k.state_bh_stride = bh_stride; k.state_chunk_stride = chunk_stride;
+        k.state = Tw; k.state_bh_stride = d.NC * d.F65; k.state_chunk_stride = d.F65;
     } else {
         float* Ttw = reinterpret_cast<float*>(ws + wl.Tt);
         RACE_TRY(run_scan<SCAN_TOTAL>(d, Tw, Ttw, st));
         k.state = Ttw; k.state_bh_stride = d.F65; k.state_chunk_stride = 0;
     }
-    return run_pass<C, MODE_BWD_K>(s, d, k, st);
+    return run_pass<C, PASS_BWD_K>(s, d, k, st);
 }
 
 #define RACE_CASE(P_, MT_)                                                   \

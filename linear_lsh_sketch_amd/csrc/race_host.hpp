@@ -23,15 +23,26 @@ struct Derived {
 };
 
 struct WsLayout {
-    size_t wt;     // back-projection operand table
-    size_t S;      // per-chunk sketch states (or chunk totals, non-causal)
-    size_t St;     // non-causal: whole-sequence sketch
+    size_t wt;     // backward: back-projection operand table
+    size_t S;      // forward: per-chunk sketch states (or chunk totals, non-causal)
+    size_t St;     // forward, non-causal: whole-sequence sketch
     size_t T;      // backward: per-chunk gradient sketch states
-    size_t Tt;     // backward non-causal: whole-sequence gradient sketch
-    size_t D;      // backward: per-token denominators
+    size_t Tt;     // backward, non-causal: whole-sequence gradient sketch
     size_t E;      // backward: per-token e = -<dO, O>/D
+    size_t Sv;     // backward without saved: the recomputed forward's saved buffer
+    size_t Ov;     // backward without saved: the recomputed forward output
     size_t total;
 };
+
+// The saved buffer: float32 sketch states (per chunk, causal; the total,
+// non-causal) then the float32 per-token denominators D.
+struct SavedLayout {
+    size_t D;
+    size_t total;
+};
+
+// Workspace kinds (race_attn_workspace_bytes' for_backward argument).
+enum { WS_FWD = 0, WS_BWD = 1, WS_BWD_RECOMPUTE = 2 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -67,26 +78,37 @@ inline race_status_t derive(const Shape& s, Derived& d) {
     return RACE_OK;
 }
 
-// Sizes of the optional saved buffer: per-chunk states (causal) or the total.
-inline size_t saved_bytes(const Shape& s, const Derived& d) {
+inline SavedLayout saved_layout(const Shape& s, const Derived& d) {
     const size_t per = (size_t)d.F65 * sizeof(float);
-    return s.causal ? (size_t)d.BH * (size_t)d.NC * per : (size_t)d.BH * per;
+    const size_t states = s.causal ? (size_t)d.BH * (size_t)d.NC * per : (size_t)d.BH * per;
+    SavedLayout l;
+    l.D = align256(states);
+    l.total = l.D + (size_t)d.BH * (size_t)s.N * sizeof(float);
+    return l;
 }
 
-inline WsLayout ws_layout(const Shape& s, const Derived& d, int for_backward) {
+inline size_t saved_bytes(const Shape& s, const Derived& d) { return saved_layout(s, d).total; }
+
+inline WsLayout ws_layout(const Shape& s, const Derived& d, int kind) {
     WsLayout w{};
     const size_t per = (size_t)d.F65 * sizeof(float);
     const size_t chunks = (size_t)d.BH * (size_t)d.NC * per;
     const size_t totals = (size_t)d.BH * per;
+    const size_t tokens = (size_t)d.BH * (size_t)s.N;
     size_t off = 0;
-    w.wt = off;  off = align256(off + (size_t)d.NPAIR * 4 * 64 * 8 * sizeof(float));
-    w.S = off;   off = align256(off + chunks);
-    w.St = off;  off = align256(off + (s.causal ? 0 : totals));
-    if (for_backward) {
+    if (kind != WS_BWD) {
+        w.S = off;   off = align256(off + chunks);
+        w.St = off;  off = align256(off + (s.causal ? 0 : totals));
+    }
+    if (kind != WS_FWD) {
+        w.wt = off;  off = align256(off + (size_t)d.NPAIR * 4 * 64 * 8 * sizeof(float));
         w.T = off;   off = align256(off + chunks);
         w.Tt = off;  off = align256(off + (s.causal ? 0 : totals));
-        w.D = off;   off = align256(off + (size_t)d.BH * (size_t)s.N * sizeof(float));
-        w.E = off;   off = align256(off + (size_t)d.BH * (size_t)s.N * sizeof(float));
+        w.E = off;   off = align256(off + tokens * sizeof(float));
+    }
+    if (kind == WS_BWD_RECOMPUTE) {
+        w.Sv = off;  off = align256(off + saved_bytes(s, d));
+        w.Ov = off;  off = align256(off + tokens * (size_t)s.d * sizeof(float));
     }
     w.total = off;
     return w;

@@ -11,20 +11,21 @@
 //
 // Decomposition (per (batch, head), the sequence cut into chunks of `chunk`
 // tokens, one workgroup per chunk, sub-blocks of 64 tokens inside a chunk):
-//   k_totals  : per-chunk sketch  M_c = sum_{b in c} phi(x_b)^T [z_b | m_b]
-//   k_scan    : exclusive prefix (causal), reverse exclusive prefix (backward
-//               key side) or total (non-causal) over chunks
-//   k_pass    : per sub-block readout against the running sketch plus the
-//               intra-sub-block causal term, then the sketch update; in the
-//               backward modes also the gradient wrt the readout-side features,
-//               the corner-softmax chain rule and the back-projection.
-// Roles in k_pass:
-//   FWD   : a = queries, b = keys,    z_b = [v | 1]          -> O
-//   BWD_Q : a = queries, b = keys,    z_b = [v | 1], y_a = [dO/D | e] -> dQ, D, e
-//   BWD_K : a = keys,    b = queries, z_b = [dO/D | e], y_a = [v | 1] -> dK, dV
-// with e = -<dO, O>/D. The sketch M = sum_b phi_b^T z_b is held in float32
-// accumulators, split by value columns over the four waves (wave w owns
-// columns 16w..16w+15; the mass column is split by feature chunk).
+//   k_totals : per-chunk sketch  M_c = sum_{b in c} phi(x_b)^T [z_b | m_b]
+//   k_scan   : exclusive prefix (causal), reverse exclusive prefix (backward
+//              key side) or total (non-causal) over chunks
+//   k_fwd    : per sub-block readout of the queries against the running key
+//              sketch plus the intra-sub-block causal term, then the sketch
+//              update -> O (and the per-token denominator D)
+//   k_bwd_q  : y = [dO/D | e], e = -<dO, O>/D; dA_Q = (key sketch) y plus the
+//              intra term; corner-softmax chain rule, back-projection -> dQ
+//   k_bwd_k  : against the reverse sketch of the queries' [dO/D | e]: the dV
+//              readout and dA_K = T [v | 1] in one sweep over the feature
+//              blocks; chain rule, back-projection -> dK, dV
+// "a" is the side that reads the sketch, "b" the side that writes it. Sketch
+// states are held in float32 accumulators, split by value columns over the
+// four waves (wave w owns columns 16w..16w+15; the mass column is split by
+// feature chunk).
 #pragma once
 
 #include <type_traits>
@@ -33,7 +34,6 @@
 
 namespace race {
 
-enum { MODE_FWD = 0, MODE_BWD_Q = 1, MODE_BWD_K = 2 };
 enum { SCAN_EXCL = 0, SCAN_REV_EXCL = 1, SCAN_TOTAL = 2 };
 
 // ---------------------------------------------------------------------------
@@ -290,13 +290,15 @@ __device__ inline void sketch_update(int fb, int w, int ln, int g, const typenam
 
 // Project the own 16-token tile for the tiles of feature block fb and write
 // the features to LDS (row layout `rows` and/or transposed `cols`); when KEEP,
-// also return the lane's operands (one per chunk of the block) in phi_frag.
+// also return the lane's operands (one per chunk of the block) in phi_frag and
+// the tanh values of its planes (one group of four per tile) in u_keep.
 template <class C, bool KEEP>
 __device__ inline void block_features(const WSrc<C>& wsrc, int fb, int lane, int w, int ln, int g,
                                       const typename Prec<C::F32>::frag xf[2], float inv, bool valid, float beta,
                                       int L, typename Prec<C::F32>::elem* rows /* [64][ROWF] or null */,
                                       typename Prec<C::F32>::elem* cols /* [FBK*32][ROWT] or null */,
-                                      typename Prec<C::F32>::frag (&phi_frag)[C::FBK]) {
+                                      typename Prec<C::F32>::frag (&phi_frag)[C::FBK],
+                                      float (&u_keep)[C::TPB][4]) {
 #pragma unroll
     for (int tb = 0; tb < C::TPB; ++tb) {
         const int t = fb * C::TPB + tb;
@@ -305,6 +307,10 @@ __device__ inline void block_features(const WSrc<C>& wsrc, int fb, int lane, int
 #pragma unroll
         for (int i = 0; i < 4; ++i) hs[i] = acc[i] * inv;
         soft_features<C>(t, g, hs, beta, L, phi, u, s);
+        if constexpr (KEEP) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) u_keep[tb][i] = u[i];
+        }
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb) {
             const int kcl = tb * C::KB + kb;
@@ -408,7 +414,9 @@ __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
 #pragma unroll
         for (int fb = 0; fb < C::NBLK; ++fb) {
             frag unused[C::FBK];
-            block_features<C, false>(wsrc, fb, lane, w, ln, g, xf, inv, valid, a.beta, a.L, nullptr, s_cols, unused);
+            float unused_u[C::TPB][4];
+            block_features<C, false>(wsrc, fb, lane, w, ln, g, xf, inv, valid, a.beta, a.L, nullptr, s_cols, unused,
+                                     unused_u);
             __syncthreads();
             sketch_update<C>(fb, w, ln, g, s_cols, s_ZT, Macc, Zacc);
             __syncthreads();
@@ -455,20 +463,21 @@ __global__ __launch_bounds__(256) void k_scan(float* __restrict__ st, float* __r
 }
 
 // ---------------------------------------------------------------------------
-// the sub-block pass
+// sub-block passes
 // ---------------------------------------------------------------------------
 struct PassArgs {
-    const void* Xa;        // readout-side rows
-    const void* Xb;        // sketch-side rows
-    const void* Zsrc;      // FWD/BWD_Q: V; BWD_K: dO
+    const void* Xa;        // readout-side rows (FWD, BWD_Q: Q; BWD_K: K)
+    const void* Xb;        // sketch-side rows (FWD, BWD_Q: K; BWD_K: Q)
+    const void* Zsrc;      // FWD, BWD_Q: V; BWD_K: dO
     const void* Ysrc;      // BWD_Q: dO; BWD_K: V
+    const void* Osrc;      // BWD_Q: the forward output O
     const void* W;         // [L, P, 64]
     const void* WTp;       // back-projection operands (k_prep)
     const float* state;    // sketch before the chunk (causal) or the total
     int64_t state_bh_stride;
     int64_t state_chunk_stride;
-    float* Dv;             // per-token D  (BWD_Q writes, BWD_K reads)
-    float* Ev;             // per-token e
+    float* Dv;             // per-token D: FWD writes it when set; BWD_Q, BWD_K read it
+    float* Ev;             // per-token e: BWD_Q writes it, BWD_K reads it
     void* out0;            // FWD: O; BWD_Q: dQ; BWD_K: dK
     void* out1;            // BWD_K: dV
     int64_t N;
@@ -478,73 +487,260 @@ struct PassArgs {
     int causal;
 };
 
-template <class C, int MODE>
-struct PassLds {
+// Sketch rows of feature block fb for the gradient contraction dA = M y:
+// [FBK*32][ROWE], value columns of wave w and the mass column (64) from the
+// wave that owns it. Only dA - <a, dA> per table is used downstream, so a
+// per-table constant may be removed: the corner mean of every value column is
+// subtracted in float32 and the mass column is shifted by `zshift`, and the
+// bf16 operand then carries the part that survives instead of a large common
+// offset. A lane holds every corner of its tables for its value column.
+template <class C>
+__device__ inline void write_sketch_rows(int fb, int w, int ln, int g, const f32x4 Macc[C::NKC * 2],
+                                         const f32x4 Zacc[C::NOWN * 2], float zshift,
+                                         typename Prec<C::F32>::elem* s_ms) {
+#pragma unroll
+    for (int tb = 0; tb < C::TPB; ++tb) {
+        float v[C::KB * 8];
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[kb * 8 + 4 * h + i] = Macc[2 * (fb * C::FBK + tb * C::KB + kb) + h][i];
+        constexpr int RR = (C::P == 4) ? 16 : C::R;
+#pragma unroll
+        for (int t0c = 0; t0c < C::KB * 8; t0c += RR) {
+            float m = 0.f;
+#pragma unroll
+            for (int r = 0; r < RR; ++r) m += v[t0c + r];
+            m *= 1.f / (float)RR;
+#pragma unroll
+            for (int r = 0; r < RR; ++r) v[t0c + r] -= m;
+        }
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int fl = 32 * (tb * C::KB + kb) + 8 * g + 4 * h + i;
+                    s_ms[fl * C::ROWE + 16 * w + ln] = to_elem<C::F32>(v[kb * 8 + 4 * h + i]);
+                }
+    }
+    if (w < C::FBK && ln == 0) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                s_ms[(32 * w + 8 * g + 4 * h + i) * C::ROWE + 64] = to_elem<C::F32>(Zacc[2 * fb + h][i] - zshift);
+    }
+}
+
+// Zero the padding columns 65..95 of the sketch rows.
+template <class C>
+__device__ inline void zero_sketch_pads(typename Prec<C::F32>::elem* s_ms) {
+    for (int idx = threadIdx.x; idx < C::FBK * 32 * 31; idx += NT)
+        s_ms[(idx / 31) * C::ROWE + 65 + idx % 31] = to_elem<C::F32>(0.f);
+}
+
+// dA of feature block fb for the own token: the sketch part M y (three
+// 32-wide K steps over the augmented width) plus, when causal, the
+// intra-sub-block part phi_b^T Cc. G[2 kcl + h] holds canonical features
+// 32 kcl + 8 g + 4 h + i of the block, matching the lane's feature order.
+template <class C>
+__device__ inline void block_grad(int ln, int g, const typename Prec<C::F32>::elem* s_ms,
+                                  const typename Prec<C::F32>::frag yf[3], const typename Prec<C::F32>::elem* s_cols,
+                                  const typename Prec<C::F32>::frag Cf[2], bool causal, f32x4 (&G)[C::FBK * 2]) {
+#pragma unroll
+    for (int m = 0; m < C::FBK * 2; ++m) {
+        const int kcl = m >> 1, h = m & 1;
+        const int fl = 32 * kcl + canon_of_row(h, ln);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 3; ++s) acc = mma(ld_frag<C::F32>(s_ms + fl * C::ROWE + 32 * s + 8 * g), yf[s], acc);
+        if (causal) {
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const typename Prec<C::F32>::elem* p = s_cols + fl * C::ROWT + 32 * s2 + 4 * g;
+                acc = mma(ld_frag2<C::F32>(p, p + 16), Cf[s2], acc);
+            }
+        }
+        G[m] = acc;
+    }
+}
+
+// Corner-softmax chain rule for projection tile t of the own token (phi and dA
+// in the lane's feature order, u = tanh of its planes), then the
+// back-projection dX += W'^T dh, two tiles per matrix-core operand.
+template <class C>
+__device__ inline void chain_backproject(int t, int lane, const float phi[C::KB * 8], const float dA[C::KB * 8],
+                                         const float u[4], float beta, const typename Prec<C::F32>::elem* WTp,
+                                         f32x4 (&dhp)[2], f32x4 (&dX)[4]) {
+    float dh[4];
+    soft_features_backward<C>(phi, dA, u, beta, dh);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dhp[t & 1][i] = dh[i];
+    if ((t & 1) == 1 || t == C::MT - 1) {
+        const typename Prec<C::F32>::frag df = pack<C::F32>(dhp[0], (t & 1) ? dhp[1] : f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+            dX[dt] = mma(ld_frag<C::F32>(WTp + ((size_t)((t >> 1) * 4 + dt) * 64 + lane) * 8), df, dX[dt]);
+        dhp[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dhp[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+}
+
+// Intra-sub-block operand of the gradient contraction: Cc[b][a] = z_b . y_a
+// over the augmented width (y = hi + lo when YLO), kept where key-side token b
+// is visible from the own token a (b <= a, or b >= a when REV) and b < nv;
+// returned as the two B operands of phi_b^T Cc (K index = b).
+template <class C, bool REV, bool YLO>
+__device__ inline void intra_operand(const typename Prec<C::F32>::elem* s_zr, const typename Prec<C::F32>::elem* s_yr,
+                                     const typename Prec<C::F32>::elem* s_ylo, int w, int ln, int g, int my, int nv,
+                                     typename Prec<C::F32>::frag (&Cf)[2]) {
+    using frag = typename Prec<C::F32>::frag;
+    f32x4 Cc[4];
+    frag yf[3];
+#pragma unroll
+    for (int s = 0; s < 3; ++s) yf[s] = ld_frag<C::F32>(s_yr + my * C::ROWE + 32 * s + 8 * g);
+#pragma unroll
+    for (int bt = 0; bt < 4; ++bt) {
+        Cc[bt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const bool vis = REV ? (bt >= w) : (bt <= w);
+        if (vis) {
+#pragma unroll
+            for (int s = 0; s < 3; ++s) {
+                const frag zf = ld_frag<C::F32>(s_zr + (16 * bt + ln) * C::ROWE + 32 * s + 8 * g);
+                Cc[bt] = mma(zf, yf[s], Cc[bt]);
+                if constexpr (YLO) Cc[bt] = mma(zf, ld_frag<C::F32>(s_ylo + my * C::ROWE + 32 * s + 8 * g), Cc[bt]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int b = 16 * bt + 4 * g + i;
+            const bool v2 = (REV ? (b >= my) : (b <= my)) && b < nv;
+            if (!v2) Cc[bt][i] = 0.f;
+        }
+    }
+    Cf[0] = pack<C::F32>(Cc[0], Cc[1]);
+    Cf[1] = pack<C::F32>(Cc[2], Cc[3]);
+}
+
+// dx = (dx_hat - x_hat <x_hat, dx_hat>) / |x| for the own token row (the chain
+// rule of x_hat = x / max(|x|, eps); below eps the map is a plain scaling).
+// dX[dt] holds columns 16 dt + 4 g .. +3.
+template <class C>
+__device__ inline void store_dx(const void* X, void* out, size_t row, bool valid, int g, float inv, float nrm,
+                                const f32x4 dX[4]) {
+    using T = typename In<C::F32>::T;
+    float xv[4][4];
+    float radial = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+        const size_t off = row * DH + 16 * dt + 4 * g;
+        if constexpr (C::F32) {
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (valid) v = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(X) + off);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xv[dt][i] = v[i];
+        } else {
+            bf16x4 v = {};
+            if (valid) v = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(X) + off);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xv[dt][i] = valid ? (float)v[i] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) radial += xv[dt][i] * inv * dX[dt][i];
+    }
+    radial = sum_groups(radial);
+    const bool tangent = nrm > NORM_EPS;
+    if (valid) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            f32x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = (tangent ? dX[dt][i] - xv[dt][i] * inv * radial : dX[dt][i]) * inv;
+            T* dst = reinterpret_cast<T*>(out) + row * DH + 16 * dt + 4 * g;
+            if constexpr (C::F32) {
+                *reinterpret_cast<f32x4*>(dst) = o;
+            } else {
+                bf16x4 ob;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ob[i] = (__bf16)o[i];
+                *reinterpret_cast<bf16x4*>(dst) = ob;
+            }
+        }
+    }
+}
+
+// Store the staged [64][ROWD] tile (thread: row tr, quarter tq) to rows t0.. of out.
+template <class C>
+__device__ inline void store_stage(void* out, size_t row0, int tr, int tq, bool tok,
+                                   const typename Prec<C::F32>::elem* s_stage) {
+    using T = typename In<C::F32>::T;
+    using frag = typename Prec<C::F32>::frag;
+    if (tok) {
+        T* o = reinterpret_cast<T*>(out) + (row0 + tr) * DH + 16 * tq;
+        const typename Prec<C::F32>::elem* src = s_stage + tr * C::ROWD + 16 * tq;
+        *reinterpret_cast<frag*>(o) = ld_frag<C::F32>(src);
+        *reinterpret_cast<frag*>(o + 8) = ld_frag<C::F32>(src + 8);
+    }
+}
+
+// LDS budget: W' is staged when it fits next to the tiles at the target
+// number of workgroups per CU, else the projections read it from global memory.
+template <class elem, int BASE, int NFLOAT, int MT, int OCC>
+struct WStage {
+    static constexpr int n_w0 = MT * 1024;
+    static constexpr bool on = ((BASE + n_w0) * (int)sizeof(elem) + NFLOAT * 4) * OCC <= 160 * 1024;
+    static constexpr int n_w = on ? n_w0 : 0;
+    static constexpr int n_elem = BASE + n_w;
+    static constexpr int bytes = n_elem * (int)sizeof(elem) + NFLOAT * 4;
+    static_assert(bytes * OCC <= 160 * 1024, "LDS budget");
+};
+
+// ---------------------------------------------------------------------------
+// forward pass: O = (sum_f phi_a,f M_f) / (sum_f phi_a,f z_f) with M, z the
+// sketch of the keys before the sub-block plus the intra-sub-block causal term;
+// then the sketch update. Also writes the per-token denominator D when Dv is set.
+// ---------------------------------------------------------------------------
+template <class C>
+struct FwdLds {
     using elem = typename Prec<C::F32>::elem;
-    static constexpr bool BWD = MODE != MODE_FWD;
     static constexpr int n_rows = TB * C::ROWF;                 // a-side features [64][ROWF]
     static constexpr int n_brow = TB * C::ROWF;                 // b-side features [64][ROWF]
     static constexpr int n_cols = C::FBK * 32 * C::ROWT;        // b-side features transposed
     static constexpr int n_zt = ZR * C::ROWT;                   // z_b transposed
     static constexpr int n_sc = TB * C::ROWT;                   // intra scores [a][b]
-    static constexpr int n_zr = BWD ? TB * C::ROWE : 0;         // z_b rows
-    static constexpr int n_yr = BWD ? TB * C::ROWE : 0;         // y_a rows
-    // bf16 residual of the query-side y rows ([g | e]): the intra-sub-block
-    // product g.v + e cancels for the first keys of a sequence, so it is
-    // formed from y = hi + lo in fp32 accumulation
-    static constexpr bool YLO = MODE == MODE_BWD_Q && !C::F32;
-    static constexpr int n_ylo = YLO ? TB * C::ROWE : 0;
-    // aliases of [rows | brow] after the feature-block loop of phase 1
-    static constexpr int n_ms = C::FBK * 32 * C::ROWE;          // sketch rows (phase 2)
-    static constexpr int n_stage = TB * C::ROWD;                // O / dV / dO staging
-    static_assert(n_ms <= n_rows + n_brow, "sketch rows must fit the feature tiles");
+    static constexpr int n_stage = TB * C::ROWD;                // O staging (alias of rows | brow)
     static_assert(n_stage <= n_rows + n_brow, "staging must fit the feature tiles");
     static constexpr int o_rows = 0;
     static constexpr int o_brow = o_rows + n_rows;
     static constexpr int o_cols = o_brow + n_brow;
     static constexpr int o_zt = o_cols + n_cols;
     static constexpr int o_sc = o_zt + n_zt;
-    static constexpr int o_zr = o_sc + n_sc;
-    static constexpr int o_yr = o_zr + n_zr;
-    static constexpr int o_ylo = o_yr + n_yr;
-    static constexpr int n_float = 4 * TB + 4 * TB + TB;      // Dpart, dpart, Dint
-    static constexpr int base_elem = o_ylo + n_ylo;
-    // Target workgroups per CU: the forward pass runs two (its VGPR budget is
-    // capped at 256 so two waves share each SIMD and hide each other's latency).
-    static constexpr int OCC = (MODE == MODE_FWD && !C::F32 && C::NKC <= 8) ? 2 : 1;
-    // W' staged in LDS when it fits (else projections read it from global memory)
-    static constexpr int n_w0 = C::MT * 1024;
-    static constexpr bool W_LDS = ((base_elem + n_w0) * (int)sizeof(elem) + n_float * 4) * OCC <= 160 * 1024;
-    static constexpr int n_w = W_LDS ? n_w0 : 0;
-    static constexpr int o_w = base_elem;
-    static constexpr int n_elem = base_elem + n_w;
-    static constexpr int bytes = n_elem * (int)sizeof(elem) + n_float * 4;
-    static_assert(bytes <= 160 * 1024, "LDS budget");
+    static constexpr int o_w = o_sc + n_sc;
+    static constexpr int n_float = 4 * TB + TB;                 // Dpart, Dint
+    // two workgroups per CU (VGPR budget 256: two waves share each SIMD)
+    static constexpr int OCC = (!C::F32 && C::NKC <= 8) ? 2 : 1;
+    using WS = WStage<elem, o_w, n_float, C::MT, OCC>;
 };
 
-template <class C, int MODE>
-__global__ __launch_bounds__(NT, (PassLds<C, MODE>::OCC)) void k_pass(PassArgs a) {
+template <class C>
+__global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
     using elem = typename Prec<C::F32>::elem;
     using frag = typename Prec<C::F32>::frag;
-    using LD = PassLds<C, MODE>;
-    using T = typename In<C::F32>::T;
-    constexpr bool BWD = MODE != MODE_FWD;
-    constexpr bool REV = MODE == MODE_BWD_K;   // b visible when b >= a, sub-blocks in reverse
-    __shared__ __attribute__((aligned(32))) elem lds[LD::n_elem];
+    using LD = FwdLds<C>;
+    __shared__ __attribute__((aligned(32))) elem lds[LD::WS::n_elem];
     __shared__ float ldf[LD::n_float];
     elem* s_rows = lds + LD::o_rows;
     elem* s_brow = lds + LD::o_brow;
     elem* s_cols = lds + LD::o_cols;
     elem* s_ZT = lds + LD::o_zt;
     elem* s_sc = lds + LD::o_sc;
-    elem* s_zr = lds + LD::o_zr;
-    elem* s_yr = lds + LD::o_yr;
-    elem* s_ylo = lds + LD::o_ylo;
-    elem* s_ms = lds + LD::o_rows;      // phase-2 alias
-    elem* s_stage = lds + LD::o_rows;   // staging alias
+    elem* s_stage = lds + LD::o_rows;   // alias after the feature-block loop
     float* f_Dpart = ldf;               // [4][64]
-    float* f_dpart = ldf + 4 * TB;      // [4][64]
-    float* f_Dint = ldf + 8 * TB;       // [64]
+    float* f_Dint = ldf + 4 * TB;       // [64]
 
     const int lane = threadIdx.x & 63, ln = lane & 15, g = lane >> 4;
     // wave index as a scalar: every branch on it is wave-uniform, so no MFMA is
@@ -556,12 +752,10 @@ __global__ __launch_bounds__(NT, (PassLds<C, MODE>::OCC)) void k_pass(PassArgs a
     const int64_t seg1 = seg0 + a.chunk < a.N ? seg0 + a.chunk : a.N;
     const size_t base = (size_t)bh * a.N;
     const elem* W = reinterpret_cast<const elem*>(a.W);
-    const elem* WTp = reinterpret_cast<const elem*>(a.WTp);
     const bool causal = a.causal != 0;
-    elem* s_w = LD::W_LDS ? lds + LD::o_w : nullptr;
-    if (LD::W_LDS) stage_w<C>(W, a.L, s_w);
-    zero_pads<C>(s_ZT, BWD ? s_zr : nullptr, BWD ? s_yr : nullptr);
-    if (LD::YLO) zero_pads<C>(s_ZT, s_ylo, nullptr);
+    elem* s_w = LD::WS::on ? lds + LD::o_w : nullptr;
+    if (LD::WS::on) stage_w<C>(W, a.L, s_w);
+    zero_pads<C>(s_ZT, nullptr, nullptr);
     __syncthreads();   // W' and the padding are written by all waves, read by each
     const WSrc<C> wsrc{s_w, W, a.L};
 
@@ -571,47 +765,28 @@ __global__ __launch_bounds__(NT, (PassLds<C, MODE>::OCC)) void k_pass(PassArgs a
     const int nsub = (int)((seg1 - seg0 + TB - 1) / TB);
     const int my = 16 * w + ln;              // own token within the sub-block
 
-    // prefetch registers (one sub-block ahead)
-    frag n_xa[2], n_xb[2], n_z[2], n_y[2];
-    float n_d = 1.f, n_e = 0.f;
+    frag n_xa[2], n_xb[2], n_z[2];
     auto issue = [&](int it2) {
-        const int sb2 = REV ? nsub - 1 - it2 : it2;
-        const int64_t t0 = seg0 + (int64_t)sb2 * TB;
+        const int64_t t0 = seg0 + (int64_t)it2 * TB;
         const int nv = (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
         load_row_raw<C::F32>(a.Xa, base + t0 + my, my < nv, g, n_xa);
         load_row_raw<C::F32>(a.Xb, base + t0 + my, my < nv, g, n_xb);
-        const bool ok = tr < nv;
-        load_q16_raw<C::F32>(a.Zsrc, (base + t0 + tr) * DH + 16 * tq, ok, n_z);
-        if constexpr (BWD) load_q16_raw<C::F32>(a.Ysrc, (base + t0 + tr) * DH + 16 * tq, ok, n_y);
-        if (REV && ok) {
-            n_d = a.Dv[base + t0 + tr];
-            n_e = a.Ev[base + t0 + tr];
-        }
+        load_q16_raw<C::F32>(a.Zsrc, (base + t0 + tr) * DH + 16 * tq, tr < nv, n_z);
     };
     issue(0);
 
     for (int it = 0; it < nsub; ++it) {
-        const int sb = REV ? nsub - 1 - it : it;
-        const int64_t t0 = seg0 + (int64_t)sb * TB;
+        const int64_t t0 = seg0 + (int64_t)it * TB;
         const int nv = (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
         const bool valid = my < nv;
-        const size_t row = base + t0 + my;
         const bool tok = tr < nv;
-
-        frag xa[2] = {n_xa[0], n_xa[1]}, xb[2] = {n_xb[0], n_xb[1]};
-        frag zr[2] = {n_z[0], n_z[1]}, yr[2];
-        if constexpr (BWD) {
-            yr[0] = n_y[0];
-            yr[1] = n_y[1];
-        }
-        const float zd = n_d, ze = n_e;
+        frag xa[2] = {n_xa[0], n_xa[1]}, xb[2] = {n_xb[0], n_xb[1]}, zr[2] = {n_z[0], n_z[1]};
         if (it + 1 < nsub) issue(it + 1);
 
         float inv_a, nrm_a, inv_b, nrm_b;
         row_norm<C::F32>(xa, inv_a, nrm_a);
         row_norm<C::F32>(xb, inv_b, nrm_b);
-        if (REV) write_aug<C>(zr, tok ? rcp_(zd) : 0.f, tok ? ze : 0.f, s_ZT, s_zr);
-        else write_aug<C>(zr, 1.f, tok ? 1.f : 0.f, s_ZT, BWD ? s_zr : nullptr);
+        write_aug<C>(zr, 1.f, tok ? 1.f : 0.f, s_ZT, nullptr);
 
         f32x4 Y[4], Dacc[4], Sc[4];
 #pragma unroll
@@ -620,19 +795,19 @@ __global__ __launch_bounds__(NT, (PassLds<C, MODE>::OCC)) void k_pass(PassArgs a
             Dacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
             Sc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        // ----------------------------- phase 1 -------------------------------
 #pragma unroll
         for (int fb = 0; fb < C::NBLK; ++fb) {
             frag phiA[C::FBK], unused[C::FBK];
-            block_features<C, true>(wsrc, fb, lane, w, ln, g, xa, inv_a, true, a.beta, a.L, s_rows, nullptr, phiA);
+            float unused_u[C::TPB][4];
+            block_features<C, true>(wsrc, fb, lane, w, ln, g, xa, inv_a, true, a.beta, a.L, s_rows, nullptr, phiA,
+                                    unused_u);
             block_features<C, false>(wsrc, fb, lane, w, ln, g, xb, inv_b, valid, a.beta, a.L, s_brow,
-                                     (!BWD && causal) ? s_cols : nullptr, unused);
+                                     causal ? s_cols : nullptr, unused, unused_u);
             __syncthreads();
             if (causal) {
 #pragma unroll
                 for (int bt = 0; bt < 4; ++bt) {
-                    const bool vis = REV ? (bt >= w) : (bt <= w);
-                    if (vis) {
+                    if (bt <= w) {
 #pragma unroll
                         for (int kcl = 0; kcl < C::FBK; ++kcl)
                             Sc[bt] = mma(ld_frag<C::F32>(s_brow + (16 * bt + ln) * C::ROWF + 32 * kcl + 8 * g),
@@ -648,18 +823,16 @@ __global__ __launch_bounds__(NT, (PassLds<C, MODE>::OCC)) void k_pass(PassArgs a
                 for (int at = 0; at < 4; ++at)
                     Y[at] = mma(ld_frag<C::F32>(s_rows + (16 * at + ln) * C::ROWF + 32 * kcl + 8 * g), mf, Y[at]);
             }
-            if (MODE != MODE_BWD_K && w < C::FBK) {
+            if (w < C::FBK) {
                 const frag zf = pack<C::F32>(Zacc[2 * fb], Zacc[2 * fb + 1]);
 #pragma unroll
                 for (int at = 0; at < 4; ++at)
                     Dacc[at] = mma(ld_frag<C::F32>(s_rows + (16 * at + ln) * C::ROWF + 32 * w + 8 * g), zf, Dacc[at]);
             }
-            if constexpr (MODE == MODE_FWD) {
-                if (causal) sketch_update<C>(fb, w, ln, g, s_cols, s_ZT, Macc, Zacc);
-            }
+            if (causal) sketch_update<C>(fb, w, ln, g, s_cols, s_ZT, Macc, Zacc);
             __syncthreads();
         }
-        // intra-sub-block term
+        // intra-sub-block term: scores of visible keys b <= a
         if (causal) {
             float dint = 0.f;
 #pragma unroll
@@ -668,24 +841,20 @@ __global__ __launch_bounds__(NT, (PassLds<C, MODE>::OCC)) void k_pass(PassArgs a
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int b = 16 * bt + 4 * g + i;
-                    const bool vis = (REV ? (b >= my) : (b <= my)) && b < nv;
+                    const bool vis = b <= my && b < nv;
                     v[i] = vis ? Sc[bt][i] : 0.f;
                     dint += v[i];
                 }
                 st_half<C::F32>(s_sc + my * C::ROWT + 16 * bt + 4 * g, v);
             }
-            if constexpr (MODE != MODE_BWD_K) {
-                dint = sum_groups(dint);
-                if (g == 0) f_Dint[my] = dint;
-            }
+            dint = sum_groups(dint);
+            if (g == 0) f_Dint[my] = dint;
         }
-        if constexpr (MODE != MODE_BWD_K) {
-            if (ln == 0) {
+        if (ln == 0) {
 #pragma unroll
-                for (int at = 0; at < 4; ++at)
+            for (int at = 0; at < 4; ++at)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) f_Dpart[w * TB + 16 * at + 4 * g + i] = Dacc[at][i];
-            }
+                for (int i = 0; i < 4; ++i) f_Dpart[w * TB + 16 * at + 4 * g + i] = Dacc[at][i];
         }
         __syncthreads();
         if (causal) {
@@ -697,307 +866,428 @@ __global__ __launch_bounds__(NT, (PassLds<C, MODE>::OCC)) void k_pass(PassArgs a
                     Y[at] = mma(ld_frag<C::F32>(s_sc + (16 * at + ln) * C::ROWT + 32 * s + 8 * g), zt, Y[at]);
             }
         }
-        // ----------------------- readout epilogues ----------------------------
-        if constexpr (MODE == MODE_FWD || MODE == MODE_BWD_Q) {
-            float rD[4][4];
 #pragma unroll
-            for (int at = 0; at < 4; ++at)
+        for (int at = 0; at < 4; ++at)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * at + 4 * g + i;
-                    float d = f_Dpart[r] + f_Dpart[TB + r] + f_Dpart[2 * TB + r] + f_Dpart[3 * TB + r];
-                    if (causal) d += f_Dint[r];
-                    rD[at][i] = rcp_(d);
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * at + 4 * g + i;
+                float d = f_Dpart[r] + f_Dpart[TB + r] + f_Dpart[2 * TB + r] + f_Dpart[3 * TB + r];
+                if (causal) d += f_Dint[r];
+                s_stage[r * C::ROWD + 16 * w + ln] = to_elem<C::F32>(Y[at][i] * rcp_(d));
+            }
+        if (a.Dv && tq == 0 && tok) {
+            float d = f_Dpart[tr] + f_Dpart[TB + tr] + f_Dpart[2 * TB + tr] + f_Dpart[3 * TB + tr];
+            if (causal) d += f_Dint[tr];
+            a.Dv[base + t0 + tr] = d;
+        }
+        __syncthreads();
+        store_stage<C>(a.out0, base + t0, tr, tq, tok, s_stage);
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// query-side backward: y = [dO/D | e] with e = -<dO, O>/D from the saved D and
+// the forward output; dA_Q = M y (sketch of the keys before the sub-block, plus
+// the intra-sub-block causal term), the corner-softmax chain rule, the
+// back-projection and the normalisation's chain rule -> dQ; also writes e.
+// ---------------------------------------------------------------------------
+template <class C>
+struct BwdQLds {
+    using elem = typename Prec<C::F32>::elem;
+    // bf16 residual of the y rows: the intra-sub-block product g.v + e
+    // cancels for the first keys of a sequence, so it is formed from
+    // y = hi + lo with float32 accumulation
+    static constexpr bool YLO = !C::F32;
+    static constexpr int n_ms = C::FBK * 32 * C::ROWE;          // sketch rows
+    static constexpr int n_cols = C::FBK * 32 * C::ROWT;        // key features transposed
+    static constexpr int n_zt = ZR * C::ROWT;                   // [v | 1] transposed
+    static constexpr int n_zr = TB * C::ROWE;                   // [v | 1] rows
+    static constexpr int n_yr = TB * C::ROWE;                   // y rows (hi)
+    static constexpr int n_ylo = YLO ? TB * C::ROWE : 0;        // y rows (lo)
+    static constexpr int o_ms = 0;
+    static constexpr int o_cols = o_ms + n_ms;
+    static constexpr int o_zt = o_cols + n_cols;
+    static constexpr int o_zr = o_zt + n_zt;
+    static constexpr int o_yr = o_zr + n_zr;
+    static constexpr int o_ylo = o_yr + n_yr;
+    static constexpr int o_w = o_ylo + n_ylo;
+    static constexpr int OCC = 1;
+    using WS = WStage<elem, o_w, 0, C::MT, OCC>;
+};
+
+template <class C>
+__global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
+    using elem = typename Prec<C::F32>::elem;
+    using frag = typename Prec<C::F32>::frag;
+    using LD = BwdQLds<C>;
+    __shared__ __attribute__((aligned(32))) elem lds[LD::WS::n_elem];
+    elem* s_ms = lds + LD::o_ms;
+    elem* s_cols = lds + LD::o_cols;
+    elem* s_ZT = lds + LD::o_zt;
+    elem* s_zr = lds + LD::o_zr;
+    elem* s_yr = lds + LD::o_yr;
+    elem* s_ylo = lds + LD::o_ylo;
+
+    const int lane = threadIdx.x & 63, ln = lane & 15, g = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int th = threadIdx.x, tr = th >> 2, tq = th & 3;
+    const int bh = blockIdx.y, c = blockIdx.x;
+    const int64_t seg0 = (int64_t)c * a.chunk;
+    const int64_t seg1 = seg0 + a.chunk < a.N ? seg0 + a.chunk : a.N;
+    const size_t base = (size_t)bh * a.N;
+    const elem* W = reinterpret_cast<const elem*>(a.W);
+    const elem* WTp = reinterpret_cast<const elem*>(a.WTp);
+    const bool causal = a.causal != 0;
+    elem* s_w = LD::WS::on ? lds + LD::o_w : nullptr;
+    if (LD::WS::on) stage_w<C>(W, a.L, s_w);
+    zero_pads<C>(s_ZT, s_zr, s_yr);
+    if (LD::YLO) zero_pads<C>(s_ZT, s_ylo, nullptr);
+    zero_sketch_pads<C>(s_ms);
+    __syncthreads();   // W' and the padding are written by all waves, read by each
+    const WSrc<C> wsrc{s_w, W, a.L};
+
+    f32x4 Macc[C::NKC * 2], Zacc[C::NOWN * 2];
+    load_state<C>(a.state + bh * a.state_bh_stride + c * a.state_chunk_stride, w, ln, g, Macc, Zacc);
+
+    const int nsub = (int)((seg1 - seg0 + TB - 1) / TB);
+    const int my = 16 * w + ln;
+
+    frag n_xa[2], n_xb[2], n_z[2], n_y[2], n_o[2];
+    float n_d = 1.f;
+    auto issue = [&](int it2) {
+        const int64_t t0 = seg0 + (int64_t)it2 * TB;
+        const int nv = (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
+        const bool ok = tr < nv;
+        load_row_raw<C::F32>(a.Xa, base + t0 + my, my < nv, g, n_xa);
+        if (causal) {
+            load_row_raw<C::F32>(a.Xb, base + t0 + my, my < nv, g, n_xb);
+            load_q16_raw<C::F32>(a.Zsrc, (base + t0 + tr) * DH + 16 * tq, ok, n_z);
+        }
+        load_q16_raw<C::F32>(a.Ysrc, (base + t0 + tr) * DH + 16 * tq, ok, n_y);
+        load_q16_raw<C::F32>(a.Osrc, (base + t0 + tr) * DH + 16 * tq, ok, n_o);
+        if (ok) n_d = a.Dv[base + t0 + tr];
+    };
+    issue(0);
+
+    for (int it = 0; it < nsub; ++it) {
+        const int64_t t0 = seg0 + (int64_t)it * TB;
+        const int nv = (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
+        const bool valid = my < nv;
+        const size_t row = base + t0 + my;
+        const bool tok = tr < nv;
+        frag xa[2] = {n_xa[0], n_xa[1]}, xb[2] = {n_xb[0], n_xb[1]};
+        frag zr[2] = {n_z[0], n_z[1]}, yr[2] = {n_y[0], n_y[1]}, orow[2] = {n_o[0], n_o[1]};
+        const float dd = n_d;
+        if (it + 1 < nsub) issue(it + 1);
+
+        float inv_a, nrm_a, inv_b = 0.f, nrm_b;
+        row_norm<C::F32>(xa, inv_a, nrm_a);
+        if (causal) {
+            row_norm<C::F32>(xb, inv_b, nrm_b);
+            write_aug<C>(zr, 1.f, tok ? 1.f : 0.f, s_ZT, s_zr);
+        }
+        // y = [dO / D | e], e = -<dO, O> / D; this thread holds 16 columns of row tr
+        {
+            float delta = 0.f;
+#pragma unroll
+            for (int cc = 0; cc < 16; ++cc) delta += q16_at<C::F32>(yr, cc) * q16_at<C::F32>(orow, cc);
+            delta += __shfl_xor(delta, 1);
+            delta += __shfl_xor(delta, 2);
+            const float rD = tok ? rcp_(dd) : 0.f;
+            const float e = -delta * rD;
+            float v[16];
+#pragma unroll
+            for (int cc = 0; cc < 16; ++cc) v[cc] = q16_at<C::F32>(yr, cc) * rD;
+            const frag h0 = pack8<C::F32>(v), h1 = pack8<C::F32>(v + 8);
+            st_frag<C::F32>(s_yr + tr * C::ROWE + 16 * tq, h0);
+            st_frag<C::F32>(s_yr + tr * C::ROWE + 16 * tq + 8, h1);
+            if constexpr (LD::YLO) {
+                float lo[16];
+#pragma unroll
+                for (int cc = 0; cc < 8; ++cc) {
+                    lo[cc] = v[cc] - elem_f<C::F32>(h0[cc]);
+                    lo[8 + cc] = v[8 + cc] - elem_f<C::F32>(h1[cc]);
                 }
-            if constexpr (MODE == MODE_FWD) {
+                st_frag<C::F32>(s_ylo + tr * C::ROWE + 16 * tq, pack8<C::F32>(lo));
+                st_frag<C::F32>(s_ylo + tr * C::ROWE + 16 * tq + 8, pack8<C::F32>(lo + 8));
+            }
+            if (tq == 0) {
+                const elem eh = to_elem<C::F32>(e);
+                s_yr[tr * C::ROWE + 64] = eh;
+                if constexpr (LD::YLO) s_ylo[tr * C::ROWE + 64] = to_elem<C::F32>(e - elem_f<C::F32>(eh));
+                if (tok) a.Ev[base + t0 + tr] = e;
+            }
+        }
+        __syncthreads();
+        frag Cf[2];
+        if (causal) intra_operand<C, false, LD::YLO>(s_zr, s_yr, s_ylo, w, ln, g, my, nv, Cf);
+        frag yf[3];
 #pragma unroll
-                for (int at = 0; at < 4; ++at)
+        for (int s = 0; s < 3; ++s) yf[s] = ld_frag<C::F32>(s_yr + my * C::ROWE + 32 * s + 8 * g);
+        f32x4 dX[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        s_stage[(16 * at + 4 * g + i) * C::ROWD + 16 * w + ln] = to_elem<C::F32>(Y[at][i] * rD[at][i]);
-                __syncthreads();
-                if (tok) {
-                    T* o = reinterpret_cast<T*>(a.out0) + (base + t0 + tr) * DH + 16 * tq;
-                    const elem* src = s_stage + tr * C::ROWD + 16 * tq;
-                    *reinterpret_cast<frag*>(o) = ld_frag<C::F32>(src);
-                    *reinterpret_cast<frag*>(o + 8) = ld_frag<C::F32>(src + 8);
-                }
-                __syncthreads();
-                continue;
-            } else {
-                // BWD_Q: O, delta = <dO, O>, e = -delta / D, y = [dO / D | e]
-                st_frag<C::F32>(s_stage + tr * C::ROWD + 16 * tq, yr[0]);
-                st_frag<C::F32>(s_stage + tr * C::ROWD + 16 * tq + 8, yr[1]);
-                __syncthreads();
+        for (int i = 0; i < 4; ++i) dX[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 dhp[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        // Every table's masses sum to the number of keys in the sketch, so the
+        // mass of a corner is that count / R plus a fluctuation: store the
+        // fluctuation (a per-table constant cancels in the chain rule).
+        const float zshift = (causal ? (float)t0 : (float)a.N) / (float)C::R;
 #pragma unroll
-                for (int at = 0; at < 4; ++at)
+        for (int fb = 0; fb < C::NBLK; ++fb) {
+            write_sketch_rows<C>(fb, w, ln, g, Macc, Zacc, zshift, s_ms);
+            if (causal) {
+                frag unused[C::FBK];
+                float unused_u[C::TPB][4];
+                block_features<C, false>(wsrc, fb, lane, w, ln, g, xb, inv_b, valid, a.beta, a.L, nullptr, s_cols,
+                                         unused, unused_u);
+            }
+            __syncthreads();
+            f32x4 G[C::FBK * 2];
+            block_grad<C>(ln, g, s_ms, yf, s_cols, Cf, causal, G);
+#pragma unroll
+            for (int tb = 0; tb < C::TPB; ++tb) {
+                const int t = fb * C::TPB + tb;
+                const f32x4 acc = wsrc.project(t, lane, ln, g, xa);
+                float hs[4], phi[C::KB * 8], u[4], s[4], dA[C::KB * 8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) hs[i] = acc[i] * inv_a;
+                soft_features<C>(t, g, hs, a.beta, a.L, phi, u, s);
+#pragma unroll
+                for (int kb = 0; kb < C::KB; ++kb) {
+                    const int kcl = tb * C::KB + kb;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int r = 16 * at + 4 * g + i;
-                        const float o = Y[at][i] * rD[at][i];
-                        float p = o * elem_f<C::F32>(s_stage[r * C::ROWD + 16 * w + ln]);
-                        p = sum_row16(p);
-                        if (ln == 0) f_dpart[w * TB + r] = p;
-                    }
-                __syncthreads();
-                {
-                    float D = 1.f, e = 0.f;
-                    if (tok) {
-                        D = f_Dpart[tr] + f_Dpart[TB + tr] + f_Dpart[2 * TB + tr] + f_Dpart[3 * TB + tr] +
-                            (causal ? f_Dint[tr] : 0.f);
-                        const float delta = f_dpart[tr] + f_dpart[TB + tr] + f_dpart[2 * TB + tr] + f_dpart[3 * TB + tr];
-                        e = -delta * rcp_(D);
-                    }
-                    const float sc = tok ? rcp_(D) : 0.f;
-                    float v[16];
-#pragma unroll
-                    for (int cc = 0; cc < 16; ++cc) v[cc] = q16_at<C::F32>(yr, cc) * sc;
-                    const frag h0 = pack8<C::F32>(v), h1 = pack8<C::F32>(v + 8);
-                    st_frag<C::F32>(s_yr + tr * C::ROWE + 16 * tq, h0);
-                    st_frag<C::F32>(s_yr + tr * C::ROWE + 16 * tq + 8, h1);
-                    if constexpr (LD::YLO) {
-                        float lo[16];
-#pragma unroll
-                        for (int cc = 0; cc < 8; ++cc) {
-                            lo[cc] = v[cc] - elem_f<C::F32>(h0[cc]);
-                            lo[8 + cc] = v[8 + cc] - elem_f<C::F32>(h1[cc]);
-                        }
-                        st_frag<C::F32>(s_ylo + tr * C::ROWE + 16 * tq, pack8<C::F32>(lo));
-                        st_frag<C::F32>(s_ylo + tr * C::ROWE + 16 * tq + 8, pack8<C::F32>(lo + 8));
-                    }
-                    if (tq == 0) {
-                        const elem eh = to_elem<C::F32>(e);
-                        s_yr[tr * C::ROWE + 64] = eh;
-                        if constexpr (LD::YLO) s_ylo[tr * C::ROWE + 64] = to_elem<C::F32>(e - elem_f<C::F32>(eh));
-                        if (tok) {
-                            a.Dv[base + t0 + tr] = D;
-                            a.Ev[base + t0 + tr] = e;
-                        }
+                        dA[kb * 8 + i] = G[2 * kcl][i];
+                        dA[kb * 8 + 4 + i] = G[2 * kcl + 1][i];
                     }
                 }
-                __syncthreads();
+                chain_backproject<C>(t, lane, phi, dA, u, a.beta, WTp, dhp, dX);
             }
-        } else {
-            // BWD_K: dV = Y (value columns); y rows = [v | 1]
-#pragma unroll
-            for (int at = 0; at < 4; ++at)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    s_stage[(16 * at + 4 * g + i) * C::ROWD + 16 * w + ln] = to_elem<C::F32>(Y[at][i]);
-            {
-                float v[16];
-#pragma unroll
-                for (int cc = 0; cc < 16; ++cc) v[cc] = q16_at<C::F32>(yr, cc);
-                st_frag<C::F32>(s_yr + tr * C::ROWE + 16 * tq, pack8<C::F32>(v));
-                st_frag<C::F32>(s_yr + tr * C::ROWE + 16 * tq + 8, pack8<C::F32>(v + 8));
-                if (tq == 0) s_yr[tr * C::ROWE + 64] = to_elem<C::F32>(tok ? 1.f : 0.f);
-            }
-            __syncthreads();
-            if (tok) {
-                T* o = reinterpret_cast<T*>(a.out1) + (base + t0 + tr) * DH + 16 * tq;
-                const elem* src = s_stage + tr * C::ROWD + 16 * tq;
-                *reinterpret_cast<frag*>(o) = ld_frag<C::F32>(src);
-                *reinterpret_cast<frag*>(o + 8) = ld_frag<C::F32>(src + 8);
-            }
+            if (causal) sketch_update<C>(fb, w, ln, g, s_cols, s_ZT, Macc, Zacc);
             __syncthreads();
         }
-        if constexpr (BWD) {
-            // ----------------------------- phase 2 ---------------------------
-            frag Cf[2];
-            if (causal) {
-                f32x4 Cc[4];
-                frag yf[3];
+        store_dx<C>(a.Xa, a.out0, row, valid, g, inv_a, nrm_a, dX);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// key-side backward, one pass over the feature blocks (sub-blocks in reverse):
+//   dV_a  = phi_a^T T_g  (+ intra: sum_{b >= a} <phi_b, phi_a> g_b)
+//   dA_K  = T [v_a | 1]  (+ intra: phi_b^T Cc, Cc[b][a] = g_b . v_a + e_b)
+// with T = sum_{b} phi_b^T [dO_b / D_b | e_b] over the queries after the
+// sub-block (the reverse sketch); then the chain rule -> dK.
+// ---------------------------------------------------------------------------
+template <class C>
+struct BwdKLds {
+    using elem = typename Prec<C::F32>::elem;
+    static constexpr int n_rows = TB * C::ROWF;                 // key features [64][ROWF]
+    static constexpr int n_brow = TB * C::ROWF;                 // query features [64][ROWF]
+    static constexpr int n_cols = C::FBK * 32 * C::ROWT;        // query features transposed
+    static constexpr int n_ms = C::FBK * 32 * C::ROWE;          // sketch rows
+    static constexpr int n_zt = ZR * C::ROWT;                   // [g | e] transposed
+    static constexpr int n_sc = TB * C::ROWT;                   // intra scores [a][b] (alias of cols | ms)
+    static constexpr int n_zr = TB * C::ROWE;                   // [g | e] rows
+    static constexpr int n_yr = TB * C::ROWE;                   // [v | 1] rows
+    static constexpr int n_stage = TB * C::ROWD;                // dV staging (alias of rows | brow)
+    static_assert(n_stage <= n_rows + n_brow, "staging must fit the feature tiles");
+    static_assert(n_sc <= n_cols + n_ms, "intra scores must fit the sketch tiles");
+    static constexpr int o_rows = 0;
+    static constexpr int o_brow = o_rows + n_rows;
+    static constexpr int o_cols = o_brow + n_brow;
+    static constexpr int o_ms = o_cols + n_cols;
+    static constexpr int o_sc = o_cols;
+    static constexpr int o_zt = o_ms + n_ms;
+    static constexpr int o_zr = o_zt + n_zt;
+    static constexpr int o_yr = o_zr + n_zr;
+    static constexpr int o_w = o_yr + n_yr;
+    static constexpr int OCC = 1;
+    using WS = WStage<elem, o_w, 0, C::MT, OCC>;
+};
+
+template <class C>
+__global__ __launch_bounds__(NT, (BwdKLds<C>::OCC)) void k_bwd_k(PassArgs a) {
+    using elem = typename Prec<C::F32>::elem;
+    using frag = typename Prec<C::F32>::frag;
+    using LD = BwdKLds<C>;
+    __shared__ __attribute__((aligned(32))) elem lds[LD::WS::n_elem];
+    elem* s_rows = lds + LD::o_rows;
+    elem* s_brow = lds + LD::o_brow;
+    elem* s_cols = lds + LD::o_cols;
+    elem* s_ms = lds + LD::o_ms;
+    elem* s_ZT = lds + LD::o_zt;
+    elem* s_sc = lds + LD::o_sc;
+    elem* s_zr = lds + LD::o_zr;
+    elem* s_yr = lds + LD::o_yr;
+    elem* s_stage = lds + LD::o_rows;   // alias after the feature-block loop
+
+    const int lane = threadIdx.x & 63, ln = lane & 15, g = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int th = threadIdx.x, tr = th >> 2, tq = th & 3;
+    const int bh = blockIdx.y, c = blockIdx.x;
+    const int64_t seg0 = (int64_t)c * a.chunk;
+    const int64_t seg1 = seg0 + a.chunk < a.N ? seg0 + a.chunk : a.N;
+    const size_t base = (size_t)bh * a.N;
+    const elem* W = reinterpret_cast<const elem*>(a.W);
+    const elem* WTp = reinterpret_cast<const elem*>(a.WTp);
+    const bool causal = a.causal != 0;
+    elem* s_w = LD::WS::on ? lds + LD::o_w : nullptr;
+    if (LD::WS::on) stage_w<C>(W, a.L, s_w);
+    zero_pads<C>(s_ZT, s_zr, s_yr);
+    zero_sketch_pads<C>(s_ms);
+    __syncthreads();   // W' and the padding are written by all waves, read by each
+    const WSrc<C> wsrc{s_w, W, a.L};
+
+    f32x4 Macc[C::NKC * 2], Zacc[C::NOWN * 2];
+    load_state<C>(a.state + bh * a.state_bh_stride + c * a.state_chunk_stride, w, ln, g, Macc, Zacc);
+
+    const int nsub = (int)((seg1 - seg0 + TB - 1) / TB);
+    const int my = 16 * w + ln;
+
+    frag n_xa[2], n_xb[2], n_z[2], n_y[2];
+    float n_d = 1.f, n_e = 0.f;
+    auto issue = [&](int it2) {
+        const int64_t t0 = seg0 + (int64_t)(nsub - 1 - it2) * TB;
+        const int nv = (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
+        const bool ok = tr < nv;
+        load_row_raw<C::F32>(a.Xa, base + t0 + my, my < nv, g, n_xa);
+        if (causal) {
+            load_row_raw<C::F32>(a.Xb, base + t0 + my, my < nv, g, n_xb);
+            load_q16_raw<C::F32>(a.Zsrc, (base + t0 + tr) * DH + 16 * tq, ok, n_z);
+            if (ok) {
+                n_d = a.Dv[base + t0 + tr];
+                n_e = a.Ev[base + t0 + tr];
+            }
+        }
+        load_q16_raw<C::F32>(a.Ysrc, (base + t0 + tr) * DH + 16 * tq, ok, n_y);
+    };
+    issue(0);
+
+    for (int it = 0; it < nsub; ++it) {
+        const int64_t t0 = seg0 + (int64_t)(nsub - 1 - it) * TB;
+        const int nv = (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
+        const bool valid = my < nv;
+        const size_t row = base + t0 + my;
+        const bool tok = tr < nv;
+        frag xa[2] = {n_xa[0], n_xa[1]}, xb[2] = {n_xb[0], n_xb[1]};
+        frag zr[2] = {n_z[0], n_z[1]}, yr[2] = {n_y[0], n_y[1]};
+        const float zd = n_d, ze = n_e;
+        if (it + 1 < nsub) issue(it + 1);
+
+        float inv_a, nrm_a, inv_b = 0.f, nrm_b;
+        row_norm<C::F32>(xa, inv_a, nrm_a);
+        if (causal) {
+            row_norm<C::F32>(xb, inv_b, nrm_b);
+            write_aug<C>(zr, tok ? rcp_(zd) : 0.f, tok ? ze : 0.f, s_ZT, s_zr);
+        }
+        // y rows = [v | 1]
+        {
+            float v[16];
 #pragma unroll
-                for (int s = 0; s < 3; ++s) yf[s] = ld_frag<C::F32>(s_yr + my * C::ROWE + 32 * s + 8 * g);
+            for (int cc = 0; cc < 16; ++cc) v[cc] = q16_at<C::F32>(yr, cc);
+            st_frag<C::F32>(s_yr + tr * C::ROWE + 16 * tq, pack8<C::F32>(v));
+            st_frag<C::F32>(s_yr + tr * C::ROWE + 16 * tq + 8, pack8<C::F32>(v + 8));
+            if (tq == 0) s_yr[tr * C::ROWE + 64] = to_elem<C::F32>(tok ? 1.f : 0.f);
+        }
+        __syncthreads();
+        frag Cf[2];
+        if (causal) intra_operand<C, true, false>(s_zr, s_yr, nullptr, w, ln, g, my, nv, Cf);
+        // where the intra scores of the previous sub-block reached into the
+        // sketch rows, their padding is cleared again
+        if constexpr (LD::n_sc > LD::n_cols) zero_sketch_pads<C>(s_ms);
+        frag yf[3];
+#pragma unroll
+        for (int s = 0; s < 3; ++s) yf[s] = ld_frag<C::F32>(s_yr + my * C::ROWE + 32 * s + 8 * g);
+        f32x4 Y[4], Sc[4], dX[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            Y[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            Sc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            dX[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        f32x4 dhp[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int fb = 0; fb < C::NBLK; ++fb) {
+            frag phiA[C::FBK], unused[C::FBK];
+            float uA[C::TPB][4], unused_u[C::TPB][4];
+            block_features<C, true>(wsrc, fb, lane, w, ln, g, xa, inv_a, valid, a.beta, a.L, s_rows, nullptr, phiA,
+                                    uA);
+            if (causal)
+                block_features<C, false>(wsrc, fb, lane, w, ln, g, xb, inv_b, valid, a.beta, a.L, s_brow, s_cols,
+                                         unused, unused_u);
+            write_sketch_rows<C>(fb, w, ln, g, Macc, Zacc, 0.f, s_ms);
+            __syncthreads();
+            if (causal) {
 #pragma unroll
                 for (int bt = 0; bt < 4; ++bt) {
-                    Cc[bt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    const bool vis = REV ? (bt >= w) : (bt <= w);
-                    if (vis) {
+                    if (bt >= w) {
 #pragma unroll
-                        for (int s = 0; s < 3; ++s) {
-                            const frag zf = ld_frag<C::F32>(s_zr + (16 * bt + ln) * C::ROWE + 32 * s + 8 * g);
-                            Cc[bt] = mma(zf, yf[s], Cc[bt]);
-                            if constexpr (LD::YLO)
-                                Cc[bt] = mma(zf, ld_frag<C::F32>(s_ylo + my * C::ROWE + 32 * s + 8 * g), Cc[bt]);
-                        }
+                        for (int kcl = 0; kcl < C::FBK; ++kcl)
+                            Sc[bt] = mma(ld_frag<C::F32>(s_brow + (16 * bt + ln) * C::ROWF + 32 * kcl + 8 * g),
+                                         phiA[kcl], Sc[bt]);
                     }
+                }
+            }
+            // dV readout of the value columns of this wave (before this block's update)
+#pragma unroll
+            for (int kcl = 0; kcl < C::FBK; ++kcl) {
+                const int kc = fb * C::FBK + kcl;
+                const frag mf = pack<C::F32>(Macc[2 * kc], Macc[2 * kc + 1]);
+#pragma unroll
+                for (int at = 0; at < 4; ++at)
+                    Y[at] = mma(ld_frag<C::F32>(s_rows + (16 * at + ln) * C::ROWF + 32 * kcl + 8 * g), mf, Y[at]);
+            }
+            f32x4 G[C::FBK * 2];
+            block_grad<C>(ln, g, s_ms, yf, s_cols, Cf, causal, G);
+#pragma unroll
+            for (int tb = 0; tb < C::TPB; ++tb) {
+                const int t = fb * C::TPB + tb;
+                float phi[C::KB * 8], dA[C::KB * 8];
+#pragma unroll
+                for (int kb = 0; kb < C::KB; ++kb) {
+                    const int kcl = tb * C::KB + kb;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) phi[kb * 8 + j] = elem_f<C::F32>(phiA[kcl][j]);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int b = 16 * bt + 4 * g + i;
-                        const bool v2 = (REV ? (b >= my) : (b <= my)) && b < nv;
-                        if (!v2) Cc[bt][i] = 0.f;
+                        dA[kb * 8 + i] = G[2 * kcl][i];
+                        dA[kb * 8 + 4 + i] = G[2 * kcl + 1][i];
                     }
                 }
-                Cf[0] = pack<C::F32>(Cc[0], Cc[1]);
-                Cf[1] = pack<C::F32>(Cc[2], Cc[3]);
+                chain_backproject<C>(t, lane, phi, dA, uA[tb], a.beta, WTp, dhp, dX);
             }
-            frag yf[3];
-#pragma unroll
-            for (int s = 0; s < 3; ++s) yf[s] = ld_frag<C::F32>(s_yr + my * C::ROWE + 32 * s + 8 * g);
-            // zero the padding columns 65..95 of the sketch rows once
-            for (int idx = threadIdx.x; idx < C::FBK * 32 * 31; idx += NT) {
-                const int r = idx / 31, cc = 65 + idx % 31;
-                s_ms[r * C::ROWE + cc] = to_elem<C::F32>(0.f);
-            }
-            f32x4 dX[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dX[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-            f32x4 dhp[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-            for (int fb = 0; fb < C::NBLK; ++fb) {
-                // sketch rows of this block (before this sub-block's update). Only
-                // dA - <a, dA> per table is used below, so each table's corner mean is
-                // subtracted in fp32 first: the bf16 operand then carries the part that
-                // survives instead of a large common offset. A lane holds every corner
-                // of its tables for its value column.
-#pragma unroll
-                for (int tb = 0; tb < C::TPB; ++tb) {
-                    float v[C::KB * 8];
-#pragma unroll
-                    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-                        for (int h = 0; h < 2; ++h)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                v[kb * 8 + 4 * h + i] = Macc[2 * (fb * C::FBK + tb * C::KB + kb) + h][i];
-                    constexpr int RR = (C::P == 4) ? 16 : C::R;
-#pragma unroll
-                    for (int t0c = 0; t0c < C::KB * 8; t0c += RR) {
-                        float m = 0.f;
-#pragma unroll
-                        for (int r = 0; r < RR; ++r) m += v[t0c + r];
-                        m *= 1.f / (float)RR;
-#pragma unroll
-                        for (int r = 0; r < RR; ++r) v[t0c + r] -= m;
-                    }
-#pragma unroll
-                    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-                        for (int h = 0; h < 2; ++h)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                const int fl = 32 * (tb * C::KB + kb) + 8 * g + 4 * h + i;
-                                s_ms[fl * C::ROWE + 16 * w + ln] = to_elem<C::F32>(v[kb * 8 + 4 * h + i]);
-                            }
-                }
-                if (w < C::FBK && ln == 0) {
-                    // Query side: every table's masses sum to the number n of keys in the
-                    // state, so z_r = n/R + (small fluctuation). A per-table constant in dA
-                    // cancels in a * (dA - <a, dA>), so store z_r - n/R: the bf16 operand
-                    // then keeps the fluctuation instead of rounding it away at large n.
-                    const float zshift = (MODE == MODE_BWD_Q) ? (causal ? (float)t0 : (float)a.N) / (float)C::R : 0.f;
-#pragma unroll
-                    for (int h = 0; h < 2; ++h)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            s_ms[(32 * w + 8 * g + 4 * h + i) * C::ROWE + 64] =
-                                to_elem<C::F32>(Zacc[2 * fb + h][i] - zshift);
-                }
-                // b-side features (own tile) -> transposed tile
-                {
-                    frag unused[C::FBK];
-                    block_features<C, false>(wsrc, fb, lane, w, ln, g, xb, inv_b, valid, a.beta, a.L, nullptr, s_cols,
-                                             unused);
-                }
-                __syncthreads();
-                f32x4 G[C::FBK * 2];
-#pragma unroll
-                for (int m = 0; m < C::FBK * 2; ++m) {
-                    const int kcl = m >> 1, h = m & 1;
-                    const int fl = 32 * kcl + canon_of_row(h, ln);
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s = 0; s < 3; ++s)
-                        acc = mma(ld_frag<C::F32>(s_ms + fl * C::ROWE + 32 * s + 8 * g), yf[s], acc);
-                    if (causal) {
-#pragma unroll
-                        for (int s2 = 0; s2 < 2; ++s2) {
-                            const elem* p = s_cols + fl * C::ROWT + 32 * s2 + 4 * g;
-                            acc = mma(ld_frag2<C::F32>(p, p + 16), Cf[s2], acc);
-                        }
-                    }
-                    G[m] = acc;
-                }
-                // chain rule and back-projection, tile by tile
-#pragma unroll
-                for (int tb = 0; tb < C::TPB; ++tb) {
-                    const int t = fb * C::TPB + tb;
-                    const f32x4 acc = wsrc.project(t, lane, ln, g, xa);
-                    float hs[4], phi[C::KB * 8], u[4], s[4], dA[C::KB * 8], dh[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) hs[i] = acc[i] * inv_a;
-                    soft_features<C>(t, g, hs, a.beta, a.L, phi, u, s);
-#pragma unroll
-                    for (int kb = 0; kb < C::KB; ++kb) {
-                        const int kcl = tb * C::KB + kb;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            dA[kb * 8 + i] = G[2 * kcl][i];
-                            dA[kb * 8 + 4 + i] = G[2 * kcl + 1][i];
-                        }
-                    }
-                    soft_features_backward<C>(phi, dA, u, a.beta, dh);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) dhp[t & 1][i] = dh[i];
-                    if ((t & 1) == 1 || t == C::MT - 1) {
-                        const frag df = pack<C::F32>(dhp[0], (t & 1) ? dhp[1] : f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-                        for (int dt = 0; dt < 4; ++dt)
-                            dX[dt] = mma(ld_frag<C::F32>(WTp + ((size_t)((t >> 1) * 4 + dt) * 64 + lane) * 8), df, dX[dt]);
-                        dhp[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-                        dhp[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    }
-                }
-                // sketch update for this block
-                if (causal) sketch_update<C>(fb, w, ln, g, s_cols, s_ZT, Macc, Zacc);
-                __syncthreads();
-            }
-            // dx = (dx_hat - x_hat <x_hat, dx_hat>) / |x|
-            {
-                float xv[4][4];
-                float radial = 0.f;
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt) {
-                    const size_t off = row * DH + 16 * dt + 4 * g;
-                    if constexpr (C::F32) {
-                        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-                        if (valid) v = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(a.Xa) + off);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) xv[dt][i] = v[i];
-                    } else {
-                        bf16x4 v = {};
-                        if (valid) v = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(a.Xa) + off);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) xv[dt][i] = valid ? (float)v[i] : 0.f;
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) radial += xv[dt][i] * inv_a * dX[dt][i];
-                }
-                radial = sum_groups(radial);
-                const bool tangent = nrm_a > NORM_EPS;
-                if (valid) {
-#pragma unroll
-                    for (int dt = 0; dt < 4; ++dt) {
-                        f32x4 o;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            o[i] = (tangent ? dX[dt][i] - xv[dt][i] * inv_a * radial : dX[dt][i]) * inv_a;
-                        using T = typename In<C::F32>::T;
-                        T* dst = reinterpret_cast<T*>(a.out0) + row * DH + 16 * dt + 4 * g;
-                        if constexpr (C::F32) {
-                            *reinterpret_cast<f32x4*>(dst) = o;
-                        } else {
-                            bf16x4 ob;
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) ob[i] = (__bf16)o[i];
-                            *reinterpret_cast<bf16x4*>(dst) = ob;
-                        }
-                    }
-                }
-            }
+            if (causal) sketch_update<C>(fb, w, ln, g, s_cols, s_ZT, Macc, Zacc);
             __syncthreads();
         }
+        // intra-sub-block dV: queries b >= a
+        if (causal) {
+#pragma unroll
+            for (int bt = 0; bt < 4; ++bt) {
+                f32x4 v;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int b = 16 * bt + 4 * g + i;
+                    v[i] = (b >= my && b < nv) ? Sc[bt][i] : 0.f;
+                }
+                st_half<C::F32>(s_sc + my * C::ROWT + 16 * bt + 4 * g, v);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const frag zt = ld_frag<C::F32>(s_ZT + (16 * w + ln) * C::ROWT + 32 * s + 8 * g);
+#pragma unroll
+                for (int at = 0; at < 4; ++at)
+                    Y[at] = mma(ld_frag<C::F32>(s_sc + (16 * at + ln) * C::ROWT + 32 * s + 8 * g), zt, Y[at]);
+            }
+        }
+#pragma unroll
+        for (int at = 0; at < 4; ++at)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                s_stage[(16 * at + 4 * g + i) * C::ROWD + 16 * w + ln] = to_elem<C::F32>(Y[at][i]);
+        __syncthreads();
+        store_stage<C>(a.out1, base + t0, tr, tq, tok, s_stage);
+        store_dx<C>(a.Xa, a.out0, row, valid, g, inv_a, nrm_a, dX);
     }
 }
 

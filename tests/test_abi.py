@@ -43,14 +43,30 @@ def test_status_strings():
 
 
 def test_workspace_and_saved_sizes():
-    # causal: per-chunk states of F * 65 floats; F = 32 * MT * KB
-    fwd = race.workspace_bytes(1, 4, 12_000_000, 64, 4, 16, True, 1024, False)
-    bwd = race.workspace_bytes(1, 4, 12_000_000, 64, 4, 16, True, 1024, True)
-    saved = race.saved_bytes(1, 4, 12_000_000, 64, 4, 16, True, 1024)
-    nchunks = -(-12_000_000 // 1024)
-    assert saved == 4 * nchunks * 256 * 65 * 4
-    assert fwd >= saved and bwd >= 2 * saved + 2 * 4 * 12_000_000 * 4
-    assert race.saved_bytes(2, 3, 100, 64, 2, 8, False, 64) == 6 * 32 * 65 * 4
+    # causal: per-chunk states of F * 65 floats (F = 32 * MT * KB), then one
+    # float32 denominator per token
+    N = 12_000_000
+    fwd = race.workspace_bytes(1, 4, N, 64, 4, 16, True, 1024, race.WS_FWD)
+    bwd = race.workspace_bytes(1, 4, N, 64, 4, 16, True, 1024, race.WS_BWD)
+    rec = race.workspace_bytes(1, 4, N, 64, 4, 16, True, 1024, race.WS_BWD_RECOMPUTE)
+    saved = race.saved_bytes(1, 4, N, 64, 4, 16, True, 1024)
+    nchunks = -(-N // 1024)
+    states = 4 * nchunks * 256 * 65 * 4
+    assert saved == -(-states // 256) * 256 + 4 * N * 4
+    assert fwd >= states
+    # gradient states and e per token
+    assert bwd >= states + 4 * N * 4
+    # plus a saved buffer and the forward output (float32 bound)
+    assert rec >= fwd + bwd + saved + 4 * N * 64 * 4
+    states_nc = 6 * 32 * 65 * 4
+    assert race.saved_bytes(2, 3, 100, 64, 2, 8, False, 64) == -(-states_nc // 256) * 256 + 6 * 100 * 4
+
+
+def test_workspace_kind_rejected():
+    out = ctypes.c_size_t(0)
+    for kind in (-1, 3):
+        assert race.lib().race_attn_workspace_bytes(1, 1, 10, 64, 4, 8, 1, 16, kind, ctypes.byref(out)) == \
+            race.RACE_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("args,code", [
@@ -72,7 +88,7 @@ def test_workspace_bytes_rejects(args, code):
 def test_forward_argument_errors_before_device_work():
     L = race.lib()
     ok = (FAKE, FAKE, FAKE, FAKE, 1, 1, 100, 64, 4, 8, 1.0, 1, 64, race.RACE_BF16, FAKE, None, FAKE)
-    need = race.workspace_bytes(1, 1, 100, 64, 4, 8, True, 64, False)
+    need = race.workspace_bytes(1, 1, 100, 64, 4, 8, True, 64, race.WS_FWD)
     # null query
     assert L.race_attn_fwd(None, *ok[1:], need, None) == race.RACE_ERR_INVALID_ARG
     # bad dtype
@@ -90,12 +106,25 @@ def test_forward_argument_errors_before_device_work():
 
 def test_backward_and_hash_argument_errors():
     L = race.lib()
-    need = race.workspace_bytes(1, 1, 100, 64, 4, 8, False, 64, True)
-    args = [FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 100, 64, 4, 8, 1.0, 0, 64, race.RACE_F32,
+    need = race.workspace_bytes(1, 1, 100, 64, 4, 8, False, 64, race.WS_BWD_RECOMPUTE)
+    need_saved = race.workspace_bytes(1, 1, 100, 64, 4, 8, False, 64, race.WS_BWD)
+    assert need_saved < need
+    # Q K V W O dO saved
+    args = [FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 1, 1, 100, 64, 4, 8, 1.0, 0, 64, race.RACE_F32,
             FAKE, FAKE, FAKE, FAKE]
     assert L.race_attn_bwd(*args, need - 1, None) == race.RACE_ERR_WORKSPACE
-    a2 = list(args); a2[16] = None   # dQ
+    a2 = list(args); a2[17] = None   # dQ
     assert L.race_attn_bwd(*a2, need, None) == race.RACE_ERR_INVALID_ARG
+    # O without saved, saved without O
+    a3 = list(args); a3[4] = FAKE
+    assert L.race_attn_bwd(*a3, need, None) == race.RACE_ERR_INVALID_ARG
+    a4 = list(args); a4[6] = FAKE
+    assert L.race_attn_bwd(*a4, need, None) == race.RACE_ERR_INVALID_ARG
+    # both given: the smaller workspace is enough, one byte less is not
+    a5 = list(args); a5[4] = FAKE; a5[6] = FAKE
+    assert L.race_attn_bwd(*a5, need_saved - 1, None) == race.RACE_ERR_WORKSPACE
+    assert L.race_attn_hash(FAKE, FAKE, 1, 1, 10, 64, 4, 8, race.RACE_F32, None, FAKE, None) == \
+        race.RACE_ERR_INVALID_ARG
     assert L.race_attn_hash(FAKE, FAKE, 1, 1, 10, 64, 4, 8, race.RACE_F32, None, FAKE, None) == \
         race.RACE_ERR_INVALID_ARG
     assert L.race_attn_hash(FAKE, FAKE, 1, 1, 10, 64, 6, 8, race.RACE_F32, FAKE, FAKE, None) == \

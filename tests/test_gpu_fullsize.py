@@ -60,7 +60,8 @@ def test_fullsize_causal(name):
     T["dO"][:, :, PREFIX:, :] = 0
     saved = race.alloc_saved(w.B, w.H, w.N, w.P, w.L, True, w.chunk, dev)
     O = race.forward(T["Q"], T["K"], T["V"], Wd, w.P, w.L, 1.0, True, w.chunk, saved=saved)
-    dQ, dK, dV = race.backward(T["Q"], T["K"], T["V"], Wd, T["dO"], w.P, w.L, 1.0, True, w.chunk, saved=saved)
+    dQ, dK, dV = race.backward(T["Q"], T["K"], T["V"], Wd, T["dO"], w.P, w.L, 1.0, True, w.chunk, O=O,
+                               saved=saved)
     torch.cuda.synchronize()
     for t, nm in ((O, "O"), (dQ, "dQ"), (dK, "dK"), (dV, "dV")):
         assert bool(torch.isfinite(t).all()), nm
@@ -86,12 +87,12 @@ def test_fullsize_causal(name):
 
     # determinism of the whole backward (random dO everywhere)
     synth.normal_device(w.seed, synth.TID_DO, T["dO"])
-    race.backward(T["Q"], T["K"], T["V"], Wd, T["dO"], w.P, w.L, 1.0, True, w.chunk, saved=saved,
+    race.backward(T["Q"], T["K"], T["V"], Wd, T["dO"], w.P, w.L, 1.0, True, w.chunk, O=O, saved=saved,
                   grads=(dQ, dK, dV))
     torch.cuda.synchronize()
     c1 = [_checksum(t) for t in (dQ, dK, dV)]
     assert all(bool(torch.isfinite(t).all()) for t in (dQ, dK, dV))
-    race.backward(T["Q"], T["K"], T["V"], Wd, T["dO"], w.P, w.L, 1.0, True, w.chunk, saved=saved,
+    race.backward(T["Q"], T["K"], T["V"], Wd, T["dO"], w.P, w.L, 1.0, True, w.chunk, O=O, saved=saved,
                   grads=(dQ, dK, dV))
     torch.cuda.synchronize()
     assert c1 == [_checksum(t) for t in (dQ, dK, dV)]

@@ -36,10 +36,14 @@ def run_case(race, B, H, N, P, L, dtype, causal, chunk, beta=1.0, dist="normal",
     x = host_inputs(seed, B, H, N, 64, P, L, dtype, dist)
     dev = torch.device("cuda:0")
     T = {k: to_torch(v, dev) for k, v in x.items()}
-    O = race.forward(T["Q"], T["K"], T["V"], T["W"], P, L, beta, causal, chunk)
+    # the training path: the forward keeps its sketch states and denominators,
+    # the backward takes them with O
+    saved = race.alloc_saved(B, H, N, P, L, causal, chunk, dev) if backward else None
+    O = race.forward(T["Q"], T["K"], T["V"], T["W"], P, L, beta, causal, chunk, saved=saved)
     grads = None
     if backward:
-        grads = race.backward(T["Q"], T["K"], T["V"], T["W"], T["dO"], P, L, beta, causal, chunk)
+        grads = race.backward(T["Q"], T["K"], T["V"], T["W"], T["dO"], P, L, beta, causal, chunk, O=O,
+                              saved=saved)
     torch.cuda.synchronize()
     res = {"O": from_torch(O)}
     if grads:
@@ -173,7 +177,8 @@ def test_saved_states_roundtrip(lib):
     for causal in (True, False):
         saved = lib.alloc_saved(1, 2, 700, 4, 16, causal, 256, dev)
         O = lib.forward(T["Q"], T["K"], T["V"], T["W"], 4, 16, 1.0, causal, 256, saved=saved)
-        g1 = lib.backward(T["Q"], T["K"], T["V"], T["W"], T["dO"], 4, 16, 1.0, causal, 256, saved=saved)
+        g1 = lib.backward(T["Q"], T["K"], T["V"], T["W"], T["dO"], 4, 16, 1.0, causal, 256, O=O, saved=saved)
+        # without O and saved the forward is recomputed inside the call: same kernels, same bits
         g0 = lib.backward(T["Q"], T["K"], T["V"], T["W"], T["dO"], 4, 16, 1.0, causal, 256)
         torch.cuda.synchronize()
         for a, b in zip(g0, g1):
