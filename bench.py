@@ -24,6 +24,7 @@ if ROOT not in sys.path:
 HBM_PEAK = 8.0e12           # bytes/s, MI355X HBM3E
 MFMA_PEAK = {"bf16": 2.5e15, "f32": 157.3e12}   # dense matrix FLOP/s
 
+COPY_BYTES = 1 << 30        # reference copy: reads and writes this many bytes
 METRIC = "RACE MHA layer fwd+bwd tokens/s (causal, N=12M) + % of HBM/MFMA roofline"
 
 
@@ -94,6 +95,9 @@ def main():
     ap.add_argument("--workload", default="causal_long_n12M")
     ap.add_argument("--cpu-sample", type=int, default=131072)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 1 GiB device-to-device copy before the steps (the reference "
+                         "dispatch for scaling HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -124,6 +128,14 @@ def main():
     ws_b = race.alloc_workspace(w.B, w.H, w.N, w.P, w.L, w.causal, w.chunk, race.WS_BWD, dev)
     saved = race.alloc_saved(w.B, w.H, w.N, w.P, w.L, w.causal, w.chunk, dev)
     torch.cuda.synchronize()
+
+    if args.calibrate_copy:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step():
         race.forward(t["Q"], t["K"], t["V"], t["W"], w.P, w.L, w.beta, w.causal, w.chunk, out=O,

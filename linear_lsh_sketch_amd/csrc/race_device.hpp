@@ -157,14 +157,18 @@ __device__ inline float rcp_(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ inline float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr float LOG2E = 1.4426950408889634f;
 
-// tanh(x) = sign(x) (1 - e^{-2|x|}) / (1 + e^{-2|x|})
-__device__ inline float fast_tanh(float x) {
-    const float t = exp2_(-2.f * LOG2E * fabsf(x));
-    return copysignf((1.f - t) * rcp_(1.f + t), x);
+// Reciprocals of four values with one hardware reciprocal: 1/q_i = (product
+// of the other three) / (product of all four). For q_i in [1, 2] (the only
+// use here) the products stay in [1, 16], so this costs a few ulp.
+__device__ inline void rcp4(const float q[4], float r[4]) {
+    const float a = q[0] * q[1], b = q[2] * q[3];
+    const float z = rcp_(a * b);
+    const float za = z * b, zb = z * a;   // 1/a, 1/b
+    r[0] = za * q[1];
+    r[1] = za * q[0];
+    r[2] = zb * q[3];
+    r[3] = zb * q[2];
 }
-
-// sigmoid(x) = 1 / (1 + e^{-x})
-__device__ inline float sigmoidf_(float x) { return rcp_(1.f + exp2_(-LOG2E * x)); }
 
 // Sum over the four lane groups holding the same column (lanes ln, ln+16, ...).
 __device__ inline float sum_groups(float v) {
@@ -201,9 +205,13 @@ struct Cfg {
     static constexpr int FBK = FBK0 < NKC ? FBK0 : NKC;
     static constexpr int TPB = FBK / KB;          // tiles per block
     static constexpr int NBLK = NKC / FBK;
-    // Mass column: in feature block fb, wave w < FBK owns chunk w of the block
-    // (global chunk fb * FBK + w); its accumulators are Zacc[2 fb + h].
-    static constexpr int NOWN = NBLK;
+    // Mass column: feature chunk c is owned by wave c % NW, in its
+    // accumulators Zacc[2 (c / NW) + h]. In feature block fb the owners are
+    // waves own_base(fb) .. own_base(fb) + FBK - 1 (local chunk w - own_base),
+    // all at accumulator pair zidx(fb).
+    static constexpr int NOWN = (NKC + NW - 1) / NW;
+    static constexpr int own_base(int fb) { return (fb * FBK) % NW; }
+    static constexpr int zidx(int fb) { return fb * FBK / NW; }
     static constexpr int NPAIR = (MT + 1) / 2;    // 32-row pairs of projection tiles
     static constexpr int PAD = Prec<F32>::PAD;
     static constexpr int ROWF = FBK * 32 + PAD;   // row stride of token x feature tiles
@@ -212,6 +220,7 @@ struct Cfg {
     static constexpr int ROWD = DH + PAD;
     static_assert(NKC % FBK == 0, "feature blocks must tile the features");
     static_assert(FBK % KB == 0, "feature blocks hold whole tables");
+    static_assert(NW % FBK == 0, "a feature block's mass chunks have distinct owner waves");
 };
 
 // table / plane of row `ri` (0..15) of projection tile t
@@ -223,66 +232,109 @@ __device__ inline void row_table(int t, int ri, int& table, int& plane) {
 }
 
 // Soft bucket features of one lane for projection tile t.
-// hs[i] = normalised projection for rows 4g+i; writes phi[KB*8] (canonical
-// order within the lane's chunks), u[4] = tanh(h), s[4] = sigmoid(2 beta u).
+// hs[i] = normalised projection of rows 4g+i (P' planes per table, TPL tables
+// per lane); writes phi[KB*8] (canonical order within the lane's chunks),
+// u[i] = tanh(hs[i]), s[i] = sigmoid(2 beta u[i]) (the probability that the
+// corner bit of plane i is set) and gu[i] = 2 beta (1 - u[i]^2).
+// The corner softmax of beta <c_r, u> factorises over planes into
+// prod_p sigmoid(2 beta c_rp u_p). With x = 2 beta u and F = e^{-|x|} <= 1,
+// sigmoid(x) = n1 / (1 + F) and sigmoid(-x) = n0 / (1 + F) where {n1, n0} =
+// {1, F} for x >= 0 and {F, 1} otherwise, so every corner is a product of
+// numerators in (0, 1] times one reciprocal per table. `keep` = false (an
+// absent token) gives phi = 0.
 template <class C>
-__device__ inline void soft_features(int t, int g, const float hs[4], float beta, int L,
-                                     float phi[C::KB * 8], float u[4], float s[4]) {
+__device__ inline void soft_features(int t, int g, const float hs[4], float beta, int L, bool keep,
+                                     float phi[C::KB * 8], float u[4], float s[4], float gu[4]) {
+    // u = tanh(hs): tanh|x| = (1 - E) / (1 + E), E = e^{-2|x|}
+    float e[4], q[4], rq[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        u[i] = fast_tanh(hs[i]);
-        s[i] = sigmoidf_(2.f * beta * u[i]);
+        e[i] = exp2_(-2.f * LOG2E * fabsf(hs[i]));
+        q[i] = 1.f + e[i];
     }
+    rcp4(q, rq);
+    float n1[4], n0[4], qf[4], rf[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        u[i] = copysignf((1.f - e[i]) * rq[i], hs[i]);
+        gu[i] = 2.f * beta * (1.f - u[i] * u[i]);
+        const float x = 2.f * beta * u[i];
+        const float F = exp2_(-LOG2E * fabsf(x));
+        n1[i] = x >= 0.f ? 1.f : F;
+        n0[i] = x >= 0.f ? F : 1.f;
+        qf[i] = 1.f + F;
+    }
+    rcp4(qf, rf);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = n1[i] * rf[i];
     if constexpr (C::P == 4) {
-        const bool ok = (t * C::TPT + g) < L;
-        float lo[4], hi[4];
+        const bool ok = keep && (t * C::TPT + g) < L;
+        // 1 / prod_p (1 + F_p) = rf[0] rf[1] rf[2] rf[3]
+        const float R = ok ? (rf[0] * rf[1]) * (rf[2] * rf[3]) : 0.f;
+        const float a1 = n1[0] * R, a0 = n0[0] * R;
+        const float lo[4] = {a0 * n0[1], a1 * n0[1], a0 * n1[1], a1 * n1[1]};
+        const float hi[4] = {n0[2] * n0[3], n1[2] * n0[3], n0[2] * n1[3], n1[2] * n1[3]};
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            lo[b] = ((b & 1) ? s[0] : 1.f - s[0]) * ((b & 2) ? s[1] : 1.f - s[1]);
-            hi[b] = ((b & 1) ? s[2] : 1.f - s[2]) * ((b & 2) ? s[3] : 1.f - s[3]);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) phi[r] = ok ? lo[r & 3] * hi[r >> 2] : 0.f;
+        for (int r = 0; r < 16; ++r) phi[r] = lo[r & 3] * hi[r >> 2];
     } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int tl = j / C::R, r = j % C::R;
-            const bool ok = (t * C::TPT + g * C::TPL + tl) < L;
-            float v = 1.f;
+            const bool ok = keep && (t * C::TPT + g * C::TPL + tl) < L;
+            float v = ok ? 1.f : 0.f;
 #pragma unroll
             for (int p = 0; p < C::P; ++p) {
-                const float sp = s[tl * C::Pp + p];
-                v *= ((r >> p) & 1) ? sp : 1.f - sp;
+                const int i = tl * C::Pp + p;
+                v *= (((r >> p) & 1) ? n1[i] : n0[i]) * rf[i];
             }
-            phi[j] = ok ? v : 0.f;
+            phi[j] = v;
         }
     }
 }
 
 // Chain rule of soft_features: given dA (same layout as phi) return dh[4]
-// (gradient wrt the normalised projections of rows 4g..4g+3).
+// (gradient wrt the normalised projections of rows 4g..4g+3). With
+// v_r = phi_r dA_r, T = sum_r v_r and S_p = sum_{r: bit p set} v_r, the
+// derivative of sum_r dA_r phi_r wrt u_p is 2 beta (S_p - s_p T), and
+// dh_p = that times (1 - u_p^2); gu = 2 beta (1 - u^2).
 template <class C>
 __device__ inline void soft_features_backward(const float phi[C::KB * 8], const float dA[C::KB * 8],
-                                              const float u[4], float beta, float dh[4]) {
+                                              const float s[4], const float gu[4], float dh[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) dh[i] = 0.f;
-    constexpr int TABLES = (C::P == 4) ? 1 : C::TPL;
-    constexpr int RR = C::R;
+    if constexpr (C::P == 4) {
+        float v[16];
 #pragma unroll
-    for (int tl = 0; tl < TABLES; ++tl) {
-        float mean = 0.f;
+        for (int r = 0; r < 16; ++r) v[r] = phi[r] * dA[r];
+        float rs[4], cs[4];   // sums over the low and over the high two bits
 #pragma unroll
-        for (int r = 0; r < RR; ++r) mean += phi[tl * RR + r] * dA[tl * RR + r];
+        for (int k = 0; k < 4; ++k) {
+            rs[k] = (v[4 * k] + v[4 * k + 1]) + (v[4 * k + 2] + v[4 * k + 3]);
+            cs[k] = (v[k] + v[k + 4]) + (v[k + 8] + v[k + 12]);
+        }
+        const float T = (rs[0] + rs[1]) + (rs[2] + rs[3]);
+        const float S[4] = {cs[1] + cs[3], cs[2] + cs[3], rs[1] + rs[3], rs[2] + rs[3]};
 #pragma unroll
-        for (int p = 0; p < C::P; ++p) {
-            float du = 0.f;
+        for (int p = 0; p < 4; ++p) dh[p] = (S[p] - s[p] * T) * gu[p];
+    } else {
 #pragma unroll
-            for (int r = 0; r < RR; ++r) {
-                const float w = phi[tl * RR + r] * (dA[tl * RR + r] - mean);
-                du += ((r >> p) & 1) ? w : -w;
+        for (int tl = 0; tl < C::TPL; ++tl) {
+            float T = 0.f, S[C::P];
+#pragma unroll
+            for (int p = 0; p < C::P; ++p) S[p] = 0.f;
+#pragma unroll
+            for (int r = 0; r < C::R; ++r) {
+                const float v = phi[tl * C::R + r] * dA[tl * C::R + r];
+                T += v;
+#pragma unroll
+                for (int p = 0; p < C::P; ++p)
+                    if ((r >> p) & 1) S[p] += v;
             }
-            const int i = tl * C::Pp + p;
-            dh[i] = beta * du * (1.f - u[i] * u[i]);
+#pragma unroll
+            for (int p = 0; p < C::P; ++p) {
+                const int i = tl * C::Pp + p;
+                dh[i] = (S[p] - s[i] * T) * gu[i];
+            }
         }
     }
 }

@@ -64,6 +64,11 @@ race_status_t run_scan(const Derived& d, float* states, float* total, hipStream_
 
 enum { PASS_FWD = 0, PASS_BWD_Q = 1, PASS_BWD_K = 2 };
 
+// The query-side backward uses feature blocks of two chunks in bf16 (smaller
+// LDS tiles and accumulator sets, so two workgroups fit on a CU).
+template <class C>
+using BwdQCfg = Cfg<C::P, C::MT, C::F32, C::F32 ? 0 : 2>;
+
 template <class C, int KIND>
 race_status_t run_pass(const Shape& s, const Derived& d, PassArgs a, hipStream_t st) {
     a.N = s.N; a.chunk = s.chunk; a.L = s.L; a.causal = s.causal;
@@ -73,7 +78,7 @@ race_status_t run_pass(const Shape& s, const Derived& d, PassArgs a, hipStream_t
         hipLaunchKernelGGL(k_fwd<C>, grid, block, 0, st, a);
     } else if constexpr (KIND == PASS_BWD_Q) {
         profile_mark("pass_bwd_q", st);
-        hipLaunchKernelGGL(k_bwd_q<C>, grid, block, 0, st, a);
+        hipLaunchKernelGGL(k_bwd_q<BwdQCfg<C>>, grid, block, 0, st, a);
     } else {
         profile_mark("pass_bwd_k", st);
         hipLaunchKernelGGL(k_bwd_k<C>, grid, block, 0, st, a);

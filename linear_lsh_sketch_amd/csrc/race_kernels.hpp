@@ -211,18 +211,18 @@ __device__ inline void load_state(const float* __restrict__ st, int w, int ln, i
                 const int f = 32 * kc + 8 * g + 4 * h + i;
                 Macc[2 * kc + h][i] = st[(size_t)f * DH + 16 * w + ln];
             }
-    const bool owner = w < C::FBK && ln == 0;   // waves w >= FBK own no mass chunk
 #pragma unroll
-    for (int fb = 0; fb < C::NBLK; ++fb) {
-        const int kc = fb * C::FBK + (owner ? w : 0);
+    for (int j = 0; j < C::NOWN; ++j) {
+        const int kc = NW * j + w;             // the chunk this wave owns
+        const bool owner = kc < C::NKC && ln == 0;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int f = 32 * kc + 8 * g + 4 * h + i;
+                const int f = 32 * (owner ? kc : 0) + 8 * g + 4 * h + i;
                 float v = 0.f;
                 if (owner) v = st[(size_t)C::F * DH + f];
-                Zacc[2 * fb + h][i] = v;
+                Zacc[2 * j + h][i] = v;
             }
     }
 }
@@ -239,16 +239,16 @@ __device__ inline void store_state(float* __restrict__ st, int w, int ln, int g,
                 const int f = 32 * kc + 8 * g + 4 * h + i;
                 st[(size_t)f * DH + 16 * w + ln] = Macc[2 * kc + h][i];
             }
-    if (w < C::FBK && ln == 0) {
 #pragma unroll
-        for (int fb = 0; fb < C::NBLK; ++fb) {
-            const int kc = fb * C::FBK + w;
+    for (int j = 0; j < C::NOWN; ++j) {
+        const int kc = NW * j + w;
+        if (kc < C::NKC && ln == 0) {
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int f = 32 * kc + 8 * g + 4 * h + i;
-                    st[(size_t)C::F * DH + f] = Zacc[2 * fb + h][i];
+                    st[(size_t)C::F * DH + f] = Zacc[2 * j + h][i];
                 }
         }
     }
@@ -275,49 +275,52 @@ __device__ inline void sketch_update(int fb, int w, int ln, int g, const typenam
             for (int s = 0; s < 2; ++s) Macc[2 * kc + h] = mma(ld_frag<C::F32>(arow + 32 * s), zt[s], Macc[2 * kc + h]);
         }
     }
-    if (w < C::FBK) {
+    const int kw = w - C::own_base(fb);        // local chunk whose mass this wave owns
+    if (kw >= 0 && kw < C::FBK) {
         frag zm[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) zm[s] = ld_frag<C::F32>(ZT + (64 + ln) * C::ROWT + 32 * s + 8 * g);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const typename Prec<C::F32>::elem* arow = cols + (32 * w + canon_of_row(h, ln)) * C::ROWT + 8 * g;
+            const typename Prec<C::F32>::elem* arow = cols + (32 * kw + canon_of_row(h, ln)) * C::ROWT + 8 * g;
 #pragma unroll
-            for (int s = 0; s < 2; ++s) Zacc[2 * fb + h] = mma(ld_frag<C::F32>(arow + 32 * s), zm[s], Zacc[2 * fb + h]);
+            for (int s = 0; s < 2; ++s)
+                Zacc[2 * C::zidx(fb) + h] = mma(ld_frag<C::F32>(arow + 32 * s), zm[s], Zacc[2 * C::zidx(fb) + h]);
         }
     }
 }
 
 // Project the own 16-token tile for the tiles of feature block fb and write
 // the features to LDS (row layout `rows` and/or transposed `cols`); when KEEP,
-// also return the lane's operands (one per chunk of the block) in phi_frag and
-// the tanh values of its planes (one group of four per tile) in u_keep.
+// also return the lane's operands (one per chunk of the block) in phi_frag and,
+// per tile of the block, the plane probabilities s and 2 beta (1 - u^2) that
+// the chain rule needs.
 template <class C, bool KEEP>
 __device__ inline void block_features(const WSrc<C>& wsrc, int fb, int lane, int w, int ln, int g,
                                       const typename Prec<C::F32>::frag xf[2], float inv, bool valid, float beta,
                                       int L, typename Prec<C::F32>::elem* rows /* [64][ROWF] or null */,
                                       typename Prec<C::F32>::elem* cols /* [FBK*32][ROWT] or null */,
                                       typename Prec<C::F32>::frag (&phi_frag)[C::FBK],
-                                      float (&u_keep)[C::TPB][4]) {
+                                      float (&s_keep)[C::TPB][4], float (&gu_keep)[C::TPB][4]) {
 #pragma unroll
     for (int tb = 0; tb < C::TPB; ++tb) {
         const int t = fb * C::TPB + tb;
         const f32x4 acc = wsrc.project(t, lane, ln, g, xf);
-        float hs[4], phi[C::KB * 8], u[4], s[4];
+        float hs[4], phi[C::KB * 8], u[4], sg[4], gu[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) hs[i] = acc[i] * inv;
-        soft_features<C>(t, g, hs, beta, L, phi, u, s);
+        soft_features<C>(t, g, hs, beta, L, valid, phi, u, sg, gu);
         if constexpr (KEEP) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) u_keep[tb][i] = u[i];
+            for (int i = 0; i < 4; ++i) {
+                s_keep[tb][i] = sg[i];
+                gu_keep[tb][i] = gu[i];
+            }
         }
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb) {
             const int kcl = tb * C::KB + kb;
-            float p8[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) p8[j] = valid ? phi[kb * 8 + j] : 0.f;
-            const typename Prec<C::F32>::frag fr = pack8<C::F32>(p8);
+            const typename Prec<C::F32>::frag fr = pack8<C::F32>(phi + kb * 8);
             if constexpr (KEEP) phi_frag[kcl] = fr;
             if (rows) st_frag<C::F32>(rows + (16 * w + ln) * C::ROWF + 32 * kcl + 8 * g, fr);
             if (cols) {
@@ -414,9 +417,9 @@ __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
 #pragma unroll
         for (int fb = 0; fb < C::NBLK; ++fb) {
             frag unused[C::FBK];
-            float unused_u[C::TPB][4];
+            float unused_s[C::TPB][4], unused_g[C::TPB][4];
             block_features<C, false>(wsrc, fb, lane, w, ln, g, xf, inv, valid, a.beta, a.L, nullptr, s_cols, unused,
-                                     unused_u);
+                                     unused_s, unused_g);
             __syncthreads();
             sketch_update<C>(fb, w, ln, g, s_cols, s_ZT, Macc, Zacc);
             __syncthreads();
@@ -527,12 +530,14 @@ __device__ inline void write_sketch_rows(int fb, int w, int ln, int g, const f32
                     s_ms[fl * C::ROWE + 16 * w + ln] = to_elem<C::F32>(v[kb * 8 + 4 * h + i]);
                 }
     }
-    if (w < C::FBK && ln == 0) {
+    const int kw = w - C::own_base(fb);
+    if (kw >= 0 && kw < C::FBK && ln == 0) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                s_ms[(32 * w + 8 * g + 4 * h + i) * C::ROWE + 64] = to_elem<C::F32>(Zacc[2 * fb + h][i] - zshift);
+                s_ms[(32 * kw + 8 * g + 4 * h + i) * C::ROWE + 64] =
+                    to_elem<C::F32>(Zacc[2 * C::zidx(fb) + h][i] - zshift);
     }
 }
 
@@ -570,14 +575,15 @@ __device__ inline void block_grad(int ln, int g, const typename Prec<C::F32>::el
 }
 
 // Corner-softmax chain rule for projection tile t of the own token (phi and dA
-// in the lane's feature order, u = tanh of its planes), then the
-// back-projection dX += W'^T dh, two tiles per matrix-core operand.
+// in the lane's feature order, s and gu of its planes as soft_features gives
+// them), then the back-projection dX += W'^T dh, two tiles per matrix-core
+// operand.
 template <class C>
 __device__ inline void chain_backproject(int t, int lane, const float phi[C::KB * 8], const float dA[C::KB * 8],
-                                         const float u[4], float beta, const typename Prec<C::F32>::elem* WTp,
+                                         const float s[4], const float gu[4], const typename Prec<C::F32>::elem* WTp,
                                          f32x4 (&dhp)[2], f32x4 (&dX)[4]) {
     float dh[4];
-    soft_features_backward<C>(phi, dA, u, beta, dh);
+    soft_features_backward<C>(phi, dA, s, gu, dh);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dhp[t & 1][i] = dh[i];
     if ((t & 1) == 1 || t == C::MT - 1) {
@@ -798,11 +804,11 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
 #pragma unroll
         for (int fb = 0; fb < C::NBLK; ++fb) {
             frag phiA[C::FBK], unused[C::FBK];
-            float unused_u[C::TPB][4];
+            float unused_s[C::TPB][4], unused_g[C::TPB][4];
             block_features<C, true>(wsrc, fb, lane, w, ln, g, xa, inv_a, true, a.beta, a.L, s_rows, nullptr, phiA,
-                                    unused_u);
+                                    unused_s, unused_g);
             block_features<C, false>(wsrc, fb, lane, w, ln, g, xb, inv_b, valid, a.beta, a.L, s_brow,
-                                     causal ? s_cols : nullptr, unused, unused_u);
+                                     causal ? s_cols : nullptr, unused, unused_s, unused_g);
             __syncthreads();
             if (causal) {
 #pragma unroll
@@ -823,11 +829,12 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
                 for (int at = 0; at < 4; ++at)
                     Y[at] = mma(ld_frag<C::F32>(s_rows + (16 * at + ln) * C::ROWF + 32 * kcl + 8 * g), mf, Y[at]);
             }
-            if (w < C::FBK) {
-                const frag zf = pack<C::F32>(Zacc[2 * fb], Zacc[2 * fb + 1]);
+            const int kw = w - C::own_base(fb);
+            if (kw >= 0 && kw < C::FBK) {
+                const frag zf = pack<C::F32>(Zacc[2 * C::zidx(fb)], Zacc[2 * C::zidx(fb) + 1]);
 #pragma unroll
                 for (int at = 0; at < 4; ++at)
-                    Dacc[at] = mma(ld_frag<C::F32>(s_rows + (16 * at + ln) * C::ROWF + 32 * w + 8 * g), zf, Dacc[at]);
+                    Dacc[at] = mma(ld_frag<C::F32>(s_rows + (16 * at + ln) * C::ROWF + 32 * kw + 8 * g), zf, Dacc[at]);
             }
             if (causal) sketch_update<C>(fb, w, ln, g, s_cols, s_ZT, Macc, Zacc);
             __syncthreads();
@@ -912,7 +919,7 @@ struct BwdQLds {
     static constexpr int o_yr = o_zr + n_zr;
     static constexpr int o_ylo = o_yr + n_yr;
     static constexpr int o_w = o_ylo + n_ylo;
-    static constexpr int OCC = 1;
+    static constexpr int OCC = (!C::F32 && C::NKC <= 8) ? 2 : 1;
     using WS = WStage<elem, o_w, 0, C::MT, OCC>;
 };
 
@@ -953,20 +960,14 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
     const int nsub = (int)((seg1 - seg0 + TB - 1) / TB);
     const int my = 16 * w + ln;
 
-    frag n_xa[2], n_xb[2], n_z[2], n_y[2], n_o[2];
-    float n_d = 1.f;
+    // the projection rows are loaded one sub-block ahead; the value, gradient
+    // and output rows at the top of their sub-block (register budget)
+    frag n_xa[2], n_xb[2];
     auto issue = [&](int it2) {
         const int64_t t0 = seg0 + (int64_t)it2 * TB;
         const int nv = (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
-        const bool ok = tr < nv;
         load_row_raw<C::F32>(a.Xa, base + t0 + my, my < nv, g, n_xa);
-        if (causal) {
-            load_row_raw<C::F32>(a.Xb, base + t0 + my, my < nv, g, n_xb);
-            load_q16_raw<C::F32>(a.Zsrc, (base + t0 + tr) * DH + 16 * tq, ok, n_z);
-        }
-        load_q16_raw<C::F32>(a.Ysrc, (base + t0 + tr) * DH + 16 * tq, ok, n_y);
-        load_q16_raw<C::F32>(a.Osrc, (base + t0 + tr) * DH + 16 * tq, ok, n_o);
-        if (ok) n_d = a.Dv[base + t0 + tr];
+        if (causal) load_row_raw<C::F32>(a.Xb, base + t0 + my, my < nv, g, n_xb);
     };
     issue(0);
 
@@ -976,9 +977,12 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
         const bool valid = my < nv;
         const size_t row = base + t0 + my;
         const bool tok = tr < nv;
+        frag zr[2], yr[2], orow[2];
+        if (causal) load_q16_raw<C::F32>(a.Zsrc, (base + t0 + tr) * DH + 16 * tq, tok, zr);
+        load_q16_raw<C::F32>(a.Ysrc, (base + t0 + tr) * DH + 16 * tq, tok, yr);
+        load_q16_raw<C::F32>(a.Osrc, (base + t0 + tr) * DH + 16 * tq, tok, orow);
+        const float dd = tok ? a.Dv[base + t0 + tr] : 1.f;
         frag xa[2] = {n_xa[0], n_xa[1]}, xb[2] = {n_xb[0], n_xb[1]};
-        frag zr[2] = {n_z[0], n_z[1]}, yr[2] = {n_y[0], n_y[1]}, orow[2] = {n_o[0], n_o[1]};
-        const float dd = n_d;
         if (it + 1 < nsub) issue(it + 1);
 
         float inv_a, nrm_a, inv_b = 0.f, nrm_b;
@@ -1022,9 +1026,6 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
         __syncthreads();
         frag Cf[2];
         if (causal) intra_operand<C, false, LD::YLO>(s_zr, s_yr, s_ylo, w, ln, g, my, nv, Cf);
-        frag yf[3];
-#pragma unroll
-        for (int s = 0; s < 3; ++s) yf[s] = ld_frag<C::F32>(s_yr + my * C::ROWE + 32 * s + 8 * g);
         f32x4 dX[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) dX[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1038,21 +1039,24 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
             write_sketch_rows<C>(fb, w, ln, g, Macc, Zacc, zshift, s_ms);
             if (causal) {
                 frag unused[C::FBK];
-                float unused_u[C::TPB][4];
+                float unused_s[C::TPB][4], unused_g[C::TPB][4];
                 block_features<C, false>(wsrc, fb, lane, w, ln, g, xb, inv_b, valid, a.beta, a.L, nullptr, s_cols,
-                                         unused, unused_u);
+                                         unused, unused_s, unused_g);
             }
             __syncthreads();
+            frag yf[3];
+#pragma unroll
+            for (int s = 0; s < 3; ++s) yf[s] = ld_frag<C::F32>(s_yr + my * C::ROWE + 32 * s + 8 * g);
             f32x4 G[C::FBK * 2];
             block_grad<C>(ln, g, s_ms, yf, s_cols, Cf, causal, G);
 #pragma unroll
             for (int tb = 0; tb < C::TPB; ++tb) {
                 const int t = fb * C::TPB + tb;
                 const f32x4 acc = wsrc.project(t, lane, ln, g, xa);
-                float hs[4], phi[C::KB * 8], u[4], s[4], dA[C::KB * 8];
+                float hs[4], phi[C::KB * 8], u[4], sg[4], gu[4], dA[C::KB * 8];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) hs[i] = acc[i] * inv_a;
-                soft_features<C>(t, g, hs, a.beta, a.L, phi, u, s);
+                soft_features<C>(t, g, hs, a.beta, a.L, true, phi, u, sg, gu);
 #pragma unroll
                 for (int kb = 0; kb < C::KB; ++kb) {
                     const int kcl = tb * C::KB + kb;
@@ -1062,7 +1066,7 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
                         dA[kb * 8 + 4 + i] = G[2 * kcl + 1][i];
                     }
                 }
-                chain_backproject<C>(t, lane, phi, dA, u, a.beta, WTp, dhp, dX);
+                chain_backproject<C>(t, lane, phi, dA, sg, gu, WTp, dhp, dX);
             }
             if (causal) sketch_update<C>(fb, w, ln, g, s_cols, s_ZT, Macc, Zacc);
             __syncthreads();
@@ -1144,6 +1148,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C>::OCC)) void k_bwd_k(PassArgs a) {
     const int nsub = (int)((seg1 - seg0 + TB - 1) / TB);
     const int my = 16 * w + ln;
 
+    // global loads are issued one sub-block ahead
     frag n_xa[2], n_xb[2], n_z[2], n_y[2];
     float n_d = 1.f, n_e = 0.f;
     auto issue = [&](int it2) {
@@ -1195,9 +1200,6 @@ __global__ __launch_bounds__(NT, (BwdKLds<C>::OCC)) void k_bwd_k(PassArgs a) {
         // where the intra scores of the previous sub-block reached into the
         // sketch rows, their padding is cleared again
         if constexpr (LD::n_sc > LD::n_cols) zero_sketch_pads<C>(s_ms);
-        frag yf[3];
-#pragma unroll
-        for (int s = 0; s < 3; ++s) yf[s] = ld_frag<C::F32>(s_yr + my * C::ROWE + 32 * s + 8 * g);
         f32x4 Y[4], Sc[4], dX[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1209,12 +1211,12 @@ __global__ __launch_bounds__(NT, (BwdKLds<C>::OCC)) void k_bwd_k(PassArgs a) {
 #pragma unroll
         for (int fb = 0; fb < C::NBLK; ++fb) {
             frag phiA[C::FBK], unused[C::FBK];
-            float uA[C::TPB][4], unused_u[C::TPB][4];
+            float sA[C::TPB][4], guA[C::TPB][4], unused_s[C::TPB][4], unused_g[C::TPB][4];
             block_features<C, true>(wsrc, fb, lane, w, ln, g, xa, inv_a, valid, a.beta, a.L, s_rows, nullptr, phiA,
-                                    uA);
+                                    sA, guA);
             if (causal)
                 block_features<C, false>(wsrc, fb, lane, w, ln, g, xb, inv_b, valid, a.beta, a.L, s_brow, s_cols,
-                                         unused, unused_u);
+                                         unused, unused_s, unused_g);
             write_sketch_rows<C>(fb, w, ln, g, Macc, Zacc, 0.f, s_ms);
             __syncthreads();
             if (causal) {
@@ -1237,6 +1239,9 @@ __global__ __launch_bounds__(NT, (BwdKLds<C>::OCC)) void k_bwd_k(PassArgs a) {
                 for (int at = 0; at < 4; ++at)
                     Y[at] = mma(ld_frag<C::F32>(s_rows + (16 * at + ln) * C::ROWF + 32 * kcl + 8 * g), mf, Y[at]);
             }
+            frag yf[3];
+#pragma unroll
+            for (int s = 0; s < 3; ++s) yf[s] = ld_frag<C::F32>(s_yr + my * C::ROWE + 32 * s + 8 * g);
             f32x4 G[C::FBK * 2];
             block_grad<C>(ln, g, s_ms, yf, s_cols, Cf, causal, G);
 #pragma unroll
@@ -1254,7 +1259,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C>::OCC)) void k_bwd_k(PassArgs a) {
                         dA[kb * 8 + 4 + i] = G[2 * kcl + 1][i];
                     }
                 }
-                chain_backproject<C>(t, lane, phi, dA, uA[tb], a.beta, WTp, dhp, dX);
+                chain_backproject<C>(t, lane, phi, dA, sA[tb], guA[tb], WTp, dhp, dX);
             }
             if (causal) sketch_update<C>(fb, w, ln, g, s_cols, s_ZT, Macc, Zacc);
             __syncthreads();
