@@ -58,6 +58,46 @@ def per_token_head_counts(w):
     return layer, kernels
 
 
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
+
+
+def source_digest() -> str:
+    """sha256 over the kernel sources and the C header: identifies the build
+    that HBM byte counters were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_lsh_sketch_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    with open(os.path.join(ROOT, "include", "race_attn.h"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, stage: str):
+    """HBM bytes per launch of `stage` (FETCH_SIZE + WRITE_SIZE, each scaled by
+    the same counter on a 1 GiB reference copy) from the committed summary
+    profiles/hbm_traffic_<workload>.md, or None when there is none for this
+    workload or it was taken on other kernel sources."""
+    path = os.path.join(TRAFFIC_DIR, f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    digest, rows = None, {}
+    for line in open(path):
+        if line.startswith("sources sha256:"):
+            digest = line.split(":", 1)[1].strip()
+        elif line.startswith("| pass_") or line.startswith("| totals_") or line.startswith("| scan_"):
+            cells = [c.strip() for c in line.strip().strip("|").split("|")]
+            try:
+                rows[cells[0]] = int(cells[-1])
+            except ValueError:
+                pass
+    if digest != source_digest():
+        return None
+    return rows.get(stage)
+
+
 def cpu_baseline(w, n_sample: int):
     """The float64 oracle on the first n_sample tokens of every head of the
     same workload (same seeded inputs), causal forward + backward."""
@@ -190,7 +230,7 @@ def main():
         roof = {"bound": "mfma", "achieved": kf * units / (avg_ms / 1e3) / 1e12, "peak": peak_f / 1e12,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(w.name, dom)
     roof["kernel"] = dom
     roof["kernel_avg_ms"] = avg_ms
     layer_t = max(layer["bytes"] * units / HBM_PEAK, layer["flops"] * units / peak_f)
