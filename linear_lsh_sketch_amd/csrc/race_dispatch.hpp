@@ -64,10 +64,10 @@ race_status_t run_scan(const Derived& d, float* states, float* total, hipStream_
 
 enum { PASS_FWD = 0, PASS_BWD_Q = 1, PASS_BWD_K = 2 };
 
-// The query-side backward uses feature blocks of two chunks in bf16 (smaller
-// LDS tiles and accumulator sets, so two workgroups fit on a CU).
+// The forward and the query-side backward use feature blocks of two chunks in
+// bf16 (smaller LDS tiles and operand sets, so two workgroups fit on a CU).
 template <class C>
-using BwdQCfg = Cfg<C::P, C::MT, C::F32, C::F32 ? 0 : 2>;
+using Blk2Cfg = Cfg<C::P, C::MT, C::F32, C::F32 ? 0 : 2>;
 
 template <class C, int KIND>
 race_status_t run_pass(const Shape& s, const Derived& d, PassArgs a, hipStream_t st) {
@@ -75,13 +75,16 @@ race_status_t run_pass(const Shape& s, const Derived& d, PassArgs a, hipStream_t
     const dim3 grid((unsigned)d.NC, (unsigned)d.BH), block(NT);
     if constexpr (KIND == PASS_FWD) {
         profile_mark("pass_fwd", st);
-        hipLaunchKernelGGL(k_fwd<C>, grid, block, 0, st, a);
+        if (s.causal) hipLaunchKernelGGL((k_fwd<Blk2Cfg<C>, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_fwd<Blk2Cfg<C>, false>), grid, block, 0, st, a);
     } else if constexpr (KIND == PASS_BWD_Q) {
         profile_mark("pass_bwd_q", st);
-        hipLaunchKernelGGL(k_bwd_q<BwdQCfg<C>>, grid, block, 0, st, a);
+        if (s.causal) hipLaunchKernelGGL((k_bwd_q<Blk2Cfg<C>, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_bwd_q<Blk2Cfg<C>, false>), grid, block, 0, st, a);
     } else {
         profile_mark("pass_bwd_k", st);
-        hipLaunchKernelGGL(k_bwd_k<C>, grid, block, 0, st, a);
+        if (s.causal) hipLaunchKernelGGL((k_bwd_k<C, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_bwd_k<C, false>), grid, block, 0, st, a);
     }
     return launch_ok();
 }

@@ -732,7 +732,7 @@ struct FwdLds {
     using WS = WStage<elem, o_w, n_float, C::MT, OCC>;
 };
 
-template <class C>
+template <class C, bool CAUSAL>
 __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
     using elem = typename Prec<C::F32>::elem;
     using frag = typename Prec<C::F32>::frag;
@@ -758,7 +758,7 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
     const int64_t seg1 = seg0 + a.chunk < a.N ? seg0 + a.chunk : a.N;
     const size_t base = (size_t)bh * a.N;
     const elem* W = reinterpret_cast<const elem*>(a.W);
-    const bool causal = a.causal != 0;
+    constexpr bool causal = CAUSAL;
     elem* s_w = LD::WS::on ? lds + LD::o_w : nullptr;
     if (LD::WS::on) stage_w<C>(W, a.L, s_w);
     zero_pads<C>(s_ZT, nullptr, nullptr);
@@ -923,7 +923,7 @@ struct BwdQLds {
     using WS = WStage<elem, o_w, 0, C::MT, OCC>;
 };
 
-template <class C>
+template <class C, bool CAUSAL>
 __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
     using elem = typename Prec<C::F32>::elem;
     using frag = typename Prec<C::F32>::frag;
@@ -945,7 +945,7 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
     const size_t base = (size_t)bh * a.N;
     const elem* W = reinterpret_cast<const elem*>(a.W);
     const elem* WTp = reinterpret_cast<const elem*>(a.WTp);
-    const bool causal = a.causal != 0;
+    constexpr bool causal = CAUSAL;
     elem* s_w = LD::WS::on ? lds + LD::o_w : nullptr;
     if (LD::WS::on) stage_w<C>(W, a.L, s_w);
     zero_pads<C>(s_ZT, s_zr, s_yr);
@@ -1109,7 +1109,7 @@ struct BwdKLds {
     using WS = WStage<elem, o_w, 0, C::MT, OCC>;
 };
 
-template <class C>
+template <class C, bool CAUSAL>
 __global__ __launch_bounds__(NT, (BwdKLds<C>::OCC)) void k_bwd_k(PassArgs a) {
     using elem = typename Prec<C::F32>::elem;
     using frag = typename Prec<C::F32>::frag;
@@ -1134,7 +1134,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C>::OCC)) void k_bwd_k(PassArgs a) {
     const size_t base = (size_t)bh * a.N;
     const elem* W = reinterpret_cast<const elem*>(a.W);
     const elem* WTp = reinterpret_cast<const elem*>(a.WTp);
-    const bool causal = a.causal != 0;
+    constexpr bool causal = CAUSAL;
     elem* s_w = LD::WS::on ? lds + LD::o_w : nullptr;
     if (LD::WS::on) stage_w<C>(W, a.L, s_w);
     zero_pads<C>(s_ZT, s_zr, s_yr);
