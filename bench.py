@@ -164,7 +164,7 @@ def main():
     t["W"] = synth.normal_device(w.seed, synth.TID_W, torch.empty((w.L, w.P, w.d), dtype=tdt, device=dev))
     O = torch.empty(shape, dtype=tdt, device=dev)
     grads = tuple(torch.empty(shape, dtype=tdt, device=dev) for _ in range(3))
-    ws_f = race.alloc_workspace(w.B, w.H, w.N, w.P, w.L, w.causal, w.chunk, race.WS_FWD, dev)
+    ws_f = race.alloc_workspace(w.B, w.H, w.N, w.P, w.L, w.causal, w.chunk, race.WS_FWD_SAVED, dev)
     ws_b = race.alloc_workspace(w.B, w.H, w.N, w.P, w.L, w.causal, w.chunk, race.WS_BWD, dev)
     saved = race.alloc_saved(w.B, w.H, w.N, w.P, w.L, w.causal, w.chunk, dev)
     torch.cuda.synchronize()

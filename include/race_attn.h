@@ -78,7 +78,8 @@ typedef enum {
 typedef enum { RACE_F32 = 0, RACE_BF16 = 1 } race_dtype_t;
 
 /* Bytes of device workspace `ws` for this shape. Writes *bytes.
- *   for_backward = 0: race_attn_fwd;
+ *   for_backward = 0: race_attn_fwd with saved = NULL;
+ *   for_backward = 3: race_attn_fwd with a `saved` buffer;
  *   for_backward = 1: race_attn_bwd given O and `saved` from the forward;
  *   for_backward = 2: race_attn_bwd with O = saved = NULL (it then recomputes
  *                     the forward into this workspace);
@@ -88,19 +89,24 @@ typedef enum { RACE_F32 = 0, RACE_BF16 = 1 } race_dtype_t;
 race_status_t race_attn_workspace_bytes(int64_t B, int64_t H, int64_t N, int d, int P, int L,
                                         int causal, int chunk, int for_backward, size_t *bytes);
 
-/* Bytes of the optional `saved` buffer a forward call fills for the backward:
- * the float32 sketch state at the start of every chunk (causal) or the
- * whole-sequence sketch (non-causal), then the float32 per-token softmax
- * denominators D_i = sum_l sum_r a_l(q_i)[r] z_l[r] (the same quantity the
- * output divides by), per (batch, head). Layout is private to the library. */
+/* Bytes of the optional `saved` buffer a forward call fills for the backward,
+ * per (batch, head): the float32 sketch state at the start of every chunk
+ * (causal) or the whole-sequence sketch (non-causal); the float32 per-token
+ * softmax denominators D_i = sum_l sum_r a_l(q_i)[r] z_l[r] (the quantity
+ * the output divides by); and, for queries and for keys, each token's
+ * per-plane values sigmoid(2 beta u) and 2 beta (1 - u^2), u = tanh of the
+ * normalised projection, with 1 / max(|x|, 1e-12), all float32, so that
+ * the backward rebuilds the soft assignments without projecting again.
+ * Layout is private to the library. */
 race_status_t race_attn_saved_bytes(int64_t B, int64_t H, int64_t N, int d, int P, int L,
                                     int causal, int chunk, size_t *bytes);
 
 /* Forward: O = RACE-Attention(Q, K, V; W, P, L, temperature, causal).
  * `temperature` is the pages' beta: it multiplies the corner logits, so a
  * larger value gives harder bucket assignments. `saved` may be NULL; if not
- * NULL it receives the sketch states and denominators (race_attn_saved_bytes).
- * `ws` must hold race_attn_workspace_bytes(..., for_backward = 0). */
+ * NULL it receives the sketch states, denominators and plane values
+ * (race_attn_saved_bytes). `ws` must hold race_attn_workspace_bytes(...,
+ * for_backward = 0), or (..., for_backward = 3) when `saved` is given. */
 race_status_t race_attn_fwd(const void *Q, const void *K, const void *V, const void *W,
                             int64_t B, int64_t H, int64_t N, int d, int P, int L,
                             float temperature, int causal, int chunk, race_dtype_t dtype,

@@ -70,12 +70,13 @@ def _check(code: int, where: str):
         raise RaceError(code, where)
 
 
-WS_FWD, WS_BWD, WS_BWD_RECOMPUTE = 0, 1, 2
+WS_FWD, WS_BWD, WS_BWD_RECOMPUTE, WS_FWD_SAVED = 0, 1, 2, 3
 
 
 def workspace_bytes(B, H, N, d, P, L, causal, chunk, kind) -> int:
-    """Workspace bytes: kind 0 forward, 1 backward given O and saved, 2 backward
-    recomputing the forward (race_attn_workspace_bytes' for_backward)."""
+    """Workspace bytes (race_attn_workspace_bytes' for_backward): kind 0
+    forward without saved, 3 forward with saved, 1 backward given O and saved,
+    2 backward recomputing the forward."""
     out = ctypes.c_size_t(0)
     _check(lib().race_attn_workspace_bytes(B, H, N, d, P, L, int(bool(causal)), chunk, int(kind),
                                            ctypes.byref(out)),
@@ -145,7 +146,7 @@ def race_attn_fwd(Q, K, V, W, P, L, temperature=1.0, causal=False, chunk=1024, o
         raise ValueError("Q, K, V must share one shape")
     O = out if out is not None else torch.empty_like(Q)
     if ws is None:
-        ws = alloc_workspace(B, H, N, P, L, causal, chunk, WS_FWD, Q.device)
+        ws = alloc_workspace(B, H, N, P, L, causal, chunk, WS_FWD_SAVED if saved is not None else WS_FWD, Q.device)
     code = lib().race_attn_fwd(_p(Q), _p(K), _p(V), _p(W), B, H, N, d, P, L, float(temperature),
                                int(bool(causal)), chunk, _dtype_code(Q), _p(O), _p(saved), _p(ws),
                                ws.numel(), _stream(stream))

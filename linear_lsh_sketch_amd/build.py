@@ -18,6 +18,10 @@ HIPCC_FLAGS = [
     "-I" + os.path.join(ROOT, "include"),
     # packed fp32 instructions stay off: hipcc may emit them from scalar float code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in VGPRs: the sketch state and the gradient
+    # tiles are also read by vector instructions, and the AGPR form made the
+    # compiler copy them between register files every sub-block
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

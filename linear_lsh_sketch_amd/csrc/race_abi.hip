@@ -81,7 +81,7 @@ const char* race_attn_profile_stage(int i) { return (i >= 0 && i < t_count) ? t_
 
 race_status_t race_attn_workspace_bytes(int64_t B, int64_t H, int64_t N, int d, int P, int L, int causal,
                                         int chunk, int for_backward, size_t* bytes) {
-    if (!bytes || for_backward < WS_FWD || for_backward > WS_BWD_RECOMPUTE) return RACE_ERR_INVALID_ARG;
+    if (!bytes || for_backward < WS_FWD || for_backward > WS_FWD_SAVED) return RACE_ERR_INVALID_ARG;
     Shape s;
     Derived dv;
     race_status_t rc = prepare(B, H, N, d, P, L, causal, chunk, s, dv);
@@ -111,7 +111,7 @@ race_status_t race_attn_fwd(const void* Q, const void* K, const void* V, const v
     Derived dv;
     race_status_t rc = prepare(B, H, N, d, P, L, causal, chunk, s, dv);
     if (rc != RACE_OK) return rc;
-    const WsLayout wl = ws_layout(s, dv, WS_FWD);
+    const WsLayout wl = ws_layout(s, dv, saved ? WS_FWD_SAVED : WS_FWD);
     if (ws_bytes < wl.total) return RACE_ERR_WORKSPACE;
     Call c{};
     c.op = OP_FWD; c.Q = Q; c.K = K; c.V = V; c.W = W; c.saved_out = saved; c.beta = temperature; c.O = O;

@@ -213,6 +213,7 @@ struct Cfg {
     static constexpr int own_base(int fb) { return (fb * FBK) % NW; }
     static constexpr int zidx(int fb) { return fb * FBK / NW; }
     static constexpr int NPAIR = (MT + 1) / 2;    // 32-row pairs of projection tiles
+    static constexpr int NPL = MT * 16;           // projection rows (planes incl. padding) per token
     static constexpr int PAD = Prec<F32>::PAD;
     static constexpr int ROWF = FBK * 32 + PAD;   // row stride of token x feature tiles
     static constexpr int ROWT = TB + PAD;         // row stride of feature x token tiles
@@ -286,6 +287,37 @@ __device__ inline void soft_features(int t, int g, const float hs[4], float beta
             for (int p = 0; p < C::P; ++p) {
                 const int i = tl * C::Pp + p;
                 v *= (((r >> p) & 1) ? n1[i] : n0[i]) * rf[i];
+            }
+            phi[j] = v;
+        }
+    }
+}
+
+// The features of projection tile t from the plane probabilities s[i] =
+// sigmoid(2 beta u_i) that soft_features computes (stored by an earlier
+// pass): phi_r = prod_p (bit p of r set ? s_p : 1 - s_p). `keep` = false
+// gives phi = 0.
+template <class C>
+__device__ inline void features_from_planes(int t, int g, const float s[4], int L, bool keep,
+                                            float phi[C::KB * 8]) {
+    if constexpr (C::P == 4) {
+        const bool ok = keep && (t * C::TPT + g) < L;
+        const float m = ok ? 1.f : 0.f;
+        const float s0 = s[0] * m, n0 = m - s0;
+        const float lo[4] = {n0 * (1.f - s[1]), s0 * (1.f - s[1]), n0 * s[1], s0 * s[1]};
+        const float hi[4] = {(1.f - s[2]) * (1.f - s[3]), s[2] * (1.f - s[3]), (1.f - s[2]) * s[3], s[2] * s[3]};
+#pragma unroll
+        for (int r = 0; r < 16; ++r) phi[r] = lo[r & 3] * hi[r >> 2];
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int tl = j / C::R, r = j % C::R;
+            const bool ok = keep && (t * C::TPT + g * C::TPL + tl) < L;
+            float v = ok ? 1.f : 0.f;
+#pragma unroll
+            for (int p = 0; p < C::P; ++p) {
+                const float sp = s[tl * C::Pp + p];
+                v *= ((r >> p) & 1) ? sp : 1.f - sp;
             }
             phi[j] = v;
         }

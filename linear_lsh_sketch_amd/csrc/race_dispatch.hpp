@@ -42,15 +42,27 @@ inline race_status_t launch_ok() {
         if (rc_ != RACE_OK) return rc_;      \
     } while (0)
 
-template <class C>
+// CACHED = false: sketch of K, [V | 1] (storing the keys' plane values in pc);
+// CACHED = true: gradient sketch of the queries from their plane values pc.
+template <class C, bool CACHED>
 race_status_t run_totals(const Shape& s, const Derived& d, const void* Xb, const void* Z, const float* Dv,
-                         const float* Ev, int kind, const void* W, float beta, float* out, hipStream_t st) {
+                         const float* Ev, const PlaneCache& pc, const void* W, float beta, float* out,
+                         hipStream_t st) {
     TotArgs a;
-    a.Xb = Xb; a.Z = Z; a.Dv = Dv; a.Ev = Ev; a.W = W; a.out = out;
-    a.N = s.N; a.chunk = s.chunk; a.nchunks = (int)d.NC; a.L = s.L; a.beta = beta; a.kind = kind;
-    profile_mark(kind == 0 ? "totals_kv" : "totals_qg", st);
-    hipLaunchKernelGGL(k_totals<C>, dim3((unsigned)d.NC, (unsigned)d.BH), dim3(NT), 0, st, a);
+    a.Xb = Xb; a.Z = Z; a.Dv = Dv; a.Ev = Ev; a.W = W; a.pc = pc; a.out = out;
+    a.N = s.N; a.chunk = s.chunk; a.nchunks = (int)d.NC; a.L = s.L; a.beta = beta;
+    profile_mark(CACHED ? "totals_qg" : "totals_kv", st);
+    hipLaunchKernelGGL((k_totals<C, CACHED>), dim3((unsigned)d.NC, (unsigned)d.BH), dim3(NT), 0, st, a);
     return launch_ok();
+}
+
+inline PlaneCache plane_cache(void* base, const CacheLayout& cl) {
+    char* b = reinterpret_cast<char*>(base);
+    PlaneCache p;
+    p.sig = reinterpret_cast<float*>(b + cl.sig);
+    p.gu = reinterpret_cast<float*>(b + cl.gu);
+    p.inv = reinterpret_cast<float*>(b + cl.inv);
+    return p;
 }
 
 template <int KIND>
@@ -89,17 +101,23 @@ race_status_t run_pass(const Shape& s, const Derived& d, PassArgs a, hipStream_t
     return launch_ok();
 }
 
-// Forward into O; when `saved` is set it receives the sketch states and D.
+// Forward into O; when `saved` is set it receives the sketch states, D and
+// the plane values of queries and keys (else the keys' go to the workspace).
 template <class C>
 race_status_t run_forward(const Shape& s, const Derived& d, const WsLayout& wl, const Call& c, void* O, void* saved) {
     char* ws = reinterpret_cast<char*>(c.ws);
     hipStream_t st = c.stream;
     const SavedLayout sl = saved_layout(s, d);
+    const CacheLayout cl = cache_layout(s, d);
+    char* sv = reinterpret_cast<char*>(saved);
+    const PlaneCache kc = plane_cache(saved ? sv + sl.k : ws + wl.Kc, cl);
+    PlaneCache qc{};
+    if (saved) qc = plane_cache(sv + sl.q, cl);
     float* Sb = (s.causal && saved) ? reinterpret_cast<float*>(saved) : reinterpret_cast<float*>(ws + wl.S);
-    RACE_TRY(run_totals<C>(s, d, c.K, c.V, nullptr, nullptr, 0, c.W, c.beta, Sb, st));
+    RACE_TRY((run_totals<C, false>(s, d, c.K, c.V, nullptr, nullptr, kc, c.W, c.beta, Sb, st)));
     PassArgs a{};
-    a.Xa = c.Q; a.Xb = c.K; a.Zsrc = c.V; a.W = c.W; a.beta = c.beta; a.out0 = O;
-    a.Dv = saved ? reinterpret_cast<float*>(reinterpret_cast<char*>(saved) + sl.D) : nullptr;
+    a.Xa = c.Q; a.ca = qc; a.cb = kc; a.Zsrc = c.V; a.W = c.W; a.beta = c.beta; a.out0 = O;
+    a.Dv = saved ? reinterpret_cast<float*>(sv + sl.D) : nullptr;
     if (s.causal) {
         RACE_TRY(run_scan<SCAN_EXCL>(d, Sb, nullptr, st));
         a.state = Sb; a.state_bh_stride = d.NC * d.F65; a.state_chunk_stride = d.F65;
@@ -135,8 +153,11 @@ race_status_t run(const Shape& s, const Derived& d, const WsLayout& wl, const Ca
         saved = ws + wl.Sv;
     }
     const SavedLayout sl = saved_layout(s, d);
+    const CacheLayout cl = cache_layout(s, d);
+    char* sv = const_cast<char*>(reinterpret_cast<const char*>(saved));
+    const PlaneCache qc = plane_cache(sv + sl.q, cl), kc = plane_cache(sv + sl.k, cl);
     const float* S = reinterpret_cast<const float*>(saved);
-    float* Dv = reinterpret_cast<float*>(const_cast<char*>(reinterpret_cast<const char*>(saved)) + sl.D);
+    float* Dv = reinterpret_cast<float*>(sv + sl.D);
     float* Ev = reinterpret_cast<float*>(ws + wl.E);
     using elem = typename Prec<C::F32>::elem;
     elem* WTp = reinterpret_cast<elem*>(ws + wl.wt);
@@ -145,7 +166,8 @@ race_status_t run(const Shape& s, const Derived& d, const WsLayout& wl, const Ca
     RACE_TRY(launch_ok());
 
     PassArgs q{};
-    q.Xa = c.Q; q.Xb = c.K; q.Zsrc = c.V; q.Ysrc = c.dO; q.Osrc = O; q.W = c.W; q.WTp = WTp; q.beta = c.beta;
+    q.Xa = c.Q; q.ca = qc; q.cb = kc; q.Zsrc = c.V; q.Ysrc = c.dO; q.Osrc = O; q.W = c.W; q.WTp = WTp;
+    q.beta = c.beta;
     q.Dv = Dv; q.Ev = Ev; q.out0 = c.dQ;
     q.state = S;
     q.state_bh_stride = s.causal ? d.NC * d.F65 : d.F65;
@@ -153,9 +175,9 @@ race_status_t run(const Shape& s, const Derived& d, const WsLayout& wl, const Ca
     RACE_TRY((run_pass<C, PASS_BWD_Q>(s, d, q, st)));
 
     float* Tw = reinterpret_cast<float*>(ws + wl.T);
-    RACE_TRY(run_totals<C>(s, d, c.Q, c.dO, Dv, Ev, 1, c.W, c.beta, Tw, st));
+    RACE_TRY((run_totals<C, true>(s, d, c.Q, c.dO, Dv, Ev, qc, c.W, c.beta, Tw, st)));
     PassArgs k{};
-    k.Xa = c.K; k.Xb = c.Q; k.Zsrc = c.dO; k.Ysrc = c.V; k.W = c.W; k.WTp = WTp; k.beta = c.beta;
+    k.Xa = c.K; k.ca = kc; k.cb = qc; k.Zsrc = c.dO; k.Ysrc = c.V; k.W = c.W; k.WTp = WTp; k.beta = c.beta;
     k.Dv = Dv; k.Ev = Ev; k.out0 = c.dK; k.out1 = c.dV;
     if (s.causal) {
         RACE_TRY(run_scan<SCAN_REV_EXCL>(d, Tw, nullptr, st));

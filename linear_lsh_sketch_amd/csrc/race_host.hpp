@@ -18,6 +18,7 @@ struct Shape {
 
 struct Derived {
     int Pp, MT, KB, F, NPAIR;
+    int NPL;       // projection rows per token (MT * 16)
     int64_t BH, NC;
     int64_t F65;   // floats per sketch state: F * 64 value sums + F masses
 };
@@ -31,18 +32,28 @@ struct WsLayout {
     size_t E;      // backward: per-token e = -<dO, O>/D
     size_t Sv;     // backward without saved: the recomputed forward's saved buffer
     size_t Ov;     // backward without saved: the recomputed forward output
+    size_t Kc;     // forward without saved: the keys' plane values
     size_t total;
 };
 
+// Plane values of one side (queries or keys), float32: sigmoid(2 beta u)
+// [rows][NPL], 2 beta (1 - u^2) [rows][NPL], 1 / max(|x|, eps) [rows].
+struct CacheLayout {
+    size_t sig, gu, inv, total;
+};
+
 // The saved buffer: float32 sketch states (per chunk, causal; the total,
-// non-causal) then the float32 per-token denominators D.
+// non-causal), the float32 per-token denominators D, then the plane values of
+// the queries and of the keys.
 struct SavedLayout {
     size_t D;
+    size_t q;       // queries' plane values
+    size_t k;       // keys' plane values
     size_t total;
 };
 
 // Workspace kinds (race_attn_workspace_bytes' for_backward argument).
-enum { WS_FWD = 0, WS_BWD = 1, WS_BWD_RECOMPUTE = 2 };
+enum { WS_FWD = 0, WS_BWD = 1, WS_BWD_RECOMPUTE = 2, WS_FWD_SAVED = 3 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -67,6 +78,7 @@ inline race_status_t derive(const Shape& s, Derived& d) {
     d.KB = (s.P == 4) ? 2 : 1;
     d.F = 32 * d.MT * d.KB;
     d.NPAIR = (d.MT + 1) / 2;
+    d.NPL = d.MT * 16;
     int64_t bh, elems;
     if (!mul_ok(s.B, s.H, bh) || !mul_ok(bh, s.N, elems) || !mul_ok(elems, s.d, elems))
         return RACE_ERR_INVALID_ARG;
@@ -78,12 +90,25 @@ inline race_status_t derive(const Shape& s, Derived& d) {
     return RACE_OK;
 }
 
+inline CacheLayout cache_layout(const Shape& s, const Derived& d) {
+    const size_t rows = (size_t)d.BH * (size_t)s.N;
+    CacheLayout c;
+    c.sig = 0;
+    c.gu = align256(rows * (size_t)d.NPL * sizeof(float));
+    c.inv = c.gu + align256(rows * (size_t)d.NPL * sizeof(float));
+    c.total = c.inv + align256(rows * sizeof(float));
+    return c;
+}
+
 inline SavedLayout saved_layout(const Shape& s, const Derived& d) {
     const size_t per = (size_t)d.F65 * sizeof(float);
     const size_t states = s.causal ? (size_t)d.BH * (size_t)d.NC * per : (size_t)d.BH * per;
+    const size_t cache = cache_layout(s, d).total;
     SavedLayout l;
     l.D = align256(states);
-    l.total = l.D + (size_t)d.BH * (size_t)s.N * sizeof(float);
+    l.q = l.D + align256((size_t)d.BH * (size_t)s.N * sizeof(float));
+    l.k = l.q + cache;
+    l.total = l.k + cache;
     return l;
 }
 
@@ -100,7 +125,10 @@ inline WsLayout ws_layout(const Shape& s, const Derived& d, int kind) {
         w.S = off;   off = align256(off + chunks);
         w.St = off;  off = align256(off + (s.causal ? 0 : totals));
     }
-    if (kind != WS_FWD) {
+    if (kind == WS_FWD) {
+        w.Kc = off;  off = align256(off + cache_layout(s, d).total);
+    }
+    if (kind == WS_BWD || kind == WS_BWD_RECOMPUTE) {
         w.wt = off;  off = align256(off + (size_t)d.NPAIR * 4 * 64 * 8 * sizeof(float));
         w.T = off;   off = align256(off + chunks);
         w.Tt = off;  off = align256(off + (s.causal ? 0 : totals));

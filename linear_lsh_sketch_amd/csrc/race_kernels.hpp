@@ -167,6 +167,34 @@ struct WSrc {
     }
 };
 
+// Per-token plane values of one side (queries or keys), written by the pass
+// that projects the rows and read by the later passes instead of projecting
+// again: s = sigmoid(2 beta u) and gu = 2 beta (1 - u^2) for every projection
+// row (tile-row order, NPL per token), and 1 / max(|x|, eps) per token, all
+// float32 (gu scales the gradient directly: no rounding to bf16).
+struct PlaneCache {
+    float* sig;   // [rows][NPL]
+    float* gu;    // [rows][NPL]
+    float* inv;   // [rows]
+};
+
+// The plane values of the own token for the tiles of one feature block.
+template <class C>
+struct Planes {
+    f32x4 s[C::TPB];
+    f32x4 gu[C::TPB];
+};
+
+template <class C, bool GU>
+__device__ inline void load_planes(const PlaneCache& pc, size_t row, bool valid, int fb, int g, Planes<C>& p) {
+#pragma unroll
+    for (int tb = 0; tb < C::TPB; ++tb) {
+        const size_t off = row * C::NPL + 16 * (fb * C::TPB + tb) + 4 * g;
+        p.s[tb] = valid ? *reinterpret_cast<const f32x4*>(pc.sig + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (GU) p.gu[tb] = valid ? *reinterpret_cast<const f32x4*>(pc.gu + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+}
+
 // Write the value tile of the 64 tokens (this thread: row th/4, quarter th%4)
 // into ZT [80][ROWT] (transposed) and optionally Zrow [64][ROWE] (rows):
 // z = [x * scale | mass]. Rows/columns 65.. stay zero from stage_constants.
@@ -290,18 +318,37 @@ __device__ inline void sketch_update(int fb, int w, int ln, int g, const typenam
     }
 }
 
+// Pack the lane's features of tile tb of the block and write them to LDS (row
+// layout `rows` and/or transposed `cols`); KEEP returns the operands.
+template <class C, bool KEEP>
+__device__ inline void emit_tile(int tb, int w, int ln, int g, const float phi[C::KB * 8],
+                                 typename Prec<C::F32>::elem* rows, typename Prec<C::F32>::elem* cols,
+                                 typename Prec<C::F32>::frag (&phi_frag)[C::FBK]) {
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+        const int kcl = tb * C::KB + kb;
+        const typename Prec<C::F32>::frag fr = pack8<C::F32>(phi + kb * 8);
+        if constexpr (KEEP) phi_frag[kcl] = fr;
+        if (rows) st_frag<C::F32>(rows + (16 * w + ln) * C::ROWF + 32 * kcl + 8 * g, fr);
+        if (cols) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) cols[(32 * kcl + 8 * g + j) * C::ROWT + 16 * w + ln] = fr[j];
+        }
+    }
+}
+
 // Project the own 16-token tile for the tiles of feature block fb and write
 // the features to LDS (row layout `rows` and/or transposed `cols`); when KEEP,
-// also return the lane's operands (one per chunk of the block) in phi_frag and,
-// per tile of the block, the plane probabilities s and 2 beta (1 - u^2) that
-// the chain rule needs.
+// also return the lane's operands (one per chunk of the block) in phi_frag.
+// With `out` set, the plane values of valid tokens are stored there (row
+// `row`) for later passes.
 template <class C, bool KEEP>
 __device__ inline void block_features(const WSrc<C>& wsrc, int fb, int lane, int w, int ln, int g,
                                       const typename Prec<C::F32>::frag xf[2], float inv, bool valid, float beta,
                                       int L, typename Prec<C::F32>::elem* rows /* [64][ROWF] or null */,
                                       typename Prec<C::F32>::elem* cols /* [FBK*32][ROWT] or null */,
-                                      typename Prec<C::F32>::frag (&phi_frag)[C::FBK],
-                                      float (&s_keep)[C::TPB][4], float (&gu_keep)[C::TPB][4]) {
+                                      typename Prec<C::F32>::frag (&phi_frag)[C::FBK], const PlaneCache* out,
+                                      size_t row) {
 #pragma unroll
     for (int tb = 0; tb < C::TPB; ++tb) {
         const int t = fb * C::TPB + tb;
@@ -310,24 +357,37 @@ __device__ inline void block_features(const WSrc<C>& wsrc, int fb, int lane, int
 #pragma unroll
         for (int i = 0; i < 4; ++i) hs[i] = acc[i] * inv;
         soft_features<C>(t, g, hs, beta, L, valid, phi, u, sg, gu);
+        if (out && valid) {
+            const size_t off = row * C::NPL + 16 * t + 4 * g;
+            *reinterpret_cast<f32x4*>(out->sig + off) = f32x4{sg[0], sg[1], sg[2], sg[3]};
+            *reinterpret_cast<f32x4*>(out->gu + off) = f32x4{gu[0], gu[1], gu[2], gu[3]};
+        }
+        emit_tile<C, KEEP>(tb, w, ln, g, phi, rows, cols, phi_frag);
+    }
+}
+
+// The same from stored plane values (no projection); when KEEP, also return
+// per tile the plane probabilities s and 2 beta (1 - u^2) for the chain rule.
+template <class C, bool KEEP>
+__device__ inline void block_features_cached(const Planes<C>& pl, int fb, int w, int ln, int g, bool valid, int L,
+                                             typename Prec<C::F32>::elem* rows,
+                                             typename Prec<C::F32>::elem* cols,
+                                             typename Prec<C::F32>::frag (&phi_frag)[C::FBK],
+                                             float (&s_keep)[C::TPB][4], float (&gu_keep)[C::TPB][4]) {
+#pragma unroll
+    for (int tb = 0; tb < C::TPB; ++tb) {
+        const int t = fb * C::TPB + tb;
+        const float sg[4] = {pl.s[tb][0], pl.s[tb][1], pl.s[tb][2], pl.s[tb][3]};
+        float phi[C::KB * 8];
+        features_from_planes<C>(t, g, sg, L, valid, phi);
         if constexpr (KEEP) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 s_keep[tb][i] = sg[i];
-                gu_keep[tb][i] = gu[i];
+                gu_keep[tb][i] = pl.gu[tb][i];
             }
         }
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) {
-            const int kcl = tb * C::KB + kb;
-            const typename Prec<C::F32>::frag fr = pack8<C::F32>(phi + kb * 8);
-            if constexpr (KEEP) phi_frag[kcl] = fr;
-            if (rows) st_frag<C::F32>(rows + (16 * w + ln) * C::ROWF + 32 * kcl + 8 * g, fr);
-            if (cols) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) cols[(32 * kcl + 8 * g + j) * C::ROWT + 16 * w + ln] = fr[j];
-            }
-        }
+        emit_tile<C, KEEP>(tb, w, ln, g, phi, rows, cols, phi_frag);
     }
 }
 
@@ -335,35 +395,38 @@ __device__ inline void block_features(const WSrc<C>& wsrc, int fb, int lane, int
 // per-chunk sketch totals
 // ---------------------------------------------------------------------------
 struct TotArgs {
-    const void* Xb;      // rows that write the sketch (K, or Q for the gradient sketch)
-    const void* Z;       // V (kind 0) or dO (kind 1)
-    const float* Dv;     // kind 1: per-token D
-    const float* Ev;     // kind 1: per-token e
+    const void* Xb;      // keys (projected here); unused for the gradient sketch
+    const void* Z;       // V, or dO for the gradient sketch
+    const float* Dv;     // gradient sketch: per-token D
+    const float* Ev;     // gradient sketch: per-token e
     const void* W;       // [L, P, 64]
+    PlaneCache pc;       // keys: where their plane values go; gradient sketch: the queries' plane values
     float* out;          // [BH][NC][F*65]
     int64_t N;
     int chunk;
     int nchunks;
     int L;
     float beta;
-    int kind;
 };
 
-template <class C>
+template <class C, bool CACHED>
 struct TotLds {
     using elem = typename Prec<C::F32>::elem;
     static constexpr int n_cols = C::FBK * 32 * C::ROWT;
     static constexpr int n_zt = ZR * C::ROWT;
-    static constexpr int n_w = C::MT * 1024;
+    static constexpr int n_w = CACHED ? 0 : C::MT * 1024;
     static constexpr int n_elem = n_cols + n_zt + n_w;
     static_assert(n_elem * (int)sizeof(elem) <= 160 * 1024, "LDS budget");
 };
 
-template <class C>
+// CACHED = false: sketch of the keys, [v | 1], projecting K (and storing the
+// keys' plane values); CACHED = true: gradient sketch of the queries,
+// [dO/D | e], from the queries' stored plane values.
+template <class C, bool CACHED>
 __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
     using elem = typename Prec<C::F32>::elem;
     using frag = typename Prec<C::F32>::frag;
-    using LD = TotLds<C>;
+    using LD = TotLds<C, CACHED>;
     __shared__ __attribute__((aligned(32))) elem lds[LD::n_elem];
     elem* s_cols = lds;
     elem* s_ZT = lds + LD::n_cols;
@@ -378,10 +441,13 @@ __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
     const int64_t seg0 = (int64_t)c * a.chunk;
     const int64_t seg1 = seg0 + a.chunk < a.N ? seg0 + a.chunk : a.N;
     const size_t base = (size_t)bh * a.N;
-    stage_w<C>(reinterpret_cast<const elem*>(a.W), a.L, s_w);
+    const int nsub = (int)((seg1 - seg0 + TB - 1) / TB);
+    const int my = 16 * w + ln;
+    if (!CACHED) stage_w<C>(reinterpret_cast<const elem*>(a.W), a.L, s_w);
     zero_pads<C>(s_ZT, nullptr, nullptr);
     __syncthreads();   // W' and the padding are written by all waves, read by each
     const WSrc<C> wsrc{s_w, reinterpret_cast<const elem*>(a.W), a.L};
+    const PlaneCache* pc_out = (!CACHED && a.pc.sig) ? &a.pc : nullptr;
 
     f32x4 Macc[C::NKC * 2], Zacc[C::NOWN * 2];
 #pragma unroll
@@ -389,37 +455,59 @@ __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
 #pragma unroll
     for (int i = 0; i < C::NOWN * 2; ++i) Zacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // prefetch registers for the next sub-block
+    // loads issued one sub-block (plane values: one feature block) ahead
     frag nx[2], nz[2];
     float nd = 1.f, ne = 0.f;
-    auto issue = [&](int64_t t0) {
-        const int nv = (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
-        load_row_raw<C::F32>(a.Xb, base + t0 + 16 * w + ln, 16 * w + ln < nv, g, nx);
+    Planes<C> pn;
+    auto nv_of = [&](int it2) {
+        const int64_t t0 = seg0 + (int64_t)it2 * TB;
+        return (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
+    };
+    auto issue = [&](int it2) {
+        const int64_t t0 = seg0 + (int64_t)it2 * TB;
+        const int nv = nv_of(it2);
+        if (!CACHED) load_row_raw<C::F32>(a.Xb, base + t0 + my, my < nv, g, nx);
         const bool ok = tr < nv;
         load_q16_raw<C::F32>(a.Z, (base + t0 + tr) * DH + 16 * tq, ok, nz);
-        if (a.kind == 1 && ok) {
+        if (CACHED && ok) {
             nd = a.Dv[base + t0 + tr];
             ne = a.Ev[base + t0 + tr];
         }
     };
-    issue(seg0);
-    for (int64_t t0 = seg0; t0 < seg1; t0 += TB) {
-        const int nv = (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
-        const bool valid = 16 * w + ln < nv;
+    auto issue_planes = [&](int it2, int fb2) {
+        load_planes<C, false>(a.pc, base + seg0 + (int64_t)it2 * TB + my, my < nv_of(it2), fb2, g, pn);
+    };
+    issue(0);
+    if (CACHED) issue_planes(0, 0);
+    for (int it = 0; it < nsub; ++it) {
+        const int64_t t0 = seg0 + (int64_t)it * TB;
+        const int nv = nv_of(it);
+        const bool valid = my < nv;
+        const size_t row = base + t0 + my;
         frag xf[2] = {nx[0], nx[1]}, zr[2] = {nz[0], nz[1]};
         const float dz = nd, ez = ne;
-        if (t0 + TB < seg1) issue(t0 + TB);
-        float inv, nrm;
-        row_norm<C::F32>(xf, inv, nrm);
+        if (it + 1 < nsub) issue(it + 1);
+        float inv = 0.f, nrm;
+        if (!CACHED) {
+            row_norm<C::F32>(xf, inv, nrm);
+            if (pc_out && valid && g == 0) pc_out->inv[row] = inv;
+        }
         const bool ok = tr < nv;
-        if (a.kind == 0) write_aug<C>(zr, 1.f, ok ? 1.f : 0.f, s_ZT, nullptr);
+        if (!CACHED) write_aug<C>(zr, 1.f, ok ? 1.f : 0.f, s_ZT, nullptr);
         else write_aug<C>(zr, ok ? rcp_(dz) : 0.f, ok ? ez : 0.f, s_ZT, nullptr);
 #pragma unroll
         for (int fb = 0; fb < C::NBLK; ++fb) {
             frag unused[C::FBK];
-            float unused_s[C::TPB][4], unused_g[C::TPB][4];
-            block_features<C, false>(wsrc, fb, lane, w, ln, g, xf, inv, valid, a.beta, a.L, nullptr, s_cols, unused,
-                                     unused_s, unused_g);
+            if constexpr (CACHED) {
+                const Planes<C> pl = pn;
+                if (fb + 1 < C::NBLK) issue_planes(it, fb + 1);
+                else if (it + 1 < nsub) issue_planes(it + 1, 0);
+                float us[C::TPB][4], ug[C::TPB][4];
+                block_features_cached<C, false>(pl, fb, w, ln, g, valid, a.L, nullptr, s_cols, unused, us, ug);
+            } else {
+                block_features<C, false>(wsrc, fb, lane, w, ln, g, xf, inv, valid, a.beta, a.L, nullptr, s_cols,
+                                         unused, pc_out, row);
+            }
             __syncthreads();
             sketch_update<C>(fb, w, ln, g, s_cols, s_ZT, Macc, Zacc);
             __syncthreads();
@@ -470,7 +558,8 @@ __global__ __launch_bounds__(256) void k_scan(float* __restrict__ st, float* __r
 // ---------------------------------------------------------------------------
 struct PassArgs {
     const void* Xa;        // readout-side rows (FWD, BWD_Q: Q; BWD_K: K)
-    const void* Xb;        // sketch-side rows (FWD, BWD_Q: K; BWD_K: Q)
+    PlaneCache ca;         // readout side's plane values: FWD stores them (if ca.sig), BWD_Q / BWD_K read them
+    PlaneCache cb;         // sketch side's plane values (read)
     const void* Zsrc;      // FWD, BWD_Q: V; BWD_K: dO
     const void* Ysrc;      // BWD_Q: dO; BWD_K: V
     const void* Osrc;      // BWD_Q: the forward output O
@@ -633,10 +722,11 @@ __device__ inline void intra_operand(const typename Prec<C::F32>::elem* s_zr, co
 }
 
 // dx = (dx_hat - x_hat <x_hat, dx_hat>) / |x| for the own token row (the chain
-// rule of x_hat = x / max(|x|, eps); below eps the map is a plain scaling).
-// dX[dt] holds columns 16 dt + 4 g .. +3.
+// rule of x_hat = x / max(|x|, eps); below eps the map is a plain scaling, and
+// inv = 1 / max(|x|, eps) tells which case holds). dX[dt] holds columns
+// 16 dt + 4 g .. +3.
 template <class C>
-__device__ inline void store_dx(const void* X, void* out, size_t row, bool valid, int g, float inv, float nrm,
+__device__ inline void store_dx(const void* X, void* out, size_t row, bool valid, int g, float inv,
                                 const f32x4 dX[4]) {
     using T = typename In<C::F32>::T;
     float xv[4][4];
@@ -659,7 +749,7 @@ __device__ inline void store_dx(const void* X, void* out, size_t row, bool valid
         for (int i = 0; i < 4; ++i) radial += xv[dt][i] * inv * dX[dt][i];
     }
     radial = sum_groups(radial);
-    const bool tangent = nrm > NORM_EPS;
+    const bool tangent = inv < rcp_(NORM_EPS);
     if (valid) {
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
@@ -764,6 +854,7 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
     zero_pads<C>(s_ZT, nullptr, nullptr);
     __syncthreads();   // W' and the padding are written by all waves, read by each
     const WSrc<C> wsrc{s_w, W, a.L};
+    const PlaneCache* pc_out = a.ca.sig ? &a.ca : nullptr;   // the queries' plane values for the backward
 
     f32x4 Macc[C::NKC * 2], Zacc[C::NOWN * 2];
     load_state<C>(a.state + bh * a.state_bh_stride + c * a.state_chunk_stride, w, ln, g, Macc, Zacc);
@@ -771,27 +862,37 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
     const int nsub = (int)((seg1 - seg0 + TB - 1) / TB);
     const int my = 16 * w + ln;              // own token within the sub-block
 
-    frag n_xa[2], n_xb[2], n_z[2];
+    // loads issued one sub-block (the keys' plane values: one feature block) ahead
+    frag n_xa[2], n_z[2];
+    Planes<C> pn;
+    auto nv_of = [&](int it2) {
+        const int64_t t0 = seg0 + (int64_t)it2 * TB;
+        return (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
+    };
     auto issue = [&](int it2) {
         const int64_t t0 = seg0 + (int64_t)it2 * TB;
-        const int nv = (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
+        const int nv = nv_of(it2);
         load_row_raw<C::F32>(a.Xa, base + t0 + my, my < nv, g, n_xa);
-        load_row_raw<C::F32>(a.Xb, base + t0 + my, my < nv, g, n_xb);
         load_q16_raw<C::F32>(a.Zsrc, (base + t0 + tr) * DH + 16 * tq, tr < nv, n_z);
     };
+    auto issue_planes = [&](int it2, int fb2) {
+        load_planes<C, false>(a.cb, base + seg0 + (int64_t)it2 * TB + my, my < nv_of(it2), fb2, g, pn);
+    };
     issue(0);
+    issue_planes(0, 0);
 
     for (int it = 0; it < nsub; ++it) {
         const int64_t t0 = seg0 + (int64_t)it * TB;
-        const int nv = (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
+        const int nv = nv_of(it);
         const bool valid = my < nv;
         const bool tok = tr < nv;
-        frag xa[2] = {n_xa[0], n_xa[1]}, xb[2] = {n_xb[0], n_xb[1]}, zr[2] = {n_z[0], n_z[1]};
+        const size_t row = base + t0 + my;
+        frag xa[2] = {n_xa[0], n_xa[1]}, zr[2] = {n_z[0], n_z[1]};
         if (it + 1 < nsub) issue(it + 1);
 
-        float inv_a, nrm_a, inv_b, nrm_b;
+        float inv_a, nrm_a;
         row_norm<C::F32>(xa, inv_a, nrm_a);
-        row_norm<C::F32>(xb, inv_b, nrm_b);
+        if (pc_out && valid && g == 0) pc_out->inv[row] = inv_a;
         write_aug<C>(zr, 1.f, tok ? 1.f : 0.f, s_ZT, nullptr);
 
         f32x4 Y[4], Dacc[4], Sc[4];
@@ -804,11 +905,14 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
 #pragma unroll
         for (int fb = 0; fb < C::NBLK; ++fb) {
             frag phiA[C::FBK], unused[C::FBK];
-            float unused_s[C::TPB][4], unused_g[C::TPB][4];
-            block_features<C, true>(wsrc, fb, lane, w, ln, g, xa, inv_a, true, a.beta, a.L, s_rows, nullptr, phiA,
-                                    unused_s, unused_g);
-            block_features<C, false>(wsrc, fb, lane, w, ln, g, xb, inv_b, valid, a.beta, a.L, s_brow,
-                                     causal ? s_cols : nullptr, unused, unused_s, unused_g);
+            const Planes<C> pl = pn;
+            if (fb + 1 < C::NBLK) issue_planes(it, fb + 1);
+            else if (it + 1 < nsub) issue_planes(it + 1, 0);
+            block_features<C, true>(wsrc, fb, lane, w, ln, g, xa, inv_a, valid, a.beta, a.L, s_rows, nullptr, phiA,
+                                    pc_out, row);
+            float us[C::TPB][4], ug[C::TPB][4];
+            block_features_cached<C, false>(pl, fb, w, ln, g, valid, a.L, s_brow, causal ? s_cols : nullptr, unused,
+                                            us, ug);
             __syncthreads();
             if (causal) {
 #pragma unroll
@@ -918,9 +1022,9 @@ struct BwdQLds {
     static constexpr int o_zr = o_zt + n_zt;
     static constexpr int o_yr = o_zr + n_zr;
     static constexpr int o_ylo = o_yr + n_yr;
-    static constexpr int o_w = o_ylo + n_ylo;
+    static constexpr int n_elem = o_ylo + n_ylo;
     static constexpr int OCC = (!C::F32 && C::NKC <= 8) ? 2 : 1;
-    using WS = WStage<elem, o_w, 0, C::MT, OCC>;
+    static_assert(n_elem * (int)sizeof(elem) * OCC <= 160 * 1024, "LDS budget");
 };
 
 template <class C, bool CAUSAL>
@@ -928,7 +1032,7 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
     using elem = typename Prec<C::F32>::elem;
     using frag = typename Prec<C::F32>::frag;
     using LD = BwdQLds<C>;
-    __shared__ __attribute__((aligned(32))) elem lds[LD::WS::n_elem];
+    __shared__ __attribute__((aligned(32))) elem lds[LD::n_elem];
     elem* s_ms = lds + LD::o_ms;
     elem* s_cols = lds + LD::o_cols;
     elem* s_ZT = lds + LD::o_zt;
@@ -943,16 +1047,12 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
     const int64_t seg0 = (int64_t)c * a.chunk;
     const int64_t seg1 = seg0 + a.chunk < a.N ? seg0 + a.chunk : a.N;
     const size_t base = (size_t)bh * a.N;
-    const elem* W = reinterpret_cast<const elem*>(a.W);
     const elem* WTp = reinterpret_cast<const elem*>(a.WTp);
     constexpr bool causal = CAUSAL;
-    elem* s_w = LD::WS::on ? lds + LD::o_w : nullptr;
-    if (LD::WS::on) stage_w<C>(W, a.L, s_w);
     zero_pads<C>(s_ZT, s_zr, s_yr);
     if (LD::YLO) zero_pads<C>(s_ZT, s_ylo, nullptr);
     zero_sketch_pads<C>(s_ms);
-    __syncthreads();   // W' and the padding are written by all waves, read by each
-    const WSrc<C> wsrc{s_w, W, a.L};
+    __syncthreads();   // the padding is written by all waves, read by each
 
     f32x4 Macc[C::NKC * 2], Zacc[C::NOWN * 2];
     load_state<C>(a.state + bh * a.state_bh_stride + c * a.state_chunk_stride, w, ln, g, Macc, Zacc);
@@ -960,20 +1060,25 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
     const int nsub = (int)((seg1 - seg0 + TB - 1) / TB);
     const int my = 16 * w + ln;
 
-    // the projection rows are loaded one sub-block ahead; the value, gradient
-    // and output rows at the top of their sub-block (register budget)
-    frag n_xa[2], n_xb[2];
-    auto issue = [&](int it2) {
+    // the plane values of queries (with 2 beta (1 - u^2)) and keys are loaded
+    // one feature block ahead; the value, gradient and output rows at the top
+    // of their sub-block (register budget)
+    Planes<C> pa, pb;
+    auto nv_of = [&](int it2) {
         const int64_t t0 = seg0 + (int64_t)it2 * TB;
-        const int nv = (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
-        load_row_raw<C::F32>(a.Xa, base + t0 + my, my < nv, g, n_xa);
-        if (causal) load_row_raw<C::F32>(a.Xb, base + t0 + my, my < nv, g, n_xb);
+        return (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
     };
-    issue(0);
+    auto issue_planes = [&](int it2, int fb2) {
+        const size_t r2 = base + seg0 + (int64_t)it2 * TB + my;
+        const bool v2 = my < nv_of(it2);
+        load_planes<C, true>(a.ca, r2, v2, fb2, g, pa);
+        if (causal) load_planes<C, false>(a.cb, r2, v2, fb2, g, pb);
+    };
+    issue_planes(0, 0);
 
     for (int it = 0; it < nsub; ++it) {
         const int64_t t0 = seg0 + (int64_t)it * TB;
-        const int nv = (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
+        const int nv = nv_of(it);
         const bool valid = my < nv;
         const size_t row = base + t0 + my;
         const bool tok = tr < nv;
@@ -982,15 +1087,8 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
         load_q16_raw<C::F32>(a.Ysrc, (base + t0 + tr) * DH + 16 * tq, tok, yr);
         load_q16_raw<C::F32>(a.Osrc, (base + t0 + tr) * DH + 16 * tq, tok, orow);
         const float dd = tok ? a.Dv[base + t0 + tr] : 1.f;
-        frag xa[2] = {n_xa[0], n_xa[1]}, xb[2] = {n_xb[0], n_xb[1]};
-        if (it + 1 < nsub) issue(it + 1);
-
-        float inv_a, nrm_a, inv_b = 0.f, nrm_b;
-        row_norm<C::F32>(xa, inv_a, nrm_a);
-        if (causal) {
-            row_norm<C::F32>(xb, inv_b, nrm_b);
-            write_aug<C>(zr, 1.f, tok ? 1.f : 0.f, s_ZT, s_zr);
-        }
+        const float inv_a = valid ? a.ca.inv[row] : 1.f;
+        if (causal) write_aug<C>(zr, 1.f, tok ? 1.f : 0.f, s_ZT, s_zr);
         // y = [dO / D | e], e = -<dO, O> / D; this thread holds 16 columns of row tr
         {
             float delta = 0.f;
@@ -1036,12 +1134,14 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
         const float zshift = (causal ? (float)t0 : (float)a.N) / (float)C::R;
 #pragma unroll
         for (int fb = 0; fb < C::NBLK; ++fb) {
+            const Planes<C> qa = pa, kb_ = pb;
+            if (fb + 1 < C::NBLK) issue_planes(it, fb + 1);
+            else if (it + 1 < nsub) issue_planes(it + 1, 0);
             write_sketch_rows<C>(fb, w, ln, g, Macc, Zacc, zshift, s_ms);
             if (causal) {
                 frag unused[C::FBK];
-                float unused_s[C::TPB][4], unused_g[C::TPB][4];
-                block_features<C, false>(wsrc, fb, lane, w, ln, g, xb, inv_b, valid, a.beta, a.L, nullptr, s_cols,
-                                         unused, unused_s, unused_g);
+                float us[C::TPB][4], ug[C::TPB][4];
+                block_features_cached<C, false>(kb_, fb, w, ln, g, valid, a.L, nullptr, s_cols, unused, us, ug);
             }
             __syncthreads();
             frag yf[3];
@@ -1052,11 +1152,13 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
 #pragma unroll
             for (int tb = 0; tb < C::TPB; ++tb) {
                 const int t = fb * C::TPB + tb;
-                const f32x4 acc = wsrc.project(t, lane, ln, g, xa);
-                float hs[4], phi[C::KB * 8], u[4], sg[4], gu[4], dA[C::KB * 8];
+                float phi[C::KB * 8], sg[4], gu[4], dA[C::KB * 8];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) hs[i] = acc[i] * inv_a;
-                soft_features<C>(t, g, hs, a.beta, a.L, true, phi, u, sg, gu);
+                for (int i = 0; i < 4; ++i) {
+                    sg[i] = qa.s[tb][i];
+                    gu[i] = qa.gu[tb][i];
+                }
+                features_from_planes<C>(t, g, sg, a.L, valid, phi);
 #pragma unroll
                 for (int kb = 0; kb < C::KB; ++kb) {
                     const int kcl = tb * C::KB + kb;
@@ -1071,7 +1173,7 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
             if (causal) sketch_update<C>(fb, w, ln, g, s_cols, s_ZT, Macc, Zacc);
             __syncthreads();
         }
-        store_dx<C>(a.Xa, a.out0, row, valid, g, inv_a, nrm_a, dX);
+        store_dx<C>(a.Xa, a.out0, row, valid, g, inv_a, dX);
     }
 }
 
@@ -1104,9 +1206,9 @@ struct BwdKLds {
     static constexpr int o_zt = o_ms + n_ms;
     static constexpr int o_zr = o_zt + n_zt;
     static constexpr int o_yr = o_zr + n_zr;
-    static constexpr int o_w = o_yr + n_yr;
+    static constexpr int n_elem = o_yr + n_yr;
     static constexpr int OCC = 1;
-    using WS = WStage<elem, o_w, 0, C::MT, OCC>;
+    static_assert(n_elem * (int)sizeof(elem) * OCC <= 160 * 1024, "LDS budget");
 };
 
 template <class C, bool CAUSAL>
@@ -1114,7 +1216,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C>::OCC)) void k_bwd_k(PassArgs a) {
     using elem = typename Prec<C::F32>::elem;
     using frag = typename Prec<C::F32>::frag;
     using LD = BwdKLds<C>;
-    __shared__ __attribute__((aligned(32))) elem lds[LD::WS::n_elem];
+    __shared__ __attribute__((aligned(32))) elem lds[LD::n_elem];
     elem* s_rows = lds + LD::o_rows;
     elem* s_brow = lds + LD::o_brow;
     elem* s_cols = lds + LD::o_cols;
@@ -1132,15 +1234,11 @@ __global__ __launch_bounds__(NT, (BwdKLds<C>::OCC)) void k_bwd_k(PassArgs a) {
     const int64_t seg0 = (int64_t)c * a.chunk;
     const int64_t seg1 = seg0 + a.chunk < a.N ? seg0 + a.chunk : a.N;
     const size_t base = (size_t)bh * a.N;
-    const elem* W = reinterpret_cast<const elem*>(a.W);
     const elem* WTp = reinterpret_cast<const elem*>(a.WTp);
     constexpr bool causal = CAUSAL;
-    elem* s_w = LD::WS::on ? lds + LD::o_w : nullptr;
-    if (LD::WS::on) stage_w<C>(W, a.L, s_w);
     zero_pads<C>(s_ZT, s_zr, s_yr);
     zero_sketch_pads<C>(s_ms);
-    __syncthreads();   // W' and the padding are written by all waves, read by each
-    const WSrc<C> wsrc{s_w, W, a.L};
+    __syncthreads();   // the padding is written by all waves, read by each
 
     f32x4 Macc[C::NKC * 2], Zacc[C::NOWN * 2];
     load_state<C>(a.state + bh * a.state_bh_stride + c * a.state_chunk_stride, w, ln, g, Macc, Zacc);
@@ -1148,16 +1246,21 @@ __global__ __launch_bounds__(NT, (BwdKLds<C>::OCC)) void k_bwd_k(PassArgs a) {
     const int nsub = (int)((seg1 - seg0 + TB - 1) / TB);
     const int my = 16 * w + ln;
 
-    // global loads are issued one sub-block ahead
-    frag n_xa[2], n_xb[2], n_z[2], n_y[2];
-    float n_d = 1.f, n_e = 0.f;
+    // global loads are issued one sub-block (plane values: one feature block) ahead
+    frag n_z[2], n_y[2];
+    float n_d = 1.f, n_e = 0.f, n_inv = 1.f;
+    Planes<C> pa, pb;
+    auto t0_of = [&](int it2) { return seg0 + (int64_t)(nsub - 1 - it2) * TB; };
+    auto nv_of = [&](int it2) {
+        const int64_t t0 = t0_of(it2);
+        return (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
+    };
     auto issue = [&](int it2) {
-        const int64_t t0 = seg0 + (int64_t)(nsub - 1 - it2) * TB;
-        const int nv = (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
+        const int64_t t0 = t0_of(it2);
+        const int nv = nv_of(it2);
         const bool ok = tr < nv;
-        load_row_raw<C::F32>(a.Xa, base + t0 + my, my < nv, g, n_xa);
+        if (my < nv) n_inv = a.ca.inv[base + t0 + my];
         if (causal) {
-            load_row_raw<C::F32>(a.Xb, base + t0 + my, my < nv, g, n_xb);
             load_q16_raw<C::F32>(a.Zsrc, (base + t0 + tr) * DH + 16 * tq, ok, n_z);
             if (ok) {
                 n_d = a.Dv[base + t0 + tr];
@@ -1166,25 +1269,26 @@ __global__ __launch_bounds__(NT, (BwdKLds<C>::OCC)) void k_bwd_k(PassArgs a) {
         }
         load_q16_raw<C::F32>(a.Ysrc, (base + t0 + tr) * DH + 16 * tq, ok, n_y);
     };
+    auto issue_planes = [&](int it2, int fb2) {
+        const size_t r2 = base + t0_of(it2) + my;
+        const bool v2 = my < nv_of(it2);
+        load_planes<C, true>(a.ca, r2, v2, fb2, g, pa);
+        if (causal) load_planes<C, false>(a.cb, r2, v2, fb2, g, pb);
+    };
     issue(0);
+    issue_planes(0, 0);
 
     for (int it = 0; it < nsub; ++it) {
-        const int64_t t0 = seg0 + (int64_t)(nsub - 1 - it) * TB;
-        const int nv = (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
+        const int64_t t0 = t0_of(it);
+        const int nv = nv_of(it);
         const bool valid = my < nv;
         const size_t row = base + t0 + my;
         const bool tok = tr < nv;
-        frag xa[2] = {n_xa[0], n_xa[1]}, xb[2] = {n_xb[0], n_xb[1]};
         frag zr[2] = {n_z[0], n_z[1]}, yr[2] = {n_y[0], n_y[1]};
-        const float zd = n_d, ze = n_e;
+        const float zd = n_d, ze = n_e, inv_a = n_inv;
         if (it + 1 < nsub) issue(it + 1);
 
-        float inv_a, nrm_a, inv_b = 0.f, nrm_b;
-        row_norm<C::F32>(xa, inv_a, nrm_a);
-        if (causal) {
-            row_norm<C::F32>(xb, inv_b, nrm_b);
-            write_aug<C>(zr, tok ? rcp_(zd) : 0.f, tok ? ze : 0.f, s_ZT, s_zr);
-        }
+        if (causal) write_aug<C>(zr, tok ? rcp_(zd) : 0.f, tok ? ze : 0.f, s_ZT, s_zr);
         // y rows = [v | 1]
         {
             float v[16];
@@ -1211,12 +1315,12 @@ __global__ __launch_bounds__(NT, (BwdKLds<C>::OCC)) void k_bwd_k(PassArgs a) {
 #pragma unroll
         for (int fb = 0; fb < C::NBLK; ++fb) {
             frag phiA[C::FBK], unused[C::FBK];
-            float sA[C::TPB][4], guA[C::TPB][4], unused_s[C::TPB][4], unused_g[C::TPB][4];
-            block_features<C, true>(wsrc, fb, lane, w, ln, g, xa, inv_a, valid, a.beta, a.L, s_rows, nullptr, phiA,
-                                    sA, guA);
-            if (causal)
-                block_features<C, false>(wsrc, fb, lane, w, ln, g, xb, inv_b, valid, a.beta, a.L, s_brow, s_cols,
-                                         unused, unused_s, unused_g);
+            float sA[C::TPB][4], guA[C::TPB][4], us[C::TPB][4], ug[C::TPB][4];
+            const Planes<C> ka = pa, qb = pb;
+            if (fb + 1 < C::NBLK) issue_planes(it, fb + 1);
+            else if (it + 1 < nsub) issue_planes(it + 1, 0);
+            block_features_cached<C, true>(ka, fb, w, ln, g, valid, a.L, s_rows, nullptr, phiA, sA, guA);
+            if (causal) block_features_cached<C, false>(qb, fb, w, ln, g, valid, a.L, s_brow, s_cols, unused, us, ug);
             write_sketch_rows<C>(fb, w, ln, g, Macc, Zacc, 0.f, s_ms);
             __syncthreads();
             if (causal) {
@@ -1292,7 +1396,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C>::OCC)) void k_bwd_k(PassArgs a) {
                 s_stage[(16 * at + 4 * g + i) * C::ROWD + 16 * w + ln] = to_elem<C::F32>(Y[at][i]);
         __syncthreads();
         store_stage<C>(a.out1, base + t0, tr, tq, tok, s_stage);
-        store_dx<C>(a.Xa, a.out0, row, valid, g, inv_a, nrm_a, dX);
+        store_dx<C>(a.Xa, a.out0, row, valid, g, inv_a, dX);
     }
 }
 

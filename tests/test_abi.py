@@ -42,29 +42,39 @@ def test_status_strings():
     assert race.status_string(99) == "RACE_ERR_UNKNOWN"
 
 
+def _a256(x):
+    return -(-x // 256) * 256
+
+
 def test_workspace_and_saved_sizes():
     # causal: per-chunk states of F * 65 floats (F = 32 * MT * KB), then one
-    # float32 denominator per token
-    N = 12_000_000
+    # float32 denominator per token, then for queries and keys the per-token
+    # plane values (16 * MT sigmoids, 16 * MT chain-rule factors, one norm)
+    N, rows = 12_000_000, 4 * 12_000_000
     fwd = race.workspace_bytes(1, 4, N, 64, 4, 16, True, 1024, race.WS_FWD)
+    fwd_s = race.workspace_bytes(1, 4, N, 64, 4, 16, True, 1024, race.WS_FWD_SAVED)
     bwd = race.workspace_bytes(1, 4, N, 64, 4, 16, True, 1024, race.WS_BWD)
     rec = race.workspace_bytes(1, 4, N, 64, 4, 16, True, 1024, race.WS_BWD_RECOMPUTE)
     saved = race.saved_bytes(1, 4, N, 64, 4, 16, True, 1024)
     nchunks = -(-N // 1024)
     states = 4 * nchunks * 256 * 65 * 4
-    assert saved == -(-states // 256) * 256 + 4 * N * 4
-    assert fwd >= states
+    cache = _a256(rows * 64 * 4) * 2 + _a256(rows * 4)
+    assert saved == _a256(states) + _a256(rows * 4) + 2 * cache
+    assert fwd_s >= states and fwd >= fwd_s + cache
     # gradient states and e per token
-    assert bwd >= states + 4 * N * 4
+    assert bwd >= states + rows * 4
     # plus a saved buffer and the forward output (float32 bound)
-    assert rec >= fwd + bwd + saved + 4 * N * 64 * 4
-    states_nc = 6 * 32 * 65 * 4
-    assert race.saved_bytes(2, 3, 100, 64, 2, 8, False, 64) == -(-states_nc // 256) * 256 + 6 * 100 * 4
+    assert rec >= fwd_s + bwd + saved + rows * 64 * 4
+    # non-causal: the total sketch (L8 P2: MT = 1, F = 32)
+    rows_nc = 6 * 100
+    cache_nc = _a256(rows_nc * 16 * 4) * 2 + _a256(rows_nc * 4)
+    assert race.saved_bytes(2, 3, 100, 64, 2, 8, False, 64) == \
+        _a256(6 * 32 * 65 * 4) + _a256(rows_nc * 4) + 2 * cache_nc
 
 
 def test_workspace_kind_rejected():
     out = ctypes.c_size_t(0)
-    for kind in (-1, 3):
+    for kind in (-1, 4):
         assert race.lib().race_attn_workspace_bytes(1, 1, 10, 64, 4, 8, 1, 16, kind, ctypes.byref(out)) == \
             race.RACE_ERR_INVALID_ARG
 
