@@ -197,10 +197,13 @@ __device__ inline void load_planes(const PlaneCache& pc, size_t row, bool valid,
 
 // Write the value tile of the 64 tokens (this thread: row th/4, quarter th%4)
 // into ZT [80][ROWT] (transposed) and optionally Zrow [64][ROWE] (rows):
-// z = [x * scale | mass]. Rows/columns 65.. stay zero from stage_constants.
+// z = [x * scale | mass]. With Zlo set, also the rows of the rounding residual
+// z - elem(z) (so that hi + lo carries z to float32 precision). Rows/columns
+// 65.. stay zero from zero_pads.
 template <class C>
 __device__ inline void write_aug(const typename Prec<C::F32>::frag zr[2], float scale, float mass,
-                                 typename Prec<C::F32>::elem* ZT, typename Prec<C::F32>::elem* Zrow) {
+                                 typename Prec<C::F32>::elem* ZT, typename Prec<C::F32>::elem* Zrow,
+                                 typename Prec<C::F32>::elem* Zlo = nullptr) {
     const int th = threadIdx.x, r = th >> 2, q = th & 3;
     float v[16];
 #pragma unroll
@@ -209,9 +212,22 @@ __device__ inline void write_aug(const typename Prec<C::F32>::frag zr[2], float 
     for (int c = 0; c < 16; ++c) ZT[(16 * q + c) * C::ROWT + r] = to_elem<C::F32>(v[c]);
     if (q == 0) ZT[64 * C::ROWT + r] = to_elem<C::F32>(mass);
     if (Zrow) {
-        st_frag<C::F32>(Zrow + r * C::ROWE + 16 * q, pack8<C::F32>(v));
-        st_frag<C::F32>(Zrow + r * C::ROWE + 16 * q + 8, pack8<C::F32>(v + 8));
-        if (q == 0) Zrow[r * C::ROWE + 64] = to_elem<C::F32>(mass);
+        const typename Prec<C::F32>::frag h0 = pack8<C::F32>(v), h1 = pack8<C::F32>(v + 8);
+        st_frag<C::F32>(Zrow + r * C::ROWE + 16 * q, h0);
+        st_frag<C::F32>(Zrow + r * C::ROWE + 16 * q + 8, h1);
+        const typename Prec<C::F32>::elem mh = to_elem<C::F32>(mass);
+        if (q == 0) Zrow[r * C::ROWE + 64] = mh;
+        if (Zlo) {
+            float lo[16];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                lo[c] = v[c] - elem_f<C::F32>(h0[c]);
+                lo[8 + c] = v[8 + c] - elem_f<C::F32>(h1[c]);
+            }
+            st_frag<C::F32>(Zlo + r * C::ROWE + 16 * q, pack8<C::F32>(lo));
+            st_frag<C::F32>(Zlo + r * C::ROWE + 16 * q + 8, pack8<C::F32>(lo + 8));
+            if (q == 0) Zlo[r * C::ROWE + 64] = to_elem<C::F32>(mass - elem_f<C::F32>(mh));
+        }
     }
 }
 
@@ -686,12 +702,16 @@ __device__ inline void chain_backproject(int t, int lane, const float phi[C::KB 
 }
 
 // Intra-sub-block operand of the gradient contraction: Cc[b][a] = z_b . y_a
-// over the augmented width (y = hi + lo when YLO), kept where key-side token b
-// is visible from the own token a (b <= a, or b >= a when REV) and b < nv;
-// returned as the two B operands of phi_b^T Cc (K index = b).
-template <class C, bool REV, bool YLO>
-__device__ inline void intra_operand(const typename Prec<C::F32>::elem* s_zr, const typename Prec<C::F32>::elem* s_yr,
-                                     const typename Prec<C::F32>::elem* s_ylo, int w, int ln, int g, int my, int nv,
+// over the augmented width (y = hi + lo when YLO, z = hi + lo when ZLO; the
+// lo x lo term is below float32 resolution), kept where sketch-side token b is
+// visible from the own token a (b <= a, or b >= a when REV) and b < nv;
+// returned as the two B operands of phi_b^T Cc (K index = b). The split
+// matters where z_b . y_a nearly cancels: a query against its only key, so it
+// is applied (lo = true) in the sub-block that starts the sequence.
+template <class C, bool REV, bool YLO, bool ZLO>
+__device__ inline void intra_operand(const typename Prec<C::F32>::elem* s_zr, const typename Prec<C::F32>::elem* s_zlo,
+                                     const typename Prec<C::F32>::elem* s_yr, const typename Prec<C::F32>::elem* s_ylo,
+                                     bool lo, int w, int ln, int g, int my, int nv,
                                      typename Prec<C::F32>::frag (&Cf)[2]) {
     using frag = typename Prec<C::F32>::frag;
     f32x4 Cc[4];
@@ -707,7 +727,9 @@ __device__ inline void intra_operand(const typename Prec<C::F32>::elem* s_zr, co
             for (int s = 0; s < 3; ++s) {
                 const frag zf = ld_frag<C::F32>(s_zr + (16 * bt + ln) * C::ROWE + 32 * s + 8 * g);
                 Cc[bt] = mma(zf, yf[s], Cc[bt]);
-                if constexpr (YLO) Cc[bt] = mma(zf, ld_frag<C::F32>(s_ylo + my * C::ROWE + 32 * s + 8 * g), Cc[bt]);
+                if (YLO && lo) Cc[bt] = mma(zf, ld_frag<C::F32>(s_ylo + my * C::ROWE + 32 * s + 8 * g), Cc[bt]);
+                if (ZLO && lo)
+                    Cc[bt] = mma(ld_frag<C::F32>(s_zlo + (16 * bt + ln) * C::ROWE + 32 * s + 8 * g), yf[s], Cc[bt]);
             }
         }
 #pragma unroll
@@ -943,7 +965,11 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
             if (causal) sketch_update<C>(fb, w, ln, g, s_cols, s_ZT, Macc, Zacc);
             __syncthreads();
         }
-        // intra-sub-block term: scores of visible keys b <= a
+        // intra-sub-block term: scores of visible keys b <= a. The value
+        // readout multiplies the scores rounded to the operand type, so the
+        // denominator sums the same rounded scores: O is then exactly a
+        // weighted mean of the values (a lone key gives O = v, and the
+        // backward's g.v + e cancels to float32 precision).
         if (causal) {
             float dint = 0.f;
 #pragma unroll
@@ -953,7 +979,7 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
                 for (int i = 0; i < 4; ++i) {
                     const int b = 16 * bt + 4 * g + i;
                     const bool vis = b <= my && b < nv;
-                    v[i] = vis ? Sc[bt][i] : 0.f;
+                    v[i] = vis ? elem_f<C::F32>(to_elem<C::F32>(Sc[bt][i])) : 0.f;
                     dint += v[i];
                 }
                 st_half<C::F32>(s_sc + my * C::ROWT + 16 * bt + 4 * g, v);
@@ -1007,8 +1033,8 @@ template <class C>
 struct BwdQLds {
     using elem = typename Prec<C::F32>::elem;
     // bf16 residual of the y rows: the intra-sub-block product g.v + e
-    // cancels for the first keys of a sequence, so it is formed from
-    // y = hi + lo with float32 accumulation
+    // cancels for a query against the first keys of a sequence, so in that
+    // sub-block it is formed from y = hi + lo with float32 accumulation
     static constexpr bool YLO = !C::F32;
     static constexpr int n_ms = C::FBK * 32 * C::ROWE;          // sketch rows
     static constexpr int n_cols = C::FBK * 32 * C::ROWT;        // key features transposed
@@ -1088,6 +1114,7 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
         load_q16_raw<C::F32>(a.Osrc, (base + t0 + tr) * DH + 16 * tq, tok, orow);
         const float dd = tok ? a.Dv[base + t0 + tr] : 1.f;
         const float inv_a = valid ? a.ca.inv[row] : 1.f;
+        const bool first = t0 == 0;   // the sub-block that starts the sequence
         if (causal) write_aug<C>(zr, 1.f, tok ? 1.f : 0.f, s_ZT, s_zr);
         // y = [dO / D | e], e = -<dO, O> / D; this thread holds 16 columns of row tr
         {
@@ -1104,7 +1131,7 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
             const frag h0 = pack8<C::F32>(v), h1 = pack8<C::F32>(v + 8);
             st_frag<C::F32>(s_yr + tr * C::ROWE + 16 * tq, h0);
             st_frag<C::F32>(s_yr + tr * C::ROWE + 16 * tq + 8, h1);
-            if constexpr (LD::YLO) {
+            if (LD::YLO && first) {
                 float lo[16];
 #pragma unroll
                 for (int cc = 0; cc < 8; ++cc) {
@@ -1117,13 +1144,14 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
             if (tq == 0) {
                 const elem eh = to_elem<C::F32>(e);
                 s_yr[tr * C::ROWE + 64] = eh;
-                if constexpr (LD::YLO) s_ylo[tr * C::ROWE + 64] = to_elem<C::F32>(e - elem_f<C::F32>(eh));
+                if (LD::YLO && first) s_ylo[tr * C::ROWE + 64] = to_elem<C::F32>(e - elem_f<C::F32>(eh));
                 if (tok) a.Ev[base + t0 + tr] = e;
             }
         }
         __syncthreads();
         frag Cf[2];
-        if (causal) intra_operand<C, false, LD::YLO>(s_zr, s_yr, s_ylo, w, ln, g, my, nv, Cf);
+        if (causal)
+            intra_operand<C, false, LD::YLO, false>(s_zr, nullptr, s_yr, s_ylo, first, w, ln, g, my, nv, Cf);
         f32x4 dX[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) dX[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1194,6 +1222,10 @@ struct BwdKLds {
     static constexpr int n_zt = ZR * C::ROWT;                   // [g | e] transposed
     static constexpr int n_sc = TB * C::ROWT;                   // intra scores [a][b] (alias of cols | ms)
     static constexpr int n_zr = TB * C::ROWE;                   // [g | e] rows
+    // bf16 residual of the [g | e] rows: the intra-sub-block product g.v + e
+    // cancels for a query against its only key
+    static constexpr bool ZLO = !C::F32;
+    static constexpr int n_zlo = ZLO ? TB * C::ROWE : 0;
     static constexpr int n_yr = TB * C::ROWE;                   // [v | 1] rows
     static constexpr int n_stage = TB * C::ROWD;                // dV staging (alias of rows | brow)
     static_assert(n_stage <= n_rows + n_brow, "staging must fit the feature tiles");
@@ -1205,7 +1237,8 @@ struct BwdKLds {
     static constexpr int o_sc = o_cols;
     static constexpr int o_zt = o_ms + n_ms;
     static constexpr int o_zr = o_zt + n_zt;
-    static constexpr int o_yr = o_zr + n_zr;
+    static constexpr int o_zlo = o_zr + n_zr;
+    static constexpr int o_yr = o_zlo + n_zlo;
     static constexpr int n_elem = o_yr + n_yr;
     static constexpr int OCC = 1;
     static_assert(n_elem * (int)sizeof(elem) * OCC <= 160 * 1024, "LDS budget");
@@ -1225,6 +1258,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C>::OCC)) void k_bwd_k(PassArgs a) {
     elem* s_sc = lds + LD::o_sc;
     elem* s_zr = lds + LD::o_zr;
     elem* s_yr = lds + LD::o_yr;
+    elem* s_zlo = lds + LD::o_zlo;
     elem* s_stage = lds + LD::o_rows;   // alias after the feature-block loop
 
     const int lane = threadIdx.x & 63, ln = lane & 15, g = lane >> 4;
@@ -1237,6 +1271,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C>::OCC)) void k_bwd_k(PassArgs a) {
     const elem* WTp = reinterpret_cast<const elem*>(a.WTp);
     constexpr bool causal = CAUSAL;
     zero_pads<C>(s_ZT, s_zr, s_yr);
+    if (LD::ZLO) zero_pads<C>(s_ZT, s_zlo, nullptr);
     zero_sketch_pads<C>(s_ms);
     __syncthreads();   // the padding is written by all waves, read by each
 
@@ -1288,7 +1323,9 @@ __global__ __launch_bounds__(NT, (BwdKLds<C>::OCC)) void k_bwd_k(PassArgs a) {
         const float zd = n_d, ze = n_e, inv_a = n_inv;
         if (it + 1 < nsub) issue(it + 1);
 
-        if (causal) write_aug<C>(zr, tok ? rcp_(zd) : 0.f, tok ? ze : 0.f, s_ZT, s_zr);
+        const bool first = t0 == 0;   // the sub-block that starts the sequence
+        if (causal)
+            write_aug<C>(zr, tok ? rcp_(zd) : 0.f, tok ? ze : 0.f, s_ZT, s_zr, (LD::ZLO && first) ? s_zlo : nullptr);
         // y rows = [v | 1]
         {
             float v[16];
@@ -1300,7 +1337,8 @@ __global__ __launch_bounds__(NT, (BwdKLds<C>::OCC)) void k_bwd_k(PassArgs a) {
         }
         __syncthreads();
         frag Cf[2];
-        if (causal) intra_operand<C, true, false>(s_zr, s_yr, nullptr, w, ln, g, my, nv, Cf);
+        if (causal)
+            intra_operand<C, true, false, LD::ZLO>(s_zr, s_zlo, s_yr, nullptr, first, w, ln, g, my, nv, Cf);
         // where the intra scores of the previous sub-block reached into the
         // sketch rows, their padding is cleared again
         if constexpr (LD::n_sc > LD::n_cols) zero_sketch_pads<C>(s_ms);
