@@ -187,6 +187,30 @@ def test_saved_states_roundtrip(lib):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_first_token_sees_only_itself(lib, dtype):
+    # Causal: the first query of a sequence attends to its own key alone, so
+    # its output is its value exactly and its query gradient is zero (the
+    # output does not depend on q_0). Both cancel only if the forward
+    # normalises by the same rounded scores it reads out with, and the
+    # backward forms g.v + e to float32 precision.
+    import torch
+    x = host_inputs(41, 1, 2, 300, 64, 4, 16, dtype)
+    dev = torch.device("cuda:0")
+    T = {k: to_torch(v, dev) for k, v in x.items()}
+    saved = lib.alloc_saved(1, 2, 300, 4, 16, True, 128, dev)
+    O = lib.forward(T["Q"], T["K"], T["V"], T["W"], 4, 16, 1.0, True, 128, saved=saved)
+    dQ, dK, dV = lib.backward(T["Q"], T["K"], T["V"], T["W"], T["dO"], 4, 16, 1.0, True, 128, O=O, saved=saved)
+    torch.cuda.synchronize()
+    print(f"[first-token] {dtype} max|O_0 - v_0| {float((O[:, :, 0] - T['V'][:, :, 0]).abs().max()):.3e} "
+          f"max|dQ_0| / max|dQ| {float(dQ[:, :, 0].float().abs().max() / dQ.float().abs().max()):.3e}", flush=True)
+    if dtype == "bf16":
+        assert torch.equal(O[:, :, 0], T["V"][:, :, 0])
+    else:
+        assert float((O[:, :, 0] - T["V"][:, :, 0]).abs().max()) <= 1e-6 * float(T["V"][:, :, 0].abs().max())
+    assert float(dQ[:, :, 0].float().abs().max()) <= 1e-3 * float(dQ.float().abs().max())
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("P,L", [(1, 7), (2, 8), (3, 5), (4, 16), (4, 32)])
 def test_hard_hash_bit_exact(lib, dtype, P, L):
     import torch
