@@ -35,12 +35,15 @@ def per_token_head_counts(w):
     writes dQ, dK, dV. FLOPs: forward 4 d L P (two projections) + 2 U (one
     sketch-sized contraction to read out, one to write), backward 8 d L P + 4 U,
     with U = 2 L R (d + 1).
-    Per kernel (its own inputs and outputs, each touched once):
-      pass_fwd   : Q, K, V in, O out;            4dLP + 2U
-      pass_bwd_q : Q, K, V, dO in, dQ out;       6dLP + U   (projections, dA_Q, back-projection)
-      pass_bwd_k : Q, K, V, dO in, dK, dV out;   6dLP + 3U  (projections, T, dV, dA_K, back-projection)
-      totals_kv  : K, V in;                      2dLP + U
-      totals_qg  : Q, dO in;                     2dLP + U
+    Per kernel: the layer tensors it reads or writes (each once; the stored
+    plane values, O, D, e and the chunk states are implementation overhead)
+    and its own contractions:
+      totals_kv  : K, V in;                    2dLP (projection) + U
+      pass_fwd   : Q, V in, O out;             2dLP (projection) + 2U
+      pass_bwd_q : Q, V, dO in, dQ out;        2dLP (back-projection) + 2U
+      totals_qg  : dO in;                      U
+      pass_bwd_v : dO in, dV out;              2U
+      pass_bwd_k : K, V, dO in, dK out;        2dLP (back-projection) + 2U
     """
     es = 2 if w.dtype == "bf16" else 4
     row = w.d * es
@@ -49,11 +52,12 @@ def per_token_head_counts(w):
     dLP = w.d * w.L * w.P
     layer = {"bytes": 4 * row + 7 * row, "flops": (4 * dLP + 2 * U) + (8 * dLP + 4 * U)}
     kernels = {
-        "pass_fwd": (4 * row, 4 * dLP + 2 * U),
-        "pass_bwd_q": (5 * row, 6 * dLP + U),
-        "pass_bwd_k": (6 * row, 6 * dLP + 3 * U),
         "totals_kv": (2 * row, 2 * dLP + U),
-        "totals_qg": (2 * row, 2 * dLP + U),
+        "pass_fwd": (3 * row, 2 * dLP + 2 * U),
+        "pass_bwd_q": (4 * row, 2 * dLP + 2 * U),
+        "totals_qg": (1 * row, U),
+        "pass_bwd_v": (2 * row, 2 * U),
+        "pass_bwd_k": (4 * row, 2 * dLP + 2 * U),
     }
     return layer, kernels
 

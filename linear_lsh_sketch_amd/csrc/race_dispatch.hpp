@@ -94,9 +94,15 @@ race_status_t run_pass(const Shape& s, const Derived& d, PassArgs a, hipStream_t
         if (s.causal) hipLaunchKernelGGL((k_bwd_q<Blk2Cfg<C>, true>), grid, block, 0, st, a);
         else hipLaunchKernelGGL((k_bwd_q<Blk2Cfg<C>, false>), grid, block, 0, st, a);
     } else {
+        // key side: dV and dK in two passes of two workgroups per CU each
+        using CK = Blk2Cfg<C>;
+        profile_mark("pass_bwd_v", st);
+        if (s.causal) hipLaunchKernelGGL((k_bwd_k<CK, true, KPART_DV>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_bwd_k<CK, false, KPART_DV>), grid, block, 0, st, a);
+        RACE_TRY(launch_ok());
         profile_mark("pass_bwd_k", st);
-        if (s.causal) hipLaunchKernelGGL((k_bwd_k<C, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_bwd_k<C, false>), grid, block, 0, st, a);
+        if (s.causal) hipLaunchKernelGGL((k_bwd_k<CK, true, KPART_DK>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_bwd_k<CK, false, KPART_DK>), grid, block, 0, st, a);
     }
     return launch_ok();
 }

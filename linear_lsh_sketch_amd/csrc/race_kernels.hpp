@@ -301,7 +301,7 @@ __device__ inline void store_state(float* __restrict__ st, int w, int ln, int g,
 // Sketch update for feature block fb from the transposed b-side features
 // (cols) and the transposed value tile: value columns of wave w, then the
 // mass accumulators of the chunk wave w owns in this block.
-template <class C>
+template <class C, bool MASS = true>
 __device__ inline void sketch_update(int fb, int w, int ln, int g, const typename Prec<C::F32>::elem* cols,
                                      const typename Prec<C::F32>::elem* ZT, f32x4 Macc[C::NKC * 2],
                                      f32x4 Zacc[C::NOWN * 2]) {
@@ -320,7 +320,7 @@ __device__ inline void sketch_update(int fb, int w, int ln, int g, const typenam
         }
     }
     const int kw = w - C::own_base(fb);        // local chunk whose mass this wave owns
-    if (kw >= 0 && kw < C::FBK) {
+    if (MASS && kw >= 0 && kw < C::FBK) {
         frag zm[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) zm[s] = ld_frag<C::F32>(ZT + (64 + ln) * C::ROWT + 32 * s + 8 * g);
@@ -1206,49 +1206,56 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// key-side backward, one pass over the feature blocks (sub-blocks in reverse):
+// key-side backward (sub-blocks in reverse), against the reverse sketch
+// T = sum_b phi_b^T [dO_b / D_b | e_b] of the queries after the sub-block:
 //   dV_a  = phi_a^T T_g  (+ intra: sum_{b >= a} <phi_b, phi_a> g_b)
 //   dA_K  = T [v_a | 1]  (+ intra: phi_b^T Cc, Cc[b][a] = g_b . v_a + e_b)
-// with T = sum_{b} phi_b^T [dO_b / D_b | e_b] over the queries after the
-// sub-block (the reverse sketch); then the chain rule -> dK.
+// then the chain rule -> dK. PART selects dV (KPART_DV), dK (KPART_DK) or
+// both in one sweep (KPART_BOTH); the split passes each fit two workgroups
+// per CU.
 // ---------------------------------------------------------------------------
-template <class C>
+enum { KPART_BOTH = 0, KPART_DV = 1, KPART_DK = 2 };
+
+template <class C, int PART>
 struct BwdKLds {
     using elem = typename Prec<C::F32>::elem;
-    static constexpr int n_rows = TB * C::ROWF;                 // key features [64][ROWF]
-    static constexpr int n_brow = TB * C::ROWF;                 // query features [64][ROWF]
+    static constexpr bool DV = PART != KPART_DK;
+    static constexpr bool DK = PART != KPART_DV;
+    static constexpr int n_rows = DV ? TB * C::ROWF : 0;        // key features [64][ROWF]
+    static constexpr int n_brow = DV ? TB * C::ROWF : 0;        // query features [64][ROWF]
     static constexpr int n_cols = C::FBK * 32 * C::ROWT;        // query features transposed
-    static constexpr int n_ms = C::FBK * 32 * C::ROWE;          // sketch rows
+    static constexpr int n_ms = DK ? C::FBK * 32 * C::ROWE : 0; // sketch rows
     static constexpr int n_zt = ZR * C::ROWT;                   // [g | e] transposed
-    static constexpr int n_sc = TB * C::ROWT;                   // intra scores [a][b] (alias of cols | ms)
-    static constexpr int n_zr = TB * C::ROWE;                   // [g | e] rows
+    static constexpr int n_sc = DV ? TB * C::ROWT : 0;          // intra scores [a][b] (alias of cols | ms)
+    static constexpr int n_zr = DK ? TB * C::ROWE : 0;          // [g | e] rows
     // bf16 residual of the [g | e] rows: the intra-sub-block product g.v + e
     // cancels for a query against its only key
-    static constexpr bool ZLO = !C::F32;
+    static constexpr bool ZLO = DK && !C::F32;
     static constexpr int n_zlo = ZLO ? TB * C::ROWE : 0;
-    static constexpr int n_yr = TB * C::ROWE;                   // [v | 1] rows
-    static constexpr int n_stage = TB * C::ROWD;                // dV staging (alias of rows | brow)
+    static constexpr int n_yr = DK ? TB * C::ROWE : 0;          // [v | 1] rows
+    static constexpr int n_stage = DV ? TB * C::ROWD : 0;       // dV staging (alias of rows | brow)
     static_assert(n_stage <= n_rows + n_brow, "staging must fit the feature tiles");
-    static_assert(n_sc <= n_cols + n_ms, "intra scores must fit the sketch tiles");
+    static constexpr bool SC_SHARED = n_sc <= n_cols + n_ms;   // else a tile of its own
     static constexpr int o_rows = 0;
     static constexpr int o_brow = o_rows + n_rows;
     static constexpr int o_cols = o_brow + n_brow;
     static constexpr int o_ms = o_cols + n_cols;
-    static constexpr int o_sc = o_cols;
     static constexpr int o_zt = o_ms + n_ms;
     static constexpr int o_zr = o_zt + n_zt;
     static constexpr int o_zlo = o_zr + n_zr;
     static constexpr int o_yr = o_zlo + n_zlo;
-    static constexpr int n_elem = o_yr + n_yr;
-    static constexpr int OCC = 1;
+    static constexpr int o_sc = SC_SHARED ? o_cols : o_yr + n_yr;
+    static constexpr int n_elem = o_yr + n_yr + (SC_SHARED ? 0 : n_sc);
+    static constexpr int OCC = (PART != KPART_BOTH && !C::F32 && C::NKC <= 8) ? 2 : 1;
     static_assert(n_elem * (int)sizeof(elem) * OCC <= 160 * 1024, "LDS budget");
 };
 
-template <class C, bool CAUSAL>
-__global__ __launch_bounds__(NT, (BwdKLds<C>::OCC)) void k_bwd_k(PassArgs a) {
+template <class C, bool CAUSAL, int PART>
+__global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs a) {
     using elem = typename Prec<C::F32>::elem;
     using frag = typename Prec<C::F32>::frag;
-    using LD = BwdKLds<C>;
+    using LD = BwdKLds<C, PART>;
+    constexpr bool DV = LD::DV, DK = LD::DK;
     __shared__ __attribute__((aligned(32))) elem lds[LD::n_elem];
     elem* s_rows = lds + LD::o_rows;
     elem* s_brow = lds + LD::o_brow;
@@ -1270,9 +1277,9 @@ __global__ __launch_bounds__(NT, (BwdKLds<C>::OCC)) void k_bwd_k(PassArgs a) {
     const size_t base = (size_t)bh * a.N;
     const elem* WTp = reinterpret_cast<const elem*>(a.WTp);
     constexpr bool causal = CAUSAL;
-    zero_pads<C>(s_ZT, s_zr, s_yr);
+    zero_pads<C>(s_ZT, DK ? s_zr : nullptr, DK ? s_yr : nullptr);
     if (LD::ZLO) zero_pads<C>(s_ZT, s_zlo, nullptr);
-    zero_sketch_pads<C>(s_ms);
+    if (DK) zero_sketch_pads<C>(s_ms);
     __syncthreads();   // the padding is written by all waves, read by each
 
     f32x4 Macc[C::NKC * 2], Zacc[C::NOWN * 2];
@@ -1281,7 +1288,9 @@ __global__ __launch_bounds__(NT, (BwdKLds<C>::OCC)) void k_bwd_k(PassArgs a) {
     const int nsub = (int)((seg1 - seg0 + TB - 1) / TB);
     const int my = 16 * w + ln;
 
-    // global loads are issued one sub-block (plane values: one feature block) ahead
+    // global loads are issued one sub-block (plane values: one feature block)
+    // ahead; in the split passes the rows at the top of their sub-block
+    constexpr bool PREFETCH = LD::OCC == 1;
     frag n_z[2], n_y[2];
     float n_d = 1.f, n_e = 0.f, n_inv = 1.f;
     Planes<C> pa, pb;
@@ -1294,7 +1303,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C>::OCC)) void k_bwd_k(PassArgs a) {
         const int64_t t0 = t0_of(it2);
         const int nv = nv_of(it2);
         const bool ok = tr < nv;
-        if (my < nv) n_inv = a.ca.inv[base + t0 + my];
+        if (DK && my < nv) n_inv = a.ca.inv[base + t0 + my];
         if (causal) {
             load_q16_raw<C::F32>(a.Zsrc, (base + t0 + tr) * DH + 16 * tq, ok, n_z);
             if (ok) {
@@ -1302,15 +1311,15 @@ __global__ __launch_bounds__(NT, (BwdKLds<C>::OCC)) void k_bwd_k(PassArgs a) {
                 n_e = a.Ev[base + t0 + tr];
             }
         }
-        load_q16_raw<C::F32>(a.Ysrc, (base + t0 + tr) * DH + 16 * tq, ok, n_y);
+        if (DK) load_q16_raw<C::F32>(a.Ysrc, (base + t0 + tr) * DH + 16 * tq, ok, n_y);
     };
     auto issue_planes = [&](int it2, int fb2) {
         const size_t r2 = base + t0_of(it2) + my;
         const bool v2 = my < nv_of(it2);
-        load_planes<C, true>(a.ca, r2, v2, fb2, g, pa);
+        load_planes<C, DK>(a.ca, r2, v2, fb2, g, pa);
         if (causal) load_planes<C, false>(a.cb, r2, v2, fb2, g, pb);
     };
-    issue(0);
+    if (PREFETCH) issue(0);
     issue_planes(0, 0);
 
     for (int it = 0; it < nsub; ++it) {
@@ -1319,15 +1328,17 @@ __global__ __launch_bounds__(NT, (BwdKLds<C>::OCC)) void k_bwd_k(PassArgs a) {
         const bool valid = my < nv;
         const size_t row = base + t0 + my;
         const bool tok = tr < nv;
+        if (!PREFETCH) issue(it);
         frag zr[2] = {n_z[0], n_z[1]}, yr[2] = {n_y[0], n_y[1]};
         const float zd = n_d, ze = n_e, inv_a = n_inv;
-        if (it + 1 < nsub) issue(it + 1);
+        if (PREFETCH && it + 1 < nsub) issue(it + 1);
 
         const bool first = t0 == 0;   // the sub-block that starts the sequence
         if (causal)
-            write_aug<C>(zr, tok ? rcp_(zd) : 0.f, tok ? ze : 0.f, s_ZT, s_zr, (LD::ZLO && first) ? s_zlo : nullptr);
-        // y rows = [v | 1]
-        {
+            write_aug<C>(zr, tok ? rcp_(zd) : 0.f, tok ? ze : 0.f, s_ZT, DK ? s_zr : nullptr,
+                         (LD::ZLO && first) ? s_zlo : nullptr);
+        if constexpr (DK) {
+            // y rows = [v | 1]
             float v[16];
 #pragma unroll
             for (int cc = 0; cc < 16; ++cc) v[cc] = q16_at<C::F32>(yr, cc);
@@ -1337,11 +1348,11 @@ __global__ __launch_bounds__(NT, (BwdKLds<C>::OCC)) void k_bwd_k(PassArgs a) {
         }
         __syncthreads();
         frag Cf[2];
-        if (causal)
+        if (DK && causal)
             intra_operand<C, true, false, LD::ZLO>(s_zr, s_zlo, s_yr, nullptr, first, w, ln, g, my, nv, Cf);
         // where the intra scores of the previous sub-block reached into the
         // sketch rows, their padding is cleared again
-        if constexpr (LD::n_sc > LD::n_cols) zero_sketch_pads<C>(s_ms);
+        if constexpr (DK && LD::SC_SHARED && LD::n_sc > LD::n_cols) zero_sketch_pads<C>(s_ms);
         f32x4 Y[4], Sc[4], dX[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1353,88 +1364,103 @@ __global__ __launch_bounds__(NT, (BwdKLds<C>::OCC)) void k_bwd_k(PassArgs a) {
 #pragma unroll
         for (int fb = 0; fb < C::NBLK; ++fb) {
             frag phiA[C::FBK], unused[C::FBK];
-            float sA[C::TPB][4], guA[C::TPB][4], us[C::TPB][4], ug[C::TPB][4];
+            float us[C::TPB][4], ug[C::TPB][4];
             const Planes<C> ka = pa, qb = pb;
             if (fb + 1 < C::NBLK) issue_planes(it, fb + 1);
             else if (it + 1 < nsub) issue_planes(it + 1, 0);
-            block_features_cached<C, true>(ka, fb, w, ln, g, valid, a.L, s_rows, nullptr, phiA, sA, guA);
-            if (causal) block_features_cached<C, false>(qb, fb, w, ln, g, valid, a.L, s_brow, s_cols, unused, us, ug);
-            write_sketch_rows<C>(fb, w, ln, g, Macc, Zacc, 0.f, s_ms);
+            if constexpr (DV) {
+                block_features_cached<C, true>(ka, fb, w, ln, g, valid, a.L, s_rows, nullptr, phiA, us, ug);
+                if (causal)
+                    block_features_cached<C, false>(qb, fb, w, ln, g, valid, a.L, s_brow, s_cols, unused, us, ug);
+            } else if (causal) {
+                block_features_cached<C, false>(qb, fb, w, ln, g, valid, a.L, nullptr, s_cols, unused, us, ug);
+            }
+            if constexpr (DK) write_sketch_rows<C>(fb, w, ln, g, Macc, Zacc, 0.f, s_ms);
             __syncthreads();
+            if constexpr (DV) {
+                if (causal) {
+#pragma unroll
+                    for (int bt = 0; bt < 4; ++bt) {
+                        if (bt >= w) {
+#pragma unroll
+                            for (int kcl = 0; kcl < C::FBK; ++kcl)
+                                Sc[bt] = mma(ld_frag<C::F32>(s_brow + (16 * bt + ln) * C::ROWF + 32 * kcl + 8 * g),
+                                             phiA[kcl], Sc[bt]);
+                        }
+                    }
+                }
+                // dV readout of the value columns of this wave (before this block's update)
+#pragma unroll
+                for (int kcl = 0; kcl < C::FBK; ++kcl) {
+                    const int kc = fb * C::FBK + kcl;
+                    const frag mf = pack<C::F32>(Macc[2 * kc], Macc[2 * kc + 1]);
+#pragma unroll
+                    for (int at = 0; at < 4; ++at)
+                        Y[at] = mma(ld_frag<C::F32>(s_rows + (16 * at + ln) * C::ROWF + 32 * kcl + 8 * g), mf, Y[at]);
+                }
+            }
+            if constexpr (DK) {
+                frag yf[3];
+#pragma unroll
+                for (int s = 0; s < 3; ++s) yf[s] = ld_frag<C::F32>(s_yr + my * C::ROWE + 32 * s + 8 * g);
+                f32x4 G[C::FBK * 2];
+                block_grad<C>(ln, g, s_ms, yf, s_cols, Cf, causal, G);
+#pragma unroll
+                for (int tb = 0; tb < C::TPB; ++tb) {
+                    const int t = fb * C::TPB + tb;
+                    float phi[C::KB * 8], dA[C::KB * 8], sg[4], gu[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        sg[i] = ka.s[tb][i];
+                        gu[i] = ka.gu[tb][i];
+                    }
+                    features_from_planes<C>(t, g, sg, a.L, valid, phi);
+#pragma unroll
+                    for (int kb = 0; kb < C::KB; ++kb) {
+                        const int kcl = tb * C::KB + kb;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            dA[kb * 8 + i] = G[2 * kcl][i];
+                            dA[kb * 8 + 4 + i] = G[2 * kcl + 1][i];
+                        }
+                    }
+                    chain_backproject<C>(t, lane, phi, dA, sg, gu, WTp, dhp, dX);
+                }
+            }
+            if (causal) sketch_update<C, DK>(fb, w, ln, g, s_cols, s_ZT, Macc, Zacc);
+            __syncthreads();
+        }
+        if constexpr (DV) {
+            // intra-sub-block dV: queries b >= a
             if (causal) {
 #pragma unroll
                 for (int bt = 0; bt < 4; ++bt) {
-                    if (bt >= w) {
-#pragma unroll
-                        for (int kcl = 0; kcl < C::FBK; ++kcl)
-                            Sc[bt] = mma(ld_frag<C::F32>(s_brow + (16 * bt + ln) * C::ROWF + 32 * kcl + 8 * g),
-                                         phiA[kcl], Sc[bt]);
-                    }
-                }
-            }
-            // dV readout of the value columns of this wave (before this block's update)
-#pragma unroll
-            for (int kcl = 0; kcl < C::FBK; ++kcl) {
-                const int kc = fb * C::FBK + kcl;
-                const frag mf = pack<C::F32>(Macc[2 * kc], Macc[2 * kc + 1]);
-#pragma unroll
-                for (int at = 0; at < 4; ++at)
-                    Y[at] = mma(ld_frag<C::F32>(s_rows + (16 * at + ln) * C::ROWF + 32 * kcl + 8 * g), mf, Y[at]);
-            }
-            frag yf[3];
-#pragma unroll
-            for (int s = 0; s < 3; ++s) yf[s] = ld_frag<C::F32>(s_yr + my * C::ROWE + 32 * s + 8 * g);
-            f32x4 G[C::FBK * 2];
-            block_grad<C>(ln, g, s_ms, yf, s_cols, Cf, causal, G);
-#pragma unroll
-            for (int tb = 0; tb < C::TPB; ++tb) {
-                const int t = fb * C::TPB + tb;
-                float phi[C::KB * 8], dA[C::KB * 8];
-#pragma unroll
-                for (int kb = 0; kb < C::KB; ++kb) {
-                    const int kcl = tb * C::KB + kb;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) phi[kb * 8 + j] = elem_f<C::F32>(phiA[kcl][j]);
+                    f32x4 v;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        dA[kb * 8 + i] = G[2 * kcl][i];
-                        dA[kb * 8 + 4 + i] = G[2 * kcl + 1][i];
+                        const int b = 16 * bt + 4 * g + i;
+                        v[i] = (b >= my && b < nv) ? Sc[bt][i] : 0.f;
                     }
+                    st_half<C::F32>(s_sc + my * C::ROWT + 16 * bt + 4 * g, v);
                 }
-                chain_backproject<C>(t, lane, phi, dA, sA[tb], guA[tb], WTp, dhp, dX);
-            }
-            if (causal) sketch_update<C>(fb, w, ln, g, s_cols, s_ZT, Macc, Zacc);
-            __syncthreads();
-        }
-        // intra-sub-block dV: queries b >= a
-        if (causal) {
+                __syncthreads();
 #pragma unroll
-            for (int bt = 0; bt < 4; ++bt) {
-                f32x4 v;
+                for (int s = 0; s < 2; ++s) {
+                    const frag zt = ld_frag<C::F32>(s_ZT + (16 * w + ln) * C::ROWT + 32 * s + 8 * g);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int b = 16 * bt + 4 * g + i;
-                    v[i] = (b >= my && b < nv) ? Sc[bt][i] : 0.f;
+                    for (int at = 0; at < 4; ++at)
+                        Y[at] = mma(ld_frag<C::F32>(s_sc + (16 * at + ln) * C::ROWT + 32 * s + 8 * g), zt, Y[at]);
                 }
-                st_half<C::F32>(s_sc + my * C::ROWT + 16 * bt + 4 * g, v);
             }
+#pragma unroll
+            for (int at = 0; at < 4; ++at)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    s_stage[(16 * at + 4 * g + i) * C::ROWD + 16 * w + ln] = to_elem<C::F32>(Y[at][i]);
             __syncthreads();
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const frag zt = ld_frag<C::F32>(s_ZT + (16 * w + ln) * C::ROWT + 32 * s + 8 * g);
-#pragma unroll
-                for (int at = 0; at < 4; ++at)
-                    Y[at] = mma(ld_frag<C::F32>(s_sc + (16 * at + ln) * C::ROWT + 32 * s + 8 * g), zt, Y[at]);
-            }
+            store_stage<C>(a.out1, base + t0, tr, tq, tok, s_stage);
         }
-#pragma unroll
-        for (int at = 0; at < 4; ++at)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                s_stage[(16 * at + 4 * g + i) * C::ROWD + 16 * w + ln] = to_elem<C::F32>(Y[at][i]);
-        __syncthreads();
-        store_stage<C>(a.out1, base + t0, tr, tq, tok, s_stage);
-        store_dx<C>(a.Xa, a.out0, row, valid, g, inv_a, dX);
+        if constexpr (DK) store_dx<C>(a.Xa, a.out0, row, valid, g, inv_a, dX);
     }
 }
 
