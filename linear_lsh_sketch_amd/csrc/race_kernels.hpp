@@ -646,10 +646,10 @@ __device__ inline void write_sketch_rows(int fb, int w, int ln, int g, const f32
     }
 }
 
-// Zero the padding columns 65..95 of the sketch rows.
+// Zero the padding columns 65..95 of `nbuf` consecutive sketch-row tiles.
 template <class C>
-__device__ inline void zero_sketch_pads(typename Prec<C::F32>::elem* s_ms) {
-    for (int idx = threadIdx.x; idx < C::FBK * 32 * 31; idx += NT)
+__device__ inline void zero_sketch_pads(typename Prec<C::F32>::elem* s_ms, int nbuf = 1) {
+    for (int idx = threadIdx.x; idx < nbuf * C::FBK * 32 * 31; idx += NT)
         s_ms[(idx / 31) * C::ROWE + 65 + idx % 31] = to_elem<C::F32>(0.f);
 }
 
@@ -1042,13 +1042,21 @@ struct BwdQLds {
     static constexpr int n_zr = TB * C::ROWE;                   // [v | 1] rows
     static constexpr int n_yr = TB * C::ROWE;                   // y rows (hi)
     static constexpr int n_ylo = YLO ? TB * C::ROWE : 0;        // y rows (lo)
+    // The per-block tiles (sketch rows, key features) are double-buffered:
+    // block fb uses buffer fb % 2, so one barrier per block separates writes
+    // from reads. The z rows (read before the block loop) share the second
+    // sketch-row buffer and the y lo rows (first sub-block of a sequence only)
+    // the feature buffers, where they fit.
+    static constexpr bool ZR_SHARED = n_zr <= n_ms;
+    static constexpr bool YLO_SHARED = n_ylo <= 2 * n_cols;
     static constexpr int o_ms = 0;
-    static constexpr int o_cols = o_ms + n_ms;
-    static constexpr int o_zt = o_cols + n_cols;
-    static constexpr int o_zr = o_zt + n_zt;
-    static constexpr int o_yr = o_zr + n_zr;
-    static constexpr int o_ylo = o_yr + n_yr;
-    static constexpr int n_elem = o_ylo + n_ylo;
+    static constexpr int o_cols = o_ms + 2 * n_ms;
+    static constexpr int o_zt = o_cols + 2 * n_cols;
+    static constexpr int o_yr = o_zt + n_zt;
+    static constexpr int o_end = o_yr + n_yr;
+    static constexpr int o_zr = ZR_SHARED ? o_ms + n_ms : o_end;
+    static constexpr int o_ylo = YLO_SHARED ? o_cols : o_end + (ZR_SHARED ? 0 : n_zr);
+    static constexpr int n_elem = o_end + (ZR_SHARED ? 0 : n_zr) + (YLO_SHARED ? 0 : n_ylo);
     static constexpr int OCC = (!C::F32 && C::NKC <= 8) ? 2 : 1;
     static_assert(n_elem * (int)sizeof(elem) * OCC <= 160 * 1024, "LDS budget");
 };
@@ -1075,9 +1083,9 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
     const size_t base = (size_t)bh * a.N;
     const elem* WTp = reinterpret_cast<const elem*>(a.WTp);
     constexpr bool causal = CAUSAL;
+    zero_sketch_pads<C>(s_ms, 2);
     zero_pads<C>(s_ZT, s_zr, s_yr);
     if (LD::YLO) zero_pads<C>(s_ZT, s_ylo, nullptr);
-    zero_sketch_pads<C>(s_ms);
     __syncthreads();   // the padding is written by all waves, read by each
 
     f32x4 Macc[C::NKC * 2], Zacc[C::NOWN * 2];
@@ -1152,6 +1160,8 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
         frag Cf[2];
         if (causal)
             intra_operand<C, false, LD::YLO, false>(s_zr, nullptr, s_yr, s_ylo, first, w, ln, g, my, nv, Cf);
+        if (LD::YLO && LD::YLO_SHARED && causal && first)
+            __syncthreads();   // the y lo rows are read; their space becomes the feature tiles
         f32x4 dX[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) dX[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1165,18 +1175,20 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
             const Planes<C> qa = pa, kb_ = pb;
             if (fb + 1 < C::NBLK) issue_planes(it, fb + 1);
             else if (it + 1 < nsub) issue_planes(it + 1, 0);
-            write_sketch_rows<C>(fb, w, ln, g, Macc, Zacc, zshift, s_ms);
+            elem* ms_b = s_ms + (fb & 1) * LD::n_ms;
+            elem* cols_b = s_cols + (fb & 1) * LD::n_cols;
+            write_sketch_rows<C>(fb, w, ln, g, Macc, Zacc, zshift, ms_b);
             if (causal) {
                 frag unused[C::FBK];
                 float us[C::TPB][4], ug[C::TPB][4];
-                block_features_cached<C, false>(kb_, fb, w, ln, g, valid, a.L, nullptr, s_cols, unused, us, ug);
+                block_features_cached<C, false>(kb_, fb, w, ln, g, valid, a.L, nullptr, cols_b, unused, us, ug);
             }
             __syncthreads();
             frag yf[3];
 #pragma unroll
             for (int s = 0; s < 3; ++s) yf[s] = ld_frag<C::F32>(s_yr + my * C::ROWE + 32 * s + 8 * g);
             f32x4 G[C::FBK * 2];
-            block_grad<C>(ln, g, s_ms, yf, s_cols, Cf, causal, G);
+            block_grad<C>(ln, g, ms_b, yf, cols_b, Cf, causal, G);
 #pragma unroll
             for (int tb = 0; tb < C::TPB; ++tb) {
                 const int t = fb * C::TPB + tb;
@@ -1198,9 +1210,9 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
                 }
                 chain_backproject<C>(t, lane, phi, dA, sg, gu, WTp, dhp, dX);
             }
-            if (causal) sketch_update<C>(fb, w, ln, g, s_cols, s_ZT, Macc, Zacc);
-            __syncthreads();
+            if (causal) sketch_update<C>(fb, w, ln, g, cols_b, s_ZT, Macc, Zacc);
         }
+        __syncthreads();   // the next sub-block rewrites ZT, the y and z rows
         store_dx<C>(a.Xa, a.out0, row, valid, g, inv_a, dX);
     }
 }
