@@ -1226,39 +1226,55 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
 // both in one sweep (KPART_BOTH); the split passes each fit two workgroups
 // per CU.
 // ---------------------------------------------------------------------------
-enum { KPART_BOTH = 0, KPART_DV = 1, KPART_DK = 2 };
+enum { KPART_DV = 1, KPART_DK = 2 };
 
 template <class C, int PART>
 struct BwdKLds {
     using elem = typename Prec<C::F32>::elem;
-    static constexpr bool DV = PART != KPART_DK;
-    static constexpr bool DK = PART != KPART_DV;
+    static constexpr bool DV = PART == KPART_DV;
+    static constexpr bool DK = PART == KPART_DK;
+    // per-block tiles; the dV pass double-buffers them (block fb uses buffer
+    // fb % 2, so one barrier per block separates writes from reads), the dK
+    // pass (register-bound) keeps one buffer and two barriers per block
+    static constexpr int NB = DV ? 2 : 1;
     static constexpr int n_rows = DV ? TB * C::ROWF : 0;        // key features [64][ROWF]
     static constexpr int n_brow = DV ? TB * C::ROWF : 0;        // query features [64][ROWF]
     static constexpr int n_cols = C::FBK * 32 * C::ROWT;        // query features transposed
     static constexpr int n_ms = DK ? C::FBK * 32 * C::ROWE : 0; // sketch rows
+    // per-sub-block tiles
     static constexpr int n_zt = ZR * C::ROWT;                   // [g | e] transposed
-    static constexpr int n_sc = DV ? TB * C::ROWT : 0;          // intra scores [a][b] (alias of cols | ms)
+    static constexpr int n_sc = DV ? TB * C::ROWT : 0;          // intra scores [a][b]
+    static constexpr int n_stage = DV ? TB * C::ROWD : 0;       // dV staging
     static constexpr int n_zr = DK ? TB * C::ROWE : 0;          // [g | e] rows
     // bf16 residual of the [g | e] rows: the intra-sub-block product g.v + e
     // cancels for a query against its only key
     static constexpr bool ZLO = DK && !C::F32;
     static constexpr int n_zlo = ZLO ? TB * C::ROWE : 0;
     static constexpr int n_yr = DK ? TB * C::ROWE : 0;          // [v | 1] rows
-    static constexpr int n_stage = DV ? TB * C::ROWD : 0;       // dV staging (alias of rows | brow)
-    static_assert(n_stage <= n_rows + n_brow, "staging must fit the feature tiles");
-    static constexpr bool SC_SHARED = n_sc <= n_cols + n_ms;   // else a tile of its own
-    static constexpr int o_rows = 0;
+    // Tiles live outside the block loop share the block buffers where they
+    // fit: the intra scores and the residual rows the feature buffers, the
+    // staging the row-feature buffers, the z rows the second sketch-row buffer.
+    static constexpr bool SC_SHARED = n_sc <= NB * n_cols;
+    static constexpr bool STAGE_SHARED = n_stage <= NB * (n_rows + n_brow);
+    static constexpr bool ZLO_SHARED = NB == 2 && n_zlo <= 2 * n_cols;
+    static constexpr bool ZR_SHARED = NB == 2 && n_zr <= n_ms;
+    static constexpr int o_rows = 0;                            // [NB][rows | brow]
     static constexpr int o_brow = o_rows + n_rows;
-    static constexpr int o_cols = o_brow + n_brow;
-    static constexpr int o_ms = o_cols + n_cols;
-    static constexpr int o_zt = o_ms + n_ms;
-    static constexpr int o_zr = o_zt + n_zt;
-    static constexpr int o_zlo = o_zr + n_zr;
-    static constexpr int o_yr = o_zlo + n_zlo;
-    static constexpr int o_sc = SC_SHARED ? o_cols : o_yr + n_yr;
-    static constexpr int n_elem = o_yr + n_yr + (SC_SHARED ? 0 : n_sc);
-    static constexpr int OCC = (PART != KPART_BOTH && !C::F32 && C::NKC <= 8) ? 2 : 1;
+    static constexpr int RB = n_rows + n_brow;                  // stride of the row-feature buffers
+    static constexpr int o_cols = NB * RB;                      // [NB][cols]
+    static constexpr int o_ms = o_cols + NB * n_cols;           // [NB][ms]
+    static constexpr int o_zt = o_ms + NB * n_ms;
+    static constexpr int o_yr = o_zt + n_zt;
+    static constexpr int o_x0 = o_yr + n_yr;                    // unshared tiles follow
+    static constexpr int o_sc = SC_SHARED ? o_cols : o_x0;
+    static constexpr int o_x1 = o_x0 + (SC_SHARED ? 0 : n_sc);
+    static constexpr int o_stage = STAGE_SHARED ? o_rows : o_x1;
+    static constexpr int o_x2 = o_x1 + (STAGE_SHARED ? 0 : n_stage);
+    static constexpr int o_zlo = ZLO_SHARED ? o_cols : o_x2;
+    static constexpr int o_x3 = o_x2 + (ZLO_SHARED ? 0 : n_zlo);
+    static constexpr int o_zr = ZR_SHARED ? o_ms + n_ms : o_x3;
+    static constexpr int n_elem = o_x3 + (ZR_SHARED ? 0 : n_zr);
+    static constexpr int OCC = (!C::F32 && C::NKC <= 8) ? 2 : 1;
     static_assert(n_elem * (int)sizeof(elem) * OCC <= 160 * 1024, "LDS budget");
 };
 
@@ -1278,7 +1294,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
     elem* s_zr = lds + LD::o_zr;
     elem* s_yr = lds + LD::o_yr;
     elem* s_zlo = lds + LD::o_zlo;
-    elem* s_stage = lds + LD::o_rows;   // alias after the feature-block loop
+    elem* s_stage = lds + LD::o_stage;
 
     const int lane = threadIdx.x & 63, ln = lane & 15, g = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1289,9 +1305,9 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
     const size_t base = (size_t)bh * a.N;
     const elem* WTp = reinterpret_cast<const elem*>(a.WTp);
     constexpr bool causal = CAUSAL;
+    if (DK) zero_sketch_pads<C>(s_ms, LD::NB);
     zero_pads<C>(s_ZT, DK ? s_zr : nullptr, DK ? s_yr : nullptr);
     if (LD::ZLO) zero_pads<C>(s_ZT, s_zlo, nullptr);
-    if (DK) zero_sketch_pads<C>(s_ms);
     __syncthreads();   // the padding is written by all waves, read by each
 
     f32x4 Macc[C::NKC * 2], Zacc[C::NOWN * 2];
@@ -1362,9 +1378,8 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
         frag Cf[2];
         if (DK && causal)
             intra_operand<C, true, false, LD::ZLO>(s_zr, s_zlo, s_yr, nullptr, first, w, ln, g, my, nv, Cf);
-        // where the intra scores of the previous sub-block reached into the
-        // sketch rows, their padding is cleared again
-        if constexpr (DK && LD::SC_SHARED && LD::n_sc > LD::n_cols) zero_sketch_pads<C>(s_ms);
+        if (LD::ZLO && LD::ZLO_SHARED && causal && first)
+            __syncthreads();   // the residual rows are read; their space becomes the feature tiles
         f32x4 Y[4], Sc[4], dX[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1380,14 +1395,19 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
             const Planes<C> ka = pa, qb = pb;
             if (fb + 1 < C::NBLK) issue_planes(it, fb + 1);
             else if (it + 1 < nsub) issue_planes(it + 1, 0);
+            const int bsel = LD::NB == 2 ? (fb & 1) : 0;
+            elem* rows_b = s_rows + bsel * LD::RB;
+            elem* brow_b = s_brow + bsel * LD::RB;
+            elem* cols_b = s_cols + bsel * LD::n_cols;
+            elem* ms_b = s_ms + bsel * LD::n_ms;
             if constexpr (DV) {
-                block_features_cached<C, true>(ka, fb, w, ln, g, valid, a.L, s_rows, nullptr, phiA, us, ug);
+                block_features_cached<C, true>(ka, fb, w, ln, g, valid, a.L, rows_b, nullptr, phiA, us, ug);
                 if (causal)
-                    block_features_cached<C, false>(qb, fb, w, ln, g, valid, a.L, s_brow, s_cols, unused, us, ug);
+                    block_features_cached<C, false>(qb, fb, w, ln, g, valid, a.L, brow_b, cols_b, unused, us, ug);
             } else if (causal) {
-                block_features_cached<C, false>(qb, fb, w, ln, g, valid, a.L, nullptr, s_cols, unused, us, ug);
+                block_features_cached<C, false>(qb, fb, w, ln, g, valid, a.L, nullptr, cols_b, unused, us, ug);
             }
-            if constexpr (DK) write_sketch_rows<C>(fb, w, ln, g, Macc, Zacc, 0.f, s_ms);
+            if constexpr (DK) write_sketch_rows<C>(fb, w, ln, g, Macc, Zacc, 0.f, ms_b);
             __syncthreads();
             if constexpr (DV) {
                 if (causal) {
@@ -1396,7 +1416,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
                         if (bt >= w) {
 #pragma unroll
                             for (int kcl = 0; kcl < C::FBK; ++kcl)
-                                Sc[bt] = mma(ld_frag<C::F32>(s_brow + (16 * bt + ln) * C::ROWF + 32 * kcl + 8 * g),
+                                Sc[bt] = mma(ld_frag<C::F32>(brow_b + (16 * bt + ln) * C::ROWF + 32 * kcl + 8 * g),
                                              phiA[kcl], Sc[bt]);
                         }
                     }
@@ -1408,7 +1428,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
                     const frag mf = pack<C::F32>(Macc[2 * kc], Macc[2 * kc + 1]);
 #pragma unroll
                     for (int at = 0; at < 4; ++at)
-                        Y[at] = mma(ld_frag<C::F32>(s_rows + (16 * at + ln) * C::ROWF + 32 * kcl + 8 * g), mf, Y[at]);
+                        Y[at] = mma(ld_frag<C::F32>(rows_b + (16 * at + ln) * C::ROWF + 32 * kcl + 8 * g), mf, Y[at]);
                 }
             }
             if constexpr (DK) {
@@ -1416,7 +1436,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
 #pragma unroll
                 for (int s = 0; s < 3; ++s) yf[s] = ld_frag<C::F32>(s_yr + my * C::ROWE + 32 * s + 8 * g);
                 f32x4 G[C::FBK * 2];
-                block_grad<C>(ln, g, s_ms, yf, s_cols, Cf, causal, G);
+                block_grad<C>(ln, g, ms_b, yf, cols_b, Cf, causal, G);
 #pragma unroll
                 for (int tb = 0; tb < C::TPB; ++tb) {
                     const int t = fb * C::TPB + tb;
@@ -1439,9 +1459,10 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
                     chain_backproject<C>(t, lane, phi, dA, sg, gu, WTp, dhp, dX);
                 }
             }
-            if (causal) sketch_update<C, DK>(fb, w, ln, g, s_cols, s_ZT, Macc, Zacc);
-            __syncthreads();
+            if (causal) sketch_update<C, DK>(fb, w, ln, g, cols_b, s_ZT, Macc, Zacc);
+            if (LD::NB == 1) __syncthreads();   // single buffer: reads done before the next block's writes
         }
+        if (LD::NB == 2) __syncthreads();   // the block tiles are read; the sub-block tiles below reuse them
         if constexpr (DV) {
             // intra-sub-block dV: queries b >= a
             if (causal) {
