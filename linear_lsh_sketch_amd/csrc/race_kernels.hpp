@@ -595,46 +595,40 @@ struct PassArgs {
     int causal;
 };
 
+// Corner mean of the sketch value column this lane holds. Every key adds a
+// unit of mass per valid table, so all valid tables of a column sum to the
+// same value (the column sum of the values in the sketch): the mean is taken
+// once, from the lane's table of the first projection tile (if that table is
+// padding, so are all the lane's tables, and it gives 0).
+template <class C>
+__device__ inline float sketch_column_mean(const f32x4 Macc[C::NKC * 2]) {
+    constexpr int RR = (C::P == 4) ? 16 : C::R;
+    float m = 0.f;
+#pragma unroll
+    for (int r = 0; r < RR; ++r) m += Macc[r >> 2][r & 3];
+    return m * (1.f / (float)RR);
+}
+
 // Sketch rows of feature block fb for the gradient contraction dA = M y:
 // [FBK*32][ROWE], value columns of wave w and the mass column (64) from the
 // wave that owns it. Only dA - <a, dA> per table is used downstream, so a
-// per-table constant may be removed: the corner mean of every value column is
-// subtracted in float32 and the mass column is shifted by `zshift`, and the
-// bf16 operand then carries the part that survives instead of a large common
-// offset. A lane holds every corner of its tables for its value column.
+// per-table constant may be removed: the corner mean `mcol` of the value
+// column is subtracted in float32 and the mass column is shifted by `zshift`,
+// and the bf16 operand then carries the part that survives instead of a large
+// common offset.
 template <class C>
 __device__ inline void write_sketch_rows(int fb, int w, int ln, int g, const f32x4 Macc[C::NKC * 2],
-                                         const f32x4 Zacc[C::NOWN * 2], float zshift,
+                                         const f32x4 Zacc[C::NOWN * 2], float mcol, float zshift,
                                          typename Prec<C::F32>::elem* s_ms) {
 #pragma unroll
-    for (int tb = 0; tb < C::TPB; ++tb) {
-        float v[C::KB * 8];
+    for (int kcl = 0; kcl < C::FBK; ++kcl)
 #pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) v[kb * 8 + 4 * h + i] = Macc[2 * (fb * C::FBK + tb * C::KB + kb) + h][i];
-        constexpr int RR = (C::P == 4) ? 16 : C::R;
-#pragma unroll
-        for (int t0c = 0; t0c < C::KB * 8; t0c += RR) {
-            float m = 0.f;
-#pragma unroll
-            for (int r = 0; r < RR; ++r) m += v[t0c + r];
-            m *= 1.f / (float)RR;
-#pragma unroll
-            for (int r = 0; r < RR; ++r) v[t0c + r] -= m;
-        }
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int fl = 32 * (tb * C::KB + kb) + 8 * g + 4 * h + i;
-                    s_ms[fl * C::ROWE + 16 * w + ln] = to_elem<C::F32>(v[kb * 8 + 4 * h + i]);
-                }
-    }
+            for (int i = 0; i < 4; ++i) {
+                const int fl = 32 * kcl + 8 * g + 4 * h + i;
+                s_ms[fl * C::ROWE + 16 * w + ln] = to_elem<C::F32>(Macc[2 * (fb * C::FBK + kcl) + h][i] - mcol);
+            }
     const int kw = w - C::own_base(fb);
     if (kw >= 0 && kw < C::FBK && ln == 0) {
 #pragma unroll
@@ -1170,6 +1164,7 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
         // mass of a corner is that count / R plus a fluctuation: store the
         // fluctuation (a per-table constant cancels in the chain rule).
         const float zshift = (causal ? (float)t0 : (float)a.N) / (float)C::R;
+        const float mcol = sketch_column_mean<C>(Macc);   // before this sub-block's updates
 #pragma unroll
         for (int fb = 0; fb < C::NBLK; ++fb) {
             const Planes<C> qa = pa, kb_ = pb;
@@ -1177,7 +1172,7 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
             else if (it + 1 < nsub) issue_planes(it + 1, 0);
             elem* ms_b = s_ms + (fb & 1) * LD::n_ms;
             elem* cols_b = s_cols + (fb & 1) * LD::n_cols;
-            write_sketch_rows<C>(fb, w, ln, g, Macc, Zacc, zshift, ms_b);
+            write_sketch_rows<C>(fb, w, ln, g, Macc, Zacc, mcol, zshift, ms_b);
             if (causal) {
                 frag unused[C::FBK];
                 float us[C::TPB][4], ug[C::TPB][4];
@@ -1388,6 +1383,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
             dX[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         f32x4 dhp[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        const float mcol = DK ? sketch_column_mean<C>(Macc) : 0.f;   // before this sub-block's updates
 #pragma unroll
         for (int fb = 0; fb < C::NBLK; ++fb) {
             frag phiA[C::FBK], unused[C::FBK];
@@ -1407,7 +1403,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
             } else if (causal) {
                 block_features_cached<C, false>(qb, fb, w, ln, g, valid, a.L, nullptr, cols_b, unused, us, ug);
             }
-            if constexpr (DK) write_sketch_rows<C>(fb, w, ln, g, Macc, Zacc, 0.f, ms_b);
+            if constexpr (DK) write_sketch_rows<C>(fb, w, ln, g, Macc, Zacc, mcol, 0.f, ms_b);
             __syncthreads();
             if constexpr (DV) {
                 if (causal) {
