@@ -94,9 +94,9 @@ race_status_t race_attn_workspace_bytes(int64_t B, int64_t H, int64_t N, int d, 
  * (causal) or the whole-sequence sketch (non-causal); the float32 per-token
  * softmax denominators D_i = sum_l sum_r a_l(q_i)[r] z_l[r] (the quantity
  * the output divides by); and, for queries and for keys, each token's
- * per-plane values sigmoid(2 beta u) and 2 beta (1 - u^2), u = tanh of the
- * normalised projection, with 1 / max(|x|, 1e-12), all float32, so that
- * the backward rebuilds the soft assignments without projecting again.
+ * per-plane u = tanh of the normalised projection (float16 for RACE_BF16,
+ * float32 for RACE_F32) with 1 / max(|x|, 1e-12) in float32, so that the
+ * backward rebuilds the soft assignments without projecting again.
  * Layout is private to the library. */
 race_status_t race_attn_saved_bytes(int64_t B, int64_t H, int64_t N, int d, int P, int L,
                                     int causal, int chunk, size_t *bytes);

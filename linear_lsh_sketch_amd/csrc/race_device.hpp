@@ -38,6 +38,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // precision policy
@@ -45,11 +46,16 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 template <bool F32>
 struct Prec;
 
+// ucache / uvec: how the per-plane soft values u = tanh(h) are kept between
+// passes (float16 for bf16 inputs: |u| <= 1, so the rounding error is below
+// 2.5e-4, far under the bf16 operand rounding; float32 otherwise).
 template <>
 struct Prec<false> {
     using elem = __bf16;
     using frag = bf16x8;
     using half = bf16x4;
+    using ucache = _Float16;
+    using uvec = f16x4;
     static constexpr int PAD = 8;  // 16 bytes
 };
 
@@ -58,6 +64,8 @@ struct Prec<true> {
     using elem = float;
     using frag = f32x8;
     using half = f32x4;
+    using ucache = float;
+    using uvec = f32x4;
     static constexpr int PAD = 8;  // 32 bytes
 };
 
@@ -232,21 +240,9 @@ __device__ inline void row_table(int t, int ri, int& table, int& plane) {
     plane = i % C::Pp;
 }
 
-// Soft bucket features of one lane for projection tile t.
-// hs[i] = normalised projection of rows 4g+i (P' planes per table, TPL tables
-// per lane); writes phi[KB*8] (canonical order within the lane's chunks),
-// u[i] = tanh(hs[i]), s[i] = sigmoid(2 beta u[i]) (the probability that the
-// corner bit of plane i is set) and gu[i] = 2 beta (1 - u[i]^2).
-// The corner softmax of beta <c_r, u> factorises over planes into
-// prod_p sigmoid(2 beta c_rp u_p). With x = 2 beta u and F = e^{-|x|} <= 1,
-// sigmoid(x) = n1 / (1 + F) and sigmoid(-x) = n0 / (1 + F) where {n1, n0} =
-// {1, F} for x >= 0 and {F, 1} otherwise, so every corner is a product of
-// numerators in (0, 1] times one reciprocal per table. `keep` = false (an
-// absent token) gives phi = 0.
-template <class C>
-__device__ inline void soft_features(int t, int g, const float hs[4], float beta, int L, bool keep,
-                                     float phi[C::KB * 8], float u[4], float s[4], float gu[4]) {
-    // u = tanh(hs): tanh|x| = (1 - E) / (1 + E), E = e^{-2|x|}
+// u = tanh(hs) for the four rows a lane holds: tanh|x| = (1 - E) / (1 + E)
+// with E = e^{-2|x|} (no overflow, accurate near 0), one shared reciprocal.
+__device__ inline void tanh4(const float hs[4], float u[4]) {
     float e[4], q[4], rq[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -254,42 +250,41 @@ __device__ inline void soft_features(int t, int g, const float hs[4], float beta
         q[i] = 1.f + e[i];
     }
     rcp4(q, rq);
-    float n1[4], n0[4], qf[4], rf[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = copysignf((1.f - e[i]) * rq[i], hs[i]);
+}
+
+// The stored form of four u values, and back. Every pass derives the soft
+// assignment of a token from the stored form, so all passes see the same
+// features bit for bit.
+template <bool F32>
+__device__ inline typename Prec<F32>::uvec round_u(const float u[4]) {
+    typename Prec<F32>::uvec v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (typename Prec<F32>::ucache)u[i];
+    return v;
+}
+
+// Per-plane values of one lane's four rows from the stored u: the corner-bit
+// probability s = sigmoid(2 beta u) (the corner softmax of beta <c_r, u>
+// factorises over planes into prod_p sigmoid(2 beta c_rp u_p)) and
+// gu = 2 beta (1 - u^2) = d(2 beta u)/dh. With x = 2 beta u and
+// F = e^{-|x|} <= 1, sigmoid(x) = n1 / (1 + F), n1 = 1 for x >= 0 else F, so
+// the four reciprocals share one (arguments in [1, 2]).
+template <bool F32>
+__device__ inline void planes_from_u(const typename Prec<F32>::uvec& uv, float beta, float s[4], float gu[4]) {
+    float F[4], qf[4], rf[4], u[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        u[i] = copysignf((1.f - e[i]) * rq[i], hs[i]);
-        gu[i] = 2.f * beta * (1.f - u[i] * u[i]);
-        const float x = 2.f * beta * u[i];
-        const float F = exp2_(-LOG2E * fabsf(x));
-        n1[i] = x >= 0.f ? 1.f : F;
-        n0[i] = x >= 0.f ? F : 1.f;
-        qf[i] = 1.f + F;
+        u[i] = (float)uv[i];
+        F[i] = exp2_(-2.f * beta * LOG2E * fabsf(u[i]));
+        qf[i] = 1.f + F[i];
     }
     rcp4(qf, rf);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = n1[i] * rf[i];
-    if constexpr (C::P == 4) {
-        const bool ok = keep && (t * C::TPT + g) < L;
-        // 1 / prod_p (1 + F_p) = rf[0] rf[1] rf[2] rf[3]
-        const float R = ok ? (rf[0] * rf[1]) * (rf[2] * rf[3]) : 0.f;
-        const float a1 = n1[0] * R, a0 = n0[0] * R;
-        const float lo[4] = {a0 * n0[1], a1 * n0[1], a0 * n1[1], a1 * n1[1]};
-        const float hi[4] = {n0[2] * n0[3], n1[2] * n0[3], n0[2] * n1[3], n1[2] * n1[3]};
-#pragma unroll
-        for (int r = 0; r < 16; ++r) phi[r] = lo[r & 3] * hi[r >> 2];
-    } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int tl = j / C::R, r = j % C::R;
-            const bool ok = keep && (t * C::TPT + g * C::TPL + tl) < L;
-            float v = ok ? 1.f : 0.f;
-#pragma unroll
-            for (int p = 0; p < C::P; ++p) {
-                const int i = tl * C::Pp + p;
-                v *= (((r >> p) & 1) ? n1[i] : n0[i]) * rf[i];
-            }
-            phi[j] = v;
-        }
+    for (int i = 0; i < 4; ++i) {
+        s[i] = (u[i] >= 0.f ? 1.f : F[i]) * rf[i];
+        gu[i] = 2.f * beta * (1.f - u[i] * u[i]);
     }
 }
 

@@ -59,8 +59,7 @@ race_status_t run_totals(const Shape& s, const Derived& d, const void* Xb, const
 inline PlaneCache plane_cache(void* base, const CacheLayout& cl) {
     char* b = reinterpret_cast<char*>(base);
     PlaneCache p;
-    p.sig = reinterpret_cast<float*>(b + cl.sig);
-    p.gu = reinterpret_cast<float*>(b + cl.gu);
+    p.u = b + cl.u;
     p.inv = reinterpret_cast<float*>(b + cl.inv);
     return p;
 }

@@ -36,10 +36,11 @@ struct WsLayout {
     size_t total;
 };
 
-// Plane values of one side (queries or keys), float32: sigmoid(2 beta u)
-// [rows][NPL], 2 beta (1 - u^2) [rows][NPL], 1 / max(|x|, eps) [rows].
+// Plane values of one side (queries or keys): u = tanh of the normalised
+// projection [rows][NPL] (float16 for bf16 inputs, float32 for float32; sized
+// for float32, the upper bound), then 1 / max(|x|, eps) [rows] in float32.
 struct CacheLayout {
-    size_t sig, gu, inv, total;
+    size_t u, inv, total;
 };
 
 // The saved buffer: float32 sketch states (per chunk, causal; the total,
@@ -93,9 +94,8 @@ inline race_status_t derive(const Shape& s, Derived& d) {
 inline CacheLayout cache_layout(const Shape& s, const Derived& d) {
     const size_t rows = (size_t)d.BH * (size_t)s.N;
     CacheLayout c;
-    c.sig = 0;
-    c.gu = align256(rows * (size_t)d.NPL * sizeof(float));
-    c.inv = c.gu + align256(rows * (size_t)d.NPL * sizeof(float));
+    c.u = 0;
+    c.inv = align256(rows * (size_t)d.NPL * sizeof(float));
     c.total = c.inv + align256(rows * sizeof(float));
     return c;
 }

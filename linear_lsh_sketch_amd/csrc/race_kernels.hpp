@@ -169,29 +169,29 @@ struct WSrc {
 
 // Per-token plane values of one side (queries or keys), written by the pass
 // that projects the rows and read by the later passes instead of projecting
-// again: s = sigmoid(2 beta u) and gu = 2 beta (1 - u^2) for every projection
-// row (tile-row order, NPL per token), and 1 / max(|x|, eps) per token, all
-// float32 (gu scales the gradient directly: no rounding to bf16).
+// again: u = tanh(h) for every projection row (tile-row order, NPL per
+// token) in Prec::ucache, and 1 / max(|x|, eps) per token in float32.
 struct PlaneCache {
-    float* sig;   // [rows][NPL]
-    float* gu;    // [rows][NPL]
+    void* u;      // [rows][NPL] of Prec::ucache
     float* inv;   // [rows]
 };
 
-// The plane values of the own token for the tiles of one feature block.
+// The stored u of the own token for the tiles of one feature block.
 template <class C>
 struct Planes {
-    f32x4 s[C::TPB];
-    f32x4 gu[C::TPB];
+    typename Prec<C::F32>::uvec u[C::TPB];
 };
 
-template <class C, bool GU>
+template <class C>
 __device__ inline void load_planes(const PlaneCache& pc, size_t row, bool valid, int fb, int g, Planes<C>& p) {
+    using U = typename Prec<C::F32>::uvec;
+    const typename Prec<C::F32>::ucache* base = reinterpret_cast<const typename Prec<C::F32>::ucache*>(pc.u);
 #pragma unroll
     for (int tb = 0; tb < C::TPB; ++tb) {
         const size_t off = row * C::NPL + 16 * (fb * C::TPB + tb) + 4 * g;
-        p.s[tb] = valid ? *reinterpret_cast<const f32x4*>(pc.sig + off) : f32x4{0.f, 0.f, 0.f, 0.f};
-        if constexpr (GU) p.gu[tb] = valid ? *reinterpret_cast<const f32x4*>(pc.gu + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+        U v = {};
+        if (valid) v = *reinterpret_cast<const U*>(base + off);
+        p.u[tb] = v;
     }
 }
 
@@ -369,14 +369,17 @@ __device__ inline void block_features(const WSrc<C>& wsrc, int fb, int lane, int
     for (int tb = 0; tb < C::TPB; ++tb) {
         const int t = fb * C::TPB + tb;
         const f32x4 acc = wsrc.project(t, lane, ln, g, xf);
-        float hs[4], phi[C::KB * 8], u[4], sg[4], gu[4];
+        float hs[4], u[4], phi[C::KB * 8], sg[4], gu[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) hs[i] = acc[i] * inv;
-        soft_features<C>(t, g, hs, beta, L, valid, phi, u, sg, gu);
+        tanh4(hs, u);
+        const typename Prec<C::F32>::uvec uq = round_u<C::F32>(u);
+        planes_from_u<C::F32>(uq, beta, sg, gu);
+        features_from_planes<C>(t, g, sg, L, valid, phi);
         if (out && valid) {
             const size_t off = row * C::NPL + 16 * t + 4 * g;
-            *reinterpret_cast<f32x4*>(out->sig + off) = f32x4{sg[0], sg[1], sg[2], sg[3]};
-            *reinterpret_cast<f32x4*>(out->gu + off) = f32x4{gu[0], gu[1], gu[2], gu[3]};
+            *reinterpret_cast<typename Prec<C::F32>::uvec*>(reinterpret_cast<typename Prec<C::F32>::ucache*>(out->u) +
+                                                            off) = uq;
         }
         emit_tile<C, KEEP>(tb, w, ln, g, phi, rows, cols, phi_frag);
     }
@@ -386,21 +389,21 @@ __device__ inline void block_features(const WSrc<C>& wsrc, int fb, int lane, int
 // per tile the plane probabilities s and 2 beta (1 - u^2) for the chain rule.
 template <class C, bool KEEP>
 __device__ inline void block_features_cached(const Planes<C>& pl, int fb, int w, int ln, int g, bool valid, int L,
-                                             typename Prec<C::F32>::elem* rows,
+                                             float beta, typename Prec<C::F32>::elem* rows,
                                              typename Prec<C::F32>::elem* cols,
                                              typename Prec<C::F32>::frag (&phi_frag)[C::FBK],
                                              float (&s_keep)[C::TPB][4], float (&gu_keep)[C::TPB][4]) {
 #pragma unroll
     for (int tb = 0; tb < C::TPB; ++tb) {
         const int t = fb * C::TPB + tb;
-        const float sg[4] = {pl.s[tb][0], pl.s[tb][1], pl.s[tb][2], pl.s[tb][3]};
-        float phi[C::KB * 8];
+        float sg[4], gu[4], phi[C::KB * 8];
+        planes_from_u<C::F32>(pl.u[tb], beta, sg, gu);
         features_from_planes<C>(t, g, sg, L, valid, phi);
         if constexpr (KEEP) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 s_keep[tb][i] = sg[i];
-                gu_keep[tb][i] = pl.gu[tb][i];
+                gu_keep[tb][i] = gu[i];
             }
         }
         emit_tile<C, KEEP>(tb, w, ln, g, phi, rows, cols, phi_frag);
@@ -463,7 +466,7 @@ __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
     zero_pads<C>(s_ZT, nullptr, nullptr);
     __syncthreads();   // W' and the padding are written by all waves, read by each
     const WSrc<C> wsrc{s_w, reinterpret_cast<const elem*>(a.W), a.L};
-    const PlaneCache* pc_out = (!CACHED && a.pc.sig) ? &a.pc : nullptr;
+    const PlaneCache* pc_out = (!CACHED && a.pc.u) ? &a.pc : nullptr;
 
     f32x4 Macc[C::NKC * 2], Zacc[C::NOWN * 2];
 #pragma unroll
@@ -491,7 +494,7 @@ __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
         }
     };
     auto issue_planes = [&](int it2, int fb2) {
-        load_planes<C, false>(a.pc, base + seg0 + (int64_t)it2 * TB + my, my < nv_of(it2), fb2, g, pn);
+        load_planes<C>(a.pc, base + seg0 + (int64_t)it2 * TB + my, my < nv_of(it2), fb2, g, pn);
     };
     issue(0);
     if (CACHED) issue_planes(0, 0);
@@ -519,7 +522,7 @@ __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
                 if (fb + 1 < C::NBLK) issue_planes(it, fb + 1);
                 else if (it + 1 < nsub) issue_planes(it + 1, 0);
                 float us[C::TPB][4], ug[C::TPB][4];
-                block_features_cached<C, false>(pl, fb, w, ln, g, valid, a.L, nullptr, s_cols, unused, us, ug);
+                block_features_cached<C, false>(pl, fb, w, ln, g, valid, a.L, a.beta, nullptr, s_cols, unused, us, ug);
             } else {
                 block_features<C, false>(wsrc, fb, lane, w, ln, g, xf, inv, valid, a.beta, a.L, nullptr, s_cols,
                                          unused, pc_out, row);
@@ -574,7 +577,7 @@ __global__ __launch_bounds__(256) void k_scan(float* __restrict__ st, float* __r
 // ---------------------------------------------------------------------------
 struct PassArgs {
     const void* Xa;        // readout-side rows (FWD, BWD_Q: Q; BWD_K: K)
-    PlaneCache ca;         // readout side's plane values: FWD stores them (if ca.sig), BWD_Q / BWD_K read them
+    PlaneCache ca;         // readout side's plane values: FWD stores them (if ca.u), BWD_Q / BWD_K read them
     PlaneCache cb;         // sketch side's plane values (read)
     const void* Zsrc;      // FWD, BWD_Q: V; BWD_K: dO
     const void* Ysrc;      // BWD_Q: dO; BWD_K: V
@@ -870,7 +873,7 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
     zero_pads<C>(s_ZT, nullptr, nullptr);
     __syncthreads();   // W' and the padding are written by all waves, read by each
     const WSrc<C> wsrc{s_w, W, a.L};
-    const PlaneCache* pc_out = a.ca.sig ? &a.ca : nullptr;   // the queries' plane values for the backward
+    const PlaneCache* pc_out = a.ca.u ? &a.ca : nullptr;   // the queries' plane values for the backward
 
     f32x4 Macc[C::NKC * 2], Zacc[C::NOWN * 2];
     load_state<C>(a.state + bh * a.state_bh_stride + c * a.state_chunk_stride, w, ln, g, Macc, Zacc);
@@ -892,7 +895,7 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
         load_q16_raw<C::F32>(a.Zsrc, (base + t0 + tr) * DH + 16 * tq, tr < nv, n_z);
     };
     auto issue_planes = [&](int it2, int fb2) {
-        load_planes<C, false>(a.cb, base + seg0 + (int64_t)it2 * TB + my, my < nv_of(it2), fb2, g, pn);
+        load_planes<C>(a.cb, base + seg0 + (int64_t)it2 * TB + my, my < nv_of(it2), fb2, g, pn);
     };
     issue(0);
     issue_planes(0, 0);
@@ -927,7 +930,7 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
             block_features<C, true>(wsrc, fb, lane, w, ln, g, xa, inv_a, valid, a.beta, a.L, s_rows, nullptr, phiA,
                                     pc_out, row);
             float us[C::TPB][4], ug[C::TPB][4];
-            block_features_cached<C, false>(pl, fb, w, ln, g, valid, a.L, s_brow, causal ? s_cols : nullptr, unused,
+            block_features_cached<C, false>(pl, fb, w, ln, g, valid, a.L, a.beta, s_brow, causal ? s_cols : nullptr, unused,
                                             us, ug);
             __syncthreads();
             if (causal) {
@@ -1099,8 +1102,8 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
     auto issue_planes = [&](int it2, int fb2) {
         const size_t r2 = base + seg0 + (int64_t)it2 * TB + my;
         const bool v2 = my < nv_of(it2);
-        load_planes<C, true>(a.ca, r2, v2, fb2, g, pa);
-        if (causal) load_planes<C, false>(a.cb, r2, v2, fb2, g, pb);
+        load_planes<C>(a.ca, r2, v2, fb2, g, pa);
+        if (causal) load_planes<C>(a.cb, r2, v2, fb2, g, pb);
     };
     issue_planes(0, 0);
 
@@ -1176,7 +1179,7 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
             if (causal) {
                 frag unused[C::FBK];
                 float us[C::TPB][4], ug[C::TPB][4];
-                block_features_cached<C, false>(kb_, fb, w, ln, g, valid, a.L, nullptr, cols_b, unused, us, ug);
+                block_features_cached<C, false>(kb_, fb, w, ln, g, valid, a.L, a.beta, nullptr, cols_b, unused, us, ug);
             }
             __syncthreads();
             frag yf[3];
@@ -1188,11 +1191,7 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
             for (int tb = 0; tb < C::TPB; ++tb) {
                 const int t = fb * C::TPB + tb;
                 float phi[C::KB * 8], sg[4], gu[4], dA[C::KB * 8];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    sg[i] = qa.s[tb][i];
-                    gu[i] = qa.gu[tb][i];
-                }
+                planes_from_u<C::F32>(qa.u[tb], a.beta, sg, gu);
                 features_from_planes<C>(t, g, sg, a.L, valid, phi);
 #pragma unroll
                 for (int kb = 0; kb < C::KB; ++kb) {
@@ -1339,8 +1338,8 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
     auto issue_planes = [&](int it2, int fb2) {
         const size_t r2 = base + t0_of(it2) + my;
         const bool v2 = my < nv_of(it2);
-        load_planes<C, DK>(a.ca, r2, v2, fb2, g, pa);
-        if (causal) load_planes<C, false>(a.cb, r2, v2, fb2, g, pb);
+        load_planes<C>(a.ca, r2, v2, fb2, g, pa);
+        if (causal) load_planes<C>(a.cb, r2, v2, fb2, g, pb);
     };
     if (PREFETCH) issue(0);
     issue_planes(0, 0);
@@ -1397,11 +1396,11 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
             elem* cols_b = s_cols + bsel * LD::n_cols;
             elem* ms_b = s_ms + bsel * LD::n_ms;
             if constexpr (DV) {
-                block_features_cached<C, true>(ka, fb, w, ln, g, valid, a.L, rows_b, nullptr, phiA, us, ug);
+                block_features_cached<C, true>(ka, fb, w, ln, g, valid, a.L, a.beta, rows_b, nullptr, phiA, us, ug);
                 if (causal)
-                    block_features_cached<C, false>(qb, fb, w, ln, g, valid, a.L, brow_b, cols_b, unused, us, ug);
+                    block_features_cached<C, false>(qb, fb, w, ln, g, valid, a.L, a.beta, brow_b, cols_b, unused, us, ug);
             } else if (causal) {
-                block_features_cached<C, false>(qb, fb, w, ln, g, valid, a.L, nullptr, cols_b, unused, us, ug);
+                block_features_cached<C, false>(qb, fb, w, ln, g, valid, a.L, a.beta, nullptr, cols_b, unused, us, ug);
             }
             if constexpr (DK) write_sketch_rows<C>(fb, w, ln, g, Macc, Zacc, mcol, 0.f, ms_b);
             __syncthreads();
@@ -1437,11 +1436,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
                 for (int tb = 0; tb < C::TPB; ++tb) {
                     const int t = fb * C::TPB + tb;
                     float phi[C::KB * 8], dA[C::KB * 8], sg[4], gu[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        sg[i] = ka.s[tb][i];
-                        gu[i] = ka.gu[tb][i];
-                    }
+                    planes_from_u<C::F32>(ka.u[tb], a.beta, sg, gu);
                     features_from_planes<C>(t, g, sg, a.L, valid, phi);
 #pragma unroll
                     for (int kb = 0; kb < C::KB; ++kb) {

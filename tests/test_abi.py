@@ -49,7 +49,7 @@ def _a256(x):
 def test_workspace_and_saved_sizes():
     # causal: per-chunk states of F * 65 floats (F = 32 * MT * KB), then one
     # float32 denominator per token, then for queries and keys the per-token
-    # plane values (16 * MT sigmoids, 16 * MT chain-rule factors, one norm)
+    # plane values (16 * MT soft values u, sized as float32, and one norm)
     N, rows = 12_000_000, 4 * 12_000_000
     fwd = race.workspace_bytes(1, 4, N, 64, 4, 16, True, 1024, race.WS_FWD)
     fwd_s = race.workspace_bytes(1, 4, N, 64, 4, 16, True, 1024, race.WS_FWD_SAVED)
@@ -58,7 +58,7 @@ def test_workspace_and_saved_sizes():
     saved = race.saved_bytes(1, 4, N, 64, 4, 16, True, 1024)
     nchunks = -(-N // 1024)
     states = 4 * nchunks * 256 * 65 * 4
-    cache = _a256(rows * 64 * 4) * 2 + _a256(rows * 4)
+    cache = _a256(rows * 64 * 4) + _a256(rows * 4)
     assert saved == _a256(states) + _a256(rows * 4) + 2 * cache
     assert fwd_s >= states and fwd >= fwd_s + cache
     # gradient states and e per token
@@ -67,7 +67,7 @@ def test_workspace_and_saved_sizes():
     assert rec >= fwd_s + bwd + saved + rows * 64 * 4
     # non-causal: the total sketch (L8 P2: MT = 1, F = 32)
     rows_nc = 6 * 100
-    cache_nc = _a256(rows_nc * 16 * 4) * 2 + _a256(rows_nc * 4)
+    cache_nc = _a256(rows_nc * 16 * 4) + _a256(rows_nc * 4)
     assert race.saved_bytes(2, 3, 100, 64, 2, 8, False, 64) == \
         _a256(6 * 32 * 65 * 4) + _a256(rows_nc * 4) + 2 * cache_nc
 
