@@ -56,7 +56,7 @@ struct Prec<false> {
     using half = bf16x4;
     using ucache = _Float16;
     using uvec = f16x4;
-    static constexpr int PAD = 8;  // 16 bytes
+    static constexpr int PAD = 16;  // 32 bytes
 };
 
 template <>
@@ -155,9 +155,12 @@ __device__ inline float elem_f(typename Prec<F32>::elem x) {
 // layout helpers
 // ---------------------------------------------------------------------------
 
-// feature (canonical f, relative to a chunk base) of accumulator row rho within
-// a pair of 16-row tiles: rho = 16 h + 4 g + i  ->  8 g + 4 h + i
-__device__ inline int canon_of_row(int h, int m) { return 8 * (m >> 2) + 4 * h + (m & 3); }
+// Tiles whose rows are features (transposed features, sketch rows) store
+// feature f = 8 g + j of a 32-feature chunk at its accumulator row
+// rho = 16 (j / 4) + 4 g + j % 4. A matrix-core operand that reads rows
+// 16 h + ln then yields, in output rows 4 g + i, the features 8 g + 4 h + i a
+// lane owns, and its 16 lanes read consecutive rows (no LDS bank conflicts).
+__device__ inline int acc_row(int g, int j) { return 16 * (j >> 2) + 4 * g + (j & 3); }
 
 // Transcendentals on the hardware units: v_exp_f32 (2^x) and v_rcp_f32, each
 // about 1 ulp; no IEEE division sequences on the hot path.

@@ -314,7 +314,7 @@ __device__ inline void sketch_update(int fb, int w, int ln, int g, const typenam
         const int kc = fb * C::FBK + kcl;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const typename Prec<C::F32>::elem* arow = cols + (32 * kcl + canon_of_row(h, ln)) * C::ROWT + 8 * g;
+            const typename Prec<C::F32>::elem* arow = cols + (32 * kcl + 16 * h + ln) * C::ROWT + 8 * g;
 #pragma unroll
             for (int s = 0; s < 2; ++s) Macc[2 * kc + h] = mma(ld_frag<C::F32>(arow + 32 * s), zt[s], Macc[2 * kc + h]);
         }
@@ -326,7 +326,7 @@ __device__ inline void sketch_update(int fb, int w, int ln, int g, const typenam
         for (int s = 0; s < 2; ++s) zm[s] = ld_frag<C::F32>(ZT + (64 + ln) * C::ROWT + 32 * s + 8 * g);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const typename Prec<C::F32>::elem* arow = cols + (32 * kw + canon_of_row(h, ln)) * C::ROWT + 8 * g;
+            const typename Prec<C::F32>::elem* arow = cols + (32 * kw + 16 * h + ln) * C::ROWT + 8 * g;
 #pragma unroll
             for (int s = 0; s < 2; ++s)
                 Zacc[2 * C::zidx(fb) + h] = mma(ld_frag<C::F32>(arow + 32 * s), zm[s], Zacc[2 * C::zidx(fb) + h]);
@@ -348,7 +348,7 @@ __device__ inline void emit_tile(int tb, int w, int ln, int g, const float phi[C
         if (rows) st_frag<C::F32>(rows + (16 * w + ln) * C::ROWF + 32 * kcl + 8 * g, fr);
         if (cols) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) cols[(32 * kcl + 8 * g + j) * C::ROWT + 16 * w + ln] = fr[j];
+            for (int j = 0; j < 8; ++j) cols[(32 * kcl + acc_row(g, j)) * C::ROWT + 16 * w + ln] = fr[j];
         }
     }
 }
@@ -629,8 +629,8 @@ __device__ inline void write_sketch_rows(int fb, int w, int ln, int g, const f32
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int fl = 32 * kcl + 8 * g + 4 * h + i;
-                s_ms[fl * C::ROWE + 16 * w + ln] = to_elem<C::F32>(Macc[2 * (fb * C::FBK + kcl) + h][i] - mcol);
+                const int rl = 32 * kcl + 16 * h + 4 * g + i;
+                s_ms[rl * C::ROWE + 16 * w + ln] = to_elem<C::F32>(Macc[2 * (fb * C::FBK + kcl) + h][i] - mcol);
             }
     const int kw = w - C::own_base(fb);
     if (kw >= 0 && kw < C::FBK && ln == 0) {
@@ -638,7 +638,7 @@ __device__ inline void write_sketch_rows(int fb, int w, int ln, int g, const f32
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                s_ms[(32 * kw + 8 * g + 4 * h + i) * C::ROWE + 64] =
+                s_ms[(32 * kw + 16 * h + 4 * g + i) * C::ROWE + 64] =
                     to_elem<C::F32>(Zacc[2 * C::zidx(fb) + h][i] - zshift);
     }
 }
@@ -661,7 +661,7 @@ __device__ inline void block_grad(int ln, int g, const typename Prec<C::F32>::el
 #pragma unroll
     for (int m = 0; m < C::FBK * 2; ++m) {
         const int kcl = m >> 1, h = m & 1;
-        const int fl = 32 * kcl + canon_of_row(h, ln);
+        const int fl = 32 * kcl + 16 * h + ln;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 3; ++s) acc = mma(ld_frag<C::F32>(s_ms + fl * C::ROWE + 32 * s + 8 * g), yf[s], acc);
