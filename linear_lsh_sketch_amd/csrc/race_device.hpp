@@ -117,25 +117,30 @@ __device__ inline typename Prec<F32>::frag ld_frag(const typename Prec<F32>::ele
     return *reinterpret_cast<const typename Prec<F32>::frag*>(p);
 }
 
-// Operand whose 8 K positions are two runs of 4 (permuted K order).
-template <bool F32>
-__device__ inline typename Prec<F32>::frag ld_frag2(const typename Prec<F32>::elem* p0,
-                                                   const typename Prec<F32>::elem* p1) {
-    using H = typename Prec<F32>::half;
-    H a = *reinterpret_cast<const H*>(p0);
-    H b = *reinterpret_cast<const H*>(p1);
-    typename Prec<F32>::frag f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f[i] = a[i];
-        f[4 + i] = b[i];
-    }
-    return f;
-}
-
 template <bool F32>
 __device__ inline void st_frag(typename Prec<F32>::elem* p, const typename Prec<F32>::frag& f) {
     *reinterpret_cast<typename Prec<F32>::frag*>(p) = f;
+}
+
+// Store element j of f at base + off[j] (8 scattered 2- or 4-byte writes);
+// bf16 elements are written from the packed register pairs (low and high
+// halves), so no value is converted twice.
+template <bool F32>
+__device__ inline void st_scatter(typename Prec<F32>::elem* base, const int (&off)[8],
+                                  const typename Prec<F32>::frag& f) {
+    if constexpr (F32) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) base[off[j]] = f[j];
+    } else {
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 w = __builtin_bit_cast(u32x4, f);
+        unsigned short* b = reinterpret_cast<unsigned short*>(base);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            b[off[2 * j]] = (unsigned short)(w[j] & 0xffffu);
+            b[off[2 * j + 1]] = (unsigned short)(w[j] >> 16);
+        }
+    }
 }
 
 template <bool F32>
@@ -161,6 +166,13 @@ __device__ inline float elem_f(typename Prec<F32>::elem x) {
 // 16 h + ln then yields, in output rows 4 g + i, the features 8 g + 4 h + i a
 // lane owns, and its 16 lanes read consecutive rows (no LDS bank conflicts).
 __device__ inline int acc_row(int g, int j) { return 16 * (j >> 2) + 4 * g + (j & 3); }
+
+// Tiles whose columns are the 64 tokens of a sub-block (transposed features,
+// transposed values, intra scores) store token b = 32 m + 16 h + 4 g + i at
+// column 32 m + 8 g + 4 h + i: the order in which two accumulator tiles of a
+// token contraction pack into one operand, so every token-contraction operand
+// is one contiguous 16-byte LDS read.
+__device__ inline int tok_pos(int b) { return (b & 32) + 8 * ((b >> 2) & 3) + 4 * ((b >> 4) & 1) + (b & 3); }
 
 // Transcendentals on the hardware units: v_exp_f32 (2^x) and v_rcp_f32, each
 // about 1 ulp; no IEEE division sequences on the hot path.

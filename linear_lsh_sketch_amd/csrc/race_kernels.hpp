@@ -208,9 +208,10 @@ __device__ inline void write_aug(const typename Prec<C::F32>::frag zr[2], float 
     float v[16];
 #pragma unroll
     for (int c = 0; c < 16; ++c) v[c] = q16_at<C::F32>(zr, c) * scale;
+    const int rp = tok_pos(r);
 #pragma unroll
-    for (int c = 0; c < 16; ++c) ZT[(16 * q + c) * C::ROWT + r] = to_elem<C::F32>(v[c]);
-    if (q == 0) ZT[64 * C::ROWT + r] = to_elem<C::F32>(mass);
+    for (int c = 0; c < 16; ++c) ZT[(16 * q + c) * C::ROWT + rp] = to_elem<C::F32>(v[c]);
+    if (q == 0) ZT[64 * C::ROWT + rp] = to_elem<C::F32>(mass);
     if (Zrow) {
         const typename Prec<C::F32>::frag h0 = pack8<C::F32>(v), h1 = pack8<C::F32>(v + 8);
         st_frag<C::F32>(Zrow + r * C::ROWE + 16 * q, h0);
@@ -347,8 +348,10 @@ __device__ inline void emit_tile(int tb, int w, int ln, int g, const float phi[C
         if constexpr (KEEP) phi_frag[kcl] = fr;
         if (rows) st_frag<C::F32>(rows + (16 * w + ln) * C::ROWF + 32 * kcl + 8 * g, fr);
         if (cols) {
+            int off[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) cols[(32 * kcl + acc_row(g, j)) * C::ROWT + 16 * w + ln] = fr[j];
+            for (int j = 0; j < 8; ++j) off[j] = (32 * kcl + acc_row(g, j)) * C::ROWT + tok_pos(16 * w + ln);
+            st_scatter<C::F32>(cols, off, fr);
         }
     }
 }
@@ -667,10 +670,8 @@ __device__ inline void block_grad(int ln, int g, const typename Prec<C::F32>::el
         for (int s = 0; s < 3; ++s) acc = mma(ld_frag<C::F32>(s_ms + fl * C::ROWE + 32 * s + 8 * g), yf[s], acc);
         if (causal) {
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                const typename Prec<C::F32>::elem* p = s_cols + fl * C::ROWT + 32 * s2 + 4 * g;
-                acc = mma(ld_frag2<C::F32>(p, p + 16), Cf[s2], acc);
-            }
+            for (int s2 = 0; s2 < 2; ++s2)
+                acc = mma(ld_frag<C::F32>(s_cols + fl * C::ROWT + 32 * s2 + 8 * g), Cf[s2], acc);
         }
         G[m] = acc;
     }
@@ -979,7 +980,7 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
                     v[i] = vis ? elem_f<C::F32>(to_elem<C::F32>(Sc[bt][i])) : 0.f;
                     dint += v[i];
                 }
-                st_half<C::F32>(s_sc + my * C::ROWT + 16 * bt + 4 * g, v);
+                st_half<C::F32>(s_sc + my * C::ROWT + tok_pos(16 * bt + 4 * g), v);
             }
             dint = sum_groups(dint);
             if (g == 0) f_Dint[my] = dint;
@@ -1465,7 +1466,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
                         const int b = 16 * bt + 4 * g + i;
                         v[i] = (b >= my && b < nv) ? Sc[bt][i] : 0.f;
                     }
-                    st_half<C::F32>(s_sc + my * C::ROWT + 16 * bt + 4 * g, v);
+                    st_half<C::F32>(s_sc + my * C::ROWT + tok_pos(16 * bt + 4 * g), v);
                 }
                 __syncthreads();
 #pragma unroll
