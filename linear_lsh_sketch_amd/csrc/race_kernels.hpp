@@ -1228,10 +1228,9 @@ struct BwdKLds {
     using elem = typename Prec<C::F32>::elem;
     static constexpr bool DV = PART == KPART_DV;
     static constexpr bool DK = PART == KPART_DK;
-    // per-block tiles; the dV pass double-buffers them (block fb uses buffer
-    // fb % 2, so one barrier per block separates writes from reads), the dK
-    // pass (register-bound) keeps one buffer and two barriers per block
-    static constexpr int NB = DV ? 2 : 1;
+    // per-block tiles, double-buffered: block fb uses buffer fb % 2, so one
+    // barrier per block separates writes from reads
+    static constexpr int NB = 2;
     static constexpr int n_rows = DV ? TB * C::ROWF : 0;        // key features [64][ROWF]
     static constexpr int n_brow = DV ? TB * C::ROWF : 0;        // query features [64][ROWF]
     static constexpr int n_cols = C::FBK * 32 * C::ROWT;        // query features transposed
