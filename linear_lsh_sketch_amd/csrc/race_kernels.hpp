@@ -299,11 +299,44 @@ __device__ inline void store_state(float* __restrict__ st, int w, int ln, int g,
     }
 }
 
-// Sketch update for feature block fb from the transposed b-side features
-// (cols) and the transposed value tile: value columns of wave w, then the
+// Matrix-core A operand of a token contraction, read from a token-row feature
+// tile rows[64][ROWF] (token b, feature 32 kcl + f of the block): lane
+// (ln, g) gets, for accumulator row 16 h + ln of feature chunk kcl (feature
+// 8 (ln / 4) + 4 h + ln % 4), the tokens at K positions 32 s + 8 g + j in
+// tok_pos order, i.e. tokens 32 s + 16 (j / 4) + 4 g + j % 4. bf16 uses two
+// LDS transpose reads (ds_read_b64_tr_b16): lane j of a 16-lane group points
+// at 4 consecutive features of one token, and the group receives the 4 x 16
+// block transposed, lane l holding element l % 4 of the lanes l / 4 + 4 i.
+template <class C>
+__device__ inline typename Prec<C::F32>::frag feat_operand(const typename Prec<C::F32>::elem* rows, int kcl, int h,
+                                                          int s, int ln, int g) {
+    typename Prec<C::F32>::frag f;
+    if constexpr (C::F32) {
+        const int fo = 32 * kcl + 8 * (ln >> 2) + 4 * h + (ln & 3);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] = rows[(32 * s + 16 * (j >> 2) + 4 * g + (j & 3)) * C::ROWF + fo];
+    } else {
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        const typename Prec<C::F32>::elem* p =
+            rows + (32 * s + 4 * g + (ln >> 2)) * C::ROWF + 32 * kcl + 8 * (ln & 3) + 4 * h;
+        const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+        const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 16 * C::ROWF));
+        const bf16x4 ab = __builtin_bit_cast(bf16x4, a), bb = __builtin_bit_cast(bf16x4, b);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[i] = ab[i];
+            f[4 + i] = bb[i];
+        }
+    }
+    return f;
+}
+
+// Sketch update for feature block fb from the b-side features (token-row tile
+// `brow`) and the transposed value tile: value columns of wave w, then the
 // mass accumulators of the chunk wave w owns in this block.
 template <class C, bool MASS = true>
-__device__ inline void sketch_update(int fb, int w, int ln, int g, const typename Prec<C::F32>::elem* cols,
+__device__ inline void sketch_update(int fb, int w, int ln, int g, const typename Prec<C::F32>::elem* brow,
                                      const typename Prec<C::F32>::elem* ZT, f32x4 Macc[C::NKC * 2],
                                      f32x4 Zacc[C::NOWN * 2]) {
     using frag = typename Prec<C::F32>::frag;
@@ -315,9 +348,9 @@ __device__ inline void sketch_update(int fb, int w, int ln, int g, const typenam
         const int kc = fb * C::FBK + kcl;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const typename Prec<C::F32>::elem* arow = cols + (32 * kcl + 16 * h + ln) * C::ROWT + 8 * g;
 #pragma unroll
-            for (int s = 0; s < 2; ++s) Macc[2 * kc + h] = mma(ld_frag<C::F32>(arow + 32 * s), zt[s], Macc[2 * kc + h]);
+            for (int s = 0; s < 2; ++s)
+                Macc[2 * kc + h] = mma(feat_operand<C>(brow, kcl, h, s, ln, g), zt[s], Macc[2 * kc + h]);
         }
     }
     const int kw = w - C::own_base(fb);        // local chunk whose mass this wave owns
@@ -327,37 +360,30 @@ __device__ inline void sketch_update(int fb, int w, int ln, int g, const typenam
         for (int s = 0; s < 2; ++s) zm[s] = ld_frag<C::F32>(ZT + (64 + ln) * C::ROWT + 32 * s + 8 * g);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const typename Prec<C::F32>::elem* arow = cols + (32 * kw + 16 * h + ln) * C::ROWT + 8 * g;
 #pragma unroll
             for (int s = 0; s < 2; ++s)
-                Zacc[2 * C::zidx(fb) + h] = mma(ld_frag<C::F32>(arow + 32 * s), zm[s], Zacc[2 * C::zidx(fb) + h]);
+                Zacc[2 * C::zidx(fb) + h] =
+                    mma(feat_operand<C>(brow, kw, h, s, ln, g), zm[s], Zacc[2 * C::zidx(fb) + h]);
         }
     }
 }
 
-// Pack the lane's features of tile tb of the block and write them to LDS (row
-// layout `rows` and/or transposed `cols`); KEEP returns the operands.
+// Pack the lane's features of tile tb of the block and write them to the
+// token-row tile `rows` (if set); KEEP returns the operands.
 template <class C, bool KEEP>
 __device__ inline void emit_tile(int tb, int w, int ln, int g, const float phi[C::KB * 8],
-                                 typename Prec<C::F32>::elem* rows, typename Prec<C::F32>::elem* cols,
-                                 typename Prec<C::F32>::frag (&phi_frag)[C::FBK]) {
+                                 typename Prec<C::F32>::elem* rows, typename Prec<C::F32>::frag (&phi_frag)[C::FBK]) {
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) {
         const int kcl = tb * C::KB + kb;
         const typename Prec<C::F32>::frag fr = pack8<C::F32>(phi + kb * 8);
         if constexpr (KEEP) phi_frag[kcl] = fr;
         if (rows) st_frag<C::F32>(rows + (16 * w + ln) * C::ROWF + 32 * kcl + 8 * g, fr);
-        if (cols) {
-            int off[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) off[j] = (32 * kcl + acc_row(g, j)) * C::ROWT + tok_pos(16 * w + ln);
-            st_scatter<C::F32>(cols, off, fr);
-        }
     }
 }
 
 // Project the own 16-token tile for the tiles of feature block fb and write
-// the features to LDS (row layout `rows` and/or transposed `cols`); when KEEP,
+// the features to the token-row tile `rows` (if set); when KEEP,
 // also return the lane's operands (one per chunk of the block) in phi_frag.
 // With `out` set, the plane values of valid tokens are stored there (row
 // `row`) for later passes.
@@ -365,7 +391,6 @@ template <class C, bool KEEP>
 __device__ inline void block_features(const WSrc<C>& wsrc, int fb, int lane, int w, int ln, int g,
                                       const typename Prec<C::F32>::frag xf[2], float inv, bool valid, float beta,
                                       int L, typename Prec<C::F32>::elem* rows /* [64][ROWF] or null */,
-                                      typename Prec<C::F32>::elem* cols /* [FBK*32][ROWT] or null */,
                                       typename Prec<C::F32>::frag (&phi_frag)[C::FBK], const PlaneCache* out,
                                       size_t row) {
 #pragma unroll
@@ -384,7 +409,7 @@ __device__ inline void block_features(const WSrc<C>& wsrc, int fb, int lane, int
             *reinterpret_cast<typename Prec<C::F32>::uvec*>(reinterpret_cast<typename Prec<C::F32>::ucache*>(out->u) +
                                                             off) = uq;
         }
-        emit_tile<C, KEEP>(tb, w, ln, g, phi, rows, cols, phi_frag);
+        emit_tile<C, KEEP>(tb, w, ln, g, phi, rows, phi_frag);
     }
 }
 
@@ -393,7 +418,6 @@ __device__ inline void block_features(const WSrc<C>& wsrc, int fb, int lane, int
 template <class C, bool KEEP>
 __device__ inline void block_features_cached(const Planes<C>& pl, int fb, int w, int ln, int g, bool valid, int L,
                                              float beta, typename Prec<C::F32>::elem* rows,
-                                             typename Prec<C::F32>::elem* cols,
                                              typename Prec<C::F32>::frag (&phi_frag)[C::FBK],
                                              float (&s_keep)[C::TPB][4], float (&gu_keep)[C::TPB][4]) {
 #pragma unroll
@@ -409,7 +433,7 @@ __device__ inline void block_features_cached(const Planes<C>& pl, int fb, int w,
                 gu_keep[tb][i] = gu[i];
             }
         }
-        emit_tile<C, KEEP>(tb, w, ln, g, phi, rows, cols, phi_frag);
+        emit_tile<C, KEEP>(tb, w, ln, g, phi, rows, phi_frag);
     }
 }
 
@@ -434,10 +458,10 @@ struct TotArgs {
 template <class C, bool CACHED>
 struct TotLds {
     using elem = typename Prec<C::F32>::elem;
-    static constexpr int n_cols = C::FBK * 32 * C::ROWT;
+    static constexpr int n_rows = TB * C::ROWF;   // features of the block, token rows
     static constexpr int n_zt = ZR * C::ROWT;
     static constexpr int n_w = CACHED ? 0 : C::MT * 1024;
-    static constexpr int n_elem = n_cols + n_zt + n_w;
+    static constexpr int n_elem = n_rows + n_zt + n_w;
     static_assert(n_elem * (int)sizeof(elem) <= 160 * 1024, "LDS budget");
 };
 
@@ -450,8 +474,8 @@ __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
     using frag = typename Prec<C::F32>::frag;
     using LD = TotLds<C, CACHED>;
     __shared__ __attribute__((aligned(32))) elem lds[LD::n_elem];
-    elem* s_cols = lds;
-    elem* s_ZT = lds + LD::n_cols;
+    elem* s_rows = lds;
+    elem* s_ZT = lds + LD::n_rows;
     elem* s_w = s_ZT + LD::n_zt;
 
     const int lane = threadIdx.x & 63, ln = lane & 15, g = lane >> 4;
@@ -525,13 +549,13 @@ __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
                 if (fb + 1 < C::NBLK) issue_planes(it, fb + 1);
                 else if (it + 1 < nsub) issue_planes(it + 1, 0);
                 float us[C::TPB][4], ug[C::TPB][4];
-                block_features_cached<C, false>(pl, fb, w, ln, g, valid, a.L, a.beta, nullptr, s_cols, unused, us, ug);
+                block_features_cached<C, false>(pl, fb, w, ln, g, valid, a.L, a.beta, s_rows, unused, us, ug);
             } else {
-                block_features<C, false>(wsrc, fb, lane, w, ln, g, xf, inv, valid, a.beta, a.L, nullptr, s_cols,
-                                         unused, pc_out, row);
+                block_features<C, false>(wsrc, fb, lane, w, ln, g, xf, inv, valid, a.beta, a.L, s_rows, unused,
+                                         pc_out, row);
             }
             __syncthreads();
-            sketch_update<C>(fb, w, ln, g, s_cols, s_ZT, Macc, Zacc);
+            sketch_update<C>(fb, w, ln, g, s_rows, s_ZT, Macc, Zacc);
             __syncthreads();
         }
     }
@@ -659,7 +683,7 @@ __device__ inline void zero_sketch_pads(typename Prec<C::F32>::elem* s_ms, int n
 // 32 kcl + 8 g + 4 h + i of the block, matching the lane's feature order.
 template <class C>
 __device__ inline void block_grad(int ln, int g, const typename Prec<C::F32>::elem* s_ms,
-                                  const typename Prec<C::F32>::frag yf[3], const typename Prec<C::F32>::elem* s_cols,
+                                  const typename Prec<C::F32>::frag yf[3], const typename Prec<C::F32>::elem* s_brow,
                                   const typename Prec<C::F32>::frag Cf[2], bool causal, f32x4 (&G)[C::FBK * 2]) {
 #pragma unroll
     for (int m = 0; m < C::FBK * 2; ++m) {
@@ -671,7 +695,7 @@ __device__ inline void block_grad(int ln, int g, const typename Prec<C::F32>::el
         if (causal) {
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
-                acc = mma(ld_frag<C::F32>(s_cols + fl * C::ROWT + 32 * s2 + 8 * g), Cf[s2], acc);
+                acc = mma(feat_operand<C>(s_brow, kcl, h, s2, ln, g), Cf[s2], acc);
         }
         G[m] = acc;
     }
@@ -823,17 +847,17 @@ struct WStage {
 template <class C>
 struct FwdLds {
     using elem = typename Prec<C::F32>::elem;
+    // Feature tiles of a block, double-buffered: block fb uses buffer fb % 2,
+    // so one barrier per block separates its writes from its reads.
     static constexpr int n_rows = TB * C::ROWF;                 // a-side features [64][ROWF]
     static constexpr int n_brow = TB * C::ROWF;                 // b-side features [64][ROWF]
-    static constexpr int n_cols = C::FBK * 32 * C::ROWT;        // b-side features transposed
     static constexpr int n_zt = ZR * C::ROWT;                   // z_b transposed
     static constexpr int n_sc = TB * C::ROWT;                   // intra scores [a][b]
-    static constexpr int n_stage = TB * C::ROWD;                // O staging (alias of rows | brow)
-    static_assert(n_stage <= n_rows + n_brow, "staging must fit the feature tiles");
-    static constexpr int o_rows = 0;
-    static constexpr int o_brow = o_rows + n_rows;
-    static constexpr int o_cols = o_brow + n_brow;
-    static constexpr int o_zt = o_cols + n_cols;
+    static constexpr int n_stage = TB * C::ROWD;                // O staging (alias of the a-side buffers)
+    static_assert(n_stage <= 2 * n_rows, "staging must fit the feature tiles");
+    static constexpr int o_rows = 0;                            // [2][rows]
+    static constexpr int o_brow = o_rows + 2 * n_rows;          // [2][brow]
+    static constexpr int o_zt = o_brow + 2 * n_brow;
     static constexpr int o_sc = o_zt + n_zt;
     static constexpr int o_w = o_sc + n_sc;
     static constexpr int n_float = 4 * TB + TB;                 // Dpart, Dint
@@ -851,7 +875,6 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
     __shared__ float ldf[LD::n_float];
     elem* s_rows = lds + LD::o_rows;
     elem* s_brow = lds + LD::o_brow;
-    elem* s_cols = lds + LD::o_cols;
     elem* s_ZT = lds + LD::o_zt;
     elem* s_sc = lds + LD::o_sc;
     elem* s_stage = lds + LD::o_rows;   // alias after the feature-block loop
@@ -899,7 +922,7 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
         load_planes<C>(a.cb, base + seg0 + (int64_t)it2 * TB + my, my < nv_of(it2), fb2, g, pn);
     };
     issue(0);
-    issue_planes(0, 0);
+    if (causal) issue_planes(0, 0);
 
     for (int it = 0; it < nsub; ++it) {
         const int64_t t0 = seg0 + (int64_t)it * TB;
@@ -925,14 +948,19 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
 #pragma unroll
         for (int fb = 0; fb < C::NBLK; ++fb) {
             frag phiA[C::FBK], unused[C::FBK];
+            elem* rows_b = s_rows + (fb & 1) * LD::n_rows;
+            elem* brow_b = s_brow + (fb & 1) * LD::n_brow;
             const Planes<C> pl = pn;
-            if (fb + 1 < C::NBLK) issue_planes(it, fb + 1);
-            else if (it + 1 < nsub) issue_planes(it + 1, 0);
-            block_features<C, true>(wsrc, fb, lane, w, ln, g, xa, inv_a, valid, a.beta, a.L, s_rows, nullptr, phiA,
-                                    pc_out, row);
-            float us[C::TPB][4], ug[C::TPB][4];
-            block_features_cached<C, false>(pl, fb, w, ln, g, valid, a.L, a.beta, s_brow, causal ? s_cols : nullptr, unused,
-                                            us, ug);
+            if (causal) {
+                if (fb + 1 < C::NBLK) issue_planes(it, fb + 1);
+                else if (it + 1 < nsub) issue_planes(it + 1, 0);
+            }
+            block_features<C, true>(wsrc, fb, lane, w, ln, g, xa, inv_a, valid, a.beta, a.L, rows_b, phiA, pc_out,
+                                    row);
+            if (causal) {
+                float us[C::TPB][4], ug[C::TPB][4];
+                block_features_cached<C, false>(pl, fb, w, ln, g, valid, a.L, a.beta, brow_b, unused, us, ug);
+            }
             __syncthreads();
             if (causal) {
 #pragma unroll
@@ -940,7 +968,7 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
                     if (bt <= w) {
 #pragma unroll
                         for (int kcl = 0; kcl < C::FBK; ++kcl)
-                            Sc[bt] = mma(ld_frag<C::F32>(s_brow + (16 * bt + ln) * C::ROWF + 32 * kcl + 8 * g),
+                            Sc[bt] = mma(ld_frag<C::F32>(brow_b + (16 * bt + ln) * C::ROWF + 32 * kcl + 8 * g),
                                          phiA[kcl], Sc[bt]);
                     }
                 }
@@ -951,17 +979,16 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
                 const frag mf = pack<C::F32>(Macc[2 * kc], Macc[2 * kc + 1]);
 #pragma unroll
                 for (int at = 0; at < 4; ++at)
-                    Y[at] = mma(ld_frag<C::F32>(s_rows + (16 * at + ln) * C::ROWF + 32 * kcl + 8 * g), mf, Y[at]);
+                    Y[at] = mma(ld_frag<C::F32>(rows_b + (16 * at + ln) * C::ROWF + 32 * kcl + 8 * g), mf, Y[at]);
             }
             const int kw = w - C::own_base(fb);
             if (kw >= 0 && kw < C::FBK) {
                 const frag zf = pack<C::F32>(Zacc[2 * C::zidx(fb)], Zacc[2 * C::zidx(fb) + 1]);
 #pragma unroll
                 for (int at = 0; at < 4; ++at)
-                    Dacc[at] = mma(ld_frag<C::F32>(s_rows + (16 * at + ln) * C::ROWF + 32 * kw + 8 * g), zf, Dacc[at]);
+                    Dacc[at] = mma(ld_frag<C::F32>(rows_b + (16 * at + ln) * C::ROWF + 32 * kw + 8 * g), zf, Dacc[at]);
             }
-            if (causal) sketch_update<C>(fb, w, ln, g, s_cols, s_ZT, Macc, Zacc);
-            __syncthreads();
+            if (causal) sketch_update<C>(fb, w, ln, g, brow_b, s_ZT, Macc, Zacc);
         }
         // intra-sub-block term: scores of visible keys b <= a. The value
         // readout multiplies the scores rounded to the operand type, so the
@@ -1035,7 +1062,7 @@ struct BwdQLds {
     // sub-block it is formed from y = hi + lo with float32 accumulation
     static constexpr bool YLO = !C::F32;
     static constexpr int n_ms = C::FBK * 32 * C::ROWE;          // sketch rows
-    static constexpr int n_cols = C::FBK * 32 * C::ROWT;        // key features transposed
+    static constexpr int n_cols = TB * C::ROWF;                 // key features, token rows
     static constexpr int n_zt = ZR * C::ROWT;                   // [v | 1] transposed
     static constexpr int n_zr = TB * C::ROWE;                   // [v | 1] rows
     static constexpr int n_yr = TB * C::ROWE;                   // y rows (hi)
@@ -1055,7 +1082,10 @@ struct BwdQLds {
     static constexpr int o_zr = ZR_SHARED ? o_ms + n_ms : o_end;
     static constexpr int o_ylo = YLO_SHARED ? o_cols : o_end + (ZR_SHARED ? 0 : n_zr);
     static constexpr int n_elem = o_end + (ZR_SHARED ? 0 : n_zr) + (YLO_SHARED ? 0 : n_ylo);
-    static constexpr int OCC = (!C::F32 && C::NKC <= 8) ? 2 : 1;
+    // two workgroups per CU where registers (bf16, up to 8 feature chunks) and
+    // LDS allow
+    static constexpr int OCC =
+        (!C::F32 && C::NKC <= 8 && n_elem * (int)sizeof(elem) * 2 <= 160 * 1024) ? 2 : 1;
     static_assert(n_elem * (int)sizeof(elem) * OCC <= 160 * 1024, "LDS budget");
 };
 
@@ -1180,7 +1210,7 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
             if (causal) {
                 frag unused[C::FBK];
                 float us[C::TPB][4], ug[C::TPB][4];
-                block_features_cached<C, false>(kb_, fb, w, ln, g, valid, a.L, a.beta, nullptr, cols_b, unused, us, ug);
+                block_features_cached<C, false>(kb_, fb, w, ln, g, valid, a.L, a.beta, cols_b, unused, us, ug);
             }
             __syncthreads();
             frag yf[3];
@@ -1233,7 +1263,7 @@ struct BwdKLds {
     static constexpr int NB = 2;
     static constexpr int n_rows = DV ? TB * C::ROWF : 0;        // key features [64][ROWF]
     static constexpr int n_brow = DV ? TB * C::ROWF : 0;        // query features [64][ROWF]
-    static constexpr int n_cols = C::FBK * 32 * C::ROWT;        // query features transposed
+    static constexpr int n_cols = DK ? TB * C::ROWF : 0;        // query features, token rows
     static constexpr int n_ms = DK ? C::FBK * 32 * C::ROWE : 0; // sketch rows
     // per-sub-block tiles
     static constexpr int n_zt = ZR * C::ROWT;                   // [g | e] transposed
@@ -1268,7 +1298,10 @@ struct BwdKLds {
     static constexpr int o_x3 = o_x2 + (ZLO_SHARED ? 0 : n_zlo);
     static constexpr int o_zr = ZR_SHARED ? o_ms + n_ms : o_x3;
     static constexpr int n_elem = o_x3 + (ZR_SHARED ? 0 : n_zr);
-    static constexpr int OCC = (!C::F32 && C::NKC <= 8) ? 2 : 1;
+    // two workgroups per CU where registers (bf16, up to 8 feature chunks) and
+    // LDS allow
+    static constexpr int OCC =
+        (!C::F32 && C::NKC <= 8 && n_elem * (int)sizeof(elem) * 2 <= 160 * 1024) ? 2 : 1;
     static_assert(n_elem * (int)sizeof(elem) * OCC <= 160 * 1024, "LDS budget");
 };
 
@@ -1396,11 +1429,11 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
             elem* cols_b = s_cols + bsel * LD::n_cols;
             elem* ms_b = s_ms + bsel * LD::n_ms;
             if constexpr (DV) {
-                block_features_cached<C, true>(ka, fb, w, ln, g, valid, a.L, a.beta, rows_b, nullptr, phiA, us, ug);
+                block_features_cached<C, true>(ka, fb, w, ln, g, valid, a.L, a.beta, rows_b, phiA, us, ug);
                 if (causal)
-                    block_features_cached<C, false>(qb, fb, w, ln, g, valid, a.L, a.beta, brow_b, cols_b, unused, us, ug);
+                    block_features_cached<C, false>(qb, fb, w, ln, g, valid, a.L, a.beta, brow_b, unused, us, ug);
             } else if (causal) {
-                block_features_cached<C, false>(qb, fb, w, ln, g, valid, a.L, a.beta, nullptr, cols_b, unused, us, ug);
+                block_features_cached<C, false>(qb, fb, w, ln, g, valid, a.L, a.beta, cols_b, unused, us, ug);
             }
             if constexpr (DK) write_sketch_rows<C>(fb, w, ln, g, Macc, Zacc, mcol, 0.f, ms_b);
             __syncthreads();
@@ -1450,7 +1483,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
                     chain_backproject<C>(t, lane, phi, dA, sg, gu, WTp, dhp, dX);
                 }
             }
-            if (causal) sketch_update<C, DK>(fb, w, ln, g, cols_b, s_ZT, Macc, Zacc);
+            if (causal) sketch_update<C, DK>(fb, w, ln, g, DV ? brow_b : cols_b, s_ZT, Macc, Zacc);
             if (LD::NB == 1) __syncthreads();   // single buffer: reads done before the next block's writes
         }
         if (LD::NB == 2) __syncthreads();   // the block tiles are read; the sub-block tiles below reuse them
