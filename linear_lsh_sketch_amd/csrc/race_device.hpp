@@ -30,7 +30,6 @@ constexpr int TB = 64;       // tokens per sub-block
 constexpr int NW = 4;        // waves per workgroup
 constexpr int NT = NW * 64;  // threads per workgroup
 constexpr int EA = 96;       // augmented width: 64 values, 1 mass column, zero padding
-constexpr int ZR = 80;       // rows of the transposed value tile: 64 values + mass tile
 constexpr float NORM_EPS = 1e-12f;
 constexpr float NEAR_ZERO = 1e-5f;
 
@@ -239,7 +238,7 @@ struct Cfg {
     static constexpr int NPL = MT * 16;           // projection rows (planes incl. padding) per token
     static constexpr int PAD = Prec<F32>::PAD;
     static constexpr int ROWF = FBK * 32 + PAD;   // row stride of token x feature tiles
-    static constexpr int ROWT = TB + PAD;         // row stride of feature x token tiles
+    static constexpr int ROWT = TB + PAD;         // row stride of token-column tiles (intra scores)
     static constexpr int ROWE = EA + PAD;         // row stride of token x augmented tiles
     static constexpr int ROWD = DH + PAD;
     static_assert(NKC % FBK == 0, "feature blocks must tile the features");

@@ -196,47 +196,37 @@ __device__ inline void load_planes(const PlaneCache& pc, size_t row, bool valid,
 }
 
 // Write the value tile of the 64 tokens (this thread: row th/4, quarter th%4)
-// into ZT [80][ROWT] (transposed) and optionally Zrow [64][ROWE] (rows):
-// z = [x * scale | mass]. With Zlo set, also the rows of the rounding residual
-// z - elem(z) (so that hi + lo carries z to float32 precision). Rows/columns
-// 65.. stay zero from zero_pads.
+// into Zrow [64][ROWE] (token rows): z = [x * scale | mass]. With Zlo set, also
+// the rows of the rounding residual z - elem(z) (so that hi + lo carries z to
+// float32 precision). Columns 65.. stay zero from zero_pads.
 template <class C>
 __device__ inline void write_aug(const typename Prec<C::F32>::frag zr[2], float scale, float mass,
-                                 typename Prec<C::F32>::elem* ZT, typename Prec<C::F32>::elem* Zrow,
-                                 typename Prec<C::F32>::elem* Zlo = nullptr) {
+                                 typename Prec<C::F32>::elem* Zrow, typename Prec<C::F32>::elem* Zlo = nullptr) {
     const int th = threadIdx.x, r = th >> 2, q = th & 3;
     float v[16];
 #pragma unroll
     for (int c = 0; c < 16; ++c) v[c] = q16_at<C::F32>(zr, c) * scale;
-    const int rp = tok_pos(r);
+    const typename Prec<C::F32>::frag h0 = pack8<C::F32>(v), h1 = pack8<C::F32>(v + 8);
+    st_frag<C::F32>(Zrow + r * C::ROWE + 16 * q, h0);
+    st_frag<C::F32>(Zrow + r * C::ROWE + 16 * q + 8, h1);
+    const typename Prec<C::F32>::elem mh = to_elem<C::F32>(mass);
+    if (q == 0) Zrow[r * C::ROWE + 64] = mh;
+    if (Zlo) {
+        float lo[16];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) ZT[(16 * q + c) * C::ROWT + rp] = to_elem<C::F32>(v[c]);
-    if (q == 0) ZT[64 * C::ROWT + rp] = to_elem<C::F32>(mass);
-    if (Zrow) {
-        const typename Prec<C::F32>::frag h0 = pack8<C::F32>(v), h1 = pack8<C::F32>(v + 8);
-        st_frag<C::F32>(Zrow + r * C::ROWE + 16 * q, h0);
-        st_frag<C::F32>(Zrow + r * C::ROWE + 16 * q + 8, h1);
-        const typename Prec<C::F32>::elem mh = to_elem<C::F32>(mass);
-        if (q == 0) Zrow[r * C::ROWE + 64] = mh;
-        if (Zlo) {
-            float lo[16];
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                lo[c] = v[c] - elem_f<C::F32>(h0[c]);
-                lo[8 + c] = v[8 + c] - elem_f<C::F32>(h1[c]);
-            }
-            st_frag<C::F32>(Zlo + r * C::ROWE + 16 * q, pack8<C::F32>(lo));
-            st_frag<C::F32>(Zlo + r * C::ROWE + 16 * q + 8, pack8<C::F32>(lo + 8));
-            if (q == 0) Zlo[r * C::ROWE + 64] = to_elem<C::F32>(mass - elem_f<C::F32>(mh));
+        for (int c = 0; c < 8; ++c) {
+            lo[c] = v[c] - elem_f<C::F32>(h0[c]);
+            lo[8 + c] = v[8 + c] - elem_f<C::F32>(h1[c]);
         }
+        st_frag<C::F32>(Zlo + r * C::ROWE + 16 * q, pack8<C::F32>(lo));
+        st_frag<C::F32>(Zlo + r * C::ROWE + 16 * q + 8, pack8<C::F32>(lo + 8));
+        if (q == 0) Zlo[r * C::ROWE + 64] = to_elem<C::F32>(mass - elem_f<C::F32>(mh));
     }
 }
 
-// Zero the constant padding of ZT (rows 65..79) and of row tiles (cols 65..95).
+// Zero the constant padding (columns 65..95) of token-row value tiles.
 template <class C>
-__device__ inline void zero_pads(typename Prec<C::F32>::elem* ZT, typename Prec<C::F32>::elem* rows_a,
-                                 typename Prec<C::F32>::elem* rows_b) {
-    for (int idx = threadIdx.x; idx < 15 * TB; idx += NT) ZT[(65 + idx / TB) * C::ROWT + idx % TB] = to_elem<C::F32>(0.f);
+__device__ inline void zero_pads(typename Prec<C::F32>::elem* rows_a, typename Prec<C::F32>::elem* rows_b) {
     if (rows_a)
         for (int idx = threadIdx.x; idx < 31 * TB; idx += NT) rows_a[(idx / 31) * C::ROWE + 65 + idx % 31] = to_elem<C::F32>(0.f);
     if (rows_b)
@@ -332,17 +322,45 @@ __device__ inline typename Prec<C::F32>::frag feat_operand(const typename Prec<C
     return f;
 }
 
+// Matrix-core B operand of a token contraction, read from a token-row value
+// tile Zrow[64][ROWE]: lane (ln, g) gets column cb + ln and the tokens at K
+// positions 32 s + 8 g + j in tok_pos order (as feat_operand). bf16: two LDS
+// transpose reads, lane j of a 16-lane group pointing at columns
+// cb + 4 (j % 4) .. +3 of one token.
+template <class C>
+__device__ inline typename Prec<C::F32>::frag val_operand(const typename Prec<C::F32>::elem* Zrow, int cb, int s,
+                                                         int ln, int g) {
+    typename Prec<C::F32>::frag f;
+    if constexpr (C::F32) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] = Zrow[(32 * s + 16 * (j >> 2) + 4 * g + (j & 3)) * C::ROWE + cb + ln];
+    } else {
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        const typename Prec<C::F32>::elem* p = Zrow + (32 * s + 4 * g + (ln >> 2)) * C::ROWE + cb + 4 * (ln & 3);
+        const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+        const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 16 * C::ROWE));
+        const bf16x4 ab = __builtin_bit_cast(bf16x4, a), bb = __builtin_bit_cast(bf16x4, b);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[i] = ab[i];
+            f[4 + i] = bb[i];
+        }
+    }
+    return f;
+}
+
 // Sketch update for feature block fb from the b-side features (token-row tile
-// `brow`) and the transposed value tile: value columns of wave w, then the
-// mass accumulators of the chunk wave w owns in this block.
+// `brow`) and the value tile Zrow: value columns of wave w, then the mass
+// accumulators of the chunk wave w owns in this block.
 template <class C, bool MASS = true>
 __device__ inline void sketch_update(int fb, int w, int ln, int g, const typename Prec<C::F32>::elem* brow,
-                                     const typename Prec<C::F32>::elem* ZT, f32x4 Macc[C::NKC * 2],
+                                     const typename Prec<C::F32>::elem* Zrow, f32x4 Macc[C::NKC * 2],
                                      f32x4 Zacc[C::NOWN * 2]) {
     using frag = typename Prec<C::F32>::frag;
     frag zt[2];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) zt[s] = ld_frag<C::F32>(ZT + (16 * w + ln) * C::ROWT + 32 * s + 8 * g);
+    for (int s = 0; s < 2; ++s) zt[s] = val_operand<C>(Zrow, 16 * w, s, ln, g);
 #pragma unroll
     for (int kcl = 0; kcl < C::FBK; ++kcl) {
         const int kc = fb * C::FBK + kcl;
@@ -357,7 +375,7 @@ __device__ inline void sketch_update(int fb, int w, int ln, int g, const typenam
     if (MASS && kw >= 0 && kw < C::FBK) {
         frag zm[2];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) zm[s] = ld_frag<C::F32>(ZT + (64 + ln) * C::ROWT + 32 * s + 8 * g);
+        for (int s = 0; s < 2; ++s) zm[s] = val_operand<C>(Zrow, 64, s, ln, g);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -459,9 +477,9 @@ template <class C, bool CACHED>
 struct TotLds {
     using elem = typename Prec<C::F32>::elem;
     static constexpr int n_rows = TB * C::ROWF;   // features of the block, token rows
-    static constexpr int n_zt = ZR * C::ROWT;
+    static constexpr int n_zr = TB * C::ROWE;     // [z | mass], token rows
     static constexpr int n_w = CACHED ? 0 : C::MT * 1024;
-    static constexpr int n_elem = n_rows + n_zt + n_w;
+    static constexpr int n_elem = n_rows + n_zr + n_w;
     static_assert(n_elem * (int)sizeof(elem) <= 160 * 1024, "LDS budget");
 };
 
@@ -475,8 +493,8 @@ __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
     using LD = TotLds<C, CACHED>;
     __shared__ __attribute__((aligned(32))) elem lds[LD::n_elem];
     elem* s_rows = lds;
-    elem* s_ZT = lds + LD::n_rows;
-    elem* s_w = s_ZT + LD::n_zt;
+    elem* s_zr = lds + LD::n_rows;
+    elem* s_w = s_zr + LD::n_zr;
 
     const int lane = threadIdx.x & 63, ln = lane & 15, g = lane >> 4;
     // wave index as a scalar: every branch on it is wave-uniform, so no MFMA is
@@ -490,7 +508,7 @@ __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
     const int nsub = (int)((seg1 - seg0 + TB - 1) / TB);
     const int my = 16 * w + ln;
     if (!CACHED) stage_w<C>(reinterpret_cast<const elem*>(a.W), a.L, s_w);
-    zero_pads<C>(s_ZT, nullptr, nullptr);
+    zero_pads<C>(s_zr, nullptr);
     __syncthreads();   // W' and the padding are written by all waves, read by each
     const WSrc<C> wsrc{s_w, reinterpret_cast<const elem*>(a.W), a.L};
     const PlaneCache* pc_out = (!CACHED && a.pc.u) ? &a.pc : nullptr;
@@ -539,8 +557,8 @@ __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
             if (pc_out && valid && g == 0) pc_out->inv[row] = inv;
         }
         const bool ok = tr < nv;
-        if (!CACHED) write_aug<C>(zr, 1.f, ok ? 1.f : 0.f, s_ZT, nullptr);
-        else write_aug<C>(zr, ok ? rcp_(dz) : 0.f, ok ? ez : 0.f, s_ZT, nullptr);
+        if (!CACHED) write_aug<C>(zr, 1.f, ok ? 1.f : 0.f, s_zr);
+        else write_aug<C>(zr, ok ? rcp_(dz) : 0.f, ok ? ez : 0.f, s_zr);
 #pragma unroll
         for (int fb = 0; fb < C::NBLK; ++fb) {
             frag unused[C::FBK];
@@ -555,7 +573,7 @@ __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
                                          pc_out, row);
             }
             __syncthreads();
-            sketch_update<C>(fb, w, ln, g, s_rows, s_ZT, Macc, Zacc);
+            sketch_update<C>(fb, w, ln, g, s_rows, s_zr, Macc, Zacc);
             __syncthreads();
         }
     }
@@ -851,14 +869,14 @@ struct FwdLds {
     // so one barrier per block separates its writes from its reads.
     static constexpr int n_rows = TB * C::ROWF;                 // a-side features [64][ROWF]
     static constexpr int n_brow = TB * C::ROWF;                 // b-side features [64][ROWF]
-    static constexpr int n_zt = ZR * C::ROWT;                   // z_b transposed
+    static constexpr int n_zr = TB * C::ROWE;                   // [z_b | mass], token rows
     static constexpr int n_sc = TB * C::ROWT;                   // intra scores [a][b]
     static constexpr int n_stage = TB * C::ROWD;                // O staging (alias of the a-side buffers)
     static_assert(n_stage <= 2 * n_rows, "staging must fit the feature tiles");
     static constexpr int o_rows = 0;                            // [2][rows]
     static constexpr int o_brow = o_rows + 2 * n_rows;          // [2][brow]
-    static constexpr int o_zt = o_brow + 2 * n_brow;
-    static constexpr int o_sc = o_zt + n_zt;
+    static constexpr int o_zr = o_brow + 2 * n_brow;
+    static constexpr int o_sc = o_zr + n_zr;
     static constexpr int o_w = o_sc + n_sc;
     static constexpr int n_float = 4 * TB + TB;                 // Dpart, Dint
     // two workgroups per CU (VGPR budget 256: two waves share each SIMD)
@@ -875,7 +893,7 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
     __shared__ float ldf[LD::n_float];
     elem* s_rows = lds + LD::o_rows;
     elem* s_brow = lds + LD::o_brow;
-    elem* s_ZT = lds + LD::o_zt;
+    elem* s_zr = lds + LD::o_zr;
     elem* s_sc = lds + LD::o_sc;
     elem* s_stage = lds + LD::o_rows;   // alias after the feature-block loop
     float* f_Dpart = ldf;               // [4][64]
@@ -894,7 +912,7 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
     constexpr bool causal = CAUSAL;
     elem* s_w = LD::WS::on ? lds + LD::o_w : nullptr;
     if (LD::WS::on) stage_w<C>(W, a.L, s_w);
-    zero_pads<C>(s_ZT, nullptr, nullptr);
+    zero_pads<C>(s_zr, nullptr);
     __syncthreads();   // W' and the padding are written by all waves, read by each
     const WSrc<C> wsrc{s_w, W, a.L};
     const PlaneCache* pc_out = a.ca.u ? &a.ca : nullptr;   // the queries' plane values for the backward
@@ -936,7 +954,7 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
         float inv_a, nrm_a;
         row_norm<C::F32>(xa, inv_a, nrm_a);
         if (pc_out && valid && g == 0) pc_out->inv[row] = inv_a;
-        write_aug<C>(zr, 1.f, tok ? 1.f : 0.f, s_ZT, nullptr);
+        write_aug<C>(zr, 1.f, tok ? 1.f : 0.f, s_zr);
 
         f32x4 Y[4], Dacc[4], Sc[4];
 #pragma unroll
@@ -988,7 +1006,7 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
                 for (int at = 0; at < 4; ++at)
                     Dacc[at] = mma(ld_frag<C::F32>(rows_b + (16 * at + ln) * C::ROWF + 32 * kw + 8 * g), zf, Dacc[at]);
             }
-            if (causal) sketch_update<C>(fb, w, ln, g, brow_b, s_ZT, Macc, Zacc);
+            if (causal) sketch_update<C>(fb, w, ln, g, brow_b, s_zr, Macc, Zacc);
         }
         // intra-sub-block term: scores of visible keys b <= a. The value
         // readout multiplies the scores rounded to the operand type, so the
@@ -1022,7 +1040,7 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
         if (causal) {
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                const frag zt = ld_frag<C::F32>(s_ZT + (16 * w + ln) * C::ROWT + 32 * s + 8 * g);
+                const frag zt = val_operand<C>(s_zr, 16 * w, s, ln, g);
 #pragma unroll
                 for (int at = 0; at < 4; ++at)
                     Y[at] = mma(ld_frag<C::F32>(s_sc + (16 * at + ln) * C::ROWT + 32 * s + 8 * g), zt, Y[at]);
@@ -1063,25 +1081,21 @@ struct BwdQLds {
     static constexpr bool YLO = !C::F32;
     static constexpr int n_ms = C::FBK * 32 * C::ROWE;          // sketch rows
     static constexpr int n_cols = TB * C::ROWF;                 // key features, token rows
-    static constexpr int n_zt = ZR * C::ROWT;                   // [v | 1] transposed
     static constexpr int n_zr = TB * C::ROWE;                   // [v | 1] rows
     static constexpr int n_yr = TB * C::ROWE;                   // y rows (hi)
     static constexpr int n_ylo = YLO ? TB * C::ROWE : 0;        // y rows (lo)
     // The per-block tiles (sketch rows, key features) are double-buffered:
     // block fb uses buffer fb % 2, so one barrier per block separates writes
-    // from reads. The z rows (read before the block loop) share the second
-    // sketch-row buffer and the y lo rows (first sub-block of a sequence only)
-    // the feature buffers, where they fit.
-    static constexpr bool ZR_SHARED = n_zr <= n_ms;
+    // from reads. The y lo rows (first sub-block of a sequence only, read
+    // before the block loop) share the feature buffers where they fit.
     static constexpr bool YLO_SHARED = n_ylo <= 2 * n_cols;
     static constexpr int o_ms = 0;
     static constexpr int o_cols = o_ms + 2 * n_ms;
-    static constexpr int o_zt = o_cols + 2 * n_cols;
-    static constexpr int o_yr = o_zt + n_zt;
+    static constexpr int o_zr = o_cols + 2 * n_cols;
+    static constexpr int o_yr = o_zr + n_zr;
     static constexpr int o_end = o_yr + n_yr;
-    static constexpr int o_zr = ZR_SHARED ? o_ms + n_ms : o_end;
-    static constexpr int o_ylo = YLO_SHARED ? o_cols : o_end + (ZR_SHARED ? 0 : n_zr);
-    static constexpr int n_elem = o_end + (ZR_SHARED ? 0 : n_zr) + (YLO_SHARED ? 0 : n_ylo);
+    static constexpr int o_ylo = YLO_SHARED ? o_cols : o_end;
+    static constexpr int n_elem = o_end + (YLO_SHARED ? 0 : n_ylo);
     // two workgroups per CU where registers (bf16, up to 8 feature chunks) and
     // LDS allow
     static constexpr int OCC =
@@ -1097,7 +1111,6 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
     __shared__ __attribute__((aligned(32))) elem lds[LD::n_elem];
     elem* s_ms = lds + LD::o_ms;
     elem* s_cols = lds + LD::o_cols;
-    elem* s_ZT = lds + LD::o_zt;
     elem* s_zr = lds + LD::o_zr;
     elem* s_yr = lds + LD::o_yr;
     elem* s_ylo = lds + LD::o_ylo;
@@ -1112,8 +1125,8 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
     const elem* WTp = reinterpret_cast<const elem*>(a.WTp);
     constexpr bool causal = CAUSAL;
     zero_sketch_pads<C>(s_ms, 2);
-    zero_pads<C>(s_ZT, s_zr, s_yr);
-    if (LD::YLO) zero_pads<C>(s_ZT, s_ylo, nullptr);
+    zero_pads<C>(s_zr, s_yr);
+    if (LD::YLO) zero_pads<C>(s_ylo, nullptr);
     __syncthreads();   // the padding is written by all waves, read by each
 
     f32x4 Macc[C::NKC * 2], Zacc[C::NOWN * 2];
@@ -1151,7 +1164,7 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
         const float dd = tok ? a.Dv[base + t0 + tr] : 1.f;
         const float inv_a = valid ? a.ca.inv[row] : 1.f;
         const bool first = t0 == 0;   // the sub-block that starts the sequence
-        if (causal) write_aug<C>(zr, 1.f, tok ? 1.f : 0.f, s_ZT, s_zr);
+        if (causal) write_aug<C>(zr, 1.f, tok ? 1.f : 0.f, s_zr);
         // y = [dO / D | e], e = -<dO, O> / D; this thread holds 16 columns of row tr
         {
             float delta = 0.f;
@@ -1235,9 +1248,9 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
                 }
                 chain_backproject<C>(t, lane, phi, dA, sg, gu, WTp, dhp, dX);
             }
-            if (causal) sketch_update<C>(fb, w, ln, g, cols_b, s_ZT, Macc, Zacc);
+            if (causal) sketch_update<C>(fb, w, ln, g, cols_b, s_zr, Macc, Zacc);
         }
-        __syncthreads();   // the next sub-block rewrites ZT, the y and z rows
+        __syncthreads();   // the next sub-block rewrites the y and z rows
         store_dx<C>(a.Xa, a.out0, row, valid, g, inv_a, dX);
     }
 }
@@ -1266,10 +1279,9 @@ struct BwdKLds {
     static constexpr int n_cols = DK ? TB * C::ROWF : 0;        // query features, token rows
     static constexpr int n_ms = DK ? C::FBK * 32 * C::ROWE : 0; // sketch rows
     // per-sub-block tiles
-    static constexpr int n_zt = ZR * C::ROWT;                   // [g | e] transposed
     static constexpr int n_sc = DV ? TB * C::ROWT : 0;          // intra scores [a][b]
     static constexpr int n_stage = DV ? TB * C::ROWD : 0;       // dV staging
-    static constexpr int n_zr = DK ? TB * C::ROWE : 0;          // [g | e] rows
+    static constexpr int n_zr = TB * C::ROWE;                   // [g | e] rows
     // bf16 residual of the [g | e] rows: the intra-sub-block product g.v + e
     // cancels for a query against its only key
     static constexpr bool ZLO = DK && !C::F32;
@@ -1277,27 +1289,24 @@ struct BwdKLds {
     static constexpr int n_yr = DK ? TB * C::ROWE : 0;          // [v | 1] rows
     // Tiles live outside the block loop share the block buffers where they
     // fit: the intra scores and the residual rows the feature buffers, the
-    // staging the row-feature buffers, the z rows the second sketch-row buffer.
+    // staging the row-feature buffers.
     static constexpr bool SC_SHARED = n_sc <= NB * n_cols;
     static constexpr bool STAGE_SHARED = n_stage <= NB * (n_rows + n_brow);
     static constexpr bool ZLO_SHARED = NB == 2 && n_zlo <= 2 * n_cols;
-    static constexpr bool ZR_SHARED = NB == 2 && n_zr <= n_ms;
     static constexpr int o_rows = 0;                            // [NB][rows | brow]
     static constexpr int o_brow = o_rows + n_rows;
     static constexpr int RB = n_rows + n_brow;                  // stride of the row-feature buffers
     static constexpr int o_cols = NB * RB;                      // [NB][cols]
     static constexpr int o_ms = o_cols + NB * n_cols;           // [NB][ms]
-    static constexpr int o_zt = o_ms + NB * n_ms;
-    static constexpr int o_yr = o_zt + n_zt;
+    static constexpr int o_zr = o_ms + NB * n_ms;
+    static constexpr int o_yr = o_zr + n_zr;
     static constexpr int o_x0 = o_yr + n_yr;                    // unshared tiles follow
     static constexpr int o_sc = SC_SHARED ? o_cols : o_x0;
     static constexpr int o_x1 = o_x0 + (SC_SHARED ? 0 : n_sc);
     static constexpr int o_stage = STAGE_SHARED ? o_rows : o_x1;
     static constexpr int o_x2 = o_x1 + (STAGE_SHARED ? 0 : n_stage);
     static constexpr int o_zlo = ZLO_SHARED ? o_cols : o_x2;
-    static constexpr int o_x3 = o_x2 + (ZLO_SHARED ? 0 : n_zlo);
-    static constexpr int o_zr = ZR_SHARED ? o_ms + n_ms : o_x3;
-    static constexpr int n_elem = o_x3 + (ZR_SHARED ? 0 : n_zr);
+    static constexpr int n_elem = o_x2 + (ZLO_SHARED ? 0 : n_zlo);
     // two workgroups per CU where registers (bf16, up to 8 feature chunks) and
     // LDS allow
     static constexpr int OCC =
@@ -1316,7 +1325,6 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
     elem* s_brow = lds + LD::o_brow;
     elem* s_cols = lds + LD::o_cols;
     elem* s_ms = lds + LD::o_ms;
-    elem* s_ZT = lds + LD::o_zt;
     elem* s_sc = lds + LD::o_sc;
     elem* s_zr = lds + LD::o_zr;
     elem* s_yr = lds + LD::o_yr;
@@ -1333,8 +1341,8 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
     const elem* WTp = reinterpret_cast<const elem*>(a.WTp);
     constexpr bool causal = CAUSAL;
     if (DK) zero_sketch_pads<C>(s_ms, LD::NB);
-    zero_pads<C>(s_ZT, DK ? s_zr : nullptr, DK ? s_yr : nullptr);
-    if (LD::ZLO) zero_pads<C>(s_ZT, s_zlo, nullptr);
+    zero_pads<C>(s_zr, DK ? s_yr : nullptr);
+    if (LD::ZLO) zero_pads<C>(s_zlo, nullptr);
     __syncthreads();   // the padding is written by all waves, read by each
 
     f32x4 Macc[C::NKC * 2], Zacc[C::NOWN * 2];
@@ -1390,7 +1398,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
 
         const bool first = t0 == 0;   // the sub-block that starts the sequence
         if (causal)
-            write_aug<C>(zr, tok ? rcp_(zd) : 0.f, tok ? ze : 0.f, s_ZT, DK ? s_zr : nullptr,
+            write_aug<C>(zr, tok ? rcp_(zd) : 0.f, tok ? ze : 0.f, s_zr,
                          (LD::ZLO && first) ? s_zlo : nullptr);
         if constexpr (DK) {
             // y rows = [v | 1]
@@ -1483,7 +1491,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
                     chain_backproject<C>(t, lane, phi, dA, sg, gu, WTp, dhp, dX);
                 }
             }
-            if (causal) sketch_update<C, DK>(fb, w, ln, g, DV ? brow_b : cols_b, s_ZT, Macc, Zacc);
+            if (causal) sketch_update<C, DK>(fb, w, ln, g, DV ? brow_b : cols_b, s_zr, Macc, Zacc);
             if (LD::NB == 1) __syncthreads();   // single buffer: reads done before the next block's writes
         }
         if (LD::NB == 2) __syncthreads();   // the block tiles are read; the sub-block tiles below reuse them
@@ -1503,7 +1511,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
                 __syncthreads();
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
-                    const frag zt = ld_frag<C::F32>(s_ZT + (16 * w + ln) * C::ROWT + 32 * s + 8 * g);
+                    const frag zt = val_operand<C>(s_zr, 16 * w, s, ln, g);
 #pragma unroll
                     for (int at = 0; at < 4; ++at)
                         Y[at] = mma(ld_frag<C::F32>(s_sc + (16 * at + ln) * C::ROWT + 32 * s + 8 * g), zt, Y[at]);
