@@ -71,6 +71,74 @@ struct In {
 // Global loads are issued one sub-block ahead ("raw" registers) and consumed
 // by the next iteration, so their latency overlaps the current sub-block.
 
+// Per-chunk tensor access through buffer resources: a workgroup addresses the
+// rows [row0, row0 + nrows) of its chunk with 32-bit byte offsets; loads of
+// rows past the end return zeros and stores there are dropped, so the ragged
+// last sub-block of a sequence needs no branches.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline rsrc_t rows_rsrc(const void* base, size_t row0, int64_t nrows, int row_bytes) {
+    char* p = base ? const_cast<char*>(reinterpret_cast<const char*>(base)) + row0 * (size_t)row_bytes : nullptr;
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, base ? (int)(nrows * row_bytes) : 0, 0x00020000);
+}
+__device__ inline u32x4 bload128(rsrc_t r, int off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0); }
+__device__ inline u32x2 bload64(rsrc_t r, int off) { return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0); }
+__device__ inline float bload_f32(rsrc_t r, int off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ inline void bstore128(rsrc_t r, int off, u32x4 v) { __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0); }
+__device__ inline void bstore64(rsrc_t r, int off, u32x2 v) { __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0); }
+__device__ inline void bstore_f32(rsrc_t r, int off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v), r, off, 0, 0);
+}
+
+// One 8-element operand (bf16: 16 bytes, float32: 32 bytes) at byte offset off.
+template <bool F32>
+__device__ inline typename Prec<F32>::frag bload_frag(rsrc_t r, int off) {
+    if constexpr (F32) {
+        const u32x4 a = bload128(r, off), b = bload128(r, off + 16);
+        const f32x4 fa = __builtin_bit_cast(f32x4, a), fb = __builtin_bit_cast(f32x4, b);
+        return f32x8{fa[0], fa[1], fa[2], fa[3], fb[0], fb[1], fb[2], fb[3]};
+    } else {
+        return __builtin_bit_cast(bf16x8, bload128(r, off));
+    }
+}
+
+template <bool F32>
+__device__ inline void bstore_frag(rsrc_t r, int off, const typename Prec<F32>::frag& f) {
+    if constexpr (F32) {
+        // whole-vector casts (a vector built from per-element bit casts
+        // compiled to a single-element load here)
+        const f32x4 lo = __builtin_shufflevector(f, f, 0, 1, 2, 3), hi = __builtin_shufflevector(f, f, 4, 5, 6, 7);
+        bstore128(r, off, __builtin_bit_cast(u32x4, lo));
+        bstore128(r, off + 16, __builtin_bit_cast(u32x4, hi));
+    } else {
+        bstore128(r, off, __builtin_bit_cast(u32x4, f));
+    }
+}
+
+// Bytes of a [*, 64] row of the input type.
+template <bool F32>
+constexpr int row_bytes() { return DH * (F32 ? 4 : 2); }
+
+// This lane's projection operand of in-chunk row rowi: K positions 32 s + 8 g .. +7.
+template <bool F32>
+__device__ inline void load_row_b(rsrc_t r, int rowi, int g, typename Prec<F32>::frag x[2]) {
+    constexpr int es = F32 ? 4 : 2;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) x[s] = bload_frag<F32>(r, rowi * row_bytes<F32>() + (32 * s + 8 * g) * es);
+}
+
+// Columns 16 q .. 16 q + 15 of in-chunk row rowi.
+template <bool F32>
+__device__ inline void load_q16_b(rsrc_t r, int rowi, int q, typename Prec<F32>::frag v[2]) {
+    constexpr int es = F32 ? 4 : 2;
+    v[0] = bload_frag<F32>(r, rowi * row_bytes<F32>() + 16 * q * es);
+    v[1] = bload_frag<F32>(r, rowi * row_bytes<F32>() + (16 * q + 8) * es);
+}
+
 // This lane's projection operand of one token row: K positions 32 s + 8 g .. +7.
 template <bool F32>
 __device__ inline void load_row_raw(const void* X, size_t row, bool valid, int g,
@@ -82,30 +150,31 @@ __device__ inline void load_row_raw(const void* X, size_t row, bool valid, int g
         x[s] = valid ? *reinterpret_cast<const typename Prec<F32>::frag*>(p + 32 * s) : zero_frag<F32>();
 }
 
-// 1 / max(|x|, eps) of the row held by load_row_raw (same in all four lane groups).
+// 1 / max(|x|, eps) of the row held by load_row_b / load_row_raw (same in all
+// four lane groups): the sum of squares (bf16: two-element dot products, exact
+// products, float32 sums) and one hardware reciprocal square root of
+// max(|x|^2, eps^2).
 template <bool F32>
-__device__ inline void row_norm(const typename Prec<F32>::frag x[2], float& inv, float& nrm) {
+__device__ inline float row_inv_norm(const typename Prec<F32>::frag x[2]) {
     float ss = 0.f;
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int s = 0; s < 2; ++s) {
+        if constexpr (F32) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float f = (float)x[s][j];
-            ss += f * f;
+            for (int j = 0; j < 8; ++j) ss += x[s][j] * x[s][j];
+        } else {
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x2 p = {x[s][2 * j], x[s][2 * j + 1]};
+                ss = __builtin_amdgcn_fdot2_f32_bf16(p, p, ss, false);
+            }
         }
+    }
     ss = sum_groups(ss);
-    nrm = sqrtf(ss);
-    inv = rcp_(fmaxf(nrm, NORM_EPS));
+    return __builtin_amdgcn_rsqf(fmaxf(ss, NORM_EPS * NORM_EPS));
 }
 
-// 16 consecutive values (columns 16 q .. 16 q + 15 of a [*, 64] row).
-template <bool F32>
-__device__ inline void load_q16_raw(const void* X, size_t off, bool ok, typename Prec<F32>::frag v[2]) {
-    using T = typename In<F32>::T;
-    const T* p = reinterpret_cast<const T*>(X) + off;
-    v[0] = ok ? *reinterpret_cast<const typename Prec<F32>::frag*>(p) : zero_frag<F32>();
-    v[1] = ok ? *reinterpret_cast<const typename Prec<F32>::frag*>(p + 8) : zero_frag<F32>();
-}
 
 template <bool F32>
 __device__ inline float q16_at(const typename Prec<F32>::frag v[2], int c) {
@@ -182,17 +251,40 @@ struct Planes {
     typename Prec<C::F32>::uvec u[C::TPB];
 };
 
+// Chunk-local view of one side's plane cache: the u rows and the inverse
+// norms of the chunk's tokens (no cache: every access out of range).
+struct PlaneRows {
+    rsrc_t u, inv;
+};
+
 template <class C>
-__device__ inline void load_planes(const PlaneCache& pc, size_t row, bool valid, int fb, int g, Planes<C>& p) {
-    using U = typename Prec<C::F32>::uvec;
-    const typename Prec<C::F32>::ucache* base = reinterpret_cast<const typename Prec<C::F32>::ucache*>(pc.u);
+__device__ inline PlaneRows plane_rows(const PlaneCache& pc, size_t row0, int64_t nrows) {
+    constexpr int ub = C::NPL * (int)sizeof(typename Prec<C::F32>::ucache);
+    return PlaneRows{rows_rsrc(pc.u, row0, pc.u ? nrows : 0, ub), rows_rsrc(pc.inv, row0, pc.inv ? nrows : 0, 4)};
+}
+
+// Byte offset of the u values of projection tile t, lane group g, in-chunk row rowi.
+template <class C>
+__device__ inline int u_offset(int rowi, int t, int g) {
+    constexpr int us = (int)sizeof(typename Prec<C::F32>::ucache);
+    return (rowi * C::NPL + 16 * t + 4 * g) * us;
+}
+
+template <class C>
+__device__ inline void load_planes(const PlaneRows& pr, int rowi, int fb, int g, Planes<C>& p) {
 #pragma unroll
     for (int tb = 0; tb < C::TPB; ++tb) {
-        const size_t off = row * C::NPL + 16 * (fb * C::TPB + tb) + 4 * g;
-        U v = {};
-        if (valid) v = *reinterpret_cast<const U*>(base + off);
-        p.u[tb] = v;
+        const int off = u_offset<C>(rowi, fb * C::TPB + tb, g);
+        if constexpr (C::F32) p.u[tb] = __builtin_bit_cast(f32x4, bload128(pr.u, off));
+        else p.u[tb] = __builtin_bit_cast(f16x4, bload64(pr.u, off));
     }
+}
+
+template <class C>
+__device__ inline void store_u(const PlaneRows& pr, int rowi, int t, int g, const typename Prec<C::F32>::uvec& uq) {
+    const int off = u_offset<C>(rowi, t, g);
+    if constexpr (C::F32) bstore128(pr.u, off, __builtin_bit_cast(u32x4, uq));
+    else bstore64(pr.u, off, __builtin_bit_cast(u32x2, uq));
 }
 
 // Write the value tile of the 64 tokens (this thread: row th/4, quarter th%4)
@@ -403,14 +495,14 @@ __device__ inline void emit_tile(int tb, int w, int ln, int g, const float phi[C
 // Project the own 16-token tile for the tiles of feature block fb and write
 // the features to the token-row tile `rows` (if set); when KEEP,
 // also return the lane's operands (one per chunk of the block) in phi_frag.
-// With `out` set, the plane values of valid tokens are stored there (row
-// `row`) for later passes.
+// With `store` set, the plane values are stored to `out` (in-chunk row rowi;
+// rows past the chunk are dropped) for later passes.
 template <class C, bool KEEP>
 __device__ inline void block_features(const WSrc<C>& wsrc, int fb, int lane, int w, int ln, int g,
                                       const typename Prec<C::F32>::frag xf[2], float inv, bool valid, float beta,
                                       int L, typename Prec<C::F32>::elem* rows /* [64][ROWF] or null */,
-                                      typename Prec<C::F32>::frag (&phi_frag)[C::FBK], const PlaneCache* out,
-                                      size_t row) {
+                                      typename Prec<C::F32>::frag (&phi_frag)[C::FBK], const PlaneRows& out,
+                                      bool store, int rowi) {
 #pragma unroll
     for (int tb = 0; tb < C::TPB; ++tb) {
         const int t = fb * C::TPB + tb;
@@ -422,11 +514,7 @@ __device__ inline void block_features(const WSrc<C>& wsrc, int fb, int lane, int
         const typename Prec<C::F32>::uvec uq = round_u<C::F32>(u);
         planes_from_u<C::F32>(uq, beta, sg, gu);
         features_from_planes<C>(t, g, sg, L, valid, phi);
-        if (out && valid) {
-            const size_t off = row * C::NPL + 16 * t + 4 * g;
-            *reinterpret_cast<typename Prec<C::F32>::uvec*>(reinterpret_cast<typename Prec<C::F32>::ucache*>(out->u) +
-                                                            off) = uq;
-        }
+        if (store) store_u<C>(out, rowi, t, g, uq);
         emit_tile<C, KEEP>(tb, w, ln, g, phi, rows, phi_frag);
     }
 }
@@ -511,7 +599,14 @@ __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
     zero_pads<C>(s_zr, nullptr);
     __syncthreads();   // W' and the padding are written by all waves, read by each
     const WSrc<C> wsrc{s_w, reinterpret_cast<const elem*>(a.W), a.L};
-    const PlaneCache* pc_out = (!CACHED && a.pc.u) ? &a.pc : nullptr;
+    const int64_t nrows = seg1 - seg0;
+    const size_t row0 = base + seg0;
+    const rsrc_t rX = rows_rsrc(CACHED ? nullptr : a.Xb, row0, nrows, row_bytes<C::F32>());
+    const rsrc_t rZ = rows_rsrc(a.Z, row0, nrows, row_bytes<C::F32>());
+    const rsrc_t rD = rows_rsrc(CACHED ? a.Dv : nullptr, row0, nrows, 4);
+    const rsrc_t rE = rows_rsrc(CACHED ? a.Ev : nullptr, row0, nrows, 4);
+    const PlaneRows pr = plane_rows<C>(a.pc, row0, nrows);
+    const bool u_out = !CACHED && a.pc.u;
 
     f32x4 Macc[C::NKC * 2], Zacc[C::NOWN * 2];
 #pragma unroll
@@ -528,33 +623,29 @@ __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
         return (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
     };
     auto issue = [&](int it2) {
-        const int64_t t0 = seg0 + (int64_t)it2 * TB;
-        const int nv = nv_of(it2);
-        if (!CACHED) load_row_raw<C::F32>(a.Xb, base + t0 + my, my < nv, g, nx);
-        const bool ok = tr < nv;
-        load_q16_raw<C::F32>(a.Z, (base + t0 + tr) * DH + 16 * tq, ok, nz);
-        if (CACHED && ok) {
-            nd = a.Dv[base + t0 + tr];
-            ne = a.Ev[base + t0 + tr];
+        const int r0 = it2 * TB;
+        if (!CACHED) load_row_b<C::F32>(rX, r0 + my, g, nx);
+        load_q16_b<C::F32>(rZ, r0 + tr, tq, nz);
+        if (CACHED) {
+            nd = bload_f32(rD, (r0 + tr) * 4);
+            ne = bload_f32(rE, (r0 + tr) * 4);
         }
     };
-    auto issue_planes = [&](int it2, int fb2) {
-        load_planes<C>(a.pc, base + seg0 + (int64_t)it2 * TB + my, my < nv_of(it2), fb2, g, pn);
-    };
+    auto issue_planes = [&](int it2, int fb2) { load_planes<C>(pr, it2 * TB + my, fb2, g, pn); };
     issue(0);
     if (CACHED) issue_planes(0, 0);
     for (int it = 0; it < nsub; ++it) {
         const int64_t t0 = seg0 + (int64_t)it * TB;
         const int nv = nv_of(it);
         const bool valid = my < nv;
-        const size_t row = base + t0 + my;
+        const int rowi = it * TB + my;
         frag xf[2] = {nx[0], nx[1]}, zr[2] = {nz[0], nz[1]};
         const float dz = nd, ez = ne;
         if (it + 1 < nsub) issue(it + 1);
-        float inv = 0.f, nrm;
+        float inv = 0.f;
         if (!CACHED) {
-            row_norm<C::F32>(xf, inv, nrm);
-            if (pc_out && valid && g == 0) pc_out->inv[row] = inv;
+            inv = row_inv_norm<C::F32>(xf);
+            if (u_out && g == 0) bstore_f32(pr.inv, rowi * 4, inv);
         }
         const bool ok = tr < nv;
         if (!CACHED) write_aug<C>(zr, 1.f, ok ? 1.f : 0.f, s_zr);
@@ -570,7 +661,7 @@ __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
                 block_features_cached<C, false>(pl, fb, w, ln, g, valid, a.L, a.beta, s_rows, unused, us, ug);
             } else {
                 block_features<C, false>(wsrc, fb, lane, w, ln, g, xf, inv, valid, a.beta, a.L, s_rows, unused,
-                                         pc_out, row);
+                                         pr, u_out, rowi);
             }
             __syncthreads();
             sketch_update<C>(fb, w, ln, g, s_rows, s_zr, Macc, Zacc);
@@ -788,61 +879,52 @@ __device__ inline void intra_operand(const typename Prec<C::F32>::elem* s_zr, co
 // inv = 1 / max(|x|, eps) tells which case holds). dX[dt] holds columns
 // 16 dt + 4 g .. +3.
 template <class C>
-__device__ inline void store_dx(const void* X, void* out, size_t row, bool valid, int g, float inv,
-                                const f32x4 dX[4]) {
-    using T = typename In<C::F32>::T;
+__device__ inline void store_dx(rsrc_t rX, rsrc_t rOut, int rowi, int g, float inv, const f32x4 dX[4]) {
+    constexpr int es = C::F32 ? 4 : 2;
     float xv[4][4];
     float radial = 0.f;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-        const size_t off = row * DH + 16 * dt + 4 * g;
+        const int off = rowi * row_bytes<C::F32>() + (16 * dt + 4 * g) * es;
         if constexpr (C::F32) {
-            f32x4 v = {0.f, 0.f, 0.f, 0.f};
-            if (valid) v = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(X) + off);
+            const f32x4 v = __builtin_bit_cast(f32x4, bload128(rX, off));
 #pragma unroll
             for (int i = 0; i < 4; ++i) xv[dt][i] = v[i];
         } else {
-            bf16x4 v = {};
-            if (valid) v = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(X) + off);
+            const bf16x4 v = __builtin_bit_cast(bf16x4, bload64(rX, off));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xv[dt][i] = valid ? (float)v[i] : 0.f;
+            for (int i = 0; i < 4; ++i) xv[dt][i] = (float)v[i];
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) radial += xv[dt][i] * inv * dX[dt][i];
     }
     radial = sum_groups(radial);
     const bool tangent = inv < rcp_(NORM_EPS);
-    if (valid) {
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-            f32x4 o;
+    for (int dt = 0; dt < 4; ++dt) {
+        f32x4 o;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = (tangent ? dX[dt][i] - xv[dt][i] * inv * radial : dX[dt][i]) * inv;
-            T* dst = reinterpret_cast<T*>(out) + row * DH + 16 * dt + 4 * g;
-            if constexpr (C::F32) {
-                *reinterpret_cast<f32x4*>(dst) = o;
-            } else {
-                bf16x4 ob;
+        for (int i = 0; i < 4; ++i) o[i] = (tangent ? dX[dt][i] - xv[dt][i] * inv * radial : dX[dt][i]) * inv;
+        const int off = rowi * row_bytes<C::F32>() + (16 * dt + 4 * g) * es;
+        if constexpr (C::F32) {
+            bstore128(rOut, off, __builtin_bit_cast(u32x4, o));
+        } else {
+            bf16x4 ob;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) ob[i] = (__bf16)o[i];
-                *reinterpret_cast<bf16x4*>(dst) = ob;
-            }
+            for (int i = 0; i < 4; ++i) ob[i] = (__bf16)o[i];
+            bstore64(rOut, off, __builtin_bit_cast(u32x2, ob));
         }
     }
 }
 
-// Store the staged [64][ROWD] tile (thread: row tr, quarter tq) to rows t0.. of out.
+// Store the staged [64][ROWD] tile (thread: row tr, quarter tq) to in-chunk
+// row rowi of the output (rows past the chunk are dropped).
 template <class C>
-__device__ inline void store_stage(void* out, size_t row0, int tr, int tq, bool tok,
-                                   const typename Prec<C::F32>::elem* s_stage) {
-    using T = typename In<C::F32>::T;
-    using frag = typename Prec<C::F32>::frag;
-    if (tok) {
-        T* o = reinterpret_cast<T*>(out) + (row0 + tr) * DH + 16 * tq;
-        const typename Prec<C::F32>::elem* src = s_stage + tr * C::ROWD + 16 * tq;
-        *reinterpret_cast<frag*>(o) = ld_frag<C::F32>(src);
-        *reinterpret_cast<frag*>(o + 8) = ld_frag<C::F32>(src + 8);
-    }
+__device__ inline void store_stage(rsrc_t out, int rowi, int tr, int tq, const typename Prec<C::F32>::elem* s_stage) {
+    constexpr int es = C::F32 ? 4 : 2;
+    const typename Prec<C::F32>::elem* src = s_stage + tr * C::ROWD + 16 * tq;
+    bstore_frag<C::F32>(out, rowi * row_bytes<C::F32>() + 16 * tq * es, ld_frag<C::F32>(src));
+    bstore_frag<C::F32>(out, rowi * row_bytes<C::F32>() + (16 * tq + 8) * es, ld_frag<C::F32>(src + 8));
 }
 
 // LDS budget: W' is staged when it fits next to the tiles at the target
@@ -915,7 +997,14 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
     zero_pads<C>(s_zr, nullptr);
     __syncthreads();   // W' and the padding are written by all waves, read by each
     const WSrc<C> wsrc{s_w, W, a.L};
-    const PlaneCache* pc_out = a.ca.u ? &a.ca : nullptr;   // the queries' plane values for the backward
+    const int64_t nrows = seg1 - seg0;
+    const size_t row0 = base + seg0;
+    const rsrc_t rXa = rows_rsrc(a.Xa, row0, nrows, row_bytes<C::F32>());
+    const rsrc_t rZ = rows_rsrc(a.Zsrc, row0, nrows, row_bytes<C::F32>());
+    const rsrc_t rO = rows_rsrc(a.out0, row0, nrows, row_bytes<C::F32>());
+    const rsrc_t rD = rows_rsrc(a.Dv, row0, nrows, 4);
+    const PlaneRows pra = plane_rows<C>(a.ca, row0, nrows), prb = plane_rows<C>(a.cb, row0, nrows);
+    const bool u_out = a.ca.u != nullptr;   // keep the queries' plane values for the backward
 
     f32x4 Macc[C::NKC * 2], Zacc[C::NOWN * 2];
     load_state<C>(a.state + bh * a.state_bh_stride + c * a.state_chunk_stride, w, ln, g, Macc, Zacc);
@@ -931,14 +1020,10 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
         return (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
     };
     auto issue = [&](int it2) {
-        const int64_t t0 = seg0 + (int64_t)it2 * TB;
-        const int nv = nv_of(it2);
-        load_row_raw<C::F32>(a.Xa, base + t0 + my, my < nv, g, n_xa);
-        load_q16_raw<C::F32>(a.Zsrc, (base + t0 + tr) * DH + 16 * tq, tr < nv, n_z);
+        load_row_b<C::F32>(rXa, it2 * TB + my, g, n_xa);
+        load_q16_b<C::F32>(rZ, it2 * TB + tr, tq, n_z);
     };
-    auto issue_planes = [&](int it2, int fb2) {
-        load_planes<C>(a.cb, base + seg0 + (int64_t)it2 * TB + my, my < nv_of(it2), fb2, g, pn);
-    };
+    auto issue_planes = [&](int it2, int fb2) { load_planes<C>(prb, it2 * TB + my, fb2, g, pn); };
     issue(0);
     if (causal) issue_planes(0, 0);
 
@@ -947,13 +1032,12 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
         const int nv = nv_of(it);
         const bool valid = my < nv;
         const bool tok = tr < nv;
-        const size_t row = base + t0 + my;
+        const int rowi = it * TB + my;
         frag xa[2] = {n_xa[0], n_xa[1]}, zr[2] = {n_z[0], n_z[1]};
         if (it + 1 < nsub) issue(it + 1);
 
-        float inv_a, nrm_a;
-        row_norm<C::F32>(xa, inv_a, nrm_a);
-        if (pc_out && valid && g == 0) pc_out->inv[row] = inv_a;
+        const float inv_a = row_inv_norm<C::F32>(xa);
+        if (u_out && g == 0) bstore_f32(pra.inv, rowi * 4, inv_a);
         write_aug<C>(zr, 1.f, tok ? 1.f : 0.f, s_zr);
 
         f32x4 Y[4], Dacc[4], Sc[4];
@@ -973,8 +1057,8 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
                 if (fb + 1 < C::NBLK) issue_planes(it, fb + 1);
                 else if (it + 1 < nsub) issue_planes(it + 1, 0);
             }
-            block_features<C, true>(wsrc, fb, lane, w, ln, g, xa, inv_a, valid, a.beta, a.L, rows_b, phiA, pc_out,
-                                    row);
+            block_features<C, true>(wsrc, fb, lane, w, ln, g, xa, inv_a, valid, a.beta, a.L, rows_b, phiA, pra,
+                                    u_out, rowi);
             if (causal) {
                 float us[C::TPB][4], ug[C::TPB][4];
                 block_features_cached<C, false>(pl, fb, w, ln, g, valid, a.L, a.beta, brow_b, unused, us, ug);
@@ -1055,13 +1139,13 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
                 if (causal) d += f_Dint[r];
                 s_stage[r * C::ROWD + 16 * w + ln] = to_elem<C::F32>(Y[at][i] * rcp_(d));
             }
-        if (a.Dv && tq == 0 && tok) {
+        if (tq == 0) {
             float d = f_Dpart[tr] + f_Dpart[TB + tr] + f_Dpart[2 * TB + tr] + f_Dpart[3 * TB + tr];
             if (causal) d += f_Dint[tr];
-            a.Dv[base + t0 + tr] = d;
+            bstore_f32(rD, (it * TB + tr) * 4, d);
         }
         __syncthreads();
-        store_stage<C>(a.out0, base + t0, tr, tq, tok, s_stage);
+        store_stage<C>(rO, it * TB + tr, tr, tq, s_stage);
         __syncthreads();
     }
 }
@@ -1134,20 +1218,28 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
 
     const int nsub = (int)((seg1 - seg0 + TB - 1) / TB);
     const int my = 16 * w + ln;
+    const int64_t nrows = seg1 - seg0;
+    const size_t row0 = base + seg0;
+    const rsrc_t rZ = rows_rsrc(a.Zsrc, row0, nrows, row_bytes<C::F32>());
+    const rsrc_t rY = rows_rsrc(a.Ysrc, row0, nrows, row_bytes<C::F32>());
+    const rsrc_t rOs = rows_rsrc(a.Osrc, row0, nrows, row_bytes<C::F32>());
+    const rsrc_t rXa = rows_rsrc(a.Xa, row0, nrows, row_bytes<C::F32>());
+    const rsrc_t rOut = rows_rsrc(a.out0, row0, nrows, row_bytes<C::F32>());
+    const rsrc_t rD = rows_rsrc(a.Dv, row0, nrows, 4);
+    const rsrc_t rE = rows_rsrc(a.Ev, row0, nrows, 4);
+    const PlaneRows pra = plane_rows<C>(a.ca, row0, nrows), prb = plane_rows<C>(a.cb, row0, nrows);
 
-    // the plane values of queries (with 2 beta (1 - u^2)) and keys are loaded
-    // one feature block ahead; the value, gradient and output rows at the top
-    // of their sub-block (register budget)
+    // the plane values of queries and keys are loaded one feature block ahead;
+    // the value, gradient and output rows at the top of their sub-block
+    // (register budget)
     Planes<C> pa, pb;
     auto nv_of = [&](int it2) {
         const int64_t t0 = seg0 + (int64_t)it2 * TB;
         return (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
     };
     auto issue_planes = [&](int it2, int fb2) {
-        const size_t r2 = base + seg0 + (int64_t)it2 * TB + my;
-        const bool v2 = my < nv_of(it2);
-        load_planes<C>(a.ca, r2, v2, fb2, g, pa);
-        if (causal) load_planes<C>(a.cb, r2, v2, fb2, g, pb);
+        load_planes<C>(pra, it2 * TB + my, fb2, g, pa);
+        if (causal) load_planes<C>(prb, it2 * TB + my, fb2, g, pb);
     };
     issue_planes(0, 0);
 
@@ -1155,14 +1247,14 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
         const int64_t t0 = seg0 + (int64_t)it * TB;
         const int nv = nv_of(it);
         const bool valid = my < nv;
-        const size_t row = base + t0 + my;
+        const int rowi = it * TB + my, rowt = it * TB + tr;
         const bool tok = tr < nv;
         frag zr[2], yr[2], orow[2];
-        if (causal) load_q16_raw<C::F32>(a.Zsrc, (base + t0 + tr) * DH + 16 * tq, tok, zr);
-        load_q16_raw<C::F32>(a.Ysrc, (base + t0 + tr) * DH + 16 * tq, tok, yr);
-        load_q16_raw<C::F32>(a.Osrc, (base + t0 + tr) * DH + 16 * tq, tok, orow);
-        const float dd = tok ? a.Dv[base + t0 + tr] : 1.f;
-        const float inv_a = valid ? a.ca.inv[row] : 1.f;
+        if (causal) load_q16_b<C::F32>(rZ, rowt, tq, zr);
+        load_q16_b<C::F32>(rY, rowt, tq, yr);
+        load_q16_b<C::F32>(rOs, rowt, tq, orow);
+        const float dd = tok ? bload_f32(rD, rowt * 4) : 1.f;
+        const float inv_a = valid ? bload_f32(pra.inv, rowi * 4) : 1.f;
         const bool first = t0 == 0;   // the sub-block that starts the sequence
         if (causal) write_aug<C>(zr, 1.f, tok ? 1.f : 0.f, s_zr);
         // y = [dO / D | e], e = -<dO, O> / D; this thread holds 16 columns of row tr
@@ -1194,7 +1286,7 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
                 const elem eh = to_elem<C::F32>(e);
                 s_yr[tr * C::ROWE + 64] = eh;
                 if (LD::YLO && first) s_ylo[tr * C::ROWE + 64] = to_elem<C::F32>(e - elem_f<C::F32>(eh));
-                if (tok) a.Ev[base + t0 + tr] = e;
+                bstore_f32(rE, rowt * 4, e);
             }
         }
         __syncthreads();
@@ -1251,7 +1343,7 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
             if (causal) sketch_update<C>(fb, w, ln, g, cols_b, s_zr, Macc, Zacc);
         }
         __syncthreads();   // the next sub-block rewrites the y and z rows
-        store_dx<C>(a.Xa, a.out0, row, valid, g, inv_a, dX);
+        store_dx<C>(rXa, rOut, rowi, g, inv_a, dX);
     }
 }
 
@@ -1362,25 +1454,30 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
         const int64_t t0 = t0_of(it2);
         return (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
     };
+    const int64_t nrows = seg1 - seg0;
+    const size_t row0 = base + seg0;
+    const rsrc_t rZ = rows_rsrc(a.Zsrc, row0, nrows, row_bytes<C::F32>());
+    const rsrc_t rY = rows_rsrc(a.Ysrc, row0, nrows, row_bytes<C::F32>());
+    const rsrc_t rXa = rows_rsrc(a.Xa, row0, nrows, row_bytes<C::F32>());
+    const rsrc_t rOut0 = rows_rsrc(a.out0, row0, nrows, row_bytes<C::F32>());
+    const rsrc_t rOut1 = rows_rsrc(a.out1, row0, nrows, row_bytes<C::F32>());
+    const rsrc_t rD = rows_rsrc(a.Dv, row0, nrows, 4);
+    const rsrc_t rE = rows_rsrc(a.Ev, row0, nrows, 4);
+    const PlaneRows pra = plane_rows<C>(a.ca, row0, nrows), prb = plane_rows<C>(a.cb, row0, nrows);
+    auto r0_of = [&](int it2) { return (nsub - 1 - it2) * TB; };   // first in-chunk row of a sub-block
     auto issue = [&](int it2) {
-        const int64_t t0 = t0_of(it2);
-        const int nv = nv_of(it2);
-        const bool ok = tr < nv;
-        if (DK && my < nv) n_inv = a.ca.inv[base + t0 + my];
+        const int r0 = r0_of(it2);
+        if (DK) n_inv = my < nv_of(it2) ? bload_f32(pra.inv, (r0 + my) * 4) : 1.f;
         if (causal) {
-            load_q16_raw<C::F32>(a.Zsrc, (base + t0 + tr) * DH + 16 * tq, ok, n_z);
-            if (ok) {
-                n_d = a.Dv[base + t0 + tr];
-                n_e = a.Ev[base + t0 + tr];
-            }
+            load_q16_b<C::F32>(rZ, r0 + tr, tq, n_z);
+            n_d = bload_f32(rD, (r0 + tr) * 4);
+            n_e = bload_f32(rE, (r0 + tr) * 4);
         }
-        if (DK) load_q16_raw<C::F32>(a.Ysrc, (base + t0 + tr) * DH + 16 * tq, ok, n_y);
+        if (DK) load_q16_b<C::F32>(rY, r0 + tr, tq, n_y);
     };
     auto issue_planes = [&](int it2, int fb2) {
-        const size_t r2 = base + t0_of(it2) + my;
-        const bool v2 = my < nv_of(it2);
-        load_planes<C>(a.ca, r2, v2, fb2, g, pa);
-        if (causal) load_planes<C>(a.cb, r2, v2, fb2, g, pb);
+        load_planes<C>(pra, r0_of(it2) + my, fb2, g, pa);
+        if (causal) load_planes<C>(prb, r0_of(it2) + my, fb2, g, pb);
     };
     if (PREFETCH) issue(0);
     issue_planes(0, 0);
@@ -1389,7 +1486,6 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
         const int64_t t0 = t0_of(it);
         const int nv = nv_of(it);
         const bool valid = my < nv;
-        const size_t row = base + t0 + my;
         const bool tok = tr < nv;
         if (!PREFETCH) issue(it);
         frag zr[2] = {n_z[0], n_z[1]}, yr[2] = {n_y[0], n_y[1]};
@@ -1523,9 +1619,9 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
                 for (int i = 0; i < 4; ++i)
                     s_stage[(16 * at + 4 * g + i) * C::ROWD + 16 * w + ln] = to_elem<C::F32>(Y[at][i]);
             __syncthreads();
-            store_stage<C>(a.out1, base + t0, tr, tq, tok, s_stage);
+            store_stage<C>(rOut1, r0_of(it) + tr, tr, tq, s_stage);
         }
-        if constexpr (DK) store_dx<C>(a.Xa, a.out0, row, valid, g, inv_a, dX);
+        if constexpr (DK) store_dx<C>(rXa, rOut0, r0_of(it) + my, g, inv_a, dX);
     }
 }
 
@@ -1545,9 +1641,8 @@ __global__ __launch_bounds__(NT) void k_hash(const void* X, const void* Wv, int6
     const bool valid = r < rows;
     const elem* W = reinterpret_cast<const elem*>(Wv);
     frag xf[2];
-    float inv, nrm;
     load_row_raw<C::F32>(X, valid ? (size_t)r : 0, valid, g, xf);
-    row_norm<C::F32>(xf, inv, nrm);
+    const float inv = row_inv_norm<C::F32>(xf);
     unsigned int nz = 0;
 #pragma unroll
     for (int t = 0; t < C::MT; ++t) {
