@@ -851,17 +851,16 @@ __device__ inline void intra_operand(const typename Prec<C::F32>::elem* s_zr, co
     for (int s = 0; s < 3; ++s) yf[s] = ld_frag<C::F32>(s_yr + my * C::ROWE + 32 * s + 8 * g);
 #pragma unroll
     for (int bt = 0; bt < 4; ++bt) {
+        // every tile is formed (the mask below keeps the visible entries), so
+        // all waves run the same instruction stream
         Cc[bt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const bool vis = REV ? (bt >= w) : (bt <= w);
-        if (vis) {
 #pragma unroll
-            for (int s = 0; s < 3; ++s) {
-                const frag zf = ld_frag<C::F32>(s_zr + (16 * bt + ln) * C::ROWE + 32 * s + 8 * g);
-                Cc[bt] = mma(zf, yf[s], Cc[bt]);
-                if (YLO && lo) Cc[bt] = mma(zf, ld_frag<C::F32>(s_ylo + my * C::ROWE + 32 * s + 8 * g), Cc[bt]);
-                if (ZLO && lo)
-                    Cc[bt] = mma(ld_frag<C::F32>(s_zlo + (16 * bt + ln) * C::ROWE + 32 * s + 8 * g), yf[s], Cc[bt]);
-            }
+        for (int s = 0; s < 3; ++s) {
+            const frag zf = ld_frag<C::F32>(s_zr + (16 * bt + ln) * C::ROWE + 32 * s + 8 * g);
+            Cc[bt] = mma(zf, yf[s], Cc[bt]);
+            if (YLO && lo) Cc[bt] = mma(zf, ld_frag<C::F32>(s_ylo + my * C::ROWE + 32 * s + 8 * g), Cc[bt]);
+            if (ZLO && lo)
+                Cc[bt] = mma(ld_frag<C::F32>(s_zlo + (16 * bt + ln) * C::ROWE + 32 * s + 8 * g), yf[s], Cc[bt]);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1067,12 +1066,10 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
             if (causal) {
 #pragma unroll
                 for (int bt = 0; bt < 4; ++bt) {
-                    if (bt <= w) {
 #pragma unroll
-                        for (int kcl = 0; kcl < C::FBK; ++kcl)
-                            Sc[bt] = mma(ld_frag<C::F32>(brow_b + (16 * bt + ln) * C::ROWF + 32 * kcl + 8 * g),
-                                         phiA[kcl], Sc[bt]);
-                    }
+                    for (int kcl = 0; kcl < C::FBK; ++kcl)
+                        Sc[bt] = mma(ld_frag<C::F32>(brow_b + (16 * bt + ln) * C::ROWF + 32 * kcl + 8 * g),
+                                     phiA[kcl], Sc[bt]);
                 }
             }
 #pragma unroll
@@ -1545,12 +1542,10 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
                 if (causal) {
 #pragma unroll
                     for (int bt = 0; bt < 4; ++bt) {
-                        if (bt >= w) {
 #pragma unroll
-                            for (int kcl = 0; kcl < C::FBK; ++kcl)
-                                Sc[bt] = mma(ld_frag<C::F32>(brow_b + (16 * bt + ln) * C::ROWF + 32 * kcl + 8 * g),
-                                             phiA[kcl], Sc[bt]);
-                        }
+                        for (int kcl = 0; kcl < C::FBK; ++kcl)
+                            Sc[bt] = mma(ld_frag<C::F32>(brow_b + (16 * bt + ln) * C::ROWF + 32 * kcl + 8 * g),
+                                         phiA[kcl], Sc[bt]);
                     }
                 }
                 // dV readout of the value columns of this wave (before this block's update)
