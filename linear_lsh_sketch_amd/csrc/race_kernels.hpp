@@ -71,6 +71,11 @@ struct In {
 // Global loads are issued one sub-block ahead ("raw" registers) and consumed
 // by the next iteration, so their latency overlaps the current sub-block.
 
+// Row stride of value tiles [z | mass] read only through transpose reads:
+// 64 values, the mass and 15 zeros (a stride the transpose reads hit without
+// LDS bank conflicts).
+constexpr int ZV = 80;
+
 // Per-chunk tensor access through buffer resources: a workgroup addresses the
 // rows [row0, row0 + nrows) of its chunk with 32-bit byte offsets; loads of
 // rows past the end return zeros and stores there are dropped, so the ragged
@@ -291,7 +296,7 @@ __device__ inline void store_u(const PlaneRows& pr, int rowi, int t, int g, cons
 // into Zrow [64][ROWE] (token rows): z = [x * scale | mass]. With Zlo set, also
 // the rows of the rounding residual z - elem(z) (so that hi + lo carries z to
 // float32 precision). Columns 65.. stay zero from zero_pads.
-template <class C>
+template <class C, int ZS = C::ROWE>
 __device__ inline void write_aug(const typename Prec<C::F32>::frag zr[2], float scale, float mass,
                                  typename Prec<C::F32>::elem* Zrow, typename Prec<C::F32>::elem* Zlo = nullptr) {
     const int th = threadIdx.x, r = th >> 2, q = th & 3;
@@ -299,10 +304,10 @@ __device__ inline void write_aug(const typename Prec<C::F32>::frag zr[2], float 
 #pragma unroll
     for (int c = 0; c < 16; ++c) v[c] = q16_at<C::F32>(zr, c) * scale;
     const typename Prec<C::F32>::frag h0 = pack8<C::F32>(v), h1 = pack8<C::F32>(v + 8);
-    st_frag<C::F32>(Zrow + r * C::ROWE + 16 * q, h0);
-    st_frag<C::F32>(Zrow + r * C::ROWE + 16 * q + 8, h1);
+    st_frag<C::F32>(Zrow + r * ZS + 16 * q, h0);
+    st_frag<C::F32>(Zrow + r * ZS + 16 * q + 8, h1);
     const typename Prec<C::F32>::elem mh = to_elem<C::F32>(mass);
-    if (q == 0) Zrow[r * C::ROWE + 64] = mh;
+    if (q == 0) Zrow[r * ZS + 64] = mh;
     if (Zlo) {
         float lo[16];
 #pragma unroll
@@ -310,19 +315,21 @@ __device__ inline void write_aug(const typename Prec<C::F32>::frag zr[2], float 
             lo[c] = v[c] - elem_f<C::F32>(h0[c]);
             lo[8 + c] = v[8 + c] - elem_f<C::F32>(h1[c]);
         }
-        st_frag<C::F32>(Zlo + r * C::ROWE + 16 * q, pack8<C::F32>(lo));
-        st_frag<C::F32>(Zlo + r * C::ROWE + 16 * q + 8, pack8<C::F32>(lo + 8));
-        if (q == 0) Zlo[r * C::ROWE + 64] = to_elem<C::F32>(mass - elem_f<C::F32>(mh));
+        st_frag<C::F32>(Zlo + r * ZS + 16 * q, pack8<C::F32>(lo));
+        st_frag<C::F32>(Zlo + r * ZS + 16 * q + 8, pack8<C::F32>(lo + 8));
+        if (q == 0) Zlo[r * ZS + 64] = to_elem<C::F32>(mass - elem_f<C::F32>(mh));
     }
 }
 
-// Zero the constant padding (columns 65..95) of token-row value tiles.
-template <class C>
+// Zero the constant padding (columns 65 .. min(ZS, 96) - 1) of token-row value
+// tiles of row stride ZS.
+template <class C, int ZS = C::ROWE>
 __device__ inline void zero_pads(typename Prec<C::F32>::elem* rows_a, typename Prec<C::F32>::elem* rows_b) {
+    constexpr int NZ = (ZS < EA ? ZS : EA) - 65;
     if (rows_a)
-        for (int idx = threadIdx.x; idx < 31 * TB; idx += NT) rows_a[(idx / 31) * C::ROWE + 65 + idx % 31] = to_elem<C::F32>(0.f);
+        for (int idx = threadIdx.x; idx < NZ * TB; idx += NT) rows_a[(idx / NZ) * ZS + 65 + idx % NZ] = to_elem<C::F32>(0.f);
     if (rows_b)
-        for (int idx = threadIdx.x; idx < 31 * TB; idx += NT) rows_b[(idx / 31) * C::ROWE + 65 + idx % 31] = to_elem<C::F32>(0.f);
+        for (int idx = threadIdx.x; idx < NZ * TB; idx += NT) rows_b[(idx / NZ) * ZS + 65 + idx % NZ] = to_elem<C::F32>(0.f);
 }
 
 // State block of one (bh, chunk): value sums [F][64] then masses [F], float32.
@@ -419,19 +426,19 @@ __device__ inline typename Prec<C::F32>::frag feat_operand(const typename Prec<C
 // positions 32 s + 8 g + j in tok_pos order (as feat_operand). bf16: two LDS
 // transpose reads, lane j of a 16-lane group pointing at columns
 // cb + 4 (j % 4) .. +3 of one token.
-template <class C>
+template <class C, int ZS = C::ROWE>
 __device__ inline typename Prec<C::F32>::frag val_operand(const typename Prec<C::F32>::elem* Zrow, int cb, int s,
                                                          int ln, int g) {
     typename Prec<C::F32>::frag f;
     if constexpr (C::F32) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) f[j] = Zrow[(32 * s + 16 * (j >> 2) + 4 * g + (j & 3)) * C::ROWE + cb + ln];
+        for (int j = 0; j < 8; ++j) f[j] = Zrow[(32 * s + 16 * (j >> 2) + 4 * g + (j & 3)) * ZS + cb + ln];
     } else {
         typedef short s16x4 __attribute__((ext_vector_type(4)));
         typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-        const typename Prec<C::F32>::elem* p = Zrow + (32 * s + 4 * g + (ln >> 2)) * C::ROWE + cb + 4 * (ln & 3);
+        const typename Prec<C::F32>::elem* p = Zrow + (32 * s + 4 * g + (ln >> 2)) * ZS + cb + 4 * (ln & 3);
         const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-        const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 16 * C::ROWE));
+        const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 16 * ZS));
         const bf16x4 ab = __builtin_bit_cast(bf16x4, a), bb = __builtin_bit_cast(bf16x4, b);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -445,14 +452,14 @@ __device__ inline typename Prec<C::F32>::frag val_operand(const typename Prec<C:
 // Sketch update for feature block fb from the b-side features (token-row tile
 // `brow`) and the value tile Zrow: value columns of wave w, then the mass
 // accumulators of the chunk wave w owns in this block.
-template <class C, bool MASS = true>
+template <class C, bool MASS = true, int ZS = C::ROWE>
 __device__ inline void sketch_update(int fb, int w, int ln, int g, const typename Prec<C::F32>::elem* brow,
                                      const typename Prec<C::F32>::elem* Zrow, f32x4 Macc[C::NKC * 2],
                                      f32x4 Zacc[C::NOWN * 2]) {
     using frag = typename Prec<C::F32>::frag;
     frag zt[2];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) zt[s] = val_operand<C>(Zrow, 16 * w, s, ln, g);
+    for (int s = 0; s < 2; ++s) zt[s] = val_operand<C, ZS>(Zrow, 16 * w, s, ln, g);
 #pragma unroll
     for (int kcl = 0; kcl < C::FBK; ++kcl) {
         const int kc = fb * C::FBK + kcl;
@@ -467,7 +474,7 @@ __device__ inline void sketch_update(int fb, int w, int ln, int g, const typenam
     if (MASS && kw >= 0 && kw < C::FBK) {
         frag zm[2];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) zm[s] = val_operand<C>(Zrow, 64, s, ln, g);
+        for (int s = 0; s < 2; ++s) zm[s] = val_operand<C, ZS>(Zrow, 64, s, ln, g);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -565,7 +572,7 @@ template <class C, bool CACHED>
 struct TotLds {
     using elem = typename Prec<C::F32>::elem;
     static constexpr int n_rows = TB * C::ROWF;   // features of the block, token rows
-    static constexpr int n_zr = TB * C::ROWE;     // [z | mass], token rows
+    static constexpr int n_zr = TB * ZV;          // [z | mass], token rows
     static constexpr int n_w = CACHED ? 0 : C::MT * 1024;
     static constexpr int n_elem = n_rows + n_zr + n_w;
     static_assert(n_elem * (int)sizeof(elem) <= 160 * 1024, "LDS budget");
@@ -596,7 +603,7 @@ __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
     const int nsub = (int)((seg1 - seg0 + TB - 1) / TB);
     const int my = 16 * w + ln;
     if (!CACHED) stage_w<C>(reinterpret_cast<const elem*>(a.W), a.L, s_w);
-    zero_pads<C>(s_zr, nullptr);
+    zero_pads<C, ZV>(s_zr, nullptr);
     __syncthreads();   // W' and the padding are written by all waves, read by each
     const WSrc<C> wsrc{s_w, reinterpret_cast<const elem*>(a.W), a.L};
     const int64_t nrows = seg1 - seg0;
@@ -648,8 +655,8 @@ __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
             if (u_out && g == 0) bstore_f32(pr.inv, rowi * 4, inv);
         }
         const bool ok = tr < nv;
-        if (!CACHED) write_aug<C>(zr, 1.f, ok ? 1.f : 0.f, s_zr);
-        else write_aug<C>(zr, ok ? rcp_(dz) : 0.f, ok ? ez : 0.f, s_zr);
+        if (!CACHED) write_aug<C, ZV>(zr, 1.f, ok ? 1.f : 0.f, s_zr);
+        else write_aug<C, ZV>(zr, ok ? rcp_(dz) : 0.f, ok ? ez : 0.f, s_zr);
 #pragma unroll
         for (int fb = 0; fb < C::NBLK; ++fb) {
             frag unused[C::FBK];
@@ -664,7 +671,7 @@ __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
                                          pr, u_out, rowi);
             }
             __syncthreads();
-            sketch_update<C>(fb, w, ln, g, s_rows, s_zr, Macc, Zacc);
+            sketch_update<C, true, ZV>(fb, w, ln, g, s_rows, s_zr, Macc, Zacc);
             __syncthreads();
         }
     }
@@ -950,7 +957,8 @@ struct FwdLds {
     // so one barrier per block separates its writes from its reads.
     static constexpr int n_rows = TB * C::ROWF;                 // a-side features [64][ROWF]
     static constexpr int n_brow = TB * C::ROWF;                 // b-side features [64][ROWF]
-    static constexpr int n_zr = TB * C::ROWE;                   // [z_b | mass], token rows
+    static constexpr int ZS = ZV;                               // value-tile row stride
+    static constexpr int n_zr = TB * ZS;                        // [z_b | mass], token rows
     static constexpr int n_sc = TB * C::ROWT;                   // intra scores [a][b]
     static constexpr int n_stage = TB * C::ROWD;                // O staging (alias of the a-side buffers)
     static_assert(n_stage <= 2 * n_rows, "staging must fit the feature tiles");
@@ -993,7 +1001,7 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
     constexpr bool causal = CAUSAL;
     elem* s_w = LD::WS::on ? lds + LD::o_w : nullptr;
     if (LD::WS::on) stage_w<C>(W, a.L, s_w);
-    zero_pads<C>(s_zr, nullptr);
+    zero_pads<C, ZV>(s_zr, nullptr);
     __syncthreads();   // W' and the padding are written by all waves, read by each
     const WSrc<C> wsrc{s_w, W, a.L};
     const int64_t nrows = seg1 - seg0;
@@ -1037,7 +1045,7 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
 
         const float inv_a = row_inv_norm<C::F32>(xa);
         if (u_out && g == 0) bstore_f32(pra.inv, rowi * 4, inv_a);
-        write_aug<C>(zr, 1.f, tok ? 1.f : 0.f, s_zr);
+        write_aug<C, ZV>(zr, 1.f, tok ? 1.f : 0.f, s_zr);
 
         f32x4 Y[4], Dacc[4], Sc[4];
 #pragma unroll
@@ -1087,7 +1095,7 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
                 for (int at = 0; at < 4; ++at)
                     Dacc[at] = mma(ld_frag<C::F32>(rows_b + (16 * at + ln) * C::ROWF + 32 * kw + 8 * g), zf, Dacc[at]);
             }
-            if (causal) sketch_update<C>(fb, w, ln, g, brow_b, s_zr, Macc, Zacc);
+            if (causal) sketch_update<C, true, ZV>(fb, w, ln, g, brow_b, s_zr, Macc, Zacc);
         }
         // intra-sub-block term: scores of visible keys b <= a. The value
         // readout multiplies the scores rounded to the operand type, so the
@@ -1121,7 +1129,7 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
         if (causal) {
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                const frag zt = val_operand<C>(s_zr, 16 * w, s, ln, g);
+                const frag zt = val_operand<C, LD::ZS>(s_zr, 16 * w, s, ln, g);
 #pragma unroll
                 for (int at = 0; at < 4; ++at)
                     Y[at] = mma(ld_frag<C::F32>(s_sc + (16 * at + ln) * C::ROWT + 32 * s + 8 * g), zt, Y[at]);
@@ -1370,16 +1378,20 @@ struct BwdKLds {
     // per-sub-block tiles
     static constexpr int n_sc = DV ? TB * C::ROWT : 0;          // intra scores [a][b]
     static constexpr int n_stage = DV ? TB * C::ROWD : 0;       // dV staging
-    static constexpr int n_zr = TB * C::ROWE;                   // [g | e] rows
+    // [g | e] rows: the dK pass also reads them as intra-product rows over the
+    // augmented width, the dV pass only through transpose reads
+    static constexpr int ZS = DK ? C::ROWE : ZV;
+    static constexpr int n_zr = TB * ZS;
     // bf16 residual of the [g | e] rows: the intra-sub-block product g.v + e
     // cancels for a query against its only key
     static constexpr bool ZLO = DK && !C::F32;
     static constexpr int n_zlo = ZLO ? TB * C::ROWE : 0;
     static constexpr int n_yr = DK ? TB * C::ROWE : 0;          // [v | 1] rows
     // Tiles live outside the block loop share the block buffers where they
-    // fit: the intra scores and the residual rows the feature buffers, the
-    // staging the row-feature buffers.
-    static constexpr bool SC_SHARED = n_sc <= NB * n_cols;
+    // fit: the intra scores the first query-feature buffer (dV) or the feature
+    // buffers (dK), the residual rows the feature buffers, the staging the
+    // first key-feature buffer.
+    static constexpr bool SC_SHARED = DV ? n_sc <= n_brow : n_sc <= NB * n_cols;
     static constexpr bool STAGE_SHARED = n_stage <= NB * (n_rows + n_brow);
     static constexpr bool ZLO_SHARED = NB == 2 && n_zlo <= 2 * n_cols;
     static constexpr int o_rows = 0;                            // [NB][rows | brow]
@@ -1390,17 +1402,20 @@ struct BwdKLds {
     static constexpr int o_zr = o_ms + NB * n_ms;
     static constexpr int o_yr = o_zr + n_zr;
     static constexpr int o_x0 = o_yr + n_yr;                    // unshared tiles follow
-    static constexpr int o_sc = SC_SHARED ? o_cols : o_x0;
+    static constexpr int o_sc = SC_SHARED ? (DV ? o_brow : o_cols) : o_x0;
     static constexpr int o_x1 = o_x0 + (SC_SHARED ? 0 : n_sc);
     static constexpr int o_stage = STAGE_SHARED ? o_rows : o_x1;
     static constexpr int o_x2 = o_x1 + (STAGE_SHARED ? 0 : n_stage);
     static constexpr int o_zlo = ZLO_SHARED ? o_cols : o_x2;
     static constexpr int n_elem = o_x2 + (ZLO_SHARED ? 0 : n_zlo);
-    // two workgroups per CU where registers (bf16, up to 8 feature chunks) and
-    // LDS allow
-    static constexpr int OCC =
-        (!C::F32 && C::NKC <= 8 && n_elem * (int)sizeof(elem) * 2 <= 160 * 1024) ? 2 : 1;
-    static_assert(n_elem * (int)sizeof(elem) * OCC <= 160 * 1024, "LDS budget");
+    static_assert(!(DV && SC_SHARED && STAGE_SHARED) || n_stage <= n_rows, "staging and scores overlap");
+    // workgroups per CU where registers (bf16, up to 8 feature chunks) and LDS
+    // allow: three for the dV pass, two for the dK pass
+    static constexpr int BYTES = n_elem * (int)sizeof(elem);
+    static constexpr int OCC = (C::F32 || C::NKC > 8) ? 1
+                               : (DV && BYTES * 3 <= 160 * 1024) ? 3
+                               : (BYTES * 2 <= 160 * 1024) ? 2 : 1;
+    static_assert(BYTES * OCC <= 160 * 1024, "LDS budget");
 };
 
 template <class C, bool CAUSAL, int PART>
@@ -1430,7 +1445,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
     const elem* WTp = reinterpret_cast<const elem*>(a.WTp);
     constexpr bool causal = CAUSAL;
     if (DK) zero_sketch_pads<C>(s_ms, LD::NB);
-    zero_pads<C>(s_zr, DK ? s_yr : nullptr);
+    zero_pads<C, LD::ZS>(s_zr, DK ? s_yr : nullptr);
     if (LD::ZLO) zero_pads<C>(s_zlo, nullptr);
     __syncthreads();   // the padding is written by all waves, read by each
 
@@ -1491,7 +1506,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
 
         const bool first = t0 == 0;   // the sub-block that starts the sequence
         if (causal)
-            write_aug<C>(zr, tok ? rcp_(zd) : 0.f, tok ? ze : 0.f, s_zr,
+            write_aug<C, LD::ZS>(zr, tok ? rcp_(zd) : 0.f, tok ? ze : 0.f, s_zr,
                          (LD::ZLO && first) ? s_zlo : nullptr);
         if constexpr (DK) {
             // y rows = [v | 1]
@@ -1582,7 +1597,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
                     chain_backproject<C>(t, lane, phi, dA, sg, gu, WTp, dhp, dX);
                 }
             }
-            if (causal) sketch_update<C, DK>(fb, w, ln, g, DV ? brow_b : cols_b, s_zr, Macc, Zacc);
+            if (causal) sketch_update<C, DK, LD::ZS>(fb, w, ln, g, DV ? brow_b : cols_b, s_zr, Macc, Zacc);
             if (LD::NB == 1) __syncthreads();   // single buffer: reads done before the next block's writes
         }
         if (LD::NB == 2) __syncthreads();   // the block tiles are read; the sub-block tiles below reuse them
@@ -1602,7 +1617,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
                 __syncthreads();
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
-                    const frag zt = val_operand<C>(s_zr, 16 * w, s, ln, g);
+                    const frag zt = val_operand<C, LD::ZS>(s_zr, 16 * w, s, ln, g);
 #pragma unroll
                     for (int at = 0; at < 4; ++at)
                         Y[at] = mma(ld_frag<C::F32>(s_sc + (16 * at + ln) * C::ROWT + 32 * s + 8 * g), zt, Y[at]);
