@@ -279,44 +279,55 @@ __device__ inline typename Prec<F32>::uvec round_u(const float u[4]) {
     return v;
 }
 
-// Per-plane values of one lane's four rows from the stored u: the corner-bit
-// probability s = sigmoid(2 beta u) (the corner softmax of beta <c_r, u>
-// factorises over planes into prod_p sigmoid(2 beta c_rp u_p)) and
-// gu = 2 beta (1 - u^2) = d(2 beta u)/dh. With x = 2 beta u and
-// F = e^{-|x|} <= 1, sigmoid(x) = n1 / (1 + F), n1 = 1 for x >= 0 else F, so
-// the four reciprocals share one (arguments in [1, 2]).
+// Feature basis. The kernels contract monomial features instead of the
+// corner probabilities: with t_p = tanh(beta u_p) each plane's factor is
+// sigmoid(2 beta c u_p) = (1 + c t_p) / 2, so the per-table kernel
+// sum_r a_r(q) a_r(k) = prod_p (1 + t_p(q) t_p(k)) / 2
+//                     = 2^-P sum_{T subset of planes} psi_T(q) psi_T(k),
+// psi_T = prod_{p in T} t_p. Feature r of a table is psi_T with T = the set
+// bits of r. The common factor 2^-P cancels in the output O = num / den and
+// in the gradients, so it is dropped. psi_{} = 1 for every table: the state
+// rows of that feature are the same for all tables (the plain sums of
+// [v | 1]), and only the forward read-out needs them exactly (it adds them
+// in float32); every other monomial averages to zero over random planes, so
+// no large common offset rides on the bf16 operands.
+
+// Per-plane values of one lane's four rows from the stored u: t = tanh(beta u)
+// and gt = dt/dh = beta (1 - t^2) (1 - u^2). tanh|x| = (1 - E) / (1 + E) with
+// E = e^{-2|x|}: no overflow, and the four reciprocals share one (arguments
+// in [1, 2]).
 template <bool F32>
-__device__ inline void planes_from_u(const typename Prec<F32>::uvec& uv, float beta, float s[4], float gu[4]) {
-    float F[4], qf[4], rf[4], u[4];
+__device__ inline void tplanes(const typename Prec<F32>::uvec& uv, float beta, float t[4], float gt[4]) {
+    float u[4], e[4], q[4], rq[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         u[i] = (float)uv[i];
-        F[i] = exp2_(-2.f * beta * LOG2E * fabsf(u[i]));
-        qf[i] = 1.f + F[i];
+        e[i] = exp2_(-2.f * beta * LOG2E * fabsf(u[i]));
+        q[i] = 1.f + e[i];
     }
-    rcp4(qf, rf);
+    rcp4(q, rq);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        s[i] = (u[i] >= 0.f ? 1.f : F[i]) * rf[i];
-        gu[i] = 2.f * beta * (1.f - u[i] * u[i]);
+        t[i] = copysignf((1.f - e[i]) * rq[i], u[i]);
+        gt[i] = beta * (1.f - t[i] * t[i]) * (1.f - u[i] * u[i]);
     }
 }
 
-// The features of projection tile t from the plane probabilities s[i] =
-// sigmoid(2 beta u_i) that soft_features computes (stored by an earlier
-// pass): phi_r = prod_p (bit p of r set ? s_p : 1 - s_p). `keep` = false
-// gives phi = 0.
+// Monomial features of projection tile t for one lane: phi[j] = psi of the
+// table and subset that lane feature j stands for (P = 4: the lane's table,
+// subset r = j + 8 kb; P < 4: table j / R of the lane, subset j % R).
+// `keep` = false (an absent token) and padded tables give phi = 0.
 template <class C>
-__device__ inline void features_from_planes(int t, int g, const float s[4], int L, bool keep,
-                                            float phi[C::KB * 8]) {
+__device__ inline void monomial_features(int t, int g, const float tt[4], int L, bool keep,
+                                         float phi[C::KB * 8]) {
     if constexpr (C::P == 4) {
         const bool ok = keep && (t * C::TPT + g) < L;
         const float m = ok ? 1.f : 0.f;
-        const float s0 = s[0] * m, n0 = m - s0;
-        const float lo[4] = {n0 * (1.f - s[1]), s0 * (1.f - s[1]), n0 * s[1], s0 * s[1]};
-        const float hi[4] = {(1.f - s[2]) * (1.f - s[3]), s[2] * (1.f - s[3]), (1.f - s[2]) * s[3], s[2] * s[3]};
+        const float a1 = m * tt[0], a2 = m * tt[1];
+        const float lo[4] = {m, a1, a2, a1 * tt[1]};      // subsets of planes {0, 1}
+        const float hi[4] = {1.f, tt[2], tt[3], tt[2] * tt[3]};   // subsets of planes {2, 3}
 #pragma unroll
-        for (int r = 0; r < 16; ++r) phi[r] = lo[r & 3] * hi[r >> 2];
+        for (int r = 0; r < 16; ++r) phi[r] = (r >> 2) == 0 ? lo[r & 3] : lo[r & 3] * hi[r >> 2];
     } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -324,60 +335,62 @@ __device__ inline void features_from_planes(int t, int g, const float s[4], int 
             const bool ok = keep && (t * C::TPT + g * C::TPL + tl) < L;
             float v = ok ? 1.f : 0.f;
 #pragma unroll
-            for (int p = 0; p < C::P; ++p) {
-                const float sp = s[tl * C::Pp + p];
-                v *= ((r >> p) & 1) ? sp : 1.f - sp;
-            }
+            for (int p = 0; p < C::P; ++p)
+                if ((r >> p) & 1) v *= tt[tl * C::Pp + p];
             phi[j] = v;
         }
     }
 }
 
-// Chain rule of soft_features: given dA (same layout as phi) return dh[4]
-// (gradient wrt the normalised projections of rows 4g..4g+3). With
-// v_r = phi_r dA_r, T = sum_r v_r and S_p = sum_{r: bit p set} v_r, the
-// derivative of sum_r dA_r phi_r wrt u_p is 2 beta (S_p - s_p T), and
-// dh_p = that times (1 - u_p^2); gu = 2 beta (1 - u^2).
+// Chain rule of monomial_features: given dA (gradient wrt the lane's
+// features, same layout as phi) return dh[4], the gradient wrt the
+// normalised projections of rows 4g..4g+3: dL/dt_p = sum over subsets T
+// containing p of dA_T prod_{q in T, q != p} t_q, times gt_p. The empty
+// subset carries no gradient.
 template <class C>
-__device__ inline void soft_features_backward(const float phi[C::KB * 8], const float dA[C::KB * 8],
-                                              const float s[4], const float gu[4], float dh[4]) {
+__device__ inline void monomial_backward(const float dA[C::KB * 8], const float tt[4], const float gt[4],
+                                         float dh[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) dh[i] = 0.f;
     if constexpr (C::P == 4) {
-        float v[16];
+        // subset r = a + 4 b, a over planes {0, 1}, b over planes {2, 3}
+        const float t01 = tt[0] * tt[1], t23 = tt[2] * tt[3];
+        float Ra[4], Cb[4];   // Ra[a] = sum_b dA[a + 4b] hi_b, Cb[b] = sum_a dA[a + 4b] lo_a
 #pragma unroll
-        for (int r = 0; r < 16; ++r) v[r] = phi[r] * dA[r];
-        float rs[4], cs[4];   // sums over the low and over the high two bits
+        for (int a = 1; a < 4; ++a) Ra[a] = dA[a] + dA[a + 4] * tt[2] + dA[a + 8] * tt[3] + dA[a + 12] * t23;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            rs[k] = (v[4 * k] + v[4 * k + 1]) + (v[4 * k + 2] + v[4 * k + 3]);
-            cs[k] = (v[k] + v[k + 4]) + (v[k + 8] + v[k + 12]);
-        }
-        const float T = (rs[0] + rs[1]) + (rs[2] + rs[3]);
-        const float S[4] = {cs[1] + cs[3], cs[2] + cs[3], rs[1] + rs[3], rs[2] + rs[3]};
-#pragma unroll
-        for (int p = 0; p < 4; ++p) dh[p] = (S[p] - s[p] * T) * gu[p];
+        for (int b = 1; b < 4; ++b)
+            Cb[b] = dA[4 * b] + dA[4 * b + 1] * tt[0] + dA[4 * b + 2] * tt[1] + dA[4 * b + 3] * t01;
+        dh[0] = (Ra[1] + Ra[3] * tt[1]) * gt[0];
+        dh[1] = (Ra[2] + Ra[3] * tt[0]) * gt[1];
+        dh[2] = (Cb[1] + Cb[3] * tt[3]) * gt[2];
+        dh[3] = (Cb[2] + Cb[3] * tt[2]) * gt[3];
     } else {
 #pragma unroll
         for (int tl = 0; tl < C::TPL; ++tl) {
-            float T = 0.f, S[C::P];
-#pragma unroll
-            for (int p = 0; p < C::P; ++p) S[p] = 0.f;
-#pragma unroll
-            for (int r = 0; r < C::R; ++r) {
-                const float v = phi[tl * C::R + r] * dA[tl * C::R + r];
-                T += v;
-#pragma unroll
-                for (int p = 0; p < C::P; ++p)
-                    if ((r >> p) & 1) S[p] += v;
-            }
 #pragma unroll
             for (int p = 0; p < C::P; ++p) {
-                const int i = tl * C::Pp + p;
-                dh[i] = (S[p] - s[i] * T) * gu[i];
+                float acc = 0.f;
+#pragma unroll
+                for (int r = 0; r < C::R; ++r) {
+                    if (!((r >> p) & 1)) continue;
+                    float prod = dA[tl * C::R + r];
+#pragma unroll
+                    for (int q = 0; q < C::P; ++q)
+                        if (q != p && ((r >> q) & 1)) prod *= tt[tl * C::Pp + q];
+                    acc += prod;
+                }
+                dh[tl * C::Pp + p] = acc * gt[tl * C::Pp + p];
             }
         }
     }
+}
+
+// True when lane feature (h, i) of accumulator tile pair kc (feature
+// j = 4 h + i of the chunk) is the empty subset of its table.
+template <class C>
+__device__ constexpr bool is_empty_subset(int kc, int h, int i) {
+    return C::P == 4 ? ((kc % C::KB) == 0 && h == 0 && i == 0) : ((4 * h + i) % C::R) == 0;
 }
 
 }  // namespace race

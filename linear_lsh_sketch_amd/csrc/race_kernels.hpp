@@ -514,36 +514,36 @@ __device__ inline void block_features(const WSrc<C>& wsrc, int fb, int lane, int
     for (int tb = 0; tb < C::TPB; ++tb) {
         const int t = fb * C::TPB + tb;
         const f32x4 acc = wsrc.project(t, lane, ln, g, xf);
-        float hs[4], u[4], phi[C::KB * 8], sg[4], gu[4];
+        float hs[4], u[4], phi[C::KB * 8], tt[4], gt[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) hs[i] = acc[i] * inv;
         tanh4(hs, u);
         const typename Prec<C::F32>::uvec uq = round_u<C::F32>(u);
-        planes_from_u<C::F32>(uq, beta, sg, gu);
-        features_from_planes<C>(t, g, sg, L, valid, phi);
+        tplanes<C::F32>(uq, beta, tt, gt);
+        monomial_features<C>(t, g, tt, L, valid, phi);
         if (store) store_u<C>(out, rowi, t, g, uq);
         emit_tile<C, KEEP>(tb, w, ln, g, phi, rows, phi_frag);
     }
 }
 
 // The same from stored plane values (no projection); when KEEP, also return
-// per tile the plane probabilities s and 2 beta (1 - u^2) for the chain rule.
+// per tile the plane values t and dt/dh for the chain rule.
 template <class C, bool KEEP>
 __device__ inline void block_features_cached(const Planes<C>& pl, int fb, int w, int ln, int g, bool valid, int L,
                                              float beta, typename Prec<C::F32>::elem* rows,
                                              typename Prec<C::F32>::frag (&phi_frag)[C::FBK],
-                                             float (&s_keep)[C::TPB][4], float (&gu_keep)[C::TPB][4]) {
+                                             float (&t_keep)[C::TPB][4], float (&gt_keep)[C::TPB][4]) {
 #pragma unroll
     for (int tb = 0; tb < C::TPB; ++tb) {
         const int t = fb * C::TPB + tb;
-        float sg[4], gu[4], phi[C::KB * 8];
-        planes_from_u<C::F32>(pl.u[tb], beta, sg, gu);
-        features_from_planes<C>(t, g, sg, L, valid, phi);
+        float tt[4], gt[4], phi[C::KB * 8];
+        tplanes<C::F32>(pl.u[tb], beta, tt, gt);
+        monomial_features<C>(t, g, tt, L, valid, phi);
         if constexpr (KEEP) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                s_keep[tb][i] = sg[i];
-                gu_keep[tb][i] = gu[i];
+                t_keep[tb][i] = tt[i];
+                gt_keep[tb][i] = gt[i];
             }
         }
         emit_tile<C, KEEP>(tb, w, ln, g, phi, rows, phi_frag);
@@ -741,31 +741,13 @@ struct PassArgs {
     int causal;
 };
 
-// Corner mean of the sketch value column this lane holds. Every key adds a
-// unit of mass per valid table, so all valid tables of a column sum to the
-// same value (the column sum of the values in the sketch): the mean is taken
-// once, from the lane's table of the first projection tile (if that table is
-// padding, so are all the lane's tables, and it gives 0).
-template <class C>
-__device__ inline float sketch_column_mean(const f32x4 Macc[C::NKC * 2]) {
-    constexpr int RR = (C::P == 4) ? 16 : C::R;
-    float m = 0.f;
-#pragma unroll
-    for (int r = 0; r < RR; ++r) m += Macc[r >> 2][r & 3];
-    return m * (1.f / (float)RR);
-}
-
 // Sketch rows of feature block fb for the gradient contraction dA = M y:
 // [FBK*32][ROWE], value columns of wave w and the mass column (64) from the
-// wave that owns it. Only dA - <a, dA> per table is used downstream, so a
-// per-table constant may be removed: the corner mean `mcol` of the value
-// column is subtracted in float32 and the mass column is shifted by `zshift`,
-// and the bf16 operand then carries the part that survives instead of a large
-// common offset.
+// wave that owns it. (In the monomial basis only the empty subset's rows carry
+// the large plain sums, and its dA is not used.)
 template <class C>
 __device__ inline void write_sketch_rows(int fb, int w, int ln, int g, const f32x4 Macc[C::NKC * 2],
-                                         const f32x4 Zacc[C::NOWN * 2], float mcol, float zshift,
-                                         typename Prec<C::F32>::elem* s_ms) {
+                                         const f32x4 Zacc[C::NOWN * 2], typename Prec<C::F32>::elem* s_ms) {
 #pragma unroll
     for (int kcl = 0; kcl < C::FBK; ++kcl)
 #pragma unroll
@@ -773,7 +755,7 @@ __device__ inline void write_sketch_rows(int fb, int w, int ln, int g, const f32
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int rl = 32 * kcl + 16 * h + 4 * g + i;
-                s_ms[rl * C::ROWE + 16 * w + ln] = to_elem<C::F32>(Macc[2 * (fb * C::FBK + kcl) + h][i] - mcol);
+                s_ms[rl * C::ROWE + 16 * w + ln] = to_elem<C::F32>(Macc[2 * (fb * C::FBK + kcl) + h][i]);
             }
     const int kw = w - C::own_base(fb);
     if (kw >= 0 && kw < C::FBK && ln == 0) {
@@ -781,8 +763,7 @@ __device__ inline void write_sketch_rows(int fb, int w, int ln, int g, const f32
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                s_ms[(32 * kw + 16 * h + 4 * g + i) * C::ROWE + 64] =
-                    to_elem<C::F32>(Zacc[2 * C::zidx(fb) + h][i] - zshift);
+                s_ms[(32 * kw + 16 * h + 4 * g + i) * C::ROWE + 64] = to_elem<C::F32>(Zacc[2 * C::zidx(fb) + h][i]);
     }
 }
 
@@ -817,16 +798,16 @@ __device__ inline void block_grad(int ln, int g, const typename Prec<C::F32>::el
     }
 }
 
-// Corner-softmax chain rule for projection tile t of the own token (phi and dA
-// in the lane's feature order, s and gu of its planes as soft_features gives
+// Chain rule of the monomial features for projection tile t of the own token
+// (dA in the lane's feature order, t and dt/dh of its planes as tplanes gives
 // them), then the back-projection dX += W'^T dh, two tiles per matrix-core
 // operand.
 template <class C>
-__device__ inline void chain_backproject(int t, int lane, const float phi[C::KB * 8], const float dA[C::KB * 8],
-                                         const float s[4], const float gu[4], const typename Prec<C::F32>::elem* WTp,
+__device__ inline void chain_backproject(int t, int lane, const float dA[C::KB * 8], const float tt[4],
+                                         const float gt[4], const typename Prec<C::F32>::elem* WTp,
                                          f32x4 (&dhp)[2], f32x4 (&dX)[4]) {
     float dh[4];
-    soft_features_backward<C>(phi, dA, s, gu, dh);
+    monomial_backward<C>(dA, tt, gt, dh);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dhp[t & 1][i] = dh[i];
     if ((t & 1) == 1 || t == C::MT - 1) {
@@ -950,6 +931,18 @@ struct WStage {
 // sketch of the keys before the sub-block plus the intra-sub-block causal term;
 // then the sketch update. Also writes the per-token denominator D when Dv is set.
 // ---------------------------------------------------------------------------
+// Matrix-core operand of state tile pair kc with the rows of the empty subset
+// set to zero (the forward read-out adds their contribution in float32).
+template <class C>
+__device__ inline typename Prec<C::F32>::frag pack_nonempty(int kc, f32x4 lo, f32x4 hi) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (is_empty_subset<C>(kc, 0, i)) lo[i] = 0.f;
+        if (is_empty_subset<C>(kc, 1, i)) hi[i] = 0.f;
+    }
+    return pack<C::F32>(lo, hi);
+}
+
 template <class C>
 struct FwdLds {
     using elem = typename Prec<C::F32>::elem;
@@ -1047,6 +1040,14 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
         if (u_out && g == 0) bstore_f32(pra.inv, rowi * 4, inv_a);
         write_aug<C, ZV>(zr, 1.f, tok ? 1.f : 0.f, s_zr);
 
+        // The empty subset's state rows (plain sums of the keys' [v | 1], the
+        // same for every valid table) enter the read-out exactly, in float32:
+        // L times the value sums of this wave's columns (held by lane group 0
+        // as table 0's first feature, before this sub-block's updates) and L
+        // times the number of keys in the state.
+        const float y_empty = (float)a.L * __shfl(Macc[0][0], ln);
+        const float d_empty = (float)a.L * (float)(causal ? t0 : a.N);
+
         f32x4 Y[4], Dacc[4], Sc[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1054,9 +1055,12 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
             Dacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
             Sc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-#pragma unroll
-        for (int fb = 0; fb < C::NBLK; ++fb) {
-            frag phiA[C::FBK], unused[C::FBK];
+        // Software-pipelined feature blocks: after the barrier that publishes
+        // block fb, a wave computes and writes the features of block fb + 1
+        // (other buffer) while its matrix-core work on block fb proceeds.
+        frag phiA[C::FBK], phiN[C::FBK];
+        auto features = [&](int fb, frag (&phi)[C::FBK]) {
+            frag unused[C::FBK];
             elem* rows_b = s_rows + (fb & 1) * LD::n_rows;
             elem* brow_b = s_brow + (fb & 1) * LD::n_brow;
             const Planes<C> pl = pn;
@@ -1064,13 +1068,20 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
                 if (fb + 1 < C::NBLK) issue_planes(it, fb + 1);
                 else if (it + 1 < nsub) issue_planes(it + 1, 0);
             }
-            block_features<C, true>(wsrc, fb, lane, w, ln, g, xa, inv_a, valid, a.beta, a.L, rows_b, phiA, pra,
+            block_features<C, true>(wsrc, fb, lane, w, ln, g, xa, inv_a, valid, a.beta, a.L, rows_b, phi, pra,
                                     u_out, rowi);
             if (causal) {
                 float us[C::TPB][4], ug[C::TPB][4];
                 block_features_cached<C, false>(pl, fb, w, ln, g, valid, a.L, a.beta, brow_b, unused, us, ug);
             }
+        };
+        features(0, phiA);
+#pragma unroll
+        for (int fb = 0; fb < C::NBLK; ++fb) {
+            const elem* rows_b = s_rows + (fb & 1) * LD::n_rows;
+            const elem* brow_b = s_brow + (fb & 1) * LD::n_brow;
             __syncthreads();
+            if (fb + 1 < C::NBLK) features(fb + 1, phiN);
             if (causal) {
 #pragma unroll
                 for (int bt = 0; bt < 4; ++bt) {
@@ -1083,19 +1094,21 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
 #pragma unroll
             for (int kcl = 0; kcl < C::FBK; ++kcl) {
                 const int kc = fb * C::FBK + kcl;
-                const frag mf = pack<C::F32>(Macc[2 * kc], Macc[2 * kc + 1]);
+                const frag mf = pack_nonempty<C>(kc, Macc[2 * kc], Macc[2 * kc + 1]);
 #pragma unroll
                 for (int at = 0; at < 4; ++at)
                     Y[at] = mma(ld_frag<C::F32>(rows_b + (16 * at + ln) * C::ROWF + 32 * kcl + 8 * g), mf, Y[at]);
             }
             const int kw = w - C::own_base(fb);
             if (kw >= 0 && kw < C::FBK) {
-                const frag zf = pack<C::F32>(Zacc[2 * C::zidx(fb)], Zacc[2 * C::zidx(fb) + 1]);
+                const frag zf = pack_nonempty<C>(fb * C::FBK + kw, Zacc[2 * C::zidx(fb)], Zacc[2 * C::zidx(fb) + 1]);
 #pragma unroll
                 for (int at = 0; at < 4; ++at)
                     Dacc[at] = mma(ld_frag<C::F32>(rows_b + (16 * at + ln) * C::ROWF + 32 * kw + 8 * g), zf, Dacc[at]);
             }
             if (causal) sketch_update<C, true, ZV>(fb, w, ln, g, brow_b, s_zr, Macc, Zacc);
+#pragma unroll
+            for (int k = 0; k < C::FBK; ++k) phiA[k] = phiN[k];
         }
         // intra-sub-block term: scores of visible keys b <= a. The value
         // readout multiplies the scores rounded to the operand type, so the
@@ -1140,12 +1153,12 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * at + 4 * g + i;
-                float d = f_Dpart[r] + f_Dpart[TB + r] + f_Dpart[2 * TB + r] + f_Dpart[3 * TB + r];
+                float d = f_Dpart[r] + f_Dpart[TB + r] + f_Dpart[2 * TB + r] + f_Dpart[3 * TB + r] + d_empty;
                 if (causal) d += f_Dint[r];
-                s_stage[r * C::ROWD + 16 * w + ln] = to_elem<C::F32>(Y[at][i] * rcp_(d));
+                s_stage[r * C::ROWD + 16 * w + ln] = to_elem<C::F32>((Y[at][i] + y_empty) * rcp_(d));
             }
         if (tq == 0) {
-            float d = f_Dpart[tr] + f_Dpart[TB + tr] + f_Dpart[2 * TB + tr] + f_Dpart[3 * TB + tr];
+            float d = f_Dpart[tr] + f_Dpart[TB + tr] + f_Dpart[2 * TB + tr] + f_Dpart[3 * TB + tr] + d_empty;
             if (causal) d += f_Dint[tr];
             bstore_f32(rD, (it * TB + tr) * 4, d);
         }
@@ -1304,11 +1317,6 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) dX[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         f32x4 dhp[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-        // Every table's masses sum to the number of keys in the sketch, so the
-        // mass of a corner is that count / R plus a fluctuation: store the
-        // fluctuation (a per-table constant cancels in the chain rule).
-        const float zshift = (causal ? (float)t0 : (float)a.N) / (float)C::R;
-        const float mcol = sketch_column_mean<C>(Macc);   // before this sub-block's updates
 #pragma unroll
         for (int fb = 0; fb < C::NBLK; ++fb) {
             const Planes<C> qa = pa, kb_ = pb;
@@ -1316,7 +1324,7 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
             else if (it + 1 < nsub) issue_planes(it + 1, 0);
             elem* ms_b = s_ms + (fb & 1) * LD::n_ms;
             elem* cols_b = s_cols + (fb & 1) * LD::n_cols;
-            write_sketch_rows<C>(fb, w, ln, g, Macc, Zacc, mcol, zshift, ms_b);
+            write_sketch_rows<C>(fb, w, ln, g, Macc, Zacc, ms_b);
             if (causal) {
                 frag unused[C::FBK];
                 float us[C::TPB][4], ug[C::TPB][4];
@@ -1331,9 +1339,8 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
 #pragma unroll
             for (int tb = 0; tb < C::TPB; ++tb) {
                 const int t = fb * C::TPB + tb;
-                float phi[C::KB * 8], sg[4], gu[4], dA[C::KB * 8];
-                planes_from_u<C::F32>(qa.u[tb], a.beta, sg, gu);
-                features_from_planes<C>(t, g, sg, a.L, valid, phi);
+                float tt[4], gt[4], dA[C::KB * 8];
+                tplanes<C::F32>(qa.u[tb], a.beta, tt, gt);
 #pragma unroll
                 for (int kb = 0; kb < C::KB; ++kb) {
                     const int kcl = tb * C::KB + kb;
@@ -1343,7 +1350,7 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
                         dA[kb * 8 + 4 + i] = G[2 * kcl + 1][i];
                     }
                 }
-                chain_backproject<C>(t, lane, phi, dA, sg, gu, WTp, dhp, dX);
+                chain_backproject<C>(t, lane, dA, tt, gt, WTp, dhp, dX);
             }
             if (causal) sketch_update<C>(fb, w, ln, g, cols_b, s_zr, Macc, Zacc);
         }
@@ -1531,7 +1538,6 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
             dX[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         f32x4 dhp[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-        const float mcol = DK ? sketch_column_mean<C>(Macc) : 0.f;   // before this sub-block's updates
 #pragma unroll
         for (int fb = 0; fb < C::NBLK; ++fb) {
             frag phiA[C::FBK], unused[C::FBK];
@@ -1551,7 +1557,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
             } else if (causal) {
                 block_features_cached<C, false>(qb, fb, w, ln, g, valid, a.L, a.beta, cols_b, unused, us, ug);
             }
-            if constexpr (DK) write_sketch_rows<C>(fb, w, ln, g, Macc, Zacc, mcol, 0.f, ms_b);
+            if constexpr (DK) write_sketch_rows<C>(fb, w, ln, g, Macc, Zacc, ms_b);
             __syncthreads();
             if constexpr (DV) {
                 if (causal) {
@@ -1582,9 +1588,8 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
 #pragma unroll
                 for (int tb = 0; tb < C::TPB; ++tb) {
                     const int t = fb * C::TPB + tb;
-                    float phi[C::KB * 8], dA[C::KB * 8], sg[4], gu[4];
-                    planes_from_u<C::F32>(ka.u[tb], a.beta, sg, gu);
-                    features_from_planes<C>(t, g, sg, a.L, valid, phi);
+                    float dA[C::KB * 8], tt[4], gt[4];
+                    tplanes<C::F32>(ka.u[tb], a.beta, tt, gt);
 #pragma unroll
                     for (int kb = 0; kb < C::KB; ++kb) {
                         const int kcl = tb * C::KB + kb;
@@ -1594,7 +1599,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
                             dA[kb * 8 + 4 + i] = G[2 * kcl + 1][i];
                         }
                     }
-                    chain_backproject<C>(t, lane, phi, dA, sg, gu, WTp, dhp, dX);
+                    chain_backproject<C>(t, lane, dA, tt, gt, WTp, dhp, dX);
                 }
             }
             if (causal) sketch_update<C, DK, LD::ZS>(fb, w, ln, g, DV ? brow_b : cols_b, s_zr, Macc, Zacc);

@@ -59,6 +59,36 @@ def test_corner_softmax_equals_product_of_sigmoids(P, beta):
     np.testing.assert_allclose(a, assignments_by_product(Q, W, beta), rtol=0, atol=1e-14)
 
 
+@pytest.mark.parametrize("P", [1, 2, 3, 4])
+@pytest.mark.parametrize("beta", [0.3, 1.0, 4.0])
+def test_corner_overlap_equals_monomial_form(P, beta):
+    """The table kernel sum_r a_r(q) a_r(k) equals 2^-P * sum over plane
+    subsets T of prod_{p in T} t_p(q) t_p(k) with t = tanh(beta * tanh(h)),
+    the form the GPU kernels contract (their features are the monomials
+    prod_{p in T} t_p). Each plane's factor sigmoid(2b u) = (1 + tanh(b u)) / 2
+    makes the sum over corners factorise into prod_p (1 + t_p(q) t_p(k)) / 2."""
+    Q, K, _, _, W = rand_case(P * 13 + int(beta * 10), 24, 8, P, 3)
+    aq, _ = dense.soft_buckets(Q, W, beta)
+    ak, _ = dense.soft_buckets(K, W, beta)
+    corner = np.einsum("ilr,jlr->ijl", aq, ak)
+
+    def t_of(X):
+        Xh = X / np.linalg.norm(X, axis=1, keepdims=True)
+        return np.tanh(beta * np.tanh(np.einsum("nd,lpd->nlp", Xh, W)))
+
+    tq, tk = t_of(Q), t_of(K)
+    mono = np.zeros_like(corner)
+    for T in range(1 << P):
+        fq = np.ones(tq.shape[:2])
+        fk = np.ones(tk.shape[:2])
+        for p in range(P):
+            if (T >> p) & 1:
+                fq = fq * tq[:, :, p]
+                fk = fk * tk[:, :, p]
+        mono += np.einsum("il,jl->ijl", fq, fk)
+    np.testing.assert_allclose(corner, mono / (1 << P), rtol=0, atol=1e-15)
+
+
 def test_assignments_sum_to_one():
     Q, _, _, _, W = rand_case(3, 50, 16, 4, 5)
     a, _ = dense.soft_buckets(Q, W, 1.0)
