@@ -798,23 +798,37 @@ __device__ inline void block_grad(int ln, int g, const typename Prec<C::F32>::el
     }
 }
 
+// True when projection tile t completes a pair of tiles (the back-projection
+// operand covers two tiles).
+template <class C>
+__device__ constexpr bool completes_pair(int t) { return (t & 1) == 1 || t == C::MT - 1; }
+
+// Back-projection operands (W'^T, four 16-column tiles) of the tile pair that
+// tile t completes, from the table k_prep writes; loaded early in a block so
+// the memory latency overlaps the block's matrix-core work.
+template <class C>
+__device__ inline void load_wtp(int t, int lane, const typename Prec<C::F32>::elem* WTp,
+                                typename Prec<C::F32>::frag (&wf)[4]) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) wf[dt] = ld_frag<C::F32>(WTp + ((size_t)((t >> 1) * 4 + dt) * 64 + lane) * 8);
+}
+
 // Chain rule of the monomial features for projection tile t of the own token
 // (dA in the lane's feature order, t and dt/dh of its planes as tplanes gives
-// them), then the back-projection dX += W'^T dh, two tiles per matrix-core
-// operand.
+// them), then, when t completes a tile pair, the back-projection
+// dX += W'^T dh with the operands wf of load_wtp.
 template <class C>
-__device__ inline void chain_backproject(int t, int lane, const float dA[C::KB * 8], const float tt[4],
-                                         const float gt[4], const typename Prec<C::F32>::elem* WTp,
-                                         f32x4 (&dhp)[2], f32x4 (&dX)[4]) {
+__device__ inline void chain_backproject(int t, const float dA[C::KB * 8], const float tt[4], const float gt[4],
+                                         const typename Prec<C::F32>::frag (&wf)[4], f32x4 (&dhp)[2],
+                                         f32x4 (&dX)[4]) {
     float dh[4];
     monomial_backward<C>(dA, tt, gt, dh);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dhp[t & 1][i] = dh[i];
-    if ((t & 1) == 1 || t == C::MT - 1) {
+    if (completes_pair<C>(t)) {
         const typename Prec<C::F32>::frag df = pack<C::F32>(dhp[0], (t & 1) ? dhp[1] : f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-            dX[dt] = mma(ld_frag<C::F32>(WTp + ((size_t)((t >> 1) * 4 + dt) * 64 + lane) * 8), df, dX[dt]);
+        for (int dt = 0; dt < 4; ++dt) dX[dt] = mma(wf[dt], df, dX[dt]);
         dhp[0] = f32x4{0.f, 0.f, 0.f, 0.f};
         dhp[1] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -865,25 +879,32 @@ __device__ inline void intra_operand(const typename Prec<C::F32>::elem* s_zr, co
 // rule of x_hat = x / max(|x|, eps); below eps the map is a plain scaling, and
 // inv = 1 / max(|x|, eps) tells which case holds). dX[dt] holds columns
 // 16 dt + 4 g .. +3.
+// The own token's row values that store_dx needs (columns 16 dt + 4 g .. +3),
+// loaded early so the memory latency overlaps the sub-block's work.
 template <class C>
-__device__ inline void store_dx(rsrc_t rX, rsrc_t rOut, int rowi, int g, float inv, const f32x4 dX[4]) {
+__device__ inline void load_dx_row(rsrc_t rX, int rowi, int g, typename Prec<C::F32>::half (&xr)[4]) {
+    constexpr int es = C::F32 ? 4 : 2;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+        const int off = rowi * row_bytes<C::F32>() + (16 * dt + 4 * g) * es;
+        if constexpr (C::F32) xr[dt] = __builtin_bit_cast(f32x4, bload128(rX, off));
+        else xr[dt] = __builtin_bit_cast(bf16x4, bload64(rX, off));
+    }
+}
+
+template <class C>
+__device__ inline void store_dx(const typename Prec<C::F32>::half (&xr)[4], rsrc_t rOut, int rowi, int g, float inv,
+                                const f32x4 dX[4]) {
     constexpr int es = C::F32 ? 4 : 2;
     float xv[4][4];
     float radial = 0.f;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-        const int off = rowi * row_bytes<C::F32>() + (16 * dt + 4 * g) * es;
-        if constexpr (C::F32) {
-            const f32x4 v = __builtin_bit_cast(f32x4, bload128(rX, off));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xv[dt][i] = v[i];
-        } else {
-            const bf16x4 v = __builtin_bit_cast(bf16x4, bload64(rX, off));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) xv[dt][i] = (float)v[i];
+        for (int i = 0; i < 4; ++i) {
+            xv[dt][i] = (float)xr[dt][i];
+            radial += xv[dt][i] * inv * dX[dt][i];
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) radial += xv[dt][i] * inv * dX[dt][i];
     }
     radial = sum_groups(radial);
     const bool tangent = inv < rcp_(NORM_EPS);
@@ -1273,6 +1294,8 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
         load_q16_b<C::F32>(rOs, rowt, tq, orow);
         const float dd = tok ? bload_f32(rD, rowt * 4) : 1.f;
         const float inv_a = valid ? bload_f32(pra.inv, rowi * 4) : 1.f;
+        typename Prec<C::F32>::half xr[4];
+        load_dx_row<C>(rXa, rowi, g, xr);
         const bool first = t0 == 0;   // the sub-block that starts the sequence
         if (causal) write_aug<C>(zr, 1.f, tok ? 1.f : 0.f, s_zr);
         // y = [dO / D | e], e = -<dO, O> / D; this thread holds 16 columns of row tr
@@ -1319,6 +1342,10 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
         f32x4 dhp[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int fb = 0; fb < C::NBLK; ++fb) {
+            frag wf[C::TPB][4];
+#pragma unroll
+            for (int tb = 0; tb < C::TPB; ++tb)
+                if (completes_pair<C>(fb * C::TPB + tb)) load_wtp<C>(fb * C::TPB + tb, lane, WTp, wf[tb]);
             const Planes<C> qa = pa, kb_ = pb;
             if (fb + 1 < C::NBLK) issue_planes(it, fb + 1);
             else if (it + 1 < nsub) issue_planes(it + 1, 0);
@@ -1350,12 +1377,12 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
                         dA[kb * 8 + 4 + i] = G[2 * kcl + 1][i];
                     }
                 }
-                chain_backproject<C>(t, lane, dA, tt, gt, WTp, dhp, dX);
+                chain_backproject<C>(t, dA, tt, gt, wf[tb], dhp, dX);
             }
             if (causal) sketch_update<C>(fb, w, ln, g, cols_b, s_zr, Macc, Zacc);
         }
         __syncthreads();   // the next sub-block rewrites the y and z rows
-        store_dx<C>(rXa, rOut, rowi, g, inv_a, dX);
+        store_dx<C>(xr, rOut, rowi, g, inv_a, dX);
     }
 }
 
@@ -1511,6 +1538,8 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
         const float zd = n_d, ze = n_e, inv_a = n_inv;
         if (PREFETCH && it + 1 < nsub) issue(it + 1);
 
+        typename Prec<C::F32>::half xr[4];
+        if constexpr (DK) load_dx_row<C>(rXa, r0_of(it) + my, g, xr);
         const bool first = t0 == 0;   // the sub-block that starts the sequence
         if (causal)
             write_aug<C, LD::ZS>(zr, tok ? rcp_(zd) : 0.f, tok ? ze : 0.f, s_zr,
@@ -1542,6 +1571,12 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
         for (int fb = 0; fb < C::NBLK; ++fb) {
             frag phiA[C::FBK], unused[C::FBK];
             float us[C::TPB][4], ug[C::TPB][4];
+            frag wf[C::TPB][4];
+            if constexpr (DK) {
+#pragma unroll
+                for (int tb = 0; tb < C::TPB; ++tb)
+                    if (completes_pair<C>(fb * C::TPB + tb)) load_wtp<C>(fb * C::TPB + tb, lane, WTp, wf[tb]);
+            }
             const Planes<C> ka = pa, qb = pb;
             if (fb + 1 < C::NBLK) issue_planes(it, fb + 1);
             else if (it + 1 < nsub) issue_planes(it + 1, 0);
@@ -1599,7 +1634,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
                             dA[kb * 8 + 4 + i] = G[2 * kcl + 1][i];
                         }
                     }
-                    chain_backproject<C>(t, lane, dA, tt, gt, WTp, dhp, dX);
+                    chain_backproject<C>(t, dA, tt, gt, wf[tb], dhp, dX);
                 }
             }
             if (causal) sketch_update<C, DK, LD::ZS>(fb, w, ln, g, DV ? brow_b : cols_b, s_zr, Macc, Zacc);
@@ -1636,7 +1671,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
             __syncthreads();
             store_stage<C>(rOut1, r0_of(it) + tr, tr, tq, s_stage);
         }
-        if constexpr (DK) store_dx<C>(rXa, rOut0, r0_of(it) + my, g, inv_a, dX);
+        if constexpr (DK) store_dx<C>(xr, rOut0, r0_of(it) + my, g, inv_a, dX);
     }
 }
 
