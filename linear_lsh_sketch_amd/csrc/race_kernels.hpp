@@ -230,14 +230,16 @@ __device__ inline f32x4 project_global(const typename Prec<C::F32>::elem* __rest
     return acc;
 }
 
-// Source of the projection operands: LDS-staged when `s_w` is set.
-template <class C>
+// Source of the projection operands: LDS-staged when STAGED (the choice is
+// made at compile time from the LDS budget, so no dead path is emitted).
+template <class C, bool STAGED = true>
 struct WSrc {
     const typename Prec<C::F32>::elem* s_w;
     const typename Prec<C::F32>::elem* W;
     int L;
     __device__ inline f32x4 project(int t, int lane, int ln, int g, const typename Prec<C::F32>::frag xf[2]) const {
-        return s_w ? project_lds<C>(s_w, t, lane, xf) : project_global<C>(W, L, t, ln, g, xf);
+        if constexpr (STAGED) return project_lds<C>(s_w, t, lane, xf);
+        else return project_global<C>(W, L, t, ln, g, xf);
     }
 };
 
@@ -504,8 +506,8 @@ __device__ inline void emit_tile(int tb, int w, int ln, int g, const float phi[C
 // also return the lane's operands (one per chunk of the block) in phi_frag.
 // With `store` set, the plane values are stored to `out` (in-chunk row rowi;
 // rows past the chunk are dropped) for later passes.
-template <class C, bool KEEP>
-__device__ inline void block_features(const WSrc<C>& wsrc, int fb, int lane, int w, int ln, int g,
+template <class C, bool KEEP, class WS>
+__device__ inline void block_features(const WS& wsrc, int fb, int lane, int w, int ln, int g,
                                       const typename Prec<C::F32>::frag xf[2], float inv, bool valid, float beta,
                                       int L, typename Prec<C::F32>::elem* rows /* [64][ROWF] or null */,
                                       typename Prec<C::F32>::frag (&phi_frag)[C::FBK], const PlaneRows& out,
@@ -1017,7 +1019,7 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
     if (LD::WS::on) stage_w<C>(W, a.L, s_w);
     zero_pads<C, ZV>(s_zr, nullptr);
     __syncthreads();   // W' and the padding are written by all waves, read by each
-    const WSrc<C> wsrc{s_w, W, a.L};
+    const WSrc<C, LD::WS::on> wsrc{s_w, W, a.L};
     const int64_t nrows = seg1 - seg0;
     const size_t row0 = base + seg0;
     const rsrc_t rXa = rows_rsrc(a.Xa, row0, nrows, row_bytes<C::F32>());
