@@ -983,7 +983,7 @@ struct FwdLds {
     static constexpr int o_zr = o_brow + 2 * n_brow;
     static constexpr int o_sc = o_zr + n_zr;
     static constexpr int o_w = o_sc + n_sc;
-    static constexpr int n_float = 4 * TB + TB;                 // Dpart, Dint
+    static constexpr int n_float = 4 * TB + TB + TB;            // Dpart, Dint, 1 / D
     // two workgroups per CU (VGPR budget 256: two waves share each SIMD)
     static constexpr int OCC = (!C::F32 && C::NKC <= 8) ? 2 : 1;
     using WS = WStage<elem, o_w, n_float, C::MT, OCC>;
@@ -1003,6 +1003,7 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
     elem* s_stage = lds + LD::o_rows;   // alias after the feature-block loop
     float* f_Dpart = ldf;               // [4][64]
     float* f_Dint = ldf + 4 * TB;       // [64]
+    float* f_rD = ldf + 5 * TB;         // [64]
 
     const int lane = threadIdx.x & 63, ln = lane & 15, g = lane >> 4;
     // wave index as a scalar: every branch on it is wave-uniform, so no MFMA is
@@ -1162,6 +1163,14 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
                 for (int i = 0; i < 4; ++i) f_Dpart[w * TB + 16 * at + 4 * g + i] = Dacc[at][i];
         }
         __syncthreads();
+        // one thread per token sums the denominator parts, stores D and
+        // publishes 1 / D for the output normalisation
+        if (tq == 0) {
+            float d = f_Dpart[tr] + f_Dpart[TB + tr] + f_Dpart[2 * TB + tr] + f_Dpart[3 * TB + tr] + d_empty;
+            if (causal) d += f_Dint[tr];
+            bstore_f32(rD, (it * TB + tr) * 4, d);
+            f_rD[tr] = rcp_(d);
+        }
         if (causal) {
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
@@ -1171,19 +1180,13 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
                     Y[at] = mma(ld_frag<C::F32>(s_sc + (16 * at + ln) * C::ROWT + 32 * s + 8 * g), zt, Y[at]);
             }
         }
+        __syncthreads();
 #pragma unroll
-        for (int at = 0; at < 4; ++at)
+        for (int at = 0; at < 4; ++at) {
+            const f32x4 rd = *reinterpret_cast<const f32x4*>(f_rD + 16 * at + 4 * g);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * at + 4 * g + i;
-                float d = f_Dpart[r] + f_Dpart[TB + r] + f_Dpart[2 * TB + r] + f_Dpart[3 * TB + r] + d_empty;
-                if (causal) d += f_Dint[r];
-                s_stage[r * C::ROWD + 16 * w + ln] = to_elem<C::F32>((Y[at][i] + y_empty) * rcp_(d));
-            }
-        if (tq == 0) {
-            float d = f_Dpart[tr] + f_Dpart[TB + tr] + f_Dpart[2 * TB + tr] + f_Dpart[3 * TB + tr] + d_empty;
-            if (causal) d += f_Dint[tr];
-            bstore_f32(rD, (it * TB + tr) * 4, d);
+            for (int i = 0; i < 4; ++i)
+                s_stage[(16 * at + 4 * g + i) * C::ROWD + 16 * w + ln] = to_elem<C::F32>((Y[at][i] + y_empty) * rd[i]);
         }
         __syncthreads();
         store_stage<C>(rO, it * TB + tr, tr, tq, s_stage);
