@@ -927,15 +927,32 @@ __device__ inline void store_dx(const typename Prec<C::F32>::half (&xr)[4], rsrc
     }
 }
 
-// Store the staged [64][ROWD] tile (thread: row tr, quarter tq) to in-chunk
-// row rowi of the output (rows past the chunk are dropped).
+// Store the transposed read-out tile Yt (C layout with rows = the wave's 16
+// columns, columns = tokens: lane (ln, g) holds columns cb + 4 g .. +3 of
+// token 16 at + ln) to in-chunk rows r0 + 16 at + ln of the output, scaling
+// token rows by rs[at] and adding add[i] per column (rows past the chunk are
+// dropped).
 template <class C>
-__device__ inline void store_stage(rsrc_t out, int rowi, int tr, int tq, const typename Prec<C::F32>::elem* s_stage) {
+__device__ inline void store_rows_t(rsrc_t out, int r0, int cb, int ln, int g, const f32x4 (&Yt)[4],
+                                    const float (&rs)[4], const float (&add)[4]) {
     constexpr int es = C::F32 ? 4 : 2;
-    const typename Prec<C::F32>::elem* src = s_stage + tr * C::ROWD + 16 * tq;
-    bstore_frag<C::F32>(out, rowi * row_bytes<C::F32>() + 16 * tq * es, ld_frag<C::F32>(src));
-    bstore_frag<C::F32>(out, rowi * row_bytes<C::F32>() + (16 * tq + 8) * es, ld_frag<C::F32>(src + 8));
+#pragma unroll
+    for (int at = 0; at < 4; ++at) {
+        f32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = (Yt[at][i] + add[i]) * rs[at];
+        const int off = (r0 + 16 * at + ln) * row_bytes<C::F32>() + (cb + 4 * g) * es;
+        if constexpr (C::F32) {
+            bstore128(out, off, __builtin_bit_cast(u32x4, o));
+        } else {
+            bf16x4 ob;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ob[i] = (__bf16)o[i];
+            bstore64(out, off, __builtin_bit_cast(u32x2, ob));
+        }
+    }
 }
+
 
 // LDS budget: W' is staged when it fits next to the tiles at the target
 // number of workgroups per CU, else the projections read it from global memory.
@@ -976,8 +993,6 @@ struct FwdLds {
     static constexpr int ZS = ZV;                               // value-tile row stride
     static constexpr int n_zr = TB * ZS;                        // [z_b | mass], token rows
     static constexpr int n_sc = TB * C::ROWT;                   // intra scores [a][b]
-    static constexpr int n_stage = TB * C::ROWD;                // O staging (alias of the a-side buffers)
-    static_assert(n_stage <= 2 * n_rows, "staging must fit the feature tiles");
     static constexpr int o_rows = 0;                            // [2][rows]
     static constexpr int o_brow = o_rows + 2 * n_rows;          // [2][brow]
     static constexpr int o_zr = o_brow + 2 * n_brow;
@@ -1000,7 +1015,6 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
     elem* s_brow = lds + LD::o_brow;
     elem* s_zr = lds + LD::o_zr;
     elem* s_sc = lds + LD::o_sc;
-    elem* s_stage = lds + LD::o_rows;   // alias after the feature-block loop
     float* f_Dpart = ldf;               // [4][64]
     float* f_Dint = ldf + 4 * TB;       // [64]
     float* f_rD = ldf + 5 * TB;         // [64]
@@ -1069,7 +1083,9 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
         // L times the value sums of this wave's columns (held by lane group 0
         // as table 0's first feature, before this sub-block's updates) and L
         // times the number of keys in the state.
-        const float y_empty = (float)a.L * __shfl(Macc[0][0], ln);
+        float y_empty[4];   // columns 16 w + 4 g + i of the transposed read-out
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y_empty[i] = (float)a.L * __shfl(Macc[0][0], 4 * g + i);
         const float d_empty = (float)a.L * (float)(causal ? t0 : a.N);
 
         f32x4 Y[4], Dacc[4], Sc[4];
@@ -1121,7 +1137,7 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
                 const frag mf = pack_nonempty<C>(kc, Macc[2 * kc], Macc[2 * kc + 1]);
 #pragma unroll
                 for (int at = 0; at < 4; ++at)
-                    Y[at] = mma(ld_frag<C::F32>(rows_b + (16 * at + ln) * C::ROWF + 32 * kcl + 8 * g), mf, Y[at]);
+                    Y[at] = mma(mf, ld_frag<C::F32>(rows_b + (16 * at + ln) * C::ROWF + 32 * kcl + 8 * g), Y[at]);
             }
             const int kw = w - C::own_base(fb);
             if (kw >= 0 && kw < C::FBK) {
@@ -1177,20 +1193,14 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
                 const frag zt = val_operand<C, LD::ZS>(s_zr, 16 * w, s, ln, g);
 #pragma unroll
                 for (int at = 0; at < 4; ++at)
-                    Y[at] = mma(ld_frag<C::F32>(s_sc + (16 * at + ln) * C::ROWT + 32 * s + 8 * g), zt, Y[at]);
+                    Y[at] = mma(zt, ld_frag<C::F32>(s_sc + (16 * at + ln) * C::ROWT + 32 * s + 8 * g), Y[at]);
             }
         }
         __syncthreads();
+        float rd[4];
 #pragma unroll
-        for (int at = 0; at < 4; ++at) {
-            const f32x4 rd = *reinterpret_cast<const f32x4*>(f_rD + 16 * at + 4 * g);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                s_stage[(16 * at + 4 * g + i) * C::ROWD + 16 * w + ln] = to_elem<C::F32>((Y[at][i] + y_empty) * rd[i]);
-        }
-        __syncthreads();
-        store_stage<C>(rO, it * TB + tr, tr, tq, s_stage);
-        __syncthreads();
+        for (int at = 0; at < 4; ++at) rd[at] = f_rD[16 * at + ln];
+        store_rows_t<C>(rO, it * TB, 16 * w, ln, g, Y, rd, y_empty);
     }
 }
 
@@ -1416,7 +1426,6 @@ struct BwdKLds {
     static constexpr int n_ms = DK ? C::FBK * 32 * C::ROWE : 0; // sketch rows
     // per-sub-block tiles
     static constexpr int n_sc = DV ? TB * C::ROWT : 0;          // intra scores [a][b]
-    static constexpr int n_stage = DV ? TB * C::ROWD : 0;       // dV staging
     // [g | e] rows: the dK pass also reads them as intra-product rows over the
     // augmented width, the dV pass only through transpose reads
     static constexpr int ZS = DK ? C::ROWE : ZV;
@@ -1428,10 +1437,8 @@ struct BwdKLds {
     static constexpr int n_yr = DK ? TB * C::ROWE : 0;          // [v | 1] rows
     // Tiles live outside the block loop share the block buffers where they
     // fit: the intra scores the first query-feature buffer (dV) or the feature
-    // buffers (dK), the residual rows the feature buffers, the staging the
-    // first key-feature buffer.
+    // buffers (dK), the residual rows the feature buffers.
     static constexpr bool SC_SHARED = DV ? n_sc <= n_brow : n_sc <= NB * n_cols;
-    static constexpr bool STAGE_SHARED = n_stage <= NB * (n_rows + n_brow);
     static constexpr bool ZLO_SHARED = NB == 2 && n_zlo <= 2 * n_cols;
     static constexpr int o_rows = 0;                            // [NB][rows | brow]
     static constexpr int o_brow = o_rows + n_rows;
@@ -1443,11 +1450,9 @@ struct BwdKLds {
     static constexpr int o_x0 = o_yr + n_yr;                    // unshared tiles follow
     static constexpr int o_sc = SC_SHARED ? (DV ? o_brow : o_cols) : o_x0;
     static constexpr int o_x1 = o_x0 + (SC_SHARED ? 0 : n_sc);
-    static constexpr int o_stage = STAGE_SHARED ? o_rows : o_x1;
-    static constexpr int o_x2 = o_x1 + (STAGE_SHARED ? 0 : n_stage);
+    static constexpr int o_x2 = o_x1;
     static constexpr int o_zlo = ZLO_SHARED ? o_cols : o_x2;
     static constexpr int n_elem = o_x2 + (ZLO_SHARED ? 0 : n_zlo);
-    static_assert(!(DV && SC_SHARED && STAGE_SHARED) || n_stage <= n_rows, "staging and scores overlap");
     // workgroups per CU where registers (bf16, up to 8 feature chunks) and LDS
     // allow: three for the dV pass, two for the dK pass
     static constexpr int BYTES = n_elem * (int)sizeof(elem);
@@ -1472,7 +1477,6 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
     elem* s_zr = lds + LD::o_zr;
     elem* s_yr = lds + LD::o_yr;
     elem* s_zlo = lds + LD::o_zlo;
-    elem* s_stage = lds + LD::o_stage;
 
     const int lane = threadIdx.x & 63, ln = lane & 15, g = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1616,7 +1620,7 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
                     const frag mf = pack<C::F32>(Macc[2 * kc], Macc[2 * kc + 1]);
 #pragma unroll
                     for (int at = 0; at < 4; ++at)
-                        Y[at] = mma(ld_frag<C::F32>(rows_b + (16 * at + ln) * C::ROWF + 32 * kcl + 8 * g), mf, Y[at]);
+                        Y[at] = mma(mf, ld_frag<C::F32>(rows_b + (16 * at + ln) * C::ROWF + 32 * kcl + 8 * g), Y[at]);
                 }
             }
             if constexpr (DK) {
@@ -1665,16 +1669,12 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
                     const frag zt = val_operand<C, LD::ZS>(s_zr, 16 * w, s, ln, g);
 #pragma unroll
                     for (int at = 0; at < 4; ++at)
-                        Y[at] = mma(ld_frag<C::F32>(s_sc + (16 * at + ln) * C::ROWT + 32 * s + 8 * g), zt, Y[at]);
+                        Y[at] = mma(zt, ld_frag<C::F32>(s_sc + (16 * at + ln) * C::ROWT + 32 * s + 8 * g), Y[at]);
                 }
+                __syncthreads();   // the value rows and scores are read before the next sub-block rewrites them
             }
-#pragma unroll
-            for (int at = 0; at < 4; ++at)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    s_stage[(16 * at + 4 * g + i) * C::ROWD + 16 * w + ln] = to_elem<C::F32>(Y[at][i]);
-            __syncthreads();
-            store_stage<C>(rOut1, r0_of(it) + tr, tr, tq, s_stage);
+            const float one[4] = {1.f, 1.f, 1.f, 1.f}, zero[4] = {0.f, 0.f, 0.f, 0.f};
+            store_rows_t<C>(rOut1, r0_of(it), 16 * w, ln, g, Y, one, zero);
         }
         if constexpr (DK) store_dx<C>(xr, rOut0, r0_of(it) + my, g, inv_a, dX);
     }
