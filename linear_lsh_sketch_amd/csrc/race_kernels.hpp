@@ -508,7 +508,7 @@ __device__ inline void emit_tile(int tb, int w, int ln, int g, const float phi[C
 // rows past the chunk are dropped) for later passes.
 template <class C, bool KEEP, class WS>
 __device__ inline void block_features(const WS& wsrc, int fb, int lane, int w, int ln, int g,
-                                      const typename Prec<C::F32>::frag xf[2], float inv, bool valid, float beta,
+                                      const typename Prec<C::F32>::frag xf[2], float inv, float beta,
                                       int L, typename Prec<C::F32>::elem* rows /* [64][ROWF] or null */,
                                       typename Prec<C::F32>::frag (&phi_frag)[C::FBK], const PlaneRows& out,
                                       bool store, int rowi) {
@@ -522,7 +522,7 @@ __device__ inline void block_features(const WS& wsrc, int fb, int lane, int w, i
         tanh4(hs, u);
         const typename Prec<C::F32>::uvec uq = round_u<C::F32>(u);
         tplanes<C::F32>(uq, beta, tt, gt);
-        monomial_features<C>(t, g, tt, L, valid, phi);
+        monomial_features<C>(t, g, tt, L, phi);
         if (store) store_u<C>(out, rowi, t, g, uq);
         emit_tile<C, KEEP>(tb, w, ln, g, phi, rows, phi_frag);
     }
@@ -531,7 +531,7 @@ __device__ inline void block_features(const WS& wsrc, int fb, int lane, int w, i
 // The same from stored plane values (no projection); when KEEP, also return
 // per tile the plane values t and dt/dh for the chain rule.
 template <class C, bool KEEP>
-__device__ inline void block_features_cached(const Planes<C>& pl, int fb, int w, int ln, int g, bool valid, int L,
+__device__ inline void block_features_cached(const Planes<C>& pl, int fb, int w, int ln, int g, int L,
                                              float beta, typename Prec<C::F32>::elem* rows,
                                              typename Prec<C::F32>::frag (&phi_frag)[C::FBK],
                                              float (&t_keep)[C::TPB][4], float (&gt_keep)[C::TPB][4]) {
@@ -540,7 +540,7 @@ __device__ inline void block_features_cached(const Planes<C>& pl, int fb, int w,
         const int t = fb * C::TPB + tb;
         float tt[4], gt[4], phi[C::KB * 8];
         tplanes<C::F32>(pl.u[tb], beta, tt, gt);
-        monomial_features<C>(t, g, tt, L, valid, phi);
+        monomial_features<C>(t, g, tt, L, phi);
         if constexpr (KEEP) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -646,7 +646,6 @@ __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
     for (int it = 0; it < nsub; ++it) {
         const int64_t t0 = seg0 + (int64_t)it * TB;
         const int nv = nv_of(it);
-        const bool valid = my < nv;
         const int rowi = it * TB + my;
         frag xf[2] = {nx[0], nx[1]}, zr[2] = {nz[0], nz[1]};
         const float dz = nd, ez = ne;
@@ -667,9 +666,9 @@ __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
                 if (fb + 1 < C::NBLK) issue_planes(it, fb + 1);
                 else if (it + 1 < nsub) issue_planes(it + 1, 0);
                 float us[C::TPB][4], ug[C::TPB][4];
-                block_features_cached<C, false>(pl, fb, w, ln, g, valid, a.L, a.beta, s_rows, unused, us, ug);
+                block_features_cached<C, false>(pl, fb, w, ln, g, a.L, a.beta, s_rows, unused, us, ug);
             } else {
-                block_features<C, false>(wsrc, fb, lane, w, ln, g, xf, inv, valid, a.beta, a.L, s_rows, unused,
+                block_features<C, false>(wsrc, fb, lane, w, ln, g, xf, inv, a.beta, a.L, s_rows, unused,
                                          pr, u_out, rowi);
             }
             __syncthreads();
@@ -686,33 +685,36 @@ __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
 template <int KIND>
 __global__ __launch_bounds__(256) void k_scan(float* __restrict__ st, float* __restrict__ total,
                                               int nchunks, int elems) {
-    // Loads of a batch of chunks are issued together so the memory round trip
-    // is paid once per batch, not once per chunk; the running sum keeps the
-    // fixed chunk order (deterministic).
-    constexpr int BATCH = 16;
+    // The loads of the next batch of chunks are issued before the running sum
+    // and the stores of the current batch, so about 2 * BATCH loads per lane
+    // stay in flight (one wave per SIMD needs that many to cover the memory
+    // latency); the running sum keeps the fixed chunk order (deterministic).
+    constexpr int BATCH = 32;
     const int e = blockIdx.x * blockDim.x + threadIdx.x;
     const int bh = blockIdx.y;
     if (e >= elems) return;
     float* p = st + (size_t)bh * nchunks * elems + e;
+    auto at = [&](int c) -> float* {
+        return p + (size_t)((KIND == SCAN_REV_EXCL) ? nchunks - 1 - c : c) * elems;
+    };
+    auto load = [&](int c0, float (&v)[BATCH]) {
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) v[k] = *at(c0 + k < nchunks ? c0 + k : nchunks - 1);
+    };
     float run = 0.f;
-    const int nfull = nchunks / BATCH * BATCH;
+    float cur[BATCH], nxt[BATCH];
+    load(0, cur);
     for (int c0 = 0; c0 < nchunks; c0 += BATCH) {
-        float v[BATCH];
-        const int n = c0 < nfull ? BATCH : nchunks - c0;
+        if (c0 + BATCH < nchunks) load(c0 + BATCH, nxt);
 #pragma unroll
         for (int k = 0; k < BATCH; ++k) {
-            const int kk = k < n ? k : 0;
-            const int c = (KIND == SCAN_REV_EXCL) ? nchunks - 1 - (c0 + kk) : c0 + kk;
-            v[k] = p[(size_t)c * elems];
-        }
-#pragma unroll
-        for (int k = 0; k < BATCH; ++k) {
-            if (k < n) {
-                const int c = (KIND == SCAN_REV_EXCL) ? nchunks - 1 - (c0 + k) : c0 + k;
-                if constexpr (KIND != SCAN_TOTAL) p[(size_t)c * elems] = run;
-                run += v[k];
+            if (c0 + k < nchunks) {
+                if constexpr (KIND != SCAN_TOTAL) *at(c0 + k) = run;
+                run += cur[k];
             }
         }
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) cur[k] = nxt[k];
     }
     if constexpr (KIND == SCAN_TOTAL) total[(size_t)bh * elems + e] = run;
 }
@@ -1068,7 +1070,6 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
     for (int it = 0; it < nsub; ++it) {
         const int64_t t0 = seg0 + (int64_t)it * TB;
         const int nv = nv_of(it);
-        const bool valid = my < nv;
         const bool tok = tr < nv;
         const int rowi = it * TB + my;
         frag xa[2] = {n_xa[0], n_xa[1]}, zr[2] = {n_z[0], n_z[1]};
@@ -1108,11 +1109,11 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
                 if (fb + 1 < C::NBLK) issue_planes(it, fb + 1);
                 else if (it + 1 < nsub) issue_planes(it + 1, 0);
             }
-            block_features<C, true>(wsrc, fb, lane, w, ln, g, xa, inv_a, valid, a.beta, a.L, rows_b, phi, pra,
+            block_features<C, true>(wsrc, fb, lane, w, ln, g, xa, inv_a, a.beta, a.L, rows_b, phi, pra,
                                     u_out, rowi);
             if (causal) {
                 float us[C::TPB][4], ug[C::TPB][4];
-                block_features_cached<C, false>(pl, fb, w, ln, g, valid, a.L, a.beta, brow_b, unused, us, ug);
+                block_features_cached<C, false>(pl, fb, w, ln, g, a.L, a.beta, brow_b, unused, us, ug);
             }
         };
         features(0, phiA);
@@ -1370,7 +1371,7 @@ __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
             if (causal) {
                 frag unused[C::FBK];
                 float us[C::TPB][4], ug[C::TPB][4];
-                block_features_cached<C, false>(kb_, fb, w, ln, g, valid, a.L, a.beta, cols_b, unused, us, ug);
+                block_features_cached<C, false>(kb_, fb, w, ln, g, a.L, a.beta, cols_b, unused, us, ug);
             }
             __syncthreads();
             frag yf[3];
@@ -1540,7 +1541,6 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
     for (int it = 0; it < nsub; ++it) {
         const int64_t t0 = t0_of(it);
         const int nv = nv_of(it);
-        const bool valid = my < nv;
         const bool tok = tr < nv;
         if (!PREFETCH) issue(it);
         frag zr[2] = {n_z[0], n_z[1]}, yr[2] = {n_y[0], n_y[1]};
@@ -1595,11 +1595,11 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
             elem* cols_b = s_cols + bsel * LD::n_cols;
             elem* ms_b = s_ms + bsel * LD::n_ms;
             if constexpr (DV) {
-                block_features_cached<C, true>(ka, fb, w, ln, g, valid, a.L, a.beta, rows_b, phiA, us, ug);
+                block_features_cached<C, true>(ka, fb, w, ln, g, a.L, a.beta, rows_b, phiA, us, ug);
                 if (causal)
-                    block_features_cached<C, false>(qb, fb, w, ln, g, valid, a.L, a.beta, brow_b, unused, us, ug);
+                    block_features_cached<C, false>(qb, fb, w, ln, g, a.L, a.beta, brow_b, unused, us, ug);
             } else if (causal) {
-                block_features_cached<C, false>(qb, fb, w, ln, g, valid, a.L, a.beta, cols_b, unused, us, ug);
+                block_features_cached<C, false>(qb, fb, w, ln, g, a.L, a.beta, cols_b, unused, us, ug);
             }
             if constexpr (DK) write_sketch_rows<C>(fb, w, ln, g, Macc, Zacc, ms_b);
             __syncthreads();
