@@ -308,11 +308,10 @@ __device__ inline void tplanes(const typename Prec<F32>::uvec& uv, float beta, f
     rcp4(q, rq);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        // sign applied on the bits (equal to copysignf for the non-negative
-        // magnitude; a copysign here meets the bf16 packing of the features,
-        // which the gfx950 backend cannot fold)
-        t[i] = __builtin_bit_cast(float, __builtin_bit_cast(unsigned, (1.f - e[i]) * rq[i]) ^
-                                             (__builtin_bit_cast(unsigned, u[i]) & 0x80000000u));
+        // the sign goes on the numerator (the same value): a copysign as the
+        // last step meets the bf16 packing of the features, a fold the gfx950
+        // backend cannot select
+        t[i] = copysignf(1.f - e[i], u[i]) * rq[i];
         gt[i] = beta * (1.f - t[i] * t[i]) * (1.f - u[i] * u[i]);
     }
 }
@@ -320,39 +319,37 @@ __device__ inline void tplanes(const typename Prec<F32>::uvec& uv, float beta, f
 // Monomial features of projection tile t for one lane: phi[j] = psi of the
 // table and subset that lane feature j stands for (P = 4: the lane's table,
 // subset r = j + 8 kb; P < 4: table j / R of the lane, subset j % R).
-// Padded tables (index >= L) give phi = 0. Tokens past the end of the chunk
-// are not masked here: their plane values load as zero (finite features),
-// their value and mass rows are zero and the in-sub-block terms mask them,
-// so they contribute nothing.
+// Nothing is masked here. Padded tables (index >= L) have all-zero projection
+// rows, so t = 0 and only their empty subset is non-zero (1): the kernels
+// discount those where they enter (the forward leaves every empty subset out
+// of its state operands; the in-sub-block scores start from -n_pad; the dV
+// read-out subtracts n_pad times the empty-subset row). Tokens past the end
+// of the chunk load zero plane values (finite features); their value and
+// mass rows are zero and the in-sub-block terms mask them.
 template <class C>
-__device__ inline void monomial_features(int t, int g, const float tt[4], int L, float phi[C::KB * 8]) {
+__device__ inline void monomial_features(const float tt[4], float phi[C::KB * 8]) {
     if constexpr (C::P == 4) {
         const float lo[4] = {1.f, tt[0], tt[1], tt[0] * tt[1]};   // subsets of planes {0, 1}
         const float hi[4] = {1.f, tt[2], tt[3], tt[2] * tt[3]};   // subsets of planes {2, 3}
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             phi[r] = (r >> 2) == 0 ? lo[r & 3] : (r & 3) == 0 ? hi[r >> 2] : lo[r & 3] * hi[r >> 2];
-        if (L < C::MT * C::TPT) {   // some tables are padding (uniform branch)
-            // an empty volatile asm keeps this a branch: flattened into
-            // selects, the masking would cost every call
-            __asm__ volatile("");
-            const bool ok = (t * C::TPT + g) < L;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) phi[r] = ok ? phi[r] : 0.f;
-        }
     } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int tl = j / C::R, r = j % C::R;
-            const bool ok = (t * C::TPT + g * C::TPL + tl) < L;
             float v = 1.f;
 #pragma unroll
             for (int p = 0; p < C::P; ++p)
                 if ((r >> p) & 1) v *= tt[tl * C::Pp + p];
-            phi[j] = ok ? v : 0.f;
+            phi[j] = v;
         }
     }
 }
+
+// Number of padded tables (projection tiles hold MT * TPT table slots).
+template <class C>
+__device__ inline int padded_tables(int L) { return C::MT * C::TPT - L; }
 
 // Chain rule of monomial_features: given dA (gradient wrt the lane's
 // features, same layout as phi) return dh[4], the gradient wrt the

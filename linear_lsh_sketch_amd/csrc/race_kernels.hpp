@@ -454,7 +454,7 @@ __device__ inline typename Prec<C::F32>::frag val_operand(const typename Prec<C:
 // Sketch update for feature block fb from the b-side features (token-row tile
 // `brow`) and the value tile Zrow: value columns of wave w, then the mass
 // accumulators of the chunk wave w owns in this block.
-template <class C, bool MASS = true, int ZS = C::ROWE>
+template <class C, bool MASS = true, int ZS = C::ROWE, bool PIPE = false>
 __device__ inline void sketch_update(int fb, int w, int ln, int g, const typename Prec<C::F32>::elem* brow,
                                      const typename Prec<C::F32>::elem* Zrow, f32x4 Macc[C::NKC * 2],
                                      f32x4 Zacc[C::NOWN * 2]) {
@@ -462,14 +462,35 @@ __device__ inline void sketch_update(int fb, int w, int ln, int g, const typenam
     frag zt[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) zt[s] = val_operand<C, ZS>(Zrow, 16 * w, s, ln, g);
+    if constexpr (PIPE && !C::F32) {
+        // Operand reads run D products ahead of the matrix cores, pinned by
+        // scheduling groups (4 reads for the value operands and 2 D for the
+        // first feature operands, then one product and the next operand's 2
+        // reads at a time): the register-pressure schedule otherwise waits
+        // out every read's latency before its product.
+        constexpr int NM = C::FBK * 4, D = 4;
+        frag A[NM];
 #pragma unroll
-    for (int kcl = 0; kcl < C::FBK; ++kcl) {
-        const int kc = fb * C::FBK + kcl;
+        for (int j = 0; j < D; ++j) A[j] = feat_operand<C>(brow, j >> 2, (j >> 1) & 1, j & 1, ln, g);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 + 2 * D, 0);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int j = 0; j < NM; ++j) {
+            if (j + D < NM) A[j + D] = feat_operand<C>(brow, (j + D) >> 2, ((j + D) >> 1) & 1, (j + D) & 1, ln, g);
+            const int kc = fb * C::FBK + (j >> 2), h = (j >> 1) & 1, s2 = j & 1;
+            Macc[2 * kc + h] = mma(A[j], zt[s2], Macc[2 * kc + h]);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (j + D < NM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+    } else {
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
-                Macc[2 * kc + h] = mma(feat_operand<C>(brow, kcl, h, s, ln, g), zt[s], Macc[2 * kc + h]);
+        for (int kcl = 0; kcl < C::FBK; ++kcl) {
+            const int kc = fb * C::FBK + kcl;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    Macc[2 * kc + h] = mma(feat_operand<C>(brow, kcl, h, s, ln, g), zt[s], Macc[2 * kc + h]);
+            }
         }
     }
     const int kw = w - C::own_base(fb);        // local chunk whose mass this wave owns
@@ -488,7 +509,7 @@ __device__ inline void sketch_update(int fb, int w, int ln, int g, const typenam
 }
 
 // Pack the lane's features of tile tb of the block and write them to the
-// token-row tile `rows` (if set); KEEP returns the operands.
+// token-row tile `rows`; KEEP also returns the operands.
 template <class C, bool KEEP>
 __device__ inline void emit_tile(int tb, int w, int ln, int g, const float phi[C::KB * 8],
                                  typename Prec<C::F32>::elem* rows, typename Prec<C::F32>::frag (&phi_frag)[C::FBK]) {
@@ -497,21 +518,21 @@ __device__ inline void emit_tile(int tb, int w, int ln, int g, const float phi[C
         const int kcl = tb * C::KB + kb;
         const typename Prec<C::F32>::frag fr = pack8<C::F32>(phi + kb * 8);
         if constexpr (KEEP) phi_frag[kcl] = fr;
-        if (rows) st_frag<C::F32>(rows + (16 * w + ln) * C::ROWF + 32 * kcl + 8 * g, fr);
+        st_frag<C::F32>(rows + (16 * w + ln) * C::ROWF + 32 * kcl + 8 * g, fr);
     }
 }
 
 // Project the own 16-token tile for the tiles of feature block fb and write
-// the features to the token-row tile `rows` (if set); when KEEP,
+// the features to the token-row tile `rows`; when KEEP,
 // also return the lane's operands (one per chunk of the block) in phi_frag.
-// With `store` set, the plane values are stored to `out` (in-chunk row rowi;
-// rows past the chunk are dropped) for later passes.
+// The plane values are stored to `out` (in-chunk row rowi; rows past the
+// chunk, or every row when there is no cache, are dropped) for later passes.
 template <class C, bool KEEP, class WS>
 __device__ inline void block_features(const WS& wsrc, int fb, int lane, int w, int ln, int g,
                                       const typename Prec<C::F32>::frag xf[2], float inv, float beta,
-                                      int L, typename Prec<C::F32>::elem* rows /* [64][ROWF] or null */,
+                                      int L, typename Prec<C::F32>::elem* rows /* [64][ROWF] */,
                                       typename Prec<C::F32>::frag (&phi_frag)[C::FBK], const PlaneRows& out,
-                                      bool store, int rowi) {
+                                      int rowi) {
 #pragma unroll
     for (int tb = 0; tb < C::TPB; ++tb) {
         const int t = fb * C::TPB + tb;
@@ -522,8 +543,8 @@ __device__ inline void block_features(const WS& wsrc, int fb, int lane, int w, i
         tanh4(hs, u);
         const typename Prec<C::F32>::uvec uq = round_u<C::F32>(u);
         tplanes<C::F32>(uq, beta, tt, gt);
-        monomial_features<C>(t, g, tt, L, phi);
-        if (store) store_u<C>(out, rowi, t, g, uq);
+        monomial_features<C>(tt, phi);
+        store_u<C>(out, rowi, t, g, uq);
         emit_tile<C, KEEP>(tb, w, ln, g, phi, rows, phi_frag);
     }
 }
@@ -540,7 +561,7 @@ __device__ inline void block_features_cached(const Planes<C>& pl, int fb, int w,
         const int t = fb * C::TPB + tb;
         float tt[4], gt[4], phi[C::KB * 8];
         tplanes<C::F32>(pl.u[tb], beta, tt, gt);
-        monomial_features<C>(t, g, tt, L, phi);
+        monomial_features<C>(tt, phi);
         if constexpr (KEEP) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -584,7 +605,7 @@ struct TotLds {
 // keys' plane values); CACHED = true: gradient sketch of the queries,
 // [dO/D | e], from the queries' stored plane values.
 template <class C, bool CACHED>
-__global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 3))) void k_totals(TotArgs a) {
     using elem = typename Prec<C::F32>::elem;
     using frag = typename Prec<C::F32>::frag;
     using LD = TotLds<C, CACHED>;
@@ -615,7 +636,6 @@ __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
     const rsrc_t rD = rows_rsrc(CACHED ? a.Dv : nullptr, row0, nrows, 4);
     const rsrc_t rE = rows_rsrc(CACHED ? a.Ev : nullptr, row0, nrows, 4);
     const PlaneRows pr = plane_rows<C>(a.pc, row0, nrows);
-    const bool u_out = !CACHED && a.pc.u;
 
     f32x4 Macc[C::NKC * 2], Zacc[C::NOWN * 2];
 #pragma unroll
@@ -653,7 +673,7 @@ __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
         float inv = 0.f;
         if (!CACHED) {
             inv = row_inv_norm<C::F32>(xf);
-            if (u_out && g == 0) bstore_f32(pr.inv, rowi * 4, inv);
+            if (g == 0) bstore_f32(pr.inv, rowi * 4, inv);
         }
         const bool ok = tr < nv;
         if (!CACHED) write_aug<C, ZV>(zr, 1.f, ok ? 1.f : 0.f, s_zr);
@@ -669,10 +689,10 @@ __global__ __launch_bounds__(NT) void k_totals(TotArgs a) {
                 block_features_cached<C, false>(pl, fb, w, ln, g, a.L, a.beta, s_rows, unused, us, ug);
             } else {
                 block_features<C, false>(wsrc, fb, lane, w, ln, g, xf, inv, a.beta, a.L, s_rows, unused,
-                                         pr, u_out, rowi);
+                                         pr, rowi);
             }
             __syncthreads();
-            sketch_update<C, true, ZV>(fb, w, ln, g, s_rows, s_zr, Macc, Zacc);
+            sketch_update<C, true, ZV, true>(fb, w, ln, g, s_rows, s_zr, Macc, Zacc);
             __syncthreads();
         }
     }
@@ -1007,7 +1027,8 @@ struct FwdLds {
 };
 
 template <class C, bool CAUSAL>
-__global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
+__global__ __launch_bounds__(NT, (FwdLds<C>::OCC))
+__attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(PassArgs a) {
     using elem = typename Prec<C::F32>::elem;
     using frag = typename Prec<C::F32>::frag;
     using LD = FwdLds<C>;
@@ -1044,7 +1065,6 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
     const rsrc_t rO = rows_rsrc(a.out0, row0, nrows, row_bytes<C::F32>());
     const rsrc_t rD = rows_rsrc(a.Dv, row0, nrows, 4);
     const PlaneRows pra = plane_rows<C>(a.ca, row0, nrows), prb = plane_rows<C>(a.cb, row0, nrows);
-    const bool u_out = a.ca.u != nullptr;   // keep the queries' plane values for the backward
 
     f32x4 Macc[C::NKC * 2], Zacc[C::NOWN * 2];
     load_state<C>(a.state + bh * a.state_bh_stride + c * a.state_chunk_stride, w, ln, g, Macc, Zacc);
@@ -1076,7 +1096,7 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
         if (it + 1 < nsub) issue(it + 1);
 
         const float inv_a = row_inv_norm<C::F32>(xa);
-        if (u_out && g == 0) bstore_f32(pra.inv, rowi * 4, inv_a);
+        if (g == 0) bstore_f32(pra.inv, rowi * 4, inv_a);   // dropped without a cache
         write_aug<C, ZV>(zr, 1.f, tok ? 1.f : 0.f, s_zr);
 
         // The empty subset's state rows (plain sums of the keys' [v | 1], the
@@ -1089,18 +1109,20 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
         for (int i = 0; i < 4; ++i) y_empty[i] = (float)a.L * __shfl(Macc[0][0], 4 * g + i);
         const float d_empty = (float)a.L * (float)(causal ? t0 : a.N);
 
+        // the scores start at -n_pad: each padded table adds 1 (its empty
+        // subset) to every query-key feature product
+        const float sc0 = -(float)padded_tables<C>(a.L);
         f32x4 Y[4], Dacc[4], Sc[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             Y[i] = f32x4{0.f, 0.f, 0.f, 0.f};
             Dacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-            Sc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            Sc[i] = f32x4{sc0, sc0, sc0, sc0};
         }
         // Software-pipelined feature blocks: after the barrier that publishes
         // block fb, a wave computes and writes the features of block fb + 1
         // (other buffer) while its matrix-core work on block fb proceeds.
-        frag phiA[C::FBK], phiN[C::FBK];
-        auto features = [&](int fb, frag (&phi)[C::FBK]) {
+        auto features = [&](int fb) {
             frag unused[C::FBK];
             elem* rows_b = s_rows + (fb & 1) * LD::n_rows;
             elem* brow_b = s_brow + (fb & 1) * LD::n_brow;
@@ -1109,27 +1131,29 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
                 if (fb + 1 < C::NBLK) issue_planes(it, fb + 1);
                 else if (it + 1 < nsub) issue_planes(it + 1, 0);
             }
-            block_features<C, true>(wsrc, fb, lane, w, ln, g, xa, inv_a, a.beta, a.L, rows_b, phi, pra,
-                                    u_out, rowi);
+            block_features<C, false>(wsrc, fb, lane, w, ln, g, xa, inv_a, a.beta, a.L, rows_b, unused, pra,
+                                     rowi);
             if (causal) {
                 float us[C::TPB][4], ug[C::TPB][4];
                 block_features_cached<C, false>(pl, fb, w, ln, g, a.L, a.beta, brow_b, unused, us, ug);
             }
         };
-        features(0, phiA);
+        features(0);
 #pragma unroll
         for (int fb = 0; fb < C::NBLK; ++fb) {
             const elem* rows_b = s_rows + (fb & 1) * LD::n_rows;
             const elem* brow_b = s_brow + (fb & 1) * LD::n_brow;
             __syncthreads();
-            if (fb + 1 < C::NBLK) features(fb + 1, phiN);
+            if (fb + 1 < C::NBLK) features(fb + 1);
             if (causal) {
+                // own features from the tile (not kept in registers)
 #pragma unroll
-                for (int bt = 0; bt < 4; ++bt) {
+                for (int kcl = 0; kcl < C::FBK; ++kcl) {
+                    const frag pa = ld_frag<C::F32>(rows_b + my * C::ROWF + 32 * kcl + 8 * g);
 #pragma unroll
-                    for (int kcl = 0; kcl < C::FBK; ++kcl)
-                        Sc[bt] = mma(ld_frag<C::F32>(brow_b + (16 * bt + ln) * C::ROWF + 32 * kcl + 8 * g),
-                                     phiA[kcl], Sc[bt]);
+                    for (int bt = 0; bt < 4; ++bt)
+                        Sc[bt] = mma(ld_frag<C::F32>(brow_b + (16 * bt + ln) * C::ROWF + 32 * kcl + 8 * g), pa,
+                                     Sc[bt]);
                 }
             }
 #pragma unroll
@@ -1147,9 +1171,7 @@ __global__ __launch_bounds__(NT, (FwdLds<C>::OCC)) void k_fwd(PassArgs a) {
                 for (int at = 0; at < 4; ++at)
                     Dacc[at] = mma(ld_frag<C::F32>(rows_b + (16 * at + ln) * C::ROWF + 32 * kw + 8 * g), zf, Dacc[at]);
             }
-            if (causal) sketch_update<C, true, ZV>(fb, w, ln, g, brow_b, s_zr, Macc, Zacc);
-#pragma unroll
-            for (int k = 0; k < C::FBK; ++k) phiA[k] = phiN[k];
+            if (causal) sketch_update<C, true, ZV, true>(fb, w, ln, g, brow_b, s_zr, Macc, Zacc);
         }
         // intra-sub-block term: scores of visible keys b <= a. The value
         // readout multiplies the scores rounded to the operand type, so the
@@ -1243,7 +1265,8 @@ struct BwdQLds {
 };
 
 template <class C, bool CAUSAL>
-__global__ __launch_bounds__(NT, (BwdQLds<C>::OCC)) void k_bwd_q(PassArgs a) {
+__global__ __launch_bounds__(NT, (BwdQLds<C>::OCC))
+__attribute__((amdgpu_waves_per_eu(BwdQLds<C>::OCC, BwdQLds<C>::OCC))) void k_bwd_q(PassArgs a) {
     using elem = typename Prec<C::F32>::elem;
     using frag = typename Prec<C::F32>::frag;
     using LD = BwdQLds<C>;
@@ -1464,7 +1487,8 @@ struct BwdKLds {
 };
 
 template <class C, bool CAUSAL, int PART>
-__global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs a) {
+__global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC))
+__attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC))) void k_bwd_k(PassArgs a) {
     using elem = typename Prec<C::F32>::elem;
     using frag = typename Prec<C::F32>::frag;
     using LD = BwdKLds<C, PART>;
@@ -1568,11 +1592,22 @@ __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC)) void k_bwd_k(PassArgs 
             intra_operand<C, true, false, LD::ZLO>(s_zr, s_zlo, s_yr, nullptr, first, w, ln, g, my, nv, Cf);
         if (LD::ZLO && LD::ZLO_SHARED && causal && first)
             __syncthreads();   // the residual rows are read; their space becomes the feature tiles
+        // Padded tables: their empty subset (1) adds 1 to every feature
+        // product, so the dV scores start at -n_pad, and n_pad times the
+        // empty-subset row of the gradient sketch (the same for every table;
+        // table 0's, held by lane group 0, before this sub-block's updates) is
+        // taken off the dV read-out (columns 16 w + 4 g + i).
+        const int npad = padded_tables<C>(a.L);
+        float y0[4] = {0.f, 0.f, 0.f, 0.f};
+        if (DV && npad > 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y0[i] = -(float)npad * __shfl(Macc[0][0], 4 * g + i);
+        }
         f32x4 Y[4], Sc[4], dX[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            Y[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-            Sc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            Y[i] = f32x4{y0[0], y0[1], y0[2], y0[3]};
+            Sc[i] = f32x4{-(float)npad, -(float)npad, -(float)npad, -(float)npad};
             dX[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         f32x4 dhp[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
