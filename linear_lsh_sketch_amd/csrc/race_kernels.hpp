@@ -1630,7 +1630,7 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
             elem* cols_b = s_cols + bsel * LD::n_cols;
             elem* ms_b = s_ms + bsel * LD::n_ms;
             if constexpr (DV) {
-                block_features_cached<C, true>(ka, fb, w, ln, g, a.L, a.beta, rows_b, phiA, us, ug);
+                block_features_cached<C, false>(ka, fb, w, ln, g, a.L, a.beta, rows_b, phiA, us, ug);
                 if (causal)
                     block_features_cached<C, false>(qb, fb, w, ln, g, a.L, a.beta, brow_b, unused, us, ug);
             } else if (causal) {
@@ -1640,12 +1640,14 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
             __syncthreads();
             if constexpr (DV) {
                 if (causal) {
+                    // own features from the tile (not kept in registers)
 #pragma unroll
-                    for (int bt = 0; bt < 4; ++bt) {
+                    for (int kcl = 0; kcl < C::FBK; ++kcl) {
+                        const frag pa = ld_frag<C::F32>(rows_b + my * C::ROWF + 32 * kcl + 8 * g);
 #pragma unroll
-                        for (int kcl = 0; kcl < C::FBK; ++kcl)
-                            Sc[bt] = mma(ld_frag<C::F32>(brow_b + (16 * bt + ln) * C::ROWF + 32 * kcl + 8 * g),
-                                         phiA[kcl], Sc[bt]);
+                        for (int bt = 0; bt < 4; ++bt)
+                            Sc[bt] = mma(ld_frag<C::F32>(brow_b + (16 * bt + ln) * C::ROWF + 32 * kcl + 8 * g), pa,
+                                         Sc[bt]);
                     }
                 }
                 // dV readout of the value columns of this wave (before this block's update)
@@ -1681,7 +1683,7 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
                     chain_backproject<C>(t, dA, tt, gt, wf[tb], dhp, dX);
                 }
             }
-            if (causal) sketch_update<C, DK, LD::ZS>(fb, w, ln, g, DV ? brow_b : cols_b, s_zr, Macc, Zacc);
+            if (causal) sketch_update<C, DK, LD::ZS, DV>(fb, w, ln, g, DV ? brow_b : cols_b, s_zr, Macc, Zacc);
             if (LD::NB == 1) __syncthreads();   // single buffer: reads done before the next block's writes
         }
         if (LD::NB == 2) __syncthreads();   // the block tiles are read; the sub-block tiles below reuse them
