@@ -103,9 +103,16 @@ def test_fp32_all_planes(lib, P, L, causal):
     run_case(lib, 1, 1, 150, P, L, "f32", causal, 100, beta=0.8, seed=7 + P)
 
 
-@pytest.mark.parametrize("P,L", [(1, 20), (2, 16), (3, 8), (4, 32)])
+@pytest.mark.parametrize("P,L", [(1, 20), (2, 16), (3, 8), (4, 32), (4, 5), (4, 13)])
 def test_bf16_causal_planes(lib, P, L):
+    # (1, 20), (4, 5) and (4, 13) leave table slots of the last projection
+    # tile empty (padded tables)
     run_case(lib, 1, 1, 333, P, L, "bf16", True, 128, beta=1.5, seed=11 + P)
+
+
+@pytest.mark.parametrize("P,L", [(4, 5), (2, 3)])
+def test_bf16_noncausal_padded_tables(lib, P, L):
+    run_case(lib, 2, 2, 300, P, L, "bf16", False, 64, beta=1.2, seed=31 + L)
 
 
 @pytest.mark.parametrize("N,chunk", [(1, 1), (63, 1000), (64, 64), (65, 7), (130, 1)])
