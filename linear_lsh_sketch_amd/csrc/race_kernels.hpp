@@ -363,6 +363,33 @@ __device__ inline void load_state(const float* __restrict__ st, int w, int ln, i
     }
 }
 
+// The same state in the transposed accumulator layout (TR): tile (kc, h)
+// holds value columns 16 w + 4 g + i (rows) of accumulator rows 32 kc + 16 h +
+// ln (columns; feature 32 kc + 8 (ln / 4) + 4 h + ln % 4), so a lane reads
+// four consecutive floats, and later writes four consecutive columns of one
+// sketch row. The mass of the chunks a wave owns sits at (g, i) = (0, 0).
+template <class C>
+__device__ inline void load_state_t(const float* __restrict__ st, int w, int ln, int g,
+                                    f32x4 Macc[C::NKC * 2], f32x4 Zacc[C::NOWN * 2]) {
+#pragma unroll
+    for (int kc = 0; kc < C::NKC; ++kc)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int f = 32 * kc + 8 * (ln >> 2) + 4 * h + (ln & 3);
+            Macc[2 * kc + h] = *reinterpret_cast<const f32x4*>(st + (size_t)f * DH + 16 * w + 4 * g);
+        }
+#pragma unroll
+    for (int j = 0; j < C::NOWN; ++j) {
+        const int kc = NW * j + w;
+        const bool owner = kc < C::NKC && g == 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int f = 32 * (owner ? kc : 0) + 8 * (ln >> 2) + 4 * h + (ln & 3);
+            Zacc[2 * j + h] = f32x4{owner ? st[(size_t)C::F * DH + f] : 0.f, 0.f, 0.f, 0.f};
+        }
+    }
+}
+
 template <class C>
 __device__ inline void store_state(float* __restrict__ st, int w, int ln, int g,
                                    const f32x4 Macc[C::NKC * 2], const f32x4 Zacc[C::NOWN * 2]) {
@@ -454,7 +481,7 @@ __device__ inline typename Prec<C::F32>::frag val_operand(const typename Prec<C:
 // Sketch update for feature block fb from the b-side features (token-row tile
 // `brow`) and the value tile Zrow: value columns of wave w, then the mass
 // accumulators of the chunk wave w owns in this block.
-template <class C, bool MASS = true, int ZS = C::ROWE, bool PIPE = false>
+template <class C, bool MASS = true, int ZS = C::ROWE, bool PIPE = false, bool TR = false>
 __device__ inline void sketch_update(int fb, int w, int ln, int g, const typename Prec<C::F32>::elem* brow,
                                      const typename Prec<C::F32>::elem* Zrow, f32x4 Macc[C::NKC * 2],
                                      f32x4 Zacc[C::NOWN * 2]) {
@@ -462,6 +489,7 @@ __device__ inline void sketch_update(int fb, int w, int ln, int g, const typenam
     frag zt[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) zt[s] = val_operand<C, ZS>(Zrow, 16 * w, s, ln, g);
+    static_assert(!(PIPE && TR), "the pipelined update uses the plain layout");
     if constexpr (PIPE && !C::F32) {
         // Operand reads run D products ahead of the matrix cores, pinned by
         // scheduling groups (4 reads for the value operands and 2 D for the
@@ -488,8 +516,12 @@ __device__ inline void sketch_update(int fb, int w, int ln, int g, const typenam
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
 #pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    Macc[2 * kc + h] = mma(feat_operand<C>(brow, kcl, h, s, ln, g), zt[s], Macc[2 * kc + h]);
+                for (int s = 0; s < 2; ++s) {
+                    if constexpr (TR)
+                        Macc[2 * kc + h] = mma(zt[s], feat_operand<C>(brow, kcl, h, s, ln, g), Macc[2 * kc + h]);
+                    else
+                        Macc[2 * kc + h] = mma(feat_operand<C>(brow, kcl, h, s, ln, g), zt[s], Macc[2 * kc + h]);
+                }
             }
         }
     }
@@ -501,9 +533,14 @@ __device__ inline void sketch_update(int fb, int w, int ln, int g, const typenam
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
-                Zacc[2 * C::zidx(fb) + h] =
-                    mma(feat_operand<C>(brow, kw, h, s, ln, g), zm[s], Zacc[2 * C::zidx(fb) + h]);
+            for (int s = 0; s < 2; ++s) {
+                if constexpr (TR)
+                    Zacc[2 * C::zidx(fb) + h] =
+                        mma(zm[s], feat_operand<C>(brow, kw, h, s, ln, g), Zacc[2 * C::zidx(fb) + h]);
+                else
+                    Zacc[2 * C::zidx(fb) + h] =
+                        mma(feat_operand<C>(brow, kw, h, s, ln, g), zm[s], Zacc[2 * C::zidx(fb) + h]);
+            }
         }
     }
 }
@@ -769,9 +806,25 @@ struct PassArgs {
 // [FBK*32][ROWE], value columns of wave w and the mass column (64) from the
 // wave that owns it. (In the monomial basis only the empty subset's rows carry
 // the large plain sums, and its dA is not used.)
-template <class C>
+template <class C, bool TR = false>
 __device__ inline void write_sketch_rows(int fb, int w, int ln, int g, const f32x4 Macc[C::NKC * 2],
                                          const f32x4 Zacc[C::NOWN * 2], typename Prec<C::F32>::elem* s_ms) {
+    if constexpr (TR) {
+        // transposed accumulators: four consecutive columns of one row per tile
+#pragma unroll
+        for (int kcl = 0; kcl < C::FBK; ++kcl)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                st_half<C::F32>(s_ms + (32 * kcl + 16 * h + ln) * C::ROWE + 16 * w + 4 * g,
+                                Macc[2 * (fb * C::FBK + kcl) + h]);
+        const int kw = w - C::own_base(fb);
+        if (kw >= 0 && kw < C::FBK && g == 0) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                s_ms[(32 * kw + 16 * h + ln) * C::ROWE + 64] = to_elem<C::F32>(Zacc[2 * C::zidx(fb) + h][0]);
+        }
+        return;
+    }
 #pragma unroll
     for (int kcl = 0; kcl < C::FBK; ++kcl)
 #pragma unroll
@@ -1292,7 +1345,11 @@ __attribute__((amdgpu_waves_per_eu(BwdQLds<C>::OCC, BwdQLds<C>::OCC))) void k_bw
     __syncthreads();   // the padding is written by all waves, read by each
 
     f32x4 Macc[C::NKC * 2], Zacc[C::NOWN * 2];
-    load_state<C>(a.state + bh * a.state_bh_stride + c * a.state_chunk_stride, w, ln, g, Macc, Zacc);
+    // bf16: the state in the transposed accumulator layout (sketch rows are
+    // then written four columns at a time)
+    constexpr bool TR = !C::F32;
+    if constexpr (TR) load_state_t<C>(a.state + bh * a.state_bh_stride + c * a.state_chunk_stride, w, ln, g, Macc, Zacc);
+    else load_state<C>(a.state + bh * a.state_bh_stride + c * a.state_chunk_stride, w, ln, g, Macc, Zacc);
 
     const int nsub = (int)((seg1 - seg0 + TB - 1) / TB);
     const int my = 16 * w + ln;
@@ -1390,7 +1447,7 @@ __attribute__((amdgpu_waves_per_eu(BwdQLds<C>::OCC, BwdQLds<C>::OCC))) void k_bw
             else if (it + 1 < nsub) issue_planes(it + 1, 0);
             elem* ms_b = s_ms + (fb & 1) * LD::n_ms;
             elem* cols_b = s_cols + (fb & 1) * LD::n_cols;
-            write_sketch_rows<C>(fb, w, ln, g, Macc, Zacc, ms_b);
+            write_sketch_rows<C, TR>(fb, w, ln, g, Macc, Zacc, ms_b);
             if (causal) {
                 frag unused[C::FBK];
                 float us[C::TPB][4], ug[C::TPB][4];
@@ -1418,7 +1475,7 @@ __attribute__((amdgpu_waves_per_eu(BwdQLds<C>::OCC, BwdQLds<C>::OCC))) void k_bw
                 }
                 chain_backproject<C>(t, dA, tt, gt, wf[tb], dhp, dX);
             }
-            if (causal) sketch_update<C>(fb, w, ln, g, cols_b, s_zr, Macc, Zacc);
+            if (causal) sketch_update<C, true, C::ROWE, false, TR>(fb, w, ln, g, cols_b, s_zr, Macc, Zacc);
         }
         __syncthreads();   // the next sub-block rewrites the y and z rows
         store_dx<C>(xr, rOut, rowi, g, inv_a, dX);
@@ -1518,7 +1575,11 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
     __syncthreads();   // the padding is written by all waves, read by each
 
     f32x4 Macc[C::NKC * 2], Zacc[C::NOWN * 2];
-    load_state<C>(a.state + bh * a.state_bh_stride + c * a.state_chunk_stride, w, ln, g, Macc, Zacc);
+    // dK, bf16: the state in the transposed accumulator layout (sketch rows are
+    // then written four columns at a time); the dV read-out needs the plain one
+    constexpr bool TR = DK && !C::F32;
+    if constexpr (TR) load_state_t<C>(a.state + bh * a.state_bh_stride + c * a.state_chunk_stride, w, ln, g, Macc, Zacc);
+    else load_state<C>(a.state + bh * a.state_bh_stride + c * a.state_chunk_stride, w, ln, g, Macc, Zacc);
 
     const int nsub = (int)((seg1 - seg0 + TB - 1) / TB);
     const int my = 16 * w + ln;
@@ -1636,7 +1697,7 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
             } else if (causal) {
                 block_features_cached<C, false>(qb, fb, w, ln, g, a.L, a.beta, cols_b, unused, us, ug);
             }
-            if constexpr (DK) write_sketch_rows<C>(fb, w, ln, g, Macc, Zacc, ms_b);
+            if constexpr (DK) write_sketch_rows<C, TR>(fb, w, ln, g, Macc, Zacc, ms_b);
             __syncthreads();
             if constexpr (DV) {
                 if (causal) {
@@ -1683,7 +1744,7 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
                     chain_backproject<C>(t, dA, tt, gt, wf[tb], dhp, dX);
                 }
             }
-            if (causal) sketch_update<C, DK, LD::ZS, DV>(fb, w, ln, g, DV ? brow_b : cols_b, s_zr, Macc, Zacc);
+            if (causal) sketch_update<C, DK, LD::ZS, DV, TR>(fb, w, ln, g, DV ? brow_b : cols_b, s_zr, Macc, Zacc);
             if (LD::NB == 1) __syncthreads();   // single buffer: reads done before the next block's writes
         }
         if (LD::NB == 2) __syncthreads();   // the block tiles are read; the sub-block tiles below reuse them
