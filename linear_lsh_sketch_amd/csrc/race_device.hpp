@@ -254,18 +254,18 @@ __device__ inline void row_table(int t, int ri, int& table, int& plane) {
     plane = i % C::Pp;
 }
 
-// u = tanh(hs) for the four rows a lane holds: tanh|x| = (1 - E) / (1 + E)
-// with E = e^{-2|x|} (no overflow, accurate near 0), one shared reciprocal.
-__device__ inline void tanh4(const float hs[4], float u[4]) {
-    float e[4], q[4], rq[4];
+// tanh(x) = 1 - 2 / (1 + e^{2x}), with the exponent scale c = 2 log2(e)
+// times any factor folded into x: e^{2x} overflows to +inf for large x (then
+// tanh = 1) and underflows to 0 for very negative x (tanh = -1); near 0 the
+// absolute error is about one float32 ulp of 1. One exponential, one
+// reciprocal and three plain operations, no sign handling.
+__device__ inline float tanh_scaled(float x, float c) { return fmaf(-2.f, rcp_(1.f + exp2_(c * x)), 1.f); }
+
+// u = tanh(acc * inv) for the four rows a lane holds.
+__device__ inline void tanh4(const float acc[4], float inv, float u[4]) {
+    const float c = 2.f * LOG2E * inv;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        e[i] = exp2_(-2.f * LOG2E * fabsf(hs[i]));
-        q[i] = 1.f + e[i];
-    }
-    rcp4(q, rq);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) u[i] = copysignf((1.f - e[i]) * rq[i], hs[i]);
+    for (int i = 0; i < 4; ++i) u[i] = tanh_scaled(acc[i], c);
 }
 
 // The stored form of four u values, and back. Every pass derives the soft
@@ -293,26 +293,15 @@ __device__ inline typename Prec<F32>::uvec round_u(const float u[4]) {
 // no large common offset rides on the bf16 operands.
 
 // Per-plane values of one lane's four rows from the stored u: t = tanh(beta u)
-// and gt = dt/dh = beta (1 - t^2) (1 - u^2). tanh|x| = (1 - E) / (1 + E) with
-// E = e^{-2|x|}: no overflow, and the four reciprocals share one (arguments
-// in [1, 2]).
+// and gt = dt/dh = beta (1 - t^2) (1 - u^2).
 template <bool F32>
 __device__ inline void tplanes(const typename Prec<F32>::uvec& uv, float beta, float t[4], float gt[4]) {
-    float u[4], e[4], q[4], rq[4];
+    const float c = 2.f * LOG2E * beta;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        u[i] = (float)uv[i];
-        e[i] = exp2_(-2.f * beta * LOG2E * fabsf(u[i]));
-        q[i] = 1.f + e[i];
-    }
-    rcp4(q, rq);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        // the sign goes on the numerator (the same value): a copysign as the
-        // last step meets the bf16 packing of the features, a fold the gfx950
-        // backend cannot select
-        t[i] = copysignf(1.f - e[i], u[i]) * rq[i];
-        gt[i] = beta * (1.f - t[i] * t[i]) * (1.f - u[i] * u[i]);
+        const float u = (float)uv[i];
+        t[i] = tanh_scaled(u, c);
+        gt[i] = beta * (1.f - t[i] * t[i]) * (1.f - u * u);
     }
 }
 

@@ -576,8 +576,8 @@ __device__ inline void block_features(const WS& wsrc, int fb, int lane, int w, i
         const f32x4 acc = wsrc.project(t, lane, ln, g, xf);
         float hs[4], u[4], phi[C::KB * 8], tt[4], gt[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) hs[i] = acc[i] * inv;
-        tanh4(hs, u);
+        for (int i = 0; i < 4; ++i) hs[i] = acc[i];
+        tanh4(hs, inv, u);
         const typename Prec<C::F32>::uvec uq = round_u<C::F32>(u);
         tplanes<C::F32>(uq, beta, tt, gt);
         monomial_features<C>(tt, phi);
