@@ -298,10 +298,17 @@ __device__ inline void store_u(const PlaneRows& pr, int rowi, int t, int g, cons
 // into Zrow [64][ROWE] (token rows): z = [x * scale | mass]. With Zlo set, also
 // the rows of the rounding residual z - elem(z) (so that hi + lo carries z to
 // float32 precision). Columns 65.. stay zero from zero_pads.
-template <class C, int ZS = C::ROWE>
+template <class C, int ZS = C::ROWE, bool UNIT = false>
 __device__ inline void write_aug(const typename Prec<C::F32>::frag zr[2], float scale, float mass,
                                  typename Prec<C::F32>::elem* Zrow, typename Prec<C::F32>::elem* Zlo = nullptr) {
     const int th = threadIdx.x, r = th >> 2, q = th & 3;
+    if constexpr (UNIT) {
+        // scale 1: the loaded rows are stored as they are
+        st_frag<C::F32>(Zrow + r * ZS + 16 * q, zr[0]);
+        st_frag<C::F32>(Zrow + r * ZS + 16 * q + 8, zr[1]);
+        if (q == 0) Zrow[r * ZS + 64] = to_elem<C::F32>(mass);
+        return;
+    }
     float v[16];
 #pragma unroll
     for (int c = 0; c < 16; ++c) v[c] = q16_at<C::F32>(zr, c) * scale;
@@ -713,7 +720,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 3))) void
             if (g == 0) bstore_f32(pr.inv, rowi * 4, inv);
         }
         const bool ok = tr < nv;
-        if (!CACHED) write_aug<C, ZV>(zr, 1.f, ok ? 1.f : 0.f, s_zr);
+        if (!CACHED) write_aug<C, ZV, true>(zr, 1.f, ok ? 1.f : 0.f, s_zr);
         else write_aug<C, ZV>(zr, ok ? rcp_(dz) : 0.f, ok ? ez : 0.f, s_zr);
 #pragma unroll
         for (int fb = 0; fb < C::NBLK; ++fb) {
@@ -1150,7 +1157,7 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
 
         const float inv_a = row_inv_norm<C::F32>(xa);
         if (g == 0) bstore_f32(pra.inv, rowi * 4, inv_a);   // dropped without a cache
-        write_aug<C, ZV>(zr, 1.f, tok ? 1.f : 0.f, s_zr);
+        write_aug<C, ZV, true>(zr, 1.f, tok ? 1.f : 0.f, s_zr);
 
         // The empty subset's state rows (plain sums of the keys' [v | 1], the
         // same for every valid table) enter the read-out exactly, in float32:
@@ -1168,7 +1175,7 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
         f32x4 Y[4], Dacc[4], Sc[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            Y[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            Y[i] = f32x4{y_empty[0], y_empty[1], y_empty[2], y_empty[3]};   // the read-out adds to it
             Dacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
             Sc[i] = f32x4{sc0, sc0, sc0, sc0};
         }
@@ -1235,15 +1242,15 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
             float dint = 0.f;
 #pragma unroll
             for (int bt = 0; bt < 4; ++bt) {
-                f32x4 v;
+                typename Prec<C::F32>::half hv;   // the rounded scores, packed once
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int b = 16 * bt + 4 * g + i;
-                    const bool vis = b <= my && b < nv;
-                    v[i] = vis ? elem_f<C::F32>(to_elem<C::F32>(Sc[bt][i])) : 0.f;
-                    dint += v[i];
+                    hv[i] = to_elem<C::F32>((b <= my && b < nv) ? Sc[bt][i] : 0.f);
                 }
-                st_half<C::F32>(s_sc + my * C::ROWT + tok_pos(16 * bt + 4 * g), v);
+                *reinterpret_cast<typename Prec<C::F32>::half*>(s_sc + my * C::ROWT + tok_pos(16 * bt + 4 * g)) = hv;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dint += elem_f<C::F32>(hv[i]);
             }
             dint = sum_groups(dint);
             if (g == 0) f_Dint[my] = dint;
@@ -1276,7 +1283,8 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
         float rd[4];
 #pragma unroll
         for (int at = 0; at < 4; ++at) rd[at] = f_rD[16 * at + ln];
-        store_rows_t<C>(rO, it * TB, 16 * w, ln, g, Y, rd, y_empty);
+        const float none[4] = {-0.f, -0.f, -0.f, -0.f};   // x + -0 = x: nothing added
+        store_rows_t<C>(rO, it * TB, 16 * w, ln, g, Y, rd, none);
     }
 }
 
@@ -1393,7 +1401,7 @@ __attribute__((amdgpu_waves_per_eu(BwdQLds<C>::OCC, BwdQLds<C>::OCC))) void k_bw
         typename Prec<C::F32>::half xr[4];
         load_dx_row<C>(rXa, rowi, g, xr);
         const bool first = t0 == 0;   // the sub-block that starts the sequence
-        if (causal) write_aug<C>(zr, 1.f, tok ? 1.f : 0.f, s_zr);
+        if (causal) write_aug<C, C::ROWE, true>(zr, 1.f, tok ? 1.f : 0.f, s_zr);
         // y = [dO / D | e], e = -<dO, O> / D; this thread holds 16 columns of row tr
         {
             float delta = 0.f;
@@ -1771,7 +1779,7 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
                 }
                 __syncthreads();   // the value rows and scores are read before the next sub-block rewrites them
             }
-            const float one[4] = {1.f, 1.f, 1.f, 1.f}, zero[4] = {0.f, 0.f, 0.f, 0.f};
+            const float one[4] = {1.f, 1.f, 1.f, 1.f}, zero[4] = {-0.f, -0.f, -0.f, -0.f};   // x + -0 = x
             store_rows_t<C>(rOut1, r0_of(it), 16 * w, ln, g, Y, one, zero);
         }
         if constexpr (DK) store_dx<C>(xr, rOut0, r0_of(it) + my, g, inv_a, dX);
