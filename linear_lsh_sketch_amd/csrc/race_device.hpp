@@ -293,7 +293,9 @@ __device__ inline typename Prec<F32>::uvec round_u(const float u[4]) {
 // no large common offset rides on the bf16 operands.
 
 // Per-plane values of one lane's four rows from the stored u: t = tanh(beta u)
-// and gt = dt/dh = beta (1 - t^2) (1 - u^2).
+// and gt = (1 - t^2) (1 - u^2), which is dt/dh / beta (the factor beta is
+// applied once per gradient row, where the normalisation's chain rule scales
+// it).
 template <bool F32>
 __device__ inline void tplanes(const typename Prec<F32>::uvec& uv, float beta, float t[4], float gt[4]) {
     const float c = 2.f * LOG2E * beta;
@@ -301,7 +303,7 @@ __device__ inline void tplanes(const typename Prec<F32>::uvec& uv, float beta, f
     for (int i = 0; i < 4; ++i) {
         const float u = (float)uv[i];
         t[i] = tanh_scaled(u, c);
-        gt[i] = beta * (1.f - t[i] * t[i]) * (1.f - u * u);
+        gt[i] = (1.f - t[i] * t[i]) * (1.f - u * u);
     }
 }
 

@@ -181,6 +181,28 @@ __device__ inline float row_inv_norm(const typename Prec<F32>::frag x[2]) {
 }
 
 
+// <a, b> over the 16 values of two q16 row quarters (bf16: packed dot
+// products with float32 sums, no conversions).
+template <bool F32>
+__device__ inline float dot16(const typename Prec<F32>::frag a[2], const typename Prec<F32>::frag b[2]) {
+    float acc = 0.f;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        if constexpr (F32) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc += a[s][j] * b[s][j];
+        } else {
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x2 pa = {a[s][2 * j], a[s][2 * j + 1]}, pb = {b[s][2 * j], b[s][2 * j + 1]};
+                acc = __builtin_amdgcn_fdot2_f32_bf16(pa, pb, acc, false);
+            }
+        }
+    }
+    return acc;
+}
+
 template <bool F32>
 __device__ inline float q16_at(const typename Prec<F32>::frag v[2], int c) {
     return (float)v[c >> 3][c & 7];
@@ -959,10 +981,6 @@ __device__ inline void intra_operand(const typename Prec<C::F32>::elem* s_zr, co
     Cf[1] = pack<C::F32>(Cc[2], Cc[3]);
 }
 
-// dx = (dx_hat - x_hat <x_hat, dx_hat>) / |x| for the own token row (the chain
-// rule of x_hat = x / max(|x|, eps); below eps the map is a plain scaling, and
-// inv = 1 / max(|x|, eps) tells which case holds). dX[dt] holds columns
-// 16 dt + 4 g .. +3.
 // The own token's row values that store_dx needs (columns 16 dt + 4 g .. +3),
 // loaded early so the memory latency overlaps the sub-block's work.
 template <class C>
@@ -976,9 +994,14 @@ __device__ inline void load_dx_row(rsrc_t rX, int rowi, int g, typename Prec<C::
     }
 }
 
+// dx = (dx_hat - x_hat <x_hat, dx_hat>) / |x| for the own token row (the chain
+// rule of x_hat = x / max(|x|, eps); below eps the map is a plain scaling, and
+// inv = 1 / max(|x|, eps) tells which case holds). dX[dt] holds columns
+// 16 dt + 4 g .. +3 of dx_hat / beta (tplanes leaves beta out of dt/dh), so
+// the final scaling is beta / max(|x|, eps).
 template <class C>
 __device__ inline void store_dx(const typename Prec<C::F32>::half (&xr)[4], rsrc_t rOut, int rowi, int g, float inv,
-                                const f32x4 dX[4]) {
+                                float beta, const f32x4 dX[4]) {
     constexpr int es = C::F32 ? 4 : 2;
     float xv[4][4];
     float radial = 0.f;
@@ -992,11 +1015,12 @@ __device__ inline void store_dx(const typename Prec<C::F32>::half (&xr)[4], rsrc
     }
     radial = sum_groups(radial);
     const bool tangent = inv < rcp_(NORM_EPS);
+    const float binv = beta * inv;   // dX carries dt/dh without its factor beta
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
         f32x4 o;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = (tangent ? dX[dt][i] - xv[dt][i] * inv * radial : dX[dt][i]) * inv;
+        for (int i = 0; i < 4; ++i) o[i] = (tangent ? dX[dt][i] - xv[dt][i] * inv * radial : dX[dt][i]) * binv;
         const int off = rowi * row_bytes<C::F32>() + (16 * dt + 4 * g) * es;
         if constexpr (C::F32) {
             bstore128(rOut, off, __builtin_bit_cast(u32x4, o));
@@ -1404,9 +1428,7 @@ __attribute__((amdgpu_waves_per_eu(BwdQLds<C>::OCC, BwdQLds<C>::OCC))) void k_bw
         if (causal) write_aug<C, C::ROWE, true>(zr, 1.f, tok ? 1.f : 0.f, s_zr);
         // y = [dO / D | e], e = -<dO, O> / D; this thread holds 16 columns of row tr
         {
-            float delta = 0.f;
-#pragma unroll
-            for (int cc = 0; cc < 16; ++cc) delta += q16_at<C::F32>(yr, cc) * q16_at<C::F32>(orow, cc);
+            float delta = dot16<C::F32>(yr, orow);
             delta += __shfl_xor(delta, 1);
             delta += __shfl_xor(delta, 2);
             const float rD = tok ? rcp_(dd) : 0.f;
@@ -1486,7 +1508,7 @@ __attribute__((amdgpu_waves_per_eu(BwdQLds<C>::OCC, BwdQLds<C>::OCC))) void k_bw
             if (causal) sketch_update<C, true, C::ROWE, false, TR>(fb, w, ln, g, cols_b, s_zr, Macc, Zacc);
         }
         __syncthreads();   // the next sub-block rewrites the y and z rows
-        store_dx<C>(xr, rOut, rowi, g, inv_a, dX);
+        store_dx<C>(xr, rOut, rowi, g, inv_a, a.beta, dX);
     }
 }
 
@@ -1782,7 +1804,7 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
             const float one[4] = {1.f, 1.f, 1.f, 1.f}, zero[4] = {-0.f, -0.f, -0.f, -0.f};   // x + -0 = x
             store_rows_t<C>(rOut1, r0_of(it), 16 * w, ln, g, Y, one, zero);
         }
-        if constexpr (DK) store_dx<C>(xr, rOut0, r0_of(it) + my, g, inv_a, dX);
+        if constexpr (DK) store_dx<C>(xr, rOut0, r0_of(it) + my, g, inv_a, a.beta, dX);
     }
 }
 
