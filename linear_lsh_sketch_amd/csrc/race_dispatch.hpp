@@ -65,11 +65,21 @@ inline PlaneCache plane_cache(void* base, const CacheLayout& cl) {
 }
 
 template <int KIND>
-race_status_t run_scan(const Derived& d, float* states, float* total, hipStream_t st) {
+race_status_t run_scan(const Shape& s, const Derived& d, float* states, float* total, float* segbuf,
+                       hipStream_t st) {
     const int elems = (int)d.F65;
+    const unsigned gx = (unsigned)((elems + 255) / 256);
     profile_mark(KIND == SCAN_EXCL ? "scan_excl" : KIND == SCAN_REV_EXCL ? "scan_rev_excl" : "scan_total", st);
-    hipLaunchKernelGGL(k_scan<KIND>, dim3((unsigned)((elems + 255) / 256), (unsigned)d.BH), dim3(256), 0, st,
-                       states, total, (int)d.NC, elems);
+    const int segs = KIND == SCAN_TOTAL ? 1 : scan_segs(s, d);
+    if (segs == 1) {
+        hipLaunchKernelGGL(k_scan<KIND>, dim3(gx, (unsigned)d.BH), dim3(256), 0, st, states, total, (int)d.NC,
+                           elems);
+        return launch_ok();
+    }
+    const dim3 grid(gx, (unsigned)(d.BH * segs));
+    hipLaunchKernelGGL(k_scan_segsum<KIND>, grid, dim3(256), 0, st, states, segbuf, (int)d.NC, elems, segs);
+    RACE_TRY(launch_ok());
+    hipLaunchKernelGGL(k_scan_segapply<KIND>, grid, dim3(256), 0, st, states, segbuf, (int)d.NC, elems, segs);
     return launch_ok();
 }
 
@@ -124,11 +134,11 @@ race_status_t run_forward(const Shape& s, const Derived& d, const WsLayout& wl, 
     a.Xa = c.Q; a.ca = qc; a.cb = kc; a.Zsrc = c.V; a.W = c.W; a.beta = c.beta; a.out0 = O;
     a.Dv = saved ? reinterpret_cast<float*>(sv + sl.D) : nullptr;
     if (s.causal) {
-        RACE_TRY(run_scan<SCAN_EXCL>(d, Sb, nullptr, st));
+        RACE_TRY(run_scan<SCAN_EXCL>(s, d, Sb, nullptr, reinterpret_cast<float*>(ws + wl.scan), st));
         a.state = Sb; a.state_bh_stride = d.NC * d.F65; a.state_chunk_stride = d.F65;
     } else {
         float* St = saved ? reinterpret_cast<float*>(saved) : reinterpret_cast<float*>(ws + wl.St);
-        RACE_TRY(run_scan<SCAN_TOTAL>(d, Sb, St, st));
+        RACE_TRY(run_scan<SCAN_TOTAL>(s, d, Sb, St, nullptr, st));
         a.state = St; a.state_bh_stride = d.F65; a.state_chunk_stride = 0;
     }
     return run_pass<C, PASS_FWD>(s, d, a, st);
@@ -185,11 +195,11 @@ race_status_t run(const Shape& s, const Derived& d, const WsLayout& wl, const Ca
     k.Xa = c.K; k.ca = kc; k.cb = qc; k.Zsrc = c.dO; k.Ysrc = c.V; k.W = c.W; k.WTp = WTp; k.beta = c.beta;
     k.Dv = Dv; k.Ev = Ev; k.out0 = c.dK; k.out1 = c.dV;
     if (s.causal) {
-        RACE_TRY(run_scan<SCAN_REV_EXCL>(d, Tw, nullptr, st));
+        RACE_TRY(run_scan<SCAN_REV_EXCL>(s, d, Tw, nullptr, reinterpret_cast<float*>(ws + wl.scan), st));
         k.state = Tw; k.state_bh_stride = d.NC * d.F65; k.state_chunk_stride = d.F65;
     } else {
         float* Ttw = reinterpret_cast<float*>(ws + wl.Tt);
-        RACE_TRY(run_scan<SCAN_TOTAL>(d, Tw, Ttw, st));
+        RACE_TRY(run_scan<SCAN_TOTAL>(s, d, Tw, Ttw, nullptr, st));
         k.state = Ttw; k.state_bh_stride = d.F65; k.state_chunk_stride = 0;
     }
     return run_pass<C, PASS_BWD_K>(s, d, k, st);

@@ -33,6 +33,7 @@ struct WsLayout {
     size_t Sv;     // backward without saved: the recomputed forward's saved buffer
     size_t Ov;     // backward without saved: the recomputed forward output
     size_t Kc;     // forward without saved: the keys' plane values
+    size_t scan;   // segment sums of the segmented chunk scan (when used)
     size_t total;
 };
 
@@ -114,6 +115,20 @@ inline SavedLayout saved_layout(const Shape& s, const Derived& d) {
 
 inline size_t saved_bytes(const Shape& s, const Derived& d) { return saved_layout(s, d).total; }
 
+// Segments of the chunk scan: one pass over the chunks when the grid of
+// (state elements / 256) x heads already has enough workgroups to keep the
+// memory busy; otherwise up to 16 segments of at least 64 chunks each,
+// summed first and then scanned from their offsets (two launches).
+inline int scan_segs(const Shape& s, const Derived& d) {
+    if (!s.causal) return 1;
+    const int64_t blocks = (d.F65 + 255) / 256 * d.BH;
+    if (blocks >= 192) return 1;
+    int64_t segs = (768 + blocks - 1) / blocks;
+    if (segs > 16) segs = 16;
+    if (segs > d.NC / 64) segs = d.NC / 64;
+    return segs < 2 ? 1 : (int)segs;
+}
+
 inline WsLayout ws_layout(const Shape& s, const Derived& d, int kind) {
     WsLayout w{};
     const size_t per = (size_t)d.F65 * sizeof(float);
@@ -138,6 +153,8 @@ inline WsLayout ws_layout(const Shape& s, const Derived& d, int kind) {
         w.Sv = off;  off = align256(off + saved_bytes(s, d));
         w.Ov = off;  off = align256(off + tokens * (size_t)s.d * sizeof(float));
     }
+    const int segs = scan_segs(s, d);
+    w.scan = off;    off = align256(off + (segs > 1 ? (size_t)d.BH * (size_t)segs * per : 0));
     w.total = off;
     return w;
 }

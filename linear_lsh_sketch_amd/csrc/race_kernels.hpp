@@ -768,41 +768,81 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 3))) void
 // ---------------------------------------------------------------------------
 // scans over chunks (one thread per state element, fixed order: deterministic)
 // ---------------------------------------------------------------------------
-template <int KIND>
-__global__ __launch_bounds__(256) void k_scan(float* __restrict__ st, float* __restrict__ total,
-                                              int nchunks, int elems) {
-    // The loads of the next batch of chunks are issued before the running sum
-    // and the stores of the current batch, so about 2 * BATCH loads per lane
-    // stay in flight (one wave per SIMD needs that many to cover the memory
-    // latency); the running sum keeps the fixed chunk order (deterministic).
+// Running sum over logical chunk positions [c0, c1) of one state element
+// (position c is chunk c, or chunk nchunks - 1 - c for the reverse scan),
+// starting from run; with WRITE each position first receives the sum of the
+// positions before it. The loads of the next batch are issued before the
+// sums and stores of the current one, so about 2 * BATCH loads per lane stay
+// in flight; the order of the additions is fixed (deterministic).
+template <int KIND, bool WRITE>
+__device__ inline float scan_range(float* p, int nchunks, int elems, int c0, int c1, float run) {
     constexpr int BATCH = 32;
-    const int e = blockIdx.x * blockDim.x + threadIdx.x;
-    const int bh = blockIdx.y;
-    if (e >= elems) return;
-    float* p = st + (size_t)bh * nchunks * elems + e;
     auto at = [&](int c) -> float* {
         return p + (size_t)((KIND == SCAN_REV_EXCL) ? nchunks - 1 - c : c) * elems;
     };
-    auto load = [&](int c0, float (&v)[BATCH]) {
+    auto load = [&](int b0, float (&v)[BATCH]) {
 #pragma unroll
-        for (int k = 0; k < BATCH; ++k) v[k] = *at(c0 + k < nchunks ? c0 + k : nchunks - 1);
+        for (int k = 0; k < BATCH; ++k) v[k] = *at(b0 + k < c1 ? b0 + k : c1 - 1);
     };
-    float run = 0.f;
+    if (c0 >= c1) return run;
     float cur[BATCH], nxt[BATCH];
-    load(0, cur);
-    for (int c0 = 0; c0 < nchunks; c0 += BATCH) {
-        if (c0 + BATCH < nchunks) load(c0 + BATCH, nxt);
+    load(c0, cur);
+    for (int b0 = c0; b0 < c1; b0 += BATCH) {
+        if (b0 + BATCH < c1) load(b0 + BATCH, nxt);
 #pragma unroll
         for (int k = 0; k < BATCH; ++k) {
-            if (c0 + k < nchunks) {
-                if constexpr (KIND != SCAN_TOTAL) *at(c0 + k) = run;
+            if (b0 + k < c1) {
+                if constexpr (WRITE) *at(b0 + k) = run;
                 run += cur[k];
             }
         }
 #pragma unroll
         for (int k = 0; k < BATCH; ++k) cur[k] = nxt[k];
     }
+    return run;
+}
+
+// One pass over all chunks (one thread per state element): exclusive prefix
+// (causal), reverse exclusive prefix (backward) or the total (non-causal).
+template <int KIND>
+__global__ __launch_bounds__(256) void k_scan(float* __restrict__ st, float* __restrict__ total,
+                                              int nchunks, int elems) {
+    const int e = blockIdx.x * blockDim.x + threadIdx.x;
+    const int bh = blockIdx.y;
+    if (e >= elems) return;
+    float* p = st + (size_t)bh * nchunks * elems + e;
+    const float run = scan_range<KIND, KIND != SCAN_TOTAL>(p, nchunks, elems, 0, nchunks, 0.f);
     if constexpr (KIND == SCAN_TOTAL) total[(size_t)bh * elems + e] = run;
+}
+
+// Segmented form of the (reverse) exclusive prefix, for grids too small to
+// keep the memory busy (few heads): the logical chunk positions are split
+// into segs segments; k_scan_segsum sums each segment, k_scan_segapply starts
+// each segment from the sum of the segments before it (fixed order).
+template <int KIND>
+__global__ __launch_bounds__(256) void k_scan_segsum(const float* __restrict__ st, float* __restrict__ segsum,
+                                                     int nchunks, int elems, int segs) {
+    const int e = blockIdx.x * blockDim.x + threadIdx.x;
+    const int bh = blockIdx.y / segs, sg = blockIdx.y % segs;
+    if (e >= elems) return;
+    const int len = (nchunks + segs - 1) / segs;
+    const int c0 = sg * len, c1 = min(nchunks, c0 + len);
+    float* p = const_cast<float*>(st) + (size_t)bh * nchunks * elems + e;
+    segsum[((size_t)bh * segs + sg) * elems + e] = scan_range<KIND, false>(p, nchunks, elems, c0, c1, 0.f);
+}
+
+template <int KIND>
+__global__ __launch_bounds__(256) void k_scan_segapply(float* __restrict__ st, const float* __restrict__ segsum,
+                                                       int nchunks, int elems, int segs) {
+    const int e = blockIdx.x * blockDim.x + threadIdx.x;
+    const int bh = blockIdx.y / segs, sg = blockIdx.y % segs;
+    if (e >= elems) return;
+    const int len = (nchunks + segs - 1) / segs;
+    const int c0 = sg * len, c1 = min(nchunks, c0 + len);
+    float run = 0.f;
+    for (int s2 = 0; s2 < sg; ++s2) run += segsum[((size_t)bh * segs + s2) * elems + e];
+    float* p = st + (size_t)bh * nchunks * elems + e;
+    scan_range<KIND, true>(p, nchunks, elems, c0, c1, run);
 }
 
 // ---------------------------------------------------------------------------

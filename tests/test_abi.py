@@ -72,6 +72,18 @@ def test_workspace_and_saved_sizes():
         _a256(6 * 32 * 65 * 4) + _a256(rows_nc * 4) + 2 * cache_nc
 
 
+def test_segmented_scan_workspace():
+    # one causal head of 2^20 tokens, L8 P1 (F = 32, 65 F floats per state):
+    # chunk 1024 gives 1024 chunks and 9 workgroups per pass, so the chunk
+    # scans run in 16 segments whose sums take BH * 16 * 65 F floats more
+    per = 32 * 65 * 4
+    seg = race.workspace_bytes(1, 1, 1 << 20, 64, 1, 8, True, 1024, race.WS_FWD_SAVED)
+    assert seg == _a256(1024 * per) + _a256(16 * per)
+    # four chunks: one pass, no segment sums
+    one = race.workspace_bytes(1, 1, 4096, 64, 1, 8, True, 1024, race.WS_FWD_SAVED)
+    assert one == _a256(4 * per)
+
+
 def test_workspace_kind_rejected():
     out = ctypes.c_size_t(0)
     for kind in (-1, 4):

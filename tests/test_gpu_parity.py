@@ -120,6 +120,18 @@ def test_edge_lengths(lib, N, chunk):
     run_case(lib, 1, 1, N, 4, 4, "f32", True, chunk, seed=N)
 
 
+def test_segmented_scan_matches_single_pass(lib):
+    """One head of a long sequence: with chunk 1024 the chunk scans run in
+    segments (sums first, then each segment from its offset), with chunk 4096
+    in one pass; the results agree to float32 rounding."""
+    outs = []
+    for chunk in (1024, 4096):
+        res, _ = run_case(lib, 1, 1, 1 << 17, 4, 4, "f32", True, chunk, seed=41, check=False)
+        outs.append(res)
+    for k in outs[0]:
+        assert rel_l2(outs[1][k], outs[0][k]) < 2e-6, k
+
+
 def test_chunk_size_independence(lib):
     outs = []
     for chunk in (64, 100, 256, 1000):
