@@ -776,7 +776,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 3))) void
 // in flight; the order of the additions is fixed (deterministic).
 template <int KIND, bool WRITE>
 __device__ inline float scan_range(float* p, int nchunks, int elems, int c0, int c1, float run) {
-    constexpr int BATCH = 32;
+    constexpr int BATCH = 16;
     auto at = [&](int c) -> float* {
         return p + (size_t)((KIND == SCAN_REV_EXCL) ? nchunks - 1 - c : c) * elems;
     };
