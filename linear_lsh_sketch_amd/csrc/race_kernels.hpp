@@ -1194,7 +1194,10 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
     load_state<C>(a.state + bh * a.state_bh_stride + c * a.state_chunk_stride, w, ln, g, Macc, Zacc);
 
     const int nsub = (int)((seg1 - seg0 + TB - 1) / TB);
-    const int my = 16 * w + ln;              // own token within the sub-block
+    // Own 16-token tile of wave w in sub-block it: (w + it) mod 4. The tiles
+    // rotate so that the in-sub-block score work, which shrinks with the
+    // tile (keys after the own tokens are skipped), evens out over the SIMDs.
+    auto own_tok = [&](int it2) { return 16 * ((w + it2) & 3) + ln; };
 
     // loads issued one sub-block (the keys' plane values: one feature block) ahead
     frag n_xa[2], n_z[2];
@@ -1204,10 +1207,10 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
         return (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
     };
     auto issue = [&](int it2) {
-        load_row_b<C::F32>(rXa, it2 * TB + my, g, n_xa);
+        load_row_b<C::F32>(rXa, it2 * TB + own_tok(it2), g, n_xa);
         load_q16_b<C::F32>(rZ, it2 * TB + tr, tq, n_z);
     };
-    auto issue_planes = [&](int it2, int fb2) { load_planes<C>(prb, it2 * TB + my, fb2, g, pn); };
+    auto issue_planes = [&](int it2, int fb2) { load_planes<C>(prb, it2 * TB + own_tok(it2), fb2, g, pn); };
     issue(0);
     if (causal) issue_planes(0, 0);
 
@@ -1215,6 +1218,8 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
         const int64_t t0 = seg0 + (int64_t)it * TB;
         const int nv = nv_of(it);
         const bool tok = tr < nv;
+        const int ow = (w + it) & 3;             // own tile (wave-uniform)
+        const int my = 16 * ow + ln;             // own token within the sub-block
         const int rowi = it * TB + my;
         frag xa[2] = {n_xa[0], n_xa[1]}, zr[2] = {n_z[0], n_z[1]};
         if (it + 1 < nsub) issue(it + 1);
@@ -1255,11 +1260,11 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
                 if (fb + 1 < C::NBLK) issue_planes(it, fb + 1);
                 else if (it + 1 < nsub) issue_planes(it + 1, 0);
             }
-            block_features<C, false>(wsrc, fb, lane, w, ln, g, xa, inv_a, a.beta, a.L, rows_b, unused, pra,
+            block_features<C, false>(wsrc, fb, lane, ow, ln, g, xa, inv_a, a.beta, a.L, rows_b, unused, pra,
                                      rowi);
             if (causal) {
                 float us[C::TPB][4], ug[C::TPB][4];
-                block_features_cached<C, false>(pl, fb, w, ln, g, a.L, a.beta, brow_b, unused, us, ug);
+                block_features_cached<C, false>(pl, fb, ow, ln, g, a.L, a.beta, brow_b, unused, us, ug);
             }
         };
         features(0);
@@ -1270,13 +1275,17 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
             __syncthreads();
             if (fb + 1 < C::NBLK) features(fb + 1);
             if (causal) {
-                // own features from the tile (not kept in registers)
+                // own features from the tile (not kept in registers); key
+                // tiles after the own one are all masked and skipped
+                frag pa[C::FBK];
 #pragma unroll
-                for (int kcl = 0; kcl < C::FBK; ++kcl) {
-                    const frag pa = ld_frag<C::F32>(rows_b + my * C::ROWF + 32 * kcl + 8 * g);
+                for (int kcl = 0; kcl < C::FBK; ++kcl) pa[kcl] = ld_frag<C::F32>(rows_b + my * C::ROWF + 32 * kcl + 8 * g);
 #pragma unroll
-                    for (int bt = 0; bt < 4; ++bt)
-                        Sc[bt] = mma(ld_frag<C::F32>(brow_b + (16 * bt + ln) * C::ROWF + 32 * kcl + 8 * g), pa,
+                for (int bt = 0; bt < 4; ++bt) {
+                    if (bt > ow) break;
+#pragma unroll
+                    for (int kcl = 0; kcl < C::FBK; ++kcl)
+                        Sc[bt] = mma(ld_frag<C::F32>(brow_b + (16 * bt + ln) * C::ROWF + 32 * kcl + 8 * g), pa[kcl],
                                      Sc[bt]);
                 }
             }
@@ -1339,8 +1348,9 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
             for (int s = 0; s < 2; ++s) {
                 const frag zt = val_operand<C, LD::ZS>(s_zr, 16 * w, s, ln, g);
 #pragma unroll
-                for (int at = 0; at < 4; ++at)
-                    Y[at] = mma(zt, ld_frag<C::F32>(s_sc + (16 * at + ln) * C::ROWT + 32 * s + 8 * g), Y[at]);
+                for (int at = 0; at < 4; ++at)   // queries 0..31 see no key of the second half
+                    if (s == 0 || at >= 2)
+                        Y[at] = mma(zt, ld_frag<C::F32>(s_sc + (16 * at + ln) * C::ROWT + 32 * s + 8 * g), Y[at]);
             }
         }
         __syncthreads();
@@ -1652,7 +1662,11 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
     else load_state<C>(a.state + bh * a.state_bh_stride + c * a.state_chunk_stride, w, ln, g, Macc, Zacc);
 
     const int nsub = (int)((seg1 - seg0 + TB - 1) / TB);
-    const int my = 16 * w + ln;
+    // Own 16-token tile of wave w in (reversed) sub-block it: the dV pass
+    // rotates it, (w + it) mod 4, so that the in-sub-block score work, which
+    // shrinks with the tile (queries before the own keys are skipped), evens
+    // out over the SIMDs; the dK pass keeps tile w.
+    auto own_tok = [&](int it2) { return 16 * (DV ? ((w + it2) & 3) : w) + ln; };
 
     // global loads are issued one sub-block (plane values: one feature block)
     // ahead; in the split passes the rows at the top of their sub-block
@@ -1678,7 +1692,7 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
     auto r0_of = [&](int it2) { return (nsub - 1 - it2) * TB; };   // first in-chunk row of a sub-block
     auto issue = [&](int it2) {
         const int r0 = r0_of(it2);
-        if (DK) n_inv = my < nv_of(it2) ? bload_f32(pra.inv, (r0 + my) * 4) : 1.f;
+        if (DK) n_inv = own_tok(it2) < nv_of(it2) ? bload_f32(pra.inv, (r0 + own_tok(it2)) * 4) : 1.f;
         if (causal) {
             load_q16_b<C::F32>(rZ, r0 + tr, tq, n_z);
             n_d = bload_f32(rD, (r0 + tr) * 4);
@@ -1687,14 +1701,16 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
         if (DK) load_q16_b<C::F32>(rY, r0 + tr, tq, n_y);
     };
     auto issue_planes = [&](int it2, int fb2) {
-        load_planes<C>(pra, r0_of(it2) + my, fb2, g, pa);
-        if (causal) load_planes<C>(prb, r0_of(it2) + my, fb2, g, pb);
+        load_planes<C>(pra, r0_of(it2) + own_tok(it2), fb2, g, pa);
+        if (causal) load_planes<C>(prb, r0_of(it2) + own_tok(it2), fb2, g, pb);
     };
     if (PREFETCH) issue(0);
     issue_planes(0, 0);
 
     for (int it = 0; it < nsub; ++it) {
         const int64_t t0 = t0_of(it);
+        const int ow = DV ? ((w + it) & 3) : w;   // own tile (wave-uniform)
+        const int my = 16 * ow + ln;
         const int nv = nv_of(it);
         const bool tok = tr < nv;
         if (!PREFETCH) issue(it);
@@ -1761,24 +1777,26 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
             elem* cols_b = s_cols + bsel * LD::n_cols;
             elem* ms_b = s_ms + bsel * LD::n_ms;
             if constexpr (DV) {
-                block_features_cached<C, false>(ka, fb, w, ln, g, a.L, a.beta, rows_b, phiA, us, ug);
+                block_features_cached<C, false>(ka, fb, ow, ln, g, a.L, a.beta, rows_b, phiA, us, ug);
                 if (causal)
-                    block_features_cached<C, false>(qb, fb, w, ln, g, a.L, a.beta, brow_b, unused, us, ug);
+                    block_features_cached<C, false>(qb, fb, ow, ln, g, a.L, a.beta, brow_b, unused, us, ug);
             } else if (causal) {
-                block_features_cached<C, false>(qb, fb, w, ln, g, a.L, a.beta, cols_b, unused, us, ug);
+                block_features_cached<C, false>(qb, fb, ow, ln, g, a.L, a.beta, cols_b, unused, us, ug);
             }
             if constexpr (DK) write_sketch_rows<C, TR>(fb, w, ln, g, Macc, Zacc, ms_b);
             __syncthreads();
             if constexpr (DV) {
                 if (causal) {
-                    // own features from the tile (not kept in registers)
+                    // own features from the tile (not kept in registers); query
+                    // tiles before the own one are all masked and skipped
 #pragma unroll
                     for (int kcl = 0; kcl < C::FBK; ++kcl) {
                         const frag pa = ld_frag<C::F32>(rows_b + my * C::ROWF + 32 * kcl + 8 * g);
 #pragma unroll
                         for (int bt = 0; bt < 4; ++bt)
-                            Sc[bt] = mma(ld_frag<C::F32>(brow_b + (16 * bt + ln) * C::ROWF + 32 * kcl + 8 * g), pa,
-                                         Sc[bt]);
+                            if (bt >= ow)
+                                Sc[bt] = mma(ld_frag<C::F32>(brow_b + (16 * bt + ln) * C::ROWF + 32 * kcl + 8 * g),
+                                             pa, Sc[bt]);
                     }
                 }
                 // dV readout of the value columns of this wave (before this block's update)
@@ -1836,8 +1854,9 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
                 for (int s = 0; s < 2; ++s) {
                     const frag zt = val_operand<C, LD::ZS>(s_zr, 16 * w, s, ln, g);
 #pragma unroll
-                    for (int at = 0; at < 4; ++at)
-                        Y[at] = mma(zt, ld_frag<C::F32>(s_sc + (16 * at + ln) * C::ROWT + 32 * s + 8 * g), Y[at]);
+                    for (int at = 0; at < 4; ++at)   // keys 32..63 see no query of the first half
+                        if (s == 1 || at < 2)
+                            Y[at] = mma(zt, ld_frag<C::F32>(s_sc + (16 * at + ln) * C::ROWT + 32 * s + 8 * g), Y[at]);
                 }
                 __syncthreads();   // the value rows and scores are read before the next sub-block rewrites them
             }
