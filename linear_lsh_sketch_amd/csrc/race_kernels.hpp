@@ -1000,7 +1000,8 @@ __device__ inline void intra_operand(const typename Prec<C::F32>::elem* s_zr, co
 #pragma unroll
     for (int bt = 0; bt < 4; ++bt) {
         // every tile is formed (the mask below keeps the visible entries), so
-        // all waves run the same instruction stream
+        // all waves run the same instruction stream (skipping the tiles the
+        // mask empties measured slower here)
         Cc[bt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 3; ++s) {
@@ -1662,11 +1663,9 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
     else load_state<C>(a.state + bh * a.state_bh_stride + c * a.state_chunk_stride, w, ln, g, Macc, Zacc);
 
     const int nsub = (int)((seg1 - seg0 + TB - 1) / TB);
-    // Own 16-token tile of wave w in (reversed) sub-block it: the dV pass
-    // rotates it, (w + it) mod 4, so that the in-sub-block score work, which
-    // shrinks with the tile (queries before the own keys are skipped), evens
-    // out over the SIMDs; the dK pass keeps tile w.
-    auto own_tok = [&](int it2) { return 16 * (DV ? ((w + it2) & 3) : w) + ln; };
+    // Own 16-token tile: w (rotating it, as the forward does, measured slower
+    // here: the register budget of three workgroups per CU has no room left).
+    const int my = 16 * w + ln;
 
     // global loads are issued one sub-block (plane values: one feature block)
     // ahead; in the split passes the rows at the top of their sub-block
@@ -1692,7 +1691,7 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
     auto r0_of = [&](int it2) { return (nsub - 1 - it2) * TB; };   // first in-chunk row of a sub-block
     auto issue = [&](int it2) {
         const int r0 = r0_of(it2);
-        if (DK) n_inv = own_tok(it2) < nv_of(it2) ? bload_f32(pra.inv, (r0 + own_tok(it2)) * 4) : 1.f;
+        if (DK) n_inv = my < nv_of(it2) ? bload_f32(pra.inv, (r0 + my) * 4) : 1.f;
         if (causal) {
             load_q16_b<C::F32>(rZ, r0 + tr, tq, n_z);
             n_d = bload_f32(rD, (r0 + tr) * 4);
@@ -1701,16 +1700,14 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
         if (DK) load_q16_b<C::F32>(rY, r0 + tr, tq, n_y);
     };
     auto issue_planes = [&](int it2, int fb2) {
-        load_planes<C>(pra, r0_of(it2) + own_tok(it2), fb2, g, pa);
-        if (causal) load_planes<C>(prb, r0_of(it2) + own_tok(it2), fb2, g, pb);
+        load_planes<C>(pra, r0_of(it2) + my, fb2, g, pa);
+        if (causal) load_planes<C>(prb, r0_of(it2) + my, fb2, g, pb);
     };
     if (PREFETCH) issue(0);
     issue_planes(0, 0);
 
     for (int it = 0; it < nsub; ++it) {
         const int64_t t0 = t0_of(it);
-        const int ow = DV ? ((w + it) & 3) : w;   // own tile (wave-uniform)
-        const int my = 16 * ow + ln;
         const int nv = nv_of(it);
         const bool tok = tr < nv;
         if (!PREFETCH) issue(it);
@@ -1777,11 +1774,11 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
             elem* cols_b = s_cols + bsel * LD::n_cols;
             elem* ms_b = s_ms + bsel * LD::n_ms;
             if constexpr (DV) {
-                block_features_cached<C, false>(ka, fb, ow, ln, g, a.L, a.beta, rows_b, phiA, us, ug);
+                block_features_cached<C, false>(ka, fb, w, ln, g, a.L, a.beta, rows_b, phiA, us, ug);
                 if (causal)
-                    block_features_cached<C, false>(qb, fb, ow, ln, g, a.L, a.beta, brow_b, unused, us, ug);
+                    block_features_cached<C, false>(qb, fb, w, ln, g, a.L, a.beta, brow_b, unused, us, ug);
             } else if (causal) {
-                block_features_cached<C, false>(qb, fb, ow, ln, g, a.L, a.beta, cols_b, unused, us, ug);
+                block_features_cached<C, false>(qb, fb, w, ln, g, a.L, a.beta, cols_b, unused, us, ug);
             }
             if constexpr (DK) write_sketch_rows<C, TR>(fb, w, ln, g, Macc, Zacc, ms_b);
             __syncthreads();
@@ -1794,7 +1791,7 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
                         const frag pa = ld_frag<C::F32>(rows_b + my * C::ROWF + 32 * kcl + 8 * g);
 #pragma unroll
                         for (int bt = 0; bt < 4; ++bt)
-                            if (bt >= ow)
+                            if (bt >= w)
                                 Sc[bt] = mma(ld_frag<C::F32>(brow_b + (16 * bt + ln) * C::ROWF + 32 * kcl + 8 * g),
                                              pa, Sc[bt]);
                     }
