@@ -9,8 +9,8 @@
 // v_mfma_f32_16x16x4_f32 per 32-wide chunk: MFMA j contracts the j-th value
 // of every lane group, so the same per-lane layout covers all 32 positions.
 //
-// Feature ("canonical f") order. L tables of R = 2^P corners give
-// F = L_pad * R features. The hash projection computes H^T = W' X^T, so a lane
+// Feature ("canonical f") order. L tables of R = 2^P features (the monomials
+// of the table's planes) give F = L_pad * R features. The hash projection computes H^T = W' X^T, so a lane
 // of a projection tile t holds rows 4g..4g+3 (= P' consecutive planes of one
 // table when P' = 4, or several whole tables when P' < 4) for one token. The
 // features the lane derives from them are numbered f = 32 kc + 8 g + j with

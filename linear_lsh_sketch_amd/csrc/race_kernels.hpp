@@ -5,23 +5,28 @@
 // hypercube corners (Italian gist.science page, Sommario tecnico section 2;
 // Korean page, 기술 요약 section 2); keys add mass and value sums per bucket;
 // queries read their own buckets; causal mode uses prefix sums (Japanese
-// page, sections 2.1 and 2.2). The corner softmax is evaluated as the product
-// of per-plane sigmoids sigmoid(2 beta c_p tanh h_p), which equals it exactly
-// because the corner logit is a sum of per-plane terms.
+// page, sections 2.1 and 2.2). The kernels contract, instead of the 2^P
+// corner probabilities of a table, the 2^P monomials prod_{p in T} tanh(beta
+// u_p) over the subsets T of its planes: a table's soft-collision kernel is
+// 2^-P times their inner product, and the constant cancels in the output and
+// the gradients (see the feature basis in race_device.hpp).
 //
 // Decomposition (per (batch, head), the sequence cut into chunks of `chunk`
 // tokens, one workgroup per chunk, sub-blocks of 64 tokens inside a chunk):
 //   k_totals : per-chunk sketch  M_c = sum_{b in c} phi(x_b)^T [z_b | m_b]
 //   k_scan   : exclusive prefix (causal), reverse exclusive prefix (backward
-//              key side) or total (non-causal) over chunks
+//              key side) or total (non-causal) over chunks; for few heads of
+//              long sequences k_scan_segsum + k_scan_segapply do the same in
+//              segments
 //   k_fwd    : per sub-block readout of the queries against the running key
 //              sketch plus the intra-sub-block causal term, then the sketch
 //              update -> O (and the per-token denominator D)
 //   k_bwd_q  : y = [dO/D | e], e = -<dO, O>/D; dA_Q = (key sketch) y plus the
-//              intra term; corner-softmax chain rule, back-projection -> dQ
+//              intra term; chain rule of the monomials and tanh,
+//              back-projection -> dQ
 //   k_bwd_k  : against the reverse sketch of the queries' [dO/D | e]: the dV
-//              readout and dA_K = T [v | 1] in one sweep over the feature
-//              blocks; chain rule, back-projection -> dK, dV
+//              readout (one launch) and dA_K = T [v | 1] with the chain rule
+//              and back-projection -> dK (a second launch)
 // "a" is the side that reads the sketch, "b" the side that writes it. Sketch
 // states are held in float32 accumulators, split by value columns over the
 // four waves (wave w owns columns 16w..16w+15; the mass column is split by
@@ -1366,8 +1371,8 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
 // ---------------------------------------------------------------------------
 // query-side backward: y = [dO/D | e] with e = -<dO, O>/D from the saved D and
 // the forward output; dA_Q = M y (sketch of the keys before the sub-block, plus
-// the intra-sub-block causal term), the corner-softmax chain rule, the
-// back-projection and the normalisation's chain rule -> dQ; also writes e.
+// the intra-sub-block causal term), the chain rule of the monomials and tanh,
+// the back-projection and the normalisation's chain rule -> dQ; also writes e.
 // ---------------------------------------------------------------------------
 template <class C>
 struct BwdQLds {
