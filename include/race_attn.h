@@ -46,7 +46,7 @@
  *     device work is enqueued. Device faults surface at the caller's next
  *     synchronisation.
  *   - Supported: d = 64; 1 <= P <= 4; L >= 1 with L * P' <= 128 where P' is P
- *     rounded up to a power of two; N >= 1; B, H >= 1; chunk >= 1; dtype
+ *     rounded up to a power of two; N >= 1; B, H >= 1; 1 <= chunk <= 2^20; dtype
  *     RACE_F32 or RACE_BF16. Other shapes return RACE_ERR_UNSUPPORTED.
  *   - Numerics: bf16 inputs are multiplied on bf16 matrix cores with float32
  *     accumulation; float32 inputs use float32 matrix cores throughout.

@@ -59,6 +59,10 @@ enum { WS_FWD = 0, WS_BWD = 1, WS_BWD_RECOMPUTE = 2, WS_FWD_SAVED = 3 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Largest chunk (tokens per workgroup): the kernels address the rows of a
+// chunk with 32-bit byte offsets, up to 512 bytes per row.
+constexpr int MAX_CHUNK = 1 << 20;
+
 inline bool mul_ok(int64_t a, int64_t b, int64_t& out) {
     if (a < 0 || b < 0) return false;
     if (a != 0 && b > INT64_MAX / a) return false;
@@ -70,6 +74,8 @@ inline race_status_t derive(const Shape& s, Derived& d) {
     if (s.B < 1 || s.H < 1 || s.N < 1 || s.d < 1 || s.P < 1 || s.L < 1 || s.chunk < 1)
         return RACE_ERR_INVALID_ARG;
     if (s.d != 64 || s.P > 4) return RACE_ERR_UNSUPPORTED;
+    // in-chunk byte offsets (rows of up to 512 bytes) are 32-bit
+    if (s.chunk > MAX_CHUNK) return RACE_ERR_UNSUPPORTED;
     d.Pp = (s.P == 3) ? 4 : s.P;
     const int64_t rows = (int64_t)s.L * d.Pp;
     if (rows > 128) return RACE_ERR_UNSUPPORTED;

@@ -101,6 +101,7 @@ def test_workspace_kind_rejected():
     ((1, 1, 10, 64, 4, 8, 1, 0, 0), race.RACE_ERR_INVALID_ARG),         # chunk = 0
     ((1, 70000, 10, 64, 4, 8, 1, 16, 0), race.RACE_ERR_UNSUPPORTED),    # B*H > 65535
     ((1 << 40, 1 << 20, 1 << 20, 64, 4, 8, 1, 16, 0), race.RACE_ERR_INVALID_ARG),  # overflow
+    ((1, 1, 10, 64, 4, 8, 1, (1 << 20) + 1, 0), race.RACE_ERR_UNSUPPORTED),  # chunk > 2^20
 ])
 def test_workspace_bytes_rejects(args, code):
     out = ctypes.c_size_t(0)
