@@ -102,6 +102,26 @@ def measured_traffic(workload: str, stage: str):
     return rows.get(stage)
 
 
+def copy_bandwidth(dev, nbytes: int = COPY_BYTES, reps: int = 5) -> float:
+    """GB/s (bytes read + bytes written) of a plain device-to-device copy of
+    nbytes on this machine: the attainable HBM rate, reported beside the nominal
+    peak."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    gbps = 2 * nbytes * reps / (s.elapsed_time(e) / 1e3) / 1e9
+    del src, dst
+    return gbps
+
+
 def cpu_baseline(w, n_sample: int):
     """The float64 oracle on the first n_sample tokens of every head of the
     same workload (same seeded inputs), causal forward + backward."""
@@ -238,6 +258,12 @@ def main():
     roof["kernel"] = dom
     roof["kernel_avg_ms"] = avg_ms
     layer_t = max(layer["bytes"] * units / HBM_PEAK, layer["flops"] * units / peak_f)
+    hbm_high_water = torch.cuda.max_memory_allocated() / 2**30
+    # the box's own copy bandwidth, beside the nominal peak (outside the timed region)
+    copy_gbps = copy_bandwidth(dev)
+    if roof["unit"] == "GB/s":
+        roof["copy_GBps_measured"] = copy_gbps
+        roof["frac_of_copy"] = roof["achieved"] / copy_gbps
 
     out = {
         "metric": METRIC,
@@ -258,8 +284,9 @@ def main():
         "roofline": roof,
         "layer_roofline": {"bound": "hbm" if layer["bytes"] * units / HBM_PEAK >= layer["flops"] * units / peak_f
                            else "mfma", "frac": layer_t / (ms_step / 1e3),
+                           "alg_GBps": layer["bytes"] * units / (ms_step / 1e3) / 1e9,
                            "alg_bytes_per_token_head": layer["bytes"], "alg_flops_per_token_head": layer["flops"]},
-        "hbm_peak_GiB": torch.cuda.max_memory_allocated() / 2**30,
+        "hbm_peak_GiB": hbm_high_water,
         "hbm_capacity_GiB": torch.cuda.get_device_properties(0).total_memory / 2**30,
         "stages_ms_per_step": {k: v / args.steps for k, v in sorted(stage_ms.items(), key=lambda kv: -kv[1])},
         "wall_s_timed": wall,
