@@ -152,3 +152,13 @@ def test_backward_and_hash_argument_errors():
         race.RACE_ERR_INVALID_ARG
     assert L.race_attn_hash(FAKE, FAKE, 1, 1, 10, 64, 6, 8, race.RACE_F32, FAKE, FAKE, None) == \
         race.RACE_ERR_UNSUPPORTED
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    # no CPU fallback: without the built library every entry point raises
+    monkeypatch.setattr(race, "_lib", None)
+    monkeypatch.setattr(race, "LIB_PATH", str(tmp_path / "libraceattn.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        race.lib()
+    with pytest.raises(RuntimeError, match="not built"):
+        race.workspace_bytes(1, 1, 10, 64, 4, 8, True, 16, race.WS_FWD)
