@@ -31,6 +31,11 @@ notes):
   * one W of shape [L, P, d] is shared by queries and keys and by all heads.
   * hard-hash id of a table = sum_p [h_p > 0] 2^p.
 
+Beyond the training path: ``hard_forward`` (one-hot buckets, the beta -> inf
+limit, output 0 when a query collides with no key) and the causal decode step
+against a running sketch (``sketch`` of a prompt, then ``decode_step`` per new
+token), the sketch standing in for the key-value cache at inference.
+
 The backward is the exact gradient of this forward (the pages state the
 method is differentiable end to end: Japanese page, section 2.2), written out
 by the chain rule.
@@ -169,6 +174,74 @@ def hard_hash(X, W):
     bits = (h > 0).astype(np.int64)
     ids = np.sum(bits << np.arange(P)[None, None, :], axis=-1).astype(np.int32)
     return ids, int(np.sum(np.abs(h) < NEAR_ZERO))
+
+
+def hard_buckets(X, W):
+    """One-hot assignment a[n, l, r] = [r == id_l(x_n)]: the limit beta -> inf
+    of the soft assignment, i.e. the discrete hash of the original RACE sketch
+    that the temperature beta softens (Japanese gist.science page, section
+    2.2, differentiability; Italian page, section 2, on hard binary LSH)."""
+    ids, _ = hard_hash(X, W)
+    R = 1 << W.shape[1]
+    return (ids[..., None] == np.arange(R)[None, None, :]).astype(np.float64)
+
+
+def assign(X, W, beta):
+    """Soft assignment for finite beta, the one-hot hard assignment for beta = inf."""
+    if np.isinf(beta):
+        return hard_buckets(X, W)
+    return soft_buckets(X, W, beta)[0]
+
+
+def hard_forward(Q, K, V, W, causal: bool = False):
+    """Hard-hash RACE output for one (batch, head): keys add [v | 1] to the one
+    bucket their sign pattern picks in each table, a query reads the bucket it
+    falls in, and O_i = sum of the read value sums / sum of the read counts;
+    O_i = 0 when no key shares a bucket with the query in any table (the
+    pages' bucket aggregation and reconstruction with one-hot assignments)."""
+    aQ, aK = hard_buckets(Q, W), hard_buckets(K, W)
+    N, L, R = aQ.shape
+    d = V.shape[1]
+    S = np.zeros((L, R, d))
+    z = np.zeros((L, R))
+    if not causal:
+        S = np.einsum("jlr,jd->lrd", aK, V)
+        z = aK.sum(axis=0)
+    O = np.zeros((N, d))
+    for i in range(N):
+        if causal:
+            S += aK[i][:, :, None] * V[i][None, None, :]
+            z += aK[i]
+        den = np.sum(aQ[i] * z)
+        if den != 0:
+            O[i] = np.einsum("lr,lrd->d", aQ[i], S) / den
+    return O
+
+
+def sketch(K, V, W, beta: float = 1.0):
+    """Key sketch of a whole sequence: S [L, R, d] = sum_j a(k_j) v_j^T and
+    z [L, R] = sum_j a(k_j) (bucket aggregation: Italian page, section 2,
+    Algoritmo; Japanese page, section 2.1). beta = inf uses the hard buckets.
+    This is the state a causal decode continues from after a prompt."""
+    aK = assign(K, W, beta)
+    return np.einsum("jlr,jd->lrd", aK, V), aK.sum(axis=0)
+
+
+def decode_step(S, z, q, k, v, W, beta: float = 1.0):
+    """One causal decode step against a running sketch (S, z): the new key k
+    with value v joins the sketch first (causal sums include the diagonal),
+    then the query q reads it out. Returns (S', z', o); o = 0 when the
+    denominator is 0 (possible only for hard buckets). The sketch replaces the
+    key-value cache: its size L * R * (d + 1) does not grow with the sequence
+    (efficient key-value caching at inference: Japanese gist.science page,
+    section 6; Korean page, section 5)."""
+    aq = assign(q[None], W, beta)[0]
+    ak = assign(k[None], W, beta)[0]
+    S = S + ak[:, :, None] * v[None, None, :]
+    z = z + ak
+    den = np.sum(aq * z)
+    o = np.einsum("lr,lrd->d", aq, S) / den if den != 0 else np.zeros(v.shape[0])
+    return S, z, o
 
 
 def forward_batched(Q, K, V, W, beta=1.0, causal=False):

@@ -233,6 +233,91 @@ def test_large_beta_many_tables_approaches_angular_attention():
 
 
 # --------------------------------------------------------------------------
+# hard buckets and the decode step against the running sketch
+# --------------------------------------------------------------------------
+
+def hard_ids_by_signs(X, W):
+    """Bucket id of each table from the signs of the raw projections (the
+    normalisation does not change a sign): bit p set when <W_lp, x> > 0."""
+    L, P, _ = W.shape
+    ids = np.zeros((X.shape[0], L), np.int64)
+    for n in range(X.shape[0]):
+        for l in range(L):
+            for p in range(P):
+                if float(np.dot(W[l, p], X[n])) > 0:
+                    ids[n, l] |= 1 << p
+    return ids
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_hard_forward_equals_pairwise_collision_count(causal):
+    """Hard RACE output = collision-weighted mean: query i gives key j the
+    weight c_ij = number of tables in which their buckets agree (j <= i when
+    causal); O_i = 0 when every c_ij is 0. Pairwise counting, no bucket sums."""
+    Q, K, V, _, W = rand_case(77, 40, 10, 3, 3)
+    iq, ik = hard_ids_by_signs(Q, W), hard_ids_by_signs(K, W)
+    N = Q.shape[0]
+    ref = np.zeros_like(V)
+    zero_rows = 0
+    for i in range(N):
+        num, den = np.zeros(V.shape[1]), 0
+        for j in range(i + 1 if causal else N):
+            c = int(np.sum(iq[i] == ik[j]))
+            num += c * V[j]
+            den += c
+        if den:
+            ref[i] = num / den
+        else:
+            zero_rows += 1
+    O = dense.hard_forward(Q, K, V, W, causal)
+    np.testing.assert_allclose(O, ref, rtol=1e-12, atol=1e-14)
+    if causal:
+        assert 0 < zero_rows < N   # both branches of the readout rule are exercised
+
+
+def test_large_beta_soft_forward_reaches_hard_forward():
+    """beta -> inf: with every |h| well away from 0 the soft assignment is the
+    one-hot of the hard id to far below float64 precision, so the soft
+    forward equals the hard one on rows that collide with some key."""
+    Q, K, V, _, W = rand_case(5, 48, 12, 2, 4)
+    h = np.einsum("nd,lpd->nlp", np.concatenate([Q, K]) /
+                  np.linalg.norm(np.concatenate([Q, K]), axis=1, keepdims=True), W)
+    keep = np.all(np.abs(h) > 0.02, axis=(1, 2))
+    Q, K, V = Q[keep[:48]][:30], K[keep[48:]][:30], V[:30]
+    hard = dense.hard_forward(Q, K, V, W, False)
+    soft = dense.forward(Q, K, V, W, 5e4, False)
+    rows = np.abs(hard).sum(1) > 0
+    assert rows.sum() > 20
+    np.testing.assert_allclose(soft[rows], hard[rows], rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("beta", [0.7, 2.5, math.inf])
+@pytest.mark.parametrize("n0", [0, 1, 17])
+def test_decode_steps_equal_pairwise_causal_attention(beta, n0):
+    """A prompt of n0 tokens sketched at once, then one decode step per later
+    token: each step's output is the causal output of that token, written as
+    pairwise kernel attention (soft: Khat_ij = sum_l <a(q_i), a(k_j)>; hard:
+    the collision count, 0 output when nothing collides)."""
+    Q, K, V, _, W = rand_case(31 + n0, 29, 10, 3, 4)
+    N, d = V.shape
+    if math.isinf(beta):
+        iq, ik = hard_ids_by_signs(Q, W), hard_ids_by_signs(K, W)
+        Kh = (iq[:, None, :] == ik[None, :, :]).sum(-1).astype(np.float64)
+    else:
+        aq = assignments_by_product(Q, W, beta)
+        ak = assignments_by_product(K, W, beta)
+        Kh = np.einsum("ilr,jlr->ij", aq, ak)
+    Kh = np.tril(Kh)
+    den = Kh.sum(1, keepdims=True)
+    ref = np.where(den > 0, (Kh @ V) / np.where(den > 0, den, 1.0), 0.0)
+    S, z = dense.sketch(K[:n0], V[:n0], W, beta)
+    for i in range(n0, N):
+        S, z, o = dense.decode_step(S, z, Q[i], K[i], V[i], W, beta)
+        np.testing.assert_allclose(o, ref[i], rtol=1e-11, atol=1e-13)
+    assert np.isclose(z.sum(), N * W.shape[0])   # every key adds one unit of mass per table
+
+
+# --------------------------------------------------------------------------
 # invariants
 # --------------------------------------------------------------------------
 
