@@ -137,10 +137,50 @@ race_status_t race_attn_hash(const void *X, const void *W, int64_t B, int64_t H,
                              int d, int P, int L, race_dtype_t dtype, int32_t *bucket_ids,
                              unsigned long long *near_zero, void *stream);
 
+/* ---- Decoding: the sketch as a constant-size key-value cache --------------
+ * Efficient key-value caching at inference is the pages' named next use of
+ * the sketch (Japanese gist.science page, section 6; Korean page, section 5).
+ * The running state of one (batch, head) is the key sketch of every token so
+ * far: per feature, the sum of the keys' feature value times [v | 1], in
+ * float32, L * 2^P * 65 floats (padded to whole projection tiles) whatever
+ * the length. Its layout is private to the library; all-zero bytes are the
+ * state of an empty sequence. `temperature` = +INFINITY selects the hard
+ * buckets (the discrete hash that the temperature softens: Japanese
+ * gist.science page, section 2.2): each table then adds [v | 1] to exactly
+ * one bucket, and a query that shares no bucket with any key outputs zeros.
+ * Finite temperatures give the soft assignment of race_attn_fwd. NaN and
+ * -INFINITY give RACE_ERR_INVALID_ARG. */
+
+/* Bytes of a running state for B * H heads: float32 [B * H][state floats].
+ * Same shape checks as race_attn_fwd. */
+race_status_t race_attn_state_bytes(int64_t B, int64_t H, int d, int P, int L, size_t *bytes);
+
+/* Prefill: state = the key sketch of the N tokens of K, V ([B, H, N, d],
+ * dtype) with hyperplanes W ([L, P, d]); overwrites `state` (device float32,
+ * race_attn_state_bytes, 16-byte aligned). `chunk` only tiles the work (any
+ * value in 1..2^20; 1024 is a good choice); the result does not depend on it
+ * beyond float32 rounding order. `ws` must hold race_attn_workspace_bytes(B,
+ * H, N, d, P, L, causal = 0, chunk, for_backward = 0, ...). The outputs of the
+ * prompt itself come from race_attn_fwd with causal = 1. */
+race_status_t race_attn_prefill(const void *K, const void *V, const void *W, int64_t B, int64_t H,
+                                int64_t N, int d, int P, int L, float temperature, int chunk,
+                                race_dtype_t dtype, float *state, void *ws, size_t ws_bytes,
+                                void *stream);
+
+/* One causal decode step for every (batch, head): q, k, v are the new
+ * token's rows ([B, H, d], dtype); k and v join `state` (in and out), then q
+ * reads it, so the output o ([B, H, d], dtype) is the causal output of this
+ * token, diagonal included (Japanese gist.science page, section 2.2, causal
+ * prefix sums). One workgroup per head; no workspace. Calls on one stream
+ * run in order; two calls that update the same state concurrently race. */
+race_status_t race_attn_decode(const void *q, const void *k, const void *v, const void *W, int64_t B,
+                               int64_t H, int d, int P, int L, float temperature, race_dtype_t dtype,
+                               float *state, void *o, void *stream);
+
 /* Profiling aid (not needed for computation). For the CALLING THREAD only:
  * `events` is an array of `capacity` (>= 2) caller-created hipEvent_t handles.
- * Each subsequent race_attn_fwd / _bwd / _hash call on this thread records
- * events[i] on its stream just before its i-th kernel launch and one more
+ * Each subsequent race_attn_fwd / _bwd / _hash / _prefill / _decode call on this
+ * thread records events[i] on its stream just before its i-th kernel launch and one more
  * event after the last launch, so stage i took elapsed(events[i], events[i+1]).
  * Pass events = NULL to stop. race_attn_profile_count() gives the number of
  * events the last call recorded; race_attn_profile_stage(i) the name of the

@@ -17,7 +17,8 @@ RACE_OK, RACE_ERR_INVALID_ARG, RACE_ERR_UNSUPPORTED, RACE_ERR_WORKSPACE, RACE_ER
 RACE_F32, RACE_BF16 = 0, 1
 
 SYMBOLS = ("race_attn_workspace_bytes", "race_attn_saved_bytes", "race_attn_fwd",
-           "race_attn_bwd", "race_attn_hash", "race_attn_profile_events", "race_attn_profile_count",
+           "race_attn_bwd", "race_attn_hash", "race_attn_state_bytes", "race_attn_prefill",
+           "race_attn_decode", "race_attn_profile_events", "race_attn_profile_count",
            "race_attn_profile_stage", "race_attn_status_string")
 
 
@@ -47,6 +48,10 @@ def lib():
         L.race_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, fl, i32, i32,
                                     i32, vp, vp, vp, vp, sz, vp]
         L.race_attn_hash.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, i32, vp, vp, vp]
+        L.race_attn_state_bytes.argtypes = [i64, i64, i32, i32, i32, ctypes.POINTER(sz)]
+        L.race_attn_prefill.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, i32, fl, i32, i32, vp, vp,
+                                        sz, vp]
+        L.race_attn_decode.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, fl, i32, vp, vp, vp]
         L.race_attn_profile_events.argtypes = [vp, i32]
         L.race_attn_profile_count.argtypes = []
         L.race_attn_profile_stage.argtypes = [i32]
@@ -54,8 +59,8 @@ def lib():
         L.race_attn_status_string.argtypes = [i32]
         L.race_attn_status_string.restype = ctypes.c_char_p
         for name in ("race_attn_workspace_bytes", "race_attn_saved_bytes", "race_attn_fwd",
-                     "race_attn_bwd", "race_attn_hash", "race_attn_profile_events",
-                     "race_attn_profile_count"):
+                     "race_attn_bwd", "race_attn_hash", "race_attn_state_bytes", "race_attn_prefill",
+                     "race_attn_decode", "race_attn_profile_events", "race_attn_profile_count"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -196,6 +201,65 @@ def race_attn_hash(X, W, P, L, stream=None):
     return ids, nz
 
 
+def state_bytes(B, H, P, L, d=64) -> int:
+    """Bytes of the float32 running sketch of B * H heads (race_attn_state_bytes)."""
+    out = ctypes.c_size_t(0)
+    _check(lib().race_attn_state_bytes(B, H, d, P, L, ctypes.byref(out)), "race_attn_state_bytes")
+    return out.value
+
+
+def alloc_state(B, H, P, L, device):
+    """A zeroed running sketch (the state of an empty sequence), float32."""
+    import torch
+    return torch.zeros(state_bytes(B, H, P, L) // 4, dtype=torch.float32, device=device)
+
+
+def race_attn_prefill(K, V, W, P, L, temperature=1.0, chunk=1024, state=None, ws=None, stream=None):
+    """Running sketch of the prompt K, V ([B, H, N, d]); temperature = inf
+    gives the hard buckets. Returns the state (float32, overwritten)."""
+    _check_inputs(K, V, W)
+    B, H, N, d = K.shape
+    if tuple(W.shape) != (L, P, d):
+        raise ValueError(f"W must be [L, P, d] = {(L, P, d)}, got {tuple(W.shape)}")
+    if V.shape != K.shape:
+        raise ValueError("K and V must share one shape")
+    if state is None:
+        state = alloc_state(B, H, P, L, K.device)
+    _check_state(state, B, H, P, L, d, K.device)
+    if ws is None:
+        ws = alloc_workspace(B, H, N, P, L, False, chunk, WS_FWD, K.device)
+    code = lib().race_attn_prefill(_p(K), _p(V), _p(W), B, H, N, d, P, L, float(temperature), chunk,
+                                   _dtype_code(K), _p(state), _p(ws), ws.numel(), _stream(stream))
+    _check(code, "race_attn_prefill")
+    return state
+
+
+def _check_state(state, B, H, P, L, d, device):
+    import torch
+    if state.dtype != torch.float32 or not state.is_contiguous() or state.device != device:
+        raise ValueError("state must be a contiguous float32 tensor on the inputs' GPU")
+    if state.numel() * 4 < state_bytes(B, H, P, L, d):
+        raise ValueError("state is smaller than race_attn_state_bytes")
+
+
+def race_attn_decode(q, k, v, W, state, P, L, temperature=1.0, out=None, stream=None):
+    """One causal decode step: q, k, v are [B, H, d]; k, v join `state` (in
+    place), then q reads it. Returns o [B, H, d]."""
+    import torch
+    _check_inputs(q, k, v, W)
+    B, H, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one shape")
+    if tuple(W.shape) != (L, P, d):
+        raise ValueError(f"W must be [L, P, d] = {(L, P, d)}, got {tuple(W.shape)}")
+    _check_state(state, B, H, P, L, d, q.device)
+    o = out if out is not None else torch.empty_like(q)
+    code = lib().race_attn_decode(_p(q), _p(k), _p(v), _p(W), B, H, d, P, L, float(temperature),
+                                  _dtype_code(q), _p(state), _p(o), _stream(stream))
+    _check(code, "race_attn_decode")
+    return o
+
+
 class StageTimer:
     """Per-kernel timing of library calls with HIP events (the library records
     them on its own stream between its launches; see race_attn_profile_events)."""
@@ -244,3 +308,5 @@ class StageTimer:
 forward = race_attn_fwd
 backward = race_attn_bwd
 hard_hash = race_attn_hash
+prefill = race_attn_prefill
+decode = race_attn_decode

@@ -155,6 +155,50 @@ race_status_t race_attn_hash(const void* X, const void* W, int64_t B, int64_t H,
     return go(dtype, s, dv, WsLayout{}, c);
 }
 
+race_status_t race_attn_state_bytes(int64_t B, int64_t H, int d, int P, int L, size_t* bytes) {
+    if (!bytes) return RACE_ERR_INVALID_ARG;
+    Shape s;
+    Derived dv;
+    race_status_t rc = prepare(B, H, 1, d, P, L, 0, 1, s, dv);
+    if (rc != RACE_OK) return rc;
+    *bytes = (size_t)dv.BH * (size_t)dv.F65 * sizeof(float);
+    return RACE_OK;
+}
+
+race_status_t race_attn_prefill(const void* K, const void* V, const void* W, int64_t B, int64_t H, int64_t N,
+                                int d, int P, int L, float temperature, int chunk, race_dtype_t dtype,
+                                float* state, void* ws, size_t ws_bytes, void* stream) {
+    if (!K || !V || !W || !state || !ws || !dtype_ok(dtype) || std::isnan(temperature) ||
+        temperature == -INFINITY || !all_aligned({K, V, W, state, ws}))
+        return RACE_ERR_INVALID_ARG;
+    Shape s;
+    Derived dv;
+    race_status_t rc = prepare(B, H, N, d, P, L, 0, chunk, s, dv);
+    if (rc != RACE_OK) return rc;
+    const WsLayout wl = ws_layout(s, dv, WS_FWD);
+    if (ws_bytes < wl.total) return RACE_ERR_WORKSPACE;
+    Call c{};
+    c.op = OP_PREFILL; c.K = K; c.V = V; c.W = W; c.beta = temperature; c.hard = std::isinf(temperature);
+    c.state = state; c.ws = ws; c.stream = reinterpret_cast<hipStream_t>(stream);
+    return go(dtype, s, dv, wl, c);
+}
+
+race_status_t race_attn_decode(const void* q, const void* k, const void* v, const void* W, int64_t B, int64_t H,
+                               int d, int P, int L, float temperature, race_dtype_t dtype, float* state, void* o,
+                               void* stream) {
+    if (!q || !k || !v || !W || !state || !o || !dtype_ok(dtype) || std::isnan(temperature) ||
+        temperature == -INFINITY || !all_aligned({state}))
+        return RACE_ERR_INVALID_ARG;
+    Shape s;
+    Derived dv;
+    race_status_t rc = prepare(B, H, 1, d, P, L, 0, 1, s, dv);
+    if (rc != RACE_OK) return rc;
+    Call c{};
+    c.op = OP_DECODE; c.Q = q; c.K = k; c.V = v; c.W = W; c.O = o; c.beta = temperature;
+    c.hard = std::isinf(temperature); c.state = state; c.stream = reinterpret_cast<hipStream_t>(stream);
+    return go(dtype, s, dv, WsLayout{}, c);
+}
+
 const char* race_attn_status_string(race_status_t status) {
     switch (status) {
         case RACE_OK: return "RACE_OK";

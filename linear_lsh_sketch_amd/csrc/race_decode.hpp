@@ -1,0 +1,167 @@
+// Causal decode against a running sketch (gfx950).
+//
+// One new token per (batch, head): its key and value join the sketch, then
+// its query reads the sketch out (causal sums include the diagonal). The
+// sketch replaces the key-value cache: L * 2^P * (d + 1) floats per head,
+// whatever the length of the sequence so far (efficient key-value caching
+// at inference: Japanese gist.science page, section 6; Korean page,
+// section 5). temperature = +inf selects the hard buckets of the original
+// discrete hash (Japanese gist.science page, section 2.2): t_p = sign(h_p),
+// so each table's monomials are those of a one-hot corner; a query that
+// collides with no key then reads a zero denominator and outputs zeros.
+//
+// The state has the layout of the kernels' sketch states: F x 64 value sums
+// (row f = canonical feature f) then F masses, F = 32 * MT * KB. Padded
+// tables (index >= L) keep the convention of the sketch kernels: their empty
+// subset is 1 for every key (so their state rows stay the plain sums of
+// [v | 1]) and every other feature is 0; the read-out leaves them out.
+//
+// Work per head: one projection of q and of k on the L * P planes, the
+// features, one read-modify-write of the state (2 * F * 65 * 4 bytes: the
+// bound) and the read-out from the updated rows while they are in registers.
+// No matrix cores: a head's update is an outer product of one feature row
+// and one value row, and the read-out a vector-matrix product over F rows.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "race_device.hpp"
+
+namespace race {
+
+constexpr int DEC_NT = 512;      // threads per workgroup (one head)
+constexpr int DEC_RG = DEC_NT / 16;   // row groups: 16 lanes cover one 64-float row
+constexpr int DEC_MAXF = 512;    // largest F (MT = 8, KB = 2)
+
+struct DecodeArgs {
+    const void *q, *k, *v, *W;
+    float* state;   // [BH][F * 65]
+    void* o;        // [BH][64]
+    int P, L, F, KB, TPT, TPL;
+    float beta;
+    int hard;
+};
+
+// Table and subset of canonical feature f (lane group g of 32-feature chunk
+// kc holds features 8 g .. 8 g + 7 of the tables of its projection rows).
+__device__ inline void feature_table_subset(int f, int P, int KB, int TPT, int TPL, int& table, int& subset) {
+    const int kc = f >> 5, g = (f >> 3) & 3, j = f & 7;
+    const int jj = j + 8 * (kc % KB);
+    const int R = 1 << P;
+    table = (kc / KB) * TPT + g * TPL + jj / R;
+    subset = jj % R;
+}
+
+template <bool F32>
+__global__ __launch_bounds__(DEC_NT) void k_decode(DecodeArgs a) {
+    using elem = typename Prec<F32>::elem;
+    __shared__ float s_x[3][DH];             // q, k, v of this head
+    __shared__ float s_inv[2];               // 1 / max(|q|, eps), 1 / max(|k|, eps)
+    __shared__ float s_t[2][128];            // t_p of each table plane, [q | k][l * P + p]
+    __shared__ float s_phi[2][DEC_MAXF];     // features of q and of k
+    __shared__ float s_num[DEC_RG][DH + 4];  // partial read-outs per row group
+    __shared__ float s_den[DEC_NT / 64];
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t bh = blockIdx.x;
+    const int F = a.F, LP = a.L * a.P;
+    float* st = a.state + (size_t)bh * (size_t)F * 65;
+
+    if (tid < 3 * DH) {
+        const int which = tid / DH, c = tid % DH;
+        const void* src = which == 0 ? a.q : which == 1 ? a.k : a.v;
+        s_x[which][c] = (float)reinterpret_cast<const elem*>(src)[bh * DH + c];
+    }
+    __syncthreads();
+    if (wv < 2) {
+        const float x = s_x[wv][lane];
+        float ss = x * x;
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) ss += __shfl_xor(ss, m);
+        if (lane == 0) s_inv[wv] = 1.f / fmaxf(sqrtf(ss), NORM_EPS);
+    }
+    __syncthreads();
+
+    // projections: thread (side, row) with row = l * P + p
+    if (tid < 2 * LP) {
+        const int side = tid / LP, row = tid % LP;
+        const elem* w = reinterpret_cast<const elem*>(a.W) + (size_t)row * DH;
+        float h = 0.f;
+#pragma unroll 16
+        for (int c = 0; c < DH; ++c) h = fmaf((float)w[c], s_x[side][c], h);
+        h *= s_inv[side];
+        float t;
+        if (a.hard) t = h > 0.f ? 1.f : (h < 0.f ? -1.f : 0.f);
+        else t = tanhf(a.beta * tanhf(h));
+        s_t[side][row] = t;
+    }
+    __syncthreads();
+
+    for (int f = tid; f < F; f += DEC_NT) {
+        int table, subset;
+        feature_table_subset(f, a.P, a.KB, a.TPT, a.TPL, table, subset);
+        float pq = 0.f, pk = subset == 0 ? 1.f : 0.f;   // padded table
+        if (table < a.L) {
+            pq = 1.f;
+            pk = 1.f;
+            for (int p = 0; p < a.P; ++p)
+                if ((subset >> p) & 1) {
+                    pq *= s_t[0][table * a.P + p];
+                    pk *= s_t[1][table * a.P + p];
+                }
+        }
+        s_phi[0][f] = pq;
+        s_phi[1][f] = pk;
+    }
+    __syncthreads();
+
+    // value sums: lane quad cq owns columns 4 cq .. 4 cq + 3 of rows rg, rg + 32, ...
+    // All rows are loaded before any is written back, so the loads overlap.
+    {
+        const int cq = tid & 15, rg = tid >> 4;
+        const int nrow = F / DEC_RG;   // F is a multiple of 32
+        const f32x4 vq = {s_x[2][4 * cq], s_x[2][4 * cq + 1], s_x[2][4 * cq + 2], s_x[2][4 * cq + 3]};
+        f32x4 s[DEC_MAXF / DEC_RG];
+#pragma unroll
+        for (int i = 0; i < DEC_MAXF / DEC_RG; ++i)
+            if (i < nrow) s[i] = *reinterpret_cast<const f32x4*>(st + (size_t)(rg + DEC_RG * i) * DH + 4 * cq);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < DEC_MAXF / DEC_RG; ++i) {
+            if (i < nrow) {
+                const int f = rg + DEC_RG * i;
+                const float pk = s_phi[1][f], pq = s_phi[0][f];
+                s[i] += pk * vq;
+                if (pk != 0.f) *reinterpret_cast<f32x4*>(st + (size_t)f * DH + 4 * cq) = s[i];
+                acc += pq * s[i];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s_num[rg][4 * cq + j] = acc[j];
+    }
+    // masses
+    {
+        float den = 0.f;
+        for (int f = tid; f < F; f += DEC_NT) {
+            const float pk = s_phi[1][f];
+            float z = st[(size_t)F * DH + f] + pk;
+            if (pk != 0.f) st[(size_t)F * DH + f] = z;
+            den = fmaf(s_phi[0][f], z, den);
+        }
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) den += __shfl_xor(den, m);
+        if (lane == 0) s_den[wv] = den;
+    }
+    __syncthreads();
+    if (tid < DH) {
+        float num = 0.f, den = 0.f;
+#pragma unroll 8
+        for (int r = 0; r < DEC_RG; ++r) num += s_num[r][tid];
+#pragma unroll
+        for (int w = 0; w < DEC_NT / 64; ++w) den += s_den[w];
+        const float o = (a.hard && den == 0.f) ? 0.f : num / den;
+        reinterpret_cast<elem*>(a.o)[bh * DH + tid] = (elem)o;
+    }
+}
+
+}  // namespace race

@@ -1,14 +1,22 @@
-// Launch sequences for the forward, backward and hash entry points.
+// Launch sequences for the forward, backward, hash, prefill and decode entry points.
 #pragma once
 
 #include <hip/hip_runtime.h>
 
+#include "race_decode.hpp"
 #include "race_host.hpp"
 #include "race_kernels.hpp"
 
 namespace race {
 
-enum { OP_FWD = 0, OP_BWD = 1, OP_HASH = 2 };
+enum { OP_FWD = 0, OP_BWD = 1, OP_HASH = 2, OP_PREFILL = 3, OP_DECODE = 4 };
+
+// Temperature the sketch kernels use for the hard buckets: tanh(beta u)
+// evaluates as 1 - 2 / (1 + 2^(2 log2(e) beta u)), and with this beta the
+// exponent overflows (t = 1) or underflows (t = -1) for every |u| >= 1e-28,
+// while u = 0 (a padded table's plane, or an exactly orthogonal row) still
+// gives t = 0.
+constexpr float HARD_BETA = 1e30f;
 
 struct Call {
     int op;
@@ -23,6 +31,8 @@ struct Call {
     const void* X;                 // hash
     int32_t* ids;                  // hash
     unsigned long long* near_zero; // hash
+    float* state;                  // prefill (out) / decode (in and out): running sketch [BH][F * 65]
+    int hard;                      // prefill / decode: one-hot buckets (temperature = +inf)
 };
 
 template <bool F32>
@@ -158,6 +168,24 @@ race_status_t run(const Shape& s, const Derived& d, const WsLayout& wl, const Ca
         return launch_ok();
     }
     if (c.op == OP_FWD) return run_forward<C>(s, d, wl, c, c.O, c.saved_out);
+    if (c.op == OP_PREFILL) {
+        // chunk sums of the keys' sketch, then their total straight into the state
+        float* Sb = reinterpret_cast<float*>(ws + wl.S);
+        const PlaneCache kc = plane_cache(ws + wl.Kc, cache_layout(s, d));
+        RACE_TRY((run_totals<C, false>(s, d, c.K, c.V, nullptr, nullptr, kc, c.W, c.hard ? HARD_BETA : c.beta,
+                                       Sb, st)));
+        return run_scan<SCAN_TOTAL>(s, d, Sb, c.state, nullptr, st);
+    }
+    if (c.op == OP_DECODE) {
+        DecodeArgs a{};
+        a.q = c.Q; a.k = c.K; a.v = c.V; a.W = c.W; a.state = c.state; a.o = c.O;
+        a.P = s.P; a.L = s.L; a.F = C::F; a.KB = C::KB; a.TPT = C::TPT; a.TPL = C::TPL;
+        a.beta = c.beta; a.hard = c.hard;
+        static_assert(C::F <= DEC_MAXF && C::F % DEC_RG == 0, "decode tiling");
+        profile_mark("decode", st);
+        hipLaunchKernelGGL(k_decode<C::F32>, dim3((unsigned)d.BH), dim3(DEC_NT), 0, st, a);
+        return launch_ok();
+    }
 
     // backward: O and what the forward kept, recomputed when not given
     const void* O = c.O_in;

@@ -154,6 +154,44 @@ def test_backward_and_hash_argument_errors():
         race.RACE_ERR_UNSUPPORTED
 
 
+def test_state_bytes():
+    # F * 65 float32 per head: F = 32 * MT * KB (L16 P4: MT 4, KB 2 -> 256;
+    # L5 P3: 5 tables of 4 padded planes -> MT 2, KB 1 -> 64; L8 P2: MT 1 -> 32)
+    for (B, H, P, L, F) in [(1, 4, 4, 16, 256), (2, 3, 3, 5, 64), (1, 1, 2, 8, 32), (1, 1, 4, 32, 512)]:
+        assert race.state_bytes(B, H, P, L) == B * H * F * 65 * 4
+    out = ctypes.c_size_t(0)
+    assert race.lib().race_attn_state_bytes(1, 1, 128, 4, 8, ctypes.byref(out)) == race.RACE_ERR_UNSUPPORTED
+    assert race.lib().race_attn_state_bytes(1, 1, 64, 5, 8, ctypes.byref(out)) == race.RACE_ERR_UNSUPPORTED
+    assert race.lib().race_attn_state_bytes(0, 1, 64, 4, 8, ctypes.byref(out)) == race.RACE_ERR_INVALID_ARG
+    assert race.lib().race_attn_state_bytes(1, 1, 64, 4, 8, None) == race.RACE_ERR_INVALID_ARG
+
+
+def test_prefill_and_decode_argument_errors():
+    L = race.lib()
+    need = race.workspace_bytes(1, 1, 100, 64, 4, 8, False, 64, race.WS_FWD)
+    # K V W B H N d P L temperature chunk dtype state ws
+    ok = [FAKE, FAKE, FAKE, 1, 1, 100, 64, 4, 8, 1.0, 64, race.RACE_BF16, FAKE, FAKE]
+    assert L.race_attn_prefill(*ok, need - 1, None) == race.RACE_ERR_WORKSPACE
+    for i, v in [(0, None), (12, None), (13, None), (11, 5), (9, float("nan")), (9, float("-inf"))]:
+        bad = list(ok); bad[i] = v
+        assert L.race_attn_prefill(*bad, need, None) == race.RACE_ERR_INVALID_ARG, i
+    bad = list(ok); bad[5] = 0   # empty prompt: the zero state needs no call
+    assert L.race_attn_prefill(*bad, need, None) == race.RACE_ERR_INVALID_ARG
+    bad = list(ok); bad[10] = (1 << 20) + 1
+    assert L.race_attn_prefill(*bad, need, None) == race.RACE_ERR_UNSUPPORTED
+    # q k v W B H d P L temperature dtype state o
+    dec = [FAKE, FAKE, FAKE, FAKE, 2, 3, 64, 4, 8, 1.0, race.RACE_F32, FAKE, FAKE]
+    for i, v in [(0, None), (3, None), (11, None), (12, None), (10, 9), (9, float("nan")),
+                 (9, float("-inf")), (4, 0)]:
+        bad = list(dec); bad[i] = v
+        assert L.race_attn_decode(*bad, None) == race.RACE_ERR_INVALID_ARG, i
+    bad = list(dec); bad[11] = ctypes.c_void_p(0x10004)   # state not 16-byte aligned
+    assert L.race_attn_decode(*bad, None) == race.RACE_ERR_INVALID_ARG
+    for i, v in [(6, 32), (7, 5), (8, 64)]:
+        bad = list(dec); bad[i] = v
+        assert L.race_attn_decode(*bad, None) == race.RACE_ERR_UNSUPPORTED, i
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     # no CPU fallback: without the built library every entry point raises
     monkeypatch.setattr(race, "_lib", None)

@@ -1,0 +1,140 @@
+"""GPU parity of the decode path: a prompt sketched by race_attn_prefill, then
+one race_attn_decode step per new token, against the float64 oracle's sketch
+and decode step (dense) or its causal forward on sampled rows (stream, for a
+long prompt).
+
+Bars (relative L2 of each step's output over all heads): 1e-5 for float32
+inputs, since every step computes in float32 (a running sum over a 2e5-token
+prompt, summed in a different order than the oracle's, stays near 1e-6);
+5e-3 for bf16 inputs, whose output rounding alone is about 2^-9 relative and
+whose prompt sketch uses bf16 feature operands, as the forward does. Hard buckets
+(temperature = inf) are compared only on inputs whose projections all stay
+at least 1e-5 from zero, where float32 and float64 agree on every sign.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from helpers import from_torch, host_inputs, rel_l2, to_f64, to_torch
+from oracle import dense
+from oracle import stream as oracle_stream
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 5e-3}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import torch
+    import linear_lsh_sketch_amd as race
+    assert torch.cuda.is_available()
+    race.lib()
+    return race
+
+
+def oracle_steps(x, n0, T, beta):
+    """Per-step oracle outputs [T, B, H, d]: dense sketch of the prompt, then
+    one decode step per token."""
+    Q, K, V = (to_f64(x[k]) for k in ("Q", "K", "V"))
+    W = to_f64(x["W"])
+    B, H = Q.shape[:2]
+    out = np.zeros((T, B, H, Q.shape[-1]))
+    for b in range(B):
+        for h in range(H):
+            S, z = dense.sketch(K[b, h, :n0], V[b, h, :n0], W, beta)
+            for s in range(T):
+                i = n0 + s
+                S, z, out[s, b, h] = dense.decode_step(S, z, Q[b, h, i], K[b, h, i], V[b, h, i], W, beta)
+    return out
+
+
+def gpu_steps(race, x, n0, T, P, L, beta, chunk):
+    import torch
+    dev = torch.device("cuda:0")
+    t = {k: to_torch(v, dev) for k, v in x.items()}
+    B, H = t["Q"].shape[:2]
+    if n0 > 0:
+        state = race.prefill(t["K"][:, :, :n0].contiguous(), t["V"][:, :, :n0].contiguous(), t["W"], P, L,
+                             beta, chunk)
+    else:
+        state = race.alloc_state(B, H, P, L, dev)
+    outs = []
+    for s in range(T):
+        i = n0 + s
+        q, k, v = (t[n][:, :, i].contiguous() for n in ("Q", "K", "V"))
+        outs.append(race.decode(q, k, v, t["W"], state, P, L, beta))
+    torch.cuda.synchronize()
+    return np.stack([from_torch(o) for o in outs])
+
+
+def min_abs_projection(x, n):
+    W = to_f64(x["W"])
+    m = math.inf
+    for name in ("Q", "K"):
+        X = to_f64(x[name])[:, :, :n].reshape(-1, W.shape[-1])
+        Xh = X / np.maximum(np.linalg.norm(X, axis=1, keepdims=True), 1e-12)
+        m = min(m, float(np.min(np.abs(np.einsum("nd,lpd->nlp", Xh, W)))))
+    return m
+
+
+def check(res, ref, dtype, label):
+    assert np.all(np.isfinite(res)), label
+    errs = [rel_l2(res[s], ref[s]) for s in range(ref.shape[0])]
+    print(f"   {label} rel_l2 per step", [f"{e:.1e}" for e in errs], flush=True)
+    assert max(errs) <= TOL[dtype], (label, errs)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("P,L", [(4, 16), (2, 8), (3, 5), (1, 3), (4, 5)])
+@pytest.mark.parametrize("n0", [0, 1, 301])
+def test_decode_soft_matches_oracle(lib, dtype, P, L, n0):
+    T, B, H, beta, chunk = 5, 2, 3, 1.0, 64
+    print(f"[case] decode soft {dtype} P={P} L={L} n0={n0} T={T} B={B} H={H} chunk={chunk}", flush=True)
+    x = host_inputs(777 + n0, B, H, n0 + T, 64, P, L, dtype)
+    check(gpu_steps(lib, x, n0, T, P, L, beta, chunk), oracle_steps(x, n0, T, beta), dtype, "o")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("P,L", [(4, 16), (2, 3), (3, 5)])
+@pytest.mark.parametrize("n0", [0, 40])
+def test_decode_hard_matches_oracle(lib, dtype, P, L, n0):
+    T, B, H, chunk = 6, 1, 2, 16
+    for seed in range(50, 80):
+        x = host_inputs(seed, B, H, n0 + T, 64, P, L, dtype)
+        if min_abs_projection(x, n0 + T) > 1e-5:
+            break
+    else:
+        pytest.fail("no seed with every projection away from zero")
+    print(f"[case] decode hard {dtype} P={P} L={L} n0={n0} T={T} seed={seed}", flush=True)
+    ref = oracle_steps(x, n0, T, math.inf)
+    res = gpu_steps(lib, x, n0, T, P, L, math.inf, chunk)
+    check(res, ref, dtype, "o")
+    # rows that collide with no key are exactly zero on both sides
+    zero = np.all(ref == 0.0, axis=-1)
+    assert np.array_equal(np.all(res == 0.0, axis=-1), zero)
+
+
+def test_decode_prefill_chunk_independent(lib):
+    """The prompt's chunking only tiles the work: chunk 64 and chunk 1024 give
+    the same decode outputs up to float32 summation order."""
+    P, L, n0, T = 4, 16, 5000, 3
+    x = host_inputs(4242, 1, 2, n0 + T, 64, P, L, "f32")
+    a = gpu_steps(lib, x, n0, T, P, L, 1.0, 64)
+    b = gpu_steps(lib, x, n0, T, P, L, 1.0, 1024)
+    assert rel_l2(a, b) < 2e-6
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_after_long_prompt(lib, dtype):
+    """A long ragged prompt at the bench's head shape (H4 P4 L16, chunk 1024):
+    four decode steps against the oracle's causal forward of the whole
+    sequence at those four rows."""
+    P, L, n0, T, H = 4, 16, 3 * 65536 + 77, 4, 4
+    print(f"[case] decode long prompt {dtype} n0={n0} H={H}", flush=True)
+    x = host_inputs(20251008, 1, H, n0 + T, 64, P, L, dtype)
+    res = gpu_steps(lib, x, n0, T, P, L, 1.0, 1024)
+    ref = oracle_stream.forward(x["Q"], x["K"], x["V"], to_f64(x["W"]), 1.0, True,
+                                sample=np.arange(n0, n0 + T))          # [1, H, T, d]
+    check(res, np.moveaxis(ref, 2, 0), dtype, "o")
