@@ -7,7 +7,9 @@ race_attn_bwd (reusing them with O).
 
 Default workload: causal, B=1, H=4, N=12,000,000, d=64, P=4, L=16,
 chunk=1024, bf16 inputs with float32 sketches; Q, K, V, dO iid N(0,1) from
-the seeded Philox stream. Prints ONE JSON line.
+the seeded Philox stream. Prints ONE JSON line. After the timed layer steps
+(outside their timed region) it also times race_attn_decode, one token per
+head against the running sketch, at the same head shape ("decode").
 """
 from __future__ import annotations
 
@@ -151,6 +153,49 @@ def cpu_baseline(w, n_sample: int):
                       f"causal fwd+bwd in float64, {dt:.1f} s"}
 
 
+DECODE_HEADS = (4, 16384)   # the long-context workload's 4 heads; 512 sequences x 32 heads (1.1 GB of
+                             # state, beyond the 256 MB last-level cache, so the rate is HBM's)
+
+
+def decode_measure(w, dev, steps: int = 200):
+    """Causal decode against the running sketch (race_attn_decode) at the
+    workload's head shape: microseconds per step (one token for every head),
+    and the state read-modify-write rate against the HBM peak. Algorithmic
+    bytes per head and step: the sketch read and written once (2 * L * 2^P *
+    (d + 1) * 4) plus q, k, v in and o out."""
+    import torch
+    import linear_lsh_sketch_amd as race
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    es = 2 if w.dtype == "bf16" else 4
+    gen = torch.Generator(device=dev).manual_seed(w.seed)
+    W = torch.randn((w.L, w.P, w.d), generator=gen, device=dev).to(tdt)
+    alg = 2 * w.L * (1 << w.P) * (w.d + 1) * 4 + 4 * w.d * es
+    res = {"workload": f"decode_P{w.P}_L{w.L}_d{w.d}_{w.dtype}", "heads": [], "us_per_step": [],
+           "alg_bytes_per_head": alg, "GBps": [], "frac_hbm": [], "tokens_per_s": []}
+    for heads in DECODE_HEADS:
+        q, k, v = (torch.randn((heads, 1, w.d), generator=gen, device=dev).to(tdt) for _ in range(3))
+        state = race.alloc_state(heads, 1, w.P, w.L, dev)
+        o = torch.empty_like(q)
+        for _ in range(5):
+            race.decode(q, k, v, W, state, w.P, w.L, w.beta, out=o)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(steps):
+            race.decode(q, k, v, W, state, w.P, w.L, w.beta, out=o)
+        e.record()
+        torch.cuda.synchronize()
+        us = s.elapsed_time(e) * 1e3 / steps
+        gbps = heads * alg / (us * 1e-6) / 1e9
+        res["heads"].append(heads)
+        res["us_per_step"].append(us)
+        res["GBps"].append(gbps)
+        res["frac_hbm"].append(gbps * 1e9 / HBM_PEAK)
+        res["tokens_per_s"].append(heads / (us * 1e-6))
+        del q, k, v, state, o
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -159,6 +204,8 @@ def main():
     ap.add_argument("--workload", default="causal_long_n12M")
     ap.add_argument("--cpu-sample", type=int, default=131072)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode-step measurement that follows the timed layer steps")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy before the steps (the reference "
                          "dispatch for scaling HBM byte counters)")
@@ -291,6 +338,8 @@ def main():
         "stages_ms_per_step": {k: v / args.steps for k, v in sorted(stage_ms.items(), key=lambda kv: -kv[1])},
         "wall_s_timed": wall,
     }
+    if not args.no_decode:
+        out["decode"] = decode_measure(w, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_sample, w.N))
     print(json.dumps(out), flush=True)

@@ -8,7 +8,8 @@
 // section 5). temperature = +inf selects the hard buckets of the original
 // discrete hash (Japanese gist.science page, section 2.2): t_p = sign(h_p),
 // so each table's monomials are those of a one-hot corner; a query that
-// collides with no key then reads a zero denominator and outputs zeros.
+// collides with no key then reads a zero denominator (exactly, for fewer
+// than 2^24 keys in the state) and outputs zeros.
 //
 // The state has the layout of the kernels' sketch states: F x 64 value sums
 // (row f = canonical feature f) then F masses, F = 32 * MT * KB. Padded
@@ -32,6 +33,7 @@ namespace race {
 constexpr int DEC_NT = 512;      // threads per workgroup (one head)
 constexpr int DEC_RG = DEC_NT / 16;   // row groups: 16 lanes cover one 64-float row
 constexpr int DEC_MAXF = 512;    // largest F (MT = 8, KB = 2)
+static_assert(DEC_MAXF <= DEC_NT, "one thread per feature and mass");
 
 struct DecodeArgs {
     const void *q, *k, *v, *W;
@@ -60,12 +62,22 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecodeArgs a) {
     __shared__ float s_t[2][128];            // t_p of each table plane, [q | k][l * P + p]
     __shared__ float s_phi[2][DEC_MAXF];     // features of q and of k
     __shared__ float s_num[DEC_RG][DH + 4];  // partial read-outs per row group
-    __shared__ float s_den[DEC_NT / 64];
+    __shared__ double s_den[DEC_NT / 64];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t bh = blockIdx.x;
     const int F = a.F, LP = a.L * a.P;
     float* st = a.state + (size_t)bh * (size_t)F * 65;
+
+    // The state rows do not depend on this token: their loads are issued
+    // first, so their latency overlaps the projections and features.
+    const int cq = tid & 15, rg = tid >> 4;
+    const int nrow = F / DEC_RG;   // F is a multiple of 32
+    f32x4 s[DEC_MAXF / DEC_RG];
+#pragma unroll
+    for (int i = 0; i < DEC_MAXF / DEC_RG; ++i)
+        if (i < nrow) s[i] = *reinterpret_cast<const f32x4*>(st + (size_t)(rg + DEC_RG * i) * DH + 4 * cq);
+    const float z_old = tid < F ? st[(size_t)F * DH + tid] : 0.f;
 
     if (tid < 3 * DH) {
         const int which = tid / DH, c = tid % DH;
@@ -97,7 +109,8 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecodeArgs a) {
     }
     __syncthreads();
 
-    for (int f = tid; f < F; f += DEC_NT) {
+    if (tid < F) {
+        const int f = tid;
         int table, subset;
         feature_table_subset(f, a.P, a.KB, a.TPT, a.TPL, table, subset);
         float pq = 0.f, pk = subset == 0 ? 1.f : 0.f;   // padded table
@@ -116,15 +129,8 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecodeArgs a) {
     __syncthreads();
 
     // value sums: lane quad cq owns columns 4 cq .. 4 cq + 3 of rows rg, rg + 32, ...
-    // All rows are loaded before any is written back, so the loads overlap.
     {
-        const int cq = tid & 15, rg = tid >> 4;
-        const int nrow = F / DEC_RG;   // F is a multiple of 32
         const f32x4 vq = {s_x[2][4 * cq], s_x[2][4 * cq + 1], s_x[2][4 * cq + 2], s_x[2][4 * cq + 3]};
-        f32x4 s[DEC_MAXF / DEC_RG];
-#pragma unroll
-        for (int i = 0; i < DEC_MAXF / DEC_RG; ++i)
-            if (i < nrow) s[i] = *reinterpret_cast<const f32x4*>(st + (size_t)(rg + DEC_RG * i) * DH + 4 * cq);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < DEC_MAXF / DEC_RG; ++i) {
@@ -139,14 +145,17 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecodeArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) s_num[rg][4 * cq + j] = acc[j];
     }
-    // masses
+    // masses (F <= DEC_NT: one per thread). The denominator is summed in
+    // float64: with hard buckets the features are 0 or +-1 and the masses
+    // integers (exact in float32 below 2^24 keys), so the sum is exact and a
+    // query that collides with no key reads exactly 0.
     {
-        float den = 0.f;
-        for (int f = tid; f < F; f += DEC_NT) {
-            const float pk = s_phi[1][f];
-            float z = st[(size_t)F * DH + f] + pk;
-            if (pk != 0.f) st[(size_t)F * DH + f] = z;
-            den = fmaf(s_phi[0][f], z, den);
+        double den = 0.0;
+        if (tid < F) {
+            const float pk = s_phi[1][tid];
+            const float z = z_old + pk;
+            if (pk != 0.f) st[(size_t)F * DH + tid] = z;
+            den = (double)s_phi[0][tid] * (double)z;
         }
 #pragma unroll
         for (int m = 1; m < 64; m <<= 1) den += __shfl_xor(den, m);
@@ -154,12 +163,13 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecodeArgs a) {
     }
     __syncthreads();
     if (tid < DH) {
-        float num = 0.f, den = 0.f;
+        float num = 0.f;
+        double den = 0.0;
 #pragma unroll 8
         for (int r = 0; r < DEC_RG; ++r) num += s_num[r][tid];
 #pragma unroll
         for (int w = 0; w < DEC_NT / 64; ++w) den += s_den[w];
-        const float o = (a.hard && den == 0.f) ? 0.f : num / den;
+        const float o = (a.hard && den == 0.0) ? 0.f : num / (float)den;
         reinterpret_cast<elem*>(a.o)[bh * DH + tid] = (elem)o;
     }
 }

@@ -138,3 +138,34 @@ def test_decode_after_long_prompt(lib, dtype):
     ref = oracle_stream.forward(x["Q"], x["K"], x["V"], to_f64(x["W"]), 1.0, True,
                                 sample=np.arange(n0, n0 + T))          # [1, H, T, d]
     check(res, np.moveaxis(ref, 2, 0), dtype, "o")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_hard_closed_forms(lib, dtype):
+    """Hard buckets, every key the same vector k*: a query equal to k* shares
+    its bucket in every table, so it reads the plain mean of all values; a
+    query equal to -k* has the complementary sign pattern in every table,
+    collides with nothing and reads exactly zero."""
+    import torch
+    P, L, n0 = 4, 16, 4097
+    dev = torch.device("cuda:0")
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    gen = torch.Generator().manual_seed(99)
+    for _ in range(100):
+        W = torch.randn((L, P, 64), generator=gen).to(tdt)
+        kstar = torch.randn(64, generator=gen).to(tdt)
+        h = W.double().reshape(-1, 64) @ kstar.double()
+        if float(h.abs().min() / kstar.double().norm()) > 1e-2:
+            break
+    V = torch.randn((1, 1, n0 + 2, 64), generator=gen).to(tdt)
+    K = kstar.expand(1, 1, n0, 64).contiguous()
+    Wd, Vd = W.to(dev), V.to(dev)
+    state = lib.prefill(K.to(dev), Vd[:, :, :n0].contiguous(), Wd, P, L, math.inf, 256)
+    k1 = kstar.reshape(1, 1, 64).to(dev)
+    o_same = lib.decode(k1, k1, Vd[:, :, n0].contiguous(), Wd, state, P, L, math.inf)
+    o_opp = lib.decode((-kstar).reshape(1, 1, 64).to(dev), k1, Vd[:, :, n0 + 1].contiguous(), Wd, state, P, L,
+                       math.inf)
+    torch.cuda.synchronize()
+    mean = V[0, 0, : n0 + 1].double().mean(0).numpy()
+    assert rel_l2(from_torch(o_same).reshape(-1), mean) <= TOL[dtype]
+    assert np.all(from_torch(o_opp) == 0.0)
