@@ -202,7 +202,7 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="causal_long_n12M")
-    ap.add_argument("--cpu-sample", type=int, default=131072)
+    ap.add_argument("--cpu-sample", type=int, default=262144)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode-step measurement that follows the timed layer steps")
