@@ -103,7 +103,9 @@ race_status_t race_attn_saved_bytes(int64_t B, int64_t H, int64_t N, int d, int 
 
 /* Forward: O = RACE-Attention(Q, K, V; W, P, L, temperature, causal).
  * `temperature` is the pages' beta: it multiplies the corner logits, so a
- * larger value gives harder bucket assignments. `saved` may be NULL; if not
+ * larger value gives harder bucket assignments. It must be finite here (the
+ * hard-bucket limit, +INFINITY, is taken by race_attn_prefill and
+ * race_attn_decode only); NaN or infinity gives RACE_ERR_INVALID_ARG. `saved` may be NULL; if not
  * NULL it receives the sketch states, denominators and plane values
  * (race_attn_saved_bytes). `ws` must hold race_attn_workspace_bytes(...,
  * for_backward = 0), or (..., for_backward = 3) when `saved` is given. */
