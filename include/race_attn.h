@@ -103,9 +103,15 @@ race_status_t race_attn_saved_bytes(int64_t B, int64_t H, int64_t N, int d, int 
 
 /* Forward: O = RACE-Attention(Q, K, V; W, P, L, temperature, causal).
  * `temperature` is the pages' beta: it multiplies the corner logits, so a
- * larger value gives harder bucket assignments. It must be finite here (the
- * hard-bucket limit, +INFINITY, is taken by race_attn_prefill and
- * race_attn_decode only); NaN or infinity gives RACE_ERR_INVALID_ARG. `saved` may be NULL; if not
+ * larger value gives harder bucket assignments. +INFINITY selects the hard
+ * buckets (one-hot of the sign pattern of the projections; the discrete hash
+ * the temperature softens: Japanese gist.science page, section 2.2) for
+ * RACE_F32 inputs; a query that shares no bucket with any key it attends to
+ * then gets O = 0 (the collision counts are exact while 2^P * L times the
+ * number of keys stays below 2^24). For RACE_BF16 inputs +INFINITY gives
+ * RACE_ERR_UNSUPPORTED (the bf16 read-out operands round the counts), and
+ * the backward takes finite temperatures only. NaN and -INFINITY give
+ * RACE_ERR_INVALID_ARG. `saved` may be NULL; if not
  * NULL it receives the sketch states, denominators and plane values
  * (race_attn_saved_bytes). `ws` must hold race_attn_workspace_bytes(...,
  * for_backward = 0), or (..., for_backward = 3) when `saved` is given. */

@@ -104,9 +104,12 @@ race_status_t race_attn_saved_bytes(int64_t B, int64_t H, int64_t N, int d, int 
 race_status_t race_attn_fwd(const void* Q, const void* K, const void* V, const void* W, int64_t B, int64_t H,
                             int64_t N, int d, int P, int L, float temperature, int causal, int chunk,
                             race_dtype_t dtype, void* O, void* saved, void* ws, size_t ws_bytes, void* stream) {
-    if (!Q || !K || !V || !W || !O || !ws || !dtype_ok(dtype) || !std::isfinite(temperature) ||
-        !all_aligned({Q, K, V, W, O, ws, saved}))
+    if (!Q || !K || !V || !W || !O || !ws || !dtype_ok(dtype) || std::isnan(temperature) ||
+        temperature == -INFINITY || !all_aligned({Q, K, V, W, O, ws, saved}))
         return RACE_ERR_INVALID_ARG;
+    const bool hard = std::isinf(temperature);
+    // hard buckets: only the float32 read-out keeps the collision counts exact
+    if (hard && dtype != RACE_F32) return RACE_ERR_UNSUPPORTED;
     Shape s;
     Derived dv;
     race_status_t rc = prepare(B, H, N, d, P, L, causal, chunk, s, dv);
@@ -115,6 +118,7 @@ race_status_t race_attn_fwd(const void* Q, const void* K, const void* V, const v
     if (ws_bytes < wl.total) return RACE_ERR_WORKSPACE;
     Call c{};
     c.op = OP_FWD; c.Q = Q; c.K = K; c.V = V; c.W = W; c.saved_out = saved; c.beta = temperature; c.O = O;
+    c.hard = hard;
     c.ws = ws; c.stream = reinterpret_cast<hipStream_t>(stream);
     return go(dtype, s, dv, wl, c);
 }

@@ -32,7 +32,7 @@ struct Call {
     int32_t* ids;                  // hash
     unsigned long long* near_zero; // hash
     float* state;                  // prefill (out) / decode (in and out): running sketch [BH][F * 65]
-    int hard;                      // prefill / decode: one-hot buckets (temperature = +inf)
+    int hard;                      // forward (float32), prefill, decode: one-hot buckets (temperature = +inf)
 };
 
 template <bool F32>
@@ -139,9 +139,10 @@ race_status_t run_forward(const Shape& s, const Derived& d, const WsLayout& wl, 
     PlaneCache qc{};
     if (saved) qc = plane_cache(sv + sl.q, cl);
     float* Sb = (s.causal && saved) ? reinterpret_cast<float*>(saved) : reinterpret_cast<float*>(ws + wl.S);
-    RACE_TRY((run_totals<C, false>(s, d, c.K, c.V, nullptr, nullptr, kc, c.W, c.beta, Sb, st)));
+    const float beta = c.hard ? HARD_BETA : c.beta;
+    RACE_TRY((run_totals<C, false>(s, d, c.K, c.V, nullptr, nullptr, kc, c.W, beta, Sb, st)));
     PassArgs a{};
-    a.Xa = c.Q; a.ca = qc; a.cb = kc; a.Zsrc = c.V; a.W = c.W; a.beta = c.beta; a.out0 = O;
+    a.Xa = c.Q; a.ca = qc; a.cb = kc; a.Zsrc = c.V; a.W = c.W; a.beta = beta; a.out0 = O; a.hard = c.hard;
     a.Dv = saved ? reinterpret_cast<float*>(sv + sl.D) : nullptr;
     if (s.causal) {
         RACE_TRY(run_scan<SCAN_EXCL>(s, d, Sb, nullptr, reinterpret_cast<float*>(ws + wl.scan), st));

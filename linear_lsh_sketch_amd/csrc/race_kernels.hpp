@@ -874,6 +874,7 @@ struct PassArgs {
     int L;
     float beta;
     int causal;
+    int hard;              // FWD: hard buckets (beta = HARD_BETA): a denominator below 2^(P-1) is 0
 };
 
 // Sketch rows of feature block fb for the gradient contraction dA = M y:
@@ -1347,7 +1348,9 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
             float d = f_Dpart[tr] + f_Dpart[TB + tr] + f_Dpart[2 * TB + tr] + f_Dpart[3 * TB + tr] + d_empty;
             if (causal) d += f_Dint[tr];
             bstore_f32(rD, (it * TB + tr) * 4, d);
-            f_rD[tr] = rcp_(d);
+            // hard buckets: D is 2^P times a collision count, so anything
+            // below half a unit is an exact zero, and O = 0 for that query
+            f_rD[tr] = (a.hard && fabsf(d) < (float)(1 << (C::P - 1))) ? 0.f : rcp_(d);
         }
         if (causal) {
 #pragma unroll

@@ -120,6 +120,13 @@ def test_forward_argument_errors_before_device_work():
     # non-finite temperature
     bad = list(ok); bad[10] = float("nan")
     assert L.race_attn_fwd(*bad, need, None) == race.RACE_ERR_INVALID_ARG
+    bad = list(ok); bad[10] = float("-inf")
+    assert L.race_attn_fwd(*bad, need, None) == race.RACE_ERR_INVALID_ARG
+    # hard buckets (temperature = +inf): float32 inputs only
+    bad = list(ok); bad[10] = float("inf")
+    assert L.race_attn_fwd(*bad, need, None) == race.RACE_ERR_UNSUPPORTED
+    bad[13] = race.RACE_F32
+    assert L.race_attn_fwd(*bad, need - 1, None) == race.RACE_ERR_WORKSPACE   # accepted up to the size check
     # workspace too small
     assert L.race_attn_fwd(*ok, need - 1, None) == race.RACE_ERR_WORKSPACE
     # unsupported head dim
@@ -143,6 +150,8 @@ def test_backward_and_hash_argument_errors():
     assert L.race_attn_bwd(*a3, need, None) == race.RACE_ERR_INVALID_ARG
     a4 = list(args); a4[6] = FAKE
     assert L.race_attn_bwd(*a4, need, None) == race.RACE_ERR_INVALID_ARG
+    a6 = list(args); a6[13] = float("inf")   # the hard limit has no gradient: rejected
+    assert L.race_attn_bwd(*a6, need, None) == race.RACE_ERR_INVALID_ARG
     # both given: the smaller workspace is enough, one byte less is not
     a5 = list(args); a5[4] = FAKE; a5[6] = FAKE
     assert L.race_attn_bwd(*a5, need_saved - 1, None) == race.RACE_ERR_WORKSPACE

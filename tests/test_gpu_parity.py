@@ -287,3 +287,37 @@ def test_long_sequence_late_tokens(lib, P, L, N):
           flush=True)
     for k in got:
         assert errs[k] <= 2e-2 and errs_late[k] <= 2e-2, (k, errs[k], errs_late[k])
+
+
+# --- hard buckets (temperature = +inf), float32 forward --------------------------
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("P,L,N,chunk", [(4, 16, 300, 64), (3, 5, 517, 128), (2, 3, 130, 64), (1, 2, 200, 32)])
+def test_hard_forward_fp32(lib, causal, P, L, N, chunk):
+    """One-hot buckets through the whole forward: against the oracle's bucket
+    sums, with queries that collide with nothing reading exactly 0. Inputs
+    keep every projection at least 1e-5 from zero (float32 and float64 then
+    agree on every sign)."""
+    import math
+    import torch
+    from oracle import dense
+    for seed in range(900, 960):
+        x = host_inputs(seed, 1, 2, N, 64, P, L, "f32")
+        W64 = to_f64(x["W"])
+        X = np.concatenate([to_f64(x["Q"]).reshape(-1, 64), to_f64(x["K"]).reshape(-1, 64)])
+        h = np.einsum("nd,lpd->nlp", X / np.linalg.norm(X, axis=1, keepdims=True), W64)
+        if np.min(np.abs(h)) > 1e-5:
+            break
+    else:
+        pytest.fail("no seed with every projection away from zero")
+    print(f"[case] hard fwd fp32 P={P} L={L} N={N} chunk={chunk} causal={causal} seed={seed}", flush=True)
+    dev = torch.device("cuda:0")
+    T = {k: to_torch(v, dev) for k, v in x.items()}
+    O = from_torch(lib.forward(T["Q"], T["K"], T["V"], T["W"], P, L, math.inf, causal, chunk))
+    ref = np.stack([dense.hard_forward(to_f64(x["Q"])[0, h_], to_f64(x["K"])[0, h_], to_f64(x["V"])[0, h_],
+                                       W64, causal) for h_ in range(2)])[None]
+    zero = np.all(ref == 0.0, axis=-1)
+    assert np.array_equal(np.all(O == 0.0, axis=-1), zero)
+    err = rel_l2(O, ref)
+    print(f"   rel_l2 {err:.2e}, zero rows {int(zero.sum())}", flush=True)
+    assert err <= TOL["f32"]
