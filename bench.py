@@ -160,7 +160,8 @@ DECODE_HEADS = (4, 16384)   # the long-context workload's 4 heads; 512 sequences
 def decode_measure(w, dev, steps: int = 200):
     """Causal decode against the running sketch (race_attn_decode) at the
     workload's head shape: microseconds per step (one token for every head),
-    and the state read-modify-write rate against the HBM peak. Algorithmic
+    launched one by one from Python and replayed from a HIP graph, and the
+    state read-modify-write rate (of the launched steps) against the HBM peak. Algorithmic
     bytes per head and step: the sketch read and written once (2 * L * 2^P *
     (d + 1) * 4) plus q, k, v in and o out."""
     import torch
@@ -171,6 +172,7 @@ def decode_measure(w, dev, steps: int = 200):
     W = torch.randn((w.L, w.P, w.d), generator=gen, device=dev).to(tdt)
     alg = 2 * w.L * (1 << w.P) * (w.d + 1) * 4 + 4 * w.d * es
     res = {"workload": f"decode_P{w.P}_L{w.L}_d{w.d}_{w.dtype}", "heads": [], "us_per_step": [],
+           "us_per_step_graph": [],
            "alg_bytes_per_head": alg, "GBps": [], "frac_hbm": [], "tokens_per_s": []}
     for heads in DECODE_HEADS:
         q, k, v = (torch.randn((heads, 1, w.d), generator=gen, device=dev).to(tdt) for _ in range(3))
@@ -186,9 +188,24 @@ def decode_measure(w, dev, steps: int = 200):
         e.record()
         torch.cuda.synchronize()
         us = s.elapsed_time(e) * 1e3 / steps
+        # the same steps captured once in a HIP graph and replayed: no host
+        # launch cost between steps (how a serving loop would issue them)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(steps):
+                race.decode(q, k, v, W, state, w.P, w.L, w.beta, out=o)
+        graph.replay()
+        torch.cuda.synchronize()
+        s.record()
+        graph.replay()
+        e.record()
+        torch.cuda.synchronize()
+        us_graph = s.elapsed_time(e) * 1e3 / steps
+        del graph
         gbps = heads * alg / (us * 1e-6) / 1e9
         res["heads"].append(heads)
         res["us_per_step"].append(us)
+        res["us_per_step_graph"].append(us_graph)
         res["GBps"].append(gbps)
         res["frac_hbm"].append(gbps * 1e9 / HBM_PEAK)
         res["tokens_per_s"].append(heads / (us * 1e-6))

@@ -179,7 +179,8 @@ race_status_t race_attn_prefill(const void *K, const void *V, const void *W, int
  * token's rows ([B, H, d], dtype); k and v join `state` (in and out), then q
  * reads it, so the output o ([B, H, d], dtype) is the causal output of this
  * token, diagonal included (Japanese gist.science page, section 2.2, causal
- * prefix sums). One workgroup per head; no workspace. Calls on one stream
+ * prefix sums). W and `state` must be 16-byte aligned (RACE_ERR_INVALID_ARG
+ * otherwise). One workgroup per head; no workspace. Calls on one stream
  * run in order; two calls that update the same state concurrently race. */
 race_status_t race_attn_decode(const void *q, const void *k, const void *v, const void *W, int64_t B,
                                int64_t H, int d, int P, int L, float temperature, race_dtype_t dtype,

@@ -191,7 +191,7 @@ race_status_t race_attn_decode(const void* q, const void* k, const void* v, cons
                                int d, int P, int L, float temperature, race_dtype_t dtype, float* state, void* o,
                                void* stream) {
     if (!q || !k || !v || !W || !state || !o || !dtype_ok(dtype) || std::isnan(temperature) ||
-        temperature == -INFINITY || !all_aligned({state}))
+        temperature == -INFINITY || !all_aligned({W, state}))
         return RACE_ERR_INVALID_ARG;
     Shape s;
     Derived dv;

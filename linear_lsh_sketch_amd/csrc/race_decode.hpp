@@ -78,6 +78,17 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecodeArgs a) {
     for (int i = 0; i < DEC_MAXF / DEC_RG; ++i)
         if (i < nrow) s[i] = *reinterpret_cast<const f32x4*>(st + (size_t)(rg + DEC_RG * i) * DH + 4 * cq);
     const float z_old = tid < F ? st[(size_t)F * DH + tid] : 0.f;
+    // so are the hyperplane rows: thread (side, row), row = l * P + p, holds
+    // all 64 weights of its row, loaded 16 bytes at a time
+    const int side = tid / LP, row = tid % LP;
+    constexpr int WV = 16 / sizeof(elem);   // elements per 16-byte load
+    typedef elem wvec __attribute__((ext_vector_type(WV)));
+    wvec wr[DH / WV];
+    if (tid < 2 * LP) {
+        const wvec* w = reinterpret_cast<const wvec*>(reinterpret_cast<const elem*>(a.W) + (size_t)row * DH);
+#pragma unroll
+        for (int j = 0; j < DH / WV; ++j) wr[j] = w[j];
+    }
 
     if (tid < 3 * DH) {
         const int which = tid / DH, c = tid % DH;
@@ -94,13 +105,13 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecodeArgs a) {
     }
     __syncthreads();
 
-    // projections: thread (side, row) with row = l * P + p
+    // projections
     if (tid < 2 * LP) {
-        const int side = tid / LP, row = tid % LP;
-        const elem* w = reinterpret_cast<const elem*>(a.W) + (size_t)row * DH;
         float h = 0.f;
-#pragma unroll 16
-        for (int c = 0; c < DH; ++c) h = fmaf((float)w[c], s_x[side][c], h);
+#pragma unroll
+        for (int j = 0; j < DH / WV; ++j)
+#pragma unroll
+            for (int e = 0; e < WV; ++e) h = fmaf((float)wr[j][e], s_x[side][WV * j + e], h);
         h *= s_inv[side];
         float t;
         if (a.hard) t = h > 0.f ? 1.f : (h < 0.f ? -1.f : 0.f);

@@ -194,8 +194,9 @@ def test_prefill_and_decode_argument_errors():
                  (9, float("-inf")), (4, 0)]:
         bad = list(dec); bad[i] = v
         assert L.race_attn_decode(*bad, None) == race.RACE_ERR_INVALID_ARG, i
-    bad = list(dec); bad[11] = ctypes.c_void_p(0x10004)   # state not 16-byte aligned
-    assert L.race_attn_decode(*bad, None) == race.RACE_ERR_INVALID_ARG
+    for i in (3, 11):   # W, state not 16-byte aligned
+        bad = list(dec); bad[i] = ctypes.c_void_p(0x10004)
+        assert L.race_attn_decode(*bad, None) == race.RACE_ERR_INVALID_ARG, i
     for i, v in [(6, 32), (7, 5), (8, 64)]:
         bad = list(dec); bad[i] = v
         assert L.race_attn_decode(*bad, None) == race.RACE_ERR_UNSUPPORTED, i
