@@ -169,3 +169,33 @@ def test_decode_hard_closed_forms(lib, dtype):
     mean = V[0, 0, : n0 + 1].double().mean(0).numpy()
     assert rel_l2(from_torch(o_same).reshape(-1), mean) <= TOL[dtype]
     assert np.all(from_torch(o_opp) == 0.0)
+
+
+def test_decode_graph_replay_matches_eager(lib):
+    """Decode steps captured in a HIP graph (as a serving loop would issue
+    them) give, on every replay, the eager steps' outputs bit for bit; the
+    state is reset by eager copies between replays."""
+    import torch
+    P, L, n0, T = 4, 16, 100, 4
+    dev = torch.device("cuda:0")
+    x = host_inputs(555, 2, 2, n0 + T, 64, P, L, "bf16")
+    t = {k: to_torch(v, dev) for k, v in x.items()}
+    init = lib.prefill(t["K"][:, :, :n0].contiguous(), t["V"][:, :, :n0].contiguous(), t["W"], P, L, 1.0, 64)
+    rows = [tuple(t[n][:, :, n0 + s].contiguous() for n in ("Q", "K", "V")) for s in range(T)]
+    outs = [torch.empty_like(rows[0][0]) for _ in range(T)]
+    state = init.clone()
+    eager = [lib.decode(*rows[s], t["W"], state, P, L, 1.0).clone() for s in range(T)]
+    eager_state = state.clone()
+    state.copy_(init)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for s in range(T):
+            lib.decode(*rows[s], t["W"], state, P, L, 1.0, out=outs[s])
+    for rep in range(3):
+        state.copy_(init)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for s in range(T):
+            assert torch.equal(outs[s], eager[s]), (rep, s)
+        assert torch.equal(state, eager_state), rep
