@@ -87,9 +87,11 @@ def check(res, ref, dtype, label):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("P,L", [(4, 16), (2, 8), (3, 5), (1, 3), (4, 5)])
+@pytest.mark.parametrize("P,L", [(4, 16), (2, 8), (3, 5), (1, 3), (4, 5), (4, 32), (2, 64), (1, 100)])
 @pytest.mark.parametrize("n0", [0, 1, 301])
 def test_decode_soft_matches_oracle(lib, dtype, P, L, n0):
+    # (4, 32): the largest state, F = 512 = one thread per feature; (2, 64),
+    # (1, 100): 128 and 100 projection rows, eight projection tiles
     T, B, H, beta, chunk = 5, 2, 3, 1.0, 64
     print(f"[case] decode soft {dtype} P={P} L={L} n0={n0} T={T} B={B} H={H} chunk={chunk}", flush=True)
     x = host_inputs(777 + n0, B, H, n0 + T, 64, P, L, dtype)
