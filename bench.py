@@ -124,6 +124,26 @@ def copy_bandwidth(dev, nbytes: int = COPY_BYTES, reps: int = 5) -> float:
     return gbps
 
 
+def matmul_rate(dev, dtype, n: int = 8192, reps: int = 10) -> float:
+    """TFLOP/s of a dense n x n x n matrix product in `dtype` (the BLAS
+    library's matrix-core kernel) on this machine: the attainable matrix rate,
+    reported beside the nominal peak."""
+    import torch
+    a = torch.randn((n, n), device=dev).to(dtype)
+    b = torch.randn((n, n), device=dev).to(dtype)
+    c = a @ b
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        c = a @ b
+    e.record()
+    torch.cuda.synchronize()
+    tflops = 2 * n ** 3 * reps / (s.elapsed_time(e) / 1e3) / 1e12
+    del a, b, c
+    return tflops
+
+
 def cpu_baseline(w, n_sample: int):
     """The float64 oracle on the first n_sample tokens of every head of the
     same workload (same seeded inputs), causal forward + backward."""
@@ -325,6 +345,7 @@ def main():
     hbm_high_water = torch.cuda.max_memory_allocated() / 2**30
     # the box's own copy bandwidth, beside the nominal peak (outside the timed region)
     copy_gbps = copy_bandwidth(dev)
+    mm_tflops = matmul_rate(dev, tdt)
     if roof["unit"] == "GB/s":
         roof["copy_GBps_measured"] = copy_gbps
         roof["frac_of_copy"] = roof["achieved"] / copy_gbps
@@ -349,6 +370,8 @@ def main():
         "layer_roofline": {"bound": "hbm" if layer["bytes"] * units / HBM_PEAK >= layer["flops"] * units / peak_f
                            else "mfma", "frac": layer_t / (ms_step / 1e3),
                            "alg_GBps": layer["bytes"] * units / (ms_step / 1e3) / 1e9,
+                           "alg_TFLOPs": layer["flops"] * units / (ms_step / 1e3) / 1e12,
+                           "copy_GBps_measured": copy_gbps, "matmul_TFLOPs_measured": mm_tflops,
                            "alg_bytes_per_token_head": layer["bytes"], "alg_flops_per_token_head": layer["flops"]},
         "hbm_peak_GiB": hbm_high_water,
         "hbm_capacity_GiB": torch.cuda.get_device_properties(0).total_memory / 2**30,
