@@ -173,29 +173,32 @@ def cpu_baseline(w, n_sample: int):
                       f"causal fwd+bwd in float64, {dt:.1f} s"}
 
 
-DECODE_HEADS = (4, 16384)   # the long-context workload's 4 heads; 512 sequences x 32 heads (1.1 GB of
-                             # state, beyond the 256 MB last-level cache, so the rate is HBM's)
+# (heads, tokens per head and call): the long-context workload's 4 heads; 512
+# sequences x 32 heads (1.1 GB of state, beyond the 256 MB last-level cache,
+# so the rate is HBM's); 256 x 32 heads extending each sequence by 8 tokens
+# per call (a draft to verify, a prompt piece)
+DECODE_CASES = ((4, 1), (16384, 1), (8192, 8))
 
 
 def decode_measure(w, dev, steps: int = 200):
     """Causal decode against the running sketch (race_attn_decode) at the
-    workload's head shape: microseconds per step (one token for every head),
+    workload's head shape: microseconds per call (T tokens for every head),
     launched one by one from Python and replayed from a HIP graph, and the
-    state read-modify-write rate (of the launched steps) against the HBM peak. Algorithmic
-    bytes per head and step: the sketch read and written once (2 * L * 2^P *
-    (d + 1) * 4) plus q, k, v in and o out."""
+    state read-modify-write rate (of the launched calls) against the HBM
+    peak. Algorithmic bytes per head and call: the sketch read and written
+    once (2 * L * 2^P * (d + 1) * 4) plus q, k, v in and o out per token."""
     import torch
     import linear_lsh_sketch_amd as race
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     es = 2 if w.dtype == "bf16" else 4
     gen = torch.Generator(device=dev).manual_seed(w.seed)
     W = torch.randn((w.L, w.P, w.d), generator=gen, device=dev).to(tdt)
-    alg = 2 * w.L * (1 << w.P) * (w.d + 1) * 4 + 4 * w.d * es
-    res = {"workload": f"decode_P{w.P}_L{w.L}_d{w.d}_{w.dtype}", "heads": [], "us_per_step": [],
-           "us_per_step_graph": [],
-           "alg_bytes_per_head": alg, "GBps": [], "frac_hbm": [], "tokens_per_s": []}
-    for heads in DECODE_HEADS:
-        q, k, v = (torch.randn((heads, 1, w.d), generator=gen, device=dev).to(tdt) for _ in range(3))
+    state_rw = 2 * w.L * (1 << w.P) * (w.d + 1) * 4
+    res = {"workload": f"decode_P{w.P}_L{w.L}_d{w.d}_{w.dtype}", "heads": [], "tokens_per_call": [],
+           "us_per_call": [], "us_per_call_graph": [], "alg_bytes_per_head": [], "GBps": [], "frac_hbm": [],
+           "tokens_per_s": [], "tokens_per_s_graph": []}
+    for heads, T in DECODE_CASES:
+        q, k, v = (torch.randn((heads, 1, T, w.d), generator=gen, device=dev).to(tdt) for _ in range(3))
         state = race.alloc_state(heads, 1, w.P, w.L, dev)
         o = torch.empty_like(q)
         for _ in range(5):
@@ -208,8 +211,8 @@ def decode_measure(w, dev, steps: int = 200):
         e.record()
         torch.cuda.synchronize()
         us = s.elapsed_time(e) * 1e3 / steps
-        # the same steps captured once in a HIP graph and replayed: no host
-        # launch cost between steps (how a serving loop would issue them)
+        # the same calls captured once in a HIP graph and replayed: no host
+        # launch cost between them (how a serving loop would issue them)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             for _ in range(steps):
@@ -222,13 +225,17 @@ def decode_measure(w, dev, steps: int = 200):
         torch.cuda.synchronize()
         us_graph = s.elapsed_time(e) * 1e3 / steps
         del graph
+        alg = state_rw + 4 * T * w.d * es
         gbps = heads * alg / (us * 1e-6) / 1e9
         res["heads"].append(heads)
-        res["us_per_step"].append(us)
-        res["us_per_step_graph"].append(us_graph)
+        res["tokens_per_call"].append(T)
+        res["us_per_call"].append(us)
+        res["us_per_call_graph"].append(us_graph)
+        res["alg_bytes_per_head"].append(alg)
         res["GBps"].append(gbps)
         res["frac_hbm"].append(gbps * 1e9 / HBM_PEAK)
-        res["tokens_per_s"].append(heads / (us * 1e-6))
+        res["tokens_per_s"].append(heads * T / (us * 1e-6))
+        res["tokens_per_s_graph"].append(heads * T / (us_graph * 1e-6))
         del q, k, v, state, o
     return res
 

@@ -175,16 +175,19 @@ race_status_t race_attn_prefill(const void *K, const void *V, const void *W, int
                                 race_dtype_t dtype, float *state, void *ws, size_t ws_bytes,
                                 void *stream);
 
-/* One causal decode step for every (batch, head): q, k, v are the new
- * token's rows ([B, H, d], dtype); k and v join `state` (in and out), then q
- * reads it, so the output o ([B, H, d], dtype) is the causal output of this
- * token, diagonal included (Japanese gist.science page, section 2.2, causal
- * prefix sums). W and `state` must be 16-byte aligned (RACE_ERR_INVALID_ARG
- * otherwise). One workgroup per head; no workspace. Calls on one stream
- * run in order; two calls that update the same state concurrently race. */
+/* Causal decode of T new tokens for every (batch, head): q, k, v are their
+ * rows ([B, H, T, d], dtype). In token order, each token's k and v join
+ * `state` (in and out), then its q reads it, so o ([B, H, T, d], dtype) holds
+ * the causal output of each token, diagonal included (Japanese gist.science
+ * page, section 2.2, causal prefix sums): T = 1 is one generation step, T > 1
+ * extends the sequence by several tokens (a draft to verify, a prompt piece)
+ * while reading and writing the state once. T >= 1. W and `state` must be
+ * 16-byte aligned (RACE_ERR_INVALID_ARG otherwise). One workgroup per head;
+ * no workspace. Calls on one stream run in order; two calls that update the
+ * same state concurrently race. */
 race_status_t race_attn_decode(const void *q, const void *k, const void *v, const void *W, int64_t B,
-                               int64_t H, int d, int P, int L, float temperature, race_dtype_t dtype,
-                               float *state, void *o, void *stream);
+                               int64_t H, int64_t T, int d, int P, int L, float temperature,
+                               race_dtype_t dtype, float *state, void *o, void *stream);
 
 /* Profiling aid (not needed for computation). For the CALLING THREAD only:
  * `events` is an array of `capacity` (>= 2) caller-created hipEvent_t handles.

@@ -51,7 +51,7 @@ def lib():
         L.race_attn_state_bytes.argtypes = [i64, i64, i32, i32, i32, ctypes.POINTER(sz)]
         L.race_attn_prefill.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, i32, fl, i32, i32, vp, vp,
                                         sz, vp]
-        L.race_attn_decode.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, fl, i32, vp, vp, vp]
+        L.race_attn_decode.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, fl, i32, vp, vp, vp]
         L.race_attn_profile_events.argtypes = [vp, i32]
         L.race_attn_profile_count.argtypes = []
         L.race_attn_profile_stage.argtypes = [i32]
@@ -243,18 +243,26 @@ def _check_state(state, B, H, P, L, d, device):
 
 
 def race_attn_decode(q, k, v, W, state, P, L, temperature=1.0, out=None, stream=None):
-    """One causal decode step: q, k, v are [B, H, d]; k, v join `state` (in
-    place), then q reads it. Returns o [B, H, d]."""
+    """Causal decode: q, k, v are [B, H, d] (one token per head) or
+    [B, H, T, d] (T tokens per head, in order); each token's k, v join
+    `state` (in place), then its q reads it. Returns o shaped like q."""
     import torch
     _check_inputs(q, k, v, W)
-    B, H, d = q.shape
+    if q.dim() == 3:
+        (B, H, d), T = q.shape, 1
+    elif q.dim() == 4:
+        B, H, T, d = q.shape
+    else:
+        raise ValueError("q must be [B, H, d] or [B, H, T, d]")
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must share one shape")
     if tuple(W.shape) != (L, P, d):
         raise ValueError(f"W must be [L, P, d] = {(L, P, d)}, got {tuple(W.shape)}")
     _check_state(state, B, H, P, L, d, q.device)
     o = out if out is not None else torch.empty_like(q)
-    code = lib().race_attn_decode(_p(q), _p(k), _p(v), _p(W), B, H, d, P, L, float(temperature),
+    if out is not None and (out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous tensor shaped like q")
+    code = lib().race_attn_decode(_p(q), _p(k), _p(v), _p(W), B, H, T, d, P, L, float(temperature),
                                   _dtype_code(q), _p(state), _p(o), _stream(stream))
     _check(code, "race_attn_decode")
     return o

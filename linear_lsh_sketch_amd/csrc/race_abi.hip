@@ -188,15 +188,16 @@ race_status_t race_attn_prefill(const void* K, const void* V, const void* W, int
 }
 
 race_status_t race_attn_decode(const void* q, const void* k, const void* v, const void* W, int64_t B, int64_t H,
-                               int d, int P, int L, float temperature, race_dtype_t dtype, float* state, void* o,
-                               void* stream) {
+                               int64_t T, int d, int P, int L, float temperature, race_dtype_t dtype, float* state,
+                               void* o, void* stream) {
     if (!q || !k || !v || !W || !state || !o || !dtype_ok(dtype) || std::isnan(temperature) ||
         temperature == -INFINITY || !all_aligned({W, state}))
         return RACE_ERR_INVALID_ARG;
     Shape s;
     Derived dv;
-    race_status_t rc = prepare(B, H, 1, d, P, L, 0, 1, s, dv);
+    race_status_t rc = prepare(B, H, T, d, P, L, 0, 1, s, dv);
     if (rc != RACE_OK) return rc;
+    if (T > 0x7fffffff) return RACE_ERR_UNSUPPORTED;
     Call c{};
     c.op = OP_DECODE; c.Q = q; c.K = k; c.V = v; c.W = W; c.O = o; c.beta = temperature;
     c.hard = std::isinf(temperature); c.state = state; c.stream = reinterpret_cast<hipStream_t>(stream);

@@ -1,7 +1,8 @@
 // Causal decode against a running sketch (gfx950).
 //
-// One new token per (batch, head): its key and value join the sketch, then
-// its query reads the sketch out (causal sums include the diagonal). The
+// T new tokens per (batch, head), in order: each token's key and value join
+// the sketch, then its query reads the sketch out (causal sums include the
+// diagonal). The
 // sketch replaces the key-value cache: L * 2^P * (d + 1) floats per head,
 // whatever the length of the sequence so far (efficient key-value caching
 // at inference: Japanese gist.science page, section 6; Korean page,
@@ -17,9 +18,10 @@
 // subset is 1 for every key (so their state rows stay the plain sums of
 // [v | 1]) and every other feature is 0; the read-out leaves them out.
 //
-// Work per head: one projection of q and of k on the L * P planes, the
-// features, one read-modify-write of the state (2 * F * 65 * 4 bytes: the
-// bound) and the read-out from the updated rows while they are in registers.
+// Work per head: one read of the state into registers, then per token one
+// projection of q and of k on the L * P planes, the features, the update of
+// the rows in registers and the read-out from them, and one write of the
+// state at the end: 2 * F * 65 * 4 bytes per call (the bound for T = 1).
 // No matrix cores: a head's update is an outer product of one feature row
 // and one value row, and the read-out a vector-matrix product over F rows.
 #pragma once
@@ -38,7 +40,8 @@ static_assert(DEC_MAXF <= DEC_NT, "one thread per feature and mass");
 struct DecodeArgs {
     const void *q, *k, *v, *W;
     float* state;   // [BH][F * 65]
-    void* o;        // [BH][64]
+    void* o;        // [BH][T][64]
+    int T;          // new tokens per head, processed in order
     int P, L, F, KB, TPT, TPL;
     float beta;
     int hard;
@@ -57,7 +60,7 @@ __device__ inline void feature_table_subset(int f, int P, int KB, int TPT, int T
 template <bool F32>
 __global__ __launch_bounds__(DEC_NT) void k_decode(DecodeArgs a) {
     using elem = typename Prec<F32>::elem;
-    __shared__ float s_x[3][DH];             // q, k, v of this head
+    __shared__ float s_x[3][DH];             // q, k, v of the current token
     __shared__ float s_inv[2];               // 1 / max(|q|, eps), 1 / max(|k|, eps)
     __shared__ float s_t[2][128];            // t_p of each table plane, [q | k][l * P + p]
     __shared__ float s_phi[2][DEC_MAXF];     // features of q and of k
@@ -69,15 +72,16 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecodeArgs a) {
     const int F = a.F, LP = a.L * a.P;
     float* st = a.state + (size_t)bh * (size_t)F * 65;
 
-    // The state rows do not depend on this token: their loads are issued
-    // first, so their latency overlaps the projections and features.
+    // The state rows do not depend on the new tokens: their loads are issued
+    // first, so their latency overlaps the first token's projections. They
+    // stay in registers for all T tokens and are written back once.
     const int cq = tid & 15, rg = tid >> 4;
     const int nrow = F / DEC_RG;   // F is a multiple of 32
     f32x4 s[DEC_MAXF / DEC_RG];
 #pragma unroll
     for (int i = 0; i < DEC_MAXF / DEC_RG; ++i)
         if (i < nrow) s[i] = *reinterpret_cast<const f32x4*>(st + (size_t)(rg + DEC_RG * i) * DH + 4 * cq);
-    const float z_old = tid < F ? st[(size_t)F * DH + tid] : 0.f;
+    float z = tid < F ? st[(size_t)F * DH + tid] : 0.f;
     // so are the hyperplane rows: thread (side, row), row = l * P + p, holds
     // all 64 weights of its row, loaded 16 bytes at a time
     const int side = tid / LP, row = tid % LP;
@@ -90,99 +94,105 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecodeArgs a) {
         for (int j = 0; j < DH / WV; ++j) wr[j] = w[j];
     }
 
-    if (tid < 3 * DH) {
-        const int which = tid / DH, c = tid % DH;
-        const void* src = which == 0 ? a.q : which == 1 ? a.k : a.v;
-        s_x[which][c] = (float)reinterpret_cast<const elem*>(src)[bh * DH + c];
-    }
-    __syncthreads();
-    if (wv < 2) {
-        const float x = s_x[wv][lane];
-        float ss = x * x;
-#pragma unroll
-        for (int m = 1; m < 64; m <<= 1) ss += __shfl_xor(ss, m);
-        if (lane == 0) s_inv[wv] = 1.f / fmaxf(sqrtf(ss), NORM_EPS);
-    }
-    __syncthreads();
-
-    // projections
-    if (tid < 2 * LP) {
-        float h = 0.f;
-#pragma unroll
-        for (int j = 0; j < DH / WV; ++j)
-#pragma unroll
-            for (int e = 0; e < WV; ++e) h = fmaf((float)wr[j][e], s_x[side][WV * j + e], h);
-        h *= s_inv[side];
-        float t;
-        if (a.hard) t = h > 0.f ? 1.f : (h < 0.f ? -1.f : 0.f);
-        else t = tanhf(a.beta * tanhf(h));
-        s_t[side][row] = t;
-    }
-    __syncthreads();
-
-    if (tid < F) {
-        const int f = tid;
-        int table, subset;
-        feature_table_subset(f, a.P, a.KB, a.TPT, a.TPL, table, subset);
-        float pq = 0.f, pk = subset == 0 ? 1.f : 0.f;   // padded table
-        if (table < a.L) {
-            pq = 1.f;
-            pk = 1.f;
-            for (int p = 0; p < a.P; ++p)
-                if ((subset >> p) & 1) {
-                    pq *= s_t[0][table * a.P + p];
-                    pk *= s_t[1][table * a.P + p];
-                }
+    for (int tok = 0; tok < a.T; ++tok) {
+        const int64_t r = bh * a.T + tok;   // row of q, k, v, o
+        __syncthreads();   // the previous token's readers of the shared arrays are done
+        if (tid < 3 * DH) {
+            const int which = tid / DH, c = tid % DH;
+            const void* src = which == 0 ? a.q : which == 1 ? a.k : a.v;
+            s_x[which][c] = (float)reinterpret_cast<const elem*>(src)[r * DH + c];
         }
-        s_phi[0][f] = pq;
-        s_phi[1][f] = pk;
-    }
-    __syncthreads();
-
-    // value sums: lane quad cq owns columns 4 cq .. 4 cq + 3 of rows rg, rg + 32, ...
-    {
-        const f32x4 vq = {s_x[2][4 * cq], s_x[2][4 * cq + 1], s_x[2][4 * cq + 2], s_x[2][4 * cq + 3]};
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        __syncthreads();
+        if (wv < 2) {
+            const float x = s_x[wv][lane];
+            float ss = x * x;
 #pragma unroll
-        for (int i = 0; i < DEC_MAXF / DEC_RG; ++i) {
-            if (i < nrow) {
-                const int f = rg + DEC_RG * i;
-                const float pk = s_phi[1][f], pq = s_phi[0][f];
-                s[i] += pk * vq;
-                if (pk != 0.f) *reinterpret_cast<f32x4*>(st + (size_t)f * DH + 4 * cq) = s[i];
-                acc += pq * s[i];
-            }
+            for (int m = 1; m < 64; m <<= 1) ss += __shfl_xor(ss, m);
+            if (lane == 0) s_inv[wv] = 1.f / fmaxf(sqrtf(ss), NORM_EPS);
         }
+        __syncthreads();
+
+        // projections
+        if (tid < 2 * LP) {
+            float h = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) s_num[rg][4 * cq + j] = acc[j];
-    }
-    // masses (F <= DEC_NT: one per thread). The denominator is summed in
-    // float64: with hard buckets the features are 0 or +-1 and the masses
-    // integers (exact in float32 below 2^24 keys), so the sum is exact and a
-    // query that collides with no key reads exactly 0.
-    {
-        double den = 0.0;
+            for (int j = 0; j < DH / WV; ++j)
+#pragma unroll
+                for (int e = 0; e < WV; ++e) h = fmaf((float)wr[j][e], s_x[side][WV * j + e], h);
+            h *= s_inv[side];
+            float t;
+            if (a.hard) t = h > 0.f ? 1.f : (h < 0.f ? -1.f : 0.f);
+            else t = tanhf(a.beta * tanhf(h));
+            s_t[side][row] = t;
+        }
+        __syncthreads();
+
         if (tid < F) {
-            const float pk = s_phi[1][tid];
-            const float z = z_old + pk;
-            if (pk != 0.f) st[(size_t)F * DH + tid] = z;
-            den = (double)s_phi[0][tid] * (double)z;
+            const int f = tid;
+            int table, subset;
+            feature_table_subset(f, a.P, a.KB, a.TPT, a.TPL, table, subset);
+            float pq = 0.f, pk = subset == 0 ? 1.f : 0.f;   // padded table
+            if (table < a.L) {
+                pq = 1.f;
+                pk = 1.f;
+                for (int p = 0; p < a.P; ++p)
+                    if ((subset >> p) & 1) {
+                        pq *= s_t[0][table * a.P + p];
+                        pk *= s_t[1][table * a.P + p];
+                    }
+            }
+            s_phi[0][f] = pq;
+            s_phi[1][f] = pk;
         }
+        __syncthreads();
+
+        // value sums: lane quad cq owns columns 4 cq .. 4 cq + 3 of rows rg, rg + 32, ...
+        {
+            const f32x4 vq = {s_x[2][4 * cq], s_x[2][4 * cq + 1], s_x[2][4 * cq + 2], s_x[2][4 * cq + 3]};
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int m = 1; m < 64; m <<= 1) den += __shfl_xor(den, m);
-        if (lane == 0) s_den[wv] = den;
-    }
-    __syncthreads();
-    if (tid < DH) {
-        float num = 0.f;
-        double den = 0.0;
+            for (int i = 0; i < DEC_MAXF / DEC_RG; ++i) {
+                if (i < nrow) {
+                    const int f = rg + DEC_RG * i;
+                    s[i] += s_phi[1][f] * vq;
+                    acc += s_phi[0][f] * s[i];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s_num[rg][4 * cq + j] = acc[j];
+        }
+        // masses (F <= DEC_NT: one per thread). The denominator is summed in
+        // float64: with hard buckets the features are 0 or +-1 and the masses
+        // integers (exact in float32 below 2^24 keys), so the sum is exact and
+        // a query that collides with no key reads exactly 0.
+        {
+            double den = 0.0;
+            if (tid < F) {
+                z += s_phi[1][tid];
+                den = (double)s_phi[0][tid] * (double)z;
+            }
+#pragma unroll
+            for (int m = 1; m < 64; m <<= 1) den += __shfl_xor(den, m);
+            if (lane == 0) s_den[wv] = den;
+        }
+        __syncthreads();
+        if (tid < DH) {
+            float num = 0.f;
+            double den = 0.0;
 #pragma unroll 8
-        for (int r = 0; r < DEC_RG; ++r) num += s_num[r][tid];
+            for (int rr = 0; rr < DEC_RG; ++rr) num += s_num[rr][tid];
 #pragma unroll
-        for (int w = 0; w < DEC_NT / 64; ++w) den += s_den[w];
-        const float o = (a.hard && den == 0.0) ? 0.f : num / (float)den;
-        reinterpret_cast<elem*>(a.o)[bh * DH + tid] = (elem)o;
+            for (int w = 0; w < DEC_NT / 64; ++w) den += s_den[w];
+            const float o = (a.hard && den == 0.0) ? 0.f : num / (float)den;
+            reinterpret_cast<elem*>(a.o)[r * DH + tid] = (elem)o;
+        }
     }
+
+    // write the state back once
+#pragma unroll
+    for (int i = 0; i < DEC_MAXF / DEC_RG; ++i)
+        if (i < nrow) *reinterpret_cast<f32x4*>(st + (size_t)(rg + DEC_RG * i) * DH + 4 * cq) = s[i];
+    if (tid < F) st[(size_t)F * DH + tid] = z;
 }
 
 }  // namespace race

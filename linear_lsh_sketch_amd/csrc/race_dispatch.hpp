@@ -179,7 +179,7 @@ race_status_t run(const Shape& s, const Derived& d, const WsLayout& wl, const Ca
     }
     if (c.op == OP_DECODE) {
         DecodeArgs a{};
-        a.q = c.Q; a.k = c.K; a.v = c.V; a.W = c.W; a.state = c.state; a.o = c.O;
+        a.q = c.Q; a.k = c.K; a.v = c.V; a.W = c.W; a.state = c.state; a.o = c.O; a.T = (int)s.N;
         a.P = s.P; a.L = s.L; a.F = C::F; a.KB = C::KB; a.TPT = C::TPT; a.TPL = C::TPL;
         a.beta = c.beta; a.hard = c.hard;
         static_assert(C::F <= DEC_MAXF && C::F % DEC_RG == 0, "decode tiling");

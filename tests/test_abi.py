@@ -188,16 +188,18 @@ def test_prefill_and_decode_argument_errors():
     assert L.race_attn_prefill(*bad, need, None) == race.RACE_ERR_INVALID_ARG
     bad = list(ok); bad[10] = (1 << 20) + 1
     assert L.race_attn_prefill(*bad, need, None) == race.RACE_ERR_UNSUPPORTED
-    # q k v W B H d P L temperature dtype state o
-    dec = [FAKE, FAKE, FAKE, FAKE, 2, 3, 64, 4, 8, 1.0, race.RACE_F32, FAKE, FAKE]
-    for i, v in [(0, None), (3, None), (11, None), (12, None), (10, 9), (9, float("nan")),
-                 (9, float("-inf")), (4, 0)]:
+    # q k v W B H T d P L temperature dtype state o
+    dec = [FAKE, FAKE, FAKE, FAKE, 2, 3, 1, 64, 4, 8, 1.0, race.RACE_F32, FAKE, FAKE]
+    for i, v in [(0, None), (3, None), (12, None), (13, None), (11, 9), (10, float("nan")),
+                 (10, float("-inf")), (4, 0), (6, 0), (6, -3)]:
         bad = list(dec); bad[i] = v
         assert L.race_attn_decode(*bad, None) == race.RACE_ERR_INVALID_ARG, i
-    for i in (3, 11):   # W, state not 16-byte aligned
+    for i in (3, 12):   # W, state not 16-byte aligned
         bad = list(dec); bad[i] = ctypes.c_void_p(0x10004)
         assert L.race_attn_decode(*bad, None) == race.RACE_ERR_INVALID_ARG, i
-    for i, v in [(6, 32), (7, 5), (8, 64)]:
+    bad = list(dec); bad[6] = 1 << 31   # more tokens than a 32-bit count
+    assert L.race_attn_decode(*bad, None) == race.RACE_ERR_UNSUPPORTED
+    for i, v in [(7, 32), (8, 5), (9, 64)]:
         bad = list(dec); bad[i] = v
         assert L.race_attn_decode(*bad, None) == race.RACE_ERR_UNSUPPORTED, i
 

@@ -201,3 +201,63 @@ def test_decode_graph_replay_matches_eager(lib):
         for s in range(T):
             assert torch.equal(outs[s], eager[s]), (rep, s)
         assert torch.equal(state, eager_state), rep
+
+
+def gpu_multi(race, x, n0, T, P, L, beta, chunk):
+    """Prompt sketch, then all T tokens in one race_attn_decode call."""
+    import torch
+    dev = torch.device("cuda:0")
+    t = {k: to_torch(v, dev) for k, v in x.items()}
+    B, H = t["Q"].shape[:2]
+    if n0 > 0:
+        state = race.prefill(t["K"][:, :, :n0].contiguous(), t["V"][:, :, :n0].contiguous(), t["W"], P, L,
+                             beta, chunk)
+    else:
+        state = race.alloc_state(B, H, P, L, dev)
+    q, k, v = (t[n][:, :, n0:n0 + T].contiguous() for n in ("Q", "K", "V"))
+    o = race.decode(q, k, v, t["W"], state, P, L, beta)
+    torch.cuda.synchronize()
+    return np.moveaxis(from_torch(o), 2, 0), state
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("P,L", [(4, 16), (3, 5), (4, 32)])
+@pytest.mark.parametrize("n0", [0, 301])
+@pytest.mark.parametrize("beta", [1.0, math.inf])
+def test_decode_several_tokens_per_call(lib, dtype, P, L, n0, beta):
+    """T = 7 tokens per head in one call (the state read and written once)
+    against the oracle's seven decode steps."""
+    T, B, H, chunk = 7, 2, 2, 64
+    seed = 4000 + n0
+    if math.isinf(beta):
+        for seed in range(4000, 4040):
+            x = host_inputs(seed, B, H, n0 + T, 64, P, L, dtype)
+            if min_abs_projection(x, n0 + T) > 1e-5:
+                break
+        else:
+            pytest.fail("no seed with every projection away from zero")
+    x = host_inputs(seed, B, H, n0 + T, 64, P, L, dtype)
+    print(f"[case] decode T={T} {dtype} P={P} L={L} n0={n0} beta={beta} seed={seed}", flush=True)
+    res, _ = gpu_multi(lib, x, n0, T, P, L, beta, chunk)
+    check(res, oracle_steps(x, n0, T, beta), dtype, "o")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_several_tokens_equal_single_steps(lib, dtype):
+    """One call with T = 9 tokens gives the outputs and the final state of
+    nine one-token calls bit for bit (same arithmetic, the state only stays
+    in registers between the tokens)."""
+    import torch
+    P, L, n0, T = 4, 16, 200, 9
+    x = host_inputs(4321, 1, 3, n0 + T, 64, P, L, dtype)
+    multi, st_multi = gpu_multi(lib, x, n0, T, P, L, 1.0, 64)
+    dev = torch.device("cuda:0")
+    t = {k: to_torch(v, dev) for k, v in x.items()}
+    state = lib.prefill(t["K"][:, :, :n0].contiguous(), t["V"][:, :, :n0].contiguous(), t["W"], P, L, 1.0, 64)
+    singles = []
+    for s in range(T):
+        q, k, v = (t[n][:, :, n0 + s].contiguous() for n in ("Q", "K", "V"))
+        singles.append(from_torch(lib.decode(q, k, v, t["W"], state, P, L, 1.0)))
+    torch.cuda.synchronize()
+    assert np.array_equal(multi, np.stack(singles))
+    assert torch.equal(st_multi, state)
