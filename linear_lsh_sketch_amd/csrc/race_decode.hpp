@@ -57,10 +57,13 @@ __device__ inline void feature_table_subset(int f, int P, int KB, int TPT, int T
     subset = jj % R;
 }
 
-template <bool F32>
-__global__ __launch_bounds__(DEC_NT) void k_decode(DecodeArgs a) {
+// T = 1: the state rows are updated and written back as soon as the
+// features are known. NR = F / 32 state rows per thread (a compile-time
+// count, so the registers match the state: 95 at F = 256 in bf16).
+template <bool F32, int NR>
+__global__ __launch_bounds__(DEC_NT) void k_decode_one(DecodeArgs a) {
     using elem = typename Prec<F32>::elem;
-    __shared__ float s_x[3][DH];             // q, k, v of the current token
+    __shared__ float s_x[3][DH];             // q, k, v of this head
     __shared__ float s_inv[2];               // 1 / max(|q|, eps), 1 / max(|k|, eps)
     __shared__ float s_t[2][128];            // t_p of each table plane, [q | k][l * P + p]
     __shared__ float s_phi[2][DEC_MAXF];     // features of q and of k
@@ -72,16 +75,14 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecodeArgs a) {
     const int F = a.F, LP = a.L * a.P;
     float* st = a.state + (size_t)bh * (size_t)F * 65;
 
-    // The state rows do not depend on the new tokens: their loads are issued
-    // first, so their latency overlaps the first token's projections. They
-    // stay in registers for all T tokens and are written back once.
+    // The state rows do not depend on this token: their loads are issued
+    // first, so their latency overlaps the projections and features.
     const int cq = tid & 15, rg = tid >> 4;
-    const int nrow = F / DEC_RG;   // F is a multiple of 32
-    f32x4 s[DEC_MAXF / DEC_RG];
+    f32x4 s[NR];
 #pragma unroll
-    for (int i = 0; i < DEC_MAXF / DEC_RG; ++i)
-        if (i < nrow) s[i] = *reinterpret_cast<const f32x4*>(st + (size_t)(rg + DEC_RG * i) * DH + 4 * cq);
-    float z = tid < F ? st[(size_t)F * DH + tid] : 0.f;
+    for (int i = 0; i < NR; ++i)
+        s[i] = *reinterpret_cast<const f32x4*>(st + (size_t)(rg + DEC_RG * i) * DH + 4 * cq);
+    const float z_old = tid < F ? st[(size_t)F * DH + tid] : 0.f;
     // so are the hyperplane rows: thread (side, row), row = l * P + p, holds
     // all 64 weights of its row, loaded 16 bytes at a time
     const int side = tid / LP, row = tid % LP;
@@ -94,13 +95,143 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecodeArgs a) {
         for (int j = 0; j < DH / WV; ++j) wr[j] = w[j];
     }
 
+    if (tid < 3 * DH) {
+        const int which = tid / DH, c = tid % DH;
+        const void* src = which == 0 ? a.q : which == 1 ? a.k : a.v;
+        s_x[which][c] = (float)reinterpret_cast<const elem*>(src)[bh * DH + c];
+    }
+    __syncthreads();
+    if (wv < 2) {
+        const float x = s_x[wv][lane];
+        float ss = x * x;
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) ss += __shfl_xor(ss, m);
+        if (lane == 0) s_inv[wv] = 1.f / fmaxf(sqrtf(ss), NORM_EPS);
+    }
+    __syncthreads();
+
+    // projections
+    if (tid < 2 * LP) {
+        float h = 0.f;
+#pragma unroll
+        for (int j = 0; j < DH / WV; ++j)
+#pragma unroll
+            for (int e = 0; e < WV; ++e) h = fmaf((float)wr[j][e], s_x[side][WV * j + e], h);
+        h *= s_inv[side];
+        float t;
+        if (a.hard) t = h > 0.f ? 1.f : (h < 0.f ? -1.f : 0.f);
+        else t = tanhf(a.beta * tanhf(h));
+        s_t[side][row] = t;
+    }
+    __syncthreads();
+
+    if (tid < F) {
+        const int f = tid;
+        int table, subset;
+        feature_table_subset(f, a.P, a.KB, a.TPT, a.TPL, table, subset);
+        float pq = 0.f, pk = subset == 0 ? 1.f : 0.f;   // padded table
+        if (table < a.L) {
+            pq = 1.f;
+            pk = 1.f;
+            for (int p = 0; p < a.P; ++p)
+                if ((subset >> p) & 1) {
+                    pq *= s_t[0][table * a.P + p];
+                    pk *= s_t[1][table * a.P + p];
+                }
+        }
+        s_phi[0][f] = pq;
+        s_phi[1][f] = pk;
+    }
+    __syncthreads();
+
+    // value sums: lane quad cq owns columns 4 cq .. 4 cq + 3 of rows rg, rg + 32, ...
+    {
+        const f32x4 vq = {s_x[2][4 * cq], s_x[2][4 * cq + 1], s_x[2][4 * cq + 2], s_x[2][4 * cq + 3]};
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int f = rg + DEC_RG * i;
+            const float pk = s_phi[1][f], pq = s_phi[0][f];
+            s[i] += pk * vq;
+            if (pk != 0.f) *reinterpret_cast<f32x4*>(st + (size_t)f * DH + 4 * cq) = s[i];
+            acc += pq * s[i];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s_num[rg][4 * cq + j] = acc[j];
+    }
+    // masses (F <= DEC_NT: one per thread). The denominator is summed in
+    // float64: with hard buckets the features are 0 or +-1 and the masses
+    // integers (exact in float32 below 2^24 keys), so the sum is exact and a
+    // query that collides with no key reads exactly 0.
+    {
+        double den = 0.0;
+        if (tid < F) {
+            const float pk = s_phi[1][tid];
+            const float z = z_old + pk;
+            if (pk != 0.f) st[(size_t)F * DH + tid] = z;
+            den = (double)s_phi[0][tid] * (double)z;
+        }
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) den += __shfl_xor(den, m);
+        if (lane == 0) s_den[wv] = den;
+    }
+    __syncthreads();
+    if (tid < DH) {
+        float num = 0.f;
+        double den = 0.0;
+#pragma unroll 8
+        for (int r = 0; r < DEC_RG; ++r) num += s_num[r][tid];
+#pragma unroll
+        for (int w = 0; w < DEC_NT / 64; ++w) den += s_den[w];
+        const float o = (a.hard && den == 0.0) ? 0.f : num / (float)den;
+        reinterpret_cast<elem*>(a.o)[bh * DH + tid] = (elem)o;
+    }
+}
+
+// T > 1: the state rows stay in registers across the tokens and are written
+// back during the last token; the hyperplanes sit in LDS and each token's
+// q, k, v rows are loaded while the previous token is processed (116
+// registers at F = 256 in bf16: two workgroups per CU).
+template <bool F32, int NR>
+__global__ __launch_bounds__(DEC_NT) void k_decode_multi(DecodeArgs a) {
+    using elem = typename Prec<F32>::elem;
+    __shared__ float s_x[3][DH];             // q, k, v of the current token
+    __shared__ float s_inv[2];               // 1 / max(|q|, eps), 1 / max(|k|, eps)
+    __shared__ float s_t[2][128];            // t_p of each table plane, [q | k][l * P + p]
+    __shared__ float s_phi[2][DEC_MAXF];     // features of q and of k
+    __shared__ float s_num[DEC_RG][DH + 4];  // partial read-outs per row group
+    __shared__ double s_den[DEC_NT / 64];
+    __shared__ float s_w[128][DH + 1];       // hyperplane rows (padded: conflict-free row reads)
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t bh = blockIdx.x;
+    const int F = a.F, LP = a.L * a.P;
+    float* st = a.state + (size_t)bh * (size_t)F * 65;
+
+    // The state rows do not depend on the new tokens: their loads are issued
+    // first, so their latency overlaps the first token's projections. They
+    // stay in registers for all T tokens and are written back once.
+    const int cq = tid & 15, rg = tid >> 4;
+    f32x4 s[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+        s[i] = *reinterpret_cast<const f32x4*>(st + (size_t)(rg + DEC_RG * i) * DH + 4 * cq);
+    float z = tid < F ? st[(size_t)F * DH + tid] : 0.f;
+    // the hyperplanes, once, into LDS (read there for every token)
+    for (int e = tid; e < LP * DH; e += DEC_NT) s_w[e / DH][e % DH] = (float)reinterpret_cast<const elem*>(a.W)[e];
+    const int side = tid / LP, row = tid % LP;
+    // q, k, v rows are loaded one token ahead: thread tid < 3 * 64 holds one
+    // element of the next token while the current one is processed
+    const int which = tid / DH, col = tid % DH;
+    const elem* src = reinterpret_cast<const elem*>(which == 0 ? a.q : which == 1 ? a.k : a.v);
+    float nx = tid < 3 * DH ? (float)src[bh * a.T * DH + col] : 0.f;
+
     for (int tok = 0; tok < a.T; ++tok) {
         const int64_t r = bh * a.T + tok;   // row of q, k, v, o
         __syncthreads();   // the previous token's readers of the shared arrays are done
         if (tid < 3 * DH) {
-            const int which = tid / DH, c = tid % DH;
-            const void* src = which == 0 ? a.q : which == 1 ? a.k : a.v;
-            s_x[which][c] = (float)reinterpret_cast<const elem*>(src)[r * DH + c];
+            s_x[which][col] = nx;
+            if (tok + 1 < a.T) nx = (float)src[(r + 1) * DH + col];
         }
         __syncthreads();
         if (wv < 2) {
@@ -115,10 +246,8 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecodeArgs a) {
         // projections
         if (tid < 2 * LP) {
             float h = 0.f;
-#pragma unroll
-            for (int j = 0; j < DH / WV; ++j)
-#pragma unroll
-                for (int e = 0; e < WV; ++e) h = fmaf((float)wr[j][e], s_x[side][WV * j + e], h);
+#pragma unroll 16
+            for (int c = 0; c < DH; ++c) h = fmaf(s_w[row][c], s_x[side][c], h);
             h *= s_inv[side];
             float t;
             if (a.hard) t = h > 0.f ? 1.f : (h < 0.f ? -1.f : 0.f);
@@ -147,16 +276,18 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecodeArgs a) {
         __syncthreads();
 
         // value sums: lane quad cq owns columns 4 cq .. 4 cq + 3 of rows rg, rg + 32, ...
+        // After the last token each row is written back as soon as it is
+        // final, so the stores overlap the read-out's reduction.
+        const bool last = tok == a.T - 1;
         {
             const f32x4 vq = {s_x[2][4 * cq], s_x[2][4 * cq + 1], s_x[2][4 * cq + 2], s_x[2][4 * cq + 3]};
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < DEC_MAXF / DEC_RG; ++i) {
-                if (i < nrow) {
-                    const int f = rg + DEC_RG * i;
-                    s[i] += s_phi[1][f] * vq;
-                    acc += s_phi[0][f] * s[i];
-                }
+            for (int i = 0; i < NR; ++i) {
+                const int f = rg + DEC_RG * i;
+                s[i] += s_phi[1][f] * vq;
+                if (last) *reinterpret_cast<f32x4*>(st + (size_t)f * DH + 4 * cq) = s[i];
+                acc += s_phi[0][f] * s[i];
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) s_num[rg][4 * cq + j] = acc[j];
@@ -168,7 +299,9 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecodeArgs a) {
         {
             double den = 0.0;
             if (tid < F) {
-                z += s_phi[1][tid];
+                const float pk = s_phi[1][tid];
+                z += pk;
+                if (last) st[(size_t)F * DH + tid] = z;
                 den = (double)s_phi[0][tid] * (double)z;
             }
 #pragma unroll
@@ -188,11 +321,6 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecodeArgs a) {
         }
     }
 
-    // write the state back once
-#pragma unroll
-    for (int i = 0; i < DEC_MAXF / DEC_RG; ++i)
-        if (i < nrow) *reinterpret_cast<f32x4*>(st + (size_t)(rg + DEC_RG * i) * DH + 4 * cq) = s[i];
-    if (tid < F) st[(size_t)F * DH + tid] = z;
 }
 
 }  // namespace race

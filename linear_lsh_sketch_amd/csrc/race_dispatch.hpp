@@ -184,7 +184,9 @@ race_status_t run(const Shape& s, const Derived& d, const WsLayout& wl, const Ca
         a.beta = c.beta; a.hard = c.hard;
         static_assert(C::F <= DEC_MAXF && C::F % DEC_RG == 0, "decode tiling");
         profile_mark("decode", st);
-        hipLaunchKernelGGL(k_decode<C::F32>, dim3((unsigned)d.BH), dim3(DEC_NT), 0, st, a);
+        constexpr int NR = C::F / DEC_RG;   // state rows per thread
+        if (a.T == 1) hipLaunchKernelGGL((k_decode_one<C::F32, NR>), dim3((unsigned)d.BH), dim3(DEC_NT), 0, st, a);
+        else hipLaunchKernelGGL((k_decode_multi<C::F32, NR>), dim3((unsigned)d.BH), dim3(DEC_NT), 0, st, a);
         return launch_ok();
     }
 
