@@ -64,7 +64,6 @@ template <bool F32, int NR>
 __global__ __launch_bounds__(DEC_NT) void k_decode_one(DecodeArgs a) {
     using elem = typename Prec<F32>::elem;
     __shared__ float s_x[3][DH];             // q, k, v of this head
-    __shared__ float s_inv[2];               // 1 / max(|q|, eps), 1 / max(|k|, eps)
     __shared__ float s_t[2][128];            // t_p of each table plane, [q | k][l * P + p]
     __shared__ float s_phi[2][DEC_MAXF];     // features of q and of k
     __shared__ float s_num[DEC_RG][DH + 4];  // partial read-outs per row group
@@ -101,23 +100,20 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_one(DecodeArgs a) {
         s_x[which][c] = (float)reinterpret_cast<const elem*>(src)[bh * DH + c];
     }
     __syncthreads();
-    if (wv < 2) {
-        const float x = s_x[wv][lane];
-        float ss = x * x;
-#pragma unroll
-        for (int m = 1; m < 64; m <<= 1) ss += __shfl_xor(ss, m);
-        if (lane == 0) s_inv[wv] = 1.f / fmaxf(sqrtf(ss), NORM_EPS);
-    }
-    __syncthreads();
 
-    // projections
+    // projections; each projection thread also sums its row's squares (the
+    // same order in both decode kernels, so they agree bit for bit)
     if (tid < 2 * LP) {
-        float h = 0.f;
+        float h = 0.f, ss = 0.f;
 #pragma unroll
         for (int j = 0; j < DH / WV; ++j)
 #pragma unroll
-            for (int e = 0; e < WV; ++e) h = fmaf((float)wr[j][e], s_x[side][WV * j + e], h);
-        h *= s_inv[side];
+            for (int e = 0; e < WV; ++e) {
+                const float x = s_x[side][WV * j + e];
+                h = fmaf((float)wr[j][e], x, h);
+                ss = fmaf(x, x, ss);
+            }
+        h *= 1.f / fmaxf(sqrtf(ss), NORM_EPS);
         float t;
         if (a.hard) t = h > 0.f ? 1.f : (h < 0.f ? -1.f : 0.f);
         else t = tanhf(a.beta * tanhf(h));
@@ -196,7 +192,6 @@ template <bool F32, int NR>
 __global__ __launch_bounds__(DEC_NT) void k_decode_multi(DecodeArgs a) {
     using elem = typename Prec<F32>::elem;
     __shared__ float s_x[3][DH];             // q, k, v of the current token
-    __shared__ float s_inv[2];               // 1 / max(|q|, eps), 1 / max(|k|, eps)
     __shared__ float s_t[2][128];            // t_p of each table plane, [q | k][l * P + p]
     __shared__ float s_phi[2][DEC_MAXF];     // features of q and of k
     __shared__ float s_num[DEC_RG][DH + 4];  // partial read-outs per row group
@@ -224,31 +219,28 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_multi(DecodeArgs a) {
     // element of the next token while the current one is processed
     const int which = tid / DH, col = tid % DH;
     const elem* src = reinterpret_cast<const elem*>(which == 0 ? a.q : which == 1 ? a.k : a.v);
-    float nx = tid < 3 * DH ? (float)src[bh * a.T * DH + col] : 0.f;
+    const int64_t r0 = bh * a.T;   // first row of this head's q, k, v, o
+    float nx = 0.f;
+    if (tid < 3 * DH) {
+        s_x[which][col] = (float)src[r0 * DH + col];
+        if (a.T > 1) nx = (float)src[(r0 + 1) * DH + col];
+    }
+    __syncthreads();
 
+    // Four barriers per token: projections | features | update and read-out
+    // | output and the next token's rows (nothing reads s_x in that phase).
     for (int tok = 0; tok < a.T; ++tok) {
-        const int64_t r = bh * a.T + tok;   // row of q, k, v, o
-        __syncthreads();   // the previous token's readers of the shared arrays are done
-        if (tid < 3 * DH) {
-            s_x[which][col] = nx;
-            if (tok + 1 < a.T) nx = (float)src[(r + 1) * DH + col];
-        }
-        __syncthreads();
-        if (wv < 2) {
-            const float x = s_x[wv][lane];
-            float ss = x * x;
-#pragma unroll
-            for (int m = 1; m < 64; m <<= 1) ss += __shfl_xor(ss, m);
-            if (lane == 0) s_inv[wv] = 1.f / fmaxf(sqrtf(ss), NORM_EPS);
-        }
-        __syncthreads();
-
-        // projections
+        const int64_t r = r0 + tok;
+        // projections, each thread with its row's norm (as in k_decode_one)
         if (tid < 2 * LP) {
-            float h = 0.f;
+            float h = 0.f, ss = 0.f;
 #pragma unroll 16
-            for (int c = 0; c < DH; ++c) h = fmaf(s_w[row][c], s_x[side][c], h);
-            h *= s_inv[side];
+            for (int c = 0; c < DH; ++c) {
+                const float x = s_x[side][c];
+                h = fmaf(s_w[row][c], x, h);
+                ss = fmaf(x, x, ss);
+            }
+            h *= 1.f / fmaxf(sqrtf(ss), NORM_EPS);
             float t;
             if (a.hard) t = h > 0.f ? 1.f : (h < 0.f ? -1.f : 0.f);
             else t = tanhf(a.beta * tanhf(h));
@@ -319,6 +311,11 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_multi(DecodeArgs a) {
             const float o = (a.hard && den == 0.0) ? 0.f : num / (float)den;
             reinterpret_cast<elem*>(a.o)[r * DH + tid] = (elem)o;
         }
+        if (tid < 3 * DH && tok + 1 < a.T) {
+            s_x[which][col] = nx;
+            if (tok + 2 < a.T) nx = (float)src[(r + 2) * DH + col];
+        }
+        __syncthreads();
     }
 
 }
