@@ -15,7 +15,8 @@ from __future__ import annotations
 
 import torch
 
-from . import WS_BWD, WS_FWD_SAVED, alloc_saved, alloc_workspace, race_attn_bwd, race_attn_fwd
+from . import (WS_BWD, WS_FWD_SAVED, alloc_saved, alloc_state, alloc_workspace, race_attn_bwd, race_attn_decode,
+               race_attn_fwd, race_attn_prefill)
 
 HEAD_DIM = 64
 
@@ -84,3 +85,36 @@ class RaceMHA(torch.nn.Module):
         q, k, v = self.split(self.wq(x)), self.split(self.wk(x)), self.split(self.wv(x))
         o = race_attention(q, k, v, self.planes, self.P, self.L, self.temperature, self.causal, self.chunk)
         return self.wo(o.transpose(1, 2).reshape(B, N, D))
+
+    # --- incremental decoding (causal blocks, no autograd) -------------------
+    # The running sketch of every head replaces the key-value cache: its size
+    # does not grow with the sequence.
+
+    @torch.no_grad()
+    def prefill(self, x):
+        """Causal outputs of a prompt x [B, N, d_model] and the running state
+        after it (pass the state to ``step``)."""
+        if not self.causal:
+            raise ValueError("incremental decoding needs a causal block")
+        B, N, D = x.shape
+        q, k, v = self.split(self.wq(x)), self.split(self.wk(x)), self.split(self.wv(x))
+        o = race_attn_fwd(q, k, v, self.planes, self.P, self.L, self.temperature, True, self.chunk)
+        state = race_attn_prefill(k, v, self.planes, self.P, self.L, self.temperature, self.chunk)
+        return self.wo(o.transpose(1, 2).reshape(B, N, D)), state
+
+    @torch.no_grad()
+    def empty_state(self, batch: int):
+        """The running state of sequences with no tokens yet."""
+        return alloc_state(batch, self.heads, self.P, self.L, self.planes.device)
+
+    @torch.no_grad()
+    def step(self, x, state):
+        """Outputs of T new tokens x [B, T, d_model] that continue the
+        sequences of `state` (updated in place), each attending causally to
+        everything before it and to itself."""
+        if not self.causal:
+            raise ValueError("incremental decoding needs a causal block")
+        B, T, D = x.shape
+        q, k, v = self.split(self.wq(x)), self.split(self.wk(x)), self.split(self.wv(x))
+        o = race_attn_decode(q, k, v, self.planes, state, self.P, self.L, self.temperature)
+        return self.wo(o.transpose(1, 2).reshape(B, T, D))

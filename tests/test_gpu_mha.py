@@ -1,7 +1,9 @@
 """The RACE multi-head attention block (linear_lsh_sketch_amd.mha) on the GPU:
 its gradients against a float64 CPU reference whose attention core is the
-oracle, and a synthetic language-model loss that can only fall if attention
-carries information from the first token to every later one.
+oracle, a synthetic language-model loss that can only fall if attention
+carries information from the first token to every later one, and
+incremental decoding (prompt, then a few tokens at a time) against the full
+forward.
 """
 import math
 
@@ -127,3 +129,32 @@ def test_mha_language_model_loss_falls(mha, dtype):
     first, last = np.mean(losses[:5]), np.mean(losses[-10:])
     print(f"   loss {first:.3f} -> {last:.3f} (ln 8 = {math.log(8):.3f})", flush=True)
     assert last < 0.3 * math.log(8), (first, last)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mha_incremental_decoding_matches_full_forward(mha, dtype):
+    """Generation with the block: a prompt through ``prefill``, then pieces of
+    1, 3 and 1 tokens through ``step``, give the rows of the full causal
+    forward of the whole sequence (the sketch stands in for the key-value
+    cache)."""
+    import torch
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    dev = torch.device("cuda:0")
+    B, n0, D = 2, 300, 128
+    torch.manual_seed(11)
+    blk = mha.RaceMHA(D, 4, 16, 1.0, True, 64, seed=2, device=dev, dtype=dt)
+    x = torch.randn(B, n0 + 5, D, device=dev).to(dt)
+    with torch.no_grad():
+        full = blk(x).float()
+    out0, state = blk.prefill(x[:, :n0])
+    pieces = [out0.float()]
+    pos = n0
+    for T in (1, 3, 1):
+        pieces.append(blk.step(x[:, pos:pos + T].contiguous(), state).float())
+        pos += T
+    got = torch.cat(pieces, dim=1)
+    torch.cuda.synchronize()
+    err = float((got - full).norm() / full.norm())
+    print(f"[case] mha incremental {dtype}: rel_l2 {err:.1e}", flush=True)
+    assert err <= (1e-5 if dtype == "f32" else 1e-2), err
+    assert torch.equal(blk.empty_state(B), torch.zeros_like(state))
