@@ -67,17 +67,23 @@ def per_token_head_counts(w):
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
+# Sources that decide what the kernels and their launches do (the C-ABI
+# front end, race_abi.hip, only validates arguments and is left out).
+KERNEL_SOURCES = ("race_device.hpp", "race_kernels.hpp", "race_decode.hpp", "race_dispatch.hpp",
+                  "race_host.hpp", "race_bf16.hip", "race_f32.hip")
+
+
 def source_digest() -> str:
-    """sha256 over the kernel sources and the C header: identifies the build
-    that HBM byte counters were taken on."""
+    """sha256 over the kernel sources: identifies the build that HBM byte
+    counters were taken on."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_lsh_sketch_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
+        if name not in KERNEL_SOURCES:
+            continue
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
-    with open(os.path.join(ROOT, "include", "race_attn.h"), "rb") as f:
-        h.update(f.read())
     return h.hexdigest()
 
 
@@ -162,15 +168,31 @@ def cpu_baseline(w, n_sample: int):
         host[name] = arr
     W = synth.normal(w.seed, synth.TID_W, (w.L, w.P, w.d), w.dtype)
     W64 = synth.bf16_bits_to_f64(W) if w.dtype == "bf16" else W.astype(np.float64)
-    threads = min(w.B * w.H, len(os.sched_getaffinity(0)))
-    os.environ.setdefault("OMP_NUM_THREADS", str(threads))
+    affinity = len(os.sched_getaffinity(0))
+    omp_env = os.environ.get("OMP_NUM_THREADS")
+    # the oracle runs one thread per (batch, head) sequence, at most the
+    # OpenMP thread count the environment allows
+    limit = affinity if omp_env is None else max(1, min(affinity, int(omp_env)))
+    threads = min(w.B * w.H, limit)
     t0 = time.perf_counter()
     oracle.forward(host["Q"], host["K"], host["V"], W64, w.beta, w.causal)
     oracle.backward(host["Q"], host["K"], host["V"], W64, host["dO"], w.beta, w.causal)
     dt = time.perf_counter() - t0
     return {"value": w.B * n_sample / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n_sample} tokens of each of the {w.B * w.H} (batch, head) sequences, "
-                      f"causal fwd+bwd in float64, {dt:.1f} s"}
+                      f"causal fwd+bwd in float64, {dt:.1f} s",
+            "affinity_cpus": affinity, "omp_num_threads": omp_env, "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # (heads, tokens per head and call): the long-context workload's 4 heads; 512
@@ -345,6 +367,7 @@ def main():
         roof = {"bound": "mfma", "achieved": kf * units / (avg_ms / 1e3) / 1e12, "peak": peak_f / 1e12,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["scope"] = "dominant kernel, one launch (the whole layer step: layer_roofline)"
     roof["traffic"] = measured_traffic(w.name, dom)
     roof["kernel"] = dom
     roof["kernel_avg_ms"] = avg_ms

@@ -32,9 +32,11 @@
  *
  * Conventions for every entry point
  *   - Tensor pointers are DEVICE pointers unless stated otherwise; the caller
- *     owns all memory; the library allocates nothing and keeps no mutable
- *     global state (thread-safe; concurrent calls on different streams with
- *     different buffers are independent).
+ *     owns all memory; the library allocates nothing. Its only mutable
+ *     global state is the calling thread's profiling hook
+ *     (race_attn_profile_events, thread-local); every entry point is
+ *     thread-safe (concurrent calls on different streams with different
+ *     buffers are independent).
  *   - Q, K, V, O, dO, dQ, dK, dV: [B, H, N, d] contiguous row-major, element
  *     type `dtype`. W: [L, P, d] contiguous, element type `dtype`, shared by
  *     queries, keys, batches and heads; it is a fixed random projection and

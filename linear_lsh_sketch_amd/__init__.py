@@ -127,6 +127,25 @@ def _check_inputs(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+def _check_like(t, ref, name):
+    """An output tensor must match its input in shape, dtype and device, and be contiguous."""
+    if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ref.dtype} tensor of shape {tuple(ref.shape)} "
+                         f"on {ref.device}")
+
+
+def _check_buf(t, nbytes, device, name):
+    """A byte buffer (workspace, saved): contiguous, on the inputs' GPU, at least nbytes long."""
+    if not t.is_contiguous() or t.device != device:
+        raise ValueError(f"{name} must be a contiguous tensor on {device}")
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, {nbytes} needed")
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
 def alloc_workspace(B, H, N, P, L, causal, chunk, kind, device):
     import torch
     n = workspace_bytes(B, H, N, 64, P, L, causal, chunk, kind)
@@ -149,12 +168,18 @@ def race_attn_fwd(Q, K, V, W, P, L, temperature=1.0, causal=False, chunk=1024, o
         raise ValueError(f"W must be [L, P, d] = {(L, P, d)}, got {tuple(W.shape)}")
     if K.shape != Q.shape or V.shape != Q.shape:
         raise ValueError("Q, K, V must share one shape")
+    if out is not None:
+        _check_like(out, Q, "out")
     O = out if out is not None else torch.empty_like(Q)
+    kind = WS_FWD_SAVED if saved is not None else WS_FWD
+    if saved is not None:
+        _check_buf(saved, saved_bytes(B, H, N, d, P, L, causal, chunk), Q.device, "saved")
     if ws is None:
-        ws = alloc_workspace(B, H, N, P, L, causal, chunk, WS_FWD_SAVED if saved is not None else WS_FWD, Q.device)
+        ws = alloc_workspace(B, H, N, P, L, causal, chunk, kind, Q.device)
+    _check_buf(ws, workspace_bytes(B, H, N, d, P, L, causal, chunk, kind), Q.device, "ws")
     code = lib().race_attn_fwd(_p(Q), _p(K), _p(V), _p(W), B, H, N, d, P, L, float(temperature),
                                int(bool(causal)), chunk, _dtype_code(Q), _p(O), _p(saved), _p(ws),
-                               ws.numel(), _stream(stream))
+                               _nbytes(ws), _stream(stream))
     _check(code, "race_attn_fwd")
     return O
 
@@ -175,15 +200,22 @@ def race_attn_bwd(Q, K, V, W, dO, P, L, temperature=1.0, causal=False, chunk=102
         _check_inputs(Q, O)
         if O.shape != Q.shape:
             raise ValueError("O must have the shape of Q")
+    if dO.shape != Q.shape:
+        raise ValueError("dO must have the shape of Q")
+    if saved is not None:
+        _check_buf(saved, saved_bytes(B, H, N, d, P, L, causal, chunk), Q.device, "saved")
     if grads is None:
         grads = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V))
     dQ, dK, dV = grads
+    for t, nm in ((dQ, "dQ"), (dK, "dK"), (dV, "dV")):
+        _check_like(t, Q, nm)
+    kind = WS_BWD if saved is not None else WS_BWD_RECOMPUTE
     if ws is None:
-        ws = alloc_workspace(B, H, N, P, L, causal, chunk, WS_BWD if saved is not None else WS_BWD_RECOMPUTE,
-                             Q.device)
+        ws = alloc_workspace(B, H, N, P, L, causal, chunk, kind, Q.device)
+    _check_buf(ws, workspace_bytes(B, H, N, d, P, L, causal, chunk, kind), Q.device, "ws")
     code = lib().race_attn_bwd(_p(Q), _p(K), _p(V), _p(W), _p(O), _p(dO), _p(saved), B, H, N, d, P, L,
                                float(temperature), int(bool(causal)), chunk, _dtype_code(Q), _p(dQ),
-                               _p(dK), _p(dV), _p(ws), ws.numel(), _stream(stream))
+                               _p(dK), _p(dV), _p(ws), _nbytes(ws), _stream(stream))
     _check(code, "race_attn_bwd")
     return dQ, dK, dV
 
@@ -193,6 +225,8 @@ def race_attn_hash(X, W, P, L, stream=None):
     import torch
     _check_inputs(X, W)
     B, H, N, d = X.shape
+    if tuple(W.shape) != (L, P, d):
+        raise ValueError(f"W must be [L, P, d] = {(L, P, d)}, got {tuple(W.shape)}")
     ids = torch.empty((B, H, N, L), dtype=torch.int32, device=X.device)
     nz = torch.zeros(1, dtype=torch.int64, device=X.device)
     code = lib().race_attn_hash(_p(X), _p(W), B, H, N, d, P, L, _dtype_code(X), _p(ids), _p(nz),
@@ -228,8 +262,9 @@ def race_attn_prefill(K, V, W, P, L, temperature=1.0, chunk=1024, state=None, ws
     _check_state(state, B, H, P, L, d, K.device)
     if ws is None:
         ws = alloc_workspace(B, H, N, P, L, False, chunk, WS_FWD, K.device)
+    _check_buf(ws, workspace_bytes(B, H, N, d, P, L, False, chunk, WS_FWD), K.device, "ws")
     code = lib().race_attn_prefill(_p(K), _p(V), _p(W), B, H, N, d, P, L, float(temperature), chunk,
-                                   _dtype_code(K), _p(state), _p(ws), ws.numel(), _stream(stream))
+                                   _dtype_code(K), _p(state), _p(ws), _nbytes(ws), _stream(stream))
     _check(code, "race_attn_prefill")
     return state
 

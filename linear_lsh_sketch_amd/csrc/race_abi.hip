@@ -7,6 +7,12 @@
 #include "race_attn.h"
 #include "race_dispatch.hpp"
 
+namespace race {
+// the launch sequences are compiled once, in their own translation units
+extern template race_status_t dispatch<true>(const Shape&, const Derived&, const WsLayout&, const Call&);
+extern template race_status_t dispatch<false>(const Shape&, const Derived&, const WsLayout&, const Call&);
+}  // namespace race
+
 using namespace race;
 
 namespace {

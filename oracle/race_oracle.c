@@ -281,6 +281,9 @@ int oracle_backward(const void *Q, const void *K, const void *V, const void *dO,
         /* pass 2, reverse order (causal) or any order (non-causal): key side */
         int64_t prev = n_sample - 1;
         for (int64_t j = N - 1; j >= 0; --j) {
+            /* every sampled row is written: the earlier tokens change nothing
+               that is returned */
+            if (sample && prev < 0) break;
             if (causal) {
                 soft_bucket(&c, Q, in_dtype, base + j, sb);
                 for (int k = 0; k < d; ++k)

@@ -212,3 +212,23 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         race.lib()
     with pytest.raises(RuntimeError, match="not built"):
         race.workspace_bytes(1, 1, 10, 64, 4, 8, True, 16, race.WS_FWD)
+
+
+def test_binding_buffer_checks_on_host_tensors():
+    """The binding's output and buffer checks (shape, dtype, device,
+    contiguity, byte size) that every entry point runs before the C call."""
+    import torch
+    ref = torch.zeros((1, 2, 8, 64), dtype=torch.bfloat16)
+    race._check_like(torch.zeros_like(ref), ref, "out")
+    for bad in (torch.zeros((1, 2, 8, 64), dtype=torch.float32),     # twice the bytes per element
+                torch.zeros((1, 2, 9, 64), dtype=torch.bfloat16),
+                torch.zeros((1, 2, 64, 8), dtype=torch.bfloat16).transpose(2, 3)):
+        with pytest.raises(ValueError):
+            race._check_like(bad, ref, "out")
+    buf = torch.zeros(100, dtype=torch.float32)          # 400 bytes
+    race._check_buf(buf, 400, buf.device, "ws")
+    with pytest.raises(ValueError):
+        race._check_buf(buf, 401, buf.device, "ws")
+    with pytest.raises(ValueError):
+        race._check_buf(buf[::2], 10, buf.device, "ws")
+    assert race._nbytes(buf) == 400

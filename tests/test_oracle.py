@@ -454,6 +454,33 @@ def test_stream_dtypes_and_sampling():
         np.testing.assert_allclose(O[1], ref0, rtol=1e-12, atol=1e-13)
 
 
+def test_stream_sampled_backward_equals_unsampled_rows():
+    """The sampled backward (rows written on the way, reverse slot mapping
+    for the key side, early stop once every sampled row is out) returns
+    exactly the sampled rows of the full backward, first and last tokens
+    included, in both modes; also with dO zero outside a late window, the
+    case the full-size goldens use."""
+    N, d, P, L = 97, 16, 3, 4
+    Qb = synth.normal(7, 1, (2, N, d), "bf16")
+    Kb = synth.normal(7, 2, (2, N, d), "bf16")
+    Vb = synth.normal(7, 3, (2, N, d), "bf16")
+    dOb = synth.normal(7, 4, (2, N, d), "bf16")
+    W = synth.bf16_bits_to_f64(synth.normal(7, 0, (L, P, d), "bf16"))
+    dO_late = dOb.copy()
+    dO_late[:, : N - 20] = 0
+    for dO in (dOb, dO_late):
+        for causal in (False, True):
+            full = stream.backward(Qb, Kb, Vb, W, dO, 1.3, causal)
+            for smp in (np.array([0, 1, 50, 95, 96]), np.array([96]), np.array([0]),
+                        np.arange(N - 20, N, 3)):
+                got = stream.backward(Qb, Kb, Vb, W, dO, 1.3, causal, sample=smp)
+                for g, f in zip(got, full):
+                    np.testing.assert_array_equal(g, f[:, smp])
+    # the late window: rows before it have zero query-side gradient
+    dQ, dK, dV = stream.backward(Qb, Kb, Vb, W, dO_late, 1.3, True)
+    assert not dQ[:, : N - 20].any() and dK[:, : N - 20].any()
+
+
 # --------------------------------------------------------------------------
 # input generator
 # --------------------------------------------------------------------------
