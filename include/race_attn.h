@@ -34,9 +34,11 @@
  *   - Tensor pointers are DEVICE pointers unless stated otherwise; the caller
  *     owns all memory; the library allocates nothing. Its only mutable
  *     global state is the calling thread's profiling hook
- *     (race_attn_profile_events, thread-local); every entry point is
- *     thread-safe (concurrent calls on different streams with different
- *     buffers are independent).
+ *     (race_attn_profile_events, thread-local) and, for
+ *     race_attn_fwd_noalloc, its fixed per-GPU scratch array and the cached
+ *     device address of it; every other entry point is thread-safe
+ *     (concurrent calls on different streams with different buffers are
+ *     independent).
  *   - Q, K, V, O, dO, dQ, dK, dV: [B, H, N, d] contiguous row-major, element
  *     type `dtype`. W: [L, P, d] contiguous, element type `dtype`, shared by
  *     queries, keys, batches and heads; it is a fixed random projection and
@@ -121,6 +123,24 @@ race_status_t race_attn_fwd(const void *Q, const void *K, const void *V, const v
                             int64_t B, int64_t H, int64_t N, int d, int P, int L,
                             float temperature, int causal, int chunk, race_dtype_t dtype,
                             void *O, void *saved, void *ws, size_t ws_bytes, void *stream);
+
+/* Allocation-free forward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): race_attn_fwd with the same arguments minus `ws`; its workspace
+ * is a fixed device array inside the library, RACE_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) on each GPU it runs on, held until the process ends. A shape whose
+ * workspace (race_attn_workspace_bytes, for_backward = 0, or 3 when `saved` is
+ * given) exceeds it returns RACE_ERR_WORKSPACE before any device work. The
+ * call allocates nothing (no hipMalloc, no allocating library routine). Every
+ * call on one GPU uses that GPU's one array and leaves its last contents
+ * there (the forward writes every workspace byte it reads, so no clearing is
+ * needed): calls that overlap on one GPU (other streams, other host threads)
+ * race and must be serialised by the caller. */
+#define RACE_NOALLOC_SCRATCH_BYTES (64u << 20)
+race_status_t race_attn_fwd_noalloc(const void *Q, const void *K, const void *V, const void *W,
+                                    int64_t B, int64_t H, int64_t N, int d, int P, int L,
+                                    float temperature, int causal, int chunk, race_dtype_t dtype,
+                                    void *O, void *saved, void *stream);
 
 /* Backward: given dO = dLoss/dO, writes dQ, dK, dV (the exact gradients of
  * the forward above; the pages train the layer end to end, Japanese

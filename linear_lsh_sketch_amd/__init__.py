@@ -17,7 +17,7 @@ RACE_OK, RACE_ERR_INVALID_ARG, RACE_ERR_UNSUPPORTED, RACE_ERR_WORKSPACE, RACE_ER
 RACE_F32, RACE_BF16 = 0, 1
 
 SYMBOLS = ("race_attn_workspace_bytes", "race_attn_saved_bytes", "race_attn_fwd",
-           "race_attn_bwd", "race_attn_hash", "race_attn_state_bytes", "race_attn_prefill",
+           "race_attn_fwd_noalloc", "race_attn_bwd", "race_attn_hash", "race_attn_state_bytes", "race_attn_prefill",
            "race_attn_decode", "race_attn_profile_events", "race_attn_profile_count",
            "race_attn_profile_stage", "race_attn_status_string")
 
@@ -45,6 +45,8 @@ def lib():
         L.race_attn_saved_bytes.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
         L.race_attn_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, fl, i32, i32, i32,
                                     vp, vp, vp, sz, vp]
+        L.race_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, fl, i32, i32,
+                                            i32, vp, vp, vp]
         L.race_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, fl, i32, i32,
                                     i32, vp, vp, vp, vp, sz, vp]
         L.race_attn_hash.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, i32, vp, vp, vp]
@@ -59,7 +61,7 @@ def lib():
         L.race_attn_status_string.argtypes = [i32]
         L.race_attn_status_string.restype = ctypes.c_char_p
         for name in ("race_attn_workspace_bytes", "race_attn_saved_bytes", "race_attn_fwd",
-                     "race_attn_bwd", "race_attn_hash", "race_attn_state_bytes", "race_attn_prefill",
+                     "race_attn_fwd_noalloc", "race_attn_bwd", "race_attn_hash", "race_attn_state_bytes", "race_attn_prefill",
                      "race_attn_decode", "race_attn_profile_events", "race_attn_profile_count"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -182,6 +184,31 @@ def race_attn_fwd(Q, K, V, W, P, L, temperature=1.0, causal=False, chunk=1024, o
                                _nbytes(ws), _stream(stream))
     _check(code, "race_attn_fwd")
     return O
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def race_attn_fwd_noalloc(Q, K, V, W, P, L, temperature=1.0, causal=False, chunk=1024, *, out,
+                          saved=None, stream=None):
+    """race_attn_fwd without a workspace argument: the library's fixed
+    per-GPU scratch array (NOALLOC_SCRATCH_BYTES) serves as the workspace, and
+    the call allocates nothing, so `out` (and `saved`, if wanted) are given by
+    the caller. Calls that overlap on one GPU share that array and race."""
+    _check_inputs(Q, K, V, W)
+    B, H, N, d = Q.shape
+    if tuple(W.shape) != (L, P, d):
+        raise ValueError(f"W must be [L, P, d] = {(L, P, d)}, got {tuple(W.shape)}")
+    if K.shape != Q.shape or V.shape != Q.shape:
+        raise ValueError("Q, K, V must share one shape")
+    _check_like(out, Q, "out")
+    if saved is not None:
+        _check_buf(saved, saved_bytes(B, H, N, d, P, L, causal, chunk), Q.device, "saved")
+    code = lib().race_attn_fwd_noalloc(_p(Q), _p(K), _p(V), _p(W), B, H, N, d, P, L, float(temperature),
+                                       int(bool(causal)), chunk, _dtype_code(Q), _p(out), _p(saved),
+                                       _stream(stream))
+    _check(code, "race_attn_fwd_noalloc")
+    return out
 
 
 def race_attn_bwd(Q, K, V, W, dO, P, L, temperature=1.0, causal=False, chunk=1024, O=None, saved=None,
@@ -349,6 +376,7 @@ class StageTimer:
 
 # short aliases
 forward = race_attn_fwd
+forward_noalloc = race_attn_fwd_noalloc
 backward = race_attn_bwd
 hard_hash = race_attn_hash
 prefill = race_attn_prefill

@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdint>
 #include <initializer_list>
+#include <mutex>
 
 #include "race_attn.h"
 #include "race_dispatch.hpp"
@@ -15,7 +16,32 @@ extern template race_status_t dispatch<false>(const Shape&, const Derived&, cons
 
 using namespace race;
 
+// Device scratch of the allocation-free forward (race_attn_fwd_noalloc): a
+// fixed array in the library's code object, one copy per GPU, held until the
+// process ends. Host code never uses its name as an address: the device
+// address of each GPU's copy comes from hipGetSymbolAddress (scratch_base).
+static __device__ __align__(256) unsigned char scratch[RACE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+// Device address of `scratch` on each GPU, looked up once per device with the
+// device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+race_status_t scratch_base(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return RACE_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return RACE_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return RACE_OK;
+}
 
 // Per-thread profiling state (race_attn_profile_events). Only the calling
 // thread's own calls read or write it, so concurrent callers do not interact.
@@ -122,6 +148,30 @@ race_status_t race_attn_fwd(const void* Q, const void* K, const void* V, const v
     if (rc != RACE_OK) return rc;
     const WsLayout wl = ws_layout(s, dv, saved ? WS_FWD_SAVED : WS_FWD);
     if (ws_bytes < wl.total) return RACE_ERR_WORKSPACE;
+    Call c{};
+    c.op = OP_FWD; c.Q = Q; c.K = K; c.V = V; c.W = W; c.saved_out = saved; c.beta = temperature; c.O = O;
+    c.hard = hard;
+    c.ws = ws; c.stream = reinterpret_cast<hipStream_t>(stream);
+    return go(dtype, s, dv, wl, c);
+}
+
+race_status_t race_attn_fwd_noalloc(const void* Q, const void* K, const void* V, const void* W, int64_t B,
+                                    int64_t H, int64_t N, int d, int P, int L, float temperature, int causal,
+                                    int chunk, race_dtype_t dtype, void* O, void* saved, void* stream) {
+    if (!Q || !K || !V || !W || !O || !dtype_ok(dtype) || std::isnan(temperature) ||
+        temperature == -INFINITY || !all_aligned({Q, K, V, W, O, saved}))
+        return RACE_ERR_INVALID_ARG;
+    const bool hard = std::isinf(temperature);
+    if (hard && dtype != RACE_F32) return RACE_ERR_UNSUPPORTED;
+    Shape s;
+    Derived dv;
+    race_status_t rc = prepare(B, H, N, d, P, L, causal, chunk, s, dv);
+    if (rc != RACE_OK) return rc;
+    const WsLayout wl = ws_layout(s, dv, saved ? WS_FWD_SAVED : WS_FWD);
+    if (wl.total > (size_t)RACE_NOALLOC_SCRATCH_BYTES) return RACE_ERR_WORKSPACE;
+    void* ws = nullptr;
+    rc = scratch_base(&ws);
+    if (rc != RACE_OK) return rc;
     Call c{};
     c.op = OP_FWD; c.Q = Q; c.K = K; c.V = V; c.W = W; c.saved_out = saved; c.beta = temperature; c.O = O;
     c.hard = hard;
