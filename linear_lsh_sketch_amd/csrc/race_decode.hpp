@@ -34,15 +34,21 @@ namespace race {
 
 constexpr int DEC_NT = 512;      // threads per workgroup (one head)
 constexpr int DEC_RG = DEC_NT / 16;   // row groups: 16 lanes cover one 64-float row
-constexpr int DEC_MAXF = 512;    // largest F (MT = 8, KB = 2)
+constexpr int DEC_MAXF = 512;    // largest F of one table group
 static_assert(DEC_MAXF <= DEC_NT, "one thread per feature and mass");
 
+// The running state of a head holds its table groups one after the other,
+// each in the layout of the sketch kernels' states: [F_g x 64 value sums |
+// F_g masses]. Full groups have F features and Lg tables, the last Fl and
+// L - (G - 1) Lg.
 struct DecodeArgs {
     const void *q, *k, *v, *W;
-    float* state;   // [BH][F * 65]
+    float* state;   // [BH][(G - 1) F * 65 + Fl * 65]
     void* o;        // [BH][T][64]
-    int T;          // new tokens per head, processed in order
+    int T;          // new tokens per head (rows of a head in q, k, v, o), processed in order
+    int tok;        // k_decode_one: the token of this launch (0 <= tok < T)
     int P, L, F, KB, TPT, TPL;
+    int G, Lg, Fl;
     float beta;
     int hard;
 };
@@ -57,9 +63,11 @@ __device__ inline void feature_table_subset(int f, int P, int KB, int TPT, int T
     subset = jj % R;
 }
 
-// T = 1: the state rows are updated and written back as soon as the
-// features are known. NR = F / 32 state rows per thread (a compile-time
-// count, so the registers match the state: 95 at F = 256 in bf16).
+// One token per launch (token a.tok of each head), every table group in
+// turn: the group's state rows are updated and written back as soon as the
+// features are known, and the read-outs of the groups are summed. NR = F / 32
+// state rows per thread of a full group (a compile-time count, so the
+// registers match the state: 95 at F = 256 in bf16).
 template <bool F32, int NR>
 __global__ __launch_bounds__(DEC_NT) void k_decode_one(DecodeArgs a) {
     using elem = typename Prec<F32>::elem;
@@ -71,121 +79,129 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_one(DecodeArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t bh = blockIdx.x;
-    const int F = a.F, LP = a.L * a.P;
-    float* st = a.state + (size_t)bh * (size_t)F * 65;
-
-    // The state rows do not depend on this token: their loads are issued
-    // first, so their latency overlaps the projections and features.
+    const int64_t r = bh * a.T + a.tok;      // row of this token in q, k, v, o
+    const int64_t head_floats = (int64_t)(a.G - 1) * a.F * 65 + (int64_t)a.Fl * 65;
+    float* st_head = a.state + (size_t)bh * (size_t)head_floats;
     const int cq = tid & 15, rg = tid >> 4;
-    f32x4 s[NR];
-#pragma unroll
-    for (int i = 0; i < NR; ++i)
-        s[i] = *reinterpret_cast<const f32x4*>(st + (size_t)(rg + DEC_RG * i) * DH + 4 * cq);
-    const float z_old = tid < F ? st[(size_t)F * DH + tid] : 0.f;
-    // so are the hyperplane rows: thread (side, row), row = l * P + p, holds
-    // all 64 weights of its row, loaded 16 bytes at a time
-    const int side = tid / LP, row = tid % LP;
     constexpr int WV = 16 / sizeof(elem);   // elements per 16-byte load
     typedef elem wvec __attribute__((ext_vector_type(WV)));
-    wvec wr[DH / WV];
-    if (tid < 2 * LP) {
-        const wvec* w = reinterpret_cast<const wvec*>(reinterpret_cast<const elem*>(a.W) + (size_t)row * DH);
-#pragma unroll
-        for (int j = 0; j < DH / WV; ++j) wr[j] = w[j];
-    }
 
     if (tid < 3 * DH) {
         const int which = tid / DH, c = tid % DH;
         const void* src = which == 0 ? a.q : which == 1 ? a.k : a.v;
-        s_x[which][c] = (float)reinterpret_cast<const elem*>(src)[bh * DH + c];
+        s_x[which][c] = (float)reinterpret_cast<const elem*>(src)[r * DH + c];
     }
-    __syncthreads();
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};   // read-out of columns 4 cq .. +3 over this thread's rows
+    double den = 0.0;                   // and over its masses
 
-    // projections; each projection thread also sums its row's squares (the
-    // same order in both decode kernels, so they agree bit for bit)
-    if (tid < 2 * LP) {
-        float h = 0.f, ss = 0.f;
+    for (int gi = 0; gi < a.G; ++gi) {
+        const bool lastg = gi == a.G - 1;
+        const int F = lastg ? a.Fl : a.F;
+        const int Lgr = lastg ? a.L - (a.G - 1) * a.Lg : a.Lg;
+        const int LP = Lgr * a.P;
+        float* st = st_head + (size_t)gi * (size_t)a.F * 65;
+        // The state rows do not depend on this token: their loads are issued
+        // first, so their latency overlaps the projections and features.
+        f32x4 s[NR];
 #pragma unroll
-        for (int j = 0; j < DH / WV; ++j)
+        for (int i = 0; i < NR; ++i)
+            if (rg + DEC_RG * i < F) s[i] = *reinterpret_cast<const f32x4*>(st + (size_t)(rg + DEC_RG * i) * DH + 4 * cq);
+        const float z_old = tid < F ? st[(size_t)F * DH + tid] : 0.f;
+        // so are the hyperplane rows: thread (side, row), row = l * P + p of
+        // the group, holds all 64 weights of its row, loaded 16 bytes at a time
+        const int side = tid / LP, row = tid % LP;
+        wvec wr[DH / WV];
+        if (tid < 2 * LP) {
+            const wvec* w = reinterpret_cast<const wvec*>(reinterpret_cast<const elem*>(a.W) +
+                                                          ((size_t)gi * a.Lg * a.P + row) * DH);
 #pragma unroll
-            for (int e = 0; e < WV; ++e) {
-                const float x = s_x[side][WV * j + e];
-                h = fmaf((float)wr[j][e], x, h);
-                ss = fmaf(x, x, ss);
-            }
-        h *= 1.f / fmaxf(sqrtf(ss), NORM_EPS);
-        float t;
-        if (a.hard) t = h > 0.f ? 1.f : (h < 0.f ? -1.f : 0.f);
-        else t = tanhf(a.beta * tanhf(h));
-        s_t[side][row] = t;
-    }
-    __syncthreads();
+            for (int j = 0; j < DH / WV; ++j) wr[j] = w[j];
+        }
+        __syncthreads();   // s_x is written; the previous group's s_t and s_phi are read
 
-    if (tid < F) {
-        const int f = tid;
-        int table, subset;
-        feature_table_subset(f, a.P, a.KB, a.TPT, a.TPL, table, subset);
-        float pq = 0.f, pk = subset == 0 ? 1.f : 0.f;   // padded table
-        if (table < a.L) {
-            pq = 1.f;
-            pk = 1.f;
-            for (int p = 0; p < a.P; ++p)
-                if ((subset >> p) & 1) {
-                    pq *= s_t[0][table * a.P + p];
-                    pk *= s_t[1][table * a.P + p];
+        // projections; each projection thread also sums its row's squares (the
+        // same order in both decode kernels, so they agree bit for bit)
+        if (tid < 2 * LP) {
+            float h = 0.f, ss = 0.f;
+#pragma unroll
+            for (int j = 0; j < DH / WV; ++j)
+#pragma unroll
+                for (int e = 0; e < WV; ++e) {
+                    const float x = s_x[side][WV * j + e];
+                    h = fmaf((float)wr[j][e], x, h);
+                    ss = fmaf(x, x, ss);
                 }
+            h *= 1.f / fmaxf(sqrtf(ss), NORM_EPS);
+            float t;
+            if (a.hard) t = h > 0.f ? 1.f : (h < 0.f ? -1.f : 0.f);
+            else t = tanhf(a.beta * tanhf(h));
+            s_t[side][row] = t;
         }
-        s_phi[0][f] = pq;
-        s_phi[1][f] = pk;
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // value sums: lane quad cq owns columns 4 cq .. 4 cq + 3 of rows rg, rg + 32, ...
-    {
-        const f32x4 vq = {s_x[2][4 * cq], s_x[2][4 * cq + 1], s_x[2][4 * cq + 2], s_x[2][4 * cq + 3]};
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < NR; ++i) {
-            const int f = rg + DEC_RG * i;
-            const float pk = s_phi[1][f], pq = s_phi[0][f];
-            s[i] += pk * vq;
-            if (pk != 0.f) *reinterpret_cast<f32x4*>(st + (size_t)f * DH + 4 * cq) = s[i];
-            acc += pq * s[i];
+        if (tid < F) {
+            const int f = tid;
+            int table, subset;
+            feature_table_subset(f, a.P, a.KB, a.TPT, a.TPL, table, subset);
+            float pq = 0.f, pk = subset == 0 ? 1.f : 0.f;   // padded table
+            if (table < Lgr) {
+                pq = 1.f;
+                pk = 1.f;
+                for (int p = 0; p < a.P; ++p)
+                    if ((subset >> p) & 1) {
+                        pq *= s_t[0][table * a.P + p];
+                        pk *= s_t[1][table * a.P + p];
+                    }
+            }
+            s_phi[0][f] = pq;
+            s_phi[1][f] = pk;
         }
+        __syncthreads();
+
+        // value sums: lane quad cq owns columns 4 cq .. 4 cq + 3 of rows rg, rg + 32, ...
+        {
+            const f32x4 vq = {s_x[2][4 * cq], s_x[2][4 * cq + 1], s_x[2][4 * cq + 2], s_x[2][4 * cq + 3]};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) s_num[rg][4 * cq + j] = acc[j];
-    }
-    // masses (F <= DEC_NT: one per thread). The denominator is summed in
-    // float64: with hard buckets the features are 0 or +-1 and the masses
-    // integers (exact in float32 below 2^24 keys), so the sum is exact and a
-    // query that collides with no key reads exactly 0.
-    {
-        double den = 0.0;
+            for (int i = 0; i < NR; ++i) {
+                const int f = rg + DEC_RG * i;
+                if (f >= F) continue;
+                const float pk = s_phi[1][f], pq = s_phi[0][f];
+                s[i] += pk * vq;
+                if (pk != 0.f) *reinterpret_cast<f32x4*>(st + (size_t)f * DH + 4 * cq) = s[i];
+                acc += pq * s[i];
+            }
+        }
+        // masses (F <= DEC_NT: one per thread). The denominator is summed in
+        // float64: with hard buckets the features are 0 or +-1 and the masses
+        // integers (exact in float32 below 2^24 keys), so the sum is exact and a
+        // query that collides with no key reads exactly 0.
         if (tid < F) {
             const float pk = s_phi[1][tid];
             const float z = z_old + pk;
             if (pk != 0.f) st[(size_t)F * DH + tid] = z;
-            den = (double)s_phi[0][tid] * (double)z;
+            den += (double)s_phi[0][tid] * (double)z;
         }
-#pragma unroll
-        for (int m = 1; m < 64; m <<= 1) den += __shfl_xor(den, m);
-        if (lane == 0) s_den[wv] = den;
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s_num[rg][4 * cq + j] = acc[j];
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) den += __shfl_xor(den, m);
+    if (lane == 0) s_den[wv] = den;
     __syncthreads();
     if (tid < DH) {
         float num = 0.f;
-        double den = 0.0;
+        double dsum = 0.0;
 #pragma unroll 8
-        for (int r = 0; r < DEC_RG; ++r) num += s_num[r][tid];
+        for (int rr = 0; rr < DEC_RG; ++rr) num += s_num[rr][tid];
 #pragma unroll
-        for (int w = 0; w < DEC_NT / 64; ++w) den += s_den[w];
-        const float o = (a.hard && den == 0.0) ? 0.f : num / (float)den;
-        reinterpret_cast<elem*>(a.o)[bh * DH + tid] = (elem)o;
+        for (int w = 0; w < DEC_NT / 64; ++w) dsum += s_den[w];
+        const float o = (a.hard && dsum == 0.0) ? 0.f : num / (float)dsum;
+        reinterpret_cast<elem*>(a.o)[r * DH + tid] = (elem)o;
     }
 }
 
-// T > 1: the state rows stay in registers across the tokens and are written
-// back during the last token; the hyperplanes sit in LDS and each token's
+// T > 1 with one table group: the state rows stay in registers across the
+// tokens and are written back during the last token; the hyperplanes sit in LDS and each token's
 // q, k, v rows are loaded while the previous token is processed (116
 // registers at F = 256 in bf16: two workgroups per CU).
 template <bool F32, int NR>

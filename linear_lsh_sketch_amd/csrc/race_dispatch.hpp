@@ -3,6 +3,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <functional>
+
 #include "race_decode.hpp"
 #include "race_host.hpp"
 #include "race_kernels.hpp"
@@ -52,38 +54,60 @@ inline race_status_t launch_ok() {
         if (rc_ != RACE_OK) return rc_;      \
     } while (0)
 
+// Compile-time configuration of one table group's launches: fn(Tag<Cfg>{})
+// for the (P, MT) pair (MT = projection tiles of the group).
+template <class C>
+struct Tag {
+    using type = C;
+};
+
+template <bool F32, class Fn>
+race_status_t with_cfg(int P, int MT, Fn&& fn) {
+#define RACE_CFG(P_, MT_) \
+    if (P == P_ && MT == MT_) return fn(Tag<Cfg<P_, MT_, F32>>{});
+    RACE_CFG(1, 1) RACE_CFG(1, 2) RACE_CFG(1, 4) RACE_CFG(1, 8)
+    RACE_CFG(2, 1) RACE_CFG(2, 2) RACE_CFG(2, 4) RACE_CFG(2, 8)
+    RACE_CFG(3, 1) RACE_CFG(3, 2) RACE_CFG(3, 4) RACE_CFG(3, 8)
+    RACE_CFG(4, 1) RACE_CFG(4, 2) RACE_CFG(4, 4)
+#undef RACE_CFG
+    return RACE_ERR_UNSUPPORTED;
+}
+
 // CACHED = false: sketch of K, [V | 1] (storing the keys' plane values in pc);
 // CACHED = true: gradient sketch of the queries from their plane values pc.
 template <class C, bool CACHED>
-race_status_t run_totals(const Shape& s, const Derived& d, const void* Xb, const void* Z, const float* Dv,
-                         const float* Ev, const PlaneCache& pc, const void* W, float beta, float* out,
-                         hipStream_t st) {
+race_status_t run_totals(const Shape& s, const Derived& d, const Group& gr, const void* Xb, const void* Z,
+                         const float* Dv, const float* Ev, const PlaneCache& pc, const void* W, float beta,
+                         float* out, hipStream_t st) {
     TotArgs a;
     a.Xb = Xb; a.Z = Z; a.Dv = Dv; a.Ev = Ev; a.W = W; a.pc = pc; a.out = out;
-    a.N = s.N; a.chunk = s.chunk; a.nchunks = (int)d.NC; a.L = s.L; a.beta = beta;
+    a.N = s.N; a.chunk = s.chunk; a.nchunks = (int)d.NC; a.L = gr.L; a.beta = beta;
     profile_mark(CACHED ? "totals_qg" : "totals_kv", st);
     hipLaunchKernelGGL((k_totals<C, CACHED>), dim3((unsigned)d.NC, (unsigned)d.BH), dim3(NT), 0, st, a);
     return launch_ok();
 }
 
-inline PlaneCache plane_cache(void* base, const CacheLayout& cl) {
+// One side's plane values (table group g) and inverse norms.
+inline PlaneCache plane_cache(void* base, const CacheLayout& cl, int g) {
     char* b = reinterpret_cast<char*>(base);
     PlaneCache p;
-    p.u = b + cl.u;
+    p.u = b + cl.u_of(g);
     p.inv = reinterpret_cast<float*>(b + cl.inv);
     return p;
 }
 
+// Scan of one group's chunk states [BH][NC][F65]; the total of head bh goes
+// to total + bh * total_stride.
 template <int KIND>
-race_status_t run_scan(const Shape& s, const Derived& d, float* states, float* total, float* segbuf,
-                       hipStream_t st) {
-    const int elems = (int)d.F65;
+race_status_t run_scan(const Shape& s, const Derived& d, int64_t F65, float* states, float* total,
+                       int64_t total_stride, float* segbuf, hipStream_t st) {
+    const int elems = (int)F65;
     const unsigned gx = (unsigned)((elems + 255) / 256);
     profile_mark(KIND == SCAN_EXCL ? "scan_excl" : KIND == SCAN_REV_EXCL ? "scan_rev_excl" : "scan_total", st);
-    const int segs = KIND == SCAN_TOTAL ? 1 : scan_segs(s, d);
+    const int segs = KIND == SCAN_TOTAL ? 1 : scan_segs(s, d, F65);
     if (segs == 1) {
         hipLaunchKernelGGL(k_scan<KIND>, dim3(gx, (unsigned)d.BH), dim3(256), 0, st, states, total, (int)d.NC,
-                           elems);
+                           elems, total_stride);
         return launch_ok();
     }
     const dim3 grid(gx, (unsigned)(d.BH * segs));
@@ -93,7 +117,7 @@ race_status_t run_scan(const Shape& s, const Derived& d, float* states, float* t
     return launch_ok();
 }
 
-enum { PASS_FWD = 0, PASS_BWD_Q = 1, PASS_BWD_K = 2 };
+enum { PASS_FWD = 0, PASS_BWD_Q = 1, PASS_BWD_V = 2, PASS_BWD_K = 3 };
 
 // The forward and the query-side backward use feature blocks of two chunks in
 // bf16 (smaller LDS tiles and operand sets, so two workgroups fit on a CU).
@@ -102,150 +126,251 @@ using Blk2Cfg = Cfg<C::P, C::MT, C::F32, C::F32 ? 0 : 2>;
 
 template <class C, int KIND>
 race_status_t run_pass(const Shape& s, const Derived& d, PassArgs a, hipStream_t st) {
-    a.N = s.N; a.chunk = s.chunk; a.L = s.L; a.causal = s.causal;
+    a.N = s.N; a.chunk = s.chunk; a.causal = s.causal;
     const dim3 grid((unsigned)d.NC, (unsigned)d.BH), block(NT);
+    using CB = Blk2Cfg<C>;
     if constexpr (KIND == PASS_FWD) {
         profile_mark("pass_fwd", st);
-        if (s.causal) hipLaunchKernelGGL((k_fwd<Blk2Cfg<C>, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_fwd<Blk2Cfg<C>, false>), grid, block, 0, st, a);
+        if (s.causal) hipLaunchKernelGGL((k_fwd<CB, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_fwd<CB, false>), grid, block, 0, st, a);
     } else if constexpr (KIND == PASS_BWD_Q) {
         profile_mark("pass_bwd_q", st);
-        if (s.causal) hipLaunchKernelGGL((k_bwd_q<Blk2Cfg<C>, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_bwd_q<Blk2Cfg<C>, false>), grid, block, 0, st, a);
-    } else {
-        // key side: dV and dK in two passes of two workgroups per CU each
-        using CK = Blk2Cfg<C>;
+        if (s.causal) hipLaunchKernelGGL((k_bwd_q<CB, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_bwd_q<CB, false>), grid, block, 0, st, a);
+    } else if constexpr (KIND == PASS_BWD_V) {
         profile_mark("pass_bwd_v", st);
-        if (s.causal) hipLaunchKernelGGL((k_bwd_k<CK, true, KPART_DV>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_bwd_k<CK, false, KPART_DV>), grid, block, 0, st, a);
-        RACE_TRY(launch_ok());
+        if (s.causal) hipLaunchKernelGGL((k_bwd_k<CB, true, KPART_DV>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_bwd_k<CB, false, KPART_DV>), grid, block, 0, st, a);
+    } else {
         profile_mark("pass_bwd_k", st);
-        if (s.causal) hipLaunchKernelGGL((k_bwd_k<CK, true, KPART_DK>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_bwd_k<CK, false, KPART_DK>), grid, block, 0, st, a);
+        if (s.causal) hipLaunchKernelGGL((k_bwd_k<CB, true, KPART_DK>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_bwd_k<CB, false, KPART_DK>), grid, block, 0, st, a);
     }
     return launch_ok();
 }
 
+// Launch one pass of every table group in order: group g adds to the partial
+// outputs of the groups before it, the last one finishes the outputs.
+template <bool F32, int KIND>
+race_status_t run_pass_groups(const Shape& s, const Derived& d, const WsLayout& wl, char* ws, PassArgs a,
+                              hipStream_t st, const std::function<void(const Group&, PassArgs&)>& per_group) {
+    for (int g = 0; g < d.G; ++g) {
+        const Group gr = group(d, g);
+        PassArgs ag = a;
+        ag.L = gr.L;
+        ag.gmode = (g > 0 ? ACC_IN : 0) | (g + 1 < d.G ? ACC_OUT : 0);
+        ag.acc = d.G > 1 ? reinterpret_cast<float*>(ws + wl.acc) : nullptr;
+        ag.accD = d.G > 1 ? reinterpret_cast<float*>(ws + wl.accD) : nullptr;
+        per_group(gr, ag);
+        RACE_TRY((with_cfg<F32>(s.P, gr.MT, [&](auto tag) {
+            using C = typename decltype(tag)::type;
+            return run_pass<C, KIND>(s, d, ag, st);
+        })));
+    }
+    return RACE_OK;
+}
+
+// Hyperplanes of table group g (W is [L, P, 64], groups are consecutive tables).
+inline const void* group_w(const void* W, const Shape& s, const Group& gr, bool f32) {
+    return reinterpret_cast<const char*>(W) + (size_t)gr.t0 * s.P * DH * (f32 ? 4 : 2);
+}
+
 // Forward into O; when `saved` is set it receives the sketch states, D and
 // the plane values of queries and keys (else the keys' go to the workspace).
-template <class C>
+template <bool F32>
 race_status_t run_forward(const Shape& s, const Derived& d, const WsLayout& wl, const Call& c, void* O, void* saved) {
     char* ws = reinterpret_cast<char*>(c.ws);
     hipStream_t st = c.stream;
     const SavedLayout sl = saved_layout(s, d);
     const CacheLayout cl = cache_layout(s, d);
     char* sv = reinterpret_cast<char*>(saved);
-    const PlaneCache kc = plane_cache(saved ? sv + sl.k : ws + wl.Kc, cl);
-    PlaneCache qc{};
-    if (saved) qc = plane_cache(sv + sl.q, cl);
+    char* kbase = saved ? sv + sl.k : ws + wl.Kc;
+    // per-chunk states (causal: in saved when given) and, non-causal, the totals
     float* Sb = (s.causal && saved) ? reinterpret_cast<float*>(saved) : reinterpret_cast<float*>(ws + wl.S);
+    float* St = saved ? reinterpret_cast<float*>(saved) : reinterpret_cast<float*>(ws + wl.St);
     const float beta = c.hard ? HARD_BETA : c.beta;
-    RACE_TRY((run_totals<C, false>(s, d, c.K, c.V, nullptr, nullptr, kc, c.W, beta, Sb, st)));
-    PassArgs a{};
-    a.Xa = c.Q; a.ca = qc; a.cb = kc; a.Zsrc = c.V; a.W = c.W; a.beta = beta; a.out0 = O; a.hard = c.hard;
-    a.Dv = saved ? reinterpret_cast<float*>(sv + sl.D) : nullptr;
-    if (s.causal) {
-        RACE_TRY(run_scan<SCAN_EXCL>(s, d, Sb, nullptr, reinterpret_cast<float*>(ws + wl.scan), st));
-        a.state = Sb; a.state_bh_stride = d.NC * d.F65; a.state_chunk_stride = d.F65;
-    } else {
-        float* St = saved ? reinterpret_cast<float*>(saved) : reinterpret_cast<float*>(ws + wl.St);
-        RACE_TRY(run_scan<SCAN_TOTAL>(s, d, Sb, St, nullptr, st));
-        a.state = St; a.state_bh_stride = d.F65; a.state_chunk_stride = 0;
+    for (int g = 0; g < d.G; ++g) {
+        const Group gr = group(d, g);
+        float* Sg = Sb + group_states_floats(d, d.NC, g);
+        const PlaneCache kc = plane_cache(kbase, cl, g);
+        const void* Wg = group_w(c.W, s, gr, F32);
+        RACE_TRY((with_cfg<F32>(s.P, gr.MT, [&](auto tag) {
+            using C = typename decltype(tag)::type;
+            return run_totals<C, false>(s, d, gr, c.K, c.V, nullptr, nullptr, kc, Wg, beta, Sg, st);
+        })));
+        if (s.causal) {
+            RACE_TRY(run_scan<SCAN_EXCL>(s, d, gr.F65, Sg, nullptr, 0, reinterpret_cast<float*>(ws + wl.scan), st));
+        } else {
+            RACE_TRY(run_scan<SCAN_TOTAL>(s, d, gr.F65, Sg, St + group_states_floats(d, 1, g), gr.F65, nullptr, st));
+        }
     }
-    return run_pass<C, PASS_FWD>(s, d, a, st);
+    PassArgs a{};
+    a.Xa = c.Q; a.Zsrc = c.V; a.beta = beta; a.out0 = O; a.hard = c.hard;
+    a.Dv = saved ? reinterpret_cast<float*>(sv + sl.D) : nullptr;
+    return run_pass_groups<F32, PASS_FWD>(s, d, wl, ws, a, st, [&](const Group& gr, PassArgs& ag) {
+        ag.W = group_w(c.W, s, gr, F32);
+        ag.ca = saved ? plane_cache(sv + sl.q, cl, gr.g) : PlaneCache{};
+        ag.cb = plane_cache(kbase, cl, gr.g);
+        if (s.causal) {
+            ag.state = Sb + group_states_floats(d, d.NC, gr.g);
+            ag.state_bh_stride = d.NC * gr.F65; ag.state_chunk_stride = gr.F65;
+        } else {
+            ag.state = St + group_states_floats(d, 1, gr.g);
+            ag.state_bh_stride = gr.F65; ag.state_chunk_stride = 0;
+        }
+    });
 }
 
-template <class C>
-race_status_t run(const Shape& s, const Derived& d, const WsLayout& wl, const Call& c) {
+template <bool F32>
+race_status_t run_backward(const Shape& s, const Derived& d, const WsLayout& wl, const Call& c) {
     char* ws = reinterpret_cast<char*>(c.ws);
     hipStream_t st = c.stream;
-    if (c.op == OP_HASH) {
-        const int64_t rows = d.BH * s.N;
-        const int64_t blocks = (rows + 63) / 64;
-        if (blocks > 0x7fffffff) return RACE_ERR_UNSUPPORTED;
-        profile_mark("hash", st);
-        hipLaunchKernelGGL(k_hash<C>, dim3((unsigned)blocks), dim3(NT), 0, st, c.X, c.W, rows, s.L, c.ids,
-                           c.near_zero);
-        return launch_ok();
-    }
-    if (c.op == OP_FWD) return run_forward<C>(s, d, wl, c, c.O, c.saved_out);
-    if (c.op == OP_PREFILL) {
-        // chunk sums of the keys' sketch, then their total straight into the state
-        float* Sb = reinterpret_cast<float*>(ws + wl.S);
-        const PlaneCache kc = plane_cache(ws + wl.Kc, cache_layout(s, d));
-        RACE_TRY((run_totals<C, false>(s, d, c.K, c.V, nullptr, nullptr, kc, c.W, c.hard ? HARD_BETA : c.beta,
-                                       Sb, st)));
-        return run_scan<SCAN_TOTAL>(s, d, Sb, c.state, nullptr, st);
-    }
-    if (c.op == OP_DECODE) {
-        DecodeArgs a{};
-        a.q = c.Q; a.k = c.K; a.v = c.V; a.W = c.W; a.state = c.state; a.o = c.O; a.T = (int)s.N;
-        a.P = s.P; a.L = s.L; a.F = C::F; a.KB = C::KB; a.TPT = C::TPT; a.TPL = C::TPL;
-        a.beta = c.beta; a.hard = c.hard;
-        static_assert(C::F <= DEC_MAXF && C::F % DEC_RG == 0, "decode tiling");
-        profile_mark("decode", st);
-        constexpr int NR = C::F / DEC_RG;   // state rows per thread
-        if (a.T == 1) hipLaunchKernelGGL((k_decode_one<C::F32, NR>), dim3((unsigned)d.BH), dim3(DEC_NT), 0, st, a);
-        else hipLaunchKernelGGL((k_decode_multi<C::F32, NR>), dim3((unsigned)d.BH), dim3(DEC_NT), 0, st, a);
-        return launch_ok();
-    }
-
-    // backward: O and what the forward kept, recomputed when not given
+    // O and what the forward kept, recomputed when not given
     const void* O = c.O_in;
     const void* saved = c.saved_in;
     if (!saved) {
-        RACE_TRY(run_forward<C>(s, d, wl, c, ws + wl.Ov, ws + wl.Sv));
+        RACE_TRY(run_forward<F32>(s, d, wl, c, ws + wl.Ov, ws + wl.Sv));
         O = ws + wl.Ov;
         saved = ws + wl.Sv;
     }
     const SavedLayout sl = saved_layout(s, d);
     const CacheLayout cl = cache_layout(s, d);
     char* sv = const_cast<char*>(reinterpret_cast<const char*>(saved));
-    const PlaneCache qc = plane_cache(sv + sl.q, cl), kc = plane_cache(sv + sl.k, cl);
     const float* S = reinterpret_cast<const float*>(saved);
     float* Dv = reinterpret_cast<float*>(sv + sl.D);
     float* Ev = reinterpret_cast<float*>(ws + wl.E);
-    using elem = typename Prec<C::F32>::elem;
-    elem* WTp = reinterpret_cast<elem*>(ws + wl.wt);
-    profile_mark("prep", st);
-    hipLaunchKernelGGL(k_prep<C>, dim3(8), dim3(256), 0, st, reinterpret_cast<const elem*>(c.W), s.L, WTp);
-    RACE_TRY(launch_ok());
+    using elem = typename Prec<F32>::elem;
+    auto wtp = [&](int g) { return reinterpret_cast<elem*>(ws + wl.wt + (size_t)g * wt_bytes(d)); };
+    for (int g = 0; g < d.G; ++g) {
+        const Group gr = group(d, g);
+        profile_mark("prep", st);
+        RACE_TRY((with_cfg<F32>(s.P, gr.MT, [&](auto tag) {
+            using C = typename decltype(tag)::type;
+            hipLaunchKernelGGL(k_prep<C>, dim3(8), dim3(256), 0, st,
+                               reinterpret_cast<const elem*>(group_w(c.W, s, gr, F32)), gr.L, wtp(g));
+            return launch_ok();
+        })));
+    }
 
     PassArgs q{};
-    q.Xa = c.Q; q.ca = qc; q.cb = kc; q.Zsrc = c.V; q.Ysrc = c.dO; q.Osrc = O; q.W = c.W; q.WTp = WTp;
-    q.beta = c.beta;
+    q.Xa = c.Q; q.Zsrc = c.V; q.Ysrc = c.dO; q.Osrc = O; q.beta = c.beta;
     q.Dv = Dv; q.Ev = Ev; q.out0 = c.dQ;
-    q.state = S;
-    q.state_bh_stride = s.causal ? d.NC * d.F65 : d.F65;
-    q.state_chunk_stride = s.causal ? d.F65 : 0;
-    RACE_TRY((run_pass<C, PASS_BWD_Q>(s, d, q, st)));
+    RACE_TRY((run_pass_groups<F32, PASS_BWD_Q>(s, d, wl, ws, q, st, [&](const Group& gr, PassArgs& ag) {
+        ag.W = group_w(c.W, s, gr, F32);
+        ag.WTp = wtp(gr.g);
+        ag.ca = plane_cache(sv + sl.q, cl, gr.g);
+        ag.cb = plane_cache(sv + sl.k, cl, gr.g);
+        ag.state = S + group_states_floats(d, s.causal ? d.NC : 1, gr.g);
+        ag.state_bh_stride = s.causal ? d.NC * gr.F65 : gr.F65;
+        ag.state_chunk_stride = s.causal ? gr.F65 : 0;
+    })));
 
+    // gradient sketches of the queries, reverse-scanned (causal) or summed
     float* Tw = reinterpret_cast<float*>(ws + wl.T);
-    RACE_TRY((run_totals<C, true>(s, d, c.Q, c.dO, Dv, Ev, qc, c.W, c.beta, Tw, st)));
-    PassArgs k{};
-    k.Xa = c.K; k.ca = kc; k.cb = qc; k.Zsrc = c.dO; k.Ysrc = c.V; k.W = c.W; k.WTp = WTp; k.beta = c.beta;
-    k.Dv = Dv; k.Ev = Ev; k.out0 = c.dK; k.out1 = c.dV;
-    if (s.causal) {
-        RACE_TRY(run_scan<SCAN_REV_EXCL>(s, d, Tw, nullptr, reinterpret_cast<float*>(ws + wl.scan), st));
-        k.state = Tw; k.state_bh_stride = d.NC * d.F65; k.state_chunk_stride = d.F65;
-    } else {
-        float* Ttw = reinterpret_cast<float*>(ws + wl.Tt);
-        RACE_TRY(run_scan<SCAN_TOTAL>(s, d, Tw, Ttw, nullptr, st));
-        k.state = Ttw; k.state_bh_stride = d.F65; k.state_chunk_stride = 0;
+    float* Ttw = reinterpret_cast<float*>(ws + wl.Tt);
+    for (int g = 0; g < d.G; ++g) {
+        const Group gr = group(d, g);
+        float* Tg = Tw + group_states_floats(d, d.NC, g);
+        RACE_TRY((with_cfg<F32>(s.P, gr.MT, [&](auto tag) {
+            using C = typename decltype(tag)::type;
+            return run_totals<C, true>(s, d, gr, c.Q, c.dO, Dv, Ev, plane_cache(sv + sl.q, cl, g),
+                                       group_w(c.W, s, gr, F32), c.beta, Tg, st);
+        })));
+        if (s.causal) {
+            RACE_TRY(run_scan<SCAN_REV_EXCL>(s, d, gr.F65, Tg, nullptr, 0, reinterpret_cast<float*>(ws + wl.scan),
+                                             st));
+        } else {
+            RACE_TRY(run_scan<SCAN_TOTAL>(s, d, gr.F65, Tg, Ttw + group_states_floats(d, 1, g), gr.F65, nullptr,
+                                          st));
+        }
     }
-    return run_pass<C, PASS_BWD_K>(s, d, k, st);
+    PassArgs k{};
+    k.Xa = c.K; k.Zsrc = c.dO; k.Ysrc = c.V; k.beta = c.beta;
+    k.Dv = Dv; k.Ev = Ev; k.out0 = c.dK; k.out1 = c.dV;
+    auto key_side = [&](const Group& gr, PassArgs& ag) {
+        ag.W = group_w(c.W, s, gr, F32);
+        ag.WTp = wtp(gr.g);
+        ag.ca = plane_cache(sv + sl.k, cl, gr.g);
+        ag.cb = plane_cache(sv + sl.q, cl, gr.g);
+        if (s.causal) {
+            ag.state = Tw + group_states_floats(d, d.NC, gr.g);
+            ag.state_bh_stride = d.NC * gr.F65; ag.state_chunk_stride = gr.F65;
+        } else {
+            ag.state = Ttw + group_states_floats(d, 1, gr.g);
+            ag.state_bh_stride = gr.F65; ag.state_chunk_stride = 0;
+        }
+    };
+    // dV of every group, then dK (each output's partials share one buffer)
+    RACE_TRY((run_pass_groups<F32, PASS_BWD_V>(s, d, wl, ws, k, st, key_side)));
+    return run_pass_groups<F32, PASS_BWD_K>(s, d, wl, ws, k, st, key_side);
 }
-
-#define RACE_CASE(P_, MT_)                                                   \
-    if (s.P == P_ && d.MT == MT_) return run<Cfg<P_, MT_, F32>>(s, d, wl, c);
 
 template <bool F32>
 race_status_t dispatch(const Shape& s, const Derived& d, const WsLayout& wl, const Call& c) {
-    RACE_CASE(1, 1) RACE_CASE(1, 2) RACE_CASE(1, 4) RACE_CASE(1, 8)
-    RACE_CASE(2, 1) RACE_CASE(2, 2) RACE_CASE(2, 4) RACE_CASE(2, 8)
-    RACE_CASE(3, 1) RACE_CASE(3, 2) RACE_CASE(3, 4) RACE_CASE(3, 8)
-    RACE_CASE(4, 1) RACE_CASE(4, 2) RACE_CASE(4, 4) RACE_CASE(4, 8)
-    return RACE_ERR_UNSUPPORTED;
+    hipStream_t st = c.stream;
+    if (c.op == OP_HASH) {
+        const int64_t rows = d.BH * s.N;
+        const int64_t blocks = (rows + 63) / 64;
+        if (blocks > 0x7fffffff) return RACE_ERR_UNSUPPORTED;
+        for (int g = 0; g < d.G; ++g) {
+            const Group gr = group(d, g);
+            profile_mark("hash", st);
+            RACE_TRY((with_cfg<F32>(s.P, gr.MT, [&](auto tag) {
+                using C = typename decltype(tag)::type;
+                hipLaunchKernelGGL(k_hash<C>, dim3((unsigned)blocks), dim3(NT), 0, st, c.X, group_w(c.W, s, gr, F32),
+                                   rows, gr.L, s.L, c.ids + gr.t0, c.near_zero);
+                return launch_ok();
+            })));
+        }
+        return RACE_OK;
+    }
+    if (c.op == OP_FWD) return run_forward<F32>(s, d, wl, c, c.O, c.saved_out);
+    if (c.op == OP_BWD) return run_backward<F32>(s, d, wl, c);
+    if (c.op == OP_PREFILL) {
+        // chunk sums of the keys' sketch, then their total straight into each
+        // group's part of the running state
+        char* ws = reinterpret_cast<char*>(c.ws);
+        float* Sb = reinterpret_cast<float*>(ws + wl.S);
+        const CacheLayout cl = cache_layout(s, d);
+        const float beta = c.hard ? HARD_BETA : c.beta;
+        for (int g = 0; g < d.G; ++g) {
+            const Group gr = group(d, g);
+            float* Sg = Sb + group_states_floats(d, d.NC, g);
+            RACE_TRY((with_cfg<F32>(s.P, gr.MT, [&](auto tag) {
+                using C = typename decltype(tag)::type;
+                return run_totals<C, false>(s, d, gr, c.K, c.V, nullptr, nullptr, plane_cache(ws + wl.Kc, cl, g),
+                                            group_w(c.W, s, gr, F32), beta, Sg, st);
+            })));
+            RACE_TRY(run_scan<SCAN_TOTAL>(s, d, gr.F65, Sg, c.state + (size_t)g * d.F65, d.F65all, nullptr, st));
+        }
+        return RACE_OK;
+    }
+    if (c.op == OP_DECODE) {
+        return with_cfg<F32>(s.P, d.MT, [&](auto tag) {
+            using C = typename decltype(tag)::type;
+            DecodeArgs a{};
+            a.q = c.Q; a.k = c.K; a.v = c.V; a.W = c.W; a.state = c.state; a.o = c.O; a.T = (int)s.N;
+            a.P = s.P; a.L = s.L; a.F = C::F; a.KB = C::KB; a.TPT = C::TPT; a.TPL = C::TPL;
+            a.G = d.G; a.Lg = d.Lg; a.Fl = d.Fl;
+            a.beta = c.beta; a.hard = c.hard;
+            static_assert(C::F <= DEC_MAXF && C::F % DEC_RG == 0, "decode tiling");
+            constexpr int NR = C::F / DEC_RG;   // state rows per thread
+            if (a.T > 1 && d.G == 1) {
+                profile_mark("decode", st);
+                hipLaunchKernelGGL((k_decode_multi<C::F32, NR>), dim3((unsigned)d.BH), dim3(DEC_NT), 0, st, a);
+                return launch_ok();
+            }
+            // one launch per token: every table group of each head in turn
+            for (int tok = 0; tok < a.T; ++tok) {
+                a.tok = tok;
+                profile_mark("decode", st);
+                hipLaunchKernelGGL((k_decode_one<C::F32, NR>), dim3((unsigned)d.BH), dim3(DEC_NT), 0, st, a);
+                RACE_TRY(launch_ok());
+            }
+            return RACE_OK;
+        });
+    }
+    return RACE_ERR_INVALID_ARG;
 }
 
 }  // namespace race

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <cmath>
+#include <initializer_list>
 
 #include "race_attn.h"
 
@@ -16,12 +17,27 @@ struct Shape {
     int causal, chunk;
 };
 
+// Tables are processed in groups of at most Lg (one launch per group and
+// pass): every pass is linear in the features of the tables, so the groups'
+// partial results add up, and only the forward's final division (and the
+// normalisation's chain rule of the gradients) waits for the last group.
+// Groups 0 .. G-2 hold Lg tables each; the last holds the rest. A group of
+// n tables has MT = ceil(n P' / 16) rounded to a power of two projection
+// tiles, F = 32 MT KB features and F * 65 floats per sketch state.
 struct Derived {
-    int Pp, MT, KB, F, NPAIR;
+    int Pp, KB;
+    int G, Lg;     // number of table groups, tables per full group
+    int MT, F, NPAIR;
     int NPL;       // projection rows per token (MT * 16)
-    int64_t BH, NC;
     int64_t F65;   // floats per sketch state: F * 64 value sums + F masses
+    int Ll, MTl, Fl, NPLl;   // the last group (equal to the full one when L % Lg == 0)
+    int64_t F65l;
+    int64_t F65all;          // all groups of one head (the running state's floats)
+    int64_t BH, NC;
 };
+
+// Largest number of table groups (launches per pass): L * 2^P <= 2^16 features.
+constexpr int MAX_FEATURES = 1 << 16;
 
 struct WsLayout {
     size_t wt;     // backward: back-projection operand table
@@ -34,14 +50,20 @@ struct WsLayout {
     size_t Ov;     // backward without saved: the recomputed forward output
     size_t Kc;     // forward without saved: the keys' plane values
     size_t scan;   // segment sums of the segmented chunk scan (when used)
+    size_t acc;    // more than one table group: partial outputs [rows][64], float32
+    size_t accD;   // and the forward's partial denominators [rows]
     size_t total;
 };
 
-// Plane values of one side (queries or keys): u = tanh of the normalised
-// projection [rows][NPL] (float16 for bf16 inputs, float32 for float32; sized
-// for float32, the upper bound), then 1 / max(|x|, eps) [rows] in float32.
+// Plane values of one side (queries or keys): per table group g,
+// u = tanh of the normalised projection [rows][NPL_g] (float16 for bf16
+// inputs, float32 for float32; sized for float32, the upper bound), then
+// 1 / max(|x|, eps) [rows] in float32 (shared by the groups).
 struct CacheLayout {
-    size_t u, inv, total;
+    size_t u;       // group 0's plane values
+    size_t ustep;   // bytes from one full group's plane values to the next
+    size_t inv, total;
+    size_t u_of(int g) const { return u + (size_t)g * ustep; }
 };
 
 // The saved buffer: float32 sketch states (per chunk, causal; the total,
@@ -77,16 +99,27 @@ inline race_status_t derive(const Shape& s, Derived& d) {
     // in-chunk byte offsets (rows of up to 512 bytes) are 32-bit
     if (s.chunk > MAX_CHUNK) return RACE_ERR_UNSUPPORTED;
     d.Pp = (s.P == 3) ? 4 : s.P;
-    const int64_t rows = (int64_t)s.L * d.Pp;
-    if (rows > 128) return RACE_ERR_UNSUPPORTED;
-    int mt = (int)((rows + 15) / 16);
-    int p2 = 1;
-    while (p2 < mt) p2 <<= 1;
-    d.MT = p2;
+    if ((int64_t)s.L << s.P > MAX_FEATURES) return RACE_ERR_UNSUPPORTED;
     d.KB = (s.P == 4) ? 2 : 1;
+    // tables per group: P = 4 up to 16 (four projection tiles, 256 features:
+    // the state fits two workgroups per CU), otherwise 128 projection rows
+    d.Lg = (s.P == 4) ? 16 : 128 / d.Pp;
+    d.G = (s.L + d.Lg - 1) / d.Lg;
+    const int Lfull = d.G > 1 ? d.Lg : s.L;
+    d.Ll = s.L - (d.G - 1) * d.Lg;
+    auto tiles = [&](int n) {
+        const int mt = (n * d.Pp + 15) / 16;
+        int p2 = 1;
+        while (p2 < mt) p2 <<= 1;
+        return p2;
+    };
+    d.MT = tiles(Lfull);
     d.F = 32 * d.MT * d.KB;
     d.NPAIR = (d.MT + 1) / 2;
     d.NPL = d.MT * 16;
+    d.MTl = tiles(d.Ll);
+    d.Fl = 32 * d.MTl * d.KB;
+    d.NPLl = d.MTl * 16;
     int64_t bh, elems;
     if (!mul_ok(s.B, s.H, bh) || !mul_ok(bh, s.N, elems) || !mul_ok(elems, s.d, elems))
         return RACE_ERR_INVALID_ARG;
@@ -94,22 +127,54 @@ inline race_status_t derive(const Shape& s, Derived& d) {
     d.BH = bh;
     d.NC = (s.N + s.chunk - 1) / s.chunk;
     d.F65 = (int64_t)d.F * 65;
+    d.F65l = (int64_t)d.Fl * 65;
+    d.F65all = (int64_t)(d.G - 1) * d.F65 + d.F65l;
     if (d.BH > 65535 || d.NC > 0x7fffffff) return RACE_ERR_UNSUPPORTED;
     return RACE_OK;
+}
+
+// Per-group view: tables [t0, t0 + L), MT projection tiles, F features.
+struct Group {
+    int g, t0, L, MT, F, NPL;
+    int64_t F65;
+};
+
+inline Group group(const Derived& d, int g) {
+    const bool last = g == d.G - 1;
+    Group r;
+    r.g = g;
+    r.t0 = g * d.Lg;
+    r.L = last ? d.Ll : d.Lg;
+    r.MT = last ? d.MTl : d.MT;
+    r.F = last ? d.Fl : d.F;
+    r.NPL = last ? d.NPLl : d.NPL;
+    r.F65 = last ? d.F65l : d.F65;
+    return r;
 }
 
 inline CacheLayout cache_layout(const Shape& s, const Derived& d) {
     const size_t rows = (size_t)d.BH * (size_t)s.N;
     CacheLayout c;
     c.u = 0;
-    c.inv = align256(rows * (size_t)d.NPL * sizeof(float));
+    c.ustep = align256(rows * (size_t)d.NPL * sizeof(float));
+    c.inv = c.u_of(d.G - 1) + align256(rows * (size_t)d.NPLl * sizeof(float));
     c.total = c.inv + align256(rows * sizeof(float));
     return c;
 }
 
+// Sketch states of all groups, group-major: group g's array
+// [BH][per_head][F65_g] starts after the full groups before it.
+// per_head = chunks (per-chunk states) or 1 (whole-sequence totals).
+inline size_t group_states_floats(const Derived& d, int64_t per_head, int g) {
+    return (size_t)g * (size_t)d.BH * (size_t)per_head * (size_t)d.F65;
+}
+inline size_t all_states_bytes(const Derived& d, int64_t per_head) {
+    return (group_states_floats(d, per_head, d.G - 1) + (size_t)d.BH * (size_t)per_head * (size_t)d.F65l) *
+           sizeof(float);
+}
+
 inline SavedLayout saved_layout(const Shape& s, const Derived& d) {
-    const size_t per = (size_t)d.F65 * sizeof(float);
-    const size_t states = s.causal ? (size_t)d.BH * (size_t)d.NC * per : (size_t)d.BH * per;
+    const size_t states = all_states_bytes(d, s.causal ? d.NC : 1);
     const size_t cache = cache_layout(s, d).total;
     SavedLayout l;
     l.D = align256(states);
@@ -125,9 +190,9 @@ inline size_t saved_bytes(const Shape& s, const Derived& d) { return saved_layou
 // (state elements / 256) x heads already has enough workgroups to keep the
 // memory busy; otherwise up to 16 segments of at least 64 chunks each,
 // summed first and then scanned from their offsets (two launches).
-inline int scan_segs(const Shape& s, const Derived& d) {
+inline int scan_segs(const Shape& s, const Derived& d, int64_t F65) {
     if (!s.causal) return 1;
-    const int64_t blocks = (d.F65 + 255) / 256 * d.BH;
+    const int64_t blocks = (F65 + 255) / 256 * d.BH;
     if (blocks >= 192) return 1;
     int64_t segs = (768 + blocks - 1) / blocks;
     if (segs > 16) segs = 16;
@@ -135,11 +200,13 @@ inline int scan_segs(const Shape& s, const Derived& d) {
     return segs < 2 ? 1 : (int)segs;
 }
 
+// Back-projection operand table of one group (k_prep), sized for float32.
+inline size_t wt_bytes(const Derived& d) { return align256((size_t)d.NPAIR * 4 * 64 * 8 * sizeof(float)); }
+
 inline WsLayout ws_layout(const Shape& s, const Derived& d, int kind) {
     WsLayout w{};
-    const size_t per = (size_t)d.F65 * sizeof(float);
-    const size_t chunks = (size_t)d.BH * (size_t)d.NC * per;
-    const size_t totals = (size_t)d.BH * per;
+    const size_t chunks = all_states_bytes(d, d.NC);
+    const size_t totals = all_states_bytes(d, 1);
     const size_t tokens = (size_t)d.BH * (size_t)s.N;
     size_t off = 0;
     if (kind != WS_BWD) {
@@ -150,7 +217,7 @@ inline WsLayout ws_layout(const Shape& s, const Derived& d, int kind) {
         w.Kc = off;  off = align256(off + cache_layout(s, d).total);
     }
     if (kind == WS_BWD || kind == WS_BWD_RECOMPUTE) {
-        w.wt = off;  off = align256(off + (size_t)d.NPAIR * 4 * 64 * 8 * sizeof(float));
+        w.wt = off;  off = align256(off + (size_t)d.G * wt_bytes(d));
         w.T = off;   off = align256(off + chunks);
         w.Tt = off;  off = align256(off + (s.causal ? 0 : totals));
         w.E = off;   off = align256(off + tokens * sizeof(float));
@@ -159,8 +226,23 @@ inline WsLayout ws_layout(const Shape& s, const Derived& d, int kind) {
         w.Sv = off;  off = align256(off + saved_bytes(s, d));
         w.Ov = off;  off = align256(off + tokens * (size_t)s.d * sizeof(float));
     }
-    const int segs = scan_segs(s, d);
-    w.scan = off;    off = align256(off + (segs > 1 ? (size_t)d.BH * (size_t)segs * per : 0));
+    // partial outputs of the groups before the last: [rows][64] and the
+    // forward's partial denominators [rows], float32
+    if (d.G > 1) {
+        w.acc = off;  off = align256(off + tokens * (size_t)s.d * sizeof(float));
+        w.accD = off; off = align256(off + tokens * sizeof(float));
+    }
+    // segment sums of one group's scan at a time (the largest of the groups)
+    size_t seg_bytes = 0;
+    for (const int64_t f65 : {d.F65, d.F65l}) {
+        const int segs = scan_segs(s, d, f65);
+        if (segs > 1) {
+            const size_t b = (size_t)d.BH * (size_t)segs * (size_t)f65 * sizeof(float);
+            if (b > seg_bytes) seg_bytes = b;
+        }
+    }
+    w.scan = off;
+    off = align256(off + seg_bytes);
     w.total = off;
     return w;
 }

@@ -809,15 +809,16 @@ __device__ inline float scan_range(float* p, int nchunks, int elems, int c0, int
 
 // One pass over all chunks (one thread per state element): exclusive prefix
 // (causal), reverse exclusive prefix (backward) or the total (non-causal).
+// The total of head bh goes to total[bh * total_stride + e].
 template <int KIND>
 __global__ __launch_bounds__(256) void k_scan(float* __restrict__ st, float* __restrict__ total,
-                                              int nchunks, int elems) {
+                                              int nchunks, int elems, int64_t total_stride) {
     const int e = blockIdx.x * blockDim.x + threadIdx.x;
     const int bh = blockIdx.y;
     if (e >= elems) return;
     float* p = st + (size_t)bh * nchunks * elems + e;
     const float run = scan_range<KIND, KIND != SCAN_TOTAL>(p, nchunks, elems, 0, nchunks, 0.f);
-    if constexpr (KIND == SCAN_TOTAL) total[(size_t)bh * elems + e] = run;
+    if constexpr (KIND == SCAN_TOTAL) total[(size_t)bh * (size_t)total_stride + e] = run;
 }
 
 // Segmented form of the (reverse) exclusive prefix, for grids too small to
@@ -875,7 +876,42 @@ struct PassArgs {
     float beta;
     int causal;
     int hard;              // FWD: hard buckets (beta = HARD_BETA): a denominator below 2^(P-1) is 0
+    // Table groups: a pass over one group of the tables adds its part of the
+    // output to the partial of the groups before it (ACC_IN) and/or leaves
+    // the sum as the next group's partial (ACC_OUT) instead of finishing the
+    // output. acc: [rows][64] float32 (O's numerators, or dQ, dK before the
+    // normalisation's chain rule, or dV); accD: the forward's denominators.
+    float* acc;
+    float* accD;
+    int gmode;
 };
+
+enum { ACC_IN = 1, ACC_OUT = 2 };
+
+// Partial output rows of one lane in the transposed read-out layout
+// (columns cb + 4 g .. +3 of rows r0 + 16 at + ln), float32.
+__device__ inline void acc_load_t(rsrc_t racc, int r0, int cb, int ln, int g, f32x4 (&Y)[4]) {
+#pragma unroll
+    for (int at = 0; at < 4; ++at) {
+        const f32x4 v = __builtin_bit_cast(f32x4, bload128(racc, ((r0 + 16 * at + ln) * DH + cb + 4 * g) * 4));
+        Y[at] += v;
+    }
+}
+__device__ inline void acc_store_t(rsrc_t racc, int r0, int cb, int ln, int g, const f32x4 (&Y)[4]) {
+#pragma unroll
+    for (int at = 0; at < 4; ++at)
+        bstore128(racc, ((r0 + 16 * at + ln) * DH + cb + 4 * g) * 4, __builtin_bit_cast(u32x4, Y[at]));
+}
+// The same for one own-token gradient row (columns 16 dt + 4 g .. +3 of row rowi).
+__device__ inline void acc_load_row(rsrc_t racc, int rowi, int g, f32x4 (&dX)[4]) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+        dX[dt] += __builtin_bit_cast(f32x4, bload128(racc, (rowi * DH + 16 * dt + 4 * g) * 4));
+}
+__device__ inline void acc_store_row(rsrc_t racc, int rowi, int g, const f32x4 (&dX)[4]) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) bstore128(racc, (rowi * DH + 16 * dt + 4 * g) * 4, __builtin_bit_cast(u32x4, dX[dt]));
+}
 
 // Sketch rows of feature block fb for the gradient contraction dA = M y:
 // [FBK*32][ROWE], value columns of wave w and the mass column (64) from the
@@ -1195,6 +1231,8 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
     const rsrc_t rZ = rows_rsrc(a.Zsrc, row0, nrows, row_bytes<C::F32>());
     const rsrc_t rO = rows_rsrc(a.out0, row0, nrows, row_bytes<C::F32>());
     const rsrc_t rD = rows_rsrc(a.Dv, row0, nrows, 4);
+    const rsrc_t rAcc = rows_rsrc(a.acc, row0, nrows, DH * 4);
+    const rsrc_t rAD = rows_rsrc(a.accD, row0, nrows, 4);
     const PlaneRows pra = plane_rows<C>(a.ca, row0, nrows), prb = plane_rows<C>(a.cb, row0, nrows);
 
     f32x4 Macc[C::NKC * 2], Zacc[C::NOWN * 2];
@@ -1347,10 +1385,15 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
         if (tq == 0) {
             float d = f_Dpart[tr] + f_Dpart[TB + tr] + f_Dpart[2 * TB + tr] + f_Dpart[3 * TB + tr] + d_empty;
             if (causal) d += f_Dint[tr];
-            bstore_f32(rD, (it * TB + tr) * 4, d);
-            // hard buckets: D is 2^P times a collision count, so anything
-            // below half a unit is an exact zero, and O = 0 for that query
-            f_rD[tr] = (a.hard && fabsf(d) < (float)(1 << (C::P - 1))) ? 0.f : rcp_(d);
+            if (a.gmode & ACC_IN) d += bload_f32(rAD, (it * TB + tr) * 4);
+            if (a.gmode & ACC_OUT) {
+                bstore_f32(rAD, (it * TB + tr) * 4, d);
+            } else {
+                bstore_f32(rD, (it * TB + tr) * 4, d);
+                // hard buckets: D is 2^P times a collision count, so anything
+                // below half a unit is an exact zero, and O = 0 for that query
+                f_rD[tr] = (a.hard && fabsf(d) < (float)(1 << (C::P - 1))) ? 0.f : rcp_(d);
+            }
         }
         if (causal) {
 #pragma unroll
@@ -1362,12 +1405,17 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
                         Y[at] = mma(zt, ld_frag<C::F32>(s_sc + (16 * at + ln) * C::ROWT + 32 * s + 8 * g), Y[at]);
             }
         }
+        if (a.gmode & ACC_IN) acc_load_t(rAcc, it * TB, 16 * w, ln, g, Y);
         __syncthreads();
-        float rd[4];
+        if (a.gmode & ACC_OUT) {
+            acc_store_t(rAcc, it * TB, 16 * w, ln, g, Y);
+        } else {
+            float rd[4];
 #pragma unroll
-        for (int at = 0; at < 4; ++at) rd[at] = f_rD[16 * at + ln];
-        const float none[4] = {-0.f, -0.f, -0.f, -0.f};   // x + -0 = x: nothing added
-        store_rows_t<C>(rO, it * TB, 16 * w, ln, g, Y, rd, none);
+            for (int at = 0; at < 4; ++at) rd[at] = f_rD[16 * at + ln];
+            const float none[4] = {-0.f, -0.f, -0.f, -0.f};   // x + -0 = x: nothing added
+            store_rows_t<C>(rO, it * TB, 16 * w, ln, g, Y, rd, none);
+        }
     }
 }
 
@@ -1453,6 +1501,7 @@ __attribute__((amdgpu_waves_per_eu(BwdQLds<C>::OCC, BwdQLds<C>::OCC))) void k_bw
     const rsrc_t rOut = rows_rsrc(a.out0, row0, nrows, row_bytes<C::F32>());
     const rsrc_t rD = rows_rsrc(a.Dv, row0, nrows, 4);
     const rsrc_t rE = rows_rsrc(a.Ev, row0, nrows, 4);
+    const rsrc_t rAcc = rows_rsrc(a.acc, row0, nrows, DH * 4);
     const PlaneRows pra = plane_rows<C>(a.ca, row0, nrows), prb = plane_rows<C>(a.cb, row0, nrows);
 
     // the plane values of queries and keys are loaded one feature block ahead;
@@ -1567,7 +1616,9 @@ __attribute__((amdgpu_waves_per_eu(BwdQLds<C>::OCC, BwdQLds<C>::OCC))) void k_bw
             if (causal) sketch_update<C, true, C::ROWE, false, TR>(fb, w, ln, g, cols_b, s_zr, Macc, Zacc);
         }
         __syncthreads();   // the next sub-block rewrites the y and z rows
-        store_dx<C>(xr, rOut, rowi, g, inv_a, a.beta, dX);
+        if (a.gmode & ACC_IN) acc_load_row(rAcc, rowi, g, dX);
+        if (a.gmode & ACC_OUT) acc_store_row(rAcc, rowi, g, dX);
+        else store_dx<C>(xr, rOut, rowi, g, inv_a, a.beta, dX);
     }
 }
 
@@ -1695,6 +1746,7 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
     const rsrc_t rOut1 = rows_rsrc(a.out1, row0, nrows, row_bytes<C::F32>());
     const rsrc_t rD = rows_rsrc(a.Dv, row0, nrows, 4);
     const rsrc_t rE = rows_rsrc(a.Ev, row0, nrows, 4);
+    const rsrc_t rAcc = rows_rsrc(a.acc, row0, nrows, DH * 4);
     const PlaneRows pra = plane_rows<C>(a.ca, row0, nrows), prb = plane_rows<C>(a.cb, row0, nrows);
     auto r0_of = [&](int it2) { return (nsub - 1 - it2) * TB; };   // first in-chunk row of a sub-block
     auto issue = [&](int it2) {
@@ -1865,18 +1917,29 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
                 }
                 __syncthreads();   // the value rows and scores are read before the next sub-block rewrites them
             }
-            const float one[4] = {1.f, 1.f, 1.f, 1.f}, zero[4] = {-0.f, -0.f, -0.f, -0.f};   // x + -0 = x
-            store_rows_t<C>(rOut1, r0_of(it), 16 * w, ln, g, Y, one, zero);
+            if (a.gmode & ACC_IN) acc_load_t(rAcc, r0_of(it), 16 * w, ln, g, Y);
+            if (a.gmode & ACC_OUT) {
+                acc_store_t(rAcc, r0_of(it), 16 * w, ln, g, Y);
+            } else {
+                const float one[4] = {1.f, 1.f, 1.f, 1.f}, zero[4] = {-0.f, -0.f, -0.f, -0.f};   // x + -0 = x
+                store_rows_t<C>(rOut1, r0_of(it), 16 * w, ln, g, Y, one, zero);
+            }
         }
-        if constexpr (DK) store_dx<C>(xr, rOut0, r0_of(it) + my, g, inv_a, a.beta, dX);
+        if constexpr (DK) {
+            if (a.gmode & ACC_IN) acc_load_row(rAcc, r0_of(it) + my, g, dX);
+            if (a.gmode & ACC_OUT) acc_store_row(rAcc, r0_of(it) + my, g, dX);
+            else store_dx<C>(xr, rOut0, r0_of(it) + my, g, inv_a, a.beta, dX);
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
 // hard-hash diagnostic
 // ---------------------------------------------------------------------------
+// ids: row r's entry for table l (of the L tables of this group) at
+// ids[r * ld + l].
 template <class C>
-__global__ __launch_bounds__(NT) void k_hash(const void* X, const void* Wv, int64_t rows, int L,
+__global__ __launch_bounds__(NT) void k_hash(const void* X, const void* Wv, int64_t rows, int L, int ld,
                                              int32_t* __restrict__ ids, unsigned long long* near_zero) {
     using elem = typename Prec<C::F32>::elem;
     using frag = typename Prec<C::F32>::frag;
@@ -1904,7 +1967,7 @@ __global__ __launch_bounds__(NT) void k_hash(const void* X, const void* Wv, int6
                 if (h > 0.f) id |= 1 << p;
                 if (valid && table < L && fabsf(h * inv) < NEAR_ZERO) ++nz;
             }
-            if (valid && table < L) ids[(size_t)r * L + table] = id;
+            if (valid && table < L) ids[(size_t)r * ld + table] = id;
         }
     }
     // wave-level sum of the near-zero count, one atomic per wave

@@ -72,6 +72,28 @@ def test_workspace_and_saved_sizes():
         _a256(6 * 32 * 65 * 4) + _a256(rows_nc * 4) + 2 * cache_nc
 
 
+def test_table_group_sizes():
+    # P4 L40 runs as table groups of 16, 16 and 8 (four, four and two
+    # projection tiles: 256, 256 and 128 features per state)
+    B, H, N, chunk = 2, 3, 1000, 128
+    rows, nch = B * H * N, -(-N // chunk)
+    f65 = (256 * 2 + 128) * 65 * 4
+    states = B * H * nch * f65
+    cache = 2 * _a256(rows * 64 * 4) + _a256(rows * 32 * 4) + _a256(rows * 4)
+    saved = race.saved_bytes(B, H, N, 64, 4, 40, True, chunk)
+    assert saved == _a256(states) + _a256(rows * 4) + 2 * cache
+    # the running state holds the groups one after the other
+    assert race.state_bytes(B, H, 4, 40) == B * H * f65
+    # the workspace adds the partial outputs of the groups before the last
+    # ([rows][64] and the denominators, float32)
+    one = race.workspace_bytes(B, H, N, 64, 4, 16, True, chunk, race.WS_BWD)
+    three = race.workspace_bytes(B, H, N, 64, 4, 40, True, chunk, race.WS_BWD)
+    assert three >= one + _a256(rows * 64 * 4) + _a256(rows * 4)
+    # P < 4: groups of 128 projection rows (P2: 64 tables)
+    assert race.state_bytes(1, 1, 2, 64) == 8 * 32 * 65 * 4
+    assert race.state_bytes(1, 1, 2, 65) == (8 + 1) * 32 * 65 * 4
+
+
 def test_segmented_scan_workspace():
     # one causal head of 2^20 tokens, L8 P1 (F = 32, 65 F floats per state):
     # chunk 1024 gives 1024 chunks and 9 workgroups per pass, so the chunk
@@ -97,7 +119,7 @@ def test_workspace_kind_rejected():
     ((1, 1, 10, 32, 4, 8, 1, 16, 0), race.RACE_ERR_UNSUPPORTED),        # d != 64
     ((1, 1, 10, 64, 5, 8, 1, 16, 0), race.RACE_ERR_UNSUPPORTED),        # P > 4
     ((1, 1, 10, 64, 0, 8, 1, 16, 0), race.RACE_ERR_INVALID_ARG),        # P = 0
-    ((1, 1, 10, 64, 4, 33, 1, 16, 0), race.RACE_ERR_UNSUPPORTED),       # L * P' > 128
+    ((1, 1, 10, 64, 4, 4097, 1, 16, 0), race.RACE_ERR_UNSUPPORTED),     # L * 2^P > 2^16
     ((1, 1, 10, 64, 4, 8, 1, 0, 0), race.RACE_ERR_INVALID_ARG),         # chunk = 0
     ((1, 70000, 10, 64, 4, 8, 1, 16, 0), race.RACE_ERR_UNSUPPORTED),    # B*H > 65535
     ((1 << 40, 1 << 20, 1 << 20, 64, 4, 8, 1, 16, 0), race.RACE_ERR_INVALID_ARG),  # overflow
@@ -199,7 +221,7 @@ def test_prefill_and_decode_argument_errors():
         assert L.race_attn_decode(*bad, None) == race.RACE_ERR_INVALID_ARG, i
     bad = list(dec); bad[6] = 1 << 31   # more tokens than a 32-bit count
     assert L.race_attn_decode(*bad, None) == race.RACE_ERR_UNSUPPORTED
-    for i, v in [(7, 32), (8, 5), (9, 64)]:
+    for i, v in [(7, 32), (8, 5), (9, 4097)]:
         bad = list(dec); bad[i] = v
         assert L.race_attn_decode(*bad, None) == race.RACE_ERR_UNSUPPORTED, i
 

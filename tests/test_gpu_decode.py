@@ -87,7 +87,8 @@ def check(res, ref, dtype, label):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("P,L", [(4, 16), (2, 8), (3, 5), (1, 3), (4, 5), (4, 32), (2, 64), (1, 100)])
+@pytest.mark.parametrize("P,L", [(4, 16), (2, 8), (3, 5), (1, 3), (4, 5), (4, 32), (2, 64), (1, 100), (4, 40),
+                                 (2, 70)])
 @pytest.mark.parametrize("n0", [0, 1, 301])
 def test_decode_soft_matches_oracle(lib, dtype, P, L, n0):
     # (4, 32): the largest state, F = 512 = one thread per feature; (2, 64),
@@ -99,7 +100,7 @@ def test_decode_soft_matches_oracle(lib, dtype, P, L, n0):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("P,L", [(4, 16), (2, 3), (3, 5)])
+@pytest.mark.parametrize("P,L", [(4, 16), (2, 3), (3, 5), (4, 20)])
 @pytest.mark.parametrize("n0", [0, 40])
 def test_decode_hard_matches_oracle(lib, dtype, P, L, n0):
     T, B, H, chunk = 6, 1, 2, 16
@@ -221,7 +222,7 @@ def gpu_multi(race, x, n0, T, P, L, beta, chunk):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("P,L", [(4, 16), (3, 5), (4, 32)])
+@pytest.mark.parametrize("P,L", [(4, 16), (3, 5), (4, 32), (4, 40)])
 @pytest.mark.parametrize("n0", [0, 301])
 @pytest.mark.parametrize("beta", [1.0, math.inf])
 def test_decode_several_tokens_per_call(lib, dtype, P, L, n0, beta):
@@ -229,6 +230,9 @@ def test_decode_several_tokens_per_call(lib, dtype, P, L, n0, beta):
     against the oracle's seven decode steps."""
     T, B, H, chunk = 7, 2, 2, 64
     seed = 4000 + n0
+    if math.isinf(beta) and L * P > 128 and n0 > 0:
+        pytest.skip("no seed keeps all 2 x 4 x 308 x L x P projections 1e-5 from zero at this size "
+                    "(hard buckets with table groups: n0 = 0 here, prompts in the hard-decode test)")
     if math.isinf(beta):
         for seed in range(4000, 4040):
             x = host_inputs(seed, B, H, n0 + T, 64, P, L, dtype)
