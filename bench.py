@@ -268,6 +268,9 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="causal_long_n12M")
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="tokens per workgroup (default: the workload's); only for the non-causal "
+                         "workload, whose chunk the configuration leaves free")
     ap.add_argument("--cpu-sample", type=int, default=262144)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true",
@@ -288,6 +291,12 @@ def main():
     from synth.workloads import BY_NAME
 
     w = BY_NAME[args.workload]
+    if args.chunk:
+        if w.causal:
+            print("--chunk applies to the non-causal workload only (the causal ones fix it)", file=sys.stderr)
+            sys.exit(2)
+        import dataclasses
+        w = dataclasses.replace(w, chunk=args.chunk)
     dev = torch.device("cuda:0")
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     shape = (w.B, w.H, w.N, w.d)

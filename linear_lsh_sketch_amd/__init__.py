@@ -334,7 +334,7 @@ class StageTimer:
     """Per-kernel timing of library calls with HIP events (the library records
     them on its own stream between its launches; see race_attn_profile_events)."""
 
-    def __init__(self, capacity: int = 17):
+    def __init__(self, capacity: int = 257):
         self.hip = ctypes.CDLL("libamdhip64.so")
         self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,

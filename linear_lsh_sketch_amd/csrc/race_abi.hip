@@ -45,7 +45,7 @@ race_status_t scratch_base(void** out) {
 
 // Per-thread profiling state (race_attn_profile_events). Only the calling
 // thread's own calls read or write it, so concurrent callers do not interact.
-constexpr int kMaxStages = 16;
+constexpr int kMaxStages = 256;
 thread_local hipEvent_t* t_events = nullptr;
 thread_local int t_capacity = 0;
 thread_local int t_count = 0;

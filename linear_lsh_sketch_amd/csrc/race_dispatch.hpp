@@ -68,7 +68,7 @@ race_status_t with_cfg(int P, int MT, Fn&& fn) {
     RACE_CFG(1, 1) RACE_CFG(1, 2) RACE_CFG(1, 4) RACE_CFG(1, 8)
     RACE_CFG(2, 1) RACE_CFG(2, 2) RACE_CFG(2, 4) RACE_CFG(2, 8)
     RACE_CFG(3, 1) RACE_CFG(3, 2) RACE_CFG(3, 4) RACE_CFG(3, 8)
-    RACE_CFG(4, 1) RACE_CFG(4, 2) RACE_CFG(4, 4)
+    RACE_CFG(4, 1) RACE_CFG(4, 2) RACE_CFG(4, 4) RACE_CFG(4, 8)
 #undef RACE_CFG
     return RACE_ERR_UNSUPPORTED;
 }
@@ -129,22 +129,44 @@ race_status_t run_pass(const Shape& s, const Derived& d, PassArgs a, hipStream_t
     a.N = s.N; a.chunk = s.chunk; a.causal = s.causal;
     const dim3 grid((unsigned)d.NC, (unsigned)d.BH), block(NT);
     using CB = Blk2Cfg<C>;
+    // causal groups of P = 4 have at most four projection tiles (race_host.hpp),
+    // so the eight-tile causal passes are never built
+    if constexpr (C::P == 4 && C::MT == 8) {
+        if (s.causal) return RACE_ERR_UNSUPPORTED;
+    }
+    constexpr bool CAUSAL_OK = !(C::P == 4 && C::MT == 8);
     if constexpr (KIND == PASS_FWD) {
         profile_mark("pass_fwd", st);
-        if (s.causal) hipLaunchKernelGGL((k_fwd<CB, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_fwd<CB, false>), grid, block, 0, st, a);
+        if constexpr (CAUSAL_OK) {
+            if (s.causal) hipLaunchKernelGGL((k_fwd<CB, true>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((k_fwd<CB, false>), grid, block, 0, st, a);
+        } else {
+            hipLaunchKernelGGL((k_fwd<CB, false>), grid, block, 0, st, a);
+        }
     } else if constexpr (KIND == PASS_BWD_Q) {
         profile_mark("pass_bwd_q", st);
-        if (s.causal) hipLaunchKernelGGL((k_bwd_q<CB, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_bwd_q<CB, false>), grid, block, 0, st, a);
+        if constexpr (CAUSAL_OK) {
+            if (s.causal) hipLaunchKernelGGL((k_bwd_q<CB, true>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((k_bwd_q<CB, false>), grid, block, 0, st, a);
+        } else {
+            hipLaunchKernelGGL((k_bwd_q<CB, false>), grid, block, 0, st, a);
+        }
     } else if constexpr (KIND == PASS_BWD_V) {
         profile_mark("pass_bwd_v", st);
-        if (s.causal) hipLaunchKernelGGL((k_bwd_k<CB, true, KPART_DV>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_bwd_k<CB, false, KPART_DV>), grid, block, 0, st, a);
+        if constexpr (CAUSAL_OK) {
+            if (s.causal) hipLaunchKernelGGL((k_bwd_k<CB, true, KPART_DV>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((k_bwd_k<CB, false, KPART_DV>), grid, block, 0, st, a);
+        } else {
+            hipLaunchKernelGGL((k_bwd_k<CB, false, KPART_DV>), grid, block, 0, st, a);
+        }
     } else {
         profile_mark("pass_bwd_k", st);
-        if (s.causal) hipLaunchKernelGGL((k_bwd_k<CB, true, KPART_DK>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_bwd_k<CB, false, KPART_DK>), grid, block, 0, st, a);
+        if constexpr (CAUSAL_OK) {
+            if (s.causal) hipLaunchKernelGGL((k_bwd_k<CB, true, KPART_DK>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((k_bwd_k<CB, false, KPART_DK>), grid, block, 0, st, a);
+        } else {
+            hipLaunchKernelGGL((k_bwd_k<CB, false, KPART_DK>), grid, block, 0, st, a);
+        }
     }
     return launch_ok();
 }

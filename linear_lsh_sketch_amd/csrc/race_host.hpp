@@ -101,9 +101,12 @@ inline race_status_t derive(const Shape& s, Derived& d) {
     d.Pp = (s.P == 3) ? 4 : s.P;
     if ((int64_t)s.L << s.P > MAX_FEATURES) return RACE_ERR_UNSUPPORTED;
     d.KB = (s.P == 4) ? 2 : 1;
-    // tables per group: P = 4 up to 16 (four projection tiles, 256 features:
-    // the state fits two workgroups per CU), otherwise 128 projection rows
-    d.Lg = (s.P == 4) ? 16 : 128 / d.Pp;
+    // tables per group: P = 4, causal: up to 16 (four projection tiles, 256
+    // features: the state fits two workgroups per CU, which pays more than the
+    // partial outputs cost); otherwise up to 128 projection rows (the
+    // non-causal passes have no in-sub-block terms, so carrying partial outputs
+    // between groups costs more than one workgroup per CU does)
+    d.Lg = (s.P == 4 && s.causal) ? 16 : 128 / d.Pp;
     d.G = (s.L + d.Lg - 1) / d.Lg;
     const int Lfull = d.G > 1 ? d.Lg : s.L;
     d.Ll = s.L - (d.G - 1) * d.Lg;
