@@ -49,9 +49,13 @@
  *     default stream). Argument errors are reported synchronously, before any
  *     device work is enqueued. Device faults surface at the caller's next
  *     synchronisation.
- *   - Supported: d = 64; 1 <= P <= 4; L >= 1 with L * P' <= 128 where P' is P
- *     rounded up to a power of two; N >= 1; B, H >= 1; 1 <= chunk <= 2^20; dtype
- *     RACE_F32 or RACE_BF16. Other shapes return RACE_ERR_UNSUPPORTED.
+ *   - Supported: d = 64; 1 <= P <= 6 (P = 6 with RACE_BF16 inputs only); L >= 1
+ *     with L * 2^P <= 65536; N >= 1; B, H >= 1 with B * H <= 65535;
+ *     1 <= chunk <= 2^20; dtype RACE_F32 or RACE_BF16. Other shapes return
+ *     RACE_ERR_UNSUPPORTED. Many tables run as consecutive groups of at most
+ *     256 features (P = 4, causal: 16 tables; P = 5: 8; P = 6: 4; otherwise
+ *     128 projection rows), one launch per group and pass, whose partial
+ *     outputs add up in float32 before the last group finishes them.
  *   - Numerics: bf16 inputs are multiplied on bf16 matrix cores with float32
  *     accumulation; float32 inputs use float32 matrix cores throughout.
  *     Sketch states and all reductions are float32. No atomics are used on

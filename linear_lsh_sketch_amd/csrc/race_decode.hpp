@@ -55,10 +55,17 @@ struct DecodeArgs {
 
 // Table and subset of canonical feature f (lane group g of 32-feature chunk
 // kc holds features 8 g .. 8 g + 7 of the tables of its projection rows).
+// P = 5, 6: a table spans two lane groups, the even one holding the subsets
+// without the top plane, the odd one those with it.
 __device__ inline void feature_table_subset(int f, int P, int KB, int TPT, int TPL, int& table, int& subset) {
     const int kc = f >> 5, g = (f >> 3) & 3, j = f & 7;
     const int jj = j + 8 * (kc % KB);
     const int R = 1 << P;
+    if (P >= 5) {
+        table = (kc / KB) * TPT + (g >> 1);
+        subset = jj + (g & 1) * (R >> 1);
+        return;
+    }
     table = (kc / KB) * TPT + g * TPL + jj / R;
     subset = jj % R;
 }

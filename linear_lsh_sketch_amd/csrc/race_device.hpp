@@ -216,11 +216,15 @@ struct Cfg {
     static constexpr int P = P_;
     static constexpr int MT = MT_;          // projection tiles of 16 rows
     static constexpr bool F32 = F32_;
-    static constexpr int Pp = (P == 3) ? 4 : P;   // planes per table, padded
+    // planes per table, padded: 1, 2, 4, or 8 (P = 5, 6: a table spans two
+    // lane groups, planes 0-3 in the even one and 4-7 in the odd one)
+    static constexpr int Pp = P <= 2 ? P : (P <= 4 ? 4 : 8);
     static constexpr int R = 1 << P;
-    static constexpr int TPL = 4 / Pp;            // tables per lane group per tile
+    static constexpr int TPL = Pp <= 4 ? 4 / Pp : 0;   // tables per lane group per tile (Pp = 8: half a table)
     static constexpr int TPT = 16 / Pp;           // tables per tile
-    static constexpr int KB = (P == 4) ? 2 : 1;   // 32-wide feature chunks per tile
+    // 32-wide feature chunks per tile: a lane group holds 8 KB features of
+    // each of its tables (P = 5, 6: half of the table's 2^P monomials)
+    static constexpr int KB = P == 6 ? 4 : (P == 4 || P == 5) ? 2 : 1;
     static constexpr int NKC = MT * KB;           // feature chunks
     static constexpr int F = 32 * NKC;            // padded feature count
     static constexpr int FBK0 = FBK_OVERRIDE ? FBK_OVERRIDE : (F32 ? KB : 4);  // chunks per feature block
@@ -250,9 +254,18 @@ struct Cfg {
 template <class C>
 __device__ inline void row_table(int t, int ri, int& table, int& plane) {
     const int g = ri >> 2, i = ri & 3;
-    table = t * C::TPT + g * C::TPL + i / C::Pp;
-    plane = i % C::Pp;
+    if constexpr (C::Pp == 8) {
+        table = t * C::TPT + (g >> 1);
+        plane = 4 * (g & 1) + i;
+    } else {
+        table = t * C::TPT + g * C::TPL + i / C::Pp;
+        plane = i % C::Pp;
+    }
 }
+
+// P = 5, 6: the plane values of the partner lane group (the other half of the
+// lane's tables: lanes l and l ^ 16 hold the same token).
+__device__ inline float partner(float x) { return __shfl_xor(x, 16); }
 
 // tanh(x) = 1 - 2 / (1 + e^{2x}), with the exponent scale c = 2 log2(e)
 // times any factor folded into x: e^{2x} overflows to +inf for large x (then
@@ -317,9 +330,41 @@ __device__ inline void tplanes(const typename Prec<F32>::uvec& uv, float beta, f
 // read-out subtracts n_pad times the empty-subset row). Tokens past the end
 // of the chunk load zero plane values (finite features); their value and
 // mass rows are zero and the in-sub-block terms mask them.
+// P = 5, 6 (two lane groups per table): the even group holds the subsets
+// without the top plane P - 1, the odd group those with it; within a group
+// feature jj is the subset jj (+ 2^(P-1) in the odd group), i.e. the
+// monomial over planes 0-3 of jj % 16, times t_4 when P = 6 and jj >= 16,
+// times t_(P-1) in the odd group. tA: planes 0-3, tB: planes 4, 5.
 template <class C>
-__device__ inline void monomial_features(const float tt[4], float phi[C::KB * 8]) {
-    if constexpr (C::P == 4) {
+__device__ inline void split_planes(const float tt[4], int g, float tA[4], float tB[2]) {
+    float pt[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pt[i] = partner(tt[i]);
+    const bool odd = g & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tA[i] = odd ? pt[i] : tt[i];
+    tB[0] = odd ? tt[0] : pt[0];
+    tB[1] = odd ? tt[1] : pt[1];
+}
+
+template <class C>
+__device__ inline void quad_monomials(const float t[4], float A[16]) {
+    const float lo[4] = {1.f, t[0], t[1], t[0] * t[1]};   // subsets of planes {0, 1}
+    const float hi[4] = {1.f, t[2], t[3], t[2] * t[3]};   // subsets of planes {2, 3}
+#pragma unroll
+    for (int r = 0; r < 16; ++r) A[r] = (r >> 2) == 0 ? lo[r & 3] : (r & 3) == 0 ? hi[r >> 2] : lo[r & 3] * hi[r >> 2];
+}
+
+template <class C>
+__device__ inline void monomial_features(const float tt[4], float phi[C::KB * 8], int g = 0) {
+    if constexpr (C::Pp == 8) {
+        float tA[4], tB[2], A[16];
+        split_planes<C>(tt, g, tA, tB);
+        quad_monomials<C>(tA, A);
+        const float top = (g & 1) ? (C::P == 6 ? tB[1] : tB[0]) : 1.f;
+#pragma unroll
+        for (int jj = 0; jj < C::KB * 8; ++jj) phi[jj] = A[jj & 15] * (C::P == 6 && jj >= 16 ? tB[0] * top : top);
+    } else if constexpr (C::P == 4) {
         const float lo[4] = {1.f, tt[0], tt[1], tt[0] * tt[1]};   // subsets of planes {0, 1}
         const float hi[4] = {1.f, tt[2], tt[3], tt[2] * tt[3]};   // subsets of planes {2, 3}
 #pragma unroll
@@ -349,10 +394,57 @@ __device__ inline int padded_tables(int L) { return C::MT * C::TPT - L; }
 // subset carries no gradient.
 template <class C>
 __device__ inline void monomial_backward(const float dA[C::KB * 8], const float tt[4], const float gt[4],
-                                         float dh[4]) {
+                                         float dh[4], int g = 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) dh[i] = 0.f;
-    if constexpr (C::P == 4) {
+    if constexpr (C::Pp == 8) {
+        // this lane's features give part of dL/dt for planes 0-5; the partner
+        // lane's give the rest; each lane keeps its own rows' sum
+        float tA[4], tB[2], A[16];
+        split_planes<C>(tt, g, tA, tB);
+        quad_monomials<C>(tA, A);
+        const bool odd = g & 1;
+        const float top = odd ? (C::P == 6 ? tB[1] : tB[0]) : 1.f;
+        // e[a] = d/dA_a of this lane's features; S0, S1 = sums against A
+        float e[16], S0 = 0.f, S1 = 0.f;
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+            const float d0 = dA[a];
+            const float d1 = C::P == 6 ? dA[a + 16] : 0.f;
+            e[a] = (d0 + d1 * tB[0]) * top;
+            S0 += d0 * A[a];
+            S1 += d1 * A[a];
+        }
+        // planes 0-3: the P = 4 chain rule of the quad monomials against e
+        const float t01 = tA[0] * tA[1], t23 = tA[2] * tA[3];
+        float Ra[4], Cb[4];
+#pragma unroll
+        for (int a = 1; a < 4; ++a) Ra[a] = e[a] + e[a + 4] * tA[2] + e[a + 8] * tA[3] + e[a + 12] * t23;
+#pragma unroll
+        for (int b = 1; b < 4; ++b) Cb[b] = e[4 * b] + e[4 * b + 1] * tA[0] + e[4 * b + 2] * tA[1] + e[4 * b + 3] * t01;
+        float dt[6];
+        dt[0] = Ra[1] + Ra[3] * tA[1];
+        dt[1] = Ra[2] + Ra[3] * tA[0];
+        dt[2] = Cb[1] + Cb[3] * tA[3];
+        dt[3] = Cb[2] + Cb[3] * tA[2];
+        if constexpr (C::P == 6) {
+            dt[4] = S1 * top;                          // features with plane 4 (jj >= 16)
+            dt[5] = odd ? S0 + S1 * tB[0] : 0.f;       // the odd group's features all hold plane 5
+        } else {
+            dt[4] = odd ? S0 : 0.f;                    // the odd group's features all hold plane 4
+            dt[5] = 0.f;
+        }
+        float tot[6];
+#pragma unroll
+        for (int p = 0; p < 6; ++p) tot[p] = dt[p] + partner(dt[p]);
+        if (odd) {
+            dh[0] = tot[4] * gt[0];
+            dh[1] = C::P == 6 ? tot[5] * gt[1] : 0.f;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dh[i] = tot[i] * gt[i];
+        }
+    } else if constexpr (C::P == 4) {
         // subset r = a + 4 b, a over planes {0, 1}, b over planes {2, 3}
         const float t01 = tt[0] * tt[1], t23 = tt[2] * tt[3];
         float Ra[4], Cb[4];   // Ra[a] = sum_b dA[a + 4b] hi_b, Cb[b] = sum_a dA[a + 4b] lo_a
@@ -387,9 +479,10 @@ __device__ inline void monomial_backward(const float dA[C::KB * 8], const float 
 }
 
 // True when lane feature (h, i) of accumulator tile pair kc (feature
-// j = 4 h + i of the chunk) is the empty subset of its table.
+// j = 4 h + i of the chunk) in lane group g is the empty subset of its table.
 template <class C>
-__device__ constexpr bool is_empty_subset(int kc, int h, int i) {
+__device__ constexpr bool is_empty_subset(int kc, int g, int h, int i) {
+    if constexpr (C::Pp == 8) return (g & 1) == 0 && (kc % C::KB) == 0 && h == 0 && i == 0;
     return C::P == 4 ? ((kc % C::KB) == 0 && h == 0 && i == 0) : ((4 * h + i) % C::R) == 0;
 }
 

@@ -69,6 +69,12 @@ race_status_t with_cfg(int P, int MT, Fn&& fn) {
     RACE_CFG(2, 1) RACE_CFG(2, 2) RACE_CFG(2, 4) RACE_CFG(2, 8)
     RACE_CFG(3, 1) RACE_CFG(3, 2) RACE_CFG(3, 4) RACE_CFG(3, 8)
     RACE_CFG(4, 1) RACE_CFG(4, 2) RACE_CFG(4, 4) RACE_CFG(4, 8)
+    RACE_CFG(5, 1) RACE_CFG(5, 2) RACE_CFG(5, 4)
+    // P = 6 in float32: a tile's 128 features per lane group, double-buffered
+    // for 64 tokens, do not fit the 160 KB of LDS
+    if constexpr (!F32) {
+        RACE_CFG(6, 1) RACE_CFG(6, 2)
+    }
 #undef RACE_CFG
     return RACE_ERR_UNSUPPORTED;
 }
@@ -121,8 +127,9 @@ enum { PASS_FWD = 0, PASS_BWD_Q = 1, PASS_BWD_V = 2, PASS_BWD_K = 3 };
 
 // The forward and the query-side backward use feature blocks of two chunks in
 // bf16 (smaller LDS tiles and operand sets, so two workgroups fit on a CU).
+// (P = 6 holds four chunks per tile: its blocks are whole tiles.)
 template <class C>
-using Blk2Cfg = Cfg<C::P, C::MT, C::F32, C::F32 ? 0 : 2>;
+using Blk2Cfg = Cfg<C::P, C::MT, C::F32, C::F32 ? 0 : (C::KB > 2 ? C::KB : 2)>;
 
 template <class C, int KIND>
 race_status_t run_pass(const Shape& s, const Derived& d, PassArgs a, hipStream_t st) {

@@ -95,18 +95,20 @@ inline bool mul_ok(int64_t a, int64_t b, int64_t& out) {
 inline race_status_t derive(const Shape& s, Derived& d) {
     if (s.B < 1 || s.H < 1 || s.N < 1 || s.d < 1 || s.P < 1 || s.L < 1 || s.chunk < 1)
         return RACE_ERR_INVALID_ARG;
-    if (s.d != 64 || s.P > 4) return RACE_ERR_UNSUPPORTED;
+    if (s.d != 64 || s.P > 6) return RACE_ERR_UNSUPPORTED;
     // in-chunk byte offsets (rows of up to 512 bytes) are 32-bit
     if (s.chunk > MAX_CHUNK) return RACE_ERR_UNSUPPORTED;
-    d.Pp = (s.P == 3) ? 4 : s.P;
+    // planes per table padded to 1, 2, 4 or 8 (P = 5, 6: two lane groups)
+    d.Pp = s.P <= 2 ? s.P : (s.P <= 4 ? 4 : 8);
     if ((int64_t)s.L << s.P > MAX_FEATURES) return RACE_ERR_UNSUPPORTED;
-    d.KB = (s.P == 4) ? 2 : 1;
+    d.KB = s.P == 6 ? 4 : (s.P == 4 || s.P == 5) ? 2 : 1;
     // tables per group: P = 4, causal: up to 16 (four projection tiles, 256
     // features: the state fits two workgroups per CU, which pays more than the
-    // partial outputs cost); otherwise up to 128 projection rows (the
-    // non-causal passes have no in-sub-block terms, so carrying partial outputs
-    // between groups costs more than one workgroup per CU does)
-    d.Lg = (s.P == 4 && s.causal) ? 16 : 128 / d.Pp;
+    // partial outputs cost); P = 5, 6: 256 features (8 and 4 tables);
+    // otherwise up to 128 projection rows (the non-causal passes have no
+    // in-sub-block terms, so carrying partial outputs between groups costs
+    // more than one workgroup per CU does)
+    d.Lg = s.P == 6 ? 4 : s.P == 5 ? 8 : (s.P == 4 && s.causal) ? 16 : 128 / d.Pp;
     d.G = (s.L + d.Lg - 1) / d.Lg;
     const int Lfull = d.G > 1 ? d.Lg : s.L;
     d.Ll = s.L - (d.G - 1) * d.Lg;

@@ -614,7 +614,7 @@ __device__ inline void block_features(const WS& wsrc, int fb, int lane, int w, i
         tanh4(hs, inv, u);
         const typename Prec<C::F32>::uvec uq = round_u<C::F32>(u);
         tplanes<C::F32>(uq, beta, tt, gt);
-        monomial_features<C>(tt, phi);
+        monomial_features<C>(tt, phi, g);
         store_u<C>(out, rowi, t, g, uq);
         emit_tile<C, KEEP>(tb, w, ln, g, phi, rows, phi_frag);
     }
@@ -632,7 +632,7 @@ __device__ inline void block_features_cached(const Planes<C>& pl, int fb, int w,
         const int t = fb * C::TPB + tb;
         float tt[4], gt[4], phi[C::KB * 8];
         tplanes<C::F32>(pl.u[tb], beta, tt, gt);
-        monomial_features<C>(tt, phi);
+        monomial_features<C>(tt, phi, g);
         if constexpr (KEEP) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -1006,11 +1006,11 @@ __device__ inline void load_wtp(int t, int lane, const typename Prec<C::F32>::el
 // them), then, when t completes a tile pair, the back-projection
 // dX += W'^T dh with the operands wf of load_wtp.
 template <class C>
-__device__ inline void chain_backproject(int t, const float dA[C::KB * 8], const float tt[4], const float gt[4],
-                                         const typename Prec<C::F32>::frag (&wf)[4], f32x4 (&dhp)[2],
-                                         f32x4 (&dX)[4]) {
+__device__ inline void chain_backproject(int t, int g, const float dA[C::KB * 8], const float tt[4],
+                                         const float gt[4], const typename Prec<C::F32>::frag (&wf)[4],
+                                         f32x4 (&dhp)[2], f32x4 (&dX)[4]) {
     float dh[4];
-    monomial_backward<C>(dA, tt, gt, dh);
+    monomial_backward<C>(dA, tt, gt, dh, g);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dhp[t & 1][i] = dh[i];
     if (completes_pair<C>(t)) {
@@ -1163,11 +1163,11 @@ struct WStage {
 // Matrix-core operand of state tile pair kc with the rows of the empty subset
 // set to zero (the forward read-out adds their contribution in float32).
 template <class C>
-__device__ inline typename Prec<C::F32>::frag pack_nonempty(int kc, f32x4 lo, f32x4 hi) {
+__device__ inline typename Prec<C::F32>::frag pack_nonempty(int kc, int g, f32x4 lo, f32x4 hi) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        if (is_empty_subset<C>(kc, 0, i)) lo[i] = 0.f;
-        if (is_empty_subset<C>(kc, 1, i)) hi[i] = 0.f;
+        if (is_empty_subset<C>(kc, g, 0, i)) lo[i] = 0.f;
+        if (is_empty_subset<C>(kc, g, 1, i)) hi[i] = 0.f;
     }
     return pack<C::F32>(lo, hi);
 }
@@ -1188,8 +1188,10 @@ struct FwdLds {
     static constexpr int o_sc = o_zr + n_zr;
     static constexpr int o_w = o_sc + n_sc;
     static constexpr int n_float = 4 * TB + TB + TB;            // Dpart, Dint, 1 / D
-    // two workgroups per CU (VGPR budget 256: two waves share each SIMD)
-    static constexpr int OCC = (!C::F32 && C::NKC <= 8) ? 2 : 1;
+    // two workgroups per CU (VGPR budget 256: two waves share each SIMD) where
+    // the tiles fit twice in the LDS
+    static constexpr int OCC =
+        (!C::F32 && C::NKC <= 8 && (o_w * (int)sizeof(elem) + n_float * 4) * 2 <= 160 * 1024) ? 2 : 1;
     using WS = WStage<elem, o_w, n_float, C::MT, OCC>;
 };
 
@@ -1337,14 +1339,14 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
 #pragma unroll
             for (int kcl = 0; kcl < C::FBK; ++kcl) {
                 const int kc = fb * C::FBK + kcl;
-                const frag mf = pack_nonempty<C>(kc, Macc[2 * kc], Macc[2 * kc + 1]);
+                const frag mf = pack_nonempty<C>(kc, g, Macc[2 * kc], Macc[2 * kc + 1]);
 #pragma unroll
                 for (int at = 0; at < 4; ++at)
                     Y[at] = mma(mf, ld_frag<C::F32>(rows_b + (16 * at + ln) * C::ROWF + 32 * kcl + 8 * g), Y[at]);
             }
             const int kw = w - C::own_base(fb);
             if (kw >= 0 && kw < C::FBK) {
-                const frag zf = pack_nonempty<C>(fb * C::FBK + kw, Zacc[2 * C::zidx(fb)], Zacc[2 * C::zidx(fb) + 1]);
+                const frag zf = pack_nonempty<C>(fb * C::FBK + kw, g, Zacc[2 * C::zidx(fb)], Zacc[2 * C::zidx(fb) + 1]);
 #pragma unroll
                 for (int at = 0; at < 4; ++at)
                     Dacc[at] = mma(ld_frag<C::F32>(rows_b + (16 * at + ln) * C::ROWF + 32 * kw + 8 * g), zf, Dacc[at]);
@@ -1611,7 +1613,7 @@ __attribute__((amdgpu_waves_per_eu(BwdQLds<C>::OCC, BwdQLds<C>::OCC))) void k_bw
                         dA[kb * 8 + 4 + i] = G[2 * kcl + 1][i];
                     }
                 }
-                chain_backproject<C>(t, dA, tt, gt, wf[tb], dhp, dX);
+                chain_backproject<C>(t, g, dA, tt, gt, wf[tb], dhp, dX);
             }
             if (causal) sketch_update<C, true, C::ROWE, false, TR>(fb, w, ln, g, cols_b, s_zr, Macc, Zacc);
         }
@@ -1886,7 +1888,7 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
                             dA[kb * 8 + 4 + i] = G[2 * kcl + 1][i];
                         }
                     }
-                    chain_backproject<C>(t, dA, tt, gt, wf[tb], dhp, dX);
+                    chain_backproject<C>(t, g, dA, tt, gt, wf[tb], dhp, dX);
                 }
             }
             if (causal) sketch_update<C, DK, LD::ZS, DV, TR>(fb, w, ln, g, DV ? brow_b : cols_b, s_zr, Macc, Zacc);
@@ -1957,6 +1959,22 @@ __global__ __launch_bounds__(NT) void k_hash(const void* X, const void* Wv, int6
 #pragma unroll
     for (int t = 0; t < C::MT; ++t) {
         const f32x4 acc = project_global<C>(W, L, t, ln, g, xf);
+        if constexpr (C::Pp == 8) {
+            // a table's planes 0-3 in the even lane group, 4-7 in the odd one
+            const int table = t * C::TPT + (g >> 1);
+            int bits = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int plane = 4 * (g & 1) + i;
+                if (plane >= C::P) continue;
+                const float h = acc[i];
+                if (h > 0.f) bits |= 1 << plane;
+                if (valid && table < L && fabsf(h * inv) < NEAR_ZERO) ++nz;
+            }
+            const int id = bits | __shfl_xor(bits, 16);
+            if (valid && table < L && (g & 1) == 0) ids[(size_t)r * ld + table] = id;
+            continue;
+        }
 #pragma unroll
         for (int tl = 0; tl < C::TPL; ++tl) {
             const int table = t * C::TPT + g * C::TPL + tl;

@@ -117,7 +117,7 @@ def test_workspace_kind_rejected():
     ((0, 1, 10, 64, 4, 8, 1, 16, 0), race.RACE_ERR_INVALID_ARG),        # B = 0
     ((1, 1, 0, 64, 4, 8, 1, 16, 0), race.RACE_ERR_INVALID_ARG),         # N = 0
     ((1, 1, 10, 32, 4, 8, 1, 16, 0), race.RACE_ERR_UNSUPPORTED),        # d != 64
-    ((1, 1, 10, 64, 5, 8, 1, 16, 0), race.RACE_ERR_UNSUPPORTED),        # P > 4
+    ((1, 1, 10, 64, 7, 8, 1, 16, 0), race.RACE_ERR_UNSUPPORTED),        # P > 6
     ((1, 1, 10, 64, 0, 8, 1, 16, 0), race.RACE_ERR_INVALID_ARG),        # P = 0
     ((1, 1, 10, 64, 4, 4097, 1, 16, 0), race.RACE_ERR_UNSUPPORTED),     # L * 2^P > 2^16
     ((1, 1, 10, 64, 4, 8, 1, 0, 0), race.RACE_ERR_INVALID_ARG),         # chunk = 0
@@ -156,6 +156,17 @@ def test_forward_argument_errors_before_device_work():
     assert L.race_attn_fwd(*bad, need, None) == race.RACE_ERR_UNSUPPORTED
 
 
+def test_p6_float32_rejected_before_device_work():
+    # P = 6 runs on bf16 inputs only; float32 is refused after the shape
+    # checks and before any launch (the pointers here are never dereferenced)
+    L = race.lib()
+    need = race.workspace_bytes(1, 1, 100, 64, 6, 4, True, 64, race.WS_FWD)
+    args = (FAKE, FAKE, FAKE, FAKE, 1, 1, 100, 64, 6, 4, 1.0, 1, 64, race.RACE_F32, FAKE, None, FAKE, need, None)
+    assert L.race_attn_fwd(*args) == race.RACE_ERR_UNSUPPORTED
+    assert L.race_attn_hash(FAKE, FAKE, 1, 1, 10, 64, 6, 4, race.RACE_F32, FAKE, FAKE, None) == \
+        race.RACE_ERR_UNSUPPORTED
+
+
 def test_backward_and_hash_argument_errors():
     L = race.lib()
     need = race.workspace_bytes(1, 1, 100, 64, 4, 8, False, 64, race.WS_BWD_RECOMPUTE)
@@ -181,7 +192,7 @@ def test_backward_and_hash_argument_errors():
         race.RACE_ERR_INVALID_ARG
     assert L.race_attn_hash(FAKE, FAKE, 1, 1, 10, 64, 4, 8, race.RACE_F32, None, FAKE, None) == \
         race.RACE_ERR_INVALID_ARG
-    assert L.race_attn_hash(FAKE, FAKE, 1, 1, 10, 64, 6, 8, race.RACE_F32, FAKE, FAKE, None) == \
+    assert L.race_attn_hash(FAKE, FAKE, 1, 1, 10, 64, 7, 8, race.RACE_F32, FAKE, FAKE, None) == \
         race.RACE_ERR_UNSUPPORTED
 
 
@@ -192,7 +203,7 @@ def test_state_bytes():
         assert race.state_bytes(B, H, P, L) == B * H * F * 65 * 4
     out = ctypes.c_size_t(0)
     assert race.lib().race_attn_state_bytes(1, 1, 128, 4, 8, ctypes.byref(out)) == race.RACE_ERR_UNSUPPORTED
-    assert race.lib().race_attn_state_bytes(1, 1, 64, 5, 8, ctypes.byref(out)) == race.RACE_ERR_UNSUPPORTED
+    assert race.lib().race_attn_state_bytes(1, 1, 64, 7, 8, ctypes.byref(out)) == race.RACE_ERR_UNSUPPORTED
     assert race.lib().race_attn_state_bytes(0, 1, 64, 4, 8, ctypes.byref(out)) == race.RACE_ERR_INVALID_ARG
     assert race.lib().race_attn_state_bytes(1, 1, 64, 4, 8, None) == race.RACE_ERR_INVALID_ARG
 
@@ -221,7 +232,7 @@ def test_prefill_and_decode_argument_errors():
         assert L.race_attn_decode(*bad, None) == race.RACE_ERR_INVALID_ARG, i
     bad = list(dec); bad[6] = 1 << 31   # more tokens than a 32-bit count
     assert L.race_attn_decode(*bad, None) == race.RACE_ERR_UNSUPPORTED
-    for i, v in [(7, 32), (8, 5), (9, 4097)]:
+    for i, v in [(7, 32), (8, 7), (9, 4097)]:
         bad = list(dec); bad[i] = v
         assert L.race_attn_decode(*bad, None) == race.RACE_ERR_UNSUPPORTED, i
 

@@ -88,9 +88,11 @@ def check(res, ref, dtype, label):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("P,L", [(4, 16), (2, 8), (3, 5), (1, 3), (4, 5), (4, 32), (2, 64), (1, 100), (4, 40),
-                                 (2, 70)])
+                                 (2, 70), (5, 8), (5, 11), (6, 4), (6, 9)])
 @pytest.mark.parametrize("n0", [0, 1, 301])
 def test_decode_soft_matches_oracle(lib, dtype, P, L, n0):
+    if P == 6 and dtype == "f32":
+        pytest.skip("P = 6 runs on bf16 inputs only")
     # (4, 32): the largest state, F = 512 = one thread per feature; (2, 64),
     # (1, 100): 128 and 100 projection rows, eight projection tiles
     T, B, H, beta, chunk = 5, 2, 3, 1.0, 64
