@@ -118,6 +118,14 @@ def test_bf16_noncausal_padded_tables(lib, P, L):
     run_case(lib, 2, 2, 300, P, L, "bf16", False, 64, beta=1.2, seed=31 + L)
 
 
+@pytest.mark.parametrize("beta", [0.5, 4.0, 16.0])
+@pytest.mark.parametrize("dtype,causal,P,L", [("bf16", True, 4, 16), ("f32", False, 2, 8), ("bf16", True, 5, 8)])
+def test_temperature_sweep(lib, beta, dtype, causal, P, L):
+    # the temperatures of the pages' bias / variance trade-off (soft at 0.5,
+    # nearly hard at 16), fwd + bwd against the oracle
+    run_case(lib, 1, 2, 600, P, L, dtype, causal, 256, beta=beta, seed=61)
+
+
 @pytest.mark.parametrize("N,chunk", [(1, 1), (63, 1000), (64, 64), (65, 7), (130, 1)])
 def test_edge_lengths(lib, N, chunk):
     run_case(lib, 1, 1, N, 4, 4, "f32", True, chunk, seed=N)

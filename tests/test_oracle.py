@@ -454,6 +454,63 @@ def test_stream_dtypes_and_sampling():
         np.testing.assert_allclose(O[1], ref0, rtol=1e-12, atol=1e-13)
 
 
+def _angular_attention(Q, K, V, P, causal=False):
+    """Brute-force attention with the sharpened angular kernel (1 - theta/pi)^P."""
+    Qh = Q / np.linalg.norm(Q, axis=1, keepdims=True)
+    Kh = K / np.linalg.norm(K, axis=1, keepdims=True)
+    Kt = (1.0 - np.arccos(np.clip(Qh @ Kh.T, -1.0, 1.0)) / np.pi) ** P
+    if causal:
+        Kt = np.tril(Kt)
+    return (Kt @ V) / Kt.sum(axis=1, keepdims=True)
+
+
+def test_beta_sweep_error_falls_with_beta_and_rises_with_P(capsys):
+    """The pages bound the error by a bias of order P / beta plus a variance
+    term that falls with the number of tables (Japanese gist.science page,
+    section 3; Korean page, section 3 item 2). With many tables (4096) the
+    oracle's error against brute-force angular attention (1 - theta/pi)^P
+    falls as beta grows from 0.5 to 4 at every P, and at every beta grows
+    with P; at beta = 64 (nearly hard buckets) only the variance is left."""
+    rng = np.random.default_rng(5)
+    N, d, L = 48, 16, 4096
+    Q, K, V = (rng.standard_normal((N, d)) for _ in range(3))
+    betas = (0.5, 1.0, 2.0, 4.0, 64.0)
+    table = {}
+    for P in (1, 2, 4):
+        ref = _angular_attention(Q, K, V, P)
+        W = rng.standard_normal((L, P, d))
+        table[P] = [float(np.linalg.norm(dense.forward(Q, K, V, W, b, False) - ref) / np.linalg.norm(ref))
+                    for b in betas]
+    with capsys.disabled():
+        print("\n   rel error vs angular attention, L = 4096, beta", betas)
+        for P, row in table.items():
+            print(f"   P={P}:", " ".join(f"{e:.3f}" for e in row))
+    for P, row in table.items():
+        assert row[0] > row[1] > row[2] > row[3], (P, row)      # bias falls with beta
+        assert row[4] < 0.35 * row[0], (P, row)                 # variance floor well below
+    for i in range(4):
+        assert table[1][i] < table[2][i] < table[4][i], i         # and grows with P
+
+
+def test_first_workload_gap_to_angular_attention(capsys):
+    """The first workload (N 512, d 64, P 2, L 8, beta 1, float32 inputs from
+    its seeded stream) against brute-force angular attention: the method's own
+    approximation error at that setting (a flat soft kernel at beta = 1 and
+    the variance of 8 tables), reported, not a parity bar."""
+    seed, N, d, P, L = 20251005, 512, 64, 2, 8
+    Q, K, V = (synth.normal(seed, t, (N, d), "f32").astype(np.float64) for t in (1, 2, 3))
+    W = synth.normal(seed, 0, (L, P, d), "f32").astype(np.float64)
+    O = dense.forward(Q, K, V, W, 1.0, False)
+    ref = _angular_attention(Q, K, V, P)
+    gap = float(np.linalg.norm(O - ref) / np.linalg.norm(ref))
+    many = dense.forward(Q, K, V, np.random.default_rng(1).standard_normal((4096, P, d)), 64.0, False)
+    gap_many = float(np.linalg.norm(many - ref) / np.linalg.norm(ref))
+    with capsys.disabled():
+        print(f"\n   first workload vs angular attention: rel L2 {gap:.3f} (L 8, beta 1); "
+              f"{gap_many:.3f} at L 4096, beta 64")
+    assert 0.05 < gap < 2.0 and gap_many < 0.5 * gap
+
+
 def test_stream_sampled_backward_equals_unsampled_rows():
     """The sampled backward (rows written on the way, reverse slot mapping
     for the key side, early stop once every sampled row is out) returns
