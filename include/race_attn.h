@@ -113,12 +113,13 @@ race_status_t race_attn_saved_bytes(int64_t B, int64_t H, int64_t N, int d, int 
  * `temperature` is the pages' beta: it multiplies the corner logits, so a
  * larger value gives harder bucket assignments. +INFINITY selects the hard
  * buckets (one-hot of the sign pattern of the projections; the discrete hash
- * the temperature softens: Japanese gist.science page, section 2.2) for
- * RACE_F32 inputs; a query that shares no bucket with any key it attends to
- * then gets O = 0 (the collision counts are exact while 2^P * L times the
- * number of keys stays below 2^24). For RACE_BF16 inputs +INFINITY gives
- * RACE_ERR_UNSUPPORTED (the bf16 read-out operands round the counts), and
- * the backward takes finite temperatures only. NaN and -INFINITY give
+ * the temperature softens: Japanese gist.science page, section 2.2); a
+ * query that shares no bucket with any key it attends to then gets O = 0.
+ * The denominators are exact collision counts (bf16 inputs feed the masses
+ * to the matrix cores in three bf16 parts) while F * N < 2^24, F = the
+ * number of features over all table groups (2^P * L rounded up to whole
+ * projection tiles); beyond that +INFINITY gives RACE_ERR_UNSUPPORTED. The
+ * backward takes finite temperatures only. NaN and -INFINITY give
  * RACE_ERR_INVALID_ARG. `saved` may be NULL; if not
  * NULL it receives the sketch states, denominators and plane values
  * (race_attn_saved_bytes). `ws` must hold race_attn_workspace_bytes(...,

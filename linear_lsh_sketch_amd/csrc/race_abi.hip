@@ -60,6 +60,11 @@ race_status_t prepare(int64_t B, int64_t H, int64_t N, int d, int P, int L, int 
 
 bool dtype_ok(race_dtype_t t) { return t == RACE_F32 || t == RACE_BF16; }
 
+// Hard buckets: the denominator sums F (all groups) products of a mass, an
+// integer of magnitude at most N, and a feature in {-1, 0, 1}, so every
+// partial sum is an exact float32 integer while F * N < 2^24.
+bool hard_exact(const Shape& s, const Derived& dv) { return (dv.F65all / 65) * s.N < (int64_t(1) << 24); }
+
 // Vector loads and stores of 16 bytes need 16-byte aligned tensors.
 bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool all_aligned(std::initializer_list<const void*> ps) {
@@ -142,12 +147,11 @@ race_status_t race_attn_fwd(const void* Q, const void* K, const void* V, const v
         temperature == -INFINITY || !all_aligned({Q, K, V, W, O, ws, saved}))
         return RACE_ERR_INVALID_ARG;
     const bool hard = std::isinf(temperature);
-    // hard buckets: only the float32 read-out keeps the collision counts exact
-    if (hard && dtype != RACE_F32) return RACE_ERR_UNSUPPORTED;
     Shape s;
     Derived dv;
     race_status_t rc = prepare(B, H, N, d, P, L, causal, chunk, s, dv);
     if (rc != RACE_OK) return rc;
+    if (hard && !hard_exact(s, dv)) return RACE_ERR_UNSUPPORTED;
     const WsLayout wl = ws_layout(s, dv, saved ? WS_FWD_SAVED : WS_FWD);
     if (ws_bytes < wl.total) return RACE_ERR_WORKSPACE;
     Call c{};
@@ -164,11 +168,11 @@ race_status_t race_attn_fwd_noalloc(const void* Q, const void* K, const void* V,
         temperature == -INFINITY || !all_aligned({Q, K, V, W, O, saved}))
         return RACE_ERR_INVALID_ARG;
     const bool hard = std::isinf(temperature);
-    if (hard && dtype != RACE_F32) return RACE_ERR_UNSUPPORTED;
     Shape s;
     Derived dv;
     race_status_t rc = prepare(B, H, N, d, P, L, causal, chunk, s, dv);
     if (rc != RACE_OK) return rc;
+    if (hard && !hard_exact(s, dv)) return RACE_ERR_UNSUPPORTED;
     const WsLayout wl = ws_layout(s, dv, saved ? WS_FWD_SAVED : WS_FWD);
     if (wl.total > (size_t)RACE_NOALLOC_SCRATCH_BYTES) return RACE_ERR_WORKSPACE;
     void* ws = nullptr;

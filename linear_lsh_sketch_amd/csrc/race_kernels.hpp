@@ -1346,10 +1346,35 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
             }
             const int kw = w - C::own_base(fb);
             if (kw >= 0 && kw < C::FBK) {
-                const frag zf = pack_nonempty<C>(fb * C::FBK + kw, g, Zacc[2 * C::zidx(fb)], Zacc[2 * C::zidx(fb) + 1]);
+                const int kcz = fb * C::FBK + kw;
+                f32x4 zl = Zacc[2 * C::zidx(fb)], zh = Zacc[2 * C::zidx(fb) + 1];
+                const frag zf = pack_nonempty<C>(kcz, g, zl, zh);
+                frag fa[4];
 #pragma unroll
-                for (int at = 0; at < 4; ++at)
-                    Dacc[at] = mma(ld_frag<C::F32>(rows_b + (16 * at + ln) * C::ROWF + 32 * kw + 8 * g), zf, Dacc[at]);
+                for (int at = 0; at < 4; ++at) {
+                    fa[at] = ld_frag<C::F32>(rows_b + (16 * at + ln) * C::ROWF + 32 * kw + 8 * g);
+                    Dacc[at] = mma(fa[at], zf, Dacc[at]);
+                }
+                if constexpr (!C::F32) {
+                    // hard buckets, bf16 operands: the masses are integers (below
+                    // 2^24) and the features 0 or +-1, so the mass operand goes in
+                    // as three bf16 parts of 8 significant bits each, and the
+                    // denominator comes out exact
+                    if (a.hard) {
+                        frag zp = zf;
+#pragma unroll
+                        for (int part = 0; part < 2; ++part) {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                zl[i] -= (float)zp[i];
+                                zh[i] -= (float)zp[4 + i];
+                            }
+                            zp = pack_nonempty<C>(kcz, g, zl, zh);
+#pragma unroll
+                            for (int at = 0; at < 4; ++at) Dacc[at] = mma(fa[at], zp, Dacc[at]);
+                        }
+                    }
+                }
             }
             if (causal) sketch_update<C, true, ZV, true>(fb, w, ln, g, brow_b, s_zr, Macc, Zacc);
         }

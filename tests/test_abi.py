@@ -144,11 +144,15 @@ def test_forward_argument_errors_before_device_work():
     assert L.race_attn_fwd(*bad, need, None) == race.RACE_ERR_INVALID_ARG
     bad = list(ok); bad[10] = float("-inf")
     assert L.race_attn_fwd(*bad, need, None) == race.RACE_ERR_INVALID_ARG
-    # hard buckets (temperature = +inf): float32 inputs only
+    # hard buckets (temperature = +inf), both dtypes: accepted up to the size
+    # check while F * N < 2^24 (F = 128 features here), refused beyond
     bad = list(ok); bad[10] = float("inf")
-    assert L.race_attn_fwd(*bad, need, None) == race.RACE_ERR_UNSUPPORTED
+    assert L.race_attn_fwd(*bad, need - 1, None) == race.RACE_ERR_WORKSPACE
     bad[13] = race.RACE_F32
-    assert L.race_attn_fwd(*bad, need - 1, None) == race.RACE_ERR_WORKSPACE   # accepted up to the size check
+    assert L.race_attn_fwd(*bad, need - 1, None) == race.RACE_ERR_WORKSPACE
+    bad[6] = 200_000
+    big = race.workspace_bytes(1, 1, 200_000, 64, 4, 8, True, 64, race.WS_FWD)
+    assert L.race_attn_fwd(*bad, big, None) == race.RACE_ERR_UNSUPPORTED
     # workspace too small
     assert L.race_attn_fwd(*ok, need - 1, None) == race.RACE_ERR_WORKSPACE
     # unsupported head dim

@@ -304,10 +304,11 @@ def test_long_sequence_late_tokens(lib, P, L, N):
 
 # --- hard buckets (temperature = +inf), float32 forward --------------------------
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("P,L,N,chunk", [(4, 16, 300, 64), (3, 5, 517, 128), (2, 3, 130, 64), (1, 2, 200, 32),
                                          (4, 20, 300, 64), (5, 3, 200, 64)])
-def test_hard_forward_fp32(lib, causal, P, L, N, chunk):
+def test_hard_forward(lib, dtype, causal, P, L, N, chunk):
     """One-hot buckets through the whole forward: against the oracle's bucket
     sums, with queries that collide with nothing reading exactly 0. Inputs
     keep every projection at least 1e-5 from zero (float32 and float64 then
@@ -316,7 +317,7 @@ def test_hard_forward_fp32(lib, causal, P, L, N, chunk):
     import torch
     from oracle import dense
     for seed in range(900, 960):
-        x = host_inputs(seed, 1, 2, N, 64, P, L, "f32")
+        x = host_inputs(seed, 1, 2, N, 64, P, L, dtype)
         W64 = to_f64(x["W"])
         X = np.concatenate([to_f64(x["Q"]).reshape(-1, 64), to_f64(x["K"]).reshape(-1, 64)])
         h = np.einsum("nd,lpd->nlp", X / np.linalg.norm(X, axis=1, keepdims=True), W64)
@@ -324,7 +325,7 @@ def test_hard_forward_fp32(lib, causal, P, L, N, chunk):
             break
     else:
         pytest.fail("no seed with every projection away from zero")
-    print(f"[case] hard fwd fp32 P={P} L={L} N={N} chunk={chunk} causal={causal} seed={seed}", flush=True)
+    print(f"[case] hard fwd {dtype} P={P} L={L} N={N} chunk={chunk} causal={causal} seed={seed}", flush=True)
     dev = torch.device("cuda:0")
     T = {k: to_torch(v, dev) for k, v in x.items()}
     O = from_torch(lib.forward(T["Q"], T["K"], T["V"], T["W"], P, L, math.inf, causal, chunk))
@@ -334,4 +335,34 @@ def test_hard_forward_fp32(lib, causal, P, L, N, chunk):
     assert np.array_equal(np.all(O == 0.0, axis=-1), zero)
     err = rel_l2(O, ref)
     print(f"   rel_l2 {err:.2e}, zero rows {int(zero.sum())}", flush=True)
-    assert err <= TOL["f32"]
+    assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_hard_forward_many_collisions(lib, dtype):
+    """Hard buckets with masses far beyond bf16's 8-bit integers: 40,000 keys
+    in few buckets (P = 1, L = 2: F = 32 features, F * N below 2^24), against
+    the oracle's collision counts; every denominator is then an exact
+    integer, so O matches to the output rounding."""
+    import math
+    import torch
+    from oracle import dense
+    N, P, L = 40_000, 1, 2
+    for seed in range(700, 760):
+        x = host_inputs(seed, 1, 1, N, 64, P, L, dtype)
+        W64 = to_f64(x["W"])
+        X = np.concatenate([to_f64(x["Q"]).reshape(-1, 64), to_f64(x["K"]).reshape(-1, 64)])
+        h = np.einsum("nd,lpd->nlp", X / np.linalg.norm(X, axis=1, keepdims=True), W64)
+        if np.min(np.abs(h)) > 1e-5:
+            break
+    else:
+        pytest.fail("no seed with every projection away from zero")
+    dev = torch.device("cuda:0")
+    T = {k: to_torch(v, dev) for k, v in x.items()}
+    for causal in (False, True):
+        O = from_torch(lib.forward(T["Q"], T["K"], T["V"], T["W"], P, L, math.inf, causal, 1024))
+        ref = dense.hard_forward(to_f64(x["Q"])[0, 0], to_f64(x["K"])[0, 0], to_f64(x["V"])[0, 0], W64, causal)[None, None]
+        err = rel_l2(O, ref)
+        print(f"[case] hard {dtype} N={N} causal={causal} seed={seed}: rel_l2 {err:.2e}", flush=True)
+        assert np.array_equal(np.all(O == 0.0, axis=-1), np.all(ref == 0.0, axis=-1))
+        assert err <= TOL[dtype]
