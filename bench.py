@@ -208,14 +208,15 @@ def decode_measure(w, dev, steps: int = 200):
     launched one by one from Python and replayed from a HIP graph, and the
     state read-modify-write rate (of the launched calls) against the HBM
     peak. Algorithmic bytes per head and call: the sketch read and written
-    once (2 * L * 2^P * (d + 1) * 4) plus q, k, v in and o out per token."""
+    once (2 * L * 2^P * (4 d + 8): float32 value sums, float64 masses) plus
+    q, k, v in and o out per token."""
     import torch
     import linear_lsh_sketch_amd as race
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     es = 2 if w.dtype == "bf16" else 4
     gen = torch.Generator(device=dev).manual_seed(w.seed)
     W = torch.randn((w.L, w.P, w.d), generator=gen, device=dev).to(tdt)
-    state_rw = 2 * w.L * (1 << w.P) * (w.d + 1) * 4
+    state_rw = 2 * w.L * (1 << w.P) * (w.d * 4 + 8)   # float32 value sums, float64 masses
     res = {"workload": f"decode_P{w.P}_L{w.L}_d{w.d}_{w.dtype}", "heads": [], "tokens_per_call": [],
            "us_per_call": [], "us_per_call_graph": [], "alg_bytes_per_head": [], "GBps": [], "frac_hbm": [],
            "tokens_per_s": [], "tokens_per_s_graph": []}

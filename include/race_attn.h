@@ -176,18 +176,19 @@ race_status_t race_attn_hash(const void *X, const void *W, int64_t B, int64_t H,
  * Efficient key-value caching at inference is the pages' named next use of
  * the sketch (Japanese gist.science page, section 6; Korean page, section 5).
  * The running state of one (batch, head) is the key sketch of every token so
- * far: per feature, the sum of the keys' feature value times [v | 1], in
- * float32, L * 2^P * 65 floats (padded to whole projection tiles) whatever
- * the length. Its layout is private to the library; all-zero bytes are the
- * state of an empty sequence. `temperature` = +INFINITY selects the hard
+ * far: per feature, the sum of the keys' feature value times v (float32) and
+ * the sum of the feature values, the mass (float64, so that counts of more
+ * than 2^24 keys stay exact): L * 2^P * (64 * 4 + 8) bytes (padded to whole
+ * projection tiles) whatever the length. Its layout is private to the
+ * library; all-zero bytes are the state of an empty sequence. `temperature` = +INFINITY selects the hard
  * buckets (the discrete hash that the temperature softens: Japanese
  * gist.science page, section 2.2): each table then adds [v | 1] to exactly
  * one bucket, and a query that shares no bucket with any key outputs zeros.
  * Finite temperatures give the soft assignment of race_attn_fwd. NaN and
  * -INFINITY give RACE_ERR_INVALID_ARG. */
 
-/* Bytes of a running state for B * H heads: float32 [B * H][state floats].
- * Same shape checks as race_attn_fwd. */
+/* Bytes of a running state for B * H heads, [B * H][state bytes], 16-byte
+ * aligned per head. Same shape checks as race_attn_fwd. */
 race_status_t race_attn_state_bytes(int64_t B, int64_t H, int d, int P, int L, size_t *bytes);
 
 /* Prefill: state = the key sketch of the N tokens of K, V ([B, H, N, d],

@@ -263,14 +263,16 @@ def race_attn_hash(X, W, P, L, stream=None):
 
 
 def state_bytes(B, H, P, L, d=64) -> int:
-    """Bytes of the float32 running sketch of B * H heads (race_attn_state_bytes)."""
+    """Bytes of the running sketch of B * H heads (race_attn_state_bytes): per
+    feature float32 value sums and a float64 mass."""
     out = ctypes.c_size_t(0)
     _check(lib().race_attn_state_bytes(B, H, d, P, L, ctypes.byref(out)), "race_attn_state_bytes")
     return out.value
 
 
 def alloc_state(B, H, P, L, device):
-    """A zeroed running sketch (the state of an empty sequence), float32."""
+    """A zeroed running sketch (the state of an empty sequence), held in a
+    float32 tensor of race_attn_state_bytes bytes."""
     import torch
     return torch.zeros(state_bytes(B, H, P, L) // 4, dtype=torch.float32, device=device)
 

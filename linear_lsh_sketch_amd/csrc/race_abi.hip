@@ -227,7 +227,7 @@ race_status_t race_attn_state_bytes(int64_t B, int64_t H, int d, int P, int L, s
     Derived dv;
     race_status_t rc = prepare(B, H, 1, d, P, L, 0, 1, s, dv);
     if (rc != RACE_OK) return rc;
-    *bytes = (size_t)dv.BH * (size_t)dv.F65all * sizeof(float);
+    *bytes = (size_t)dv.BH * (size_t)dv.RSall * sizeof(float);
     return RACE_OK;
 }
 

@@ -9,8 +9,8 @@
 // section 5). temperature = +inf selects the hard buckets of the original
 // discrete hash (Japanese gist.science page, section 2.2): t_p = sign(h_p),
 // so each table's monomials are those of a one-hot corner; a query that
-// collides with no key then reads a zero denominator (exactly, for fewer
-// than 2^24 keys in the state) and outputs zeros.
+// collides with no key then reads a zero denominator (exactly: the masses
+// and the denominator are float64) and outputs zeros.
 //
 // The state has the layout of the kernels' sketch states: F x 64 value sums
 // (row f = canonical feature f) then F masses, F = 32 * MT * KB. Padded
@@ -21,7 +21,7 @@
 // Work per head: one read of the state into registers, then per token one
 // projection of q and of k on the L * P planes, the features, the update of
 // the rows in registers and the read-out from them, and one write of the
-// state at the end: 2 * F * 65 * 4 bytes per call (the bound for T = 1).
+// state at the end: 2 * F * (64 * 4 + 8) bytes per call (the bound for T = 1).
 // No matrix cores: a head's update is an outer product of one feature row
 // and one value row, and the read-out a vector-matrix product over F rows.
 #pragma once
@@ -38,12 +38,13 @@ constexpr int DEC_MAXF = 512;    // largest F of one table group
 static_assert(DEC_MAXF <= DEC_NT, "one thread per feature and mass");
 
 // The running state of a head holds its table groups one after the other,
-// each in the layout of the sketch kernels' states: [F_g x 64 value sums |
-// F_g masses]. Full groups have F features and Lg tables, the last Fl and
-// L - (G - 1) Lg.
+// each as [F_g x 64 float32 value sums | F_g float64 masses] (66 F_g floats;
+// rows in the feature order of the sketch kernels' states): the masses count
+// keys exactly beyond 2^24. Full groups have F features and Lg tables, the
+// last Fl and L - (G - 1) Lg.
 struct DecodeArgs {
     const void *q, *k, *v, *W;
-    float* state;   // [BH][(G - 1) F * 65 + Fl * 65]
+    float* state;   // [BH][(G - 1) F * 66 + Fl * 66]
     void* o;        // [BH][T][64]
     int T;          // new tokens per head (rows of a head in q, k, v, o), processed in order
     int tok;        // k_decode_one: the token of this launch (0 <= tok < T)
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_one(DecodeArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t bh = blockIdx.x;
     const int64_t r = bh * a.T + a.tok;      // row of this token in q, k, v, o
-    const int64_t head_floats = (int64_t)(a.G - 1) * a.F * 65 + (int64_t)a.Fl * 65;
+    const int64_t head_floats = (int64_t)(a.G - 1) * a.F * 66 + (int64_t)a.Fl * 66;
     float* st_head = a.state + (size_t)bh * (size_t)head_floats;
     const int cq = tid & 15, rg = tid >> 4;
     constexpr int WV = 16 / sizeof(elem);   // elements per 16-byte load
@@ -106,14 +107,15 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_one(DecodeArgs a) {
         const int F = lastg ? a.Fl : a.F;
         const int Lgr = lastg ? a.L - (a.G - 1) * a.Lg : a.Lg;
         const int LP = Lgr * a.P;
-        float* st = st_head + (size_t)gi * (size_t)a.F * 65;
+        float* st = st_head + (size_t)gi * (size_t)a.F * 66;
+        double* zs = reinterpret_cast<double*>(st + (size_t)F * DH);
         // The state rows do not depend on this token: their loads are issued
         // first, so their latency overlaps the projections and features.
         f32x4 s[NR];
 #pragma unroll
         for (int i = 0; i < NR; ++i)
             if (rg + DEC_RG * i < F) s[i] = *reinterpret_cast<const f32x4*>(st + (size_t)(rg + DEC_RG * i) * DH + 4 * cq);
-        const float z_old = tid < F ? st[(size_t)F * DH + tid] : 0.f;
+        const double z_old = tid < F ? zs[tid] : 0.0;
         // so are the hyperplane rows: thread (side, row), row = l * P + p of
         // the group, holds all 64 weights of its row, loaded 16 bytes at a time
         const int side = tid / LP, row = tid % LP;
@@ -178,15 +180,15 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_one(DecodeArgs a) {
                 acc += pq * s[i];
             }
         }
-        // masses (F <= DEC_NT: one per thread). The denominator is summed in
+        // masses (F <= DEC_NT: one per thread), and the denominator, in
         // float64: with hard buckets the features are 0 or +-1 and the masses
-        // integers (exact in float32 below 2^24 keys), so the sum is exact and a
-        // query that collides with no key reads exactly 0.
+        // integers, so the sum is exact and a query that collides with no key
+        // reads exactly 0.
         if (tid < F) {
             const float pk = s_phi[1][tid];
-            const float z = z_old + pk;
-            if (pk != 0.f) st[(size_t)F * DH + tid] = z;
-            den += (double)s_phi[0][tid] * (double)z;
+            const double z = z_old + (double)pk;
+            if (pk != 0.f) zs[tid] = z;
+            den += (double)s_phi[0][tid] * z;
         }
     }
 #pragma unroll
@@ -224,7 +226,8 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_multi(DecodeArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t bh = blockIdx.x;
     const int F = a.F, LP = a.L * a.P;
-    float* st = a.state + (size_t)bh * (size_t)F * 65;
+    float* st = a.state + (size_t)bh * (size_t)F * 66;
+    double* zs = reinterpret_cast<double*>(st + (size_t)F * DH);
 
     // The state rows do not depend on the new tokens: their loads are issued
     // first, so their latency overlaps the first token's projections. They
@@ -234,7 +237,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_multi(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < NR; ++i)
         s[i] = *reinterpret_cast<const f32x4*>(st + (size_t)(rg + DEC_RG * i) * DH + 4 * cq);
-    float z = tid < F ? st[(size_t)F * DH + tid] : 0.f;
+    double z = tid < F ? zs[tid] : 0.0;
     // the hyperplanes, once, into LDS (read there for every token)
     for (int e = tid; e < LP * DH; e += DEC_NT) s_w[e / DH][e % DH] = (float)reinterpret_cast<const elem*>(a.W)[e];
     const int side = tid / LP, row = tid % LP;
@@ -307,17 +310,16 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_multi(DecodeArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) s_num[rg][4 * cq + j] = acc[j];
         }
-        // masses (F <= DEC_NT: one per thread). The denominator is summed in
-        // float64: with hard buckets the features are 0 or +-1 and the masses
-        // integers (exact in float32 below 2^24 keys), so the sum is exact and
-        // a query that collides with no key reads exactly 0.
+        // masses (F <= DEC_NT: one per thread) and the denominator in float64:
+        // with hard buckets the features are 0 or +-1 and the masses integers,
+        // so the sum is exact and a query that collides with no key reads
+        // exactly 0.
         {
             double den = 0.0;
             if (tid < F) {
-                const float pk = s_phi[1][tid];
-                z += pk;
-                if (last) st[(size_t)F * DH + tid] = z;
-                den = (double)s_phi[0][tid] * (double)z;
+                z += (double)s_phi[1][tid];
+                if (last) zs[tid] = z;
+                den = (double)s_phi[0][tid] * z;
             }
 #pragma unroll
             for (int m = 1; m < 64; m <<= 1) den += __shfl_xor(den, m);

@@ -33,7 +33,7 @@ struct Call {
     const void* X;                 // hash
     int32_t* ids;                  // hash
     unsigned long long* near_zero; // hash
-    float* state;                  // prefill (out) / decode (in and out): running sketch [BH][F * 65]
+    float* state;                  // prefill (out) / decode (in and out): running sketch [BH][RSall]
     int hard;                      // forward (float32), prefill, decode: one-hot buckets (temperature = +inf)
 };
 
@@ -370,7 +370,10 @@ race_status_t dispatch(const Shape& s, const Derived& d, const WsLayout& wl, con
                 return run_totals<C, false>(s, d, gr, c.K, c.V, nullptr, nullptr, plane_cache(ws + wl.Kc, cl, g),
                                             group_w(c.W, s, gr, F32), beta, Sg, st);
             })));
-            RACE_TRY(run_scan<SCAN_TOTAL>(s, d, gr.F65, Sg, c.state + (size_t)g * d.F65, d.F65all, nullptr, st));
+            profile_mark("state_total", st);
+            hipLaunchKernelGGL(k_state_total<SCAN_TOTAL>, dim3((unsigned)((gr.F65 + 255) / 256), (unsigned)d.BH), dim3(256), 0,
+                               st, Sg, c.state + (size_t)g * d.F * 66, (int)d.NC, gr.F, d.RSall);
+            RACE_TRY(launch_ok());
         }
         return RACE_OK;
     }

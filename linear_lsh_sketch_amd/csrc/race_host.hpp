@@ -32,7 +32,9 @@ struct Derived {
     int64_t F65;   // floats per sketch state: F * 64 value sums + F masses
     int Ll, MTl, Fl, NPLl;   // the last group (equal to the full one when L % Lg == 0)
     int64_t F65l;
-    int64_t F65all;          // all groups of one head (the running state's floats)
+    int64_t F65all;          // all groups of one head (a chunk state's floats)
+    int64_t RSall;           // the running state of one head, in floats: per group F x 64
+                             // float32 value sums and F float64 masses (66 F floats)
     int64_t BH, NC;
 };
 
@@ -134,6 +136,7 @@ inline race_status_t derive(const Shape& s, Derived& d) {
     d.F65 = (int64_t)d.F * 65;
     d.F65l = (int64_t)d.Fl * 65;
     d.F65all = (int64_t)(d.G - 1) * d.F65 + d.F65l;
+    d.RSall = (int64_t)(d.G - 1) * d.F * 66 + (int64_t)d.Fl * 66;
     if (d.BH > 65535 || d.NC > 0x7fffffff) return RACE_ERR_UNSUPPORTED;
     return RACE_OK;
 }

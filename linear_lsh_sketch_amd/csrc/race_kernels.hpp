@@ -821,6 +821,27 @@ __global__ __launch_bounds__(256) void k_scan(float* __restrict__ st, float* __r
     if constexpr (KIND == SCAN_TOTAL) total[(size_t)bh * (size_t)total_stride + e] = run;
 }
 
+// Total of the chunk states of one head and table group into its part of a
+// running decode state: the F x 64 value sums in float32 (the chunk states'
+// type) and the F masses summed and stored in float64, so that counts beyond
+// 2^24 keys stay exact.
+template <int KIND = SCAN_TOTAL>
+__global__ __launch_bounds__(256) void k_state_total(const float* __restrict__ st, float* __restrict__ state,
+                                                     int nchunks, int F, int64_t head_floats) {
+    const int e = blockIdx.x * blockDim.x + threadIdx.x;
+    const int bh = blockIdx.y;
+    if (e >= F * 65) return;
+    const float* p = st + (size_t)bh * nchunks * (size_t)(F * 65) + e;
+    float* out = state + (size_t)bh * (size_t)head_floats;
+    if (e < F * DH) {
+        out[e] = scan_range<SCAN_TOTAL, false>(const_cast<float*>(p), nchunks, F * 65, 0, nchunks, 0.f);
+    } else {
+        double z = 0.0;
+        for (int c = 0; c < nchunks; ++c) z += (double)p[(size_t)c * (F * 65)];
+        reinterpret_cast<double*>(out + (size_t)F * DH)[e - F * DH] = z;
+    }
+}
+
 // Segmented form of the (reverse) exclusive prefix, for grids too small to
 // keep the memory busy (few heads): the logical chunk positions are split
 // into segs segments; k_scan_segsum sums each segment, k_scan_segapply starts

@@ -78,20 +78,21 @@ def test_table_group_sizes():
     B, H, N, chunk = 2, 3, 1000, 128
     rows, nch = B * H * N, -(-N // chunk)
     f65 = (256 * 2 + 128) * 65 * 4
+    f66 = (256 * 2 + 128) * 66 * 4     # running state: float64 masses
     states = B * H * nch * f65
     cache = 2 * _a256(rows * 64 * 4) + _a256(rows * 32 * 4) + _a256(rows * 4)
     saved = race.saved_bytes(B, H, N, 64, 4, 40, True, chunk)
     assert saved == _a256(states) + _a256(rows * 4) + 2 * cache
     # the running state holds the groups one after the other
-    assert race.state_bytes(B, H, 4, 40) == B * H * f65
+    assert race.state_bytes(B, H, 4, 40) == B * H * f66
     # the workspace adds the partial outputs of the groups before the last
     # ([rows][64] and the denominators, float32)
     one = race.workspace_bytes(B, H, N, 64, 4, 16, True, chunk, race.WS_BWD)
     three = race.workspace_bytes(B, H, N, 64, 4, 40, True, chunk, race.WS_BWD)
     assert three >= one + _a256(rows * 64 * 4) + _a256(rows * 4)
     # P < 4: groups of 128 projection rows (P2: 64 tables)
-    assert race.state_bytes(1, 1, 2, 64) == 8 * 32 * 65 * 4
-    assert race.state_bytes(1, 1, 2, 65) == (8 + 1) * 32 * 65 * 4
+    assert race.state_bytes(1, 1, 2, 64) == 8 * 32 * 66 * 4
+    assert race.state_bytes(1, 1, 2, 65) == (8 + 1) * 32 * 66 * 4
 
 
 def test_segmented_scan_workspace():
@@ -201,10 +202,11 @@ def test_backward_and_hash_argument_errors():
 
 
 def test_state_bytes():
-    # F * 65 float32 per head: F = 32 * MT * KB (L16 P4: MT 4, KB 2 -> 256;
-    # L5 P3: 5 tables of 4 padded planes -> MT 2, KB 1 -> 64; L8 P2: MT 1 -> 32)
+    # per head and feature 64 float32 value sums and a float64 mass (66 floats):
+    # F = 32 * MT * KB (L16 P4: MT 4, KB 2 -> 256; L5 P3: 5 tables of 4 padded
+    # planes -> MT 2, KB 1 -> 64; L8 P2: MT 1 -> 32)
     for (B, H, P, L, F) in [(1, 4, 4, 16, 256), (2, 3, 3, 5, 64), (1, 1, 2, 8, 32), (1, 1, 4, 32, 512)]:
-        assert race.state_bytes(B, H, P, L) == B * H * F * 65 * 4
+        assert race.state_bytes(B, H, P, L) == B * H * F * 66 * 4
     out = ctypes.c_size_t(0)
     assert race.lib().race_attn_state_bytes(1, 1, 128, 4, 8, ctypes.byref(out)) == race.RACE_ERR_UNSUPPORTED
     assert race.lib().race_attn_state_bytes(1, 1, 64, 7, 8, ctypes.byref(out)) == race.RACE_ERR_UNSUPPORTED

@@ -203,7 +203,8 @@ def test_decode_graph_replay_matches_eager(lib):
         torch.cuda.synchronize()
         for s in range(T):
             assert torch.equal(outs[s], eager[s]), (rep, s)
-        assert torch.equal(state, eager_state), rep
+        # bitwise (the float64 masses seen through float32 may hold NaN patterns)
+        assert torch.equal(state.view(torch.int32), eager_state.view(torch.int32)), rep
 
 
 def gpu_multi(race, x, n0, T, P, L, beta, chunk):
@@ -266,4 +267,40 @@ def test_decode_several_tokens_equal_single_steps(lib, dtype):
         singles.append(from_torch(lib.decode(q, k, v, t["W"], state, P, L, 1.0)))
     torch.cuda.synchronize()
     assert np.array_equal(multi, np.stack(singles))
-    assert torch.equal(st_multi, state)
+    assert torch.equal(st_multi.view(torch.int32), state.view(torch.int32))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_masses_count_beyond_2_24(lib, dtype):
+    """The running state's masses are float64, so a state that already holds
+    more than 2^24 keys still adds every new key exactly. White-box: the masses
+    of a hard-bucket state (prompt of 40 tokens, P4 L16: one table group, F =
+    256 features, value sums [256 x 64] float32 then 256 float64 masses) are
+    raised by 2^25 + 1 (not a float32 number); one decode step must then change
+    each mass by exactly the new key's feature value (0 or +-1), and the empty
+    subsets by exactly 1."""
+    import torch
+    B, H, P, L, n0 = 1, 2, 4, 16, 40
+    x = host_inputs(77, B, H, n0 + 1, 64, P, L, dtype)
+    dev = torch.device("cuda:0")
+    t = {k: to_torch(v, dev) for k, v in x.items()}
+    state = lib.prefill(t["K"][:, :, :n0].contiguous(), t["V"][:, :, :n0].contiguous(), t["W"], P, L,
+                        math.inf, 64)
+    F = 256
+    per_head = state.numel() // (B * H)
+    assert per_head == F * 66
+    heads = state.view(B * H, per_head)
+    masses = heads[:, F * 64:].contiguous().view(torch.float64)       # [BH, F]
+    offset = float(2 ** 25 + 1)
+    masses += offset
+    heads[:, F * 64:] = masses.view(torch.float32)
+    before = masses.clone()
+    lib.decode(*(t[n][:, :, n0].contiguous() for n in ("Q", "K", "V")), t["W"], state, P, L, math.inf)
+    torch.cuda.synchronize()
+    after = heads[:, F * 64:].contiguous().view(torch.float64)
+    delta = (after - before).cpu().numpy()
+    assert np.all(np.isin(delta, (-1.0, 0.0, 1.0))), np.unique(delta)
+    # the empty subset of each table (feature 32 * (2 t) + 8 g for table 4 t + g)
+    empty = [64 * (tb // 4) + 8 * (tb % 4) for tb in range(L)]
+    assert np.all(delta[:, empty] == 1.0)
+    assert np.all(after.cpu().numpy()[:, empty] == before.cpu().numpy()[:, empty] + 1.0)
