@@ -41,8 +41,9 @@
  *     independent).
  *   - Q, K, V, O, dO, dQ, dK, dV: [B, H, N, d] contiguous row-major, element
  *     type `dtype`. W: [L, P, d] contiguous, element type `dtype`, shared by
- *     queries, keys, batches and heads; it is a fixed random projection and
- *     receives no gradient.
+ *     queries, keys, batches and heads, or [H, L, P, d] (one set per head)
+ *     when RACE_W_PER_HEAD is or'ed into `dtype`; it is a fixed random
+ *     projection and receives no gradient.
  *   - Every tensor pointer (and ws, saved) must be 16-byte aligned, else
  *     RACE_ERR_INVALID_ARG.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
@@ -85,13 +86,20 @@ typedef enum {
 
 typedef enum { RACE_F32 = 0, RACE_BF16 = 1 } race_dtype_t;
 
+/* Or'ed into the dtype argument of any entry point (and into for_backward of
+ * race_attn_workspace_bytes): W is [H, L, P, d], one set of hyperplanes per
+ * head (head h of every batch uses W[h]), instead of one [L, P, d] for all
+ * heads. */
+#define RACE_W_PER_HEAD 0x100
+
 /* Bytes of device workspace `ws` for this shape. Writes *bytes.
  *   for_backward = 0: race_attn_fwd with saved = NULL;
  *   for_backward = 3: race_attn_fwd with a `saved` buffer;
  *   for_backward = 1: race_attn_bwd given O and `saved` from the forward;
  *   for_backward = 2: race_attn_bwd with O = saved = NULL (it then recomputes
  *                     the forward into this workspace);
- * any other value gives RACE_ERR_INVALID_ARG. The size depends on dtype only
+ * any other value gives RACE_ERR_INVALID_ARG; or'ed with RACE_W_PER_HEAD, the
+ * size for per-head hyperplanes. The size depends on dtype only
  * through element sizes, so it is computed for RACE_F32, an upper bound for
  * both dtypes. */
 race_status_t race_attn_workspace_bytes(int64_t B, int64_t H, int64_t N, int d, int P, int L,

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(HERE, "libraceattn.so")
 
 RACE_OK, RACE_ERR_INVALID_ARG, RACE_ERR_UNSUPPORTED, RACE_ERR_WORKSPACE, RACE_ERR_HIP = range(5)
 RACE_F32, RACE_BF16 = 0, 1
+RACE_W_PER_HEAD = 0x100      # or'ed into dtype: W is [H, L, P, d]
 
 SYMBOLS = ("race_attn_workspace_bytes", "race_attn_saved_bytes", "race_attn_fwd",
            "race_attn_fwd_noalloc", "race_attn_bwd", "race_attn_hash", "race_attn_state_bytes", "race_attn_prefill",
@@ -98,6 +99,16 @@ def saved_bytes(B, H, N, d, P, L, causal, chunk) -> int:
     return out.value
 
 
+def _w_flag(W, H, L, P, d):
+    """RACE_W_PER_HEAD for per-head hyperplanes W [H, L, P, d], 0 for shared
+    W [L, P, d]; anything else raises."""
+    if tuple(W.shape) == (L, P, d):
+        return 0
+    if tuple(W.shape) == (H, L, P, d):
+        return RACE_W_PER_HEAD
+    raise ValueError(f"W must be [L, P, d] = {(L, P, d)} or [H, L, P, d] = {(H, L, P, d)}, got {tuple(W.shape)}")
+
+
 def _dtype_code(t):
     import torch
     if t.dtype == torch.float32:
@@ -149,6 +160,7 @@ def _nbytes(t):
 
 
 def alloc_workspace(B, H, N, P, L, causal, chunk, kind, device):
+    """kind: WS_* (or'ed with RACE_W_PER_HEAD for per-head hyperplanes)."""
     import torch
     n = workspace_bytes(B, H, N, 64, P, L, causal, chunk, kind)
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
@@ -166,21 +178,20 @@ def race_attn_fwd(Q, K, V, W, P, L, temperature=1.0, causal=False, chunk=1024, o
     import torch
     _check_inputs(Q, K, V, W)
     B, H, N, d = Q.shape
-    if tuple(W.shape) != (L, P, d):
-        raise ValueError(f"W must be [L, P, d] = {(L, P, d)}, got {tuple(W.shape)}")
+    wf = _w_flag(W, H, L, P, d)
     if K.shape != Q.shape or V.shape != Q.shape:
         raise ValueError("Q, K, V must share one shape")
     if out is not None:
         _check_like(out, Q, "out")
     O = out if out is not None else torch.empty_like(Q)
-    kind = WS_FWD_SAVED if saved is not None else WS_FWD
+    kind = (WS_FWD_SAVED if saved is not None else WS_FWD) | wf
     if saved is not None:
         _check_buf(saved, saved_bytes(B, H, N, d, P, L, causal, chunk), Q.device, "saved")
     if ws is None:
         ws = alloc_workspace(B, H, N, P, L, causal, chunk, kind, Q.device)
     _check_buf(ws, workspace_bytes(B, H, N, d, P, L, causal, chunk, kind), Q.device, "ws")
     code = lib().race_attn_fwd(_p(Q), _p(K), _p(V), _p(W), B, H, N, d, P, L, float(temperature),
-                               int(bool(causal)), chunk, _dtype_code(Q), _p(O), _p(saved), _p(ws),
+                               int(bool(causal)), chunk, _dtype_code(Q) | wf, _p(O), _p(saved), _p(ws),
                                _nbytes(ws), _stream(stream))
     _check(code, "race_attn_fwd")
     return O
@@ -197,15 +208,14 @@ def race_attn_fwd_noalloc(Q, K, V, W, P, L, temperature=1.0, causal=False, chunk
     the caller. Calls that overlap on one GPU share that array and race."""
     _check_inputs(Q, K, V, W)
     B, H, N, d = Q.shape
-    if tuple(W.shape) != (L, P, d):
-        raise ValueError(f"W must be [L, P, d] = {(L, P, d)}, got {tuple(W.shape)}")
+    wf = _w_flag(W, H, L, P, d)
     if K.shape != Q.shape or V.shape != Q.shape:
         raise ValueError("Q, K, V must share one shape")
     _check_like(out, Q, "out")
     if saved is not None:
         _check_buf(saved, saved_bytes(B, H, N, d, P, L, causal, chunk), Q.device, "saved")
     code = lib().race_attn_fwd_noalloc(_p(Q), _p(K), _p(V), _p(W), B, H, N, d, P, L, float(temperature),
-                                       int(bool(causal)), chunk, _dtype_code(Q), _p(out), _p(saved),
+                                       int(bool(causal)), chunk, _dtype_code(Q) | wf, _p(out), _p(saved),
                                        _stream(stream))
     _check(code, "race_attn_fwd_noalloc")
     return out
@@ -221,8 +231,7 @@ def race_attn_bwd(Q, K, V, W, dO, P, L, temperature=1.0, causal=False, chunk=102
     if (O is None) != (saved is None):
         raise ValueError("O and saved are given together or not at all")
     B, H, N, d = Q.shape
-    if tuple(W.shape) != (L, P, d):
-        raise ValueError(f"W must be [L, P, d] = {(L, P, d)}, got {tuple(W.shape)}")
+    wf = _w_flag(W, H, L, P, d)
     if O is not None:
         _check_inputs(Q, O)
         if O.shape != Q.shape:
@@ -236,12 +245,12 @@ def race_attn_bwd(Q, K, V, W, dO, P, L, temperature=1.0, causal=False, chunk=102
     dQ, dK, dV = grads
     for t, nm in ((dQ, "dQ"), (dK, "dK"), (dV, "dV")):
         _check_like(t, Q, nm)
-    kind = WS_BWD if saved is not None else WS_BWD_RECOMPUTE
+    kind = (WS_BWD if saved is not None else WS_BWD_RECOMPUTE) | wf
     if ws is None:
         ws = alloc_workspace(B, H, N, P, L, causal, chunk, kind, Q.device)
     _check_buf(ws, workspace_bytes(B, H, N, d, P, L, causal, chunk, kind), Q.device, "ws")
     code = lib().race_attn_bwd(_p(Q), _p(K), _p(V), _p(W), _p(O), _p(dO), _p(saved), B, H, N, d, P, L,
-                               float(temperature), int(bool(causal)), chunk, _dtype_code(Q), _p(dQ),
+                               float(temperature), int(bool(causal)), chunk, _dtype_code(Q) | wf, _p(dQ),
                                _p(dK), _p(dV), _p(ws), _nbytes(ws), _stream(stream))
     _check(code, "race_attn_bwd")
     return dQ, dK, dV
@@ -252,11 +261,10 @@ def race_attn_hash(X, W, P, L, stream=None):
     import torch
     _check_inputs(X, W)
     B, H, N, d = X.shape
-    if tuple(W.shape) != (L, P, d):
-        raise ValueError(f"W must be [L, P, d] = {(L, P, d)}, got {tuple(W.shape)}")
+    wf = _w_flag(W, H, L, P, d)
     ids = torch.empty((B, H, N, L), dtype=torch.int32, device=X.device)
     nz = torch.zeros(1, dtype=torch.int64, device=X.device)
-    code = lib().race_attn_hash(_p(X), _p(W), B, H, N, d, P, L, _dtype_code(X), _p(ids), _p(nz),
+    code = lib().race_attn_hash(_p(X), _p(W), B, H, N, d, P, L, _dtype_code(X) | wf, _p(ids), _p(nz),
                                 _stream(stream))
     _check(code, "race_attn_hash")
     return ids, nz
@@ -282,8 +290,7 @@ def race_attn_prefill(K, V, W, P, L, temperature=1.0, chunk=1024, state=None, ws
     gives the hard buckets. Returns the state (float32, overwritten)."""
     _check_inputs(K, V, W)
     B, H, N, d = K.shape
-    if tuple(W.shape) != (L, P, d):
-        raise ValueError(f"W must be [L, P, d] = {(L, P, d)}, got {tuple(W.shape)}")
+    wf = _w_flag(W, H, L, P, d)
     if V.shape != K.shape:
         raise ValueError("K and V must share one shape")
     if state is None:
@@ -293,7 +300,7 @@ def race_attn_prefill(K, V, W, P, L, temperature=1.0, chunk=1024, state=None, ws
         ws = alloc_workspace(B, H, N, P, L, False, chunk, WS_FWD, K.device)
     _check_buf(ws, workspace_bytes(B, H, N, d, P, L, False, chunk, WS_FWD), K.device, "ws")
     code = lib().race_attn_prefill(_p(K), _p(V), _p(W), B, H, N, d, P, L, float(temperature), chunk,
-                                   _dtype_code(K), _p(state), _p(ws), _nbytes(ws), _stream(stream))
+                                   _dtype_code(K) | wf, _p(state), _p(ws), _nbytes(ws), _stream(stream))
     _check(code, "race_attn_prefill")
     return state
 
@@ -320,14 +327,13 @@ def race_attn_decode(q, k, v, W, state, P, L, temperature=1.0, out=None, stream=
         raise ValueError("q must be [B, H, d] or [B, H, T, d]")
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must share one shape")
-    if tuple(W.shape) != (L, P, d):
-        raise ValueError(f"W must be [L, P, d] = {(L, P, d)}, got {tuple(W.shape)}")
+    wf = _w_flag(W, H, L, P, d)
     _check_state(state, B, H, P, L, d, q.device)
     o = out if out is not None else torch.empty_like(q)
     if out is not None and (out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous()):
         raise ValueError("out must be a contiguous tensor shaped like q")
     code = lib().race_attn_decode(_p(q), _p(k), _p(v), _p(W), B, H, T, d, P, L, float(temperature),
-                                  _dtype_code(q), _p(state), _p(o), _stream(stream))
+                                  _dtype_code(q) | wf, _p(state), _p(o), _stream(stream))
     _check(code, "race_attn_decode")
     return o
 

@@ -55,10 +55,18 @@ thread_local hipStream_t t_stream = nullptr;
 race_status_t prepare(int64_t B, int64_t H, int64_t N, int d, int P, int L, int causal, int chunk,
                       Shape& s, Derived& dv) {
     s.B = B; s.H = H; s.N = N; s.d = d; s.P = P; s.L = L; s.causal = causal ? 1 : 0; s.chunk = chunk;
+    s.w_per_head = 0;
     return derive(s, dv);
 }
 
-bool dtype_ok(race_dtype_t t) { return t == RACE_F32 || t == RACE_BF16; }
+// The element type, and whether W holds one set of hyperplanes per head
+// (RACE_W_PER_HEAD or'ed into the dtype argument).
+bool dtype_ok(int t) {
+    const int base = t & ~RACE_W_PER_HEAD;
+    return base == RACE_F32 || base == RACE_BF16;
+}
+race_dtype_t base_dtype(int t) { return (race_dtype_t)(t & ~RACE_W_PER_HEAD); }
+int per_head(int t) { return (t & RACE_W_PER_HEAD) ? 1 : 0; }
 
 // Hard buckets: the denominator sums F (all groups) products of a mass, an
 // integer of magnitude at most N, and a feature in {-1, 0, 1}, so every
@@ -82,7 +90,8 @@ race_status_t guarded(race_status_t (*fn)(const Shape&, const Derived&, const Ws
     }
 }
 
-race_status_t go(race_dtype_t dtype, const Shape& s, const Derived& dv, const WsLayout& wl, const Call& c) {
+race_status_t go(race_dtype_t dtype_flags, const Shape& s, const Derived& dv, const WsLayout& wl, const Call& c) {
+    const race_dtype_t dtype = base_dtype(dtype_flags);
     // P = 6 runs on bf16 inputs only (a table's monomials exceed the LDS in float32)
     if (dtype == RACE_F32 && s.P == 6) return RACE_ERR_UNSUPPORTED;
     (void)hipGetLastError();  // clear a stale error so it is not reported as ours
@@ -120,12 +129,14 @@ const char* race_attn_profile_stage(int i) { return (i >= 0 && i < t_count) ? t_
 
 race_status_t race_attn_workspace_bytes(int64_t B, int64_t H, int64_t N, int d, int P, int L, int causal,
                                         int chunk, int for_backward, size_t* bytes) {
-    if (!bytes || for_backward < WS_FWD || for_backward > WS_FWD_SAVED) return RACE_ERR_INVALID_ARG;
+    const int kind = for_backward & ~RACE_W_PER_HEAD;
+    if (!bytes || kind < WS_FWD || kind > WS_FWD_SAVED) return RACE_ERR_INVALID_ARG;
     Shape s;
     Derived dv;
     race_status_t rc = prepare(B, H, N, d, P, L, causal, chunk, s, dv);
     if (rc != RACE_OK) return rc;
-    *bytes = ws_layout(s, dv, for_backward).total;
+    s.w_per_head = per_head(for_backward);
+    *bytes = ws_layout(s, dv, kind).total;
     return RACE_OK;
 }
 
@@ -151,6 +162,7 @@ race_status_t race_attn_fwd(const void* Q, const void* K, const void* V, const v
     Derived dv;
     race_status_t rc = prepare(B, H, N, d, P, L, causal, chunk, s, dv);
     if (rc != RACE_OK) return rc;
+    s.w_per_head = per_head(dtype);
     if (hard && !hard_exact(s, dv)) return RACE_ERR_UNSUPPORTED;
     const WsLayout wl = ws_layout(s, dv, saved ? WS_FWD_SAVED : WS_FWD);
     if (ws_bytes < wl.total) return RACE_ERR_WORKSPACE;
@@ -172,6 +184,7 @@ race_status_t race_attn_fwd_noalloc(const void* Q, const void* K, const void* V,
     Derived dv;
     race_status_t rc = prepare(B, H, N, d, P, L, causal, chunk, s, dv);
     if (rc != RACE_OK) return rc;
+    s.w_per_head = per_head(dtype);
     if (hard && !hard_exact(s, dv)) return RACE_ERR_UNSUPPORTED;
     const WsLayout wl = ws_layout(s, dv, saved ? WS_FWD_SAVED : WS_FWD);
     if (wl.total > (size_t)RACE_NOALLOC_SCRATCH_BYTES) return RACE_ERR_WORKSPACE;
@@ -197,6 +210,7 @@ race_status_t race_attn_bwd(const void* Q, const void* K, const void* V, const v
     Derived dv;
     race_status_t rc = prepare(B, H, N, d, P, L, causal, chunk, s, dv);
     if (rc != RACE_OK) return rc;
+    s.w_per_head = per_head(dtype);
     const WsLayout wl = ws_layout(s, dv, saved ? WS_BWD : WS_BWD_RECOMPUTE);
     if (ws_bytes < wl.total) return RACE_ERR_WORKSPACE;
     Call c{};
@@ -215,6 +229,7 @@ race_status_t race_attn_hash(const void* X, const void* W, int64_t B, int64_t H,
     Derived dv;
     race_status_t rc = prepare(B, H, N, d, P, L, 0, 1, s, dv);
     if (rc != RACE_OK) return rc;
+    s.w_per_head = per_head(dtype);
     Call c{};
     c.op = OP_HASH; c.X = X; c.W = W; c.ids = bucket_ids; c.near_zero = near_zero;
     c.stream = reinterpret_cast<hipStream_t>(stream);
@@ -241,6 +256,7 @@ race_status_t race_attn_prefill(const void* K, const void* V, const void* W, int
     Derived dv;
     race_status_t rc = prepare(B, H, N, d, P, L, 0, chunk, s, dv);
     if (rc != RACE_OK) return rc;
+    s.w_per_head = per_head(dtype);
     const WsLayout wl = ws_layout(s, dv, WS_FWD);
     if (ws_bytes < wl.total) return RACE_ERR_WORKSPACE;
     Call c{};
@@ -259,6 +275,7 @@ race_status_t race_attn_decode(const void* q, const void* k, const void* v, cons
     Derived dv;
     race_status_t rc = prepare(B, H, T, d, P, L, 0, 1, s, dv);
     if (rc != RACE_OK) return rc;
+    s.w_per_head = per_head(dtype);
     if (T > 0x7fffffff) return RACE_ERR_UNSUPPORTED;
     Call c{};
     c.op = OP_DECODE; c.Q = q; c.K = k; c.V = v; c.W = W; c.O = o; c.beta = temperature;

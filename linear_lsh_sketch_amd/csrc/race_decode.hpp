@@ -52,6 +52,8 @@ struct DecodeArgs {
     int G, Lg, Fl;
     float beta;
     int hard;
+    int H;          // heads: W of head bh at W + (bh % H) * w_hs bytes (0: one W for all)
+    int64_t w_hs;
 };
 
 // Table and subset of canonical feature f (lane group g of 32-feature chunk
@@ -121,8 +123,9 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_one(DecodeArgs a) {
         const int side = tid / LP, row = tid % LP;
         wvec wr[DH / WV];
         if (tid < 2 * LP) {
-            const wvec* w = reinterpret_cast<const wvec*>(reinterpret_cast<const elem*>(a.W) +
-                                                          ((size_t)gi * a.Lg * a.P + row) * DH);
+            const wvec* w = reinterpret_cast<const wvec*>(
+                reinterpret_cast<const elem*>(reinterpret_cast<const char*>(a.W) + (bh % a.H) * a.w_hs) +
+                ((size_t)gi * a.Lg * a.P + row) * DH);
 #pragma unroll
             for (int j = 0; j < DH / WV; ++j) wr[j] = w[j];
         }
@@ -239,7 +242,8 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_multi(DecodeArgs a) {
         s[i] = *reinterpret_cast<const f32x4*>(st + (size_t)(rg + DEC_RG * i) * DH + 4 * cq);
     double z = tid < F ? zs[tid] : 0.0;
     // the hyperplanes, once, into LDS (read there for every token)
-    for (int e = tid; e < LP * DH; e += DEC_NT) s_w[e / DH][e % DH] = (float)reinterpret_cast<const elem*>(a.W)[e];
+    const elem* Wh = reinterpret_cast<const elem*>(reinterpret_cast<const char*>(a.W) + (bh % a.H) * a.w_hs);
+    for (int e = tid; e < LP * DH; e += DEC_NT) s_w[e / DH][e % DH] = (float)Wh[e];
     const int side = tid / LP, row = tid % LP;
     // q, k, v rows are loaded one token ahead: thread tid < 3 * 64 holds one
     // element of the next token while the current one is processed

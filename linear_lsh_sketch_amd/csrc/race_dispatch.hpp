@@ -79,6 +79,11 @@ race_status_t with_cfg(int P, int MT, Fn&& fn) {
     return RACE_ERR_UNSUPPORTED;
 }
 
+// Bytes between the hyperplanes of consecutive heads (0: one W for all).
+inline int64_t w_head_bytes(const Shape& s, bool f32) {
+    return s.w_per_head ? (int64_t)s.L * s.P * DH * (f32 ? 4 : 2) : 0;
+}
+
 // CACHED = false: sketch of K, [V | 1] (storing the keys' plane values in pc);
 // CACHED = true: gradient sketch of the queries from their plane values pc.
 template <class C, bool CACHED>
@@ -88,6 +93,7 @@ race_status_t run_totals(const Shape& s, const Derived& d, const Group& gr, cons
     TotArgs a;
     a.Xb = Xb; a.Z = Z; a.Dv = Dv; a.Ev = Ev; a.W = W; a.pc = pc; a.out = out;
     a.N = s.N; a.chunk = s.chunk; a.nchunks = (int)d.NC; a.L = gr.L; a.beta = beta;
+    a.H = (int)s.H; a.w_hs = w_head_bytes(s, C::F32);
     profile_mark(CACHED ? "totals_qg" : "totals_kv", st);
     hipLaunchKernelGGL((k_totals<C, CACHED>), dim3((unsigned)d.NC, (unsigned)d.BH), dim3(NT), 0, st, a);
     return launch_ok();
@@ -187,6 +193,9 @@ race_status_t run_pass_groups(const Shape& s, const Derived& d, const WsLayout& 
         const Group gr = group(d, g);
         PassArgs ag = a;
         ag.L = gr.L;
+        ag.H = (int)s.H;
+        ag.w_hs = w_head_bytes(s, F32);
+        ag.wt_hs = s.w_per_head ? (int64_t)wt_bytes(d) : 0;
         ag.gmode = (g > 0 ? ACC_IN : 0) | (g + 1 < d.G ? ACC_OUT : 0);
         ag.acc = d.G > 1 ? reinterpret_cast<float*>(ws + wl.acc) : nullptr;
         ag.accD = d.G > 1 ? reinterpret_cast<float*>(ws + wl.accD) : nullptr;
@@ -269,14 +278,18 @@ race_status_t run_backward(const Shape& s, const Derived& d, const WsLayout& wl,
     float* Dv = reinterpret_cast<float*>(sv + sl.D);
     float* Ev = reinterpret_cast<float*>(ws + wl.E);
     using elem = typename Prec<F32>::elem;
-    auto wtp = [&](int g) { return reinterpret_cast<elem*>(ws + wl.wt + (size_t)g * wt_bytes(d)); };
+    // back-projection tables: one per group and head of W
+    const int64_t hw = s.w_per_head ? s.H : 1;
+    auto wtp = [&](int g) { return reinterpret_cast<elem*>(ws + wl.wt + (size_t)g * hw * wt_bytes(d)); };
     for (int g = 0; g < d.G; ++g) {
         const Group gr = group(d, g);
         profile_mark("prep", st);
         RACE_TRY((with_cfg<F32>(s.P, gr.MT, [&](auto tag) {
             using C = typename decltype(tag)::type;
-            hipLaunchKernelGGL(k_prep<C>, dim3(8), dim3(256), 0, st,
-                               reinterpret_cast<const elem*>(group_w(c.W, s, gr, F32)), gr.L, wtp(g));
+            hipLaunchKernelGGL(k_prep<C>, dim3(8, (unsigned)hw), dim3(256), 0, st,
+                               reinterpret_cast<const elem*>(group_w(c.W, s, gr, F32)), gr.L, wtp(g),
+                               w_head_bytes(s, F32) / (int64_t)sizeof(elem),
+                               s.w_per_head ? (int64_t)(wt_bytes(d) / sizeof(elem)) : 0);
             return launch_ok();
         })));
     }
@@ -338,16 +351,16 @@ template <bool F32>
 race_status_t dispatch(const Shape& s, const Derived& d, const WsLayout& wl, const Call& c) {
     hipStream_t st = c.stream;
     if (c.op == OP_HASH) {
-        const int64_t rows = d.BH * s.N;
-        const int64_t blocks = (rows + 63) / 64;
+        const int64_t blocks = (s.N + 63) / 64;   // per (batch, head) sequence
         if (blocks > 0x7fffffff) return RACE_ERR_UNSUPPORTED;
         for (int g = 0; g < d.G; ++g) {
             const Group gr = group(d, g);
             profile_mark("hash", st);
             RACE_TRY((with_cfg<F32>(s.P, gr.MT, [&](auto tag) {
                 using C = typename decltype(tag)::type;
-                hipLaunchKernelGGL(k_hash<C>, dim3((unsigned)blocks), dim3(NT), 0, st, c.X, group_w(c.W, s, gr, F32),
-                                   rows, gr.L, s.L, c.ids + gr.t0, c.near_zero);
+                hipLaunchKernelGGL(k_hash<C>, dim3((unsigned)blocks, (unsigned)d.BH), dim3(NT), 0, st, c.X,
+                                   group_w(c.W, s, gr, F32), s.N, gr.L, s.L, (int)s.H, w_head_bytes(s, F32),
+                                   c.ids + gr.t0, c.near_zero);
                 return launch_ok();
             })));
         }
@@ -385,6 +398,7 @@ race_status_t dispatch(const Shape& s, const Derived& d, const WsLayout& wl, con
             a.P = s.P; a.L = s.L; a.F = C::F; a.KB = C::KB; a.TPT = C::TPT; a.TPL = C::TPL;
             a.G = d.G; a.Lg = d.Lg; a.Fl = d.Fl;
             a.beta = c.beta; a.hard = c.hard;
+            a.H = (int)s.H; a.w_hs = w_head_bytes(s, C::F32);
             static_assert(C::F <= DEC_MAXF && C::F % DEC_RG == 0, "decode tiling");
             constexpr int NR = C::F / DEC_RG;   // state rows per thread
             if (a.T > 1 && d.G == 1) {

@@ -15,6 +15,7 @@ struct Shape {
     int64_t B, H, N;
     int d, P, L;
     int causal, chunk;
+    int w_per_head;   // W is [H, L, P, d] (head h of every batch uses W[h]) instead of [L, P, d]
 };
 
 // Tables are processed in groups of at most Lg (one launch per group and
@@ -225,7 +226,7 @@ inline WsLayout ws_layout(const Shape& s, const Derived& d, int kind) {
         w.Kc = off;  off = align256(off + cache_layout(s, d).total);
     }
     if (kind == WS_BWD || kind == WS_BWD_RECOMPUTE) {
-        w.wt = off;  off = align256(off + (size_t)d.G * wt_bytes(d));
+        w.wt = off;  off = align256(off + (size_t)d.G * (s.w_per_head ? (size_t)s.H : 1) * wt_bytes(d));
         w.T = off;   off = align256(off + chunks);
         w.Tt = off;  off = align256(off + (s.causal ? 0 : totals));
         w.E = off;   off = align256(off + tokens * sizeof(float));

@@ -45,10 +45,14 @@ enum { SCAN_EXCL = 0, SCAN_REV_EXCL = 1, SCAN_TOTAL = 2 };
 // Back-projection operand table: W'^T in the paired-tile K order (row 4g+j
 // of tile 2m for j < 4, row 4g+j-4 of tile 2m+1 otherwise).
 // ---------------------------------------------------------------------------
+// One table per head of W (blockIdx.y; heads w_hs elements apart in W and
+// wt_hs apart in WTp: 0 and 0 when W is shared).
 template <class C>
 __global__ void k_prep(const typename Prec<C::F32>::elem* __restrict__ W, int L,
-                       typename Prec<C::F32>::elem* __restrict__ WTp) {
+                       typename Prec<C::F32>::elem* __restrict__ WTp, int64_t w_hs, int64_t wt_hs) {
     using elem = typename Prec<C::F32>::elem;
+    W += blockIdx.y * w_hs;
+    WTp += blockIdx.y * wt_hs;
     const int n2 = C::NPAIR * 4 * 64 * 8;
     for (int k = blockIdx.x * blockDim.x + threadIdx.x; k < n2; k += gridDim.x * blockDim.x) {
         elem v = to_elem<C::F32>(0.f);
@@ -660,6 +664,8 @@ struct TotArgs {
     int nchunks;
     int L;
     float beta;
+    int H;               // heads (W of sequence bh: W + (bh % H) * w_hs bytes)
+    int64_t w_hs;        // bytes between the heads' hyperplanes; 0: one W for all
 };
 
 template <class C, bool CACHED>
@@ -696,10 +702,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 3))) void
     const size_t base = (size_t)bh * a.N;
     const int nsub = (int)((seg1 - seg0 + TB - 1) / TB);
     const int my = 16 * w + ln;
-    if (!CACHED) stage_w<C>(reinterpret_cast<const elem*>(a.W), a.L, s_w);
+    const elem* Wh = reinterpret_cast<const elem*>(reinterpret_cast<const char*>(a.W) + (bh % a.H) * a.w_hs);
+    if (!CACHED) stage_w<C>(Wh, a.L, s_w);
     zero_pads<C, ZV>(s_zr, nullptr);
     __syncthreads();   // W' and the padding are written by all waves, read by each
-    const WSrc<C> wsrc{s_w, reinterpret_cast<const elem*>(a.W), a.L};
+    const WSrc<C> wsrc{s_w, Wh, a.L};
     const int64_t nrows = seg1 - seg0;
     const size_t row0 = base + seg0;
     const rsrc_t rX = rows_rsrc(CACHED ? nullptr : a.Xb, row0, nrows, row_bytes<C::F32>());
@@ -905,6 +912,9 @@ struct PassArgs {
     float* acc;
     float* accD;
     int gmode;
+    int H;                 // heads: W of sequence bh at W + (bh % H) * w_hs bytes, its
+    int64_t w_hs;          // back-projection table at WTp + (bh % H) * wt_hs bytes
+    int64_t wt_hs;         // (both 0 when one W serves every head)
 };
 
 enum { ACC_IN = 1, ACC_OUT = 2 };
@@ -1241,7 +1251,7 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
     const int64_t seg0 = (int64_t)c * a.chunk;
     const int64_t seg1 = seg0 + a.chunk < a.N ? seg0 + a.chunk : a.N;
     const size_t base = (size_t)bh * a.N;
-    const elem* W = reinterpret_cast<const elem*>(a.W);
+    const elem* W = reinterpret_cast<const elem*>(reinterpret_cast<const char*>(a.W) + (bh % a.H) * a.w_hs);
     constexpr bool causal = CAUSAL;
     elem* s_w = LD::WS::on ? lds + LD::o_w : nullptr;
     if (LD::WS::on) stage_w<C>(W, a.L, s_w);
@@ -1524,7 +1534,7 @@ __attribute__((amdgpu_waves_per_eu(BwdQLds<C>::OCC, BwdQLds<C>::OCC))) void k_bw
     const int64_t seg0 = (int64_t)c * a.chunk;
     const int64_t seg1 = seg0 + a.chunk < a.N ? seg0 + a.chunk : a.N;
     const size_t base = (size_t)bh * a.N;
-    const elem* WTp = reinterpret_cast<const elem*>(a.WTp);
+    const elem* WTp = reinterpret_cast<const elem*>(reinterpret_cast<const char*>(a.WTp) + (bh % a.H) * a.wt_hs);
     constexpr bool causal = CAUSAL;
     zero_sketch_pads<C>(s_ms, 2);
     zero_pads<C>(s_zr, s_yr);
@@ -1755,7 +1765,7 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
     const int64_t seg0 = (int64_t)c * a.chunk;
     const int64_t seg1 = seg0 + a.chunk < a.N ? seg0 + a.chunk : a.N;
     const size_t base = (size_t)bh * a.N;
-    const elem* WTp = reinterpret_cast<const elem*>(a.WTp);
+    const elem* WTp = reinterpret_cast<const elem*>(reinterpret_cast<const char*>(a.WTp) + (bh % a.H) * a.wt_hs);
     constexpr bool causal = CAUSAL;
     if (DK) zero_sketch_pads<C>(s_ms, LD::NB);
     zero_pads<C, LD::ZS>(s_zr, DK ? s_yr : nullptr);
@@ -1985,19 +1995,23 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
 // hard-hash diagnostic
 // ---------------------------------------------------------------------------
 // ids: row r's entry for table l (of the L tables of this group) at
-// ids[r * ld + l].
+// ids[r * ld + l]. Block (x, y) takes rows 64 x .. 64 x + 63 of sequence y
+// (N rows each), so a wave's 16 rows share one head's hyperplanes.
 template <class C>
-__global__ __launch_bounds__(NT) void k_hash(const void* X, const void* Wv, int64_t rows, int L, int ld,
-                                             int32_t* __restrict__ ids, unsigned long long* near_zero) {
+__global__ __launch_bounds__(NT) void k_hash(const void* X, const void* Wv, int64_t N, int L, int ld, int H,
+                                             int64_t w_hs, int32_t* __restrict__ ids,
+                                             unsigned long long* near_zero) {
     using elem = typename Prec<C::F32>::elem;
     using frag = typename Prec<C::F32>::frag;
     const int lane = threadIdx.x & 63, ln = lane & 15, g = lane >> 4;
     // wave index as a scalar: every branch on it is wave-uniform, so no MFMA is
     // ever issued under a partial or empty EXEC mask
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t r = ((int64_t)blockIdx.x * NW + w) * 16 + ln;
-    const bool valid = r < rows;
-    const elem* W = reinterpret_cast<const elem*>(Wv);
+    const int64_t bh = blockIdx.y;
+    const int64_t n = ((int64_t)blockIdx.x * NW + w) * 16 + ln;
+    const bool valid = n < N;
+    const int64_t r = bh * N + n;
+    const elem* W = reinterpret_cast<const elem*>(reinterpret_cast<const char*>(Wv) + (bh % H) * w_hs);
     frag xf[2];
     load_row_raw<C::F32>(X, valid ? (size_t)r : 0, valid, g, xf);
     const float inv = row_inv_norm<C::F32>(xf);

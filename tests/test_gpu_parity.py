@@ -366,3 +366,71 @@ def test_hard_forward_many_collisions(lib, dtype):
         print(f"[case] hard {dtype} N={N} causal={causal} seed={seed}: rel_l2 {err:.2e}", flush=True)
         assert np.array_equal(np.all(O == 0.0, axis=-1), np.all(ref == 0.0, axis=-1))
         assert err <= TOL[dtype]
+
+
+# --- one set of hyperplanes per head ----------------------------------------------
+
+@pytest.mark.parametrize("dtype,causal,P,L", [("f32", True, 4, 8), ("bf16", True, 4, 20), ("bf16", False, 2, 8),
+                                             ("bf16", True, 5, 9)])
+def test_per_head_hyperplanes(lib, dtype, causal, P, L):
+    """W of shape [H, L, P, d]: head h of every batch projects on W[h]. Forward,
+    backward and hard-hash ids against the oracle run head by head with that
+    head's W; (4, 20) and (5, 9) also run as table groups."""
+    import synth
+    import torch
+    B, H, N, chunk = 2, 3, 400, 128
+    print(f"[case] per-head W {dtype} causal={causal} P={P} L={L}", flush=True)
+    x = host_inputs(808, B, H, N, 64, P, L, dtype)
+    Wh = synth.normal(808, synth.TID_W, (H, L, P, 64), dtype)
+    dev = torch.device("cuda:0")
+    T = {k: to_torch(v, dev) for k, v in x.items()}
+    Wd = to_torch(Wh, dev)
+    saved = lib.alloc_saved(B, H, N, P, L, causal, chunk, dev)
+    O = lib.forward(T["Q"], T["K"], T["V"], Wd, P, L, 1.1, causal, chunk, saved=saved)
+    dQ, dK, dV = lib.backward(T["Q"], T["K"], T["V"], Wd, T["dO"], P, L, 1.1, causal, chunk, O=O, saved=saved)
+    ids, _ = lib.hard_hash(T["Q"], Wd, P, L)
+    torch.cuda.synchronize()
+    got = {"O": from_torch(O), "dQ": from_torch(dQ), "dK": from_torch(dK), "dV": from_torch(dV)}
+    ref = {k: np.zeros_like(v) for k, v in got.items()}
+    mism = 0
+    for h in range(H):
+        W64 = to_f64(Wh[h])
+        sl = (slice(None), h)
+        ref["O"][sl] = oracle.forward(x["Q"][sl], x["K"][sl], x["V"][sl], W64, 1.1, causal)
+        ref["dQ"][sl], ref["dK"][sl], ref["dV"][sl] = oracle.backward(x["Q"][sl], x["K"][sl], x["V"][sl], W64,
+                                                                      x["dO"][sl], 1.1, causal)
+        rid, _ = oracle.hard_hash(x["Q"][sl], W64)
+        mism += int((ids[:, h].cpu().numpy() != rid).sum())
+    errs = {k: rel_l2(got[k], ref[k]) for k in got}
+    print("   rel_l2", {k: f"{v:.2e}" for k, v in errs.items()}, f"hash mismatches {mism}", flush=True)
+    for k, e in errs.items():
+        assert e <= TOL[dtype], (k, e)
+    assert mism <= 2   # only where a projection is within float rounding of zero
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_per_head_hyperplanes_decode(lib, dtype):
+    """Prefill + decode steps with per-head hyperplanes (P4 L20: two table
+    groups) against the oracle's sketch and decode step per head."""
+    import synth
+    import torch
+    from oracle import dense
+    B, H, n0, Tn, P, L = 1, 3, 50, 3, 4, 20
+    x = host_inputs(909, B, H, n0 + Tn, 64, P, L, dtype)
+    Wh = synth.normal(909, synth.TID_W, (H, L, P, 64), dtype)
+    dev = torch.device("cuda:0")
+    t = {k: to_torch(v, dev) for k, v in x.items()}
+    Wd = to_torch(Wh, dev)
+    state = lib.prefill(t["K"][:, :, :n0].contiguous(), t["V"][:, :, :n0].contiguous(), Wd, P, L, 0.9, 32)
+    outs = [from_torch(lib.decode(*(t[n][:, :, n0 + s].contiguous() for n in ("Q", "K", "V")), Wd, state, P, L,
+                                  0.9)) for s in range(Tn)]
+    torch.cuda.synchronize()
+    for h in range(H):
+        W64 = to_f64(Wh[h])
+        Q, K, V = (to_f64(x[n])[0, h] for n in ("Q", "K", "V"))
+        S, z = dense.sketch(K[:n0], V[:n0], W64, 0.9)
+        for s in range(Tn):
+            i = n0 + s
+            S, z, o = dense.decode_step(S, z, Q[i], K[i], V[i], W64, 0.9)
+            err = rel_l2(outs[s][0, h], o)
+            assert err <= (1e-5 if dtype == "f32" else 5e-3), (h, s, err)
