@@ -159,16 +159,16 @@ def _nbytes(t):
     return t.numel() * t.element_size()
 
 
-def alloc_workspace(B, H, N, P, L, causal, chunk, kind, device):
+def alloc_workspace(B, H, N, P, L, causal, chunk, kind, device, d=64):
     """kind: WS_* (or'ed with RACE_W_PER_HEAD for per-head hyperplanes)."""
     import torch
-    n = workspace_bytes(B, H, N, 64, P, L, causal, chunk, kind)
+    n = workspace_bytes(B, H, N, d, P, L, causal, chunk, kind)
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
 
-def alloc_saved(B, H, N, P, L, causal, chunk, device):
+def alloc_saved(B, H, N, P, L, causal, chunk, device, d=64):
     import torch
-    n = saved_bytes(B, H, N, 64, P, L, causal, chunk)
+    n = saved_bytes(B, H, N, d, P, L, causal, chunk)
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
 
@@ -188,7 +188,7 @@ def race_attn_fwd(Q, K, V, W, P, L, temperature=1.0, causal=False, chunk=1024, o
     if saved is not None:
         _check_buf(saved, saved_bytes(B, H, N, d, P, L, causal, chunk), Q.device, "saved")
     if ws is None:
-        ws = alloc_workspace(B, H, N, P, L, causal, chunk, kind, Q.device)
+        ws = alloc_workspace(B, H, N, P, L, causal, chunk, kind, Q.device, d)
     _check_buf(ws, workspace_bytes(B, H, N, d, P, L, causal, chunk, kind), Q.device, "ws")
     code = lib().race_attn_fwd(_p(Q), _p(K), _p(V), _p(W), B, H, N, d, P, L, float(temperature),
                                int(bool(causal)), chunk, _dtype_code(Q) | wf, _p(O), _p(saved), _p(ws),
@@ -247,7 +247,7 @@ def race_attn_bwd(Q, K, V, W, dO, P, L, temperature=1.0, causal=False, chunk=102
         _check_like(t, Q, nm)
     kind = (WS_BWD if saved is not None else WS_BWD_RECOMPUTE) | wf
     if ws is None:
-        ws = alloc_workspace(B, H, N, P, L, causal, chunk, kind, Q.device)
+        ws = alloc_workspace(B, H, N, P, L, causal, chunk, kind, Q.device, d)
     _check_buf(ws, workspace_bytes(B, H, N, d, P, L, causal, chunk, kind), Q.device, "ws")
     code = lib().race_attn_bwd(_p(Q), _p(K), _p(V), _p(W), _p(O), _p(dO), _p(saved), B, H, N, d, P, L,
                                float(temperature), int(bool(causal)), chunk, _dtype_code(Q) | wf, _p(dQ),
@@ -278,11 +278,11 @@ def state_bytes(B, H, P, L, d=64) -> int:
     return out.value
 
 
-def alloc_state(B, H, P, L, device):
+def alloc_state(B, H, P, L, device, d=64):
     """A zeroed running sketch (the state of an empty sequence), held in a
     float32 tensor of race_attn_state_bytes bytes."""
     import torch
-    return torch.zeros(state_bytes(B, H, P, L) // 4, dtype=torch.float32, device=device)
+    return torch.zeros(state_bytes(B, H, P, L, d) // 4, dtype=torch.float32, device=device)
 
 
 def race_attn_prefill(K, V, W, P, L, temperature=1.0, chunk=1024, state=None, ws=None, stream=None):
@@ -294,10 +294,10 @@ def race_attn_prefill(K, V, W, P, L, temperature=1.0, chunk=1024, state=None, ws
     if V.shape != K.shape:
         raise ValueError("K and V must share one shape")
     if state is None:
-        state = alloc_state(B, H, P, L, K.device)
+        state = alloc_state(B, H, P, L, K.device, d)
     _check_state(state, B, H, P, L, d, K.device)
     if ws is None:
-        ws = alloc_workspace(B, H, N, P, L, False, chunk, WS_FWD, K.device)
+        ws = alloc_workspace(B, H, N, P, L, False, chunk, WS_FWD, K.device, d)
     _check_buf(ws, workspace_bytes(B, H, N, d, P, L, False, chunk, WS_FWD), K.device, "ws")
     code = lib().race_attn_prefill(_p(K), _p(V), _p(W), B, H, N, d, P, L, float(temperature), chunk,
                                    _dtype_code(K) | wf, _p(state), _p(ws), _nbytes(ws), _stream(stream))

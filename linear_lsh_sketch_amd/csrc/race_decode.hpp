@@ -54,6 +54,7 @@ struct DecodeArgs {
     int hard;
     int H;          // heads: W of head bh at W + (bh % H) * w_hs bytes (0: one W for all)
     int64_t w_hs;
+    int dh;         // head dimension: 64, or 32 (columns 32..63 read as zero)
 };
 
 // Table and subset of canonical feature f (lane group g of 32-feature chunk
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_one(DecodeArgs a) {
     if (tid < 3 * DH) {
         const int which = tid / DH, c = tid % DH;
         const void* src = which == 0 ? a.q : which == 1 ? a.k : a.v;
-        s_x[which][c] = (float)reinterpret_cast<const elem*>(src)[r * DH + c];
+        s_x[which][c] = c < a.dh ? (float)reinterpret_cast<const elem*>(src)[r * a.dh + c] : 0.f;
     }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};   // read-out of columns 4 cq .. +3 over this thread's rows
     double den = 0.0;                   // and over its masses
@@ -125,9 +126,16 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_one(DecodeArgs a) {
         if (tid < 2 * LP) {
             const wvec* w = reinterpret_cast<const wvec*>(
                 reinterpret_cast<const elem*>(reinterpret_cast<const char*>(a.W) + (bh % a.H) * a.w_hs) +
-                ((size_t)gi * a.Lg * a.P + row) * DH);
+                ((size_t)gi * a.Lg * a.P + row) * a.dh);
 #pragma unroll
-            for (int j = 0; j < DH / WV; ++j) wr[j] = w[j];
+            for (int j = 0; j < DH / WV; ++j) {
+                if (j * WV < a.dh) {
+                    wr[j] = w[j];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < WV; ++e) wr[j][e] = (elem)0.f;
+                }
+            }
         }
         __syncthreads();   // s_x is written; the previous group's s_t and s_phi are read
 
@@ -208,7 +216,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_one(DecodeArgs a) {
 #pragma unroll
         for (int w = 0; w < DEC_NT / 64; ++w) dsum += s_den[w];
         const float o = (a.hard && dsum == 0.0) ? 0.f : num / (float)dsum;
-        reinterpret_cast<elem*>(a.o)[r * DH + tid] = (elem)o;
+        if (tid < a.dh) reinterpret_cast<elem*>(a.o)[r * a.dh + tid] = (elem)o;
     }
 }
 
@@ -243,7 +251,10 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_multi(DecodeArgs a) {
     double z = tid < F ? zs[tid] : 0.0;
     // the hyperplanes, once, into LDS (read there for every token)
     const elem* Wh = reinterpret_cast<const elem*>(reinterpret_cast<const char*>(a.W) + (bh % a.H) * a.w_hs);
-    for (int e = tid; e < LP * DH; e += DEC_NT) s_w[e / DH][e % DH] = (float)Wh[e];
+    for (int e = tid; e < LP * DH; e += DEC_NT) {
+        const int c = e % DH;
+        s_w[e / DH][c] = c < a.dh ? (float)Wh[(e / DH) * a.dh + c] : 0.f;
+    }
     const int side = tid / LP, row = tid % LP;
     // q, k, v rows are loaded one token ahead: thread tid < 3 * 64 holds one
     // element of the next token while the current one is processed
@@ -251,9 +262,10 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_multi(DecodeArgs a) {
     const elem* src = reinterpret_cast<const elem*>(which == 0 ? a.q : which == 1 ? a.k : a.v);
     const int64_t r0 = bh * a.T;   // first row of this head's q, k, v, o
     float nx = 0.f;
+    const bool in_col = col < a.dh;
     if (tid < 3 * DH) {
-        s_x[which][col] = (float)src[r0 * DH + col];
-        if (a.T > 1) nx = (float)src[(r0 + 1) * DH + col];
+        s_x[which][col] = in_col ? (float)src[r0 * a.dh + col] : 0.f;
+        if (a.T > 1 && in_col) nx = (float)src[(r0 + 1) * a.dh + col];
     }
     __syncthreads();
 
@@ -338,11 +350,11 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_multi(DecodeArgs a) {
 #pragma unroll
             for (int w = 0; w < DEC_NT / 64; ++w) den += s_den[w];
             const float o = (a.hard && den == 0.0) ? 0.f : num / (float)den;
-            reinterpret_cast<elem*>(a.o)[r * DH + tid] = (elem)o;
+            if (tid < a.dh) reinterpret_cast<elem*>(a.o)[r * a.dh + tid] = (elem)o;
         }
         if (tid < 3 * DH && tok + 1 < a.T) {
             s_x[which][col] = nx;
-            if (tok + 2 < a.T) nx = (float)src[(r + 2) * DH + col];
+            if (tok + 2 < a.T && in_col) nx = (float)src[(r + 2) * a.dh + col];
         }
         __syncthreads();
     }

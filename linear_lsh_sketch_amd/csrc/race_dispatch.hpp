@@ -81,7 +81,7 @@ race_status_t with_cfg(int P, int MT, Fn&& fn) {
 
 // Bytes between the hyperplanes of consecutive heads (0: one W for all).
 inline int64_t w_head_bytes(const Shape& s, bool f32) {
-    return s.w_per_head ? (int64_t)s.L * s.P * DH * (f32 ? 4 : 2) : 0;
+    return s.w_per_head ? (int64_t)s.L * s.P * s.d * (f32 ? 4 : 2) : 0;
 }
 
 // CACHED = false: sketch of K, [V | 1] (storing the keys' plane values in pc);
@@ -93,7 +93,7 @@ race_status_t run_totals(const Shape& s, const Derived& d, const Group& gr, cons
     TotArgs a;
     a.Xb = Xb; a.Z = Z; a.Dv = Dv; a.Ev = Ev; a.W = W; a.pc = pc; a.out = out;
     a.N = s.N; a.chunk = s.chunk; a.nchunks = (int)d.NC; a.L = gr.L; a.beta = beta;
-    a.H = (int)s.H; a.w_hs = w_head_bytes(s, C::F32);
+    a.H = (int)s.H; a.w_hs = w_head_bytes(s, C::F32); a.dh = s.d;
     profile_mark(CACHED ? "totals_qg" : "totals_kv", st);
     hipLaunchKernelGGL((k_totals<C, CACHED>), dim3((unsigned)d.NC, (unsigned)d.BH), dim3(NT), 0, st, a);
     return launch_ok();
@@ -196,6 +196,7 @@ race_status_t run_pass_groups(const Shape& s, const Derived& d, const WsLayout& 
         ag.H = (int)s.H;
         ag.w_hs = w_head_bytes(s, F32);
         ag.wt_hs = s.w_per_head ? (int64_t)wt_bytes(d) : 0;
+        ag.dh = s.d;
         ag.gmode = (g > 0 ? ACC_IN : 0) | (g + 1 < d.G ? ACC_OUT : 0);
         ag.acc = d.G > 1 ? reinterpret_cast<float*>(ws + wl.acc) : nullptr;
         ag.accD = d.G > 1 ? reinterpret_cast<float*>(ws + wl.accD) : nullptr;
@@ -210,7 +211,7 @@ race_status_t run_pass_groups(const Shape& s, const Derived& d, const WsLayout& 
 
 // Hyperplanes of table group g (W is [L, P, 64], groups are consecutive tables).
 inline const void* group_w(const void* W, const Shape& s, const Group& gr, bool f32) {
-    return reinterpret_cast<const char*>(W) + (size_t)gr.t0 * s.P * DH * (f32 ? 4 : 2);
+    return reinterpret_cast<const char*>(W) + (size_t)gr.t0 * s.P * s.d * (f32 ? 4 : 2);
 }
 
 // Forward into O; when `saved` is set it receives the sketch states, D and
@@ -289,7 +290,7 @@ race_status_t run_backward(const Shape& s, const Derived& d, const WsLayout& wl,
             hipLaunchKernelGGL(k_prep<C>, dim3(8, (unsigned)hw), dim3(256), 0, st,
                                reinterpret_cast<const elem*>(group_w(c.W, s, gr, F32)), gr.L, wtp(g),
                                w_head_bytes(s, F32) / (int64_t)sizeof(elem),
-                               s.w_per_head ? (int64_t)(wt_bytes(d) / sizeof(elem)) : 0);
+                               s.w_per_head ? (int64_t)(wt_bytes(d) / sizeof(elem)) : 0, s.d);
             return launch_ok();
         })));
     }
@@ -359,7 +360,7 @@ race_status_t dispatch(const Shape& s, const Derived& d, const WsLayout& wl, con
             RACE_TRY((with_cfg<F32>(s.P, gr.MT, [&](auto tag) {
                 using C = typename decltype(tag)::type;
                 hipLaunchKernelGGL(k_hash<C>, dim3((unsigned)blocks, (unsigned)d.BH), dim3(NT), 0, st, c.X,
-                                   group_w(c.W, s, gr, F32), s.N, gr.L, s.L, (int)s.H, w_head_bytes(s, F32),
+                                   group_w(c.W, s, gr, F32), s.N, gr.L, s.L, (int)s.H, w_head_bytes(s, F32), s.d,
                                    c.ids + gr.t0, c.near_zero);
                 return launch_ok();
             })));
@@ -398,7 +399,7 @@ race_status_t dispatch(const Shape& s, const Derived& d, const WsLayout& wl, con
             a.P = s.P; a.L = s.L; a.F = C::F; a.KB = C::KB; a.TPT = C::TPT; a.TPL = C::TPL;
             a.G = d.G; a.Lg = d.Lg; a.Fl = d.Fl;
             a.beta = c.beta; a.hard = c.hard;
-            a.H = (int)s.H; a.w_hs = w_head_bytes(s, C::F32);
+            a.H = (int)s.H; a.w_hs = w_head_bytes(s, C::F32); a.dh = s.d;
             static_assert(C::F <= DEC_MAXF && C::F % DEC_RG == 0, "decode tiling");
             constexpr int NR = C::F / DEC_RG;   // state rows per thread
             if (a.T > 1 && d.G == 1) {

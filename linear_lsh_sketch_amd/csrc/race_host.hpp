@@ -98,7 +98,7 @@ inline bool mul_ok(int64_t a, int64_t b, int64_t& out) {
 inline race_status_t derive(const Shape& s, Derived& d) {
     if (s.B < 1 || s.H < 1 || s.N < 1 || s.d < 1 || s.P < 1 || s.L < 1 || s.chunk < 1)
         return RACE_ERR_INVALID_ARG;
-    if (s.d != 64 || s.P > 6) return RACE_ERR_UNSUPPORTED;
+    if ((s.d != 64 && s.d != 32) || s.P > 6) return RACE_ERR_UNSUPPORTED;
     // in-chunk byte offsets (rows of up to 512 bytes) are 32-bit
     if (s.chunk > MAX_CHUNK) return RACE_ERR_UNSUPPORTED;
     // planes per table padded to 1, 2, 4 or 8 (P = 5, 6: two lane groups)
@@ -235,10 +235,11 @@ inline WsLayout ws_layout(const Shape& s, const Derived& d, int kind) {
         w.Sv = off;  off = align256(off + saved_bytes(s, d));
         w.Ov = off;  off = align256(off + tokens * (size_t)s.d * sizeof(float));
     }
-    // partial outputs of the groups before the last: [rows][64] and the
-    // forward's partial denominators [rows], float32
+    // partial outputs of the groups before the last: [rows][64] (the
+    // kernels' working width, whatever the head dimension) and the forward's
+    // partial denominators [rows], float32
     if (d.G > 1) {
-        w.acc = off;  off = align256(off + tokens * (size_t)s.d * sizeof(float));
+        w.acc = off;  off = align256(off + tokens * (size_t)64 * sizeof(float));
         w.accD = off; off = align256(off + tokens * sizeof(float));
     }
     // segment sums of one group's scan at a time (the largest of the groups)

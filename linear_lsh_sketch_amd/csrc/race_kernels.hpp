@@ -49,7 +49,7 @@ enum { SCAN_EXCL = 0, SCAN_REV_EXCL = 1, SCAN_TOTAL = 2 };
 // wt_hs apart in WTp: 0 and 0 when W is shared).
 template <class C>
 __global__ void k_prep(const typename Prec<C::F32>::elem* __restrict__ W, int L,
-                       typename Prec<C::F32>::elem* __restrict__ WTp, int64_t w_hs, int64_t wt_hs) {
+                       typename Prec<C::F32>::elem* __restrict__ WTp, int64_t w_hs, int64_t wt_hs, int dh) {
     using elem = typename Prec<C::F32>::elem;
     W += blockIdx.y * w_hs;
     WTp += blockIdx.y * wt_hs;
@@ -63,7 +63,7 @@ __global__ void k_prep(const typename Prec<C::F32>::elem* __restrict__ W, int L,
         if (tile < C::MT) {
             int table, plane;
             row_table<C>(tile, ri, table, plane);
-            if (table < L && plane < C::P) v = W[((size_t)table * C::P + plane) * DH + d];
+            if (table < L && plane < C::P && d < dh) v = W[((size_t)table * C::P + plane) * dh + d];
         }
         WTp[k] = v;
     }
@@ -133,35 +133,45 @@ __device__ inline void bstore_frag(rsrc_t r, int off, const typename Prec<F32>::
     }
 }
 
-// Bytes of a [*, 64] row of the input type.
+// Bytes of a [*, dh] row of the input type. The kernels work on 64 columns;
+// a head dimension dh = 32 leaves columns 32..63 zero on load (the norms,
+// projections and value sums are then those of the 32 real columns) and
+// unwritten on store.
 template <bool F32>
-constexpr int row_bytes() { return DH * (F32 ? 4 : 2); }
+__device__ inline int row_bytes(int dh) { return dh * (F32 ? 4 : 2); }
 
 // This lane's projection operand of in-chunk row rowi: K positions 32 s + 8 g .. +7.
 template <bool F32>
-__device__ inline void load_row_b(rsrc_t r, int rowi, int g, typename Prec<F32>::frag x[2]) {
+__device__ inline void load_row_b(rsrc_t r, int rowi, int g, typename Prec<F32>::frag x[2], int dh) {
     constexpr int es = F32 ? 4 : 2;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) x[s] = bload_frag<F32>(r, rowi * row_bytes<F32>() + (32 * s + 8 * g) * es);
+    for (int s = 0; s < 2; ++s)
+        x[s] = 32 * s < dh ? bload_frag<F32>(r, rowi * row_bytes<F32>(dh) + (32 * s + 8 * g) * es) : zero_frag<F32>();
 }
 
 // Columns 16 q .. 16 q + 15 of in-chunk row rowi.
 template <bool F32>
-__device__ inline void load_q16_b(rsrc_t r, int rowi, int q, typename Prec<F32>::frag v[2]) {
+__device__ inline void load_q16_b(rsrc_t r, int rowi, int q, typename Prec<F32>::frag v[2], int dh) {
     constexpr int es = F32 ? 4 : 2;
-    v[0] = bload_frag<F32>(r, rowi * row_bytes<F32>() + 16 * q * es);
-    v[1] = bload_frag<F32>(r, rowi * row_bytes<F32>() + (16 * q + 8) * es);
+    if (16 * q < dh) {
+        v[0] = bload_frag<F32>(r, rowi * row_bytes<F32>(dh) + 16 * q * es);
+        v[1] = bload_frag<F32>(r, rowi * row_bytes<F32>(dh) + (16 * q + 8) * es);
+    } else {
+        v[0] = zero_frag<F32>();
+        v[1] = zero_frag<F32>();
+    }
 }
 
 // This lane's projection operand of one token row: K positions 32 s + 8 g .. +7.
 template <bool F32>
 __device__ inline void load_row_raw(const void* X, size_t row, bool valid, int g,
-                                    typename Prec<F32>::frag x[2]) {
+                                    typename Prec<F32>::frag x[2], int dh) {
     using T = typename In<F32>::T;
-    const T* p = reinterpret_cast<const T*>(X) + row * DH + 8 * g;
+    const T* p = reinterpret_cast<const T*>(X) + row * dh + 8 * g;
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-        x[s] = valid ? *reinterpret_cast<const typename Prec<F32>::frag*>(p + 32 * s) : zero_frag<F32>();
+        x[s] = (valid && 32 * s < dh) ? *reinterpret_cast<const typename Prec<F32>::frag*>(p + 32 * s)
+                                      : zero_frag<F32>();
 }
 
 // 1 / max(|x|, eps) of the row held by load_row_b / load_row_raw (same in all
@@ -221,13 +231,14 @@ __device__ inline float q16_at(const typename Prec<F32>::frag v[2], int c) {
 // [tile][K half s][lane][8], filled once per workgroup.
 template <class C>
 __device__ inline void stage_w(const typename Prec<C::F32>::elem* __restrict__ W, int L,
-                               typename Prec<C::F32>::elem* s_w) {
+                               typename Prec<C::F32>::elem* s_w, int dh) {
     for (int idx = threadIdx.x; idx < C::MT * 1024; idx += NT) {
         const int t = idx / 1024, s = (idx / 512) & 1, l = (idx / 8) & 63, j = idx & 7;
         int table, plane;
         row_table<C>(t, l & 15, table, plane);
         typename Prec<C::F32>::elem v = to_elem<C::F32>(0.f);
-        if (table < L && plane < C::P) v = W[((size_t)table * C::P + plane) * DH + 32 * s + 8 * (l >> 4) + j];
+        const int col = 32 * s + 8 * (l >> 4) + j;
+        if (table < L && plane < C::P && col < dh) v = W[((size_t)table * C::P + plane) * dh + col];
         s_w[idx] = v;
     }
 }
@@ -245,15 +256,15 @@ __device__ inline f32x4 project_lds(const typename Prec<C::F32>::elem* s_w, int 
 // Same from W in global memory (used where LDS is full, and by the hash kernel).
 template <class C>
 __device__ inline f32x4 project_global(const typename Prec<C::F32>::elem* __restrict__ W, int L, int t, int ln,
-                                       int g, const typename Prec<C::F32>::frag xf[2]) {
+                                       int g, const typename Prec<C::F32>::frag xf[2], int dh) {
     int table, plane;
     row_table<C>(t, ln, table, plane);
     const bool ok = table < L && plane < C::P;
-    const typename Prec<C::F32>::elem* wr = W + ((size_t)(ok ? table * C::P + plane : 0)) * DH + 8 * g;
+    const typename Prec<C::F32>::elem* wr = W + ((size_t)(ok ? table * C::P + plane : 0)) * dh + 8 * g;
     typename Prec<C::F32>::frag wf[2] = {zero_frag<C::F32>(), zero_frag<C::F32>()};
     if (ok) {
         wf[0] = ld_frag<C::F32>(wr);
-        wf[1] = ld_frag<C::F32>(wr + 32);
+        if (dh > 32) wf[1] = ld_frag<C::F32>(wr + 32);
     }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     acc = mma(wf[0], xf[0], acc);
@@ -268,9 +279,10 @@ struct WSrc {
     const typename Prec<C::F32>::elem* s_w;
     const typename Prec<C::F32>::elem* W;
     int L;
+    int dh;
     __device__ inline f32x4 project(int t, int lane, int ln, int g, const typename Prec<C::F32>::frag xf[2]) const {
         if constexpr (STAGED) return project_lds<C>(s_w, t, lane, xf);
-        else return project_global<C>(W, L, t, ln, g, xf);
+        else return project_global<C>(W, L, t, ln, g, xf, dh);
     }
 };
 
@@ -666,6 +678,7 @@ struct TotArgs {
     float beta;
     int H;               // heads (W of sequence bh: W + (bh % H) * w_hs bytes)
     int64_t w_hs;        // bytes between the heads' hyperplanes; 0: one W for all
+    int dh;              // head dimension: 64, or 32 (columns 32..63 zero)
 };
 
 template <class C, bool CACHED>
@@ -703,14 +716,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 3))) void
     const int nsub = (int)((seg1 - seg0 + TB - 1) / TB);
     const int my = 16 * w + ln;
     const elem* Wh = reinterpret_cast<const elem*>(reinterpret_cast<const char*>(a.W) + (bh % a.H) * a.w_hs);
-    if (!CACHED) stage_w<C>(Wh, a.L, s_w);
+    if (!CACHED) stage_w<C>(Wh, a.L, s_w, a.dh);
     zero_pads<C, ZV>(s_zr, nullptr);
     __syncthreads();   // W' and the padding are written by all waves, read by each
-    const WSrc<C> wsrc{s_w, Wh, a.L};
+    const WSrc<C> wsrc{s_w, Wh, a.L, a.dh};
     const int64_t nrows = seg1 - seg0;
     const size_t row0 = base + seg0;
-    const rsrc_t rX = rows_rsrc(CACHED ? nullptr : a.Xb, row0, nrows, row_bytes<C::F32>());
-    const rsrc_t rZ = rows_rsrc(a.Z, row0, nrows, row_bytes<C::F32>());
+    const rsrc_t rX = rows_rsrc(CACHED ? nullptr : a.Xb, row0, nrows, row_bytes<C::F32>(a.dh));
+    const rsrc_t rZ = rows_rsrc(a.Z, row0, nrows, row_bytes<C::F32>(a.dh));
     const rsrc_t rD = rows_rsrc(CACHED ? a.Dv : nullptr, row0, nrows, 4);
     const rsrc_t rE = rows_rsrc(CACHED ? a.Ev : nullptr, row0, nrows, 4);
     const PlaneRows pr = plane_rows<C>(a.pc, row0, nrows);
@@ -731,8 +744,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 3))) void
     };
     auto issue = [&](int it2) {
         const int r0 = it2 * TB;
-        if (!CACHED) load_row_b<C::F32>(rX, r0 + my, g, nx);
-        load_q16_b<C::F32>(rZ, r0 + tr, tq, nz);
+        if (!CACHED) load_row_b<C::F32>(rX, r0 + my, g, nx, a.dh);
+        load_q16_b<C::F32>(rZ, r0 + tr, tq, nz, a.dh);
         if (CACHED) {
             nd = bload_f32(rD, (r0 + tr) * 4);
             ne = bload_f32(rE, (r0 + tr) * 4);
@@ -915,6 +928,7 @@ struct PassArgs {
     int H;                 // heads: W of sequence bh at W + (bh % H) * w_hs bytes, its
     int64_t w_hs;          // back-projection table at WTp + (bh % H) * wt_hs bytes
     int64_t wt_hs;         // (both 0 when one W serves every head)
+    int dh;                // head dimension: 64, or 32 (columns 32..63 zero)
 };
 
 enum { ACC_IN = 1, ACC_OUT = 2 };
@@ -1098,13 +1112,19 @@ __device__ inline void intra_operand(const typename Prec<C::F32>::elem* s_zr, co
 // The own token's row values that store_dx needs (columns 16 dt + 4 g .. +3),
 // loaded early so the memory latency overlaps the sub-block's work.
 template <class C>
-__device__ inline void load_dx_row(rsrc_t rX, int rowi, int g, typename Prec<C::F32>::half (&xr)[4]) {
+__device__ inline void load_dx_row(rsrc_t rX, int rowi, int g, typename Prec<C::F32>::half (&xr)[4], int dh) {
     constexpr int es = C::F32 ? 4 : 2;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-        const int off = rowi * row_bytes<C::F32>() + (16 * dt + 4 * g) * es;
-        if constexpr (C::F32) xr[dt] = __builtin_bit_cast(f32x4, bload128(rX, off));
-        else xr[dt] = __builtin_bit_cast(bf16x4, bload64(rX, off));
+        const int off = rowi * row_bytes<C::F32>(dh) + (16 * dt + 4 * g) * es;
+        if (16 * dt >= dh) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xr[dt][i] = to_elem<C::F32>(0.f);
+        } else if constexpr (C::F32) {
+            xr[dt] = __builtin_bit_cast(f32x4, bload128(rX, off));
+        } else {
+            xr[dt] = __builtin_bit_cast(bf16x4, bload64(rX, off));
+        }
     }
 }
 
@@ -1115,7 +1135,7 @@ __device__ inline void load_dx_row(rsrc_t rX, int rowi, int g, typename Prec<C::
 // the final scaling is beta / max(|x|, eps).
 template <class C>
 __device__ inline void store_dx(const typename Prec<C::F32>::half (&xr)[4], rsrc_t rOut, int rowi, int g, float inv,
-                                float beta, const f32x4 dX[4]) {
+                                float beta, const f32x4 dX[4], int dh) {
     constexpr int es = C::F32 ? 4 : 2;
     float xv[4][4];
     float radial = 0.f;
@@ -1132,10 +1152,11 @@ __device__ inline void store_dx(const typename Prec<C::F32>::half (&xr)[4], rsrc
     const float binv = beta * inv;   // dX carries dt/dh without its factor beta
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
+        if (16 * dt >= dh) break;
         f32x4 o;
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = (tangent ? dX[dt][i] - xv[dt][i] * inv * radial : dX[dt][i]) * binv;
-        const int off = rowi * row_bytes<C::F32>() + (16 * dt + 4 * g) * es;
+        const int off = rowi * row_bytes<C::F32>(dh) + (16 * dt + 4 * g) * es;
         if constexpr (C::F32) {
             bstore128(rOut, off, __builtin_bit_cast(u32x4, o));
         } else {
@@ -1154,14 +1175,15 @@ __device__ inline void store_dx(const typename Prec<C::F32>::half (&xr)[4], rsrc
 // dropped).
 template <class C>
 __device__ inline void store_rows_t(rsrc_t out, int r0, int cb, int ln, int g, const f32x4 (&Yt)[4],
-                                    const float (&rs)[4], const float (&add)[4]) {
+                                    const float (&rs)[4], const float (&add)[4], int dh) {
     constexpr int es = C::F32 ? 4 : 2;
+    if (cb >= dh) return;   // columns past the head dimension (wave-uniform)
 #pragma unroll
     for (int at = 0; at < 4; ++at) {
         f32x4 o;
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = (Yt[at][i] + add[i]) * rs[at];
-        const int off = (r0 + 16 * at + ln) * row_bytes<C::F32>() + (cb + 4 * g) * es;
+        const int off = (r0 + 16 * at + ln) * row_bytes<C::F32>(dh) + (cb + 4 * g) * es;
         if constexpr (C::F32) {
             bstore128(out, off, __builtin_bit_cast(u32x4, o));
         } else {
@@ -1254,15 +1276,15 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
     const elem* W = reinterpret_cast<const elem*>(reinterpret_cast<const char*>(a.W) + (bh % a.H) * a.w_hs);
     constexpr bool causal = CAUSAL;
     elem* s_w = LD::WS::on ? lds + LD::o_w : nullptr;
-    if (LD::WS::on) stage_w<C>(W, a.L, s_w);
+    if (LD::WS::on) stage_w<C>(W, a.L, s_w, a.dh);
     zero_pads<C, ZV>(s_zr, nullptr);
     __syncthreads();   // W' and the padding are written by all waves, read by each
-    const WSrc<C, LD::WS::on> wsrc{s_w, W, a.L};
+    const WSrc<C, LD::WS::on> wsrc{s_w, W, a.L, a.dh};
     const int64_t nrows = seg1 - seg0;
     const size_t row0 = base + seg0;
-    const rsrc_t rXa = rows_rsrc(a.Xa, row0, nrows, row_bytes<C::F32>());
-    const rsrc_t rZ = rows_rsrc(a.Zsrc, row0, nrows, row_bytes<C::F32>());
-    const rsrc_t rO = rows_rsrc(a.out0, row0, nrows, row_bytes<C::F32>());
+    const rsrc_t rXa = rows_rsrc(a.Xa, row0, nrows, row_bytes<C::F32>(a.dh));
+    const rsrc_t rZ = rows_rsrc(a.Zsrc, row0, nrows, row_bytes<C::F32>(a.dh));
+    const rsrc_t rO = rows_rsrc(a.out0, row0, nrows, row_bytes<C::F32>(a.dh));
     const rsrc_t rD = rows_rsrc(a.Dv, row0, nrows, 4);
     const rsrc_t rAcc = rows_rsrc(a.acc, row0, nrows, DH * 4);
     const rsrc_t rAD = rows_rsrc(a.accD, row0, nrows, 4);
@@ -1285,8 +1307,8 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
         return (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
     };
     auto issue = [&](int it2) {
-        load_row_b<C::F32>(rXa, it2 * TB + own_tok(it2), g, n_xa);
-        load_q16_b<C::F32>(rZ, it2 * TB + tr, tq, n_z);
+        load_row_b<C::F32>(rXa, it2 * TB + own_tok(it2), g, n_xa, a.dh);
+        load_q16_b<C::F32>(rZ, it2 * TB + tr, tq, n_z, a.dh);
     };
     auto issue_planes = [&](int it2, int fb2) { load_planes<C>(prb, it2 * TB + own_tok(it2), fb2, g, pn); };
     issue(0);
@@ -1472,7 +1494,7 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
 #pragma unroll
             for (int at = 0; at < 4; ++at) rd[at] = f_rD[16 * at + ln];
             const float none[4] = {-0.f, -0.f, -0.f, -0.f};   // x + -0 = x: nothing added
-            store_rows_t<C>(rO, it * TB, 16 * w, ln, g, Y, rd, none);
+            store_rows_t<C>(rO, it * TB, 16 * w, ln, g, Y, rd, none, a.dh);
         }
     }
 }
@@ -1552,11 +1574,11 @@ __attribute__((amdgpu_waves_per_eu(BwdQLds<C>::OCC, BwdQLds<C>::OCC))) void k_bw
     const int my = 16 * w + ln;
     const int64_t nrows = seg1 - seg0;
     const size_t row0 = base + seg0;
-    const rsrc_t rZ = rows_rsrc(a.Zsrc, row0, nrows, row_bytes<C::F32>());
-    const rsrc_t rY = rows_rsrc(a.Ysrc, row0, nrows, row_bytes<C::F32>());
-    const rsrc_t rOs = rows_rsrc(a.Osrc, row0, nrows, row_bytes<C::F32>());
-    const rsrc_t rXa = rows_rsrc(a.Xa, row0, nrows, row_bytes<C::F32>());
-    const rsrc_t rOut = rows_rsrc(a.out0, row0, nrows, row_bytes<C::F32>());
+    const rsrc_t rZ = rows_rsrc(a.Zsrc, row0, nrows, row_bytes<C::F32>(a.dh));
+    const rsrc_t rY = rows_rsrc(a.Ysrc, row0, nrows, row_bytes<C::F32>(a.dh));
+    const rsrc_t rOs = rows_rsrc(a.Osrc, row0, nrows, row_bytes<C::F32>(a.dh));
+    const rsrc_t rXa = rows_rsrc(a.Xa, row0, nrows, row_bytes<C::F32>(a.dh));
+    const rsrc_t rOut = rows_rsrc(a.out0, row0, nrows, row_bytes<C::F32>(a.dh));
     const rsrc_t rD = rows_rsrc(a.Dv, row0, nrows, 4);
     const rsrc_t rE = rows_rsrc(a.Ev, row0, nrows, 4);
     const rsrc_t rAcc = rows_rsrc(a.acc, row0, nrows, DH * 4);
@@ -1583,13 +1605,13 @@ __attribute__((amdgpu_waves_per_eu(BwdQLds<C>::OCC, BwdQLds<C>::OCC))) void k_bw
         const int rowi = it * TB + my, rowt = it * TB + tr;
         const bool tok = tr < nv;
         frag zr[2], yr[2], orow[2];
-        if (causal) load_q16_b<C::F32>(rZ, rowt, tq, zr);
-        load_q16_b<C::F32>(rY, rowt, tq, yr);
-        load_q16_b<C::F32>(rOs, rowt, tq, orow);
+        if (causal) load_q16_b<C::F32>(rZ, rowt, tq, zr, a.dh);
+        load_q16_b<C::F32>(rY, rowt, tq, yr, a.dh);
+        load_q16_b<C::F32>(rOs, rowt, tq, orow, a.dh);
         const float dd = tok ? bload_f32(rD, rowt * 4) : 1.f;
         const float inv_a = valid ? bload_f32(pra.inv, rowi * 4) : 1.f;
         typename Prec<C::F32>::half xr[4];
-        load_dx_row<C>(rXa, rowi, g, xr);
+        load_dx_row<C>(rXa, rowi, g, xr, a.dh);
         const bool first = t0 == 0;   // the sub-block that starts the sequence
         if (causal) write_aug<C, C::ROWE, true>(zr, 1.f, tok ? 1.f : 0.f, s_zr);
         // y = [dO / D | e], e = -<dO, O> / D; this thread holds 16 columns of row tr
@@ -1676,7 +1698,7 @@ __attribute__((amdgpu_waves_per_eu(BwdQLds<C>::OCC, BwdQLds<C>::OCC))) void k_bw
         __syncthreads();   // the next sub-block rewrites the y and z rows
         if (a.gmode & ACC_IN) acc_load_row(rAcc, rowi, g, dX);
         if (a.gmode & ACC_OUT) acc_store_row(rAcc, rowi, g, dX);
-        else store_dx<C>(xr, rOut, rowi, g, inv_a, a.beta, dX);
+        else store_dx<C>(xr, rOut, rowi, g, inv_a, a.beta, dX, a.dh);
     }
 }
 
@@ -1797,11 +1819,11 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
     };
     const int64_t nrows = seg1 - seg0;
     const size_t row0 = base + seg0;
-    const rsrc_t rZ = rows_rsrc(a.Zsrc, row0, nrows, row_bytes<C::F32>());
-    const rsrc_t rY = rows_rsrc(a.Ysrc, row0, nrows, row_bytes<C::F32>());
-    const rsrc_t rXa = rows_rsrc(a.Xa, row0, nrows, row_bytes<C::F32>());
-    const rsrc_t rOut0 = rows_rsrc(a.out0, row0, nrows, row_bytes<C::F32>());
-    const rsrc_t rOut1 = rows_rsrc(a.out1, row0, nrows, row_bytes<C::F32>());
+    const rsrc_t rZ = rows_rsrc(a.Zsrc, row0, nrows, row_bytes<C::F32>(a.dh));
+    const rsrc_t rY = rows_rsrc(a.Ysrc, row0, nrows, row_bytes<C::F32>(a.dh));
+    const rsrc_t rXa = rows_rsrc(a.Xa, row0, nrows, row_bytes<C::F32>(a.dh));
+    const rsrc_t rOut0 = rows_rsrc(a.out0, row0, nrows, row_bytes<C::F32>(a.dh));
+    const rsrc_t rOut1 = rows_rsrc(a.out1, row0, nrows, row_bytes<C::F32>(a.dh));
     const rsrc_t rD = rows_rsrc(a.Dv, row0, nrows, 4);
     const rsrc_t rE = rows_rsrc(a.Ev, row0, nrows, 4);
     const rsrc_t rAcc = rows_rsrc(a.acc, row0, nrows, DH * 4);
@@ -1811,11 +1833,11 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
         const int r0 = r0_of(it2);
         if (DK) n_inv = my < nv_of(it2) ? bload_f32(pra.inv, (r0 + my) * 4) : 1.f;
         if (causal) {
-            load_q16_b<C::F32>(rZ, r0 + tr, tq, n_z);
+            load_q16_b<C::F32>(rZ, r0 + tr, tq, n_z, a.dh);
             n_d = bload_f32(rD, (r0 + tr) * 4);
             n_e = bload_f32(rE, (r0 + tr) * 4);
         }
-        if (DK) load_q16_b<C::F32>(rY, r0 + tr, tq, n_y);
+        if (DK) load_q16_b<C::F32>(rY, r0 + tr, tq, n_y, a.dh);
     };
     auto issue_planes = [&](int it2, int fb2) {
         load_planes<C>(pra, r0_of(it2) + my, fb2, g, pa);
@@ -1834,7 +1856,7 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
         if (PREFETCH && it + 1 < nsub) issue(it + 1);
 
         typename Prec<C::F32>::half xr[4];
-        if constexpr (DK) load_dx_row<C>(rXa, r0_of(it) + my, g, xr);
+        if constexpr (DK) load_dx_row<C>(rXa, r0_of(it) + my, g, xr, a.dh);
         const bool first = t0 == 0;   // the sub-block that starts the sequence
         if (causal)
             write_aug<C, LD::ZS>(zr, tok ? rcp_(zd) : 0.f, tok ? ze : 0.f, s_zr,
@@ -1980,13 +2002,13 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
                 acc_store_t(rAcc, r0_of(it), 16 * w, ln, g, Y);
             } else {
                 const float one[4] = {1.f, 1.f, 1.f, 1.f}, zero[4] = {-0.f, -0.f, -0.f, -0.f};   // x + -0 = x
-                store_rows_t<C>(rOut1, r0_of(it), 16 * w, ln, g, Y, one, zero);
+                store_rows_t<C>(rOut1, r0_of(it), 16 * w, ln, g, Y, one, zero, a.dh);
             }
         }
         if constexpr (DK) {
             if (a.gmode & ACC_IN) acc_load_row(rAcc, r0_of(it) + my, g, dX);
             if (a.gmode & ACC_OUT) acc_store_row(rAcc, r0_of(it) + my, g, dX);
-            else store_dx<C>(xr, rOut0, r0_of(it) + my, g, inv_a, a.beta, dX);
+            else store_dx<C>(xr, rOut0, r0_of(it) + my, g, inv_a, a.beta, dX, a.dh);
         }
     }
 }
@@ -1999,7 +2021,7 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
 // (N rows each), so a wave's 16 rows share one head's hyperplanes.
 template <class C>
 __global__ __launch_bounds__(NT) void k_hash(const void* X, const void* Wv, int64_t N, int L, int ld, int H,
-                                             int64_t w_hs, int32_t* __restrict__ ids,
+                                             int64_t w_hs, int dh, int32_t* __restrict__ ids,
                                              unsigned long long* near_zero) {
     using elem = typename Prec<C::F32>::elem;
     using frag = typename Prec<C::F32>::frag;
@@ -2013,12 +2035,12 @@ __global__ __launch_bounds__(NT) void k_hash(const void* X, const void* Wv, int6
     const int64_t r = bh * N + n;
     const elem* W = reinterpret_cast<const elem*>(reinterpret_cast<const char*>(Wv) + (bh % H) * w_hs);
     frag xf[2];
-    load_row_raw<C::F32>(X, valid ? (size_t)r : 0, valid, g, xf);
+    load_row_raw<C::F32>(X, valid ? (size_t)r : 0, valid, g, xf, dh);
     const float inv = row_inv_norm<C::F32>(xf);
     unsigned int nz = 0;
 #pragma unroll
     for (int t = 0; t < C::MT; ++t) {
-        const f32x4 acc = project_global<C>(W, L, t, ln, g, xf);
+        const f32x4 acc = project_global<C>(W, L, t, ln, g, xf, dh);
         if constexpr (C::Pp == 8) {
             // a table's planes 0-3 in the even lane group, 4-7 in the odd one
             const int table = t * C::TPT + (g >> 1);

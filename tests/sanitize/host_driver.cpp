@@ -35,6 +35,8 @@ static int check_shape(int64_t B, int64_t H, int64_t N, int d, int P, int L, int
         const WsLayout w = ws_layout(s, dv, kind);
         bad |= w.total < w.scan;
         if (kind == WS_BWD_RECOMPUTE) bad |= w.total < sl.total;
+        // the group partials are addressed as [rows][64] float32 whatever d is
+        if (dv.G > 1) bad |= w.accD < w.acc + (size_t)dv.BH * (size_t)N * 64 * sizeof(float);
     }
     for (int g = 0; g < dv.G; ++g) {
         const int segs = scan_segs(s, dv, group(dv, g).F65);
@@ -60,6 +62,7 @@ int main() {
     const int64_t big[][3] = {{1ll << 40, 1ll << 20, 1ll << 20}, {1, 70000, 10}, {INT64_MAX, 1, 1}, {1, 1, INT64_MAX}};
     for (auto& b : big) bad |= check_shape(b[0], b[1], b[2], 64, 4, 8, 1, 16, n_ok);
     for (int d : {0, 32, 63, 65, 128}) bad |= check_shape(1, 1, 10, d, 4, 8, 1, 16, n_ok);
+    for (int P : {4, 5}) bad |= check_shape(2, 2, 500, 32, P, 40, 1, 128, n_ok);   // d = 32 with table groups
     std::printf("host driver: %d of %d shapes valid, %s\n", n_ok, n_all, bad ? "FAILED" : "ok");
     return bad ? 1 : 0;
 }

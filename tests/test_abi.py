@@ -117,7 +117,7 @@ def test_workspace_kind_rejected():
 @pytest.mark.parametrize("args,code", [
     ((0, 1, 10, 64, 4, 8, 1, 16, 0), race.RACE_ERR_INVALID_ARG),        # B = 0
     ((1, 1, 0, 64, 4, 8, 1, 16, 0), race.RACE_ERR_INVALID_ARG),         # N = 0
-    ((1, 1, 10, 32, 4, 8, 1, 16, 0), race.RACE_ERR_UNSUPPORTED),        # d != 64
+    ((1, 1, 10, 48, 4, 8, 1, 16, 0), race.RACE_ERR_UNSUPPORTED),        # d not 32 or 64
     ((1, 1, 10, 64, 7, 8, 1, 16, 0), race.RACE_ERR_UNSUPPORTED),        # P > 6
     ((1, 1, 10, 64, 0, 8, 1, 16, 0), race.RACE_ERR_INVALID_ARG),        # P = 0
     ((1, 1, 10, 64, 4, 4097, 1, 16, 0), race.RACE_ERR_UNSUPPORTED),     # L * 2^P > 2^16
@@ -238,7 +238,7 @@ def test_prefill_and_decode_argument_errors():
         assert L.race_attn_decode(*bad, None) == race.RACE_ERR_INVALID_ARG, i
     bad = list(dec); bad[6] = 1 << 31   # more tokens than a 32-bit count
     assert L.race_attn_decode(*bad, None) == race.RACE_ERR_UNSUPPORTED
-    for i, v in [(7, 32), (8, 7), (9, 4097)]:
+    for i, v in [(7, 48), (8, 7), (9, 4097)]:
         bad = list(dec); bad[i] = v
         assert L.race_attn_decode(*bad, None) == race.RACE_ERR_UNSUPPORTED, i
 

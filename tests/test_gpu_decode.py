@@ -59,7 +59,7 @@ def gpu_steps(race, x, n0, T, P, L, beta, chunk):
         state = race.prefill(t["K"][:, :, :n0].contiguous(), t["V"][:, :, :n0].contiguous(), t["W"], P, L,
                              beta, chunk)
     else:
-        state = race.alloc_state(B, H, P, L, dev)
+        state = race.alloc_state(B, H, P, L, dev, t["Q"].shape[-1])
     outs = []
     for s in range(T):
         i = n0 + s
@@ -217,7 +217,7 @@ def gpu_multi(race, x, n0, T, P, L, beta, chunk):
         state = race.prefill(t["K"][:, :, :n0].contiguous(), t["V"][:, :, :n0].contiguous(), t["W"], P, L,
                              beta, chunk)
     else:
-        state = race.alloc_state(B, H, P, L, dev)
+        state = race.alloc_state(B, H, P, L, dev, t["Q"].shape[-1])
     q, k, v = (t[n][:, :, n0:n0 + T].contiguous() for n in ("Q", "K", "V"))
     o = race.decode(q, k, v, t["W"], state, P, L, beta)
     torch.cuda.synchronize()
@@ -304,3 +304,16 @@ def test_decode_masses_count_beyond_2_24(lib, dtype):
     empty = [64 * (tb // 4) + 8 * (tb % 4) for tb in range(L)]
     assert np.all(delta[:, empty] == 1.0)
     assert np.all(after.cpu().numpy()[:, empty] == before.cpu().numpy()[:, empty] + 1.0)
+
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("P,L", [(4, 16), (4, 40), (2, 8)])
+def test_decode_head_dim_32(lib, dtype, P, L):
+    """Prefill, one-token steps and a seven-token call with 32-element rows."""
+    B, H, n0, T = 1, 2, 120, 7
+    x = host_inputs(3300 + L, B, H, n0 + T, 32, P, L, dtype)
+    ref = oracle_steps(x, n0, T, 1.0)
+    check(gpu_steps(lib, x, n0, T, P, L, 1.0, 64), ref, dtype, "d32 steps")
+    res, _ = gpu_multi(lib, x, n0, T, P, L, 1.0, 64)
+    check(res, ref, dtype, "d32 multi")

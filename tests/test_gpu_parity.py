@@ -29,16 +29,16 @@ def lib():
 
 
 def run_case(race, B, H, N, P, L, dtype, causal, chunk, beta=1.0, dist="normal", seed=1234,
-             backward=True, check=True):
+             backward=True, check=True, d=64):
     import torch
-    print(f"[case] B={B} H={H} N={N} P={P} L={L} {dtype} causal={causal} chunk={chunk} "
+    print(f"[case] B={B} H={H} N={N} d={d} P={P} L={L} {dtype} causal={causal} chunk={chunk} "
           f"beta={beta} dist={dist} seed={seed} bwd={backward}", flush=True)
-    x = host_inputs(seed, B, H, N, 64, P, L, dtype, dist)
+    x = host_inputs(seed, B, H, N, d, P, L, dtype, dist)
     dev = torch.device("cuda:0")
     T = {k: to_torch(v, dev) for k, v in x.items()}
     # the training path: the forward keeps its sketch states and denominators,
     # the backward takes them with O
-    saved = race.alloc_saved(B, H, N, P, L, causal, chunk, dev) if backward else None
+    saved = race.alloc_saved(B, H, N, P, L, causal, chunk, dev, d) if backward else None
     O = race.forward(T["Q"], T["K"], T["V"], T["W"], P, L, beta, causal, chunk, saved=saved)
     grads = None
     if backward:
@@ -434,3 +434,42 @@ def test_per_head_hyperplanes_decode(lib, dtype):
             S, z, o = dense.decode_step(S, z, Q[i], K[i], V[i], W64, 0.9)
             err = rel_l2(outs[s][0, h], o)
             assert err <= (1e-5 if dtype == "f32" else 5e-3), (h, s, err)
+
+
+
+# --- head dimension 32 ----------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,causal,P,L", [("bf16", True, 4, 16), ("bf16", False, 4, 20), ("f32", True, 2, 8),
+                                             ("f32", False, 4, 5), ("bf16", True, 5, 9), ("bf16", True, 4, 40)])
+def test_head_dim_32(lib, dtype, causal, P, L):
+    # rows of 32 elements (the kernels' columns 32..63 load as zeros and are
+    # never stored); (4, 20), (5, 9) and (4, 40) also run as table groups
+    run_case(lib, 2, 2, 500, P, L, dtype, causal, 128, beta=1.2, seed=3232, d=32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_head_dim_32_hash_and_hard(lib, dtype):
+    import math
+    import torch
+    from oracle import dense
+    P, L, N = 4, 8, 300
+    for seed in range(320, 380):
+        x = host_inputs(seed, 1, 2, N, 32, P, L, dtype)
+        W64 = to_f64(x["W"])
+        X = np.concatenate([to_f64(x["Q"]).reshape(-1, 32), to_f64(x["K"]).reshape(-1, 32)])
+        h = np.einsum("nd,lpd->nlp", X / np.linalg.norm(X, axis=1, keepdims=True), W64)
+        if np.min(np.abs(h)) > 1e-5:
+            break
+    else:
+        pytest.fail("no seed with every projection away from zero")
+    dev = torch.device("cuda:0")
+    T = {k: to_torch(v, dev) for k, v in x.items()}
+    ids, _ = lib.hard_hash(T["Q"], T["W"], P, L)
+    O = from_torch(lib.forward(T["Q"], T["K"], T["V"], T["W"], P, L, math.inf, True, 64))
+    torch.cuda.synchronize()
+    ref_ids, _ = oracle.hard_hash(x["Q"], W64)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    ref = np.stack([dense.hard_forward(to_f64(x["Q"])[0, h_], to_f64(x["K"])[0, h_], to_f64(x["V"])[0, h_],
+                                       W64, True) for h_ in range(2)])[None]
+    assert np.array_equal(np.all(O == 0.0, axis=-1), np.all(ref == 0.0, axis=-1))
+    assert rel_l2(O, ref) <= TOL[dtype]
