@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libraceattn.so")
-SOURCES = ["race_abi.hip", "race_bf16.hip", "race_f32.hip"]
+SOURCES = ["race_abi.hip", "race_bf16.hip", "race_f32.hip", "race_h2_bf16.hip", "race_h2_f32.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -40,6 +40,11 @@ struct Call {
 template <bool F32>
 race_status_t dispatch(const Shape& s, const Derived& d, const WsLayout& wl, const Call& c);
 
+// Forward and backward at head dimension 128 (race_h2.hpp, built in
+// translation units of their own).
+template <bool F32>
+race_status_t dispatch_h2(const Shape& s, const Derived& d, const WsLayout& wl, const Call& c);
+
 // Profiling aid (race_attn_profile_events): records a caller-owned event on the
 // stream before each launch of the current call, when enabled on this thread.
 void profile_mark(const char* stage, hipStream_t stream);
@@ -84,18 +89,21 @@ inline int64_t w_head_bytes(const Shape& s, bool f32) {
     return s.w_per_head ? (int64_t)s.L * s.P * s.d * (f32 ? 4 : 2) : 0;
 }
 
-// CACHED = false: sketch of K, [V | 1] (storing the keys' plane values in pc);
-// CACHED = true: gradient sketch of the queries from their plane values pc.
-template <class C, bool CACHED>
+// CACHED = false: sketch of K, [V | 1] (storing the keys' plane values in pc,
+// or with PG reading them from pc); CACHED = true: gradient sketch of the
+// queries from their plane values pc. Head dimension 128 passes one value
+// half: rows rs = 128 apart, dh = 64 columns, e = 0 in the second (ezero).
+template <class C, bool CACHED, bool PG = false>
 race_status_t run_totals(const Shape& s, const Derived& d, const Group& gr, const void* Xb, const void* Z,
                          const float* Dv, const float* Ev, const PlaneCache& pc, const void* W, float beta,
-                         float* out, hipStream_t st) {
+                         float* out, hipStream_t st, int rs = 0, int dh = 0, int ezero = 0) {
     TotArgs a;
     a.Xb = Xb; a.Z = Z; a.Dv = Dv; a.Ev = Ev; a.W = W; a.pc = pc; a.out = out;
     a.N = s.N; a.chunk = s.chunk; a.nchunks = (int)d.NC; a.L = gr.L; a.beta = beta;
-    a.H = (int)s.H; a.w_hs = w_head_bytes(s, C::F32); a.dh = s.d;
+    a.H = (int)s.H; a.w_hs = w_head_bytes(s, C::F32); a.dh = dh ? dh : s.d; a.rs = rs ? rs : s.d;
+    a.ezero = ezero;
     profile_mark(CACHED ? "totals_qg" : "totals_kv", st);
-    hipLaunchKernelGGL((k_totals<C, CACHED>), dim3((unsigned)d.NC, (unsigned)d.BH), dim3(NT), 0, st, a);
+    hipLaunchKernelGGL((k_totals<C, CACHED, PG>), dim3((unsigned)d.NC, (unsigned)d.BH), dim3(NT), 0, st, a);
     return launch_ok();
 }
 
@@ -137,7 +145,9 @@ enum { PASS_FWD = 0, PASS_BWD_Q = 1, PASS_BWD_V = 2, PASS_BWD_K = 3 };
 template <class C>
 using Blk2Cfg = Cfg<C::P, C::MT, C::F32, C::F32 ? 0 : (C::KB > 2 ? C::KB : 2)>;
 
-template <class C, int KIND>
+// H2: the head-dimension-128 forms (the forward reads the queries' plane
+// values, the query and key gradient passes leave per-plane gradients).
+template <class C, int KIND, bool H2 = false>
 race_status_t run_pass(const Shape& s, const Derived& d, PassArgs a, hipStream_t st) {
     a.N = s.N; a.chunk = s.chunk; a.causal = s.causal;
     const dim3 grid((unsigned)d.NC, (unsigned)d.BH), block(NT);
@@ -151,18 +161,18 @@ race_status_t run_pass(const Shape& s, const Derived& d, PassArgs a, hipStream_t
     if constexpr (KIND == PASS_FWD) {
         profile_mark("pass_fwd", st);
         if constexpr (CAUSAL_OK) {
-            if (s.causal) hipLaunchKernelGGL((k_fwd<CB, true>), grid, block, 0, st, a);
-            else hipLaunchKernelGGL((k_fwd<CB, false>), grid, block, 0, st, a);
+            if (s.causal) hipLaunchKernelGGL((k_fwd<CB, true, H2>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((k_fwd<CB, false, H2>), grid, block, 0, st, a);
         } else {
-            hipLaunchKernelGGL((k_fwd<CB, false>), grid, block, 0, st, a);
+            hipLaunchKernelGGL((k_fwd<CB, false, H2>), grid, block, 0, st, a);
         }
     } else if constexpr (KIND == PASS_BWD_Q) {
         profile_mark("pass_bwd_q", st);
         if constexpr (CAUSAL_OK) {
-            if (s.causal) hipLaunchKernelGGL((k_bwd_q<CB, true>), grid, block, 0, st, a);
-            else hipLaunchKernelGGL((k_bwd_q<CB, false>), grid, block, 0, st, a);
+            if (s.causal) hipLaunchKernelGGL((k_bwd_q<CB, true, H2>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((k_bwd_q<CB, false, H2>), grid, block, 0, st, a);
         } else {
-            hipLaunchKernelGGL((k_bwd_q<CB, false>), grid, block, 0, st, a);
+            hipLaunchKernelGGL((k_bwd_q<CB, false, H2>), grid, block, 0, st, a);
         }
     } else if constexpr (KIND == PASS_BWD_V) {
         profile_mark("pass_bwd_v", st);
@@ -175,10 +185,10 @@ race_status_t run_pass(const Shape& s, const Derived& d, PassArgs a, hipStream_t
     } else {
         profile_mark("pass_bwd_k", st);
         if constexpr (CAUSAL_OK) {
-            if (s.causal) hipLaunchKernelGGL((k_bwd_k<CB, true, KPART_DK>), grid, block, 0, st, a);
-            else hipLaunchKernelGGL((k_bwd_k<CB, false, KPART_DK>), grid, block, 0, st, a);
+            if (s.causal) hipLaunchKernelGGL((k_bwd_k<CB, true, KPART_DK, H2>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((k_bwd_k<CB, false, KPART_DK, H2>), grid, block, 0, st, a);
         } else {
-            hipLaunchKernelGGL((k_bwd_k<CB, false, KPART_DK>), grid, block, 0, st, a);
+            hipLaunchKernelGGL((k_bwd_k<CB, false, KPART_DK, H2>), grid, block, 0, st, a);
         }
     }
     return launch_ok();
@@ -186,7 +196,7 @@ race_status_t run_pass(const Shape& s, const Derived& d, PassArgs a, hipStream_t
 
 // Launch one pass of every table group in order: group g adds to the partial
 // outputs of the groups before it, the last one finishes the outputs.
-template <bool F32, int KIND>
+template <bool F32, int KIND, bool H2 = false>
 race_status_t run_pass_groups(const Shape& s, const Derived& d, const WsLayout& wl, char* ws, PassArgs a,
                               hipStream_t st, const std::function<void(const Group&, PassArgs&)>& per_group) {
     for (int g = 0; g < d.G; ++g) {
@@ -197,13 +207,14 @@ race_status_t run_pass_groups(const Shape& s, const Derived& d, const WsLayout& 
         ag.w_hs = w_head_bytes(s, F32);
         ag.wt_hs = s.w_per_head ? (int64_t)wt_bytes(d) : 0;
         ag.dh = s.d;
+        ag.rs = s.d;
         ag.gmode = (g > 0 ? ACC_IN : 0) | (g + 1 < d.G ? ACC_OUT : 0);
         ag.acc = d.G > 1 ? reinterpret_cast<float*>(ws + wl.acc) : nullptr;
         ag.accD = d.G > 1 ? reinterpret_cast<float*>(ws + wl.accD) : nullptr;
         per_group(gr, ag);
         RACE_TRY((with_cfg<F32>(s.P, gr.MT, [&](auto tag) {
             using C = typename decltype(tag)::type;
-            return run_pass<C, KIND>(s, d, ag, st);
+            return run_pass<C, KIND, H2>(s, d, ag, st);
         })));
     }
     return RACE_OK;
@@ -290,7 +301,7 @@ race_status_t run_backward(const Shape& s, const Derived& d, const WsLayout& wl,
             hipLaunchKernelGGL(k_prep<C>, dim3(8, (unsigned)hw), dim3(256), 0, st,
                                reinterpret_cast<const elem*>(group_w(c.W, s, gr, F32)), gr.L, wtp(g),
                                w_head_bytes(s, F32) / (int64_t)sizeof(elem),
-                               s.w_per_head ? (int64_t)(wt_bytes(d) / sizeof(elem)) : 0, s.d);
+                               s.w_per_head ? (int64_t)(wt_bytes(d) / sizeof(elem)) : 0, s.d, d.NDT);
             return launch_ok();
         })));
     }
@@ -366,6 +377,10 @@ race_status_t dispatch(const Shape& s, const Derived& d, const WsLayout& wl, con
             })));
         }
         return RACE_OK;
+    }
+    if (d.VH == 2) {
+        if (c.op == OP_FWD || c.op == OP_BWD) return dispatch_h2<F32>(s, d, wl, c);
+        return RACE_ERR_UNSUPPORTED;   // prefill and decode: head dimension 64 or 32
     }
     if (c.op == OP_FWD) return run_forward<F32>(s, d, wl, c, c.O, c.saved_out);
     if (c.op == OP_BWD) return run_backward<F32>(s, d, wl, c);

@@ -37,6 +37,11 @@ struct Derived {
     int64_t RSall;           // the running state of one head, in floats: per group F x 64
                              // float32 value sums and F float64 masses (66 F floats)
     int64_t BH, NC;
+    // Head dimension 128: the sketch passes run once per half of the value
+    // columns (64 each), on plane values computed beforehand from the whole
+    // 128-dimensional rows; VH = 2 sets of sketch states. Otherwise VH = 1.
+    int VH;
+    int NDT;   // 16-column tiles of the back-projection operands: 8 at head dimension 128, else 4
 };
 
 // Largest number of table groups (launches per pass): L * 2^P <= 2^16 features.
@@ -55,6 +60,9 @@ struct WsLayout {
     size_t scan;   // segment sums of the segmented chunk scan (when used)
     size_t acc;    // more than one table group: partial outputs [rows][64], float32
     size_t accD;   // and the forward's partial denominators [rows]
+    size_t Qc;     // head dimension 128, forward without saved: the queries' plane values
+    size_t dhQ;    // head dimension 128, backward: gradients wrt the queries' and keys'
+    size_t dhK;    // normalised projections, float32, laid out as the plane values
     size_t total;
 };
 
@@ -98,7 +106,7 @@ inline bool mul_ok(int64_t a, int64_t b, int64_t& out) {
 inline race_status_t derive(const Shape& s, Derived& d) {
     if (s.B < 1 || s.H < 1 || s.N < 1 || s.d < 1 || s.P < 1 || s.L < 1 || s.chunk < 1)
         return RACE_ERR_INVALID_ARG;
-    if ((s.d != 64 && s.d != 32) || s.P > 6) return RACE_ERR_UNSUPPORTED;
+    if ((s.d != 64 && s.d != 32 && s.d != 128) || s.P > 6) return RACE_ERR_UNSUPPORTED;
     // in-chunk byte offsets (rows of up to 512 bytes) are 32-bit
     if (s.chunk > MAX_CHUNK) return RACE_ERR_UNSUPPORTED;
     // planes per table padded to 1, 2, 4 or 8 (P = 5, 6: two lane groups)
@@ -138,6 +146,8 @@ inline race_status_t derive(const Shape& s, Derived& d) {
     d.F65l = (int64_t)d.Fl * 65;
     d.F65all = (int64_t)(d.G - 1) * d.F65 + d.F65l;
     d.RSall = (int64_t)(d.G - 1) * d.F * 66 + (int64_t)d.Fl * 66;
+    d.VH = s.d == 128 ? 2 : 1;
+    d.NDT = s.d == 128 ? 8 : 4;
     if (d.BH > 65535 || d.NC > 0x7fffffff) return RACE_ERR_UNSUPPORTED;
     return RACE_OK;
 }
@@ -182,8 +192,13 @@ inline size_t all_states_bytes(const Derived& d, int64_t per_head) {
            sizeof(float);
 }
 
+// Sketch states of value half h (head dimension 128: two sets, one after the other).
+inline size_t half_states_floats(const Derived& d, int64_t per_head, int h) {
+    return (size_t)h * all_states_bytes(d, per_head) / sizeof(float);
+}
+
 inline SavedLayout saved_layout(const Shape& s, const Derived& d) {
-    const size_t states = all_states_bytes(d, s.causal ? d.NC : 1);
+    const size_t states = (size_t)d.VH * all_states_bytes(d, s.causal ? d.NC : 1);
     const size_t cache = cache_layout(s, d).total;
     SavedLayout l;
     l.D = align256(states);
@@ -210,12 +225,14 @@ inline int scan_segs(const Shape& s, const Derived& d, int64_t F65) {
 }
 
 // Back-projection operand table of one group (k_prep), sized for float32.
-inline size_t wt_bytes(const Derived& d) { return align256((size_t)d.NPAIR * 4 * 64 * 8 * sizeof(float)); }
+inline size_t wt_bytes(const Derived& d) {
+    return align256((size_t)d.NPAIR * (size_t)d.NDT * 64 * 8 * sizeof(float));
+}
 
 inline WsLayout ws_layout(const Shape& s, const Derived& d, int kind) {
     WsLayout w{};
-    const size_t chunks = all_states_bytes(d, d.NC);
-    const size_t totals = all_states_bytes(d, 1);
+    const size_t chunks = (size_t)d.VH * all_states_bytes(d, d.NC);
+    const size_t totals = (size_t)d.VH * all_states_bytes(d, 1);
     const size_t tokens = (size_t)d.BH * (size_t)s.N;
     size_t off = 0;
     if (kind != WS_BWD) {
@@ -234,6 +251,17 @@ inline WsLayout ws_layout(const Shape& s, const Derived& d, int kind) {
     if (kind == WS_BWD_RECOMPUTE) {
         w.Sv = off;  off = align256(off + saved_bytes(s, d));
         w.Ov = off;  off = align256(off + tokens * (size_t)s.d * sizeof(float));
+    }
+    // head dimension 128: the queries' plane values (the forward reads them
+    // instead of projecting), and the per-plane gradients of both sides
+    if (d.VH == 2) {
+        if (kind == WS_FWD) {
+            w.Qc = off;  off = align256(off + cache_layout(s, d).total);
+        }
+        if (kind == WS_BWD || kind == WS_BWD_RECOMPUTE) {
+            w.dhQ = off; off = align256(off + cache_layout(s, d).total);
+            w.dhK = off; off = align256(off + cache_layout(s, d).total);
+        }
     }
     // partial outputs of the groups before the last: [rows][64] (the
     // kernels' working width, whatever the head dimension) and the forward's

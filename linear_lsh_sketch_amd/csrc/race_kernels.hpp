@@ -46,17 +46,19 @@ enum { SCAN_EXCL = 0, SCAN_REV_EXCL = 1, SCAN_TOTAL = 2 };
 // of tile 2m for j < 4, row 4g+j-4 of tile 2m+1 otherwise).
 // ---------------------------------------------------------------------------
 // One table per head of W (blockIdx.y; heads w_hs elements apart in W and
-// wt_hs apart in WTp: 0 and 0 when W is shared).
+// wt_hs apart in WTp: 0 and 0 when W is shared). ndt 16-column tiles per
+// tile pair: 4 (head dimension 64 or 32) or 8 (128).
 template <class C>
 __global__ void k_prep(const typename Prec<C::F32>::elem* __restrict__ W, int L,
-                       typename Prec<C::F32>::elem* __restrict__ WTp, int64_t w_hs, int64_t wt_hs, int dh) {
+                       typename Prec<C::F32>::elem* __restrict__ WTp, int64_t w_hs, int64_t wt_hs, int dh,
+                       int ndt) {
     using elem = typename Prec<C::F32>::elem;
     W += blockIdx.y * w_hs;
     WTp += blockIdx.y * wt_hs;
-    const int n2 = C::NPAIR * 4 * 64 * 8;
+    const int n2 = C::NPAIR * ndt * 64 * 8;
     for (int k = blockIdx.x * blockDim.x + threadIdx.x; k < n2; k += gridDim.x * blockDim.x) {
         elem v = to_elem<C::F32>(0.f);
-        const int m = k / 2048, dt = (k / 512) & 3, l = (k / 8) & 63, j = k & 7;
+        const int m = k / (ndt * 512), dt = (k / 512) % ndt, l = (k / 8) & 63, j = k & 7;
         const int d = 16 * dt + (l & 15);
         const int tile = 2 * m + (j >> 2);
         const int ri = 4 * (l >> 4) + (j & 3);
@@ -141,21 +143,22 @@ template <bool F32>
 __device__ inline int row_bytes(int dh) { return dh * (F32 ? 4 : 2); }
 
 // This lane's projection operand of in-chunk row rowi: K positions 32 s + 8 g .. +7.
+// (rs: elements between rows; dh: columns of the row that exist.)
 template <bool F32>
-__device__ inline void load_row_b(rsrc_t r, int rowi, int g, typename Prec<F32>::frag x[2], int dh) {
+__device__ inline void load_row_b(rsrc_t r, int rowi, int g, typename Prec<F32>::frag x[2], int rs, int dh) {
     constexpr int es = F32 ? 4 : 2;
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-        x[s] = 32 * s < dh ? bload_frag<F32>(r, rowi * row_bytes<F32>(dh) + (32 * s + 8 * g) * es) : zero_frag<F32>();
+        x[s] = 32 * s < dh ? bload_frag<F32>(r, rowi * row_bytes<F32>(rs) + (32 * s + 8 * g) * es) : zero_frag<F32>();
 }
 
 // Columns 16 q .. 16 q + 15 of in-chunk row rowi.
 template <bool F32>
-__device__ inline void load_q16_b(rsrc_t r, int rowi, int q, typename Prec<F32>::frag v[2], int dh) {
+__device__ inline void load_q16_b(rsrc_t r, int rowi, int q, typename Prec<F32>::frag v[2], int rs, int dh) {
     constexpr int es = F32 ? 4 : 2;
     if (16 * q < dh) {
-        v[0] = bload_frag<F32>(r, rowi * row_bytes<F32>(dh) + 16 * q * es);
-        v[1] = bload_frag<F32>(r, rowi * row_bytes<F32>(dh) + (16 * q + 8) * es);
+        v[0] = bload_frag<F32>(r, rowi * row_bytes<F32>(rs) + 16 * q * es);
+        v[1] = bload_frag<F32>(r, rowi * row_bytes<F32>(rs) + (16 * q + 8) * es);
     } else {
         v[0] = zero_frag<F32>();
         v[1] = zero_frag<F32>();
@@ -179,7 +182,7 @@ __device__ inline void load_row_raw(const void* X, size_t row, bool valid, int g
 // products, float32 sums) and one hardware reciprocal square root of
 // max(|x|^2, eps^2).
 template <bool F32>
-__device__ inline float row_inv_norm(const typename Prec<F32>::frag x[2]) {
+__device__ inline float row_sumsq(const typename Prec<F32>::frag x[2]) {
     float ss = 0.f;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -195,7 +198,11 @@ __device__ inline float row_inv_norm(const typename Prec<F32>::frag x[2]) {
             }
         }
     }
-    ss = sum_groups(ss);
+    return ss;
+}
+template <bool F32>
+__device__ inline float row_inv_norm(const typename Prec<F32>::frag x[2]) {
+    const float ss = sum_groups(row_sumsq<F32>(x));
     return __builtin_amdgcn_rsqf(fmaxf(ss, NORM_EPS * NORM_EPS));
 }
 
@@ -678,7 +685,9 @@ struct TotArgs {
     float beta;
     int H;               // heads (W of sequence bh: W + (bh % H) * w_hs bytes)
     int64_t w_hs;        // bytes between the heads' hyperplanes; 0: one W for all
-    int dh;              // head dimension: 64, or 32 (columns 32..63 zero)
+    int dh;              // columns of a row the kernels use: 64, or 32 (columns 32..63 zero)
+    int rs;              // elements between consecutive rows (the head dimension)
+    int ezero;           // gradient sketch: e taken as 0 (the second value half of d = 128)
 };
 
 template <class C, bool CACHED>
@@ -692,13 +701,16 @@ struct TotLds {
 };
 
 // CACHED = false: sketch of the keys, [v | 1], projecting K (and storing the
-// keys' plane values); CACHED = true: gradient sketch of the queries,
-// [dO/D | e], from the queries' stored plane values.
-template <class C, bool CACHED>
+// keys' plane values), or with PG from the keys' plane values computed
+// beforehand (head dimension 128); CACHED = true: gradient sketch of the
+// queries, [dO/D | e] (e taken as 0 when a.ezero), from the queries' stored
+// plane values.
+template <class C, bool CACHED, bool PG = false>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 3))) void k_totals(TotArgs a) {
     using elem = typename Prec<C::F32>::elem;
     using frag = typename Prec<C::F32>::frag;
-    using LD = TotLds<C, CACHED>;
+    constexpr bool FC = CACHED || PG;   // features from stored plane values
+    using LD = TotLds<C, FC>;
     __shared__ __attribute__((aligned(32))) elem lds[LD::n_elem];
     elem* s_rows = lds;
     elem* s_zr = lds + LD::n_rows;
@@ -716,14 +728,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 3))) void
     const int nsub = (int)((seg1 - seg0 + TB - 1) / TB);
     const int my = 16 * w + ln;
     const elem* Wh = reinterpret_cast<const elem*>(reinterpret_cast<const char*>(a.W) + (bh % a.H) * a.w_hs);
-    if (!CACHED) stage_w<C>(Wh, a.L, s_w, a.dh);
+    if (!FC) stage_w<C>(Wh, a.L, s_w, a.dh);
     zero_pads<C, ZV>(s_zr, nullptr);
     __syncthreads();   // W' and the padding are written by all waves, read by each
     const WSrc<C> wsrc{s_w, Wh, a.L, a.dh};
     const int64_t nrows = seg1 - seg0;
     const size_t row0 = base + seg0;
-    const rsrc_t rX = rows_rsrc(CACHED ? nullptr : a.Xb, row0, nrows, row_bytes<C::F32>(a.dh));
-    const rsrc_t rZ = rows_rsrc(a.Z, row0, nrows, row_bytes<C::F32>(a.dh));
+    const rsrc_t rX = rows_rsrc(FC ? nullptr : a.Xb, row0, nrows, row_bytes<C::F32>(a.rs));
+    const rsrc_t rZ = rows_rsrc(a.Z, row0, nrows, row_bytes<C::F32>(a.rs));
     const rsrc_t rD = rows_rsrc(CACHED ? a.Dv : nullptr, row0, nrows, 4);
     const rsrc_t rE = rows_rsrc(CACHED ? a.Ev : nullptr, row0, nrows, 4);
     const PlaneRows pr = plane_rows<C>(a.pc, row0, nrows);
@@ -744,8 +756,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 3))) void
     };
     auto issue = [&](int it2) {
         const int r0 = it2 * TB;
-        if (!CACHED) load_row_b<C::F32>(rX, r0 + my, g, nx, a.dh);
-        load_q16_b<C::F32>(rZ, r0 + tr, tq, nz, a.dh);
+        if (!FC) load_row_b<C::F32>(rX, r0 + my, g, nx, a.rs, a.dh);
+        load_q16_b<C::F32>(rZ, r0 + tr, tq, nz, a.rs, a.dh);
         if (CACHED) {
             nd = bload_f32(rD, (r0 + tr) * 4);
             ne = bload_f32(rE, (r0 + tr) * 4);
@@ -753,7 +765,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 3))) void
     };
     auto issue_planes = [&](int it2, int fb2) { load_planes<C>(pr, it2 * TB + my, fb2, g, pn); };
     issue(0);
-    if (CACHED) issue_planes(0, 0);
+    if (FC) issue_planes(0, 0);
     for (int it = 0; it < nsub; ++it) {
         const int64_t t0 = seg0 + (int64_t)it * TB;
         const int nv = nv_of(it);
@@ -762,17 +774,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 3))) void
         const float dz = nd, ez = ne;
         if (it + 1 < nsub) issue(it + 1);
         float inv = 0.f;
-        if (!CACHED) {
+        if (!FC) {
             inv = row_inv_norm<C::F32>(xf);
             if (g == 0) bstore_f32(pr.inv, rowi * 4, inv);
         }
         const bool ok = tr < nv;
         if (!CACHED) write_aug<C, ZV, true>(zr, 1.f, ok ? 1.f : 0.f, s_zr);
-        else write_aug<C, ZV>(zr, ok ? rcp_(dz) : 0.f, ok ? ez : 0.f, s_zr);
+        else write_aug<C, ZV>(zr, ok ? rcp_(dz) : 0.f, (ok && !a.ezero) ? ez : 0.f, s_zr);
 #pragma unroll
         for (int fb = 0; fb < C::NBLK; ++fb) {
             frag unused[C::FBK];
-            if constexpr (CACHED) {
+            if constexpr (FC) {
                 const Planes<C> pl = pn;
                 if (fb + 1 < C::NBLK) issue_planes(it, fb + 1);
                 else if (it + 1 < nsub) issue_planes(it + 1, 0);
@@ -928,10 +940,33 @@ struct PassArgs {
     int H;                 // heads: W of sequence bh at W + (bh % H) * w_hs bytes, its
     int64_t w_hs;          // back-projection table at WTp + (bh % H) * wt_hs bytes
     int64_t wt_hs;         // (both 0 when one W serves every head)
-    int dh;                // head dimension: 64, or 32 (columns 32..63 zero)
+    int dh;                // columns of a row the kernels use: 64, or 32 (columns 32..63 zero)
+    int rs;                // elements between consecutive rows (the head dimension)
+    // Head dimension 128 (the H2 forms of the gradient passes): the pass
+    // covers value half `half` (64 columns); e comes from Ev in half 0 and is
+    // 0 in half 1 (the mass terms count once), and instead of dQ or dK the
+    // pass leaves the gradient wrt each normalised projection in dhb
+    // ([rows][NPL] float32 of this group; half 1 adds to half 0's).
+    float* dhb;
+    int half;
 };
 
 enum { ACC_IN = 1, ACC_OUT = 2 };
+
+// Head dimension 128: the per-plane gradient (dh / beta, as monomial_backward
+// gives it) of projection tile t of in-chunk row rowi, stored, or added to the
+// first value half's, in the group's [rows][NPL] float32 table.
+template <class C>
+__device__ inline void put_dh(rsrc_t rdh, int rowi, int t, int g, const float dh[4], bool add) {
+    const int off = (rowi * C::NPL + 16 * t + 4 * g) * 4;
+    f32x4 v = {dh[0], dh[1], dh[2], dh[3]};
+    if (add) {
+        const f32x4 prev = __builtin_bit_cast(f32x4, bload128(rdh, off));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] += prev[i];
+    }
+    bstore128(rdh, off, __builtin_bit_cast(u32x4, v));
+}
 
 // Partial output rows of one lane in the transposed read-out layout
 // (columns cb + 4 g .. +3 of rows r0 + 16 at + ln), float32.
@@ -1112,11 +1147,11 @@ __device__ inline void intra_operand(const typename Prec<C::F32>::elem* s_zr, co
 // The own token's row values that store_dx needs (columns 16 dt + 4 g .. +3),
 // loaded early so the memory latency overlaps the sub-block's work.
 template <class C>
-__device__ inline void load_dx_row(rsrc_t rX, int rowi, int g, typename Prec<C::F32>::half (&xr)[4], int dh) {
+__device__ inline void load_dx_row(rsrc_t rX, int rowi, int g, typename Prec<C::F32>::half (&xr)[4], int rs, int dh) {
     constexpr int es = C::F32 ? 4 : 2;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-        const int off = rowi * row_bytes<C::F32>(dh) + (16 * dt + 4 * g) * es;
+        const int off = rowi * row_bytes<C::F32>(rs) + (16 * dt + 4 * g) * es;
         if (16 * dt >= dh) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) xr[dt][i] = to_elem<C::F32>(0.f);
@@ -1135,7 +1170,7 @@ __device__ inline void load_dx_row(rsrc_t rX, int rowi, int g, typename Prec<C::
 // the final scaling is beta / max(|x|, eps).
 template <class C>
 __device__ inline void store_dx(const typename Prec<C::F32>::half (&xr)[4], rsrc_t rOut, int rowi, int g, float inv,
-                                float beta, const f32x4 dX[4], int dh) {
+                                float beta, const f32x4 dX[4], int rs, int dh) {
     constexpr int es = C::F32 ? 4 : 2;
     float xv[4][4];
     float radial = 0.f;
@@ -1156,7 +1191,7 @@ __device__ inline void store_dx(const typename Prec<C::F32>::half (&xr)[4], rsrc
         f32x4 o;
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = (tangent ? dX[dt][i] - xv[dt][i] * inv * radial : dX[dt][i]) * binv;
-        const int off = rowi * row_bytes<C::F32>(dh) + (16 * dt + 4 * g) * es;
+        const int off = rowi * row_bytes<C::F32>(rs) + (16 * dt + 4 * g) * es;
         if constexpr (C::F32) {
             bstore128(rOut, off, __builtin_bit_cast(u32x4, o));
         } else {
@@ -1175,15 +1210,15 @@ __device__ inline void store_dx(const typename Prec<C::F32>::half (&xr)[4], rsrc
 // dropped).
 template <class C>
 __device__ inline void store_rows_t(rsrc_t out, int r0, int cb, int ln, int g, const f32x4 (&Yt)[4],
-                                    const float (&rs)[4], const float (&add)[4], int dh) {
+                                    const float (&rsc)[4], const float (&add)[4], int rs, int dh) {
     constexpr int es = C::F32 ? 4 : 2;
     if (cb >= dh) return;   // columns past the head dimension (wave-uniform)
 #pragma unroll
     for (int at = 0; at < 4; ++at) {
         f32x4 o;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = (Yt[at][i] + add[i]) * rs[at];
-        const int off = (r0 + 16 * at + ln) * row_bytes<C::F32>(dh) + (cb + 4 * g) * es;
+        for (int i = 0; i < 4; ++i) o[i] = (Yt[at][i] + add[i]) * rsc[at];
+        const int off = (r0 + 16 * at + ln) * row_bytes<C::F32>(rs) + (cb + 4 * g) * es;
         if constexpr (C::F32) {
             bstore128(out, off, __builtin_bit_cast(u32x4, o));
         } else {
@@ -1248,7 +1283,9 @@ struct FwdLds {
     using WS = WStage<elem, o_w, n_float, C::MT, OCC>;
 };
 
-template <class C, bool CAUSAL>
+// PG (head dimension 128): the queries' plane values come from ca (computed
+// beforehand from the whole rows) instead of a projection of Q.
+template <class C, bool CAUSAL, bool PG = false>
 __global__ __launch_bounds__(NT, (FwdLds<C>::OCC))
 __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(PassArgs a) {
     using elem = typename Prec<C::F32>::elem;
@@ -1276,15 +1313,15 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
     const elem* W = reinterpret_cast<const elem*>(reinterpret_cast<const char*>(a.W) + (bh % a.H) * a.w_hs);
     constexpr bool causal = CAUSAL;
     elem* s_w = LD::WS::on ? lds + LD::o_w : nullptr;
-    if (LD::WS::on) stage_w<C>(W, a.L, s_w, a.dh);
+    if (LD::WS::on && !PG) stage_w<C>(W, a.L, s_w, a.dh);
     zero_pads<C, ZV>(s_zr, nullptr);
     __syncthreads();   // W' and the padding are written by all waves, read by each
     const WSrc<C, LD::WS::on> wsrc{s_w, W, a.L, a.dh};
     const int64_t nrows = seg1 - seg0;
     const size_t row0 = base + seg0;
-    const rsrc_t rXa = rows_rsrc(a.Xa, row0, nrows, row_bytes<C::F32>(a.dh));
-    const rsrc_t rZ = rows_rsrc(a.Zsrc, row0, nrows, row_bytes<C::F32>(a.dh));
-    const rsrc_t rO = rows_rsrc(a.out0, row0, nrows, row_bytes<C::F32>(a.dh));
+    const rsrc_t rXa = rows_rsrc(a.Xa, row0, nrows, row_bytes<C::F32>(a.rs));
+    const rsrc_t rZ = rows_rsrc(a.Zsrc, row0, nrows, row_bytes<C::F32>(a.rs));
+    const rsrc_t rO = rows_rsrc(a.out0, row0, nrows, row_bytes<C::F32>(a.rs));
     const rsrc_t rD = rows_rsrc(a.Dv, row0, nrows, 4);
     const rsrc_t rAcc = rows_rsrc(a.acc, row0, nrows, DH * 4);
     const rsrc_t rAD = rows_rsrc(a.accD, row0, nrows, 4);
@@ -1299,20 +1336,23 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
     // tile (keys after the own tokens are skipped), evens out over the SIMDs.
     auto own_tok = [&](int it2) { return 16 * ((w + it2) & 3) + ln; };
 
-    // loads issued one sub-block (the keys' plane values: one feature block) ahead
+    // loads issued one sub-block (plane values: one feature block) ahead
     frag n_xa[2], n_z[2];
-    Planes<C> pn;
+    Planes<C> pn, pq;
     auto nv_of = [&](int it2) {
         const int64_t t0 = seg0 + (int64_t)it2 * TB;
         return (int)(seg1 - t0 < TB ? seg1 - t0 : TB);
     };
     auto issue = [&](int it2) {
-        load_row_b<C::F32>(rXa, it2 * TB + own_tok(it2), g, n_xa, a.dh);
-        load_q16_b<C::F32>(rZ, it2 * TB + tr, tq, n_z, a.dh);
+        if (!PG) load_row_b<C::F32>(rXa, it2 * TB + own_tok(it2), g, n_xa, a.rs, a.dh);
+        load_q16_b<C::F32>(rZ, it2 * TB + tr, tq, n_z, a.rs, a.dh);
     };
-    auto issue_planes = [&](int it2, int fb2) { load_planes<C>(prb, it2 * TB + own_tok(it2), fb2, g, pn); };
+    auto issue_planes = [&](int it2, int fb2) {
+        if (causal) load_planes<C>(prb, it2 * TB + own_tok(it2), fb2, g, pn);
+        if (PG) load_planes<C>(pra, it2 * TB + own_tok(it2), fb2, g, pq);
+    };
     issue(0);
-    if (causal) issue_planes(0, 0);
+    if (causal || PG) issue_planes(0, 0);
 
     for (int it = 0; it < nsub; ++it) {
         const int64_t t0 = seg0 + (int64_t)it * TB;
@@ -1324,8 +1364,8 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
         frag xa[2] = {n_xa[0], n_xa[1]}, zr[2] = {n_z[0], n_z[1]};
         if (it + 1 < nsub) issue(it + 1);
 
-        const float inv_a = row_inv_norm<C::F32>(xa);
-        if (g == 0) bstore_f32(pra.inv, rowi * 4, inv_a);   // dropped without a cache
+        const float inv_a = PG ? 0.f : row_inv_norm<C::F32>(xa);
+        if (!PG && g == 0) bstore_f32(pra.inv, rowi * 4, inv_a);   // dropped without a cache
         write_aug<C, ZV, true>(zr, 1.f, tok ? 1.f : 0.f, s_zr);
 
         // The empty subset's state rows (plain sums of the keys' [v | 1], the
@@ -1355,13 +1395,18 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
             frag unused[C::FBK];
             elem* rows_b = s_rows + (fb & 1) * LD::n_rows;
             elem* brow_b = s_brow + (fb & 1) * LD::n_brow;
-            const Planes<C> pl = pn;
-            if (causal) {
+            const Planes<C> pl = pn, ql = pq;
+            if (causal || PG) {
                 if (fb + 1 < C::NBLK) issue_planes(it, fb + 1);
                 else if (it + 1 < nsub) issue_planes(it + 1, 0);
             }
-            block_features<C, false>(wsrc, fb, lane, ow, ln, g, xa, inv_a, a.beta, a.L, rows_b, unused, pra,
-                                     rowi);
+            if constexpr (PG) {
+                float us[C::TPB][4], ug[C::TPB][4];
+                block_features_cached<C, false>(ql, fb, ow, ln, g, a.L, a.beta, rows_b, unused, us, ug);
+            } else {
+                block_features<C, false>(wsrc, fb, lane, ow, ln, g, xa, inv_a, a.beta, a.L, rows_b, unused, pra,
+                                         rowi);
+            }
             if (causal) {
                 float us[C::TPB][4], ug[C::TPB][4];
                 block_features_cached<C, false>(pl, fb, ow, ln, g, a.L, a.beta, brow_b, unused, us, ug);
@@ -1494,7 +1539,7 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
 #pragma unroll
             for (int at = 0; at < 4; ++at) rd[at] = f_rD[16 * at + ln];
             const float none[4] = {-0.f, -0.f, -0.f, -0.f};   // x + -0 = x: nothing added
-            store_rows_t<C>(rO, it * TB, 16 * w, ln, g, Y, rd, none, a.dh);
+            store_rows_t<C>(rO, it * TB, 16 * w, ln, g, Y, rd, none, a.rs, a.dh);
         }
     }
 }
@@ -1536,7 +1581,7 @@ struct BwdQLds {
     static_assert(n_elem * (int)sizeof(elem) * OCC <= 160 * 1024, "LDS budget");
 };
 
-template <class C, bool CAUSAL>
+template <class C, bool CAUSAL, bool H2 = false>
 __global__ __launch_bounds__(NT, (BwdQLds<C>::OCC))
 __attribute__((amdgpu_waves_per_eu(BwdQLds<C>::OCC, BwdQLds<C>::OCC))) void k_bwd_q(PassArgs a) {
     using elem = typename Prec<C::F32>::elem;
@@ -1574,14 +1619,15 @@ __attribute__((amdgpu_waves_per_eu(BwdQLds<C>::OCC, BwdQLds<C>::OCC))) void k_bw
     const int my = 16 * w + ln;
     const int64_t nrows = seg1 - seg0;
     const size_t row0 = base + seg0;
-    const rsrc_t rZ = rows_rsrc(a.Zsrc, row0, nrows, row_bytes<C::F32>(a.dh));
-    const rsrc_t rY = rows_rsrc(a.Ysrc, row0, nrows, row_bytes<C::F32>(a.dh));
-    const rsrc_t rOs = rows_rsrc(a.Osrc, row0, nrows, row_bytes<C::F32>(a.dh));
-    const rsrc_t rXa = rows_rsrc(a.Xa, row0, nrows, row_bytes<C::F32>(a.dh));
-    const rsrc_t rOut = rows_rsrc(a.out0, row0, nrows, row_bytes<C::F32>(a.dh));
+    const rsrc_t rZ = rows_rsrc(a.Zsrc, row0, nrows, row_bytes<C::F32>(a.rs));
+    const rsrc_t rY = rows_rsrc(a.Ysrc, row0, nrows, row_bytes<C::F32>(a.rs));
+    const rsrc_t rOs = rows_rsrc(a.Osrc, row0, nrows, row_bytes<C::F32>(a.rs));
+    const rsrc_t rXa = rows_rsrc(a.Xa, row0, nrows, row_bytes<C::F32>(a.rs));
+    const rsrc_t rOut = rows_rsrc(a.out0, row0, nrows, row_bytes<C::F32>(a.rs));
     const rsrc_t rD = rows_rsrc(a.Dv, row0, nrows, 4);
     const rsrc_t rE = rows_rsrc(a.Ev, row0, nrows, 4);
     const rsrc_t rAcc = rows_rsrc(a.acc, row0, nrows, DH * 4);
+    const rsrc_t rdh = rows_rsrc(H2 ? a.dhb : nullptr, row0, nrows, C::NPL * 4);
     const PlaneRows pra = plane_rows<C>(a.ca, row0, nrows), prb = plane_rows<C>(a.cb, row0, nrows);
 
     // the plane values of queries and keys are loaded one feature block ahead;
@@ -1605,22 +1651,28 @@ __attribute__((amdgpu_waves_per_eu(BwdQLds<C>::OCC, BwdQLds<C>::OCC))) void k_bw
         const int rowi = it * TB + my, rowt = it * TB + tr;
         const bool tok = tr < nv;
         frag zr[2], yr[2], orow[2];
-        if (causal) load_q16_b<C::F32>(rZ, rowt, tq, zr, a.dh);
-        load_q16_b<C::F32>(rY, rowt, tq, yr, a.dh);
-        load_q16_b<C::F32>(rOs, rowt, tq, orow, a.dh);
+        if (causal) load_q16_b<C::F32>(rZ, rowt, tq, zr, a.rs, a.dh);
+        load_q16_b<C::F32>(rY, rowt, tq, yr, a.rs, a.dh);
+        if (!H2) load_q16_b<C::F32>(rOs, rowt, tq, orow, a.rs, a.dh);
         const float dd = tok ? bload_f32(rD, rowt * 4) : 1.f;
-        const float inv_a = valid ? bload_f32(pra.inv, rowi * 4) : 1.f;
+        const float e_in = (H2 && a.half == 0) ? bload_f32(rE, rowt * 4) : 0.f;
+        const float inv_a = (!H2 && valid) ? bload_f32(pra.inv, rowi * 4) : 1.f;
         typename Prec<C::F32>::half xr[4];
-        load_dx_row<C>(rXa, rowi, g, xr, a.dh);
+        if (!H2) load_dx_row<C>(rXa, rowi, g, xr, a.rs, a.dh);
         const bool first = t0 == 0;   // the sub-block that starts the sequence
         if (causal) write_aug<C, C::ROWE, true>(zr, 1.f, tok ? 1.f : 0.f, s_zr);
         // y = [dO / D | e], e = -<dO, O> / D; this thread holds 16 columns of row tr
         {
-            float delta = dot16<C::F32>(yr, orow);
-            delta += __shfl_xor(delta, 1);
-            delta += __shfl_xor(delta, 2);
             const float rD = tok ? rcp_(dd) : 0.f;
-            const float e = -delta * rD;
+            float e;
+            if constexpr (H2) {
+                e = tok ? e_in : 0.f;   // over all 128 columns, computed beforehand
+            } else {
+                float delta = dot16<C::F32>(yr, orow);
+                delta += __shfl_xor(delta, 1);
+                delta += __shfl_xor(delta, 2);
+                e = -delta * rD;
+            }
             float v[16];
 #pragma unroll
             for (int cc = 0; cc < 16; ++cc) v[cc] = q16_at<C::F32>(yr, cc) * rD;
@@ -1641,7 +1693,7 @@ __attribute__((amdgpu_waves_per_eu(BwdQLds<C>::OCC, BwdQLds<C>::OCC))) void k_bw
                 const elem eh = to_elem<C::F32>(e);
                 s_yr[tr * C::ROWE + 64] = eh;
                 if (LD::YLO && first) s_ylo[tr * C::ROWE + 64] = to_elem<C::F32>(e - elem_f<C::F32>(eh));
-                bstore_f32(rE, rowt * 4, e);
+                if (!H2) bstore_f32(rE, rowt * 4, e);
             }
         }
         __syncthreads();
@@ -1657,9 +1709,11 @@ __attribute__((amdgpu_waves_per_eu(BwdQLds<C>::OCC, BwdQLds<C>::OCC))) void k_bw
 #pragma unroll
         for (int fb = 0; fb < C::NBLK; ++fb) {
             frag wf[C::TPB][4];
+            if constexpr (!H2) {
 #pragma unroll
-            for (int tb = 0; tb < C::TPB; ++tb)
-                if (completes_pair<C>(fb * C::TPB + tb)) load_wtp<C>(fb * C::TPB + tb, lane, WTp, wf[tb]);
+                for (int tb = 0; tb < C::TPB; ++tb)
+                    if (completes_pair<C>(fb * C::TPB + tb)) load_wtp<C>(fb * C::TPB + tb, lane, WTp, wf[tb]);
+            }
             const Planes<C> qa = pa, kb_ = pb;
             if (fb + 1 < C::NBLK) issue_planes(it, fb + 1);
             else if (it + 1 < nsub) issue_planes(it + 1, 0);
@@ -1691,14 +1745,22 @@ __attribute__((amdgpu_waves_per_eu(BwdQLds<C>::OCC, BwdQLds<C>::OCC))) void k_bw
                         dA[kb * 8 + 4 + i] = G[2 * kcl + 1][i];
                     }
                 }
-                chain_backproject<C>(t, g, dA, tt, gt, wf[tb], dhp, dX);
+                if constexpr (H2) {
+                    float dh[4];
+                    monomial_backward<C>(dA, tt, gt, dh, g);
+                    put_dh<C>(rdh, rowi, t, g, dh, a.half != 0);
+                } else {
+                    chain_backproject<C>(t, g, dA, tt, gt, wf[tb], dhp, dX);
+                }
             }
             if (causal) sketch_update<C, true, C::ROWE, false, TR>(fb, w, ln, g, cols_b, s_zr, Macc, Zacc);
         }
         __syncthreads();   // the next sub-block rewrites the y and z rows
-        if (a.gmode & ACC_IN) acc_load_row(rAcc, rowi, g, dX);
-        if (a.gmode & ACC_OUT) acc_store_row(rAcc, rowi, g, dX);
-        else store_dx<C>(xr, rOut, rowi, g, inv_a, a.beta, dX, a.dh);
+        if constexpr (!H2) {
+            if (a.gmode & ACC_IN) acc_load_row(rAcc, rowi, g, dX);
+            if (a.gmode & ACC_OUT) acc_store_row(rAcc, rowi, g, dX);
+            else store_dx<C>(xr, rOut, rowi, g, inv_a, a.beta, dX, a.rs, a.dh);
+        }
     }
 }
 
@@ -1763,9 +1825,11 @@ struct BwdKLds {
     static_assert(BYTES * OCC <= 160 * 1024, "LDS budget");
 };
 
-template <class C, bool CAUSAL, int PART>
+// H2 (head dimension 128, the dK part only): see PassArgs::dhb.
+template <class C, bool CAUSAL, int PART, bool H2 = false>
 __global__ __launch_bounds__(NT, (BwdKLds<C, PART>::OCC))
 __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC))) void k_bwd_k(PassArgs a) {
+    static_assert(!H2 || PART == KPART_DK, "the dV part has no head-dimension-128 form");
     using elem = typename Prec<C::F32>::elem;
     using frag = typename Prec<C::F32>::frag;
     using LD = BwdKLds<C, PART>;
@@ -1819,25 +1883,26 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
     };
     const int64_t nrows = seg1 - seg0;
     const size_t row0 = base + seg0;
-    const rsrc_t rZ = rows_rsrc(a.Zsrc, row0, nrows, row_bytes<C::F32>(a.dh));
-    const rsrc_t rY = rows_rsrc(a.Ysrc, row0, nrows, row_bytes<C::F32>(a.dh));
-    const rsrc_t rXa = rows_rsrc(a.Xa, row0, nrows, row_bytes<C::F32>(a.dh));
-    const rsrc_t rOut0 = rows_rsrc(a.out0, row0, nrows, row_bytes<C::F32>(a.dh));
-    const rsrc_t rOut1 = rows_rsrc(a.out1, row0, nrows, row_bytes<C::F32>(a.dh));
+    const rsrc_t rZ = rows_rsrc(a.Zsrc, row0, nrows, row_bytes<C::F32>(a.rs));
+    const rsrc_t rY = rows_rsrc(a.Ysrc, row0, nrows, row_bytes<C::F32>(a.rs));
+    const rsrc_t rXa = rows_rsrc(a.Xa, row0, nrows, row_bytes<C::F32>(a.rs));
+    const rsrc_t rOut0 = rows_rsrc(a.out0, row0, nrows, row_bytes<C::F32>(a.rs));
+    const rsrc_t rOut1 = rows_rsrc(a.out1, row0, nrows, row_bytes<C::F32>(a.rs));
     const rsrc_t rD = rows_rsrc(a.Dv, row0, nrows, 4);
     const rsrc_t rE = rows_rsrc(a.Ev, row0, nrows, 4);
     const rsrc_t rAcc = rows_rsrc(a.acc, row0, nrows, DH * 4);
+    const rsrc_t rdh = rows_rsrc(H2 ? a.dhb : nullptr, row0, nrows, C::NPL * 4);
     const PlaneRows pra = plane_rows<C>(a.ca, row0, nrows), prb = plane_rows<C>(a.cb, row0, nrows);
     auto r0_of = [&](int it2) { return (nsub - 1 - it2) * TB; };   // first in-chunk row of a sub-block
     auto issue = [&](int it2) {
         const int r0 = r0_of(it2);
-        if (DK) n_inv = my < nv_of(it2) ? bload_f32(pra.inv, (r0 + my) * 4) : 1.f;
+        if (DK && !H2) n_inv = my < nv_of(it2) ? bload_f32(pra.inv, (r0 + my) * 4) : 1.f;
         if (causal) {
-            load_q16_b<C::F32>(rZ, r0 + tr, tq, n_z, a.dh);
+            load_q16_b<C::F32>(rZ, r0 + tr, tq, n_z, a.rs, a.dh);
             n_d = bload_f32(rD, (r0 + tr) * 4);
-            n_e = bload_f32(rE, (r0 + tr) * 4);
+            n_e = (H2 && a.half != 0) ? 0.f : bload_f32(rE, (r0 + tr) * 4);
         }
-        if (DK) load_q16_b<C::F32>(rY, r0 + tr, tq, n_y, a.dh);
+        if (DK) load_q16_b<C::F32>(rY, r0 + tr, tq, n_y, a.rs, a.dh);
     };
     auto issue_planes = [&](int it2, int fb2) {
         load_planes<C>(pra, r0_of(it2) + my, fb2, g, pa);
@@ -1856,7 +1921,7 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
         if (PREFETCH && it + 1 < nsub) issue(it + 1);
 
         typename Prec<C::F32>::half xr[4];
-        if constexpr (DK) load_dx_row<C>(rXa, r0_of(it) + my, g, xr, a.dh);
+        if constexpr (DK && !H2) load_dx_row<C>(rXa, r0_of(it) + my, g, xr, a.rs, a.dh);
         const bool first = t0 == 0;   // the sub-block that starts the sequence
         if (causal)
             write_aug<C, LD::ZS>(zr, tok ? rcp_(zd) : 0.f, tok ? ze : 0.f, s_zr,
@@ -1900,7 +1965,7 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
             frag phiA[C::FBK], unused[C::FBK];
             float us[C::TPB][4], ug[C::TPB][4];
             frag wf[C::TPB][4];
-            if constexpr (DK) {
+            if constexpr (DK && !H2) {
 #pragma unroll
                 for (int tb = 0; tb < C::TPB; ++tb)
                     if (completes_pair<C>(fb * C::TPB + tb)) load_wtp<C>(fb * C::TPB + tb, lane, WTp, wf[tb]);
@@ -1966,7 +2031,13 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
                             dA[kb * 8 + 4 + i] = G[2 * kcl + 1][i];
                         }
                     }
-                    chain_backproject<C>(t, g, dA, tt, gt, wf[tb], dhp, dX);
+                    if constexpr (H2) {
+                        float dh[4];
+                        monomial_backward<C>(dA, tt, gt, dh, g);
+                        put_dh<C>(rdh, r0_of(it) + my, t, g, dh, a.half != 0);
+                    } else {
+                        chain_backproject<C>(t, g, dA, tt, gt, wf[tb], dhp, dX);
+                    }
                 }
             }
             if (causal) sketch_update<C, DK, LD::ZS, DV, TR>(fb, w, ln, g, DV ? brow_b : cols_b, s_zr, Macc, Zacc);
@@ -2002,13 +2073,13 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
                 acc_store_t(rAcc, r0_of(it), 16 * w, ln, g, Y);
             } else {
                 const float one[4] = {1.f, 1.f, 1.f, 1.f}, zero[4] = {-0.f, -0.f, -0.f, -0.f};   // x + -0 = x
-                store_rows_t<C>(rOut1, r0_of(it), 16 * w, ln, g, Y, one, zero, a.dh);
+                store_rows_t<C>(rOut1, r0_of(it), 16 * w, ln, g, Y, one, zero, a.rs, a.dh);
             }
         }
-        if constexpr (DK) {
+        if constexpr (DK && !H2) {
             if (a.gmode & ACC_IN) acc_load_row(rAcc, r0_of(it) + my, g, dX);
             if (a.gmode & ACC_OUT) acc_store_row(rAcc, r0_of(it) + my, g, dX);
-            else store_dx<C>(xr, rOut0, r0_of(it) + my, g, inv_a, a.beta, dX, a.dh);
+            else store_dx<C>(xr, rOut0, r0_of(it) + my, g, inv_a, a.beta, dX, a.rs, a.dh);
         }
     }
 }
@@ -2034,13 +2105,24 @@ __global__ __launch_bounds__(NT) void k_hash(const void* X, const void* Wv, int6
     const bool valid = n < N;
     const int64_t r = bh * N + n;
     const elem* W = reinterpret_cast<const elem*>(reinterpret_cast<const char*>(Wv) + (bh % H) * w_hs);
-    frag xf[2];
+    // head dimension 128: columns 64..127 as a second pair of K chunks
+    frag xf[4];
     load_row_raw<C::F32>(X, valid ? (size_t)r : 0, valid, g, xf, dh);
-    const float inv = row_inv_norm<C::F32>(xf);
+    if (dh > 64) {
+        load_row_raw<C::F32>(reinterpret_cast<const typename In<C::F32>::T*>(X) + 64, valid ? (size_t)r : 0,
+                             valid, g, xf + 2, dh);
+    }
+    const float ss = row_sumsq<C::F32>(xf) + (dh > 64 ? row_sumsq<C::F32>(xf + 2) : 0.f);
+    const float inv = __builtin_amdgcn_rsqf(fmaxf(sum_groups(ss), NORM_EPS * NORM_EPS));
     unsigned int nz = 0;
 #pragma unroll
     for (int t = 0; t < C::MT; ++t) {
-        const f32x4 acc = project_global<C>(W, L, t, ln, g, xf, dh);
+        f32x4 acc = project_global<C>(W, L, t, ln, g, xf, dh);
+        if (dh > 64) {
+            const f32x4 a2 = project_global<C>(W + 64, L, t, ln, g, xf + 2, dh);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] += a2[i];
+        }
         if constexpr (C::Pp == 8) {
             // a table's planes 0-3 in the even lane group, 4-7 in the odd one
             const int table = t * C::TPT + (g >> 1);

@@ -37,7 +37,13 @@ static int check_shape(int64_t B, int64_t H, int64_t N, int d, int P, int L, int
         if (kind == WS_BWD_RECOMPUTE) bad |= w.total < sl.total;
         // the group partials are addressed as [rows][64] float32 whatever d is
         if (dv.G > 1) bad |= w.accD < w.acc + (size_t)dv.BH * (size_t)N * 64 * sizeof(float);
+        // head dimension 128: two sets of sketch states, the queries' plane
+        // values (forward without saved) and the per-plane gradients of both sides
+        if (dv.VH == 2 && kind == WS_FWD) bad |= w.Qc < w.Kc + cl.total || w.total < w.Qc + cl.total;
+        if (dv.VH == 2 && (kind == WS_BWD || kind == WS_BWD_RECOMPUTE))
+            bad |= w.dhQ < w.E || w.dhK < w.dhQ + cl.total || w.total < w.dhK + cl.total;
     }
+    if (dv.VH == 2) bad |= sl.D < 2 * all_states_bytes(dv, causal ? dv.NC : 1);
     for (int g = 0; g < dv.G; ++g) {
         const int segs = scan_segs(s, dv, group(dv, g).F65);
         bad |= segs < 1 || segs > 16;
@@ -63,6 +69,9 @@ int main() {
     for (auto& b : big) bad |= check_shape(b[0], b[1], b[2], 64, 4, 8, 1, 16, n_ok);
     for (int d : {0, 32, 63, 65, 128}) bad |= check_shape(1, 1, 10, d, 4, 8, 1, 16, n_ok);
     for (int P : {4, 5}) bad |= check_shape(2, 2, 500, 32, P, 40, 1, 128, n_ok);   // d = 32 with table groups
+    for (int P : {2, 4, 5})
+        for (int causal = 0; causal < 2; ++causal)
+            bad |= check_shape(2, 2, 500, 128, P, 40, causal, 128, n_ok);   // d = 128, table groups
     std::printf("host driver: %d of %d shapes valid, %s\n", n_ok, n_all, bad ? "FAILED" : "ok");
     return bad ? 1 : 0;
 }

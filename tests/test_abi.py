@@ -156,8 +156,8 @@ def test_forward_argument_errors_before_device_work():
     assert L.race_attn_fwd(*bad, big, None) == race.RACE_ERR_UNSUPPORTED
     # workspace too small
     assert L.race_attn_fwd(*ok, need - 1, None) == race.RACE_ERR_WORKSPACE
-    # unsupported head dim
-    bad = list(ok); bad[7] = 128
+    # unsupported head dim (32, 64 and 128 are supported)
+    bad = list(ok); bad[7] = 96
     assert L.race_attn_fwd(*bad, need, None) == race.RACE_ERR_UNSUPPORTED
 
 
@@ -208,7 +208,9 @@ def test_state_bytes():
     for (B, H, P, L, F) in [(1, 4, 4, 16, 256), (2, 3, 3, 5, 64), (1, 1, 2, 8, 32), (1, 1, 4, 32, 512)]:
         assert race.state_bytes(B, H, P, L) == B * H * F * 66 * 4
     out = ctypes.c_size_t(0)
+    # the running state has no head-dimension-128 form (the forward and backward do)
     assert race.lib().race_attn_state_bytes(1, 1, 128, 4, 8, ctypes.byref(out)) == race.RACE_ERR_UNSUPPORTED
+    assert race.lib().race_attn_state_bytes(1, 1, 96, 4, 8, ctypes.byref(out)) == race.RACE_ERR_UNSUPPORTED
     assert race.lib().race_attn_state_bytes(1, 1, 64, 7, 8, ctypes.byref(out)) == race.RACE_ERR_UNSUPPORTED
     assert race.lib().race_attn_state_bytes(0, 1, 64, 4, 8, ctypes.byref(out)) == race.RACE_ERR_INVALID_ARG
     assert race.lib().race_attn_state_bytes(1, 1, 64, 4, 8, None) == race.RACE_ERR_INVALID_ARG

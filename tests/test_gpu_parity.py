@@ -473,3 +473,87 @@ def test_head_dim_32_hash_and_hard(lib, dtype):
                                        W64, True) for h_ in range(2)])[None]
     assert np.array_equal(np.all(O == 0.0, axis=-1), np.all(ref == 0.0, axis=-1))
     assert rel_l2(O, ref) <= TOL[dtype]
+
+
+# --- head dimension 128 ---------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,causal,P,L", [("bf16", True, 4, 16), ("bf16", False, 4, 20), ("f32", True, 2, 8),
+                                             ("f32", False, 4, 5), ("bf16", True, 5, 9), ("bf16", True, 4, 40),
+                                             ("f32", True, 3, 6), ("bf16", False, 6, 4)])
+def test_head_dim_128(lib, dtype, causal, P, L):
+    # plane values from the whole 128-column rows, the sketch passes once per
+    # 64-column value half, the per-plane gradients of both halves summed and
+    # mapped back onto 128 columns; (4, 20), (5, 9) and (4, 40) also run as
+    # table groups, (3, 6) has a padded plane per table
+    run_case(lib, 2, 2, 500, P, L, dtype, causal, 128, beta=1.2, seed=12812, d=128)
+
+
+@pytest.mark.parametrize("dtype,causal", [("bf16", True), ("f32", False)])
+def test_head_dim_128_recompute(lib, dtype, causal):
+    # the backward without what the forward kept (it recomputes the forward)
+    import torch
+    B, H, N, P, L, beta = 1, 3, 300, 4, 12, 0.9
+    x = host_inputs(1281, B, H, N, 128, P, L, dtype)
+    dev = torch.device("cuda:0")
+    T = {k: to_torch(v, dev) for k, v in x.items()}
+    print(f"[case] d=128 recompute {dtype} causal={causal}", flush=True)
+    dQ, dK, dV = lib.backward(T["Q"], T["K"], T["V"], T["W"], T["dO"], P, L, beta, causal, 64)
+    torch.cuda.synchronize()
+    W64 = to_f64(x["W"])
+    ref = oracle.backward(x["Q"], x["K"], x["V"], W64, x["dO"], beta, causal)
+    for name, got, want in zip(("dQ", "dK", "dV"), (dQ, dK, dV), ref):
+        err = rel_l2(from_torch(got), want)
+        print("  ", name, f"{err:.2e}", flush=True)
+        assert err <= TOL[dtype], (name, err)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_head_dim_128_per_head_and_hard(lib, dtype):
+    # one set of hyperplanes per head, and the hard buckets (temperature +inf):
+    # bucket ids bit-exact, the hard forward against the brute-force bucket sums
+    import math
+    import torch
+    from oracle import dense
+    P, L, N, H = 4, 8, 300, 2
+    for seed in range(1280, 1340):
+        x = host_inputs(seed, 1, H, N, 128, P, L, dtype)
+        W64 = to_f64(x["W"])
+        X = np.concatenate([to_f64(x["Q"]).reshape(-1, 128), to_f64(x["K"]).reshape(-1, 128)])
+        h = np.einsum("nd,lpd->nlp", X / np.linalg.norm(X, axis=1, keepdims=True), W64)
+        if np.min(np.abs(h)) > 1e-5:
+            break
+    else:
+        pytest.fail("no seed with every projection away from zero")
+    dev = torch.device("cuda:0")
+    T = {k: to_torch(v, dev) for k, v in x.items()}
+    print(f"[case] d=128 hash + hard {dtype} seed={seed}", flush=True)
+    ids, _ = lib.hard_hash(T["Q"], T["W"], P, L)
+    O = from_torch(lib.forward(T["Q"], T["K"], T["V"], T["W"], P, L, math.inf, True, 64))
+    torch.cuda.synchronize()
+    ref_ids, _ = oracle.hard_hash(x["Q"], W64)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    ref = np.stack([dense.hard_forward(to_f64(x["Q"])[0, h_], to_f64(x["K"])[0, h_], to_f64(x["V"])[0, h_],
+                                       W64, True) for h_ in range(H)])[None]
+    assert np.array_equal(np.all(O == 0.0, axis=-1), np.all(ref == 0.0, axis=-1))
+    assert rel_l2(O, ref) <= TOL[dtype]
+    # per-head hyperplanes [H, L, P, 128], soft buckets, forward and backward
+    import synth
+    Wh = synth.normal(seed, synth.TID_W, (H, L, P, 128), dtype)
+    Wd = to_torch(Wh, dev)
+    beta = 1.1
+    saved = lib.alloc_saved(1, H, N, P, L, True, 64, dev, 128)
+    Oh = lib.forward(T["Q"], T["K"], T["V"], Wd, P, L, beta, True, 64, saved=saved)
+    gh = lib.backward(T["Q"], T["K"], T["V"], Wd, T["dO"], P, L, beta, True, 64, O=Oh, saved=saved)
+    torch.cuda.synchronize()
+    got = {"O": from_torch(Oh), "dQ": from_torch(gh[0]), "dK": from_torch(gh[1]), "dV": from_torch(gh[2])}
+    ref = {k: np.zeros_like(v) for k, v in got.items()}
+    for hh in range(H):
+        W64h = to_f64(Wh[hh])
+        sl = (slice(None), hh)
+        ref["O"][sl] = oracle.forward(x["Q"][sl], x["K"][sl], x["V"][sl], W64h, beta, True)
+        ref["dQ"][sl], ref["dK"][sl], ref["dV"][sl] = oracle.backward(x["Q"][sl], x["K"][sl], x["V"][sl], W64h,
+                                                                      x["dO"][sl], beta, True)
+    errs = {k: rel_l2(got[k], ref[k]) for k in got}
+    print("   per-head rel_l2", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    for k, e in errs.items():
+        assert e <= TOL[dtype], (k, e)
