@@ -74,18 +74,53 @@ __device__ inline void feature_table_subset(int f, int P, int KB, int TPT, int T
     subset = jj % R;
 }
 
-// One token per launch (token a.tok of each head), every table group in
-// turn: the group's state rows are updated and written back as soon as the
-// features are known, and the read-outs of the groups are summed. NR = F / 32
-// state rows per thread of a full group (a compile-time count, so the
-// registers match the state: 95 at F = 256 in bf16).
+// Lanes per projection row: a group's 2 L P rows (the query's and the key's
+// planes; L P <= 128 per group) spread over the workgroup, two consecutive
+// lanes per row (each over 32 columns), combined by a shuffle. (Four lanes
+// per row measured slower at every head count, one lane per row slower for
+// few heads.)
+__device__ inline int dec_parts(int) { return 2; }
+
+// The parts' partial projections and squared norms summed over the row's
+// lanes (every lane of the workgroup takes part), then the plane value
+// t = tanh(beta tanh(h / |x|)), or the sign of h with hard buckets, with the
+// sketch kernels' hardware tanh and reciprocal square root.
+__device__ inline float dec_plane_t(float h, float ss, int parts, float beta, int hard) {
+    for (int m = 1; m < parts; m <<= 1) {
+        h += __shfl_xor(h, m);
+        ss += __shfl_xor(ss, m);
+    }
+    h *= __builtin_amdgcn_rsqf(fmaxf(ss, NORM_EPS * NORM_EPS));
+    if (hard) return h > 0.f ? 1.f : (h < 0.f ? -1.f : 0.f);
+    return tanh_scaled(tanh_scaled(h, 2.f * LOG2E), 2.f * LOG2E * beta);
+}
+
+// This thread's read-out partial (columns 4 cq .. +3 over its rows) summed
+// over the four row groups of its wave (lanes 16 apart), into s_num[wave].
+__device__ inline void dec_reduce_num(f32x4 acc, float (*s_num)[DH + 4], int wv, int lane, int cq) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        acc[j] += __shfl_xor(acc[j], 16);
+        acc[j] += __shfl_xor(acc[j], 32);
+    }
+    if (lane < 16) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s_num[wv][4 * cq + j] = acc[j];
+    }
+}
+
+// More than one table group: one token per launch (token a.tok of each
+// head), every table group in turn: the group's state rows are updated and
+// written back as soon as the features are known, and the read-outs of the
+// groups are summed. NR = F / 32 state rows per thread of a full group (a
+// compile-time count).
 template <bool F32, int NR>
 __global__ __launch_bounds__(DEC_NT) void k_decode_one(DecodeArgs a) {
     using elem = typename Prec<F32>::elem;
     __shared__ float s_x[3][DH];             // q, k, v of this head
     __shared__ float s_t[2][128];            // t_p of each table plane, [q | k][l * P + p]
     __shared__ float s_phi[2][DEC_MAXF];     // features of q and of k
-    __shared__ float s_num[DEC_RG][DH + 4];  // partial read-outs per row group
+    __shared__ float s_num[DEC_NT / 64][DH + 4];  // partial read-outs per wave
     __shared__ double s_den[DEC_NT / 64];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -119,17 +154,19 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_one(DecodeArgs a) {
         for (int i = 0; i < NR; ++i)
             if (rg + DEC_RG * i < F) s[i] = *reinterpret_cast<const f32x4*>(st + (size_t)(rg + DEC_RG * i) * DH + 4 * cq);
         const double z_old = tid < F ? zs[tid] : 0.0;
-        // so are the hyperplane rows: thread (side, row), row = l * P + p of
-        // the group, holds all 64 weights of its row, loaded 16 bytes at a time
-        const int side = tid / LP, row = tid % LP;
-        wvec wr[DH / WV];
-        if (tid < 2 * LP) {
+        // so are the hyperplane rows: projection row pr = side * L P + l * P + p
+        // of the group takes `parts` lanes, part pi holding columns
+        // pi * ncol .. + ncol - 1 of its weights, loaded 16 bytes at a time
+        const int parts = dec_parts(LP), ncol = DH / parts;
+        const int pr = tid / parts, pi = tid % parts, side = pr / LP, row = pr % LP, c0 = pi * ncol;
+        wvec wr[DH / WV / 2];
+        if (pr < 2 * LP) {
             const wvec* w = reinterpret_cast<const wvec*>(
                 reinterpret_cast<const elem*>(reinterpret_cast<const char*>(a.W) + (bh % a.H) * a.w_hs) +
-                ((size_t)gi * a.Lg * a.P + row) * a.dh);
+                ((size_t)gi * a.Lg * a.P + row) * a.dh + c0);
 #pragma unroll
-            for (int j = 0; j < DH / WV; ++j) {
-                if (j * WV < a.dh) {
+            for (int j = 0; j < DH / WV / 2; ++j) {
+                if (j * WV < ncol && c0 + j * WV < a.dh) {
                     wr[j] = w[j];
                 } else {
 #pragma unroll
@@ -139,23 +176,24 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_one(DecodeArgs a) {
         }
         __syncthreads();   // s_x is written; the previous group's s_t and s_phi are read
 
-        // projections; each projection thread also sums its row's squares (the
-        // same order in both decode kernels, so they agree bit for bit)
-        if (tid < 2 * LP) {
+        // projections; each part also sums its columns' squares (the same
+        // order in both decode kernels)
+        {
             float h = 0.f, ss = 0.f;
+            if (pr < 2 * LP) {
 #pragma unroll
-            for (int j = 0; j < DH / WV; ++j)
+                for (int j = 0; j < DH / WV / 2; ++j) {
+                    if (j * WV >= ncol) break;
 #pragma unroll
-                for (int e = 0; e < WV; ++e) {
-                    const float x = s_x[side][WV * j + e];
-                    h = fmaf((float)wr[j][e], x, h);
-                    ss = fmaf(x, x, ss);
+                    for (int e = 0; e < WV; ++e) {
+                        const float x = s_x[side][c0 + WV * j + e];
+                        h = fmaf((float)wr[j][e], x, h);
+                        ss = fmaf(x, x, ss);
+                    }
                 }
-            h *= 1.f / fmaxf(sqrtf(ss), NORM_EPS);
-            float t;
-            if (a.hard) t = h > 0.f ? 1.f : (h < 0.f ? -1.f : 0.f);
-            else t = tanhf(a.beta * tanhf(h));
-            s_t[side][row] = t;
+            }
+            const float t = dec_plane_t(h, ss, parts, a.beta, a.hard);
+            if (pr < 2 * LP && pi == 0) s_t[side][row] = t;
         }
         __syncthreads();
 
@@ -202,8 +240,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_one(DecodeArgs a) {
             den += (double)s_phi[0][tid] * z;
         }
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) s_num[rg][4 * cq + j] = acc[j];
+    dec_reduce_num(acc, s_num, wv, lane, cq);
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) den += __shfl_xor(den, m);
     if (lane == 0) s_den[wv] = den;
@@ -211,8 +248,8 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_one(DecodeArgs a) {
     if (tid < DH) {
         float num = 0.f;
         double dsum = 0.0;
-#pragma unroll 8
-        for (int rr = 0; rr < DEC_RG; ++rr) num += s_num[rr][tid];
+#pragma unroll
+        for (int rr = 0; rr < DEC_NT / 64; ++rr) num += s_num[rr][tid];
 #pragma unroll
         for (int w = 0; w < DEC_NT / 64; ++w) dsum += s_den[w];
         const float o = (a.hard && dsum == 0.0) ? 0.f : num / (float)dsum;
@@ -220,17 +257,19 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_one(DecodeArgs a) {
     }
 }
 
-// T > 1 with one table group: the state rows stay in registers across the
-// tokens and are written back during the last token; the hyperplanes sit in LDS and each token's
-// q, k, v rows are loaded while the previous token is processed (116
-// registers at F = 256 in bf16: two workgroups per CU).
+// One table group, any T: the state rows stay in registers across the
+// tokens and are written back during the last token; the hyperplanes sit in
+// LDS and each token's q, k, v rows are loaded while the previous token is
+// processed (100 registers at F = 256 in bf16: two workgroups per CU; the
+// one-launch-per-token kernel above needs 184 with its group loop, one
+// workgroup per CU, and took 745 us against 407 us for 16,384 heads).
 template <bool F32, int NR>
 __global__ __launch_bounds__(DEC_NT) void k_decode_multi(DecodeArgs a) {
     using elem = typename Prec<F32>::elem;
     __shared__ float s_x[3][DH];             // q, k, v of the current token
     __shared__ float s_t[2][128];            // t_p of each table plane, [q | k][l * P + p]
     __shared__ float s_phi[2][DEC_MAXF];     // features of q and of k
-    __shared__ float s_num[DEC_RG][DH + 4];  // partial read-outs per row group
+    __shared__ float s_num[DEC_NT / 64][DH + 4];  // partial read-outs per wave
     __shared__ double s_den[DEC_NT / 64];
     __shared__ float s_w[128][DH + 1];       // hyperplane rows (padded: conflict-free row reads)
 
@@ -249,13 +288,27 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_multi(DecodeArgs a) {
     for (int i = 0; i < NR; ++i)
         s[i] = *reinterpret_cast<const f32x4*>(st + (size_t)(rg + DEC_RG * i) * DH + 4 * cq);
     double z = tid < F ? zs[tid] : 0.0;
-    // the hyperplanes, once, into LDS (read there for every token)
+    // the hyperplanes, once, into LDS (read there for every token), 16 bytes
+    // per load
     const elem* Wh = reinterpret_cast<const elem*>(reinterpret_cast<const char*>(a.W) + (bh % a.H) * a.w_hs);
-    for (int e = tid; e < LP * DH; e += DEC_NT) {
-        const int c = e % DH;
-        s_w[e / DH][c] = c < a.dh ? (float)Wh[(e / DH) * a.dh + c] : 0.f;
+    {
+        constexpr int WV = 16 / sizeof(elem);
+        typedef elem wvec __attribute__((ext_vector_type(WV)));
+        for (int e = tid; e < LP * (DH / WV); e += DEC_NT) {
+            const int wrow = e / (DH / WV), c = (e % (DH / WV)) * WV;
+            wvec v;
+            if (c < a.dh) {
+                v = *reinterpret_cast<const wvec*>(Wh + (size_t)wrow * a.dh + c);
+            } else {
+#pragma unroll
+                for (int j = 0; j < WV; ++j) v[j] = (elem)0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < WV; ++j) s_w[wrow][c + j] = (float)v[j];
+        }
     }
-    const int side = tid / LP, row = tid % LP;
+    const int parts = dec_parts(LP), ncol = DH / parts;
+    const int pr = tid / parts, pi = tid % parts, side = pr / LP, row = pr % LP, c0 = pi * ncol;
     // q, k, v rows are loaded one token ahead: thread tid < 3 * 64 holds one
     // element of the next token while the current one is processed
     const int which = tid / DH, col = tid % DH;
@@ -273,20 +326,19 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_multi(DecodeArgs a) {
     // | output and the next token's rows (nothing reads s_x in that phase).
     for (int tok = 0; tok < a.T; ++tok) {
         const int64_t r = r0 + tok;
-        // projections, each thread with its row's norm (as in k_decode_one)
-        if (tid < 2 * LP) {
+        // projections, each part with its columns' squares (as in k_decode_one)
+        {
             float h = 0.f, ss = 0.f;
-#pragma unroll 16
-            for (int c = 0; c < DH; ++c) {
-                const float x = s_x[side][c];
-                h = fmaf(s_w[row][c], x, h);
-                ss = fmaf(x, x, ss);
+            if (pr < 2 * LP) {
+#pragma unroll 8
+                for (int c = c0; c < c0 + ncol; ++c) {
+                    const float x = s_x[side][c];
+                    h = fmaf(s_w[row][c], x, h);
+                    ss = fmaf(x, x, ss);
+                }
             }
-            h *= 1.f / fmaxf(sqrtf(ss), NORM_EPS);
-            float t;
-            if (a.hard) t = h > 0.f ? 1.f : (h < 0.f ? -1.f : 0.f);
-            else t = tanhf(a.beta * tanhf(h));
-            s_t[side][row] = t;
+            const float t = dec_plane_t(h, ss, parts, a.beta, a.hard);
+            if (pr < 2 * LP && pi == 0) s_t[side][row] = t;
         }
         __syncthreads();
 
@@ -323,8 +375,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_multi(DecodeArgs a) {
                 if (last) *reinterpret_cast<f32x4*>(st + (size_t)f * DH + 4 * cq) = s[i];
                 acc += s_phi[0][f] * s[i];
             }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) s_num[rg][4 * cq + j] = acc[j];
+            dec_reduce_num(acc, s_num, wv, lane, cq);
         }
         // masses (F <= DEC_NT: one per thread) and the denominator in float64:
         // with hard buckets the features are 0 or +-1 and the masses integers,
@@ -345,8 +396,8 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_multi(DecodeArgs a) {
         if (tid < DH) {
             float num = 0.f;
             double den = 0.0;
-#pragma unroll 8
-            for (int rr = 0; rr < DEC_RG; ++rr) num += s_num[rr][tid];
+#pragma unroll
+            for (int rr = 0; rr < DEC_NT / 64; ++rr) num += s_num[rr][tid];
 #pragma unroll
             for (int w = 0; w < DEC_NT / 64; ++w) den += s_den[w];
             const float o = (a.hard && den == 0.0) ? 0.f : num / (float)den;

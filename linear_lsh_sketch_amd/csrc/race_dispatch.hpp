@@ -417,7 +417,7 @@ race_status_t dispatch(const Shape& s, const Derived& d, const WsLayout& wl, con
             a.H = (int)s.H; a.w_hs = w_head_bytes(s, C::F32); a.dh = s.d;
             static_assert(C::F <= DEC_MAXF && C::F % DEC_RG == 0, "decode tiling");
             constexpr int NR = C::F / DEC_RG;   // state rows per thread
-            if (a.T > 1 && d.G == 1) {
+            if (d.G == 1) {
                 profile_mark("decode", st);
                 hipLaunchKernelGGL((k_decode_multi<C::F32, NR>), dim3((unsigned)d.BH), dim3(DEC_NT), 0, st, a);
                 return launch_ok();
