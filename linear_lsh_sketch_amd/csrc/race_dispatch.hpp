@@ -96,12 +96,13 @@ inline int64_t w_head_bytes(const Shape& s, bool f32) {
 template <class C, bool CACHED, bool PG = false>
 race_status_t run_totals(const Shape& s, const Derived& d, const Group& gr, const void* Xb, const void* Z,
                          const float* Dv, const float* Ev, const PlaneCache& pc, const void* W, float beta,
-                         float* out, hipStream_t st, int rs = 0, int dh = 0, int ezero = 0) {
+                         float* out, hipStream_t st, int rs = 0, int dh = 0, int ezero = 0, int f32form = 0) {
     TotArgs a;
     a.Xb = Xb; a.Z = Z; a.Dv = Dv; a.Ev = Ev; a.W = W; a.pc = pc; a.out = out;
     a.N = s.N; a.chunk = s.chunk; a.nchunks = (int)d.NC; a.L = gr.L; a.beta = beta;
     a.H = (int)s.H; a.w_hs = w_head_bytes(s, C::F32); a.dh = dh ? dh : s.d; a.rs = rs ? rs : s.d;
     a.ezero = ezero;
+    a.f32form = f32form;
     profile_mark(CACHED ? "totals_qg" : "totals_kv", st);
     hipLaunchKernelGGL((k_totals<C, CACHED, PG>), dim3((unsigned)d.NC, (unsigned)d.BH), dim3(NT), 0, st, a);
     return launch_ok();
@@ -116,24 +117,28 @@ inline PlaneCache plane_cache(void* base, const CacheLayout& cl, int g) {
     return p;
 }
 
-// Scan of one group's chunk states [BH][NC][F65]; the total of head bh goes
-// to total + bh * total_stride.
+// Scan of one group's chunk states [BH][NC][F65 floats] (F features; the
+// compact form of bf16 inputs: 32 F words of bf16 pairs, then 33 F + 64 -
+// 32 F float32 words); the total of head bh goes to total + bh * total_stride.
 template <int KIND>
-race_status_t run_scan(const Shape& s, const Derived& d, int64_t F65, float* states, float* total,
-                       int64_t total_stride, float* segbuf, hipStream_t st) {
-    const int elems = (int)F65;
-    const unsigned gx = (unsigned)((elems + 255) / 256);
+race_status_t run_scan(const Shape& s, const Derived& d, int64_t F65, int F, bool compact, float* states,
+                       float* total, int64_t total_stride, float* segbuf, hipStream_t st) {
+    ScanShape sh;
+    sh.nchunks = (int)d.NC;
+    sh.stride = (int)F65;
+    sh.npair = compact ? 32 * F : 0;
+    sh.nwords = compact ? 33 * F + DH : (int)F65;
+    const unsigned gx = (unsigned)((sh.nwords + 255) / 256);
     profile_mark(KIND == SCAN_EXCL ? "scan_excl" : KIND == SCAN_REV_EXCL ? "scan_rev_excl" : "scan_total", st);
-    const int segs = KIND == SCAN_TOTAL ? 1 : scan_segs(s, d, F65);
+    const int segs = KIND == SCAN_TOTAL ? 1 : scan_segs(s, d, sh.nwords);
     if (segs == 1) {
-        hipLaunchKernelGGL(k_scan<KIND>, dim3(gx, (unsigned)d.BH), dim3(256), 0, st, states, total, (int)d.NC,
-                           elems, total_stride);
+        hipLaunchKernelGGL(k_scan<KIND>, dim3(gx, (unsigned)d.BH), dim3(256), 0, st, states, total, sh, total_stride);
         return launch_ok();
     }
     const dim3 grid(gx, (unsigned)(d.BH * segs));
-    hipLaunchKernelGGL(k_scan_segsum<KIND>, grid, dim3(256), 0, st, states, segbuf, (int)d.NC, elems, segs);
+    hipLaunchKernelGGL(k_scan_segsum<KIND>, grid, dim3(256), 0, st, states, segbuf, sh, segs);
     RACE_TRY(launch_ok());
-    hipLaunchKernelGGL(k_scan_segapply<KIND>, grid, dim3(256), 0, st, states, segbuf, (int)d.NC, elems, segs);
+    hipLaunchKernelGGL(k_scan_segapply<KIND>, grid, dim3(256), 0, st, states, segbuf, sh, segs);
     return launch_ok();
 }
 
@@ -249,9 +254,11 @@ race_status_t run_forward(const Shape& s, const Derived& d, const WsLayout& wl, 
             return run_totals<C, false>(s, d, gr, c.K, c.V, nullptr, nullptr, kc, Wg, beta, Sg, st);
         })));
         if (s.causal) {
-            RACE_TRY(run_scan<SCAN_EXCL>(s, d, gr.F65, Sg, nullptr, 0, reinterpret_cast<float*>(ws + wl.scan), st));
+            RACE_TRY(run_scan<SCAN_EXCL>(s, d, gr.F65, gr.F, !F32, Sg, nullptr, 0,
+                                         reinterpret_cast<float*>(ws + wl.scan), st));
         } else {
-            RACE_TRY(run_scan<SCAN_TOTAL>(s, d, gr.F65, Sg, St + group_states_floats(d, 1, g), gr.F65, nullptr, st));
+            RACE_TRY(run_scan<SCAN_TOTAL>(s, d, gr.F65, gr.F, !F32, Sg, St + group_states_floats(d, 1, g), gr.F65,
+                                          nullptr, st));
         }
     }
     PassArgs a{};
@@ -331,11 +338,11 @@ race_status_t run_backward(const Shape& s, const Derived& d, const WsLayout& wl,
                                        group_w(c.W, s, gr, F32), c.beta, Tg, st);
         })));
         if (s.causal) {
-            RACE_TRY(run_scan<SCAN_REV_EXCL>(s, d, gr.F65, Tg, nullptr, 0, reinterpret_cast<float*>(ws + wl.scan),
-                                             st));
+            RACE_TRY(run_scan<SCAN_REV_EXCL>(s, d, gr.F65, gr.F, !F32, Tg, nullptr, 0,
+                                             reinterpret_cast<float*>(ws + wl.scan), st));
         } else {
-            RACE_TRY(run_scan<SCAN_TOTAL>(s, d, gr.F65, Tg, Ttw + group_states_floats(d, 1, g), gr.F65, nullptr,
-                                          st));
+            RACE_TRY(run_scan<SCAN_TOTAL>(s, d, gr.F65, gr.F, !F32, Tg, Ttw + group_states_floats(d, 1, g), gr.F65,
+                                          nullptr, st));
         }
     }
     PassArgs k{};
@@ -397,7 +404,7 @@ race_status_t dispatch(const Shape& s, const Derived& d, const WsLayout& wl, con
             RACE_TRY((with_cfg<F32>(s.P, gr.MT, [&](auto tag) {
                 using C = typename decltype(tag)::type;
                 return run_totals<C, false>(s, d, gr, c.K, c.V, nullptr, nullptr, plane_cache(ws + wl.Kc, cl, g),
-                                            group_w(c.W, s, gr, F32), beta, Sg, st);
+                                            group_w(c.W, s, gr, F32), beta, Sg, st, 0, 0, 0, 1);
             })));
             profile_mark("state_total", st);
             hipLaunchKernelGGL(k_state_total<SCAN_TOTAL>, dim3((unsigned)((gr.F65 + 255) / 256), (unsigned)d.BH), dim3(256), 0,

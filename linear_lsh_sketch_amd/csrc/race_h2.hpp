@@ -286,11 +286,11 @@ race_status_t run_forward_h2(const Shape& s, const Derived& d, const WsLayout& w
                                                   nullptr, beta, Sg, st, D128, 64);
             })));
             if (s.causal) {
-                RACE_TRY(run_scan<SCAN_EXCL>(s, d, gr.F65, Sg, nullptr, 0, reinterpret_cast<float*>(ws + wl.scan),
-                                             st));
+                RACE_TRY(run_scan<SCAN_EXCL>(s, d, gr.F65, gr.F, !F32, Sg, nullptr, 0,
+                                             reinterpret_cast<float*>(ws + wl.scan), st));
             } else {
-                RACE_TRY(run_scan<SCAN_TOTAL>(s, d, gr.F65, Sg, St + group_states_floats(d, 1, g), gr.F65, nullptr,
-                                              st));
+                RACE_TRY(run_scan<SCAN_TOTAL>(s, d, gr.F65, gr.F, !F32, Sg, St + group_states_floats(d, 1, g), gr.F65,
+                                              nullptr, st));
             }
         }
         PassArgs a{};
@@ -387,10 +387,10 @@ race_status_t run_backward_h2(const Shape& s, const Derived& d, const WsLayout& 
                                            plane_cache(qbase, cl, g), nullptr, c.beta, Tg, st, D128, 64, h);
             })));
             if (s.causal) {
-                RACE_TRY(run_scan<SCAN_REV_EXCL>(s, d, gr.F65, Tg, nullptr, 0,
+                RACE_TRY(run_scan<SCAN_REV_EXCL>(s, d, gr.F65, gr.F, !F32, Tg, nullptr, 0,
                                                  reinterpret_cast<float*>(ws + wl.scan), st));
             } else {
-                RACE_TRY(run_scan<SCAN_TOTAL>(s, d, gr.F65, Tg,
+                RACE_TRY(run_scan<SCAN_TOTAL>(s, d, gr.F65, gr.F, !F32, Tg,
                                               Ttw + half_states_floats(d, 1, h) + group_states_floats(d, 1, g),
                                               gr.F65, nullptr, st));
             }

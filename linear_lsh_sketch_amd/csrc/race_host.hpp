@@ -211,12 +211,12 @@ inline SavedLayout saved_layout(const Shape& s, const Derived& d) {
 inline size_t saved_bytes(const Shape& s, const Derived& d) { return saved_layout(s, d).total; }
 
 // Segments of the chunk scan: one pass over the chunks when the grid of
-// (state elements / 256) x heads already has enough workgroups to keep the
+// (state words / 256) x heads already has enough workgroups to keep the
 // memory busy; otherwise up to 16 segments of at least 64 chunks each,
 // summed first and then scanned from their offsets (two launches).
-inline int scan_segs(const Shape& s, const Derived& d, int64_t F65) {
+inline int scan_segs(const Shape& s, const Derived& d, int64_t nwords) {
     if (!s.causal) return 1;
-    const int64_t blocks = (F65 + 255) / 256 * d.BH;
+    const int64_t blocks = (nwords + 255) / 256 * d.BH;
     if (blocks >= 192) return 1;
     int64_t segs = (768 + blocks - 1) / blocks;
     if (segs > 16) segs = 16;
@@ -270,13 +270,19 @@ inline WsLayout ws_layout(const Shape& s, const Derived& d, int kind) {
         w.acc = off;  off = align256(off + tokens * (size_t)64 * sizeof(float));
         w.accD = off; off = align256(off + tokens * sizeof(float));
     }
-    // segment sums of one group's scan at a time (the largest of the groups)
+    // segment sums of one group's scan at a time (the largest of the groups,
+    // either state form: float32, F65 words, F65 floats per segment; compact,
+    // 33 F + 64 words of which 32 F bf16 pairs, F65 + 64 floats per segment)
     size_t seg_bytes = 0;
-    for (const int64_t f65 : {d.F65, d.F65l}) {
-        const int segs = scan_segs(s, d, f65);
-        if (segs > 1) {
-            const size_t b = (size_t)d.BH * (size_t)segs * (size_t)f65 * sizeof(float);
-            if (b > seg_bytes) seg_bytes = b;
+    for (const int F : {d.F, d.Fl}) {
+        const int64_t f65 = (int64_t)F * 65;
+        const int64_t forms[2][2] = {{f65, f65}, {33 * (int64_t)F + 64, f65 + 64}};
+        for (const auto& fm : forms) {
+            const int segs = scan_segs(s, d, fm[0]);
+            if (segs > 1) {
+                const size_t b = (size_t)d.BH * (size_t)segs * (size_t)fm[1] * sizeof(float);
+                if (b > seg_bytes) seg_bytes = b;
+            }
         }
     }
     w.scan = off;

@@ -392,9 +392,55 @@ __device__ inline void zero_pads(typename Prec<C::F32>::elem* rows_a, typename P
 }
 
 // State block of one (bh, chunk): value sums [F][64] then masses [F], float32.
+// Sketch states between the passes. float32 inputs: [F x 64 value sums |
+// F masses], float32. bf16 inputs (the compact form, half the bytes of the
+// value sums, which the passes round to bf16 operands anyway): the F x 64
+// value sums in bf16 (row f at bf16 index 64 f), then the F masses in
+// float32 (float index 32 F: exact counts for the hard buckets), then the
+// 64 value sums of the empty subset in float32 (float index 33 F: the
+// forward's exact float32 term; it is the row of every table's empty subset,
+// so the same for all). Either form sits in a slot of F * 65 floats.
+template <class C>
+struct StateForm {
+    static constexpr bool compact = !C::F32;
+    static constexpr int mass = compact ? 32 * C::F : DH * C::F;   // float index of the masses
+    static constexpr int empty = 33 * C::F;                        // compact: the empty subset's row
+};
+
+__device__ inline float bf16_at(const float* st, int i) {
+    return (float)reinterpret_cast<const __bf16*>(st)[i];
+}
+
 template <class C>
 __device__ inline void load_state(const float* __restrict__ st, int w, int ln, int g,
                                   f32x4 Macc[C::NKC * 2], f32x4 Zacc[C::NOWN * 2]) {
+    using SF = StateForm<C>;
+    if constexpr (SF::compact) {
+#pragma unroll
+        for (int kc = 0; kc < C::NKC; ++kc)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int f = 32 * kc + 8 * g + 4 * h + i;
+                    Macc[2 * kc + h][i] = bf16_at(st, f * DH + 16 * w + ln);
+                }
+        // feature 0 (table 0's empty subset) from its float32 copy
+        if (g == 0) Macc[0][0] = st[SF::empty + 16 * w + ln];
+#pragma unroll
+        for (int j = 0; j < C::NOWN; ++j) {
+            const int kc = NW * j + w;
+            const bool owner = kc < C::NKC && ln == 0;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int f = 32 * (owner ? kc : 0) + 8 * g + 4 * h + i;
+                    Zacc[2 * j + h][i] = owner ? st[SF::mass + f] : 0.f;
+                }
+        }
+        return;
+    }
 #pragma unroll
     for (int kc = 0; kc < C::NKC; ++kc)
 #pragma unroll
@@ -428,12 +474,20 @@ __device__ inline void load_state(const float* __restrict__ st, int w, int ln, i
 template <class C>
 __device__ inline void load_state_t(const float* __restrict__ st, int w, int ln, int g,
                                     f32x4 Macc[C::NKC * 2], f32x4 Zacc[C::NOWN * 2]) {
+    using SF = StateForm<C>;
 #pragma unroll
     for (int kc = 0; kc < C::NKC; ++kc)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int f = 32 * kc + 8 * (ln >> 2) + 4 * h + (ln & 3);
-            Macc[2 * kc + h] = *reinterpret_cast<const f32x4*>(st + (size_t)f * DH + 16 * w + 4 * g);
+            if constexpr (SF::compact) {
+                const bf16x4 v = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(st) + f * DH +
+                                                                  16 * w + 4 * g);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Macc[2 * kc + h][i] = (float)v[i];
+            } else {
+                Macc[2 * kc + h] = *reinterpret_cast<const f32x4*>(st + (size_t)f * DH + 16 * w + 4 * g);
+            }
         }
 #pragma unroll
     for (int j = 0; j < C::NOWN; ++j) {
@@ -442,14 +496,40 @@ __device__ inline void load_state_t(const float* __restrict__ st, int w, int ln,
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int f = 32 * (owner ? kc : 0) + 8 * (ln >> 2) + 4 * h + (ln & 3);
-            Zacc[2 * j + h] = f32x4{owner ? st[(size_t)C::F * DH + f] : 0.f, 0.f, 0.f, 0.f};
+            Zacc[2 * j + h] = f32x4{owner ? st[SF::mass + f] : 0.f, 0.f, 0.f, 0.f};
         }
     }
 }
 
-template <class C>
+// COMPACT: the compact form for bf16 inputs (else float32).
+template <class C, bool COMPACT = StateForm<C>::compact>
 __device__ inline void store_state(float* __restrict__ st, int w, int ln, int g,
                                    const f32x4 Macc[C::NKC * 2], const f32x4 Zacc[C::NOWN * 2]) {
+    if constexpr (COMPACT) {
+        using SF = StateForm<C>;
+        __bf16* sv = reinterpret_cast<__bf16*>(st);
+#pragma unroll
+        for (int kc = 0; kc < C::NKC; ++kc)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int f = 32 * kc + 8 * g + 4 * h + i;
+                    sv[f * DH + 16 * w + ln] = (__bf16)Macc[2 * kc + h][i];
+                }
+        if (g == 0) st[SF::empty + 16 * w + ln] = Macc[0][0];
+#pragma unroll
+        for (int j = 0; j < C::NOWN; ++j) {
+            const int kc = NW * j + w;
+            if (kc < C::NKC && ln == 0) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) st[SF::mass + 32 * kc + 8 * g + 4 * h + i] = Zacc[2 * j + h][i];
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int kc = 0; kc < C::NKC; ++kc)
 #pragma unroll
@@ -688,6 +768,7 @@ struct TotArgs {
     int dh;              // columns of a row the kernels use: 64, or 32 (columns 32..63 zero)
     int rs;              // elements between consecutive rows (the head dimension)
     int ezero;           // gradient sketch: e taken as 0 (the second value half of d = 128)
+    int f32form;         // bf16 inputs: write the float32 form (the running decode state's source)
 };
 
 template <class C, bool CACHED>
@@ -799,23 +880,31 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 3))) void
             __syncthreads();
         }
     }
-    store_state<C>(a.out + ((size_t)bh * a.nchunks + c) * (size_t)(C::F * 65), w, ln, g, Macc, Zacc);
+    float* out = a.out + ((size_t)bh * a.nchunks + c) * (size_t)(C::F * 65);
+    if (StateForm<C>::compact && a.f32form) store_state<C, false>(out, w, ln, g, Macc, Zacc);
+    else store_state<C>(out, w, ln, g, Macc, Zacc);
 }
 
 // ---------------------------------------------------------------------------
 // scans over chunks (one thread per state element, fixed order: deterministic)
 // ---------------------------------------------------------------------------
-// Running sum over logical chunk positions [c0, c1) of one state element
+// Running sum over logical chunk positions [c0, c1) of one state word
 // (position c is chunk c, or chunk nchunks - 1 - c for the reverse scan),
 // starting from run; with WRITE each position first receives the sum of the
-// positions before it. The loads of the next batch are issued before the
-// sums and stores of the current one, so about 2 * BATCH loads per lane stay
-// in flight; the order of the additions is fixed (deterministic).
-template <int KIND, bool WRITE>
-__device__ inline float scan_range(float* p, int nchunks, int elems, int c0, int c1, float run) {
+// positions before it. A word is one float32 value, or (PAIR: the value sums
+// of the compact form) two bf16 values summed in two float32 runs, each
+// prefix rounded once to bf16. The loads of the next batch are issued before
+// the sums and stores of the current one, so about 2 * BATCH loads per lane
+// stay in flight; the order of the additions is fixed (deterministic).
+struct Run2 {
+    float a, b;
+};
+
+template <int KIND, bool WRITE, bool PAIR>
+__device__ inline Run2 scan_range(float* p, int nchunks, int stride, int c0, int c1, Run2 run) {
     constexpr int BATCH = 16;
     auto at = [&](int c) -> float* {
-        return p + (size_t)((KIND == SCAN_REV_EXCL) ? nchunks - 1 - c : c) * elems;
+        return p + (size_t)((KIND == SCAN_REV_EXCL) ? nchunks - 1 - c : c) * stride;
     };
     auto load = [&](int b0, float (&v)[BATCH]) {
 #pragma unroll
@@ -829,8 +918,16 @@ __device__ inline float scan_range(float* p, int nchunks, int elems, int c0, int
 #pragma unroll
         for (int k = 0; k < BATCH; ++k) {
             if (b0 + k < c1) {
-                if constexpr (WRITE) *at(b0 + k) = run;
-                run += cur[k];
+                if constexpr (PAIR) {
+                    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+                    if constexpr (WRITE) *at(b0 + k) = __builtin_bit_cast(float, bf16x2{(__bf16)run.a, (__bf16)run.b});
+                    const bf16x2 v = __builtin_bit_cast(bf16x2, cur[k]);
+                    run.a += (float)v[0];
+                    run.b += (float)v[1];
+                } else {
+                    if constexpr (WRITE) *at(b0 + k) = run.a;
+                    run.a += cur[k];
+                }
             }
         }
 #pragma unroll
@@ -839,24 +936,44 @@ __device__ inline float scan_range(float* p, int nchunks, int elems, int c0, int
     return run;
 }
 
-// One pass over all chunks (one thread per state element): exclusive prefix
+// Words of one chunk slot (stride floats apart): the first npair hold bf16
+// pairs (the compact form's value sums; 0 for the float32 form), the rest up
+// to nwords one float32 each. Segment sums keep two floats per pair word:
+// word e < npair at 2 e, 2 e + 1, word e >= npair at npair + e.
+struct ScanShape {
+    int nchunks, stride, nwords, npair;
+};
+
+// One pass over all chunks (one thread per state word): exclusive prefix
 // (causal), reverse exclusive prefix (backward) or the total (non-causal).
-// The total of head bh goes to total[bh * total_stride + e].
+// The total of head bh goes to total + bh * total_stride (same form).
 template <int KIND>
-__global__ __launch_bounds__(256) void k_scan(float* __restrict__ st, float* __restrict__ total,
-                                              int nchunks, int elems, int64_t total_stride) {
+__global__ __launch_bounds__(256) void k_scan(float* __restrict__ st, float* __restrict__ total, ScanShape sh,
+                                              int64_t total_stride) {
     const int e = blockIdx.x * blockDim.x + threadIdx.x;
     const int bh = blockIdx.y;
-    if (e >= elems) return;
-    float* p = st + (size_t)bh * nchunks * elems + e;
-    const float run = scan_range<KIND, KIND != SCAN_TOTAL>(p, nchunks, elems, 0, nchunks, 0.f);
-    if constexpr (KIND == SCAN_TOTAL) total[(size_t)bh * (size_t)total_stride + e] = run;
+    if (e >= sh.nwords) return;
+    float* p = st + (size_t)bh * sh.nchunks * sh.stride + e;
+    constexpr bool W = KIND != SCAN_TOTAL;
+    Run2 run{0.f, 0.f};
+    if (e < sh.npair) {
+        run = scan_range<KIND, W, true>(p, sh.nchunks, sh.stride, 0, sh.nchunks, run);
+        if constexpr (KIND == SCAN_TOTAL) {
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            total[(size_t)bh * (size_t)total_stride + e] =
+                __builtin_bit_cast(float, bf16x2{(__bf16)run.a, (__bf16)run.b});
+        }
+    } else {
+        run = scan_range<KIND, W, false>(p, sh.nchunks, sh.stride, 0, sh.nchunks, run);
+        if constexpr (KIND == SCAN_TOTAL) total[(size_t)bh * (size_t)total_stride + e] = run.a;
+    }
 }
 
 // Total of the chunk states of one head and table group into its part of a
 // running decode state: the F x 64 value sums in float32 (the chunk states'
-// type) and the F masses summed and stored in float64, so that counts beyond
-// 2^24 keys stay exact.
+// type; the chunk states of a prefill are in the float32 form) and the F
+// masses summed and stored in float64, so that counts beyond 2^24 keys stay
+// exact.
 template <int KIND = SCAN_TOTAL>
 __global__ __launch_bounds__(256) void k_state_total(const float* __restrict__ st, float* __restrict__ state,
                                                      int nchunks, int F, int64_t head_floats) {
@@ -866,7 +983,7 @@ __global__ __launch_bounds__(256) void k_state_total(const float* __restrict__ s
     const float* p = st + (size_t)bh * nchunks * (size_t)(F * 65) + e;
     float* out = state + (size_t)bh * (size_t)head_floats;
     if (e < F * DH) {
-        out[e] = scan_range<SCAN_TOTAL, false>(const_cast<float*>(p), nchunks, F * 65, 0, nchunks, 0.f);
+        out[e] = scan_range<SCAN_TOTAL, false, false>(const_cast<float*>(p), nchunks, F * 65, 0, nchunks, Run2{0.f, 0.f}).a;
     } else {
         double z = 0.0;
         for (int c = 0; c < nchunks; ++c) z += (double)p[(size_t)c * (F * 65)];
@@ -878,30 +995,49 @@ __global__ __launch_bounds__(256) void k_state_total(const float* __restrict__ s
 // keep the memory busy (few heads): the logical chunk positions are split
 // into segs segments; k_scan_segsum sums each segment, k_scan_segapply starts
 // each segment from the sum of the segments before it (fixed order).
+// segsum: per head and segment npair + nwords floats (ScanShape).
 template <int KIND>
 __global__ __launch_bounds__(256) void k_scan_segsum(const float* __restrict__ st, float* __restrict__ segsum,
-                                                     int nchunks, int elems, int segs) {
+                                                     ScanShape sh, int segs) {
     const int e = blockIdx.x * blockDim.x + threadIdx.x;
     const int bh = blockIdx.y / segs, sg = blockIdx.y % segs;
-    if (e >= elems) return;
-    const int len = (nchunks + segs - 1) / segs;
-    const int c0 = sg * len, c1 = min(nchunks, c0 + len);
-    float* p = const_cast<float*>(st) + (size_t)bh * nchunks * elems + e;
-    segsum[((size_t)bh * segs + sg) * elems + e] = scan_range<KIND, false>(p, nchunks, elems, c0, c1, 0.f);
+    if (e >= sh.nwords) return;
+    const int len = (sh.nchunks + segs - 1) / segs;
+    const int c0 = sg * len, c1 = min(sh.nchunks, c0 + len);
+    float* p = const_cast<float*>(st) + (size_t)bh * sh.nchunks * sh.stride + e;
+    float* out = segsum + ((size_t)bh * segs + sg) * (size_t)(sh.npair + sh.nwords);
+    if (e < sh.npair) {
+        const Run2 r = scan_range<KIND, false, true>(p, sh.nchunks, sh.stride, c0, c1, Run2{0.f, 0.f});
+        out[2 * e] = r.a;
+        out[2 * e + 1] = r.b;
+    } else {
+        out[sh.npair + e] = scan_range<KIND, false, false>(p, sh.nchunks, sh.stride, c0, c1, Run2{0.f, 0.f}).a;
+    }
 }
 
 template <int KIND>
 __global__ __launch_bounds__(256) void k_scan_segapply(float* __restrict__ st, const float* __restrict__ segsum,
-                                                       int nchunks, int elems, int segs) {
+                                                       ScanShape sh, int segs) {
     const int e = blockIdx.x * blockDim.x + threadIdx.x;
     const int bh = blockIdx.y / segs, sg = blockIdx.y % segs;
-    if (e >= elems) return;
-    const int len = (nchunks + segs - 1) / segs;
-    const int c0 = sg * len, c1 = min(nchunks, c0 + len);
-    float run = 0.f;
-    for (int s2 = 0; s2 < sg; ++s2) run += segsum[((size_t)bh * segs + s2) * elems + e];
-    float* p = st + (size_t)bh * nchunks * elems + e;
-    scan_range<KIND, true>(p, nchunks, elems, c0, c1, run);
+    if (e >= sh.nwords) return;
+    const int len = (sh.nchunks + segs - 1) / segs;
+    const int c0 = sg * len, c1 = min(sh.nchunks, c0 + len);
+    const size_t per = (size_t)(sh.npair + sh.nwords);
+    const bool pair = e < sh.npair;
+    Run2 run{0.f, 0.f};
+    for (int s2 = 0; s2 < sg; ++s2) {
+        const float* in = segsum + ((size_t)bh * segs + s2) * per;
+        if (pair) {
+            run.a += in[2 * e];
+            run.b += in[2 * e + 1];
+        } else {
+            run.a += in[sh.npair + e];
+        }
+    }
+    float* p = st + (size_t)bh * sh.nchunks * sh.stride + e;
+    if (pair) scan_range<KIND, true, true>(p, sh.nchunks, sh.stride, c0, c1, run);
+    else scan_range<KIND, true, false>(p, sh.nchunks, sh.stride, c0, c1, run);
 }
 
 // ---------------------------------------------------------------------------

@@ -63,8 +63,12 @@ def test_workspace_and_saved_sizes():
     assert fwd_s >= states and fwd >= fwd_s + cache
     # gradient states and e per token
     assert bwd >= states + rows * 4
-    # plus a saved buffer and the forward output (float32 bound)
-    assert rec >= fwd_s + bwd + saved + rows * 64 * 4
+    # plus a saved buffer and the forward output (float32 bound); each kind
+    # holds one buffer for the segment sums of the chunk scan (at most 16
+    # segments of F * 65 + 64 floats per head), which the recompute kind
+    # shares between its forward and backward
+    seg_max = 4 * 16 * (256 * 65 + 64) * 4
+    assert rec >= fwd_s + bwd + saved + rows * 64 * 4 - 2 * seg_max
     # non-causal: the total sketch (L8 P2: MT = 1, F = 32)
     rows_nc = 6 * 100
     cache_nc = _a256(rows_nc * 16 * 4) + _a256(rows_nc * 4)
@@ -98,10 +102,12 @@ def test_table_group_sizes():
 def test_segmented_scan_workspace():
     # one causal head of 2^20 tokens, L8 P1 (F = 32, 65 F floats per state):
     # chunk 1024 gives 1024 chunks and 9 workgroups per pass, so the chunk
-    # scans run in 16 segments whose sums take BH * 16 * 65 F floats more
+    # scans run in 16 segments whose sums take BH * 16 * (65 F + 64) floats
+    # more (sized for the compact form of bf16 inputs: two floats per word of
+    # bf16 value pairs, and the float32 row of the empty subset)
     per = 32 * 65 * 4
     seg = race.workspace_bytes(1, 1, 1 << 20, 64, 1, 8, True, 1024, race.WS_FWD_SAVED)
-    assert seg == _a256(1024 * per) + _a256(16 * per)
+    assert seg == _a256(1024 * per) + _a256(16 * (per + 64 * 4))
     # four chunks: one pass, no segment sums
     one = race.workspace_bytes(1, 1, 4096, 64, 1, 8, True, 1024, race.WS_FWD_SAVED)
     assert one == _a256(4 * per)
