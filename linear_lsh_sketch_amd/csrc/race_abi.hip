@@ -242,7 +242,6 @@ race_status_t race_attn_state_bytes(int64_t B, int64_t H, int d, int P, int L, s
     Derived dv;
     race_status_t rc = prepare(B, H, 1, d, P, L, 0, 1, s, dv);
     if (rc != RACE_OK) return rc;
-    if (dv.VH != 1) return RACE_ERR_UNSUPPORTED;   // the running state: head dimension 64 or 32
     *bytes = (size_t)dv.BH * (size_t)dv.RSall * sizeof(float);
     return RACE_OK;
 }
@@ -257,7 +256,6 @@ race_status_t race_attn_prefill(const void* K, const void* V, const void* W, int
     Derived dv;
     race_status_t rc = prepare(B, H, N, d, P, L, 0, chunk, s, dv);
     if (rc != RACE_OK) return rc;
-    if (dv.VH != 1) return RACE_ERR_UNSUPPORTED;
     s.w_per_head = per_head(dtype);
     const WsLayout wl = ws_layout(s, dv, WS_FWD);
     if (ws_bytes < wl.total) return RACE_ERR_WORKSPACE;
@@ -277,7 +275,6 @@ race_status_t race_attn_decode(const void* q, const void* k, const void* v, cons
     Derived dv;
     race_status_t rc = prepare(B, H, T, d, P, L, 0, 1, s, dv);
     if (rc != RACE_OK) return rc;
-    if (dv.VH != 1) return RACE_ERR_UNSUPPORTED;
     s.w_per_head = per_head(dtype);
     if (T > 0x7fffffff) return RACE_ERR_UNSUPPORTED;
     Call c{};

@@ -38,14 +38,20 @@ constexpr int DEC_MAXF = 512;    // largest F of one table group
 static_assert(DEC_MAXF <= DEC_NT, "one thread per feature and mass");
 
 // The running state of a head holds its table groups one after the other,
-// each as [F_g x 64 float32 value sums | F_g float64 masses] (66 F_g floats;
-// rows in the feature order of the sketch kernels' states): the masses count
-// keys exactly beyond 2^24. Full groups have F features and Lg tables, the
-// last Fl and L - (G - 1) Lg.
+// each as [VH halves of F_g x 64 float32 value sums | F_g float64 masses]
+// (RW = 64 VH + 2 floats per feature; rows in the feature order of the sketch
+// kernels' states): the masses count keys exactly beyond 2^24. VH = 2 at head
+// dimension 128 (value columns 0..63, then 64..127), else 1. Full groups have
+// F features and Lg tables, the last Fl and L - (G - 1) Lg.
+//
+// Head dimension 128: the planes project the whole 128-column q and k rows,
+// and each launch updates and reads out one value half; the second half runs
+// first and leaves the masses as they were (it counts the new keys in its
+// registers), then the first half updates them too and stores them.
 struct DecodeArgs {
     const void *q, *k, *v, *W;
-    float* state;   // [BH][(G - 1) F * 66 + Fl * 66]
-    void* o;        // [BH][T][64]
+    float* state;   // [BH][((G - 1) F + Fl) RW]
+    void* o;        // [BH][T][dh]
     int T;          // new tokens per head (rows of a head in q, k, v, o), processed in order
     int tok;        // k_decode_one: the token of this launch (0 <= tok < T)
     int P, L, F, KB, TPT, TPL;
@@ -54,7 +60,10 @@ struct DecodeArgs {
     int hard;
     int H;          // heads: W of head bh at W + (bh % H) * w_hs bytes (0: one W for all)
     int64_t w_hs;
-    int dh;         // head dimension: 64, or 32 (columns 32..63 read as zero)
+    int dh;         // head dimension (row length of q, k, v, o and W): 32, 64 or 128
+    int VH;         // value halves of the state (2 at head dimension 128, else 1)
+    int half;       // the value half of this launch
+    int store_mass; // store the updated masses (0: the second half, before the first)
 };
 
 // Table and subset of canonical feature f (lane group g of 32-feature chunk
@@ -114,10 +123,12 @@ __device__ inline void dec_reduce_num(f32x4 acc, float (*s_num)[DH + 4], int wv,
 // written back as soon as the features are known, and the read-outs of the
 // groups are summed. NR = F / 32 state rows per thread of a full group (a
 // compile-time count).
-template <bool F32, int NR>
+// XW: projection width (64, or 128 at head dimension 128).
+template <bool F32, int NR, int XW>
 __global__ __launch_bounds__(DEC_NT) void k_decode_one(DecodeArgs a) {
     using elem = typename Prec<F32>::elem;
-    __shared__ float s_x[3][DH];             // q, k, v of this head
+    __shared__ float s_x[2][XW];             // q, k of this head
+    __shared__ float s_v[DH];                // this launch's value half
     __shared__ float s_t[2][128];            // t_p of each table plane, [q | k][l * P + p]
     __shared__ float s_phi[2][DEC_MAXF];     // features of q and of k
     __shared__ float s_num[DEC_NT / 64][DH + 4];  // partial read-outs per wave
@@ -126,17 +137,20 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_one(DecodeArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t bh = blockIdx.x;
     const int64_t r = bh * a.T + a.tok;      // row of this token in q, k, v, o
-    const int64_t head_floats = (int64_t)(a.G - 1) * a.F * 66 + (int64_t)a.Fl * 66;
+    const int RW = DH * a.VH + 2;
+    const int64_t head_floats = ((int64_t)(a.G - 1) * a.F + a.Fl) * RW;
     float* st_head = a.state + (size_t)bh * (size_t)head_floats;
     const int cq = tid & 15, rg = tid >> 4;
+    const int vcols = a.dh < DH ? a.dh : DH, vc0 = DH * a.half;   // this half's value columns
     constexpr int WV = 16 / sizeof(elem);   // elements per 16-byte load
     typedef elem wvec __attribute__((ext_vector_type(WV)));
 
-    if (tid < 3 * DH) {
-        const int which = tid / DH, c = tid % DH;
-        const void* src = which == 0 ? a.q : which == 1 ? a.k : a.v;
+    if (tid < 2 * XW) {
+        const int which = tid / XW, c = tid % XW;
+        const void* src = which == 0 ? a.q : a.k;
         s_x[which][c] = c < a.dh ? (float)reinterpret_cast<const elem*>(src)[r * a.dh + c] : 0.f;
     }
+    if (tid < DH) s_v[tid] = tid < vcols ? (float)reinterpret_cast<const elem*>(a.v)[r * a.dh + vc0 + tid] : 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};   // read-out of columns 4 cq .. +3 over this thread's rows
     double den = 0.0;                   // and over its masses
 
@@ -145,8 +159,9 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_one(DecodeArgs a) {
         const int F = lastg ? a.Fl : a.F;
         const int Lgr = lastg ? a.L - (a.G - 1) * a.Lg : a.Lg;
         const int LP = Lgr * a.P;
-        float* st = st_head + (size_t)gi * (size_t)a.F * 66;
-        double* zs = reinterpret_cast<double*>(st + (size_t)F * DH);
+        float* stg = st_head + (size_t)gi * (size_t)a.F * RW;
+        float* st = stg + (size_t)a.half * F * DH;   // this half's value sums
+        double* zs = reinterpret_cast<double*>(stg + (size_t)a.VH * F * DH);
         // The state rows do not depend on this token: their loads are issued
         // first, so their latency overlaps the projections and features.
         f32x4 s[NR];
@@ -157,15 +172,15 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_one(DecodeArgs a) {
         // so are the hyperplane rows: projection row pr = side * L P + l * P + p
         // of the group takes `parts` lanes, part pi holding columns
         // pi * ncol .. + ncol - 1 of its weights, loaded 16 bytes at a time
-        const int parts = dec_parts(LP), ncol = DH / parts;
+        const int parts = dec_parts(LP), ncol = XW / parts;
         const int pr = tid / parts, pi = tid % parts, side = pr / LP, row = pr % LP, c0 = pi * ncol;
-        wvec wr[DH / WV / 2];
+        wvec wr[XW / WV / 2];
         if (pr < 2 * LP) {
             const wvec* w = reinterpret_cast<const wvec*>(
                 reinterpret_cast<const elem*>(reinterpret_cast<const char*>(a.W) + (bh % a.H) * a.w_hs) +
                 ((size_t)gi * a.Lg * a.P + row) * a.dh + c0);
 #pragma unroll
-            for (int j = 0; j < DH / WV / 2; ++j) {
+            for (int j = 0; j < XW / WV / 2; ++j) {
                 if (j * WV < ncol && c0 + j * WV < a.dh) {
                     wr[j] = w[j];
                 } else {
@@ -182,7 +197,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_one(DecodeArgs a) {
             float h = 0.f, ss = 0.f;
             if (pr < 2 * LP) {
 #pragma unroll
-                for (int j = 0; j < DH / WV / 2; ++j) {
+                for (int j = 0; j < XW / WV / 2; ++j) {
                     if (j * WV >= ncol) break;
 #pragma unroll
                     for (int e = 0; e < WV; ++e) {
@@ -218,7 +233,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_one(DecodeArgs a) {
 
         // value sums: lane quad cq owns columns 4 cq .. 4 cq + 3 of rows rg, rg + 32, ...
         {
-            const f32x4 vq = {s_x[2][4 * cq], s_x[2][4 * cq + 1], s_x[2][4 * cq + 2], s_x[2][4 * cq + 3]};
+            const f32x4 vq = {s_v[4 * cq], s_v[4 * cq + 1], s_v[4 * cq + 2], s_v[4 * cq + 3]};
 #pragma unroll
             for (int i = 0; i < NR; ++i) {
                 const int f = rg + DEC_RG * i;
@@ -236,7 +251,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_one(DecodeArgs a) {
         if (tid < F) {
             const float pk = s_phi[1][tid];
             const double z = z_old + (double)pk;
-            if (pk != 0.f) zs[tid] = z;
+            if (pk != 0.f && a.store_mass) zs[tid] = z;
             den += (double)s_phi[0][tid] * z;
         }
     }
@@ -253,7 +268,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_one(DecodeArgs a) {
 #pragma unroll
         for (int w = 0; w < DEC_NT / 64; ++w) dsum += s_den[w];
         const float o = (a.hard && dsum == 0.0) ? 0.f : num / (float)dsum;
-        if (tid < a.dh) reinterpret_cast<elem*>(a.o)[r * a.dh + tid] = (elem)o;
+        if (tid < vcols) reinterpret_cast<elem*>(a.o)[r * a.dh + vc0 + tid] = (elem)o;
     }
 }
 
@@ -263,21 +278,23 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_one(DecodeArgs a) {
 // processed (100 registers at F = 256 in bf16: two workgroups per CU; the
 // one-launch-per-token kernel above needs 184 with its group loop, one
 // workgroup per CU, and took 745 us against 407 us for 16,384 heads).
-template <bool F32, int NR>
+template <bool F32, int NR, int XW>
 __global__ __launch_bounds__(DEC_NT) void k_decode_multi(DecodeArgs a) {
     using elem = typename Prec<F32>::elem;
-    __shared__ float s_x[3][DH];             // q, k, v of the current token
+    __shared__ float s_x[2][XW];             // q, k of the current token
+    __shared__ float s_v[DH];                // its value half
     __shared__ float s_t[2][128];            // t_p of each table plane, [q | k][l * P + p]
     __shared__ float s_phi[2][DEC_MAXF];     // features of q and of k
     __shared__ float s_num[DEC_NT / 64][DH + 4];  // partial read-outs per wave
     __shared__ double s_den[DEC_NT / 64];
-    __shared__ float s_w[128][DH + 1];       // hyperplane rows (padded: conflict-free row reads)
+    __shared__ float s_w[128][XW + 1];       // hyperplane rows (padded: conflict-free row reads)
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t bh = blockIdx.x;
     const int F = a.F, LP = a.L * a.P;
-    float* st = a.state + (size_t)bh * (size_t)F * 66;
-    double* zs = reinterpret_cast<double*>(st + (size_t)F * DH);
+    float* sth = a.state + (size_t)bh * (size_t)F * (DH * a.VH + 2);
+    float* st = sth + (size_t)a.half * F * DH;   // this half's value sums
+    double* zs = reinterpret_cast<double*>(sth + (size_t)a.VH * F * DH);
 
     // The state rows do not depend on the new tokens: their loads are issued
     // first, so their latency overlaps the first token's projections. They
@@ -294,8 +311,8 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_multi(DecodeArgs a) {
     {
         constexpr int WV = 16 / sizeof(elem);
         typedef elem wvec __attribute__((ext_vector_type(WV)));
-        for (int e = tid; e < LP * (DH / WV); e += DEC_NT) {
-            const int wrow = e / (DH / WV), c = (e % (DH / WV)) * WV;
+        for (int e = tid; e < LP * (XW / WV); e += DEC_NT) {
+            const int wrow = e / (XW / WV), c = (e % (XW / WV)) * WV;
             wvec v;
             if (c < a.dh) {
                 v = *reinterpret_cast<const wvec*>(Wh + (size_t)wrow * a.dh + c);
@@ -307,17 +324,23 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_multi(DecodeArgs a) {
             for (int j = 0; j < WV; ++j) s_w[wrow][c + j] = (float)v[j];
         }
     }
-    const int parts = dec_parts(LP), ncol = DH / parts;
+    const int parts = dec_parts(LP), ncol = XW / parts;
     const int pr = tid / parts, pi = tid % parts, side = pr / LP, row = pr % LP, c0 = pi * ncol;
-    // q, k, v rows are loaded one token ahead: thread tid < 3 * 64 holds one
-    // element of the next token while the current one is processed
-    const int which = tid / DH, col = tid % DH;
-    const elem* src = reinterpret_cast<const elem*>(which == 0 ? a.q : which == 1 ? a.k : a.v);
+    // q, k, v rows are loaded one token ahead: thread tid < 2 XW + 64 holds
+    // one element (of q, of k, or of the value half) of the next token while
+    // the current one is processed
+    const int vcols = a.dh < DH ? a.dh : DH;
+    const bool isv = tid >= 2 * XW;
+    const int which = isv ? 2 : tid / XW, col = isv ? tid - 2 * XW : tid % XW;
+    const elem* src = reinterpret_cast<const elem*>(which == 0 ? a.q : which == 1 ? a.k : a.v) +
+                      (isv ? DH * a.half : 0);
+    float* dst = isv ? &s_v[col < DH ? col : 0] : &s_x[which][col];
+    const bool loads = tid < 2 * XW + DH;
     const int64_t r0 = bh * a.T;   // first row of this head's q, k, v, o
     float nx = 0.f;
-    const bool in_col = col < a.dh;
-    if (tid < 3 * DH) {
-        s_x[which][col] = in_col ? (float)src[r0 * a.dh + col] : 0.f;
+    const bool in_col = col < (isv ? vcols : a.dh);
+    if (loads) {
+        *dst = in_col ? (float)src[r0 * a.dh + col] : 0.f;
         if (a.T > 1 && in_col) nx = (float)src[(r0 + 1) * a.dh + col];
     }
     __syncthreads();
@@ -366,7 +389,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_multi(DecodeArgs a) {
         // final, so the stores overlap the read-out's reduction.
         const bool last = tok == a.T - 1;
         {
-            const f32x4 vq = {s_x[2][4 * cq], s_x[2][4 * cq + 1], s_x[2][4 * cq + 2], s_x[2][4 * cq + 3]};
+            const f32x4 vq = {s_v[4 * cq], s_v[4 * cq + 1], s_v[4 * cq + 2], s_v[4 * cq + 3]};
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int i = 0; i < NR; ++i) {
@@ -385,7 +408,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_multi(DecodeArgs a) {
             double den = 0.0;
             if (tid < F) {
                 z += (double)s_phi[1][tid];
-                if (last) zs[tid] = z;
+                if (last && a.store_mass) zs[tid] = z;
                 den = (double)s_phi[0][tid] * z;
             }
 #pragma unroll
@@ -401,10 +424,10 @@ __global__ __launch_bounds__(DEC_NT) void k_decode_multi(DecodeArgs a) {
 #pragma unroll
             for (int w = 0; w < DEC_NT / 64; ++w) den += s_den[w];
             const float o = (a.hard && den == 0.0) ? 0.f : num / (float)den;
-            if (tid < a.dh) reinterpret_cast<elem*>(a.o)[r * a.dh + tid] = (elem)o;
+            if (tid < vcols) reinterpret_cast<elem*>(a.o)[r * a.dh + DH * a.half + tid] = (elem)o;
         }
-        if (tid < 3 * DH && tok + 1 < a.T) {
-            s_x[which][col] = nx;
+        if (loads && tok + 1 < a.T) {
+            *dst = nx;
             if (tok + 2 < a.T && in_col) nx = (float)src[(r + 2) * a.dh + col];
         }
         __syncthreads();

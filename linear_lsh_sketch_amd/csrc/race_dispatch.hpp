@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <functional>
+#include <type_traits>
 
 #include "race_decode.hpp"
 #include "race_host.hpp"
@@ -385,10 +386,7 @@ race_status_t dispatch(const Shape& s, const Derived& d, const WsLayout& wl, con
         }
         return RACE_OK;
     }
-    if (d.VH == 2) {
-        if (c.op == OP_FWD || c.op == OP_BWD) return dispatch_h2<F32>(s, d, wl, c);
-        return RACE_ERR_UNSUPPORTED;   // prefill and decode: head dimension 64 or 32
-    }
+    if (d.VH == 2 && c.op != OP_DECODE) return dispatch_h2<F32>(s, d, wl, c);
     if (c.op == OP_FWD) return run_forward<F32>(s, d, wl, c, c.O, c.saved_out);
     if (c.op == OP_BWD) return run_backward<F32>(s, d, wl, c);
     if (c.op == OP_PREFILL) {
@@ -407,8 +405,9 @@ race_status_t dispatch(const Shape& s, const Derived& d, const WsLayout& wl, con
                                             group_w(c.W, s, gr, F32), beta, Sg, st, 0, 0, 0, 1);
             })));
             profile_mark("state_total", st);
-            hipLaunchKernelGGL(k_state_total<SCAN_TOTAL>, dim3((unsigned)((gr.F65 + 255) / 256), (unsigned)d.BH), dim3(256), 0,
-                               st, Sg, c.state + (size_t)g * d.F * 66, (int)d.NC, gr.F, d.RSall);
+            hipLaunchKernelGGL(k_state_total<SCAN_TOTAL>, dim3((unsigned)((gr.F65 + 255) / 256), (unsigned)d.BH),
+                               dim3(256), 0, st, Sg, c.state + (size_t)g * d.F * d.RW, (int)d.NC, gr.F, d.RSall,
+                               (int64_t)gr.F * DH);
             RACE_TRY(launch_ok());
         }
         return RACE_OK;
@@ -421,20 +420,37 @@ race_status_t dispatch(const Shape& s, const Derived& d, const WsLayout& wl, con
             a.P = s.P; a.L = s.L; a.F = C::F; a.KB = C::KB; a.TPT = C::TPT; a.TPL = C::TPL;
             a.G = d.G; a.Lg = d.Lg; a.Fl = d.Fl;
             a.beta = c.beta; a.hard = c.hard;
-            a.H = (int)s.H; a.w_hs = w_head_bytes(s, C::F32); a.dh = s.d;
+            a.H = (int)s.H; a.w_hs = w_head_bytes(s, C::F32); a.dh = s.d; a.VH = d.VH;
             static_assert(C::F <= DEC_MAXF && C::F % DEC_RG == 0, "decode tiling");
             constexpr int NR = C::F / DEC_RG;   // state rows per thread
+            // head dimension 128: the second value half first, without storing
+            // the masses, then the first half
+            auto launch = [&](auto xw, auto one) {
+                constexpr int XW = decltype(xw)::value;
+                for (int h = d.VH - 1; h >= 0; --h) {
+                    a.half = h;
+                    a.store_mass = h == 0;
+                    profile_mark("decode", st);
+                    if constexpr (decltype(one)::value) {
+                        hipLaunchKernelGGL((k_decode_one<C::F32, NR, XW>), dim3((unsigned)d.BH), dim3(DEC_NT), 0, st,
+                                           a);
+                    } else {
+                        hipLaunchKernelGGL((k_decode_multi<C::F32, NR, XW>), dim3((unsigned)d.BH), dim3(DEC_NT), 0,
+                                           st, a);
+                    }
+                    RACE_TRY(launch_ok());
+                }
+                return RACE_OK;
+            };
+            using X64 = std::integral_constant<int, 64>;
+            using X128 = std::integral_constant<int, 128>;
             if (d.G == 1) {
-                profile_mark("decode", st);
-                hipLaunchKernelGGL((k_decode_multi<C::F32, NR>), dim3((unsigned)d.BH), dim3(DEC_NT), 0, st, a);
-                return launch_ok();
+                return s.d == 128 ? launch(X128{}, std::false_type{}) : launch(X64{}, std::false_type{});
             }
-            // one launch per token: every table group of each head in turn
+            // one launch per token (and value half): every table group of each head in turn
             for (int tok = 0; tok < a.T; ++tok) {
                 a.tok = tok;
-                profile_mark("decode", st);
-                hipLaunchKernelGGL((k_decode_one<C::F32, NR>), dim3((unsigned)d.BH), dim3(DEC_NT), 0, st, a);
-                RACE_TRY(launch_ok());
+                RACE_TRY(s.d == 128 ? launch(X128{}, std::true_type{}) : launch(X64{}, std::true_type{}));
             }
             return RACE_OK;
         });

@@ -431,10 +431,43 @@ race_status_t run_backward_h2(const Shape& s, const Derived& d, const WsLayout& 
     return run_backproject<F32>(s, d, c.K, kbase, cl, dhK, wtp(0), c.dK, c.beta, st);
 }
 
+// Prefill: the keys' plane values, then per value half the chunk sums of the
+// keys' sketch (float32 form) and their total into that half's value sums of
+// each group's part of the running state (the masses with the first half).
+template <bool F32>
+race_status_t run_prefill_h2(const Shape& s, const Derived& d, const WsLayout& wl, const Call& c) {
+    char* ws = reinterpret_cast<char*>(c.ws);
+    hipStream_t st = c.stream;
+    float* Sb = reinterpret_cast<float*>(ws + wl.S);
+    const CacheLayout cl = cache_layout(s, d);
+    char* kbase = ws + wl.Kc;
+    const float beta = c.hard ? HARD_BETA : c.beta;
+    RACE_TRY(run_planes<F32>(s, d, c.K, c.W, kbase, cl, st));
+    for (int h = 0; h < 2; ++h) {
+        for (int g = 0; g < d.G; ++g) {
+            const Group gr = group(d, g);
+            float* Sg = Sb + group_states_floats(d, d.NC, g);
+            RACE_TRY((with_cfg<F32>(s.P, gr.MT, [&](auto tag) {
+                using C = typename decltype(tag)::type;
+                return run_totals<C, false, true>(s, d, gr, nullptr, half_cols<F32>(c.V, h), nullptr, nullptr,
+                                                  plane_cache(kbase, cl, g), nullptr, beta, Sg, st, D128, 64, 0, 1);
+            })));
+            profile_mark("state_total", st);
+            float* vals = c.state + (size_t)g * d.F * d.RW + (size_t)h * gr.F * DH;
+            hipLaunchKernelGGL(k_state_total<SCAN_TOTAL>, dim3((unsigned)((gr.F65 + 255) / 256), (unsigned)d.BH),
+                               dim3(256), 0, st, Sg, vals, (int)d.NC, gr.F, d.RSall,
+                               h == 0 ? (int64_t)2 * gr.F * DH : (int64_t)-1);
+            RACE_TRY(launch_ok());
+        }
+    }
+    return RACE_OK;
+}
+
 template <bool F32>
 race_status_t dispatch_h2(const Shape& s, const Derived& d, const WsLayout& wl, const Call& c) {
     if (c.op == OP_FWD) return run_forward_h2<F32>(s, d, wl, c, c.O, c.saved_out);
     if (c.op == OP_BWD) return run_backward_h2<F32>(s, d, wl, c);
+    if (c.op == OP_PREFILL) return run_prefill_h2<F32>(s, d, wl, c);
     return RACE_ERR_UNSUPPORTED;
 }
 

@@ -34,8 +34,9 @@ struct Derived {
     int Ll, MTl, Fl, NPLl;   // the last group (equal to the full one when L % Lg == 0)
     int64_t F65l;
     int64_t F65all;          // all groups of one head (a chunk state's floats)
-    int64_t RSall;           // the running state of one head, in floats: per group F x 64
-                             // float32 value sums and F float64 masses (66 F floats)
+    int64_t RSall;           // the running state of one head, in floats: per group VH halves of
+                             // F x 64 float32 value sums and F float64 masses (RW F floats)
+    int RW;                  // 64 VH + 2
     int64_t BH, NC;
     // Head dimension 128: the sketch passes run once per half of the value
     // columns (64 each), on plane values computed beforehand from the whole
@@ -145,8 +146,9 @@ inline race_status_t derive(const Shape& s, Derived& d) {
     d.F65 = (int64_t)d.F * 65;
     d.F65l = (int64_t)d.Fl * 65;
     d.F65all = (int64_t)(d.G - 1) * d.F65 + d.F65l;
-    d.RSall = (int64_t)(d.G - 1) * d.F * 66 + (int64_t)d.Fl * 66;
     d.VH = s.d == 128 ? 2 : 1;
+    d.RW = 64 * d.VH + 2;
+    d.RSall = ((int64_t)(d.G - 1) * d.F + d.Fl) * d.RW;
     d.NDT = s.d == 128 ? 8 : 4;
     if (d.BH > 65535 || d.NC > 0x7fffffff) return RACE_ERR_UNSUPPORTED;
     return RACE_OK;

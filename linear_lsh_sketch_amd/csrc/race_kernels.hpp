@@ -969,25 +969,26 @@ __global__ __launch_bounds__(256) void k_scan(float* __restrict__ st, float* __r
     }
 }
 
-// Total of the chunk states of one head and table group into its part of a
-// running decode state: the F x 64 value sums in float32 (the chunk states'
-// type; the chunk states of a prefill are in the float32 form) and the F
-// masses summed and stored in float64, so that counts beyond 2^24 keys stay
-// exact.
+// Total of the chunk states of one head and table group (float32 form) into
+// its part of a running decode state: the F x 64 value sums in float32 at
+// vals + bh * head_floats, and the F masses summed and stored in float64 at
+// mass_off floats after that (mass_off < 0: not stored; the second value
+// half at head dimension 128), so that counts beyond 2^24 keys stay exact.
 template <int KIND = SCAN_TOTAL>
-__global__ __launch_bounds__(256) void k_state_total(const float* __restrict__ st, float* __restrict__ state,
-                                                     int nchunks, int F, int64_t head_floats) {
+__global__ __launch_bounds__(256) void k_state_total(const float* __restrict__ st, float* __restrict__ vals,
+                                                     int nchunks, int F, int64_t head_floats, int64_t mass_off) {
     const int e = blockIdx.x * blockDim.x + threadIdx.x;
     const int bh = blockIdx.y;
     if (e >= F * 65) return;
     const float* p = st + (size_t)bh * nchunks * (size_t)(F * 65) + e;
-    float* out = state + (size_t)bh * (size_t)head_floats;
+    float* out = vals + (size_t)bh * (size_t)head_floats;
     if (e < F * DH) {
-        out[e] = scan_range<SCAN_TOTAL, false, false>(const_cast<float*>(p), nchunks, F * 65, 0, nchunks, Run2{0.f, 0.f}).a;
-    } else {
+        out[e] = scan_range<SCAN_TOTAL, false, false>(const_cast<float*>(p), nchunks, F * 65, 0, nchunks,
+                                                       Run2{0.f, 0.f}).a;
+    } else if (mass_off >= 0) {
         double z = 0.0;
         for (int c = 0; c < nchunks; ++c) z += (double)p[(size_t)c * (F * 65)];
-        reinterpret_cast<double*>(out + (size_t)F * DH)[e - F * DH] = z;
+        reinterpret_cast<double*>(out + mass_off)[e - F * DH] = z;
     }
 }
 

@@ -214,8 +214,9 @@ def test_state_bytes():
     for (B, H, P, L, F) in [(1, 4, 4, 16, 256), (2, 3, 3, 5, 64), (1, 1, 2, 8, 32), (1, 1, 4, 32, 512)]:
         assert race.state_bytes(B, H, P, L) == B * H * F * 66 * 4
     out = ctypes.c_size_t(0)
-    # the running state has no head-dimension-128 form (the forward and backward do)
-    assert race.lib().race_attn_state_bytes(1, 1, 128, 4, 8, ctypes.byref(out)) == race.RACE_ERR_UNSUPPORTED
+    # head dimension 128: two halves of value sums per feature (F = 128 at L8 P4)
+    assert race.lib().race_attn_state_bytes(1, 1, 128, 4, 8, ctypes.byref(out)) == race.RACE_OK
+    assert out.value == 128 * 130 * 4 and race.state_bytes(2, 3, 4, 8, 128) == 6 * 128 * 130 * 4
     assert race.lib().race_attn_state_bytes(1, 1, 96, 4, 8, ctypes.byref(out)) == race.RACE_ERR_UNSUPPORTED
     assert race.lib().race_attn_state_bytes(1, 1, 64, 7, 8, ctypes.byref(out)) == race.RACE_ERR_UNSUPPORTED
     assert race.lib().race_attn_state_bytes(0, 1, 64, 4, 8, ctypes.byref(out)) == race.RACE_ERR_INVALID_ARG

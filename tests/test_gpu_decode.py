@@ -317,3 +317,50 @@ def test_decode_head_dim_32(lib, dtype, P, L):
     check(gpu_steps(lib, x, n0, T, P, L, 1.0, 64), ref, dtype, "d32 steps")
     res, _ = gpu_multi(lib, x, n0, T, P, L, 1.0, 64)
     check(res, ref, dtype, "d32 multi")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("P,L", [(4, 16), (4, 40), (2, 8), (5, 9)])
+def test_decode_head_dim_128(lib, dtype, P, L):
+    """Prefill, one-token steps and a seven-token call with 128-element rows:
+    the planes project all 128 columns, each value half of the state is
+    updated by its own launch and the masses are counted once; (4, 40) and
+    (5, 9) run as table groups."""
+    B, H, n0, T = 1, 2, 120, 7
+    x = host_inputs(12800 + L, B, H, n0 + T, 128, P, L, dtype)
+    print(f"[case] decode d=128 {dtype} P={P} L={L}", flush=True)
+    ref = oracle_steps(x, n0, T, 1.0)
+    check(gpu_steps(lib, x, n0, T, P, L, 1.0, 64), ref, dtype, "d128 steps")
+    res, _ = gpu_multi(lib, x, n0, T, P, L, 1.0, 64)
+    check(res, ref, dtype, "d128 multi")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_head_dim_128_hard_masses(lib, dtype):
+    """Hard buckets at head dimension 128: every step changes each mass by
+    exactly 0 or +-1 once (the two value halves count a key once), and the
+    outputs match the oracle's decode step."""
+    import torch
+    P, L, n0, T = 4, 16, 200, 5
+    for seed in range(12900, 12940):
+        x = host_inputs(seed, 1, 2, n0 + T, 128, P, L, dtype)
+        if min_abs_projection(x, n0 + T) > 1e-5:
+            break
+    else:
+        pytest.fail("no seed with every projection away from zero")
+    print(f"[case] decode d=128 hard {dtype} seed={seed}", flush=True)
+    ref = oracle_steps(x, n0, T, math.inf)
+    res, state = gpu_multi(lib, x, n0, T, P, L, math.inf, 64)
+    check(res, ref, dtype, "d128 hard")
+    dev = torch.device("cuda:0")
+    t = {k: to_torch(v, dev) for k, v in x.items()}
+    before = lib.prefill(t["K"][:, :, :n0].contiguous(), t["V"][:, :, :n0].contiguous(), t["W"], P, L, math.inf, 64)
+    F = 256
+    per_head = F * 130
+    assert before.numel() == 2 * per_head
+    m0 = before.view(2, per_head)[:, F * 128:].contiguous().view(torch.float64).cpu().numpy()
+    m1 = state.view(2, per_head)[:, F * 128:].contiguous().view(torch.float64).cpu().numpy()
+    delta = m1 - m0
+    # T keys: every mass moves by an integer in [-T, T], the empty subsets by exactly T
+    assert np.all(delta == np.round(delta)) and np.all(np.abs(delta) <= T)
+    assert np.max(delta) == T
