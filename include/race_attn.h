@@ -50,17 +50,23 @@
  *     default stream). Argument errors are reported synchronously, before any
  *     device work is enqueued. Device faults surface at the caller's next
  *     synchronisation.
- *   - Supported: d = 64 or 32; 1 <= P <= 6 (P = 6 with RACE_BF16 inputs only); L >= 1
+ *   - Supported: d = 32, 64 or 128; 1 <= P <= 6 (P = 6 with RACE_BF16 inputs only); L >= 1
  *     with L * 2^P <= 65536; N >= 1; B, H >= 1 with B * H <= 65535;
  *     1 <= chunk <= 2^20; dtype RACE_F32 or RACE_BF16. Other shapes return
  *     RACE_ERR_UNSUPPORTED. Many tables run as consecutive groups of at most
  *     256 features (P = 4, causal: 16 tables; P = 5: 8; P = 6: 4; otherwise
  *     128 projection rows), one launch per group and pass, whose partial
- *     outputs add up in float32 before the last group finishes them.
+ *     outputs add up in float32 before the last group finishes them. At
+ *     d = 128 the plane values come from the whole rows and every sketch pass
+ *     runs once per half of 64 value columns.
  *   - Numerics: bf16 inputs are multiplied on bf16 matrix cores with float32
  *     accumulation; float32 inputs use float32 matrix cores throughout.
- *     Sketch states and all reductions are float32. No atomics are used on
- *     the attention path, so results are bitwise reproducible run to run.
+ *     Running sums and all reductions are float32. Between passes the chunk
+ *     sketch states are float32 for RACE_F32 inputs; for RACE_BF16 inputs
+ *     their value sums are stored in bf16 (the precision of the matrix-core
+ *     operands they feed), their masses and the empty subset's value sums in
+ *     float32. No atomics are used on the attention path, so results are
+ *     bitwise reproducible run to run.
  *   - `chunk` is the number of tokens a workgroup owns; per-chunk sketch
  *     states are published and prefix-scanned at that granularity. Results do
  *     not depend on it beyond float32 rounding.
@@ -106,8 +112,9 @@ race_status_t race_attn_workspace_bytes(int64_t B, int64_t H, int64_t N, int d, 
                                         int causal, int chunk, int for_backward, size_t *bytes);
 
 /* Bytes of the optional `saved` buffer a forward call fills for the backward,
- * per (batch, head): the float32 sketch state at the start of every chunk
- * (causal) or the whole-sequence sketch (non-causal); the float32 per-token
+ * per (batch, head): the sketch state at the start of every chunk (causal)
+ * or the whole-sequence sketch (non-causal), sized as float32 (bf16 value
+ * sums for RACE_BF16, see Numerics above); the float32 per-token
  * softmax denominators D_i = sum_l sum_r a_l(q_i)[r] z_l[r] (the quantity
  * the output divides by); and, for queries and for keys, each token's
  * per-plane u = tanh of the normalised projection (float16 for RACE_BF16,
@@ -186,8 +193,9 @@ race_status_t race_attn_hash(const void *X, const void *W, int64_t B, int64_t H,
  * The running state of one (batch, head) is the key sketch of every token so
  * far: per feature, the sum of the keys' feature value times v (float32) and
  * the sum of the feature values, the mass (float64, so that counts of more
- * than 2^24 keys stay exact): L * 2^P * (64 * 4 + 8) bytes (padded to whole
- * projection tiles) whatever the length. Its layout is private to the
+ * than 2^24 keys stay exact): L * 2^P * (64 * 4 + 8) bytes (d = 32 or 64;
+ * d = 128: L * 2^P * (128 * 4 + 8); padded to whole projection tiles)
+ * whatever the length. Its layout is private to the
  * library; all-zero bytes are the state of an empty sequence. `temperature` = +INFINITY selects the hard
  * buckets (the discrete hash that the temperature softens: Japanese
  * gist.science page, section 2.2): each table then adds [v | 1] to exactly
