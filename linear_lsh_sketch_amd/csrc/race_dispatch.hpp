@@ -166,11 +166,22 @@ race_status_t run_pass(const Shape& s, const Derived& d, PassArgs a, hipStream_t
     constexpr bool CAUSAL_OK = !(C::P == 4 && C::MT == 8);
     if constexpr (KIND == PASS_FWD) {
         profile_mark("pass_fwd", st);
-        if constexpr (CAUSAL_OK) {
-            if (s.causal) hipLaunchKernelGGL((k_fwd<CB, true, H2>), grid, block, 0, st, a);
-            else hipLaunchKernelGGL((k_fwd<CB, false, H2>), grid, block, 0, st, a);
+        // bf16 hard buckets run their own instantiation (the exact
+        // denominator); float32 needs none
+        auto fwd = [&](auto hard) {
+            constexpr bool HD = decltype(hard)::value;
+            if constexpr (CAUSAL_OK) {
+                if (s.causal) hipLaunchKernelGGL((k_fwd<CB, true, H2, HD>), grid, block, 0, st, a);
+                else hipLaunchKernelGGL((k_fwd<CB, false, H2, HD>), grid, block, 0, st, a);
+            } else {
+                hipLaunchKernelGGL((k_fwd<CB, false, H2, HD>), grid, block, 0, st, a);
+            }
+        };
+        if constexpr (!C::F32) {
+            if (a.hard) fwd(std::true_type{});
+            else fwd(std::false_type{});
         } else {
-            hipLaunchKernelGGL((k_fwd<CB, false, H2>), grid, block, 0, st, a);
+            fwd(std::false_type{});
         }
     } else if constexpr (KIND == PASS_BWD_Q) {
         profile_mark("pass_bwd_q", st);

@@ -1421,8 +1421,10 @@ struct FwdLds {
 };
 
 // PG (head dimension 128): the queries' plane values come from ca (computed
-// beforehand from the whole rows) instead of a projection of Q.
-template <class C, bool CAUSAL, bool PG = false>
+// beforehand from the whole rows) instead of a projection of Q. HARD (bf16
+// inputs, hard buckets): the exact denominator read-out below; a separate
+// instantiation, so that the soft kernels keep their registers.
+template <class C, bool CAUSAL, bool PG = false, bool HARD = false>
 __global__ __launch_bounds__(NT, (FwdLds<C>::OCC))
 __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(PassArgs a) {
     using elem = typename Prec<C::F32>::elem;
@@ -1595,7 +1597,7 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
                     // 2^24) and the features 0 or +-1, so the mass operand goes in
                     // as three bf16 parts of 8 significant bits each, and the
                     // denominator comes out exact
-                    if (a.hard) {
+                    if constexpr (HARD) {
                         frag zp = zf;
 #pragma unroll
                         for (int part = 0; part < 2; ++part) {
