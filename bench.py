@@ -364,10 +364,15 @@ def main():
 
     layer, kernels = per_token_head_counts(w)
     units = w.token_heads
-    # dominant kernel: largest total time in the timed region
+    # dominant kernel: largest total time in the timed region. A pass runs as
+    # one launch per table group, each over every token and its group's
+    # features, so one launch's share of the algorithmic count is 1 / launches
+    # per step.
     dom = max(stage_ms, key=lambda k: stage_ms[k])
     avg_ms = stage_ms[dom] / stage_n[dom]
+    per_step = stage_n[dom] / args.steps
     kb, kf = kernels.get(dom, (0, 0))
+    kb, kf = kb / per_step, kf / per_step
     peak_f = MFMA_PEAK[w.dtype]
     t_hbm, t_mma = kb * units / HBM_PEAK, kf * units / peak_f
     if t_hbm >= t_mma:
@@ -381,6 +386,7 @@ def main():
     roof["traffic"] = measured_traffic(w.name, dom)
     roof["kernel"] = dom
     roof["kernel_avg_ms"] = avg_ms
+    roof["launches_per_step"] = per_step
     layer_t = max(layer["bytes"] * units / HBM_PEAK, layer["flops"] * units / peak_f)
     hbm_high_water = torch.cuda.max_memory_allocated() / 2**30
     # the box's own copy bandwidth, beside the nominal peak (outside the timed region)
