@@ -409,15 +409,17 @@ def test_per_head_hyperplanes(lib, dtype, causal, P, L):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_per_head_hyperplanes_decode(lib, dtype):
+@pytest.mark.parametrize("d", [64, 128])
+def test_per_head_hyperplanes_decode(lib, dtype, d):
     """Prefill + decode steps with per-head hyperplanes (P4 L20: two table
     groups) against the oracle's sketch and decode step per head."""
     import synth
     import torch
     from oracle import dense
     B, H, n0, Tn, P, L = 1, 3, 50, 3, 4, 20
-    x = host_inputs(909, B, H, n0 + Tn, 64, P, L, dtype)
-    Wh = synth.normal(909, synth.TID_W, (H, L, P, 64), dtype)
+    print(f"[case] per-head decode {dtype} d={d}", flush=True)
+    x = host_inputs(909, B, H, n0 + Tn, d, P, L, dtype)
+    Wh = synth.normal(909, synth.TID_W, (H, L, P, d), dtype)
     dev = torch.device("cuda:0")
     t = {k: to_torch(v, dev) for k, v in x.items()}
     Wd = to_torch(Wh, dev)
