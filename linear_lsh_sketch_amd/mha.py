@@ -18,21 +18,22 @@ import torch
 from . import (WS_BWD, WS_FWD_SAVED, alloc_saved, alloc_state, alloc_workspace, race_attn_bwd, race_attn_decode,
                race_attn_fwd, race_attn_prefill)
 
-HEAD_DIM = 64
+HEAD_DIM = 64          # default head dimension (32, 64 and 128 are supported)
 
 
 class RaceAttnFunction(torch.autograd.Function):
     """O = RACE-attention(Q, K, V) with the exact gradient of the kernels'
-    forward. Q, K, V: [B, H, N, 64] contiguous, one dtype (bf16 or float32);
-    W: [L, P, 64]. The forward keeps the sketch states, denominators and plane
-    values (`saved`) for the backward, which takes them with O."""
+    forward. Q, K, V: [B, H, N, d] contiguous (d = 32, 64 or 128), one dtype
+    (bf16 or float32); W: [L, P, d]. The forward keeps the sketch states,
+    denominators and plane values (`saved`) for the backward, which takes
+    them with O."""
 
     @staticmethod
     def forward(ctx, Q, K, V, W, P, L, temperature, causal, chunk):
         Q, K, V = Q.contiguous(), K.contiguous(), V.contiguous()
-        B, H, N, _ = Q.shape
-        saved = alloc_saved(B, H, N, P, L, causal, chunk, Q.device)
-        ws = alloc_workspace(B, H, N, P, L, causal, chunk, WS_FWD_SAVED, Q.device)
+        B, H, N, d = Q.shape
+        saved = alloc_saved(B, H, N, P, L, causal, chunk, Q.device, d)
+        ws = alloc_workspace(B, H, N, P, L, causal, chunk, WS_FWD_SAVED, Q.device, d)
         O = race_attn_fwd(Q, K, V, W, P, L, temperature, causal, chunk, saved=saved, ws=ws)
         ctx.save_for_backward(Q, K, V, W, O)
         ctx.saved_buf = saved
@@ -43,8 +44,8 @@ class RaceAttnFunction(torch.autograd.Function):
     def backward(ctx, dO):
         Q, K, V, W, O = ctx.saved_tensors
         P, L, temperature, causal, chunk = ctx.cfg
-        B, H, N, _ = Q.shape
-        ws = alloc_workspace(B, H, N, P, L, causal, chunk, WS_BWD, Q.device)
+        B, H, N, d = Q.shape
+        ws = alloc_workspace(B, H, N, P, L, causal, chunk, WS_BWD, Q.device, d)
         dQ, dK, dV = race_attn_bwd(Q, K, V, W, dO.contiguous(), P, L, temperature, causal, chunk, O=O,
                                    saved=ctx.saved_buf, ws=ws)
         ctx.saved_buf = None
@@ -52,20 +53,24 @@ class RaceAttnFunction(torch.autograd.Function):
 
 
 def race_attention(Q, K, V, W, P, L, temperature=1.0, causal=True, chunk=1024):
-    """Differentiable RACE attention of [B, H, N, 64] tensors."""
+    """Differentiable RACE attention of [B, H, N, d] tensors."""
     return RaceAttnFunction.apply(Q, K, V, W, P, L, temperature, causal, chunk)
 
 
 class RaceMHA(torch.nn.Module):
     """Multi-head attention with the RACE core: x [B, N, d_model] ->
-    [B, N, d_model], d_model = heads * 64, bias-free projections."""
+    [B, N, d_model], d_model = heads * head_dim (head_dim 32, 64 or 128),
+    bias-free projections."""
 
     def __init__(self, d_model: int, P: int = 4, L: int = 16, temperature: float = 1.0, causal: bool = True,
-                 chunk: int = 1024, seed: int = 0, device=None, dtype=None):
+                 chunk: int = 1024, seed: int = 0, device=None, dtype=None, head_dim: int = HEAD_DIM):
         super().__init__()
-        if d_model % HEAD_DIM:
-            raise ValueError(f"d_model must be a multiple of {HEAD_DIM}")
-        self.heads = d_model // HEAD_DIM
+        if head_dim not in (32, 64, 128):
+            raise ValueError("head_dim must be 32, 64 or 128")
+        if d_model % head_dim:
+            raise ValueError(f"d_model must be a multiple of {head_dim}")
+        self.head_dim = head_dim
+        self.heads = d_model // head_dim
         self.P, self.L, self.temperature, self.causal, self.chunk = P, L, temperature, causal, chunk
         kw = {"device": device, "dtype": dtype}
         self.wq = torch.nn.Linear(d_model, d_model, bias=False, **kw)
@@ -73,12 +78,12 @@ class RaceMHA(torch.nn.Module):
         self.wv = torch.nn.Linear(d_model, d_model, bias=False, **kw)
         self.wo = torch.nn.Linear(d_model, d_model, bias=False, **kw)
         gen = torch.Generator().manual_seed(seed)
-        planes = torch.randn((L, P, HEAD_DIM), generator=gen, dtype=torch.float32)
+        planes = torch.randn((L, P, head_dim), generator=gen, dtype=torch.float32)
         self.register_buffer("planes", planes.to(device=device, dtype=dtype or torch.float32))
 
     def split(self, t):
         B, N, _ = t.shape
-        return t.view(B, N, self.heads, HEAD_DIM).transpose(1, 2).contiguous()
+        return t.view(B, N, self.heads, self.head_dim).transpose(1, 2).contiguous()
 
     def forward(self, x):
         B, N, D = x.shape
@@ -105,7 +110,7 @@ class RaceMHA(torch.nn.Module):
     @torch.no_grad()
     def empty_state(self, batch: int):
         """The running state of sequences with no tokens yet."""
-        return alloc_state(batch, self.heads, self.P, self.L, self.planes.device)
+        return alloc_state(batch, self.heads, self.P, self.L, self.planes.device, self.head_dim)
 
     @torch.no_grad()
     def step(self, x, state):

@@ -50,18 +50,19 @@ def oracle_core():
     return OracleCore
 
 
-@pytest.mark.parametrize("causal", [True, False])
-def test_mha_block_gradients_match_float64_reference(mha, causal):
+@pytest.mark.parametrize("causal,hd", [(True, 64), (False, 64), (True, 128), (False, 32)])
+def test_mha_block_gradients_match_float64_reference(mha, causal, hd):
     """Float32 block on the GPU (projections in the BLAS library, core in the
     library's kernels) against the same block in float64 on the CPU with the
     oracle as its core: output, input gradient and the four projection
-    weights' gradients."""
+    weights' gradients; head dimensions 64, 128 and 32."""
     import torch
-    B, N, D, P, L, chunk, beta = 2, 150, 128, 4, 8, 64, 1.3
-    print(f"[case] mha grads causal={causal} B={B} N={N} D={D} P={P} L={L} chunk={chunk}", flush=True)
+    B, N, D, P, L, chunk, beta = 2, 150, 2 * hd, 4, 8, 64, 1.3
+    print(f"[case] mha grads causal={causal} B={B} N={N} D={D} head_dim={hd} P={P} L={L} chunk={chunk}",
+          flush=True)
     torch.manual_seed(3)
     dev = torch.device("cuda:0")
-    blk = mha.RaceMHA(D, P, L, beta, causal, chunk, seed=5, device=dev, dtype=torch.float32)
+    blk = mha.RaceMHA(D, P, L, beta, causal, chunk, seed=5, device=dev, dtype=torch.float32, head_dim=hd)
     x = torch.randn(B, N, D)
     g = torch.randn(B, N, D)
     xg = x.to(dev).requires_grad_(True)
@@ -76,7 +77,7 @@ def test_mha_block_gradients_match_float64_reference(mha, causal):
     xr = x.double().requires_grad_(True)
 
     def split(t):
-        return t.view(B, N, blk.heads, 64).transpose(1, 2).contiguous()
+        return t.view(B, N, blk.heads, hd).transpose(1, 2).contiguous()
 
     q, k, v = (split(xr @ ws[n].T) for n in ("wq", "wk", "wv"))
     o = Core.apply(q, k, v, planes, beta, causal)
@@ -131,8 +132,8 @@ def test_mha_language_model_loss_falls(mha, dtype):
     assert last < 0.3 * math.log(8), (first, last)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_mha_incremental_decoding_matches_full_forward(mha, dtype):
+@pytest.mark.parametrize("dtype,hd", [("f32", 64), ("bf16", 64), ("f32", 128), ("bf16", 128)])
+def test_mha_incremental_decoding_matches_full_forward(mha, dtype, hd):
     """Generation with the block: a prompt through ``prefill``, then pieces of
     1, 3 and 1 tokens through ``step``, give the rows of the full causal
     forward of the whole sequence (the sketch stands in for the key-value
@@ -140,9 +141,9 @@ def test_mha_incremental_decoding_matches_full_forward(mha, dtype):
     import torch
     dt = torch.float32 if dtype == "f32" else torch.bfloat16
     dev = torch.device("cuda:0")
-    B, n0, D = 2, 300, 128
+    B, n0, D = 2, 300, 2 * hd
     torch.manual_seed(11)
-    blk = mha.RaceMHA(D, 4, 16, 1.0, True, 64, seed=2, device=dev, dtype=dt)
+    blk = mha.RaceMHA(D, 4, 16, 1.0, True, 64, seed=2, device=dev, dtype=dt, head_dim=hd)
     x = torch.randn(B, n0 + 5, D, device=dev).to(dt)
     with torch.no_grad():
         full = blk(x).float()
@@ -155,6 +156,6 @@ def test_mha_incremental_decoding_matches_full_forward(mha, dtype):
     got = torch.cat(pieces, dim=1)
     torch.cuda.synchronize()
     err = float((got - full).norm() / full.norm())
-    print(f"[case] mha incremental {dtype}: rel_l2 {err:.1e}", flush=True)
+    print(f"[case] mha incremental {dtype} head_dim={hd}: rel_l2 {err:.1e}", flush=True)
     assert err <= (1e-5 if dtype == "f32" else 1e-2), err
     assert torch.equal(blk.empty_state(B), torch.zeros_like(state))
