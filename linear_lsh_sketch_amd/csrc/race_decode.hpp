@@ -21,7 +21,7 @@
 // Work per head: one read of the state into registers, then per token one
 // projection of q and of k on the L * P planes, the features, the update of
 // the rows in registers and the read-out from them, and one write of the
-// state at the end: 2 * F * (64 * 4 + 8) bytes per call (the bound for T = 1).
+// state at the end: 2 * F * (64 VH * 4 + 8) bytes per call (the bound for T = 1).
 // No matrix cores: a head's update is an outer product of one feature row
 // and one value row, and the read-out a vector-matrix product over F rows.
 #pragma once

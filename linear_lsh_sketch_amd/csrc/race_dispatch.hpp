@@ -237,7 +237,8 @@ race_status_t run_pass_groups(const Shape& s, const Derived& d, const WsLayout& 
     return RACE_OK;
 }
 
-// Hyperplanes of table group g (W is [L, P, 64], groups are consecutive tables).
+// Hyperplanes of table group g (W is [L, P, d], or [H, L, P, d] with the
+// heads w_head_bytes apart; groups are consecutive tables).
 inline const void* group_w(const void* W, const Shape& s, const Group& gr, bool f32) {
     return reinterpret_cast<const char*>(W) + (size_t)gr.t0 * s.P * s.d * (f32 ? 4 : 2);
 }

@@ -78,7 +78,8 @@ struct CacheLayout {
     size_t u_of(int g) const { return u + (size_t)g * ustep; }
 };
 
-// The saved buffer: float32 sketch states (per chunk, causal; the total,
+// The saved buffer: sketch states in slots of F * 65 floats (float32, or the
+// compact form for bf16 inputs; per chunk, causal; the total,
 // non-causal), the float32 per-token denominators D, then the plane values of
 // the queries and of the keys.
 struct SavedLayout {

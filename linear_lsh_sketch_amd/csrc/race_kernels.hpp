@@ -704,7 +704,7 @@ __device__ inline void emit_tile(int tb, int w, int ln, int g, const float phi[C
 template <class C, bool KEEP, class WS>
 __device__ inline void block_features(const WS& wsrc, int fb, int lane, int w, int ln, int g,
                                       const typename Prec<C::F32>::frag xf[2], float inv, float beta,
-                                      int L, typename Prec<C::F32>::elem* rows /* [64][ROWF] */,
+                                      typename Prec<C::F32>::elem* rows /* [64][ROWF] */,
                                       typename Prec<C::F32>::frag (&phi_frag)[C::FBK], const PlaneRows& out,
                                       int rowi) {
 #pragma unroll
@@ -726,13 +726,12 @@ __device__ inline void block_features(const WS& wsrc, int fb, int lane, int w, i
 // The same from stored plane values (no projection); when KEEP, also return
 // per tile the plane values t and dt/dh for the chain rule.
 template <class C, bool KEEP>
-__device__ inline void block_features_cached(const Planes<C>& pl, int fb, int w, int ln, int g, int L,
-                                             float beta, typename Prec<C::F32>::elem* rows,
+__device__ inline void block_features_cached(const Planes<C>& pl, int w, int ln, int g, float beta,
+                                             typename Prec<C::F32>::elem* rows,
                                              typename Prec<C::F32>::frag (&phi_frag)[C::FBK],
                                              float (&t_keep)[C::TPB][4], float (&gt_keep)[C::TPB][4]) {
 #pragma unroll
     for (int tb = 0; tb < C::TPB; ++tb) {
-        const int t = fb * C::TPB + tb;
         float tt[4], gt[4], phi[C::KB * 8];
         tplanes<C::F32>(pl.u[tb], beta, tt, gt);
         monomial_features<C>(tt, phi, g);
@@ -755,7 +754,7 @@ struct TotArgs {
     const void* Z;       // V, or dO for the gradient sketch
     const float* Dv;     // gradient sketch: per-token D
     const float* Ev;     // gradient sketch: per-token e
-    const void* W;       // [L, P, 64]
+    const void* W;       // [L, P, d] (this group's tables; per head: W of head h at + h * w_hs bytes)
     PlaneCache pc;       // keys: where their plane values go; gradient sketch: the queries' plane values
     float* out;          // [BH][NC][F*65]
     int64_t N;
@@ -848,7 +847,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 3))) void
     issue(0);
     if (FC) issue_planes(0, 0);
     for (int it = 0; it < nsub; ++it) {
-        const int64_t t0 = seg0 + (int64_t)it * TB;
         const int nv = nv_of(it);
         const int rowi = it * TB + my;
         frag xf[2] = {nx[0], nx[1]}, zr[2] = {nz[0], nz[1]};
@@ -870,9 +868,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 3))) void
                 if (fb + 1 < C::NBLK) issue_planes(it, fb + 1);
                 else if (it + 1 < nsub) issue_planes(it + 1, 0);
                 float us[C::TPB][4], ug[C::TPB][4];
-                block_features_cached<C, false>(pl, fb, w, ln, g, a.L, a.beta, s_rows, unused, us, ug);
+                block_features_cached<C, false>(pl, w, ln, g, a.beta, s_rows, unused, us, ug);
             } else {
-                block_features<C, false>(wsrc, fb, lane, w, ln, g, xf, inv, a.beta, a.L, s_rows, unused,
+                block_features<C, false>(wsrc, fb, lane, w, ln, g, xf, inv, a.beta, s_rows, unused,
                                          pr, rowi);
             }
             __syncthreads();
@@ -1051,7 +1049,7 @@ struct PassArgs {
     const void* Zsrc;      // FWD, BWD_Q: V; BWD_K: dO
     const void* Ysrc;      // BWD_Q: dO; BWD_K: V
     const void* Osrc;      // BWD_Q: the forward output O
-    const void* W;         // [L, P, 64]
+    const void* W;         // [L, P, d] (this group's tables; per head: W of head h at + h * w_hs bytes)
     const void* WTp;       // back-projection operands (k_prep)
     const float* state;    // sketch before the chunk (causal) or the total
     int64_t state_bh_stride;
@@ -1249,7 +1247,7 @@ __device__ inline void chain_backproject(int t, int g, const float dA[C::KB * 8]
 template <class C, bool REV, bool YLO, bool ZLO>
 __device__ inline void intra_operand(const typename Prec<C::F32>::elem* s_zr, const typename Prec<C::F32>::elem* s_zlo,
                                      const typename Prec<C::F32>::elem* s_yr, const typename Prec<C::F32>::elem* s_ylo,
-                                     bool lo, int w, int ln, int g, int my, int nv,
+                                     bool lo, int ln, int g, int my, int nv,
                                      typename Prec<C::F32>::frag (&Cf)[2]) {
     using frag = typename Prec<C::F32>::frag;
     f32x4 Cc[4];
@@ -1541,14 +1539,14 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
             }
             if constexpr (PG) {
                 float us[C::TPB][4], ug[C::TPB][4];
-                block_features_cached<C, false>(ql, fb, ow, ln, g, a.L, a.beta, rows_b, unused, us, ug);
+                block_features_cached<C, false>(ql, ow, ln, g, a.beta, rows_b, unused, us, ug);
             } else {
-                block_features<C, false>(wsrc, fb, lane, ow, ln, g, xa, inv_a, a.beta, a.L, rows_b, unused, pra,
+                block_features<C, false>(wsrc, fb, lane, ow, ln, g, xa, inv_a, a.beta, rows_b, unused, pra,
                                          rowi);
             }
             if (causal) {
                 float us[C::TPB][4], ug[C::TPB][4];
-                block_features_cached<C, false>(pl, fb, ow, ln, g, a.L, a.beta, brow_b, unused, us, ug);
+                block_features_cached<C, false>(pl, ow, ln, g, a.beta, brow_b, unused, us, ug);
             }
         };
         features(0);
@@ -1838,7 +1836,7 @@ __attribute__((amdgpu_waves_per_eu(BwdQLds<C>::OCC, BwdQLds<C>::OCC))) void k_bw
         __syncthreads();
         frag Cf[2];
         if (causal)
-            intra_operand<C, false, LD::YLO, false>(s_zr, nullptr, s_yr, s_ylo, first, w, ln, g, my, nv, Cf);
+            intra_operand<C, false, LD::YLO, false>(s_zr, nullptr, s_yr, s_ylo, first, ln, g, my, nv, Cf);
         if (LD::YLO && LD::YLO_SHARED && causal && first)
             __syncthreads();   // the y lo rows are read; their space becomes the feature tiles
         f32x4 dX[4];
@@ -1862,7 +1860,7 @@ __attribute__((amdgpu_waves_per_eu(BwdQLds<C>::OCC, BwdQLds<C>::OCC))) void k_bw
             if (causal) {
                 frag unused[C::FBK];
                 float us[C::TPB][4], ug[C::TPB][4];
-                block_features_cached<C, false>(kb_, fb, w, ln, g, a.L, a.beta, cols_b, unused, us, ug);
+                block_features_cached<C, false>(kb_, w, ln, g, a.beta, cols_b, unused, us, ug);
             }
             __syncthreads();
             frag yf[3];
@@ -2077,7 +2075,7 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
         __syncthreads();
         frag Cf[2];
         if (DK && causal)
-            intra_operand<C, true, false, LD::ZLO>(s_zr, s_zlo, s_yr, nullptr, first, w, ln, g, my, nv, Cf);
+            intra_operand<C, true, false, LD::ZLO>(s_zr, s_zlo, s_yr, nullptr, first, ln, g, my, nv, Cf);
         if (LD::ZLO && LD::ZLO_SHARED && causal && first)
             __syncthreads();   // the residual rows are read; their space becomes the feature tiles
         // Padded tables: their empty subset (1) adds 1 to every feature
@@ -2118,11 +2116,11 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
             elem* cols_b = s_cols + bsel * LD::n_cols;
             elem* ms_b = s_ms + bsel * LD::n_ms;
             if constexpr (DV) {
-                block_features_cached<C, false>(ka, fb, w, ln, g, a.L, a.beta, rows_b, phiA, us, ug);
+                block_features_cached<C, false>(ka, w, ln, g, a.beta, rows_b, phiA, us, ug);
                 if (causal)
-                    block_features_cached<C, false>(qb, fb, w, ln, g, a.L, a.beta, brow_b, unused, us, ug);
+                    block_features_cached<C, false>(qb, w, ln, g, a.beta, brow_b, unused, us, ug);
             } else if (causal) {
-                block_features_cached<C, false>(qb, fb, w, ln, g, a.L, a.beta, cols_b, unused, us, ug);
+                block_features_cached<C, false>(qb, w, ln, g, a.beta, cols_b, unused, us, ug);
             }
             if constexpr (DK) write_sketch_rows<C, TR>(fb, w, ln, g, Macc, Zacc, ms_b);
             __syncthreads();
