@@ -247,7 +247,7 @@ struct Cfg {
     static constexpr int ROWD = DH + PAD;
     static_assert(NKC % FBK == 0, "feature blocks must tile the features");
     static_assert(FBK % KB == 0, "feature blocks hold whole tables");
-    static_assert(NW % FBK == 0, "a feature block's mass chunks have distinct owner waves");
+    static_assert(NW % FBK == 0 || FBK % NW == 0, "a feature block's mass chunks have distinct owner waves");
 };
 
 // table / plane of row `ri` (0..15) of projection tile t

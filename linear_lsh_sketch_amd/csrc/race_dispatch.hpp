@@ -105,7 +105,11 @@ race_status_t run_totals(const Shape& s, const Derived& d, const Group& gr, cons
     a.ezero = ezero;
     a.f32form = f32form;
     profile_mark(CACHED ? "totals_qg" : "totals_kv", st);
-    hipLaunchKernelGGL((k_totals<C, CACHED, PG>), dim3((unsigned)d.NC, (unsigned)d.BH), dim3(NT), 0, st, a);
+    // bf16 groups of eight feature chunks take them as one block (one
+    // feature-tile write and two barriers per sub-block; the value operands
+    // are read once); the LDS still fits three workgroups per CU
+    using CT = Cfg<C::P, C::MT, C::F32, (!C::F32 && C::NKC == 8) ? 8 : 0>;
+    hipLaunchKernelGGL((k_totals<CT, CACHED, PG>), dim3((unsigned)d.NC, (unsigned)d.BH), dim3(NT), 0, st, a);
     return launch_ok();
 }
 

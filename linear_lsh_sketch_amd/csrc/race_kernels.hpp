@@ -662,6 +662,26 @@ __device__ inline void sketch_update(int fb, int w, int ln, int g, const typenam
             }
         }
     }
+    if constexpr (MASS && C::FBK > NW) {
+        // blocks wider than the workgroup: wave w owns local chunks w + NW j
+        frag zm[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) zm[s] = val_operand<C, ZS>(Zrow, 64, s, ln, g);
+#pragma unroll
+        for (int j = 0; j < C::FBK / NW; ++j) {
+            const int kw = w + NW * j;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    f32x4& acc = Zacc[2 * (C::zidx(fb) + j) + h];
+                    if constexpr (TR) acc = mma(zm[s], feat_operand<C>(brow, kw, h, s, ln, g), acc);
+                    else acc = mma(feat_operand<C>(brow, kw, h, s, ln, g), zm[s], acc);
+                }
+            }
+        }
+        return;
+    }
     const int kw = w - C::own_base(fb);        // local chunk whose mass this wave owns
     if (MASS && kw >= 0 && kw < C::FBK) {
         frag zm[2];
