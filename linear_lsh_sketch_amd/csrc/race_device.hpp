@@ -234,7 +234,8 @@ struct Cfg {
     // Mass column: feature chunk c is owned by wave c % NW, in its
     // accumulators Zacc[2 (c / NW) + h]. In feature block fb the owners are
     // waves own_base(fb) .. own_base(fb) + FBK - 1 (local chunk w - own_base),
-    // all at accumulator pair zidx(fb).
+    // all at accumulator pair zidx(fb); a block of more than NW chunks gives
+    // wave w its local chunks w + NW j, at pairs zidx(fb) + j.
     static constexpr int NOWN = (NKC + NW - 1) / NW;
     static constexpr int own_base(int fb) { return (fb * FBK) % NW; }
     static constexpr int zidx(int fb) { return fb * FBK / NW; }
