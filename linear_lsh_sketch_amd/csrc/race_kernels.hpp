@@ -1926,9 +1926,9 @@ __attribute__((amdgpu_waves_per_eu(BwdQLds<C>::OCC, BwdQLds<C>::OCC))) void k_bw
 // T = sum_b phi_b^T [dO_b / D_b | e_b] of the queries after the sub-block:
 //   dV_a  = phi_a^T T_g  (+ intra: sum_{b >= a} <phi_b, phi_a> g_b)
 //   dA_K  = T [v_a | 1]  (+ intra: phi_b^T Cc, Cc[b][a] = g_b . v_a + e_b)
-// then the chain rule -> dK. PART selects dV (KPART_DV), dK (KPART_DK) or
-// both in one sweep (KPART_BOTH); the split passes each fit two workgroups
-// per CU.
+// then the chain rule -> dK. PART selects dV (KPART_DV) or dK (KPART_DK),
+// two launches: split, the dV pass fits three workgroups per CU and the dK
+// pass two.
 // ---------------------------------------------------------------------------
 enum { KPART_DV = 1, KPART_DK = 2 };
 
@@ -1959,7 +1959,7 @@ struct BwdKLds {
     // fit: the intra scores the first query-feature buffer (dV) or the feature
     // buffers (dK), the residual rows the feature buffers.
     static constexpr bool SC_SHARED = DV ? n_sc <= n_brow : n_sc <= NB * n_cols;
-    static constexpr bool ZLO_SHARED = NB == 2 && n_zlo <= 2 * n_cols;
+    static constexpr bool ZLO_SHARED = n_zlo <= NB * n_cols;
     static constexpr int o_rows = 0;                            // [NB][rows | brow]
     static constexpr int o_brow = o_rows + n_rows;
     static constexpr int RB = n_rows + n_brow;                  // stride of the row-feature buffers
@@ -2119,7 +2119,7 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
         f32x4 dhp[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int fb = 0; fb < C::NBLK; ++fb) {
-            frag phiA[C::FBK], unused[C::FBK];
+            frag unused[C::FBK];
             float us[C::TPB][4], ug[C::TPB][4];
             frag wf[C::TPB][4];
             if constexpr (DK && !H2) {
@@ -2130,13 +2130,13 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
             const Planes<C> ka = pa, qb = pb;
             if (fb + 1 < C::NBLK) issue_planes(it, fb + 1);
             else if (it + 1 < nsub) issue_planes(it + 1, 0);
-            const int bsel = LD::NB == 2 ? (fb & 1) : 0;
+            const int bsel = fb & 1;
             elem* rows_b = s_rows + bsel * LD::RB;
             elem* brow_b = s_brow + bsel * LD::RB;
             elem* cols_b = s_cols + bsel * LD::n_cols;
             elem* ms_b = s_ms + bsel * LD::n_ms;
             if constexpr (DV) {
-                block_features_cached<C, false>(ka, w, ln, g, a.beta, rows_b, phiA, us, ug);
+                block_features_cached<C, false>(ka, w, ln, g, a.beta, rows_b, unused, us, ug);
                 if (causal)
                     block_features_cached<C, false>(qb, w, ln, g, a.beta, brow_b, unused, us, ug);
             } else if (causal) {
@@ -2198,9 +2198,8 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
                 }
             }
             if (causal) sketch_update<C, DK, LD::ZS, DV, TR>(fb, w, ln, g, DV ? brow_b : cols_b, s_zr, Macc, Zacc);
-            if (LD::NB == 1) __syncthreads();   // single buffer: reads done before the next block's writes
         }
-        if (LD::NB == 2) __syncthreads();   // the block tiles are read; the sub-block tiles below reuse them
+        __syncthreads();   // the block tiles are read; the sub-block tiles below reuse them
         if constexpr (DV) {
             // intra-sub-block dV: queries b >= a
             if (causal) {
