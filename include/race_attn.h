@@ -50,7 +50,7 @@
  *     default stream). Argument errors are reported synchronously, before any
  *     device work is enqueued. Device faults surface at the caller's next
  *     synchronisation.
- *   - Supported: d = 32, 64 or 128; 1 <= P <= 6 (P = 6 with RACE_BF16 inputs only); L >= 1
+ *   - Supported: d = 32, 64 or 128; 1 <= P <= 6; L >= 1
  *     with L * 2^P <= 65536; N >= 1; B, H >= 1 with B * H <= 65535;
  *     1 <= chunk <= 2^20; dtype RACE_F32 or RACE_BF16. Other shapes return
  *     RACE_ERR_UNSUPPORTED. Many tables run as consecutive groups of at most

@@ -92,8 +92,6 @@ race_status_t guarded(race_status_t (*fn)(const Shape&, const Derived&, const Ws
 
 race_status_t go(race_dtype_t dtype_flags, const Shape& s, const Derived& dv, const WsLayout& wl, const Call& c) {
     const race_dtype_t dtype = base_dtype(dtype_flags);
-    // P = 6 runs on bf16 inputs only (a table's monomials exceed the LDS in float32)
-    if (dtype == RACE_F32 && s.P == 6) return RACE_ERR_UNSUPPORTED;
     (void)hipGetLastError();  // clear a stale error so it is not reported as ours
     t_count = 0;
     t_stream = c.stream;

@@ -76,11 +76,7 @@ race_status_t with_cfg(int P, int MT, Fn&& fn) {
     RACE_CFG(3, 1) RACE_CFG(3, 2) RACE_CFG(3, 4) RACE_CFG(3, 8)
     RACE_CFG(4, 1) RACE_CFG(4, 2) RACE_CFG(4, 4) RACE_CFG(4, 8)
     RACE_CFG(5, 1) RACE_CFG(5, 2) RACE_CFG(5, 4)
-    // P = 6 in float32: a tile's 128 features per lane group, double-buffered
-    // for 64 tokens, do not fit the 160 KB of LDS
-    if constexpr (!F32) {
-        RACE_CFG(6, 1) RACE_CFG(6, 2)
-    }
+    RACE_CFG(6, 1) RACE_CFG(6, 2)
 #undef RACE_CFG
     return RACE_ERR_UNSUPPORTED;
 }

@@ -1418,19 +1418,24 @@ __device__ inline typename Prec<C::F32>::frag pack_nonempty(int kc, int g, f32x4
 template <class C>
 struct FwdLds {
     using elem = typename Prec<C::F32>::elem;
-    // Feature tiles of a block, double-buffered: block fb uses buffer fb % 2,
-    // so one barrier per block separates its writes from its reads.
     static constexpr int n_rows = TB * C::ROWF;                 // a-side features [64][ROWF]
     static constexpr int n_brow = TB * C::ROWF;                 // b-side features [64][ROWF]
     static constexpr int ZS = ZV;                               // value-tile row stride
     static constexpr int n_zr = TB * ZS;                        // [z_b | mass], token rows
     static constexpr int n_sc = TB * C::ROWT;                   // intra scores [a][b]
-    static constexpr int o_rows = 0;                            // [2][rows]
-    static constexpr int o_brow = o_rows + 2 * n_rows;          // [2][brow]
-    static constexpr int o_zr = o_brow + 2 * n_brow;
+    static constexpr int n_float = 4 * TB + TB + TB;            // Dpart, Dint, 1 / D
+    // Feature tiles of a block, double-buffered where they fit: block fb uses
+    // buffer fb % 2, so one barrier per block separates its writes from its
+    // reads. A single buffer (float32, P = 6: 136-float rows) takes a second
+    // barrier per block before the next block's writes.
+    static constexpr int NB =
+        ((2 * n_rows + 2 * n_brow + n_zr + n_sc) * (int)sizeof(elem) + n_float * 4 <= 160 * 1024) ? 2 : 1;
+    static_assert(NB == 2 || (C::F32 && C::P == 6), "single buffers for float32 P = 6 only");
+    static constexpr int o_rows = 0;                            // [NB][rows]
+    static constexpr int o_brow = o_rows + NB * n_rows;         // [NB][brow]
+    static constexpr int o_zr = o_brow + NB * n_brow;
     static constexpr int o_sc = o_zr + n_zr;
     static constexpr int o_w = o_sc + n_sc;
-    static constexpr int n_float = 4 * TB + TB + TB;            // Dpart, Dint, 1 / D
     // two workgroups per CU (VGPR budget 256: two waves share each SIMD) where
     // the tiles fit twice in the LDS
     static constexpr int OCC =
@@ -1548,10 +1553,13 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
         // Software-pipelined feature blocks: after the barrier that publishes
         // block fb, a wave computes and writes the features of block fb + 1
         // (other buffer) while its matrix-core work on block fb proceeds.
+        // With a single buffer the features of block fb are written after
+        // the reads of block fb - 1.
+        auto buf = [](int fb) { return LD::NB == 2 ? (fb & 1) : 0; };
         auto features = [&](int fb) {
             frag unused[C::FBK];
-            elem* rows_b = s_rows + (fb & 1) * LD::n_rows;
-            elem* brow_b = s_brow + (fb & 1) * LD::n_brow;
+            elem* rows_b = s_rows + buf(fb) * LD::n_rows;
+            elem* brow_b = s_brow + buf(fb) * LD::n_brow;
             const Planes<C> pl = pn, ql = pq;
             if (causal || PG) {
                 if (fb + 1 < C::NBLK) issue_planes(it, fb + 1);
@@ -1569,13 +1577,17 @@ __attribute__((amdgpu_waves_per_eu(FwdLds<C>::OCC, FwdLds<C>::OCC))) void k_fwd(
                 block_features_cached<C, false>(pl, ow, ln, g, a.beta, brow_b, unused, us, ug);
             }
         };
-        features(0);
+        if (LD::NB == 2) features(0);
 #pragma unroll
         for (int fb = 0; fb < C::NBLK; ++fb) {
-            const elem* rows_b = s_rows + (fb & 1) * LD::n_rows;
-            const elem* brow_b = s_brow + (fb & 1) * LD::n_brow;
+            const elem* rows_b = s_rows + buf(fb) * LD::n_rows;
+            const elem* brow_b = s_brow + buf(fb) * LD::n_brow;
+            if (LD::NB == 1) {
+                if (fb > 0) __syncthreads();   // block fb - 1's tiles are read
+                features(fb);
+            }
             __syncthreads();
-            if (fb + 1 < C::NBLK) features(fb + 1);
+            if (LD::NB == 2 && fb + 1 < C::NBLK) features(fb + 1);
             if (causal) {
                 // own features from the tile (not kept in registers); key
                 // tiles after the own one are all masked and skipped
@@ -1719,14 +1731,18 @@ struct BwdQLds {
     static constexpr int n_zr = TB * C::ROWE;                   // [v | 1] rows
     static constexpr int n_yr = TB * C::ROWE;                   // y rows (hi)
     static constexpr int n_ylo = YLO ? TB * C::ROWE : 0;        // y rows (lo)
-    // The per-block tiles (sketch rows, key features) are double-buffered:
-    // block fb uses buffer fb % 2, so one barrier per block separates writes
-    // from reads. The y lo rows (first sub-block of a sequence only, read
-    // before the block loop) share the feature buffers where they fit.
-    static constexpr bool YLO_SHARED = n_ylo <= 2 * n_cols;
+    // The per-block tiles (sketch rows, key features) are double-buffered
+    // where they fit: block fb uses buffer fb % 2, so one barrier per block
+    // separates writes from reads (a single buffer, float32 P = 6, takes a
+    // second barrier per block). The y lo rows (first sub-block of a sequence
+    // only, read before the block loop) share the feature buffers where they
+    // fit.
+    static constexpr int NB = ((2 * n_ms + 2 * n_cols + n_zr + n_yr) * (int)sizeof(elem) <= 160 * 1024) ? 2 : 1;
+    static_assert(NB == 2 || (C::F32 && C::P == 6), "single buffers for float32 P = 6 only");
+    static constexpr bool YLO_SHARED = n_ylo <= NB * n_cols;
     static constexpr int o_ms = 0;
-    static constexpr int o_cols = o_ms + 2 * n_ms;
-    static constexpr int o_zr = o_cols + 2 * n_cols;
+    static constexpr int o_cols = o_ms + NB * n_ms;
+    static constexpr int o_zr = o_cols + NB * n_cols;
     static constexpr int o_yr = o_zr + n_zr;
     static constexpr int o_end = o_yr + n_yr;
     static constexpr int o_ylo = YLO_SHARED ? o_cols : o_end;
@@ -1760,7 +1776,7 @@ __attribute__((amdgpu_waves_per_eu(BwdQLds<C>::OCC, BwdQLds<C>::OCC))) void k_bw
     const size_t base = (size_t)bh * a.N;
     const elem* WTp = reinterpret_cast<const elem*>(reinterpret_cast<const char*>(a.WTp) + (bh % a.H) * a.wt_hs);
     constexpr bool causal = CAUSAL;
-    zero_sketch_pads<C>(s_ms, 2);
+    zero_sketch_pads<C>(s_ms, LD::NB);
     zero_pads<C>(s_zr, s_yr);
     if (LD::YLO) zero_pads<C>(s_ylo, nullptr);
     __syncthreads();   // the padding is written by all waves, read by each
@@ -1874,8 +1890,9 @@ __attribute__((amdgpu_waves_per_eu(BwdQLds<C>::OCC, BwdQLds<C>::OCC))) void k_bw
             const Planes<C> qa = pa, kb_ = pb;
             if (fb + 1 < C::NBLK) issue_planes(it, fb + 1);
             else if (it + 1 < nsub) issue_planes(it + 1, 0);
-            elem* ms_b = s_ms + (fb & 1) * LD::n_ms;
-            elem* cols_b = s_cols + (fb & 1) * LD::n_cols;
+            const int bsel = LD::NB == 2 ? (fb & 1) : 0;
+            elem* ms_b = s_ms + bsel * LD::n_ms;
+            elem* cols_b = s_cols + bsel * LD::n_cols;
             write_sketch_rows<C, TR>(fb, w, ln, g, Macc, Zacc, ms_b);
             if (causal) {
                 frag unused[C::FBK];
@@ -1911,6 +1928,7 @@ __attribute__((amdgpu_waves_per_eu(BwdQLds<C>::OCC, BwdQLds<C>::OCC))) void k_bw
                 }
             }
             if (causal) sketch_update<C, true, C::ROWE, false, TR>(fb, w, ln, g, cols_b, s_zr, Macc, Zacc);
+            if (LD::NB == 1) __syncthreads();   // single buffer: read before the next block's writes
         }
         __syncthreads();   // the next sub-block rewrites the y and z rows
         if constexpr (!H2) {
@@ -1937,9 +1955,6 @@ struct BwdKLds {
     using elem = typename Prec<C::F32>::elem;
     static constexpr bool DV = PART == KPART_DV;
     static constexpr bool DK = PART == KPART_DK;
-    // per-block tiles, double-buffered: block fb uses buffer fb % 2, so one
-    // barrier per block separates writes from reads
-    static constexpr int NB = 2;
     static constexpr int n_rows = DV ? TB * C::ROWF : 0;        // key features [64][ROWF]
     static constexpr int n_brow = DV ? TB * C::ROWF : 0;        // query features [64][ROWF]
     static constexpr int n_cols = DK ? TB * C::ROWF : 0;        // query features, token rows
@@ -1955,6 +1970,12 @@ struct BwdKLds {
     static constexpr bool ZLO = DK && !C::F32;
     static constexpr int n_zlo = ZLO ? TB * C::ROWE : 0;
     static constexpr int n_yr = DK ? TB * C::ROWE : 0;          // [v | 1] rows
+    // per-block tiles, double-buffered where they fit: block fb uses buffer
+    // fb % 2, so one barrier per block separates writes from reads (a single
+    // buffer, float32 P = 6, takes a second barrier per block)
+    static constexpr int NB =
+        ((2 * (n_rows + n_brow + n_cols + n_ms) + TB * ZS + n_yr) * (int)sizeof(elem) <= 160 * 1024) ? 2 : 1;
+    static_assert(NB == 2 || (C::F32 && C::P == 6), "single buffers for float32 P = 6 only");
     // Tiles live outside the block loop share the block buffers where they
     // fit: the intra scores the first query-feature buffer (dV) or the feature
     // buffers (dK), the residual rows the feature buffers.
@@ -2130,7 +2151,7 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
             const Planes<C> ka = pa, qb = pb;
             if (fb + 1 < C::NBLK) issue_planes(it, fb + 1);
             else if (it + 1 < nsub) issue_planes(it + 1, 0);
-            const int bsel = fb & 1;
+            const int bsel = LD::NB == 2 ? (fb & 1) : 0;
             elem* rows_b = s_rows + bsel * LD::RB;
             elem* brow_b = s_brow + bsel * LD::RB;
             elem* cols_b = s_cols + bsel * LD::n_cols;
@@ -2198,6 +2219,7 @@ __attribute__((amdgpu_waves_per_eu(BwdKLds<C, PART>::OCC, BwdKLds<C, PART>::OCC)
                 }
             }
             if (causal) sketch_update<C, DK, LD::ZS, DV, TR>(fb, w, ln, g, DV ? brow_b : cols_b, s_zr, Macc, Zacc);
+            if (LD::NB == 1) __syncthreads();   // single buffer: read before the next block's writes
         }
         __syncthreads();   // the block tiles are read; the sub-block tiles below reuse them
         if constexpr (DV) {

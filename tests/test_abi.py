@@ -167,15 +167,17 @@ def test_forward_argument_errors_before_device_work():
     assert L.race_attn_fwd(*bad, need, None) == race.RACE_ERR_UNSUPPORTED
 
 
-def test_p6_float32_rejected_before_device_work():
-    # P = 6 runs on bf16 inputs only; float32 is refused after the shape
-    # checks and before any launch (the pointers here are never dereferenced)
+def test_p6_sizes_for_both_dtypes():
+    # P = 6 is supported for both input types: the sizes are reported, and an
+    # undersized workspace is still refused before any launch (the pointers
+    # here are never dereferenced)
     L = race.lib()
     need = race.workspace_bytes(1, 1, 100, 64, 6, 4, True, 64, race.WS_FWD)
-    args = (FAKE, FAKE, FAKE, FAKE, 1, 1, 100, 64, 6, 4, 1.0, 1, 64, race.RACE_F32, FAKE, None, FAKE, need, None)
-    assert L.race_attn_fwd(*args) == race.RACE_ERR_UNSUPPORTED
-    assert L.race_attn_hash(FAKE, FAKE, 1, 1, 10, 64, 6, 4, race.RACE_F32, FAKE, FAKE, None) == \
-        race.RACE_ERR_UNSUPPORTED
+    assert need > 0 and race.saved_bytes(1, 1, 100, 64, 6, 4, True, 64) > 0
+    for dt in (race.RACE_F32, race.RACE_BF16):
+        args = (FAKE, FAKE, FAKE, FAKE, 1, 1, 100, 64, 6, 4, 1.0, 1, 64, dt, FAKE, None, FAKE, need - 1, None)
+        assert L.race_attn_fwd(*args) == race.RACE_ERR_WORKSPACE
+    assert race.state_bytes(1, 1, 6, 4) > 0
 
 
 def test_backward_and_hash_argument_errors():

@@ -91,8 +91,6 @@ def check(res, ref, dtype, label):
                                  (2, 70), (5, 8), (5, 11), (6, 4), (6, 9)])
 @pytest.mark.parametrize("n0", [0, 1, 301])
 def test_decode_soft_matches_oracle(lib, dtype, P, L, n0):
-    if P == 6 and dtype == "f32":
-        pytest.skip("P = 6 runs on bf16 inputs only")
     # (4, 32): the largest state, F = 512 = one thread per feature; (2, 64),
     # (1, 100): 128 and 100 projection rows, eight projection tiles
     T, B, H, beta, chunk = 5, 2, 3, 1.0, 64

@@ -97,9 +97,12 @@ def test_causal_extreme_shape_bf16(lib):
 
 # --- precision / shape coverage -------------------------------------------------
 
-@pytest.mark.parametrize("P,L", [(1, 5), (2, 8), (3, 4), (4, 3), (4, 8), (4, 20), (1, 130), (5, 3), (5, 9)])
+@pytest.mark.parametrize("P,L", [(1, 5), (2, 8), (3, 4), (4, 3), (4, 8), (4, 20), (1, 130), (5, 3), (5, 9),
+                                 (6, 4), (6, 9)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp32_all_planes(lib, P, L, causal):
+    # (6, 4), (6, 9): float32 P = 6 runs the gradient passes with single-buffered
+    # block tiles (the double-buffered ones exceed the LDS)
     run_case(lib, 1, 1, 150, P, L, "f32", causal, 100, beta=0.8, seed=7 + P)
 
 
@@ -244,8 +247,6 @@ def test_first_token_sees_only_itself(lib, dtype):
 @pytest.mark.parametrize("P,L", [(1, 7), (2, 8), (3, 5), (4, 16), (4, 32), (4, 40), (1, 150), (5, 9), (6, 5)])
 def test_hard_hash_bit_exact(lib, dtype, P, L):
     import torch
-    if P == 6 and dtype == "f32":
-        pytest.skip("P = 6 runs on bf16 inputs only")
     x = host_inputs(31 + P, 2, 3, 777, 64, P, L, dtype)
     dev = torch.device("cuda:0")
     X = to_torch(x["Q"], dev)
@@ -307,7 +308,7 @@ def test_long_sequence_late_tokens(lib, P, L, N):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("P,L,N,chunk", [(4, 16, 300, 64), (3, 5, 517, 128), (2, 3, 130, 64), (1, 2, 200, 32),
-                                         (4, 20, 300, 64), (5, 3, 200, 64)])
+                                         (4, 20, 300, 64), (5, 3, 200, 64), (6, 5, 200, 64)])
 def test_hard_forward(lib, dtype, causal, P, L, N, chunk):
     """One-hot buckets through the whole forward: against the oracle's bucket
     sums, with queries that collide with nothing reading exactly 0. Inputs
@@ -481,7 +482,7 @@ def test_head_dim_32_hash_and_hard(lib, dtype):
 
 @pytest.mark.parametrize("dtype,causal,P,L", [("bf16", True, 4, 16), ("bf16", False, 4, 20), ("f32", True, 2, 8),
                                              ("f32", False, 4, 5), ("bf16", True, 5, 9), ("bf16", True, 4, 40),
-                                             ("f32", True, 3, 6), ("bf16", False, 6, 4)])
+                                             ("f32", True, 3, 6), ("bf16", False, 6, 4), ("f32", True, 6, 5)])
 def test_head_dim_128(lib, dtype, causal, P, L):
     # plane values from the whole 128-column rows, the sketch passes once per
     # 64-column value half, the per-plane gradients of both halves summed and
