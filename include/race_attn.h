@@ -66,7 +66,11 @@
  *     their value sums are stored in bf16 (the precision of the matrix-core
  *     operands they feed), their masses and the empty subset's value sums in
  *     float32. No atomics are used on the attention path, so results are
- *     bitwise reproducible run to run.
+ *     bitwise reproducible run to run. The read-out sums monomial terms that
+ *     cancel for a query whose soft collisions with the keys are nearly
+ *     zero (sharp temperatures with few tables); such rows lose accuracy in
+ *     proportion to the operand precision over their denominator, most with
+ *     RACE_BF16 inputs, where RACE_F32 keeps it.
  *   - `chunk` is the number of tokens a workgroup owns; per-chunk sketch
  *     states are published and prefix-scanned at that granularity. Results do
  *     not depend on it beyond float32 rounding.
