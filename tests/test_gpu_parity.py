@@ -560,3 +560,37 @@ def test_head_dim_128_per_head_and_hard(lib, dtype):
     print("   per-head rel_l2", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
     for k, e in errs.items():
         assert e <= TOL[dtype], (k, e)
+
+
+# --- seeded random shapes ------------------------------------------------------
+
+def _random_shapes(n, seed=11):
+    """n shapes drawn from the supported set away from the small-denominator
+    regime (temperature <= 2, at least 4 tables, at least 2 tokens): P 1..6,
+    L 4..70, d 32 / 64 / 128, ragged N and chunk, both modes and dtypes,
+    normal or clustered keys."""
+    import random
+    rng = random.Random(seed)
+    out = []
+    while len(out) < n:
+        P = rng.randint(1, 6)
+        L = rng.choice([rng.randint(4, 40), rng.randint(4, 70)])
+        d = rng.choice([64, 64, 32, 128])
+        N = rng.choice([2, 63, 64, 65, rng.randint(2, 700)])
+        chunk = rng.choice([1, 5, 64, 100, 128, rng.randint(1, 900)])
+        causal = rng.random() < 0.6
+        dtype = rng.choice(["bf16", "f32"])
+        beta = rng.choice([0.5, 1.0, 2.0])
+        B, H = rng.choice([(1, 1), (1, 2), (2, 3)])
+        dist = rng.choice(["normal", "normal", "mixture"])
+        if L * (1 << P) <= 65536:
+            out.append((len(out), P, L, d, N, chunk, causal, dtype, beta, B, H, dist))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_shapes(40),
+                         ids=lambda c: f"{c[0]}-P{c[1]}-L{c[2]}-d{c[3]}-N{c[4]}-ch{c[5]}-"
+                                       f"{'causal' if c[6] else 'full'}-{c[7]}-b{c[8]}-{c[11]}")
+def test_random_shapes(lib, case):
+    i, P, L, d, N, chunk, causal, dtype, beta, B, H, dist = case
+    run_case(lib, B, H, N, P, L, dtype, causal, chunk, beta=beta, dist=dist, seed=31000 + i, d=d)
